@@ -1,0 +1,170 @@
+"""ctypes shim over the fp64 CPU oracle (``mhc_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py``.  The product library never imports
+it, and it imports nothing from the product package.
+
+All results are returned as unrounded float64 numpy arrays; callers round them
+(``round_bf16``, ``np.float32``) where a comparison needs the rounded value.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from pathlib import Path
+
+import numpy as np
+
+_DIR = Path(__file__).resolve().parent
+_SRC = _DIR / "mhc_oracle.c"
+_LIB_PATH = _DIR / "libmhc_oracle.so"
+_lib = None
+
+HC = 4
+MIX = 24
+
+
+def build(verbose: bool = False) -> Path:
+    """Compile the oracle with gcc (plain -O2, no fast-math, no FMA contraction)."""
+    cmd = ["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+           "-o", str(_LIB_PATH) + ".tmp", str(_SRC), "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(str(_LIB_PATH) + ".tmp", _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not _LIB_PATH.exists() or _LIB_PATH.stat().st_mtime < _SRC.stat().st_mtime:
+        build()
+    lib = ctypes.CDLL(str(_LIB_PATH))
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    D = ctypes.c_double
+    lib.orc_f64_to_bf16.argtypes = [D]
+    lib.orc_f64_to_bf16.restype = ctypes.c_uint16
+    lib.orc_round_bf16.argtypes = [P, I64, P]
+    lib.orc_rms.argtypes = [P, I64, I64, D, P, P]
+    lib.orc_project.argtypes = [P, P, I64, I64, P]
+    lib.orc_mix_activation.argtypes = [P, P, P, P, I64, D, D, P, P, P]
+    lib.orc_sinkhorn.argtypes = [P, I64, ctypes.c_int, D, P]
+    lib.orc_collapse.argtypes = [P, P, I64, I64, P]
+    lib.orc_post.argtypes = [P, P, P, P, I64, I64, P]
+    lib.orc_pre.argtypes = [P, P, P, P, I64, I64, D, D, D, D, ctypes.c_int, P, P, P, P, P, P]
+    for f in ("orc_round_bf16", "orc_rms", "orc_project", "orc_mix_activation", "orc_sinkhorn",
+              "orc_collapse", "orc_post", "orc_pre"):
+        getattr(lib, f).restype = None
+    _lib = lib
+    return lib
+
+
+def _c(a: np.ndarray, dtype) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _p(a: np.ndarray):
+    return ctypes.c_void_p(a.ctypes.data) if a is not None else None
+
+
+def round_bf16(v: np.ndarray) -> np.ndarray:
+    """Round fp64 values to bf16 bit patterns (nearest, ties to even), directly from fp64."""
+    v = _c(v, np.float64)
+    out = np.empty(v.shape, dtype=np.uint16)
+    _load().orc_round_bf16(_p(v), v.size, _p(out))
+    return out
+
+
+def rms(res: np.ndarray, rms_eps: float):
+    """Step A1: (sqsum [T], rstd [T]) of res [T,4,H] (bf16 bits)."""
+    res = _c(res, np.uint16)
+    T, hc, H = res.shape
+    assert hc == HC
+    sq = np.empty(T)
+    rstd = np.empty(T)
+    _load().orc_rms(_p(res), T, H, rms_eps, _p(sq), _p(rstd))
+    return sq, rstd
+
+
+def project(res: np.ndarray, hc_fn: np.ndarray) -> np.ndarray:
+    """Step A2: dot [T,24] = res_flat @ hc_fn^T in fp64."""
+    res = _c(res, np.uint16)
+    hc_fn = _c(hc_fn, np.float32)
+    T, hc, H = res.shape
+    assert hc == HC and hc_fn.shape == (MIX, HC * H)
+    dot = np.empty((T, MIX))
+    _load().orc_project(_p(res), _p(hc_fn), T, H, _p(dot))
+    return dot
+
+
+def mix_activation(dot, rstd, hc_scale, hc_base, pre_eps, post_mult):
+    """Step A3: (pre [T,4], post [T,4], comb_logits [T,4,4])."""
+    dot = _c(dot, np.float64)
+    rstd = _c(rstd, np.float64)
+    hc_scale = _c(hc_scale, np.float32)
+    hc_base = _c(hc_base, np.float32)
+    T = dot.shape[0]
+    pre = np.empty((T, HC))
+    post = np.empty((T, HC))
+    logits = np.empty((T, HC, HC))
+    _load().orc_mix_activation(_p(dot), _p(rstd), _p(hc_scale), _p(hc_base), T, pre_eps, post_mult,
+                               _p(pre), _p(post), _p(logits))
+    return pre, post, logits
+
+
+def sinkhorn(logits: np.ndarray, num_iters: int = 20, eps: float = 1e-6) -> np.ndarray:
+    """Step A4: [n,4,4] logits -> [n,4,4] Sinkhorn projection (fp64)."""
+    lg = _c(logits, np.float64)
+    shape = lg.shape
+    assert shape[-2:] == (HC, HC)
+    n = int(np.prod(shape[:-2])) if len(shape) > 2 else 1
+    out = np.empty(shape)
+    _load().orc_sinkhorn(_p(lg), n, int(num_iters), eps, _p(out))
+    return out
+
+
+def collapse(res: np.ndarray, pre: np.ndarray) -> np.ndarray:
+    """Step A5: y [T,H] = sum_i pre[:,i] * res[:,i,:]."""
+    res = _c(res, np.uint16)
+    pre = _c(pre, np.float64)
+    T, hc, H = res.shape
+    y = np.empty((T, H))
+    _load().orc_collapse(_p(res), _p(pre), T, H, _p(y))
+    return y
+
+
+def post(x: np.ndarray, res: np.ndarray, post: np.ndarray, comb: np.ndarray) -> np.ndarray:
+    """Step A6: out [T,4,H] (fp64, unrounded)."""
+    x = _c(x, np.uint16)
+    res = _c(res, np.uint16)
+    post_ = _c(post, np.float64).reshape(-1, HC)
+    comb = _c(comb, np.float64).reshape(-1, HC, HC)
+    T, hc, H = res.shape
+    assert x.shape == (T, H) and post_.shape[0] == T and comb.shape[0] == T
+    out = np.empty((T, HC, H))
+    _load().orc_post(_p(x), _p(res), _p(post_), _p(comb), T, H, _p(out))
+    return out
+
+
+def pre(res, hc_fn, hc_scale, hc_base, rms_eps=1e-6, pre_eps=1e-6, sinkhorn_eps=1e-6, post_mult=1.0,
+        num_iters=20):
+    """Whole pre-map.  Returns dict of fp64 arrays: y, post, comb, pre, dot, rstd."""
+    res = _c(res, np.uint16)
+    hc_fn = _c(hc_fn, np.float32)
+    hc_scale = _c(hc_scale, np.float32)
+    hc_base = _c(hc_base, np.float32)
+    T, hc, H = res.shape
+    assert hc == HC and hc_fn.shape == (MIX, HC * H) and hc_scale.shape == (3,) and hc_base.shape == (MIX,)
+    y = np.empty((T, H))
+    post_ = np.empty((T, HC))
+    comb = np.empty((T, HC, HC))
+    pre_ = np.empty((T, HC))
+    dot = np.empty((T, MIX))
+    rstd = np.empty(T)
+    _load().orc_pre(_p(res), _p(hc_fn), _p(hc_scale), _p(hc_base), T, H, rms_eps, pre_eps, sinkhorn_eps,
+                    post_mult, int(num_iters), _p(y), _p(post_), _p(comb), _p(pre_), _p(dot), _p(rstd))
+    return dict(y=y, post=post_, comb=comb, pre=pre_, dot=dot, rstd=rstd)

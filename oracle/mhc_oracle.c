@@ -1,0 +1,272 @@
+/*
+ * mhc_oracle.c -- plain, slow, fp64 CPU oracle for the mHC residual-mixing path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header or constant with the HIP library, and the product path never calls it.
+ *
+ * Every step is written from the pages' definitions, one scalar loop per
+ * formula, with fp64 arithmetic throughout.  bf16 and fp32 inputs are widened
+ * exactly; results are returned unrounded in fp64 (the tests round them, or
+ * compare against the unrounded value).
+ *
+ * Sources (page title -> section):
+ *  - "FlashInfer mHC 模块深度解析" (FlashInfer mHC article), section 1: HC = 4 and
+ *    the 24-logit layout pre[0:4], post[4:8], comb[8:24] viewed as 4x4.
+ *  - same article, section 2.1: the post-map formula
+ *    out[n][h] = x[h]*post[n] + sum_o res[o][h]*comb[o][n].
+ *  - same article, section 3.4: rstd = rsqrt(sqrsum/K + rms_eps), K = 4H
+ *    (section 4: the denominator is fixed at 4*H when the sum is computed in-kernel).
+ *  - same article, section 5.2 (test reference implementation): mixes = dot*rstd,
+ *    per-group scale and base, pre = sigmoid + pre_eps, post = sigmoid * post_mult,
+ *    comb = Sinkhorn of the comb logits, layer_input = sum_i pre_i * res_i;
+ *    and the Sinkhorn schedule: softmax over the last axis, + eps, then
+ *    `repeat` rounds of (row normalise, column normalise).
+ *  - metrale glm5next_mhc.rs, `glm_hc_post` doc comment: the same post formula
+ *    with comb[i][j] weighting old stream i into new stream j.
+ *  - metrale glm5next_mhc.rs, `Glm5NextMhcSiteWeights`: hc_fn is
+ *    [mix_hc, hc_mult*hidden] and hc_scale holds the pre, post, comb scales in
+ *    that order.
+ *
+ * Readings where the pages are silent (each also listed in the design notes):
+ *  - flatten order of [4, H] into the K = 4H projection axis: k = i*H + h;
+ *  - the Sinkhorn eps is added once after the softmax; the row and column
+ *    divisions carry no eps; the softmax subtracts the row maximum;
+ *  - `num_iters` counts (row, column) pairs, with no early exit.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+
+#define ORC_HC 4
+#define ORC_MIX 24
+
+/* bf16 bit pattern -> double, exact (bf16 is the top half of an IEEE binary32). */
+static double orc_bf16_to_f64(uint16_t b)
+{
+    uint32_t u = ((uint32_t)b) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Round a double to the nearest bfloat16 (ties to even), directly from fp64
+ * (no intermediate binary32 rounding).  bf16 keeps 8 significant bits and the
+ * binary32 exponent range. */
+uint16_t orc_f64_to_bf16(double v)
+{
+    if (isnan(v)) {
+        return (uint16_t)0x7FC0u;
+    }
+    double a = fabs(v);
+    double r;
+    if (a == 0.0 || isinf(v)) {
+        r = v;
+    } else {
+        int e;
+        frexp(a, &e); /* a = m * 2^e, 0.5 <= m < 1: leading bit has weight 2^(e-1) */
+        int ulp_exp = e - 8; /* 8 significant bits */
+        if (ulp_exp < -133) {
+            ulp_exp = -133; /* binary32 subnormal spacing */
+        }
+        double q = ldexp(a, -ulp_exp);
+        double qr = nearbyint(q); /* default rounding mode: nearest, ties to even */
+        r = copysign(ldexp(qr, ulp_exp), v);
+        if (fabs(r) >= ldexp(1.0, 128)) {
+            r = copysign(INFINITY, v);
+        }
+    }
+    float f = (float)r; /* exact: r has at most 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(u >> 16);
+}
+
+void orc_round_bf16(const double *v, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        out[i] = orc_f64_to_bf16(v[i]);
+    }
+}
+
+/* Step A1 (FlashInfer mHC article, sections 3.4 and 5.2): per-token sum of
+ * squares over the 4 streams and rstd = 1 / sqrt(S / (4H) + rms_eps). */
+void orc_rms(const uint16_t *res, int64_t T, int64_t H, double rms_eps, double *sqsum, double *rstd)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        double s = 0.0;
+        for (int64_t i = 0; i < ORC_HC; ++i) {
+            for (int64_t h = 0; h < H; ++h) {
+                double v = orc_bf16_to_f64(res[(t * ORC_HC + i) * H + h]);
+                s += v * v;
+            }
+        }
+        if (sqsum) {
+            sqsum[t] = s;
+        }
+        rstd[t] = 1.0 / sqrt(s / (double)(ORC_HC * H) + rms_eps);
+    }
+}
+
+/* Step A2: dot[t][r] = sum_k hc_fn[r][k] * res_flat[t][k], with the streams
+ * flattened as k = i*H + h.  hc_fn is [24, 4H] row-major. */
+void orc_project(const uint16_t *res, const float *hc_fn, int64_t T, int64_t H, double *dot)
+{
+    const int64_t K = ORC_HC * H;
+    for (int64_t t = 0; t < T; ++t) {
+        const uint16_t *row = res + t * K;
+        for (int64_t r = 0; r < ORC_MIX; ++r) {
+            const float *w = hc_fn + r * K;
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                acc += (double)w[k] * orc_bf16_to_f64(row[k]);
+            }
+            dot[t * ORC_MIX + r] = acc;
+        }
+    }
+}
+
+static double orc_sigmoid(double z)
+{
+    return 1.0 / (1.0 + exp(-z));
+}
+
+/* Step A3 (FlashInfer mHC article, section 5.2): m = dot * rstd, then
+ *   pre_i  = sigmoid(m_i * s0 + b_i) + pre_eps
+ *   post_i = sigmoid(m_{4+i} * s1 + b_{4+i}) * post_mult
+ *   L_ij   = m_{8+4i+j} * s2 + b_{8+4i+j}            (comb logits, 4x4 row-major)
+ * with hc_scale = (s0, s1, s2) in the order pre, post, comb. */
+void orc_mix_activation(const double *dot, const double *rstd, const float *hc_scale, const float *hc_base,
+                        int64_t T, double pre_eps, double post_mult, double *pre, double *post, double *comb_logits)
+{
+    const double s_pre = hc_scale[0], s_post = hc_scale[1], s_comb = hc_scale[2];
+    for (int64_t t = 0; t < T; ++t) {
+        const double *d = dot + t * ORC_MIX;
+        for (int i = 0; i < ORC_HC; ++i) {
+            double m = d[i] * rstd[t];
+            pre[t * ORC_HC + i] = orc_sigmoid(m * s_pre + (double)hc_base[i]) + pre_eps;
+        }
+        for (int i = 0; i < ORC_HC; ++i) {
+            double m = d[ORC_HC + i] * rstd[t];
+            post[t * ORC_HC + i] = orc_sigmoid(m * s_post + (double)hc_base[ORC_HC + i]) * post_mult;
+        }
+        for (int c = 0; c < ORC_HC * ORC_HC; ++c) {
+            double m = d[2 * ORC_HC + c] * rstd[t];
+            comb_logits[t * ORC_HC * ORC_HC + c] = m * s_comb + (double)hc_base[2 * ORC_HC + c];
+        }
+    }
+}
+
+/* Step A4 (FlashInfer mHC article, section 5.2, the Sinkhorn reference; rwkv-ops
+ * sinkhorn_knopp docstring for the [.., N, N] -> doubly-stochastic contract):
+ *   P = softmax(L, over each row) + eps
+ *   repeat num_iters times: divide each row by its sum; divide each column by its sum.
+ * `logits` and `out` are [n, 4, 4] row-major; they may be the same array. */
+void orc_sinkhorn(const double *logits, int64_t n, int num_iters, double eps, double *out)
+{
+    for (int64_t b = 0; b < n; ++b) {
+        double P[ORC_HC][ORC_HC];
+        const double *L = logits + b * ORC_HC * ORC_HC;
+        for (int i = 0; i < ORC_HC; ++i) {
+            double mx = L[i * ORC_HC];
+            for (int j = 1; j < ORC_HC; ++j) {
+                if (L[i * ORC_HC + j] > mx) {
+                    mx = L[i * ORC_HC + j];
+                }
+            }
+            double s = 0.0;
+            for (int j = 0; j < ORC_HC; ++j) {
+                P[i][j] = exp(L[i * ORC_HC + j] - mx);
+                s += P[i][j];
+            }
+            for (int j = 0; j < ORC_HC; ++j) {
+                P[i][j] = P[i][j] / s + eps;
+            }
+        }
+        for (int it = 0; it < num_iters; ++it) {
+            for (int i = 0; i < ORC_HC; ++i) {
+                double s = 0.0;
+                for (int j = 0; j < ORC_HC; ++j) {
+                    s += P[i][j];
+                }
+                for (int j = 0; j < ORC_HC; ++j) {
+                    P[i][j] /= s;
+                }
+            }
+            for (int j = 0; j < ORC_HC; ++j) {
+                double s = 0.0;
+                for (int i = 0; i < ORC_HC; ++i) {
+                    s += P[i][j];
+                }
+                for (int i = 0; i < ORC_HC; ++i) {
+                    P[i][j] /= s;
+                }
+            }
+        }
+        double *O = out + b * ORC_HC * ORC_HC;
+        for (int i = 0; i < ORC_HC; ++i) {
+            for (int j = 0; j < ORC_HC; ++j) {
+                O[i * ORC_HC + j] = P[i][j];
+            }
+        }
+    }
+}
+
+/* Step A5 (FlashInfer mHC article, sections 3.4 and 5.2; rwkv-ops
+ * stream_aggregate): y[t][h] = sum_i pre[t][i] * res[t][i][h]. */
+void orc_collapse(const uint16_t *res, const double *pre, int64_t T, int64_t H, double *y)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t h = 0; h < H; ++h) {
+            double acc = 0.0;
+            for (int i = 0; i < ORC_HC; ++i) {
+                acc += pre[t * ORC_HC + i] * orc_bf16_to_f64(res[(t * ORC_HC + i) * H + h]);
+            }
+            y[t * H + h] = acc;
+        }
+    }
+}
+
+/* Step A6 (FlashInfer mHC article, section 2.1; metrale glm_hc_post):
+ *   out[t][n][h] = x[t][h] * post[t][n] + sum_o res[t][o][h] * comb[t][o][n]. */
+void orc_post(const uint16_t *x, const uint16_t *res, const double *post, const double *comb, int64_t T, int64_t H,
+              double *out)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        for (int n = 0; n < ORC_HC; ++n) {
+            for (int64_t h = 0; h < H; ++h) {
+                double acc = orc_bf16_to_f64(x[t * H + h]) * post[t * ORC_HC + n];
+                for (int o = 0; o < ORC_HC; ++o) {
+                    acc += orc_bf16_to_f64(res[(t * ORC_HC + o) * H + h]) * comb[(t * ORC_HC + o) * ORC_HC + n];
+                }
+                out[(t * ORC_HC + n) * H + h] = acc;
+            }
+        }
+    }
+}
+
+/* The whole pre-map, one token at a time: A1 -> A2 -> A3 -> A4 -> A5.
+ * Outputs (fp64, unrounded): y [T,H], post [T,4], comb [T,4,4], pre [T,4];
+ * `dot` [T,24] and `rstd` [T] are optional (may be NULL). */
+void orc_pre(const uint16_t *res, const float *hc_fn, const float *hc_scale, const float *hc_base, int64_t T,
+             int64_t H, double rms_eps, double pre_eps, double sinkhorn_eps, double post_mult, int num_iters,
+             double *y, double *post, double *comb, double *pre, double *dot_out, double *rstd_out)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        const uint16_t *r = res + t * ORC_HC * H;
+        double rstd, dot[ORC_MIX], logits[ORC_HC * ORC_HC];
+        orc_rms(r, 1, H, rms_eps, NULL, &rstd);
+        orc_project(r, hc_fn, 1, H, dot);
+        orc_mix_activation(dot, &rstd, hc_scale, hc_base, 1, pre_eps, post_mult, pre + t * ORC_HC,
+                           post + t * ORC_HC, logits);
+        orc_sinkhorn(logits, 1, num_iters, sinkhorn_eps, comb + t * ORC_HC * ORC_HC);
+        orc_collapse(r, pre + t * ORC_HC, 1, H, y + t * H);
+        if (dot_out) {
+            memcpy(dot_out + t * ORC_MIX, dot, sizeof dot);
+        }
+        if (rstd_out) {
+            rstd_out[t] = rstd;
+        }
+    }
+}

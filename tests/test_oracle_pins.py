@@ -1,0 +1,374 @@
+"""Pins of the fp64 CPU oracle against facts that do not come from the oracle itself.
+
+Each test targets a plausible mistake: a dropped term, a wrong sign or index,
+a transposed operand, a wrong softmax axis, a wrong iteration count or order,
+eps in the wrong place, a wrong flatten order, a wrong scale order.
+
+Independent routes used here: numpy matmul/einsum (library primitives),
+closed forms, the textbook scaling-vector form of Sinkhorn-Knopp (Sinkhorn &
+Knopp 1967: P = diag(u) K diag(v), u = 1/(K v), v = 1/(K^T u)), invariants
+(permutation equivariance, column sums) and bit-level rounding facts.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from mhc_inputs import (HC, MIX, bf16_bits_to_f32, f32_to_bf16_bits, layer_inputs, sinkhorn_logits,
+                        stress_logits)
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def _bf16_f64(bits):
+    return bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def _round_bf16_np(v):
+    """Test-side fp64 -> bf16 rounding (nearest-even on the float64 bit pattern).
+
+    bf16 keeps 8 of float64's 53 significant bits, so 45 bits are dropped.
+    Valid for normal values in binary32 range, which is all these tests use.
+    """
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    u = v.view(np.uint64)
+    r = (u + np.uint64((1 << 44) - 1) + ((u >> np.uint64(45)) & np.uint64(1))) >> np.uint64(45)
+    r64 = (r << np.uint64(45)).view(np.float64)
+    return f32_to_bf16_bits(r64.astype(np.float32))
+
+
+def _sk_scaling(logits, num_iters, eps):
+    """Textbook Sinkhorn-Knopp on K = softmax_rows(L) + eps via scaling vectors."""
+    L = np.asarray(logits, dtype=np.float64)
+    K = np.exp(L - L.max(axis=-1, keepdims=True))
+    K = K / K.sum(axis=-1, keepdims=True) + eps
+    v = np.ones(L.shape[:-1])
+    for _ in range(num_iters):
+        u = 1.0 / np.einsum("...ij,...j->...i", K, v)
+        v = 1.0 / np.einsum("...ij,...i->...j", K, u)
+    return u[..., :, None] * K * v[..., None, :]
+
+
+# ---------------------------------------------------------------- rounding
+
+def test_bf16_rounding_bit_facts():
+    r = lambda v: int(oracle.round_bf16(np.array([v]))[0])
+    assert r(1.0) == 0x3F80
+    assert r(-2.0) == 0xC000
+    assert r(0.0) == 0x0000
+    assert r(-0.0) == 0x8000
+    # exact halfway cases go to the even neighbour
+    assert r(1.0 + 2.0 ** -8) == 0x3F80
+    assert r(1.0 + 3 * 2.0 ** -8) == 0x3F82
+    # just above halfway rounds up -- rounding through binary32 first would
+    # lose the 2^-30 and tie back to even (0x3F80)
+    assert r(1.0 + 2.0 ** -8 + 2.0 ** -30) == 0x3F81
+    assert r(float("inf")) == 0x7F80
+    assert r(3.5e38) == 0x7F80  # beyond the largest bf16 -> inf
+
+
+def test_bf16_rounding_matches_independent_rounders():
+    g = np.random.default_rng(11)
+    v32 = (g.standard_normal(20000) * np.exp(g.uniform(-20, 20, 20000))).astype(np.float32)
+    # for binary32-representable values, the generator's binary32 rounder is an independent check
+    assert np.array_equal(oracle.round_bf16(v32.astype(np.float64)), f32_to_bf16_bits(v32))
+    v64 = g.standard_normal(20000) * np.exp(g.uniform(-20, 20, 20000))
+    assert np.array_equal(oracle.round_bf16(v64), _round_bf16_np(v64))
+
+
+# ---------------------------------------------------------------- A1: RMS statistic
+
+def test_rms_constant_closed_form():
+    T, H, c, eps = 3, 37, 1.5, 1e-6
+    res = np.full((T, HC, H), f32_to_bf16_bits(np.array([c], np.float32))[0], dtype=np.uint16)
+    sq, rstd = oracle.rms(res, eps)
+    assert np.allclose(sq, 4 * H * c * c, rtol=0, atol=1e-12)
+    assert np.allclose(rstd, 1.0 / math.sqrt(c * c + eps), rtol=1e-15)
+
+
+def test_rms_matches_numpy_and_k_is_4h():
+    inp = layer_inputs(5, 48, cfg=101)
+    sq, rstd = oracle.rms(inp.res, 1e-6)
+    r = _bf16_f64(inp.res)
+    assert np.allclose(sq, (r * r).sum(axis=(1, 2)), rtol=1e-14)
+    assert np.allclose(rstd, 1.0 / np.sqrt((r * r).mean(axis=(1, 2)) + 1e-6), rtol=1e-14)
+
+
+# ---------------------------------------------------------------- A2: projection
+
+def test_project_matches_matmul_with_row_major_flatten():
+    inp = layer_inputs(6, 40, cfg=102)
+    dot = oracle.project(inp.res, inp.hc_fn)
+    ref = _bf16_f64(inp.res).reshape(6, HC * 40) @ inp.hc_fn.astype(np.float64).T
+    assert np.allclose(dot, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_project_one_hot_rows_pick_stream_i_element_h():
+    T, H = 4, 16
+    inp = layer_inputs(T, H, cfg=103)
+    fn = np.zeros((MIX, HC * H), np.float32)
+    picks = [(r, r % HC, (5 * r + 3) % H) for r in range(MIX)]
+    for r, i, h in picks:
+        fn[r, i * H + h] = 1.0
+    dot = oracle.project(inp.res, fn)
+    r64 = _bf16_f64(inp.res)
+    for r, i, h in picks:
+        assert np.array_equal(dot[:, r], r64[:, i, h])
+
+
+# ---------------------------------------------------------------- A3: activations
+
+def _sig(z):
+    return 1.0 / (1.0 + np.exp(-np.asarray(z, dtype=np.float64)))
+
+
+def test_activation_zero_scale_gives_base_layout():
+    g = np.random.default_rng(5)
+    T = 3
+    dot = g.standard_normal((T, MIX))
+    rstd = g.uniform(0.5, 2, T)
+    base = g.standard_normal(MIX).astype(np.float32)
+    pre, post, L = oracle.mix_activation(dot, rstd, np.zeros(3, np.float32), base, 1e-6, 2.0)
+    b = base.astype(np.float64)
+    for t in range(T):
+        assert np.allclose(pre[t], _sig(b[0:4]) + 1e-6, rtol=1e-15)
+        assert np.allclose(post[t], 2.0 * _sig(b[4:8]), rtol=1e-15)
+        assert np.array_equal(L[t], b[8:24].reshape(4, 4))
+
+
+def test_activation_sigmoid_of_zero_is_half():
+    pre, post, L = oracle.mix_activation(np.zeros((1, MIX)), np.ones(1), np.ones(3, np.float32),
+                                         np.zeros(MIX, np.float32), 1e-6, 1.0)
+    assert np.all(pre == 0.5 + 1e-6) and np.all(post == 0.5) and np.all(L == 0.0)
+
+
+def test_activation_scale_order_pre_post_comb_and_rstd():
+    T = 2
+    dot = np.zeros((T, MIX))
+    dot[:, 1] = 0.3   # a pre logit
+    dot[:, 6] = -0.7  # a post logit
+    dot[:, 8 + 4 * 2 + 1] = 0.9  # comb[2][1]
+    rstd = np.array([2.0, 0.5])
+    s = np.array([3.0, 5.0, 7.0], np.float32)
+    pre, post, L = oracle.mix_activation(dot, rstd, s, np.zeros(MIX, np.float32), 1e-6, 1.0)
+    for t in range(T):
+        assert math.isclose(pre[t, 1], _sig(0.3 * rstd[t] * 3.0) + 1e-6, rel_tol=1e-15)
+        assert math.isclose(post[t, 2], _sig(-0.7 * rstd[t] * 5.0), rel_tol=1e-15)
+        assert math.isclose(L[t, 2, 1], 0.9 * rstd[t] * 7.0, rel_tol=1e-15)
+        assert pre[t, 0] == 0.5 + 1e-6 and L[t, 1, 2] == 0.0
+
+
+# ---------------------------------------------------------------- A4: Sinkhorn
+
+def test_sinkhorn_constant_and_separable_give_quarter():
+    lg = np.zeros((3, 4, 4))
+    lg[1] = 5.0
+    a = np.array([3.0, -2.0, 0.5, -7.0])
+    b = np.array([-1.0, 4.0, 2.5, -3.5])
+    lg[2] = a[:, None] + b[None, :]
+    for it in (1, 2, 20):
+        out = oracle.sinkhorn(lg, it, 1e-6)
+        assert np.allclose(out, 0.25, atol=1e-15)
+
+
+def test_sinkhorn_one_iteration_closed_form_pins_softmax_axis():
+    # L = 8 at (0,1), 0 elsewhere.  K = softmax_rows(L) + eps has equal row sums,
+    # so one (row, column) round gives P_ij = K_ij / sum_i K_ij.
+    eps = 1e-6
+    L = np.zeros((1, 4, 4))
+    L[0, 0, 1] = 8.0
+    Q = math.exp(8) / (math.exp(8) + 3)
+    q = 1.0 / (math.exp(8) + 3)
+    K = np.full((4, 4), 0.25 + eps)
+    K[0] = [q + eps, Q + eps, q + eps, q + eps]
+    P = K / K.sum(axis=0, keepdims=True)
+    out = oracle.sinkhorn(L, 1, eps)[0]
+    assert np.allclose(out, P, rtol=1e-14, atol=1e-16)
+    # the column-axis softmax would give a different matrix
+    Kc = np.full((4, 4), 0.25 + eps)
+    Kc[:, 1] = [Q + eps, q + eps, q + eps, q + eps]
+    assert not np.allclose(out, Kc / Kc.sum(axis=0, keepdims=True), atol=1e-3)
+
+
+@pytest.mark.parametrize("iters", [1, 2, 3, 7, 20])
+def test_sinkhorn_matches_textbook_scaling_form(iters):
+    lg = sinkhorn_logits(2000, seed=3)
+    out = oracle.sinkhorn(lg, iters, 1e-6)
+    ref = _sk_scaling(lg, iters, 1e-6)
+    assert np.allclose(out, ref, rtol=0, atol=1e-13)
+
+
+def test_sinkhorn_iteration_count_matters():
+    lg = sinkhorn_logits(500, seed=4)
+    a = oracle.sinkhorn(lg, 19, 1e-6)
+    b = oracle.sinkhorn(lg, 20, 1e-6)
+    assert np.abs(a - b).max() > 1e-4  # adjacent counts are distinguishable at the 1e-5 tolerance
+
+
+def test_sinkhorn_columns_sum_to_one_and_rows_converge():
+    lg = sinkhorn_logits(4000, seed=5)
+    out = oracle.sinkhorn(lg, 20, 1e-6)
+    assert np.abs(out.sum(axis=-2) - 1).max() < 1e-14  # last step normalises columns
+    assert np.all(out > 0)
+    lg1 = np.random.default_rng(6).standard_normal((500, 4, 4))
+    lim = oracle.sinkhorn(lg1, 2000, 1e-6)
+    assert np.abs(lim.sum(axis=-1) - 1).max() < 1e-9
+    assert np.abs(lim.sum(axis=-2) - 1).max() < 1e-14
+
+
+def test_sinkhorn_permutation_equivariance():
+    lg = sinkhorn_logits(300, seed=7).astype(np.float64)
+    perm = np.array([2, 0, 3, 1])
+    Pm = np.eye(4)[perm]
+    out = oracle.sinkhorn(lg, 20, 1e-6)
+    out_p = oracle.sinkhorn(Pm @ lg @ Pm.T, 20, 1e-6)
+    assert np.allclose(out_p, Pm @ out @ Pm.T, atol=1e-14)
+
+
+def test_sinkhorn_eps_added_once_after_softmax():
+    # Softmax of [0, -1000, -1000, -1000] is one-hot; only the post-softmax eps keeps
+    # the other entries positive, so the column of zeros fills with eps-sized mass.
+    L = np.full((1, 4, 4), -1000.0)
+    for i in range(4):
+        L[0, i, 0] = 0.0
+    out = oracle.sinkhorn(L, 5, 1e-6)[0]
+    ref = _sk_scaling(L, 5, 1e-6)[0]
+    assert np.allclose(out, ref, atol=1e-14)
+    assert np.allclose(out.sum(axis=0), 1.0, atol=1e-14)
+    assert np.all(out[:, 1:] > 0)
+
+
+def test_sinkhorn_log_of_doubly_stochastic_is_fixed_point():
+    d = 0.7 * np.eye(4) + 0.3 * np.roll(np.eye(4), 1, axis=1)
+    d = 0.9 * d + 0.1 * 0.25
+    out = oracle.sinkhorn(np.log(d)[None], 20, 1e-6)[0]
+    assert np.abs(out - d).max() < 5e-6
+
+
+def test_stress_logits_in_range():
+    s = stress_logits()
+    assert s.shape == (8, 4, 4) and np.abs(s).max() <= 8.0
+    out = oracle.sinkhorn(s, 20, 1e-6)
+    assert np.all(np.isfinite(out)) and np.abs(out.sum(axis=-2) - 1).max() < 1e-14
+
+
+# ---------------------------------------------------------------- A5: collapse
+
+def test_collapse_matches_einsum_and_one_hot():
+    inp = layer_inputs(4, 33, cfg=104)
+    g = np.random.default_rng(8)
+    pre = g.uniform(0, 1, (4, HC))
+    y = oracle.collapse(inp.res, pre)
+    assert np.allclose(y, np.einsum("ti,tih->th", pre, _bf16_f64(inp.res)), rtol=1e-15, atol=1e-15)
+    oh = np.zeros((4, HC))
+    oh[:, 2] = 1.0
+    assert np.array_equal(oracle.collapse(inp.res, oh), _bf16_f64(inp.res)[:, 2, :])
+
+
+# ---------------------------------------------------------------- A6: post-map
+
+def test_post_identity_comb_unit_post_is_res_plus_x_bit_exact():
+    inp = layer_inputs(5, 64, cfg=105)
+    T, H = 5, 64
+    out = oracle.post(inp.x, inp.res, np.ones((T, HC)), np.broadcast_to(np.eye(HC), (T, HC, HC)))
+    ref = _bf16_f64(inp.res) + _bf16_f64(inp.x)[:, None, :]
+    assert np.array_equal(out, ref)
+    assert np.array_equal(oracle.round_bf16(out), _round_bf16_np(ref))
+
+
+def test_post_identity_comb_zero_post_is_res():
+    inp = layer_inputs(3, 50, cfg=106)
+    out = oracle.post(inp.x, inp.res, np.zeros((3, HC)), np.broadcast_to(np.eye(HC), (3, HC, HC)))
+    assert np.array_equal(oracle.round_bf16(out), inp.res)
+
+
+def test_post_permutation_comb_orientation():
+    # comb[o][n] = 1 when n = perm[o]: old stream o moves to new stream perm[o]
+    inp = layer_inputs(3, 20, cfg=107)
+    perm = [1, 3, 0, 2]
+    comb = np.zeros((3, HC, HC))
+    for o, n in enumerate(perm):
+        comb[:, o, n] = 1.0
+    out = oracle.post(inp.x, inp.res, np.zeros((3, HC)), comb)
+    r = _bf16_f64(inp.res)
+    for o, n in enumerate(perm):
+        assert np.array_equal(out[:, n], r[:, o])
+
+
+def test_post_matches_einsum():
+    inp = layer_inputs(4, 24, cfg=108)
+    g = np.random.default_rng(9)
+    post = g.uniform(0, 2, (4, HC))
+    comb = g.uniform(0, 1, (4, HC, HC))
+    out = oracle.post(inp.x, inp.res, post, comb)
+    ref = _bf16_f64(inp.x)[:, None, :] * post[:, :, None] + np.einsum("toh,ton->tnh", _bf16_f64(inp.res), comb)
+    assert np.allclose(out, ref, rtol=1e-14, atol=1e-14)
+
+
+# ---------------------------------------------------------------- whole pre-map
+
+def _pre_numpy(inp, rms_eps=1e-6, pre_eps=1e-6, sk_eps=1e-6, post_mult=1.0, iters=20):
+    """Composition of library routines and closed forms, independent of the oracle's loops."""
+    r = _bf16_f64(inp.res)
+    T, _, H = r.shape
+    flat = r.reshape(T, HC * H)
+    rstd = 1.0 / np.sqrt((flat * flat).sum(axis=1) / (HC * H) + rms_eps)
+    m = (flat @ inp.hc_fn.astype(np.float64).T) * rstd[:, None]
+    s = inp.hc_scale.astype(np.float64)
+    b = inp.hc_base.astype(np.float64)
+    pre = _sig(m[:, 0:4] * s[0] + b[0:4]) + pre_eps
+    post = _sig(m[:, 4:8] * s[1] + b[4:8]) * post_mult
+    comb = _sk_scaling((m[:, 8:24] * s[2] + b[8:24]).reshape(T, 4, 4), iters, sk_eps)
+    y = np.einsum("ti,tih->th", pre, r)
+    return y, post, comb, pre
+
+
+@pytest.mark.parametrize("post_mult", [1.0, 2.0])
+def test_pre_matches_independent_composition(post_mult):
+    inp = layer_inputs(16, 256, cfg=1)
+    o = oracle.pre(inp.res, inp.hc_fn, inp.hc_scale, inp.hc_base, post_mult=post_mult)
+    y, post, comb, pre = _pre_numpy(inp, post_mult=post_mult)
+    assert np.allclose(o["pre"], pre, atol=1e-13)
+    assert np.allclose(o["post"], post, atol=1e-13)
+    assert np.allclose(o["comb"], comb, atol=1e-12)
+    assert np.allclose(o["y"], y, atol=1e-12)
+
+
+def test_pre_hc_permutation_equivariance():
+    """Permuting streams, hc_fn column blocks, pre/post rows and comb indices alike
+    leaves y unchanged, permutes post and conjugates comb."""
+    T, H = 6, 40
+    inp = layer_inputs(T, H, cfg=109)
+    perm = np.array([3, 0, 2, 1])
+    res_p = inp.res[:, perm, :]
+    fn = inp.hc_fn.reshape(MIX, HC, H)[:, perm, :]
+    rows = np.concatenate([perm, 4 + perm, [8 + 4 * perm[i] + perm[j] for i in range(4) for j in range(4)]])
+    fn_p = fn[rows].reshape(MIX, HC * H)
+    base_p = inp.hc_base[rows]
+    a = oracle.pre(inp.res, inp.hc_fn, inp.hc_scale, inp.hc_base)
+    b = oracle.pre(res_p, fn_p, inp.hc_scale, base_p)
+    assert np.allclose(b["y"], a["y"], atol=1e-13)
+    assert np.allclose(b["post"], a["post"][:, perm], atol=1e-15)
+    assert np.allclose(b["pre"], a["pre"][:, perm], atol=1e-15)
+    assert np.allclose(b["comb"], a["comb"][:, perm][:, :, perm], atol=1e-13)
+
+
+def test_pre_zero_scale_collapse_selects_stream():
+    T, H = 3, 30
+    inp = layer_inputs(T, H, cfg=110, scale=(0.0, 0.0, 0.0))
+    inp.hc_base[:4] = [30.0, -30.0, -30.0, -30.0]
+    o = oracle.pre(inp.res, inp.hc_fn, inp.hc_scale, inp.hc_base)
+    r = _bf16_f64(inp.res)
+    assert np.allclose(o["y"], r[:, 0, :], atol=1e-5)
+    assert np.allclose(o["pre"][:, 0], 1.0 + 1e-6, atol=1e-12)
+
+
+def test_sinkhorn_subtracts_row_max_before_exp():
+    # The FlashInfer mHC article (section 3.4) subtracts the row maximum before the
+    # softmax; with logits near 1000 the un-shifted exp overflows to inf/nan.
+    L = np.array([[[1000.0, 999.0, 0.0, 0.0], [0.0, 1000.0, 998.0, 0.0],
+                   [0.0, 0.0, 1000.0, 0.0], [997.0, 0.0, 0.0, 1000.0]]])
+    out = oracle.sinkhorn(L, 20, 1e-6)
+    assert np.all(np.isfinite(out))
+    assert np.allclose(out, _sk_scaling(L, 20, 1e-6), atol=1e-13)
