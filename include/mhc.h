@@ -1,0 +1,137 @@
+/*
+ * mhc.h -- C ABI of libmhc, the MI355X (gfx950) manifold-constrained
+ * hyper-connection (mHC) residual-mixing library.
+ *
+ * HC (the number of residual streams) is fixed at 4, and every token carries
+ * 24 mixing logits laid out as pre[0:4], post[4:8], comb[8:24] (a 4x4 matrix,
+ * row-major) -- "FlashInfer mHC 模块深度解析" (FlashInfer mHC article),
+ * section 1.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - bf16 tensors are passed as uint16_t bit patterns; fp32 tensors as float.
+ *    Streams and activations are bf16, mixing coefficients fp32 (FlashInfer
+ *    mHC article, sections 2.2 and 3.1).
+ *  - Every tensor pointer is a DEVICE pointer to dense row-major memory:
+ *        res   [T, 4, H]  bf16   residual streams
+ *        x     [T, H]     bf16   sublayer output (post-map input)
+ *        y     [T, H]     bf16   layer input (pre-map output)
+ *        out   [T, 4, H]  bf16   new residual streams (post-map output)
+ *        post  [T, 4]     fp32   (the same memory as [T, 4, 1])
+ *        comb  [T, 4, 4]  fp32   comb[t][o][n] weights old stream o into new stream n
+ *        pre   [T, 4]     fp32
+ *        hc_fn [24, 4H]   fp32   projection; column k = i*H + h (stream i, element h)
+ *        hc_scale [3]     fp32   logit scales of pre, post, comb, in that order
+ *        hc_base  [24]    fp32   logit biases
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Work is enqueued asynchronously on it; no call synchronises the host.
+ *  - Ownership: the caller owns every buffer.  The library never allocates,
+ *    frees or retains device memory; outputs are written in place.
+ *  - Errors: arguments are validated on the host before anything is enqueued.
+ *    On any error nothing is launched and no output is touched.  T == 0 is a
+ *    successful no-op.  MHC_ERROR_LAUNCH reports a failed enqueue
+ *    (hipGetLastError after the launch).
+ *  - Results are deterministic: no floating-point atomics; for fixed shapes
+ *    repeated calls give bit-identical outputs.
+ *  - Any H >= 1 is accepted.  Rows whose byte size is not a multiple of 16,
+ *    or base pointers that are not 16-byte aligned, take a scalar path.
+ */
+#ifndef MHC_H_
+#define MHC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MHC_ABI_VERSION 1
+#define MHC_HC 4
+#define MHC_MIX 24
+
+typedef enum mhc_status {
+    MHC_SUCCESS = 0,
+    MHC_ERROR_INVALID_VALUE = 1, /* null required pointer, bad size or parameter, forbidden overlap */
+    MHC_ERROR_WORKSPACE = 2,     /* workspace missing or smaller than mhc_pre_fused_workspace_bytes() */
+    MHC_ERROR_LAUNCH = 3         /* the HIP runtime rejected a kernel launch */
+} mhc_status;
+
+/* Returns MHC_ABI_VERSION. */
+int mhc_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char *mhc_status_string(mhc_status status);
+
+/*
+ * mhc_sinkhorn -- fixed-iteration Sinkhorn-Knopp projection of 4x4 logit
+ * matrices (FlashInfer mHC article, section 5.2, the Sinkhorn reference;
+ * rwkv-ops mhu_jax.py, sinkhorn_knopp):
+ *     P = softmax(L over each row, row maximum subtracted) + eps
+ *     repeat num_iters times: divide every row by its sum, then every column by its sum
+ *
+ *   logits   [n_mats, 4, 4] fp32, device
+ *   out      [n_mats, 4, 4] fp32, device; may equal `logits` exactly (in place),
+ *            must not overlap it otherwise
+ *   n_mats   >= 0
+ *   num_iters >= 1 (the count of (row, column) rounds; no early exit)
+ *   eps      finite and > 0
+ */
+mhc_status mhc_sinkhorn(const float *logits, float *out, int64_t n_mats, int32_t num_iters, float eps,
+                        void *stream);
+
+/*
+ * Size in bytes of the device workspace mhc_pre_fused needs for (T, H)
+ * (split-K partial sums of the projection and the per-token pre weights).
+ * Returns 0 for T <= 0 or H <= 0.
+ */
+size_t mhc_pre_fused_workspace_bytes(int64_t T, int64_t H);
+
+/*
+ * mhc_pre_fused -- the mHC pre-map (FlashInfer mHC article, sections 3.4 and
+ * 5.2; metrale hyper_connection_dispatch.rs, hc_pre_site argument list):
+ *     S_t      = sum_{i,h} res[t][i][h]^2,     rstd_t = 1 / sqrt(S_t / (4H) + rms_eps)
+ *     m_t[r]   = rstd_t * sum_k hc_fn[r][k] * res_flat[t][k]          (k = i*H + h)
+ *     pre[t][i]  = sigmoid(m_t[i]   * hc_scale[0] + hc_base[i]) + pre_eps
+ *     post[t][i] = sigmoid(m_t[4+i] * hc_scale[1] + hc_base[4+i]) * post_mult
+ *     comb[t]    = Sinkhorn(L), L[i][j] = m_t[8+4i+j] * hc_scale[2] + hc_base[8+4i+j]
+ *     y[t][h]    = bf16( sum_i pre[t][i] * res[t][i][h] )   (fp32 accumulation, nearest-even)
+ *
+ *   res, hc_fn, hc_scale, hc_base   inputs (layouts above), device
+ *   T >= 0, H >= 1
+ *   rms_eps, pre_eps, sinkhorn_eps  finite; rms_eps and sinkhorn_eps > 0, pre_eps >= 0
+ *   post_mult                       finite
+ *   num_iters                       >= 1
+ *   y [T,H], post [T,4], comb [T,4,4]   outputs, device; y must not overlap res
+ *   pre [T,4]                       optional output (may be NULL)
+ *   workspace                       device scratch of at least
+ *                                   mhc_pre_fused_workspace_bytes(T, H) bytes, 256-byte aligned;
+ *                                   may be NULL only when that size is 0.  Its contents on entry
+ *                                   are ignored; calls sharing one workspace must be ordered on
+ *                                   one stream.
+ */
+mhc_status mhc_pre_fused(const uint16_t *res, const float *hc_fn, const float *hc_scale, const float *hc_base,
+                         int64_t T, int64_t H, float rms_eps, float pre_eps, float sinkhorn_eps, float post_mult,
+                         int32_t num_iters, uint16_t *y, float *post, float *comb, float *pre, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
+/*
+ * mhc_post -- the mHC post-map (FlashInfer mHC article, section 2.1; metrale
+ * glm5next_mhc.rs, glm_hc_post):
+ *     out[t][n][h] = bf16( x[t][h] * post[t][n] + sum_o res[t][o][h] * comb[t][o][n] )
+ *   (fp32 accumulation, round to nearest-even)
+ *
+ *   x [T,H], res [T,4,H], post [T,4], comb [T,4,4]   inputs, device
+ *   T >= 0, H >= 1
+ *   out [T,4,H]   output, device; may equal `res` exactly (in-place update: every
+ *                 element reads all four old streams before it is written), must
+ *                 not overlap res otherwise, nor x, post or comb.
+ */
+mhc_status mhc_post(const uint16_t *x, const uint16_t *res, const float *post, const float *comb, int64_t T,
+                    int64_t H, uint16_t *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MHC_H_ */

@@ -1,0 +1,207 @@
+"""Python binding over libmhc, the MI355X (gfx950) mHC residual-mixing library.
+
+The functions below carry the names of the C entry points declared in
+``include/mhc.h`` and only marshal arguments: shape/dtype checks, output and
+workspace allocation through PyTorch, device pointers and the current HIP
+stream.  Every step of the computation runs in the library's HIP kernels; if
+``libmhc.so`` is missing or cannot be loaded, every call raises.
+
+Shapes follow the FlashInfer mHC API ("FlashInfer mHC 模块深度解析", sections
+2.2 and 3.1): leading token dimensions are flattened, HC is fixed at 4,
+streams/activations are bf16 and mixing coefficients fp32.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+import torch
+
+HC = 4
+MIX = 24
+LIB_PATH = Path(__file__).resolve().parent / "libmhc.so"
+
+MHC_SUCCESS = 0
+MHC_ERROR_INVALID_VALUE = 1
+MHC_ERROR_WORKSPACE = 2
+MHC_ERROR_LAUNCH = 3
+
+_lib = None
+
+
+class MHCError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: status {status} ({status_string(status)})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmhc.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not LIB_PATH.exists():
+        raise ImportError(f"{LIB_PATH} is missing; build it with `python -m mhc_hyper_connection_amd.build`")
+    L = ctypes.CDLL(str(LIB_PATH))
+    P, I64, I32, F, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    L.mhc_abi_version.argtypes = []
+    L.mhc_abi_version.restype = ctypes.c_int
+    L.mhc_status_string.argtypes = [ctypes.c_int]
+    L.mhc_status_string.restype = ctypes.c_char_p
+    L.mhc_sinkhorn.argtypes = [P, P, I64, I32, F, P]
+    L.mhc_sinkhorn.restype = ctypes.c_int
+    L.mhc_pre_fused_workspace_bytes.argtypes = [I64, I64]
+    L.mhc_pre_fused_workspace_bytes.restype = SZ
+    L.mhc_pre_fused.argtypes = [P, P, P, P, I64, I64, F, F, F, F, I32, P, P, P, P, P, SZ, P]
+    L.mhc_pre_fused.restype = ctypes.c_int
+    L.mhc_post.argtypes = [P, P, P, P, I64, I64, P, P]
+    L.mhc_post.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().mhc_status_string(int(status)).decode()
+
+
+def abi_version() -> int:
+    return lib().mhc_abi_version()
+
+
+def _check(fn: str, status: int):
+    if status != MHC_SUCCESS:
+        raise MHCError(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype):
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _same_device(*ts):
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) > 1:
+        raise ValueError(f"all tensors must be on one device, got {sorted(map(str, devs))}")
+
+
+def mhc_sinkhorn(logits: torch.Tensor, out: torch.Tensor | None = None, num_iters: int = 20,
+                 eps: float = 1e-6) -> torch.Tensor:
+    """Fixed-count Sinkhorn-Knopp projection of [..., 4, 4] fp32 logits (``out`` may be ``logits``)."""
+    _need(logits, "logits", torch.float32)
+    if logits.dim() < 2 or tuple(logits.shape[-2:]) != (HC, HC):
+        raise ValueError(f"logits must be [..., 4, 4], got {tuple(logits.shape)}")
+    if out is None:
+        out = torch.empty_like(logits)
+    _need(out, "out", torch.float32)
+    if out.shape != logits.shape:
+        raise ValueError("out must have the shape of logits")
+    _same_device(logits, out)
+    n = logits.numel() // (HC * HC)
+    _check("mhc_sinkhorn", lib().mhc_sinkhorn(_ptr(logits), _ptr(out), n, int(num_iters), float(eps),
+                                              _stream(logits.device)))
+    return out
+
+
+def mhc_pre_fused_workspace_bytes(T: int, H: int) -> int:
+    return int(lib().mhc_pre_fused_workspace_bytes(int(T), int(H)))
+
+
+def mhc_pre_fused(res: torch.Tensor, hc_fn: torch.Tensor, hc_scale: torch.Tensor, hc_base: torch.Tensor,
+                  rms_eps: float = 1e-6, pre_eps: float = 1e-6, sinkhorn_eps: float = 1e-6,
+                  post_mult: float = 1.0, num_iters: int = 20, *, y=None, post=None, comb=None, pre=None,
+                  return_pre: bool = False, workspace: torch.Tensor | None = None):
+    """The pre-map.  res [..., 4, H] bf16 -> (y [..., H] bf16, post [..., 4] fp32, comb [..., 4, 4] fp32
+    [, pre [..., 4] fp32]).  Outputs may be passed in (contiguous, right shape) to be written in place."""
+    _need(res, "res", torch.bfloat16)
+    if res.dim() < 2 or res.shape[-2] != HC:
+        raise ValueError(f"res must be [..., 4, H], got {tuple(res.shape)}")
+    H = res.shape[-1]
+    outer = tuple(res.shape[:-2])
+    T = res.numel() // (HC * H) if H > 0 else 0
+    _need(hc_fn, "hc_fn", torch.float32)
+    if tuple(hc_fn.shape) != (MIX, HC * H):
+        raise ValueError(f"hc_fn must be [24, 4H] = [24, {HC * H}], got {tuple(hc_fn.shape)}")
+    _need(hc_scale, "hc_scale", torch.float32)
+    if tuple(hc_scale.shape) != (3,):
+        raise ValueError("hc_scale must be [3] (pre, post, comb)")
+    _need(hc_base, "hc_base", torch.float32)
+    if tuple(hc_base.shape) != (MIX,):
+        raise ValueError("hc_base must be [24]")
+    dev = res.device
+    if y is None:
+        y = torch.empty(outer + (H,), dtype=torch.bfloat16, device=dev)
+    if post is None:
+        post = torch.empty(outer + (HC,), dtype=torch.float32, device=dev)
+    if comb is None:
+        comb = torch.empty(outer + (HC, HC), dtype=torch.float32, device=dev)
+    if pre is None and return_pre:
+        pre = torch.empty(outer + (HC,), dtype=torch.float32, device=dev)
+    _need(y, "y", torch.bfloat16)
+    _need(post, "post", torch.float32)
+    _need(comb, "comb", torch.float32)
+    if y.numel() != T * H or post.numel() != T * HC or comb.numel() != T * HC * HC:
+        raise ValueError("output sizes do not match res")
+    if pre is not None:
+        _need(pre, "pre", torch.float32)
+        if pre.numel() != T * HC:
+            raise ValueError("pre must hold [T, 4] values")
+    _same_device(res, hc_fn, hc_scale, hc_base, y, post, comb, pre)
+    need = mhc_pre_fused_workspace_bytes(T, H)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8)
+    _check("mhc_pre_fused", lib().mhc_pre_fused(
+        _ptr(res), _ptr(hc_fn), _ptr(hc_scale), _ptr(hc_base), T, H, float(rms_eps), float(pre_eps),
+        float(sinkhorn_eps), float(post_mult), int(num_iters), _ptr(y), _ptr(post), _ptr(comb), _ptr(pre),
+        _ptr(workspace), workspace.numel(), _stream(dev)))
+    if return_pre:
+        return y, post, comb, pre
+    return y, post, comb
+
+
+def mhc_post(x: torch.Tensor, res: torch.Tensor, post: torch.Tensor, comb: torch.Tensor,
+             out: torch.Tensor | None = None) -> torch.Tensor:
+    """The post-map.  x [..., H] bf16, res [..., 4, H] bf16, post [..., 4] or [..., 4, 1] fp32,
+    comb [..., 4, 4] fp32 -> out [..., 4, H] bf16 (``out`` may be ``res`` for an in-place update)."""
+    _need(res, "res", torch.bfloat16)
+    if res.dim() < 2 or res.shape[-2] != HC:
+        raise ValueError(f"residual.shape[-2] / HC must be 4, got {tuple(res.shape)}")
+    H = res.shape[-1]
+    outer = tuple(res.shape[:-2])
+    T = res.numel() // (HC * H) if H > 0 else 0
+    _need(x, "x", torch.bfloat16)
+    if tuple(x.shape) != outer + (H,):
+        raise ValueError(f"x must be {outer + (H,)}, got {tuple(x.shape)}")
+    _need(post, "post", torch.float32)
+    if tuple(post.shape) not in (outer + (HC,), outer + (HC, 1)):
+        raise ValueError(f"post must be {outer + (HC,)} or {outer + (HC, 1)}, got {tuple(post.shape)}")
+    _need(comb, "comb", torch.float32)
+    if tuple(comb.shape) != outer + (HC, HC):
+        raise ValueError(f"comb must be {outer + (HC, HC)}, got {tuple(comb.shape)}")
+    if out is None:
+        out = torch.empty_like(res)
+    _need(out, "out", torch.bfloat16)
+    if out.shape != res.shape:
+        raise ValueError("out must have the shape of res")
+    _same_device(x, res, post, comb, out)
+    _check("mhc_post", lib().mhc_post(_ptr(x), _ptr(res), _ptr(post), _ptr(comb), T, H, _ptr(out),
+                                      _stream(res.device)))
+    return out
+
+
+__all__ = ["mhc_sinkhorn", "mhc_pre_fused", "mhc_pre_fused_workspace_bytes", "mhc_post", "lib", "abi_version",
+           "status_string", "MHCError", "HC", "MIX"]

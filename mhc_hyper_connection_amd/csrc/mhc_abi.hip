@@ -1,0 +1,158 @@
+// mhc_abi.hip -- the extern "C" entry points of libmhc: argument validation on
+// the host, then kernel launches on the caller's stream.  No entry point
+// allocates, frees or synchronises.
+#include "../../include/mhc.h"
+#include "mhc_internal.h"
+
+#include <math.h>
+
+namespace {
+
+using mhc::PreGeom;
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Do [a, a + an) and [b, b + bn) share a byte?
+bool overlaps(const void *a, size_t an, const void *b, size_t bn)
+{
+    if (!a || !b || an == 0 || bn == 0) {
+        return false;
+    }
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + bn && b0 < a0 + an;
+}
+
+bool finite(float v) { return isfinite(v) != 0; }
+
+// Every size the kernels index stays below 2^31 wavefronts / elements per row.
+bool sizes_ok(int64_t T, int64_t H)
+{
+    if (T < 0 || H < 1 || H > kMaxDim || T > kMaxDim) {
+        return false;
+    }
+    const int64_t waves = T * ((H + 63) / 64);
+    return waves < ((int64_t)1 << 31) / 4;
+}
+
+mhc_status launch_status(hipError_t e) { return e == hipSuccess ? MHC_SUCCESS : MHC_ERROR_LAUNCH; }
+
+} // namespace
+
+extern "C" {
+
+int mhc_abi_version(void) { return MHC_ABI_VERSION; }
+
+const char *mhc_status_string(mhc_status status)
+{
+    switch (status) {
+    case MHC_SUCCESS:
+        return "success";
+    case MHC_ERROR_INVALID_VALUE:
+        return "invalid argument";
+    case MHC_ERROR_WORKSPACE:
+        return "workspace missing or too small";
+    case MHC_ERROR_LAUNCH:
+        return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+mhc_status mhc_sinkhorn(const float *logits, float *out, int64_t n_mats, int32_t num_iters, float eps, void *stream)
+{
+    if (n_mats < 0 || n_mats > ((int64_t)1 << 40) || num_iters < 1 || !finite(eps) || !(eps > 0.0f)) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    if (n_mats == 0) {
+        return MHC_SUCCESS;
+    }
+    if (!logits || !out) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    const size_t bytes = (size_t)n_mats * 16 * sizeof(float);
+    if ((const void *)out != (const void *)logits && overlaps(out, bytes, logits, bytes)) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    const bool vec4 = aligned16(logits) && aligned16(out);
+    return launch_status(mhc::launch_sinkhorn(logits, out, n_mats, num_iters, eps, (hipStream_t)stream, vec4));
+}
+
+size_t mhc_pre_fused_workspace_bytes(int64_t T, int64_t H)
+{
+    if (T <= 0 || H <= 0 || !sizes_ok(T, H)) {
+        return 0;
+    }
+    return mhc::pre_geometry(T, H).total_bytes;
+}
+
+mhc_status mhc_pre_fused(const uint16_t *res, const float *hc_fn, const float *hc_scale, const float *hc_base,
+                         int64_t T, int64_t H, float rms_eps, float pre_eps, float sinkhorn_eps, float post_mult,
+                         int32_t num_iters, uint16_t *y, float *post, float *comb, float *pre, void *workspace,
+                         size_t workspace_bytes, void *stream)
+{
+    if (!sizes_ok(T, H) || num_iters < 1 || !finite(rms_eps) || !(rms_eps > 0.0f) || !finite(pre_eps) ||
+        pre_eps < 0.0f || !finite(sinkhorn_eps) || !(sinkhorn_eps > 0.0f) || !finite(post_mult)) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    if (T == 0) {
+        return MHC_SUCCESS;
+    }
+    if (!res || !hc_fn || !hc_scale || !hc_base || !y || !post || !comb) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    const PreGeom g = mhc::pre_geometry(T, H);
+    if (!workspace || workspace_bytes < g.total_bytes || ((uintptr_t)workspace & 255u) != 0) {
+        return MHC_ERROR_WORKSPACE;
+    }
+    const size_t res_b = (size_t)T * 4 * H * 2, y_b = (size_t)T * H * 2;
+    const size_t post_b = (size_t)T * 4 * 4, comb_b = (size_t)T * 16 * 4, pre_b = pre ? (size_t)T * 4 * 4 : 0;
+    const size_t fn_b = (size_t)24 * 4 * H * 4;
+    // Outputs must not overlap inputs, each other, or the workspace.
+    const void *outs[5] = {y, post, comb, pre, workspace};
+    const size_t outn[5] = {y_b, post_b, comb_b, pre_b, g.total_bytes};
+    const void *ins[4] = {res, hc_fn, hc_scale, hc_base};
+    const size_t inn[4] = {res_b, fn_b, 3 * 4, 24 * 4};
+    for (int a = 0; a < 5; ++a) {
+        for (int b = 0; b < 4; ++b) {
+            if (overlaps(outs[a], outn[a], ins[b], inn[b])) {
+                return MHC_ERROR_INVALID_VALUE;
+            }
+        }
+        for (int b = a + 1; b < 5; ++b) {
+            if (overlaps(outs[a], outn[a], outs[b], outn[b])) {
+                return MHC_ERROR_INVALID_VALUE;
+            }
+        }
+    }
+    const bool vec8 = (H % 8 == 0) && aligned16(res) && aligned16(hc_fn) && aligned16(y);
+    return launch_status(mhc::launch_pre(res, hc_fn, hc_scale, hc_base, g, rms_eps, pre_eps, sinkhorn_eps,
+                                         post_mult, num_iters, y, post, comb, pre, workspace, (hipStream_t)stream,
+                                         vec8));
+}
+
+mhc_status mhc_post(const uint16_t *x, const uint16_t *res, const float *post, const float *comb, int64_t T,
+                    int64_t H, uint16_t *out, void *stream)
+{
+    if (!sizes_ok(T, H)) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    if (T == 0) {
+        return MHC_SUCCESS;
+    }
+    if (!x || !res || !post || !comb || !out) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    const size_t res_b = (size_t)T * 4 * H * 2, x_b = (size_t)T * H * 2;
+    const size_t post_b = (size_t)T * 4 * 4, comb_b = (size_t)T * 16 * 4;
+    if ((const void *)out != (const void *)res && overlaps(out, res_b, res, res_b)) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    if (overlaps(out, res_b, x, x_b) || overlaps(out, res_b, post, post_b) || overlaps(out, res_b, comb, comb_b)) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    const bool vec8 = (H % 8 == 0) && aligned16(x) && aligned16(res) && aligned16(out);
+    return launch_status(mhc::launch_post(x, res, post, comb, T, H, out, (hipStream_t)stream, vec8));
+}
+
+} // extern "C"

@@ -1,0 +1,117 @@
+"""Host-side checks of libmhc's C ABI (no GPU needed, no kernel is launched).
+
+Every call here fails validation, or is a T == 0 no-op, before any HIP call,
+so fake non-null pointers are never dereferenced.
+"""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+import mhc_hyper_connection_amd as mhc
+
+HEADER = Path(__file__).resolve().parents[1] / "include" / "mhc.h"
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: validation rejects before use
+FAKE2 = ctypes.c_void_p(0x20000000)
+NULL = None
+
+
+def _declared():
+    text = HEADER.read_text()
+    return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(mhc_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = mhc.lib()
+    names = _declared()
+    assert {"mhc_sinkhorn", "mhc_pre_fused", "mhc_pre_fused_workspace_bytes", "mhc_post",
+            "mhc_abi_version", "mhc_status_string"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_status_strings():
+    ver = int(re.search(r"#define MHC_ABI_VERSION (\d+)", HEADER.read_text()).group(1))
+    assert mhc.abi_version() == ver
+    assert mhc.status_string(0) == "success"
+    for s in (1, 2, 3):
+        assert mhc.status_string(s) not in ("success", "unknown status")
+    assert mhc.status_string(99) == "unknown status"
+
+
+def test_workspace_bytes():
+    assert mhc.mhc_pre_fused_workspace_bytes(0, 7168) == 0
+    assert mhc.mhc_pre_fused_workspace_bytes(16, 0) == 0
+    a = mhc.mhc_pre_fused_workspace_bytes(16, 256)
+    b = mhc.mhc_pre_fused_workspace_bytes(8192, 7168)
+    assert a > 0 and b > a and b % 256 == 0
+    # the per-token partial records stay a small fraction of the streams
+    assert b < 0.1 * 8192 * 4 * 7168 * 2
+
+
+def test_sinkhorn_validation():
+    lib = mhc.lib()
+    assert lib.mhc_sinkhorn(FAKE, FAKE2, -1, 20, 1e-6, NULL) == mhc.MHC_ERROR_INVALID_VALUE
+    assert lib.mhc_sinkhorn(FAKE, FAKE2, 10, 0, 1e-6, NULL) == mhc.MHC_ERROR_INVALID_VALUE
+    assert lib.mhc_sinkhorn(FAKE, FAKE2, 10, 20, 0.0, NULL) == mhc.MHC_ERROR_INVALID_VALUE
+    assert lib.mhc_sinkhorn(FAKE, FAKE2, 10, 20, float("nan"), NULL) == mhc.MHC_ERROR_INVALID_VALUE
+    assert lib.mhc_sinkhorn(NULL, FAKE2, 10, 20, 1e-6, NULL) == mhc.MHC_ERROR_INVALID_VALUE
+    # partial overlap of out and logits
+    assert lib.mhc_sinkhorn(FAKE, ctypes.c_void_p(0x10000 + 64), 10, 20, 1e-6, NULL) == mhc.MHC_ERROR_INVALID_VALUE
+    assert lib.mhc_sinkhorn(NULL, NULL, 0, 20, 1e-6, NULL) == mhc.MHC_SUCCESS  # empty: no-op
+
+
+def _pre(lib, **kw):
+    a = dict(res=FAKE, fn=ctypes.c_void_p(0x4000000), sc=ctypes.c_void_p(0x8000000), base=ctypes.c_void_p(0x8001000),
+             T=16, H=256, rms=1e-6, pe=1e-6, se=1e-6, pm=1.0, it=20, y=ctypes.c_void_p(0x9000000),
+             post=ctypes.c_void_p(0xA000000), comb=ctypes.c_void_p(0xB000000), pre=None,
+             ws=ctypes.c_void_p(0xC000000), wsb=1 << 30)
+    a.update(kw)
+    return lib.mhc_pre_fused(a["res"], a["fn"], a["sc"], a["base"], a["T"], a["H"], a["rms"], a["pe"], a["se"],
+                             a["pm"], a["it"], a["y"], a["post"], a["comb"], a["pre"], a["ws"], a["wsb"], NULL)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(T=-1), dict(H=0), dict(it=0), dict(rms=0.0), dict(se=-1e-6), dict(pe=-1.0),
+    dict(rms=float("inf")), dict(pm=float("nan")), dict(res=None), dict(fn=None), dict(sc=None),
+    dict(base=None), dict(y=None), dict(post=None), dict(comb=None),
+    dict(y=ctypes.c_void_p(0x10000 + 100)),           # y overlaps res
+    dict(comb=ctypes.c_void_p(0xA000000 + 32)),        # comb overlaps post
+    dict(pre=ctypes.c_void_p(0xB000000)),              # pre overlaps comb
+])
+def test_pre_validation_invalid(kw):
+    assert _pre(mhc.lib(), **kw) == mhc.MHC_ERROR_INVALID_VALUE
+
+
+def test_pre_validation_workspace():
+    lib = mhc.lib()
+    need = mhc.mhc_pre_fused_workspace_bytes(16, 256)
+    assert _pre(lib, wsb=need - 1) == mhc.MHC_ERROR_WORKSPACE
+    assert _pre(lib, ws=None) == mhc.MHC_ERROR_WORKSPACE
+    assert _pre(lib, ws=ctypes.c_void_p(0xC000000 + 8)) == mhc.MHC_ERROR_WORKSPACE  # not 256-byte aligned
+    assert _pre(lib, T=0, res=None, y=None, ws=None) == mhc.MHC_SUCCESS  # empty: no-op
+
+
+def test_post_validation():
+    lib = mhc.lib()
+    x, res, post, comb, out = (ctypes.c_void_p(v) for v in (0x100000, 0x200000, 0x300000, 0x310000, 0x400000))
+    call = lambda **k: lib.mhc_post(k.get("x", x), k.get("res", res), k.get("post", post), k.get("comb", comb),
+                                    k.get("T", 8), k.get("H", 64), k.get("out", out), NULL)
+    E = mhc.MHC_ERROR_INVALID_VALUE
+    assert call(T=-1) == E
+    assert call(H=0) == E
+    for name in ("x", "res", "post", "comb", "out"):
+        assert call(**{name: None}) == E
+    assert call(out=ctypes.c_void_p(0x200000 + 2)) == E  # partial overlap with res
+    assert call(out=ctypes.c_void_p(0x100000 - 64)) == E  # overlaps x
+    assert call(T=0, x=None, res=None, post=None, comb=None, out=None) == mhc.MHC_SUCCESS
+
+
+def test_binding_rejects_cpu_tensors_before_the_library():
+    import torch
+    with pytest.raises(ValueError):
+        mhc.mhc_post(torch.zeros(2, 8, dtype=torch.bfloat16), torch.zeros(2, 4, 8, dtype=torch.bfloat16),
+                     torch.zeros(2, 4), torch.zeros(2, 4, 4))
+    with pytest.raises(ValueError):
+        mhc.mhc_sinkhorn(torch.zeros(3, 4, 4))
