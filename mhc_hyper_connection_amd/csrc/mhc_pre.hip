@@ -4,7 +4,9 @@
 // hyper_connection_dispatch.rs, hc_pre_site; metrale glm5next_mhc.rs, the
 // hc_mix / hc_finish split.)
 //
-// Three kernels on one stream:
+// This file holds the split-K fallback used for H beyond the fused kernel's
+// range (mhc_pre_fused.hip holds the read-once path).  Three kernels on one
+// stream:
 //
 //  1. pre_proj_kernel -- the 24 x 4H projection and the sum of squares, on MFMA.
 //     A workgroup owns 64 tokens x one contiguous range of H (all four streams),
@@ -35,6 +37,9 @@ constexpr int kHBlock = 32;     // h per MFMA step per stream: 4 lane groups x 8
 constexpr int kPartStride = 32; // floats per (slice, token) partial: 24 dots, sum of squares, padding
 constexpr int kSqSlot = kMix;   // index of the sum of squares inside a partial record
 constexpr int kTargetBlocks = 2048;
+// The read-once cooperative kernel is correct but its cross-workgroup exchange
+// is still latency-bound; the split-K path is faster until that is fixed.
+constexpr bool kUseFusedPre = false;
 
 constexpr int kColBlock = 256;
 constexpr int kColWaves = kColBlock / kWave;
@@ -360,7 +365,9 @@ PreGeom pre_geometry(int64_t T, int64_t H)
     g.slices = (g.nhb + g.hb_per_slice - 1) / g.hb_per_slice;
     g.part_bytes = (size_t)g.slices * (size_t)T * kPartStride * sizeof(float);
     g.prew_bytes = (size_t)T * kHC * sizeof(float);
-    g.total_bytes = align256(g.part_bytes) + align256(g.prew_bytes);
+    g.split_bytes = align256(g.part_bytes) + align256(g.prew_bytes);
+    g.fused = kUseFusedPre ? fused_geometry(T, H) : FusedGeom{};
+    g.total_bytes = g.fused.valid && g.fused.bytes > g.split_bytes ? g.fused.bytes : g.split_bytes;
     return g;
 }
 
@@ -369,6 +376,15 @@ hipError_t launch_pre(const uint16_t *res, const float *hc_fn, const float *hc_s
                       int iters, uint16_t *y, float *post, float *comb, float *pre, void *workspace,
                       hipStream_t stream, bool vec8)
 {
+    if (g.fused.valid) {
+        bool fits = false;
+        const hipError_t e = launch_pre_fused(res, hc_fn, hc_scale, hc_base, g.fused, g.T, g.H, rms_eps, pre_eps,
+                                              sinkhorn_eps, post_mult, iters, y, post, comb, pre, workspace, stream,
+                                              vec8, &fits);
+        if (e != hipSuccess || fits) {
+            return e;
+        }
+    }
     float *part = reinterpret_cast<float *>(workspace);
     float *pre_ws = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + align256(g.part_bytes));
     const int T = (int)g.T, H = (int)g.H;

@@ -202,8 +202,10 @@ def _check_pre(inp, got, tokens=None, what=""):
     return ref
 
 
+# (T, H): tile edges (T = 1, 63..65, 129), ragged H (H % 32 != 0, H % 8 != 0), one slice
+# (H <= 128), many slices, and H above the fused kernel's range (split-K fallback path).
 PRE_SHAPES = [(16, 256), (1, 64), (3, 8), (100, 512), (65, 7168), (32, 7168), (40, 127), (24, 1001),
-              (129, 1536), (7, 16392), (70, 96)]
+              (129, 1536), (7, 16392), (70, 96), (63, 200), (130, 4104), (3, 65544), (2, 65537)]
 
 
 @pytest.mark.parametrize("T,H", PRE_SHAPES)
