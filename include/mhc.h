@@ -81,9 +81,13 @@ mhc_status mhc_sinkhorn(const float *logits, float *out, int64_t n_mats, int32_t
                         void *stream);
 
 /*
- * Size in bytes of the device workspace mhc_pre_fused needs for (T, H)
- * (split-K partial sums of the projection and the per-token pre weights).
- * Returns 0 for T <= 0 or H <= 0.
+ * Size in bytes of the device workspace mhc_pre_fused needs for (T, H): the
+ * projection weights split into bf16 terms in MFMA operand order (384 * H
+ * bytes, rounded up), the per-slice partial sums of the projection (100 bytes
+ * per token per 128-wide slice of H) and the per-token totals (128 bytes per
+ * token).  Tokens beyond 2^31 bytes of partial sums are processed in chunks
+ * that reuse the same space.  Returns 0 for T <= 0, H <= 0 or H beyond the
+ * pre-map limit.
  */
 size_t mhc_pre_fused_workspace_bytes(int64_t T, int64_t H);
 
@@ -98,7 +102,8 @@ size_t mhc_pre_fused_workspace_bytes(int64_t T, int64_t H);
  *     y[t][h]    = bf16( sum_i pre[t][i] * res[t][i][h] )   (fp32 accumulation, nearest-even)
  *
  *   res, hc_fn, hc_scale, hc_base   inputs (layouts above), device
- *   T >= 0, H >= 1
+ *   T >= 0, 1 <= H <= 2097152 (the streams of a 64-token tile are addressed with
+ *                     32-bit byte offsets)
  *   rms_eps, pre_eps, sinkhorn_eps  finite; rms_eps and sinkhorn_eps > 0, pre_eps >= 0
  *   post_mult                       finite
  *   num_iters                       >= 1

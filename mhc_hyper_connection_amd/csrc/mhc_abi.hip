@@ -1,7 +1,7 @@
 // mhc_abi.hip -- the extern "C" entry points of libmhc: argument validation on
 // the host, then kernel launches on the caller's stream.  No entry point
 // allocates, frees or synchronises.
-#include "../../include/mhc.h"
+#include "mhc.h"
 #include "mhc_internal.h"
 
 #include <math.h>
@@ -11,6 +11,8 @@ namespace {
 using mhc::PreGeom;
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
+// The pre-map addresses a 64-token tile of the streams with 32-bit byte offsets.
+constexpr int64_t kPreMaxH = (int64_t)1 << 21;
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -80,7 +82,7 @@ mhc_status mhc_sinkhorn(const float *logits, float *out, int64_t n_mats, int32_t
 
 size_t mhc_pre_fused_workspace_bytes(int64_t T, int64_t H)
 {
-    if (T <= 0 || H <= 0 || !sizes_ok(T, H)) {
+    if (T <= 0 || H <= 0 || H > kPreMaxH || !sizes_ok(T, H)) {
         return 0;
     }
     return mhc::pre_geometry(T, H).total_bytes;
@@ -91,7 +93,7 @@ mhc_status mhc_pre_fused(const uint16_t *res, const float *hc_fn, const float *h
                          int32_t num_iters, uint16_t *y, float *post, float *comb, float *pre, void *workspace,
                          size_t workspace_bytes, void *stream)
 {
-    if (!sizes_ok(T, H) || num_iters < 1 || !finite(rms_eps) || !(rms_eps > 0.0f) || !finite(pre_eps) ||
+    if (!sizes_ok(T, H) || H > kPreMaxH || num_iters < 1 || !finite(rms_eps) || !(rms_eps > 0.0f) || !finite(pre_eps) ||
         pre_eps < 0.0f || !finite(sinkhorn_eps) || !(sinkhorn_eps > 0.0f) || !finite(post_mult)) {
         return MHC_ERROR_INVALID_VALUE;
     }
@@ -125,7 +127,7 @@ mhc_status mhc_pre_fused(const uint16_t *res, const float *hc_fn, const float *h
             }
         }
     }
-    const bool vec8 = (H % 8 == 0) && aligned16(res) && aligned16(hc_fn) && aligned16(y);
+    const bool vec8 = (H % 8 == 0) && aligned16(res) && aligned16(y);
     return launch_status(mhc::launch_pre(res, hc_fn, hc_scale, hc_base, g, rms_eps, pre_eps, sinkhorn_eps,
                                          post_mult, num_iters, y, post, comb, pre, workspace, (hipStream_t)stream,
                                          vec8));

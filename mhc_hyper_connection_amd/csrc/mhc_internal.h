@@ -15,34 +15,19 @@ hipError_t launch_post(const uint16_t *x, const uint16_t *res, const float *post
 hipError_t launch_sinkhorn(const float *logits, float *out, int64_t n, int iters, float eps, hipStream_t stream,
                            bool vec4);
 
-// Fused (read-once) pre-map: tiles of 64 tokens x slices of 128 h, persistent grid.
-constexpr int64_t kFusedMaxH = 65536;
-struct FusedGeom {
-    bool valid;
-    int tiles, nhb, S, nclass, nzero;
-    size_t off_bfrag, off_part, off_prew, off_sync, bytes;
-};
-FusedGeom fused_geometry(int64_t T, int64_t H);
-// Launches the prep and fused kernels.  Sets *fits = false (and launches nothing)
-// when the device cannot keep enough workgroups resident for the tile barriers.
-hipError_t launch_pre_fused(const uint16_t *res, const float *hc_fn, const float *hc_scale, const float *hc_base,
-                            const FusedGeom &f, int64_t T, int64_t H, float rms_eps, float pre_eps,
-                            float sinkhorn_eps, float post_mult, int iters, uint16_t *y, float *post, float *comb,
-                            float *pre, void *workspace, hipStream_t stream, bool vec8, bool *fits);
-
-// Pre-map geometry.  The split-K fallback (three kernels, streams read twice)
-// covers H beyond kFusedMaxH and devices that cannot host the fused grid.
+// Pre-map geometry.  Tokens are processed in chunks of `chunk` (a multiple of
+// 64) so that every buffer view the kernels build stays below 2^31 bytes.
 struct PreGeom {
     int64_t T, H;
-    int tiles;        // token tiles of 64
-    int nhb;          // ceil(H / 32)
-    int slices;       // K splits
-    int hb_per_slice; // H blocks per split
-    size_t part_bytes;  // [slices][T][32] fp32 partial sums
-    size_t prew_bytes;  // [T][4] fp32 pre weights
-    size_t split_bytes;  // split-K fallback workspace
-    FusedGeom fused;
-    size_t total_bytes; // workspace size: covers whichever path runs
+    int64_t chunk;     // tokens per launch chunk
+    int tiles;         // 64-token tiles in one chunk
+    int nhb;           // ceil(H / 32)
+    int slices;        // workgroups per 64-token tile in the projection
+    size_t off_frag;   // split weights in MFMA operand order
+    size_t off_rec;    // partial records of one chunk
+    size_t rec_bytes;
+    size_t off_prew;   // per-token field sums of one chunk
+    size_t total_bytes;
 };
 PreGeom pre_geometry(int64_t T, int64_t H);
 

@@ -4,24 +4,29 @@
 // hyper_connection_dispatch.rs, hc_pre_site; metrale glm5next_mhc.rs, the
 // hc_mix / hc_finish split.)
 //
-// This file holds the split-K fallback used for H beyond the fused kernel's
-// range (mhc_pre_fused.hip holds the read-once path).  Three kernels on one
-// stream:
+// Four kernels on one stream:
 //
-//  1. pre_proj_kernel -- the 24 x 4H projection and the sum of squares, on MFMA.
-//     A workgroup owns 64 tokens x one contiguous range of H (all four streams),
-//     i.e. a split-K slice.  The streams are bf16, so they feed
-//     v_mfma_f32_16x16x32_bf16 unchanged.  hc_fn is fp32; each value is split
-//     exactly into three bf16 terms hi + mid + lo (truncations: 8 + 8 + 8
-//     significant bits), so three bf16 products accumulated in fp32 reproduce
-//     the fp32 weight without rounding it.  The sum of squares rides along on
-//     v_dot2_f32_bf16 from the same registers.  Each workgroup writes one
-//     partial record [25] per token and slice (no atomics; fixed reduction order).
-//  2. pre_mix_kernel -- one lane per token: sums the partials in slice order,
-//     rstd, the sigmoid mixes and the 4x4 Sinkhorn in registers; writes post,
-//     comb, pre.
-//  3. pre_collapse_kernel -- y = sum_i pre_i * res_i, one wavefront per
-//     (token, 512-element H tile), 16-byte loads, coefficients in SGPRs.
+//  1. pre_prep_kernel -- splits every fp32 weight of hc_fn exactly into three
+//     bf16 terms hi + mid + lo (successive truncations: 8 + 8 + 8 significant
+//     bits) and stores them in the order of the MFMA B operand, so the
+//     projection loop issues only 16-byte loads and MFMAs.  Three bf16
+//     products accumulated in fp32 reproduce the fp32 weight without rounding
+//     it.
+//  2. pre_proj_kernel -- the 24 x 4H projection and the sum of squares.  A
+//     workgroup owns (64 tokens, a 128-wide slice of H across all 4 streams):
+//     the bf16 streams feed v_mfma_f32_16x16x32_bf16 unchanged, the sum of
+//     squares rides on v_dot2_f32_bf16 from the same registers, and each
+//     workgroup writes one 25-float partial record per token.
+//  3. pre_mixsum_kernel -- sums every record field of every token over the
+//     slices in a fixed order, so the result does not depend on timing.
+//  4. pre_collapse_kernel -- one wavefront per (token, 512-wide H tile): rstd
+//     and the pre weights from the token's sums (wave-uniform, in SGPRs), then
+//     y = sum_i pre_i * res_i with 16-byte loads.  The wavefront of each
+//     token's first tile also computes post and the 4x4 Sinkhorn of comb.
+//
+// The streams are read twice (passes 2 and 3).  A read-once variant that
+// holds the slice in VGPRs across per-tile workgroup barriers is correct on
+// this hardware but spends more time waiting at the barriers than it saves.
 #include "mhc_device.h"
 #include "mhc_internal.h"
 
@@ -29,258 +34,356 @@ namespace mhc {
 
 namespace {
 
-constexpr int kProjBlock = 256;
-constexpr int kProjWaves = kProjBlock / kWave;
-constexpr int kTileTokens = 64; // 4 MFMA row tiles of 16 tokens
-constexpr int kMTiles = kTileTokens / 16;
-constexpr int kHBlock = 32;     // h per MFMA step per stream: 4 lane groups x 8
-constexpr int kPartStride = 32; // floats per (slice, token) partial: 24 dots, sum of squares, padding
-constexpr int kSqSlot = kMix;   // index of the sum of squares inside a partial record
-constexpr int kTargetBlocks = 2048;
-// The read-once cooperative kernel is correct but its cross-workgroup exchange
-// is still latency-bound; the split-K path is faster until that is fixed.
-constexpr bool kUseFusedPre = false;
+constexpr int kPWaves = 4;
+constexpr int kPBlock = kPWaves * kWave;
+constexpr int kPTok = 64;        // tokens per tile
+constexpr int kPMT = kPTok / 16; // MFMA row tiles per wave
+constexpr int kPHB = 32;         // h per block: 4 lane groups x 8
+constexpr int kPNHB = 1;         // blocks per wave
+constexpr int kPSliceH = kPWaves * kPNHB * kPHB;
+constexpr int kRec = kMix + 1;                    // partial record fields: 24 dots + sum of squares
+constexpr int kFragPerHbStream = 3 * 64 + 3 * 32; // hi/mid/lo of column tile 0 (64 lanes) and 1 (32 lanes)
+constexpr int kNT = 2;                            // cache policy nt: streaming
+constexpr int kBufWord3 = 0x00020000;
 
 constexpr int kColBlock = 256;
 constexpr int kColWaves = kColBlock / kWave;
 constexpr int kColVecTile = kWave * 8;
 
-// v == hi + mid + lo exactly for normal fp32 v: each term is a truncation of
-// what remains to bf16 (8 significant bits), and a 24-bit significand has no
-// bits left after three of them.
-__device__ __forceinline__ void split3(const float *v, bf16x8 &hi, bf16x8 &mid, bf16x8 &lo)
+// The record field of projection column `col`: the 4 pre logits, then the sum
+// of squares, then post and comb.  Records are field-major ([25][64]) so one
+// field of the 64 tokens is 256 contiguous bytes.
+constexpr int kFSq = kHC;
+__device__ __forceinline__ int field_of_col(int col) { return col < kHC ? col : col + 1; }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_view(const void *base, uint32_t bytes)
 {
-    u32x4 ph, pm, pl;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kBufWord3);
+}
+
+// v == hi + mid + lo exactly for normal fp32 v (three successive bf16 truncations).
+__device__ __forceinline__ void split3x8(const float *v, u32x4 &ph, u32x4 &pm, u32x4 &pl)
+{
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        uint32_t h0 = __float_as_uint(v[2 * q]) & 0xFFFF0000u;
-        uint32_t h1 = __float_as_uint(v[2 * q + 1]) & 0xFFFF0000u;
-        float r0 = v[2 * q] - __uint_as_float(h0);
-        float r1 = v[2 * q + 1] - __uint_as_float(h1);
-        uint32_t m0 = __float_as_uint(r0) & 0xFFFF0000u;
-        uint32_t m1 = __float_as_uint(r1) & 0xFFFF0000u;
-        float l0 = r0 - __uint_as_float(m0);
-        float l1 = r1 - __uint_as_float(m1);
+        const uint32_t h0 = __float_as_uint(v[2 * q]) & 0xFFFF0000u;
+        const uint32_t h1 = __float_as_uint(v[2 * q + 1]) & 0xFFFF0000u;
+        const float r0 = v[2 * q] - __uint_as_float(h0);
+        const float r1 = v[2 * q + 1] - __uint_as_float(h1);
+        const uint32_t m0 = __float_as_uint(r0) & 0xFFFF0000u;
+        const uint32_t m1 = __float_as_uint(r1) & 0xFFFF0000u;
+        const float l0 = r0 - __uint_as_float(m0);
+        const float l1 = r1 - __uint_as_float(m1);
         ph[q] = (h0 >> 16) | h1;
         pm[q] = (m0 >> 16) | m1;
         pl[q] = (__float_as_uint(l0) >> 16) | (__float_as_uint(l1) & 0xFFFF0000u);
     }
-    hi = __builtin_bit_cast(bf16x8, ph);
-    mid = __builtin_bit_cast(bf16x8, pm);
-    lo = __builtin_bit_cast(bf16x8, pl);
 }
 
-// Eight consecutive bf16 of a stream row starting at h (zeros past H or past T).
-template <bool kVec>
-__device__ __forceinline__ u32x4 load_a(const uint16_t *p, int h, int H, bool ok)
+// One thread per (h block, stream, operand slot).  Slot < 64: column tile 0,
+// MFMA lane = slot (weight row = slot % 16).  Slot >= 64: column tile 1, rows
+// 16..23 only; entry g*8 + c stands for MFMA lane 16g + c (c < 8).
+__global__ __launch_bounds__(256) void pre_prep_kernel(const float *__restrict__ hc_fn, int H, int nhb,
+                                                       u32x4 *__restrict__ frag)
 {
-    u32x4 w = {0u, 0u, 0u, 0u};
-    if (kVec) {
-        if (ok && h < H) {
-            w = load_nt16(p);
-        }
-    } else if (ok) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            uint32_t lo = (h + 2 * q < H) ? (uint32_t)p[2 * q] : 0u;
-            uint32_t hi = (h + 2 * q + 1 < H) ? (uint32_t)p[2 * q + 1] : 0u;
-            w[q] = lo | (hi << 16);
-        }
+    const int gid = blockIdx.x * 256 + threadIdx.x;
+    constexpr int slots = kFragPerHbStream / 3; // 96
+    if (gid >= nhb * kHC * slots) {
+        return;
     }
-    return w;
-}
-
-template <bool kVec>
-__device__ __forceinline__ void load_b(const float *p, int h, int H, bool ok, float *v)
-{
+    const int slot = gid % slots;
+    const int hbi = gid / slots; // hb * 4 + i
+    const int i = hbi % kHC;
+    const int hb = hbi / kHC;
+    int n, g, c;
+    if (slot < 64) {
+        n = 0;
+        g = slot >> 4;
+        c = slot & 15;
+    } else {
+        n = 1;
+        g = (slot - 64) >> 3;
+        c = (slot - 64) & 7;
+    }
+    const int r = n * 16 + c;
+    const int h = hb * kPHB + g * 8;
+    float v[8];
+    const float *src = hc_fn + (size_t)r * kHC * H + (size_t)i * H + h;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        v[j] = 0.0f;
+        v[j] = (h + j < H) ? src[j] : 0.0f;
     }
-    if (kVec) {
-        if (ok && h < H) {
-            const f32x4 v0 = *reinterpret_cast<const f32x4 *>(p);
-            const f32x4 v1 = *reinterpret_cast<const f32x4 *>(p + 4);
-            v[0] = v0[0], v[1] = v0[1], v[2] = v0[2], v[3] = v0[3];
-            v[4] = v1[0], v[5] = v1[1], v[6] = v1[2], v[7] = v1[3];
-        }
-    } else if (ok) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            v[j] = (h + j < H) ? p[j] : 0.0f;
-        }
+    u32x4 ph, pm, pl;
+    split3x8(v, ph, pm, pl);
+    u32x4 *dst = frag + (size_t)hbi * kFragPerHbStream;
+    if (n == 0) {
+        dst[0 * 64 + slot] = ph;
+        dst[1 * 64 + slot] = pm;
+        dst[2 * 64 + slot] = pl;
+    } else {
+        const int k = slot - 64;
+        dst[192 + 0 * 32 + k] = ph;
+        dst[192 + 1 * 32 + k] = pm;
+        dst[192 + 2 * 32 + k] = pl;
     }
 }
 
-// MFMA operand layout (16x16x32 bf16): lane l holds row/column (l % 16) and the
-// 8 k-values of lane group g = l / 16; the result lane l, register q holds
-// row 4g + q, column l % 16.  Here a k-step is one stream i and 32 consecutive
-// h (lane group g takes h = 32*hb + 8g .. +8), identically for A and B.
+struct ProjArgs {
+    const uint16_t *res;
+    const u32x4 *frag;
+    int T, H, nhb, S;
+    float *rec; // [tiles][S][25][64]
+};
+
+// MFMA operand layout (16x16x32 bf16): lane l holds row/column l % 16 and the 8
+// k-values of lane group g = l / 16; result register q of lane l is row 4g + q,
+// column l % 16.  A k-step here is one stream i and 32 consecutive h (lane group
+// g takes h = 32*hb + 8g .. +8), identically for A (tokens) and B (weights).
 template <bool kVec>
-__global__ __launch_bounds__(kProjBlock) void pre_proj_kernel(const uint16_t *__restrict__ res,
-                                                              const float *__restrict__ hc_fn, int T, int H,
-                                                              int nhb, int hb_per_slice, float *__restrict__ part)
+__global__ __launch_bounds__(kPBlock, 2) void pre_proj_kernel(ProjArgs a)
 {
-    const int tile = blockIdx.x;
-    const int slice = blockIdx.y;
-    const int w = threadIdx.x >> 6;
-    const int lane = threadIdx.x & (kWave - 1);
+    __shared__ float red[kPWaves][kPTok][kMix];
+    __shared__ float sqp[kPWaves][4][kPTok];
+
+    // slice fastest: the workgroups in flight together read whole rows of a few
+    // tiles, and (with S a multiple of 8) each XCD only ever needs the weight
+    // fragments of one slice in eight.
+    const int tile = blockIdx.x / a.S;
+    const int slice = blockIdx.x - tile * a.S;
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int lane = tid & (kWave - 1);
     const int g = lane >> 4;
     const int c = lane & 15;
-    const int t0 = tile * kTileTokens;
-    const int hb_begin = slice * hb_per_slice;
-    const int hb_end = min(nhb, hb_begin + hb_per_slice);
-    const size_t K = (size_t)kHC * H;
+    const int S = a.S;
+    const int H = a.H;
+    const int t0 = tile * kPTok;
+    const int ntok = min(kPTok, a.T - t0);
 
-    f32x4 acc[kMTiles][2];
-    float sq[kMTiles];
+    // ---------------- load the slice (buffer loads: rows past T read as zero)
+    u32x4 d[kPNHB][kPMT][kHC];
+    const __amdgpu_buffer_rsrc_t vres =
+        buf_view(a.res + (size_t)t0 * kHC * H, (uint32_t)((size_t)ntok * kHC * H * sizeof(uint16_t)));
 #pragma unroll
-    for (int m = 0; m < kMTiles; ++m) {
-        acc[m][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-        acc[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-        sq[m] = 0.0f;
+    for (int b = 0; b < kPNHB; ++b) {
+        const int hb = (slice * kPNHB + b) * kPWaves + w;
+        const int h = hb * kPHB + g * 8;
+#pragma unroll
+        for (int m = 0; m < kPMT; ++m) {
+#pragma unroll
+            for (int i = 0; i < kHC; ++i) {
+                const int row = (m * 16 + c) * kHC + i;
+                if (kVec) {
+                    // past H (ragged last block): an offset beyond the view reads zeros
+                    const uint32_t off = h < H ? (uint32_t)(row * H + h) * 2u : 0xFFFFFFF0u;
+                    d[b][m][i] =
+                        __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vres, (int)off, 0, kNT));
+                } else {
+                    u32x4 v = {0u, 0u, 0u, 0u};
+                    if (m * 16 + c < ntok) {
+                        const uint16_t *p = a.res + ((size_t)t0 * kHC + row) * H + h;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const uint32_t lo = (h + 2 * q < H) ? (uint32_t)p[2 * q] : 0u;
+                            const uint32_t hi = (h + 2 * q + 1 < H) ? (uint32_t)p[2 * q + 1] : 0u;
+                            v[q] = lo | (hi << 16);
+                        }
+                    }
+                    d[b][m][i] = v;
+                }
+            }
+        }
     }
 
-    for (int hb = hb_begin + w; hb < hb_end; hb += kProjWaves) {
-        const int h = hb * kHBlock + g * 8;
+    // ---------------- project: 24 weight rows (hi/mid/lo) x 64 tokens
+    f32x4 acc[kPMT][2];
 #pragma unroll
-        for (int i = 0; i < kHC; ++i) {
-            bf16x8 a[kMTiles];
+    for (int m = 0; m < kPMT; ++m) {
+        acc[m][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
-            for (int m = 0; m < kMTiles; ++m) {
-                const int t = t0 + m * 16 + c;
-                const u32x4 wa = load_a<kVec>(res + ((size_t)t * kHC + i) * H + h, h, H, t < T);
+    for (int b = 0; b < kPNHB; ++b) {
+        const int hb = (slice * kPNHB + b) * kPWaves + w;
+        if (hb < a.nhb) { // wave-uniform
+            // All weight fragments of the block are requested before the first MFMA,
+            // so their L2 latency overlaps with the stream loads above.
+            const u32x4 *fp = a.frag + (size_t)hb * kHC * kFragPerHbStream;
+            u32x4 b0[kHC][3], b1[kHC][3];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    // Copy the element to a scalar first: hipcc (clang 22) miscompiles
-                    // __builtin_bit_cast applied directly to an ext_vector element
-                    // (it reads element 0 for every q).
-                    const uint32_t wq = wa[q];
-                    const bf16x2 pr = __builtin_bit_cast(bf16x2, wq);
-                    sq[m] = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, sq[m], false);
+            for (int i = 0; i < kHC; ++i) {
+#pragma unroll
+                for (int s = 0; s < 3; ++s) {
+                    b0[i][s] = fp[i * kFragPerHbStream + s * 64 + lane];
+                    b1[i][s] = fp[i * kFragPerHbStream + 192 + s * 32 + ((g * 8 + c) & 31)];
                 }
-                a[m] = __builtin_bit_cast(bf16x8, wa);
-            }
-            bf16x8 b[2][3];
-#pragma unroll
-            for (int n = 0; n < 2; ++n) {
-                const int r = n * 16 + c;
-                float v[8];
-                load_b<kVec>(hc_fn + (size_t)r * K + (size_t)i * H + h, h, H, r < kMix, v);
-                split3(v, b[n][0], b[n][1], b[n][2]);
             }
 #pragma unroll
-            for (int s = 0; s < 3; ++s) {
+            for (int i = 0; i < kHC; ++i) {
 #pragma unroll
-                for (int m = 0; m < kMTiles; ++m) {
+                for (int s = 0; s < 3; ++s) {
+                    const bf16x8 B0 = __builtin_bit_cast(bf16x8, b0[i][s]);
+                    // lanes with c >= 8 stand for weight rows >= 24: zero
+                    const bf16x8 B1 = __builtin_bit_cast(bf16x8, c < 8 ? b1[i][s] : u32x4{0u, 0u, 0u, 0u});
 #pragma unroll
-                    for (int n = 0; n < 2; ++n) {
-                        acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m], b[n][s], acc[m][n], 0, 0, 0);
+                    for (int m = 0; m < kPMT; ++m) {
+                        const bf16x8 A = __builtin_bit_cast(bf16x8, d[b][m][i]);
+                        acc[m][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B0, acc[m][0], 0, 0, 0);
+                        acc[m][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B1, acc[m][1], 0, 0, 0);
                     }
                 }
             }
         }
     }
-
-    // Reduce the four waves (and, for the sum of squares, the four lane groups)
-    // through LDS in a fixed order.
-    __shared__ float red[kProjWaves][kTileTokens][kMix];
-    __shared__ float sqr[kProjWaves][4][kTileTokens];
+    float sq[kPMT];
 #pragma unroll
-    for (int m = 0; m < kMTiles; ++m) {
+    for (int m = 0; m < kPMT; ++m) {
+        sq[m] = 0.0f;
+#pragma unroll
+        for (int b = 0; b < kPNHB; ++b) {
+#pragma unroll
+            for (int i = 0; i < kHC; ++i) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    // Copy to a scalar first: hipcc (clang 22) miscompiles __builtin_bit_cast
+                    // applied directly to an ext_vector element (it reads element 0 for every k).
+                    const uint32_t wk = d[b][m][i][k];
+                    const bf16x2 pr = __builtin_bit_cast(bf16x2, wk);
+                    sq[m] = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, sq[m], false);
+                }
+            }
+        }
+    }
+
+    // ---------------- workgroup reduction -> this slice's partial record
+#pragma unroll
+    for (int m = 0; m < kPMT; ++m) {
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
             const int col = n * 16 + c;
             if (col < kMix) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    red[w][m * 16 + 4 * g + q][col] = acc[m][n][q];
+                for (int k = 0; k < 4; ++k) {
+                    red[w][m * 16 + 4 * g + k][col] = acc[m][n][k];
                 }
             }
         }
-        sqr[w][g][m * 16 + c] = sq[m];
+        sqp[w][g][m * 16 + c] = sq[m];
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < kTileTokens * (kMix + 1); e += kProjBlock) {
-        const int tok = e / (kMix + 1);
-        const int r = e - tok * (kMix + 1);
-        float v;
-        if (r < kMix) {
-            v = ((red[0][tok][r] + red[1][tok][r]) + red[2][tok][r]) + red[3][tok][r];
-        } else {
-            v = 0.0f;
+    float *rec = a.rec + ((size_t)tile * S + slice) * (kRec * kPTok);
+    const int tok = tid & (kPTok - 1);
+    for (int col = tid >> 6; col < kMix; col += kPWaves) {
+        float v = red[0][tok][col];
 #pragma unroll
-            for (int ww = 0; ww < kProjWaves; ++ww) {
+        for (int ww = 1; ww < kPWaves; ++ww) {
+            v += red[ww][tok][col];
+        }
+        rec[field_of_col(col) * kPTok + tok] = v;
+    }
+    if (tid < kPTok) {
+        float v = 0.0f;
 #pragma unroll
-                for (int gg = 0; gg < 4; ++gg) {
-                    v += sqr[ww][gg][tok];
-                }
+        for (int ww = 0; ww < kPWaves; ++ww) {
+#pragma unroll
+            for (int gg = 0; gg < 4; ++gg) {
+                v += sqp[ww][gg][tid];
             }
         }
-        const int t = t0 + tok;
-        if (t < T) {
-            part[((size_t)slice * T + t) * kPartStride + r] = v;
-        }
+        rec[kFSq * kPTok + tid] = v;
     }
 }
 
-__global__ __launch_bounds__(256) void pre_mix_kernel(const float *__restrict__ part, int T, int slices, float k_denom,
-                                                      const float *__restrict__ hc_scale,
-                                                      const float *__restrict__ hc_base, float rms_eps,
-                                                      float pre_eps, float sk_eps, float post_mult, int iters,
-                                                      float *__restrict__ post, float *__restrict__ comb,
-                                                      float *__restrict__ pre_out, float *__restrict__ pre_ws)
+// Per-token sums of the 25 record fields over the slices.  Block = (tile,
+// field): thread (token, slice group k) adds slices k, k+4, ... (independent
+// loads in flight), then the four group sums are added in a fixed order.
+constexpr int kSumStride = 32; // floats per token in the sums array (25 used)
+__global__ __launch_bounds__(256) void pre_mixsum_kernel(const float *__restrict__ rec, int T, int S,
+                                                         float *__restrict__ sums)
 {
-    const int t = blockIdx.x * 256 + threadIdx.x;
-    if (t >= T) {
-        return;
+    __shared__ float part[4][kPTok];
+    const int tile = blockIdx.x / kRec;
+    const int f = blockIdx.x - tile * kRec;
+    const int tok = threadIdx.x & (kPTok - 1);
+    const int k = threadIdx.x >> 6;
+    const float *src = rec + (size_t)tile * S * (kRec * kPTok) + f * kPTok + tok;
+    float v = 0.0f;
+    int s = k;
+    for (; s + 12 < S; s += 16) {
+        const float e0 = src[(size_t)s * (kRec * kPTok)];
+        const float e1 = src[(size_t)(s + 4) * (kRec * kPTok)];
+        const float e2 = src[(size_t)(s + 8) * (kRec * kPTok)];
+        const float e3 = src[(size_t)(s + 12) * (kRec * kPTok)];
+        v += e0;
+        v += e1;
+        v += e2;
+        v += e3;
     }
-    float d[kPartStride];
-#pragma unroll
-    for (int r = 0; r < kPartStride; ++r) {
-        d[r] = 0.0f;
+    for (; s < S; s += 4) {
+        v += src[(size_t)s * (kRec * kPTok)];
     }
-    for (int s = 0; s < slices; ++s) {
-        const f32x4 *p = reinterpret_cast<const f32x4 *>(part + ((size_t)s * T + t) * kPartStride);
+    part[k][tok] = v;
+    __syncthreads();
+    const int t = tile * kPTok + threadIdx.x;
+    if (threadIdx.x < kPTok && t < T) {
+        sums[(size_t)t * kSumStride + f] =
+            ((part[0][threadIdx.x] + part[1][threadIdx.x]) + part[2][threadIdx.x]) + part[3][threadIdx.x];
+    }
+}
+
+struct MixArgs {
+    const float *sums; // [T][32]: 4 pre logits, sum of squares, 4 post logits, 16 comb logits
+    const float *hc_scale;
+    const float *hc_base;
+    float k_denom, rms_eps, pre_eps, sk_eps, post_mult;
+    int iters;
+    float *post, *comb, *pre_out;
+};
+
+// pre weights of token t from its sums (wave-uniform).
+__device__ __forceinline__ void token_pre(const MixArgs &m, int t, float *p, float &rstd)
+{
+    const float *d = m.sums + (size_t)t * kSumStride;
+    rstd = 1.0f / sqrtf(d[kFSq] / m.k_denom + m.rms_eps);
 #pragma unroll
-        for (int q = 0; q < 7; ++q) { // records hold 25 used floats: 7 float4 cover them
-            const f32x4 v = p[q];
-            d[4 * q] += v[0];
-            d[4 * q + 1] += v[1];
-            d[4 * q + 2] += v[2];
-            d[4 * q + 3] += v[3];
+    for (int i = 0; i < kHC; ++i) {
+        p[i] = sigmoidf_fast(fmaf(d[i] * rstd, m.hc_scale[0], m.hc_base[i])) + m.pre_eps;
+    }
+}
+
+// post, comb (Sinkhorn) and the optional pre output of token t (one lane writes).
+__device__ __forceinline__ void token_mix_outputs(const MixArgs &m, int t, const float *p, float rstd, bool writer)
+{
+    const float *d = m.sums + (size_t)t * kSumStride;
+    float post[kHC];
+#pragma unroll
+    for (int i = 0; i < kHC; ++i) {
+        post[i] = sigmoidf_fast(fmaf(d[kFSq + 1 + i] * rstd, m.hc_scale[1], m.hc_base[kHC + i])) * m.post_mult;
+    }
+    float P16[kHC * kHC];
+#pragma unroll
+    for (int e = 0; e < kHC * kHC; ++e) {
+        P16[e] = fmaf(d[kFSq + 1 + kHC + e] * rstd, m.hc_scale[2], m.hc_base[2 * kHC + e]);
+    }
+    sinkhorn4x4(P16, m.iters, m.sk_eps);
+    if (writer) {
+#pragma unroll
+        for (int i = 0; i < kHC; ++i) {
+            m.post[(size_t)t * kHC + i] = post[i];
+            if (m.pre_out) {
+                m.pre_out[(size_t)t * kHC + i] = p[i];
+            }
         }
-    }
-    const float rstd = 1.0f / sqrtf(d[kSqSlot] / k_denom + rms_eps);
-    const float s_pre = hc_scale[0], s_post = hc_scale[1], s_comb = hc_scale[2];
-    float pw[kHC];
 #pragma unroll
-    for (int i = 0; i < kHC; ++i) {
-        pw[i] = sigmoidf_fast(fmaf(d[i] * rstd, s_pre, hc_base[i])) + pre_eps;
-        post[t * kHC + i] = sigmoidf_fast(fmaf(d[kHC + i] * rstd, s_post, hc_base[kHC + i])) * post_mult;
-    }
-    float P[kHC * kHC];
-#pragma unroll
-    for (int e = 0; e < kHC * kHC; ++e) {
-        P[e] = fmaf(d[2 * kHC + e] * rstd, s_comb, hc_base[2 * kHC + e]);
-    }
-    sinkhorn4x4(P, iters, sk_eps);
-#pragma unroll
-    for (int e = 0; e < kHC * kHC; ++e) {
-        comb[t * kHC * kHC + e] = P[e];
-    }
-#pragma unroll
-    for (int i = 0; i < kHC; ++i) {
-        pre_ws[t * kHC + i] = pw[i];
-        if (pre_out) {
-            pre_out[t * kHC + i] = pw[i];
+        for (int e = 0; e < kHC * kHC; ++e) {
+            m.comb[(size_t)t * kHC * kHC + e] = P16[e];
         }
     }
 }
 
-__global__ __launch_bounds__(kColBlock) void pre_collapse_vec8_kernel(const uint16_t *__restrict__ res,
-                                                                      const float *__restrict__ pre_ws, int T, int H,
-                                                                      int tiles_per_token, uint16_t *__restrict__ y)
+__global__ __launch_bounds__(kColBlock) void pre_collapse_vec8_kernel(const uint16_t *__restrict__ res, MixArgs mx,
+                                                                      int T, int H, int tiles_per_token,
+                                                                      uint16_t *__restrict__ y)
 {
     const int wave = uniform(blockIdx.x * kColWaves + (threadIdx.x >> 6));
     const int lane = threadIdx.x & (kWave - 1);
@@ -289,15 +392,10 @@ __global__ __launch_bounds__(kColBlock) void pre_collapse_vec8_kernel(const uint
     if (t >= T) {
         return;
     }
+    float p[kHC], rstd;
+    token_pre(mx, t, p, rstd);
     const int h = tile * kColVecTile + lane * 8;
-    if (h >= H) {
-        return;
-    }
-    float p[kHC];
-#pragma unroll
-    for (int i = 0; i < kHC; ++i) {
-        p[i] = pre_ws[t * kHC + i];
-    }
+    if (h < H) {
     const size_t row = (size_t)t * kHC * H + h;
     u32x4 rw[kHC];
 #pragma unroll
@@ -317,11 +415,15 @@ __global__ __launch_bounds__(kColBlock) void pre_collapse_vec8_kernel(const uint
         yw[q] = pack_bf16x2(lo, hi);
     }
     store_nt16(y + (size_t)t * H + h, yw);
+    }
+    if (tile == 0) {
+        token_mix_outputs(mx, t, p, rstd, lane == 0);
+    }
 }
 
 __global__ __launch_bounds__(kColBlock) void pre_collapse_scalar_kernel(const uint16_t *__restrict__ res,
-                                                                        const float *__restrict__ pre_ws, int T,
-                                                                        int H, int tiles_per_token,
+                                                                        MixArgs mx, int T, int H,
+                                                                        int tiles_per_token,
                                                                         uint16_t *__restrict__ y)
 {
     const int wave = uniform(blockIdx.x * kColWaves + (threadIdx.x >> 6));
@@ -331,17 +433,21 @@ __global__ __launch_bounds__(kColBlock) void pre_collapse_scalar_kernel(const ui
     if (t >= T) {
         return;
     }
+    float p[kHC], rstd;
+    token_pre(mx, t, p, rstd);
     const int h = tile * kWave + lane;
-    if (h >= H) {
-        return;
-    }
-    const size_t row = (size_t)t * kHC * H + h;
-    float a = bf16_to_f32(res[row]) * pre_ws[t * kHC];
+    if (h < H) {
+        const size_t row = (size_t)t * kHC * H + h;
+        float a = bf16_to_f32(res[row]) * p[0];
 #pragma unroll
-    for (int i = 1; i < kHC; ++i) {
-        a = fmaf(bf16_to_f32(res[row + (size_t)i * H]), pre_ws[t * kHC + i], a);
+        for (int i = 1; i < kHC; ++i) {
+            a = fmaf(bf16_to_f32(res[row + (size_t)i * H]), p[i], a);
+        }
+        y[(size_t)t * H + h] = f32_to_bf16(a);
     }
-    y[(size_t)t * H + h] = f32_to_bf16(a);
+    if (tile == 0) {
+        token_mix_outputs(mx, t, p, rstd, lane == 0);
+    }
 }
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -356,18 +462,25 @@ PreGeom pre_geometry(int64_t T, int64_t H)
     if (T <= 0 || H <= 0) {
         return g;
     }
-    g.tiles = (int)((T + kTileTokens - 1) / kTileTokens);
-    g.nhb = (int)((H + kHBlock - 1) / kHBlock);
-    int s = (kTargetBlocks + g.tiles - 1) / g.tiles;
-    const int max_s = g.nhb / kProjWaves > 1 ? g.nhb / kProjWaves : 1; // >= one H block per wave
-    s = s < 1 ? 1 : (s > max_s ? max_s : s);
-    g.hb_per_slice = (g.nhb + s - 1) / s;
-    g.slices = (g.nhb + g.hb_per_slice - 1) / g.hb_per_slice;
-    g.part_bytes = (size_t)g.slices * (size_t)T * kPartStride * sizeof(float);
-    g.prew_bytes = (size_t)T * kHC * sizeof(float);
-    g.split_bytes = align256(g.part_bytes) + align256(g.prew_bytes);
-    g.fused = kUseFusedPre ? fused_geometry(T, H) : FusedGeom{};
-    g.total_bytes = g.fused.valid && g.fused.bytes > g.split_bytes ? g.fused.bytes : g.split_bytes;
+    g.nhb = (int)((H + kPHB - 1) / kPHB);
+    g.slices = (int)((H + kPSliceH - 1) / kPSliceH);
+    const int64_t tiles_total = (T + kPTok - 1) / kPTok;
+    const size_t rec_per_tile = (size_t)g.slices * kRec * kPTok * sizeof(float);
+    int64_t max_tiles = (int64_t)(((size_t)1 << 31) / rec_per_tile);
+    if (max_tiles < 1) {
+        max_tiles = 1;
+    }
+    g.tiles = (int)(tiles_total < max_tiles ? tiles_total : max_tiles);
+    g.chunk = (int64_t)g.tiles * kPTok;
+    size_t off = 0;
+    g.off_frag = off;
+    off += align256((size_t)g.nhb * kHC * kFragPerHbStream * sizeof(u32x4));
+    g.off_rec = off;
+    g.rec_bytes = (size_t)g.tiles * rec_per_tile;
+    off += align256(g.rec_bytes);
+    g.off_prew = off;
+    off += align256((size_t)g.chunk * kSumStride * sizeof(float));
+    g.total_bytes = off;
     return g;
 }
 
@@ -376,47 +489,74 @@ hipError_t launch_pre(const uint16_t *res, const float *hc_fn, const float *hc_s
                       int iters, uint16_t *y, float *post, float *comb, float *pre, void *workspace,
                       hipStream_t stream, bool vec8)
 {
-    if (g.fused.valid) {
-        bool fits = false;
-        const hipError_t e = launch_pre_fused(res, hc_fn, hc_scale, hc_base, g.fused, g.T, g.H, rms_eps, pre_eps,
-                                              sinkhorn_eps, post_mult, iters, y, post, comb, pre, workspace, stream,
-                                              vec8, &fits);
-        if (e != hipSuccess || fits) {
-            return e;
-        }
-    }
-    float *part = reinterpret_cast<float *>(workspace);
-    float *pre_ws = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + align256(g.part_bytes));
-    const int T = (int)g.T, H = (int)g.H;
-    const dim3 pgrid((unsigned)g.tiles, (unsigned)g.slices);
-    if (vec8) {
-        pre_proj_kernel<true><<<pgrid, dim3(kProjBlock), 0, stream>>>(res, hc_fn, T, H, g.nhb, g.hb_per_slice, part);
-    } else {
-        pre_proj_kernel<false><<<pgrid, dim3(kProjBlock), 0, stream>>>(res, hc_fn, T, H, g.nhb, g.hb_per_slice,
-                                                                        part);
-    }
+    char *ws = reinterpret_cast<char *>(workspace);
+    u32x4 *frag = reinterpret_cast<u32x4 *>(ws + g.off_frag);
+    const int H = (int)g.H;
+
+    const int prep_threads = g.nhb * kHC * (kFragPerHbStream / 3);
+    pre_prep_kernel<<<dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, stream>>>(hc_fn, H, g.nhb, frag);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
         return e;
     }
-    pre_mix_kernel<<<dim3((unsigned)((T + 255) / 256)), dim3(256), 0, stream>>>(
-        part, T, g.slices, (float)(kHC * g.H), hc_scale, hc_base, rms_eps, pre_eps, sinkhorn_eps, post_mult, iters,
-        post, comb, pre, pre_ws);
-    e = hipGetLastError();
-    if (e != hipSuccess) {
-        return e;
+    float *sums = reinterpret_cast<float *>(ws + g.off_prew);
+    for (int64_t c0 = 0; c0 < g.T; c0 += g.chunk) {
+        const int Tc = (int)(g.T - c0 < g.chunk ? g.T - c0 : g.chunk);
+        const int tiles = (Tc + kPTok - 1) / kPTok;
+        ProjArgs a;
+        a.res = res + (size_t)c0 * kHC * H;
+        a.frag = frag;
+        a.T = Tc;
+        a.H = H;
+        a.nhb = g.nhb;
+        a.S = g.slices;
+        a.rec = reinterpret_cast<float *>(ws + g.off_rec);
+        const dim3 pgrid((unsigned)(tiles * g.slices));
+        if (vec8) {
+            pre_proj_kernel<true><<<pgrid, dim3(kPBlock), 0, stream>>>(a);
+        } else {
+            pre_proj_kernel<false><<<pgrid, dim3(kPBlock), 0, stream>>>(a);
+        }
+        e = hipGetLastError();
+        if (e != hipSuccess) {
+            return e;
+        }
+        pre_mixsum_kernel<<<dim3((unsigned)(tiles * kRec)), dim3(256), 0, stream>>>(a.rec, Tc, g.slices, sums);
+        e = hipGetLastError();
+        if (e != hipSuccess) {
+            return e;
+        }
+        MixArgs mx;
+        mx.sums = sums;
+        mx.hc_scale = hc_scale;
+        mx.hc_base = hc_base;
+        mx.k_denom = (float)(kHC * g.H);
+        mx.rms_eps = rms_eps;
+        mx.pre_eps = pre_eps;
+        mx.sk_eps = sinkhorn_eps;
+        mx.post_mult = post_mult;
+        mx.iters = iters;
+        mx.post = post + (size_t)c0 * kHC;
+        mx.comb = comb + (size_t)c0 * kHC * kHC;
+        mx.pre_out = pre ? pre + (size_t)c0 * kHC : nullptr;
+        const int tile = vec8 ? kColVecTile : kWave;
+        const int64_t htiles = (g.H + tile - 1) / tile;
+        const int64_t blocks = ((int64_t)Tc * htiles + kColWaves - 1) / kColWaves;
+        const uint16_t *rc = res + (size_t)c0 * kHC * H;
+        uint16_t *yc = y + (size_t)c0 * H;
+        if (vec8) {
+            pre_collapse_vec8_kernel<<<dim3((unsigned)blocks), dim3(kColBlock), 0, stream>>>(rc, mx, Tc, H,
+                                                                                             (int)htiles, yc);
+        } else {
+            pre_collapse_scalar_kernel<<<dim3((unsigned)blocks), dim3(kColBlock), 0, stream>>>(rc, mx, Tc, H,
+                                                                                               (int)htiles, yc);
+        }
+        e = hipGetLastError();
+        if (e != hipSuccess) {
+            return e;
+        }
     }
-    const int tile = vec8 ? kColVecTile : kWave;
-    const int64_t tiles = (g.H + tile - 1) / tile;
-    const int64_t blocks = (g.T * tiles + kColWaves - 1) / kColWaves;
-    if (vec8) {
-        pre_collapse_vec8_kernel<<<dim3((unsigned)blocks), dim3(kColBlock), 0, stream>>>(res, pre_ws, T, H,
-                                                                                         (int)tiles, y);
-    } else {
-        pre_collapse_scalar_kernel<<<dim3((unsigned)blocks), dim3(kColBlock), 0, stream>>>(res, pre_ws, T, H,
-                                                                                           (int)tiles, y);
-    }
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 } // namespace mhc
