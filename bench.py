@@ -44,6 +44,9 @@ def parse():
                     help="run only one call in the timed loop (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="(no GPU) turn two rocprofv3 --pmc CSV runs into the stored per-kernel HBM traffic")
+    ap.add_argument("--traffic-command", default="", help="the profiling command, recorded with --write-traffic")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -51,6 +54,10 @@ def parse():
 
 def main():
     args = parse()
+    if args.write_traffic:
+        _, T, H = WORKLOADS[args.workload]
+        write_traffic(args.write_traffic[0], args.write_traffic[1], T, H, args.traffic_command)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (the mHC path shards tokens with no exchange; "
               "no multi-GPU run is implemented here). Use --gpus 1.", file=sys.stderr)
@@ -149,28 +156,43 @@ def main():
         step_bytes = (pre_b if args.only in ("all", "pre") else 0) + (post_b if args.only in ("all", "post") else 0)
     eff_gbps = step_bytes / (ms_step * 1e-3) / 1e9
 
-    # Roofline of the dominant call (largest share of the step).
-    cand = []
+    # Per-call rooflines.  mhc_post and mhc_sinkhorn are one kernel launch each;
+    # mhc_pre_fused is four (weight split, projection, slice sums, collapse).
+    calls = {}
     if "pre_ms" in breakdown:
-        cand.append(("mhc_pre_fused", breakdown["pre_ms"], pre_b))
+        col = "pre_collapse_vec8_kernel" if H % 8 == 0 else "pre_collapse_scalar_kernel"
+        proj = "pre_proj_kernel"
+        calls["mhc_pre_fused"] = ("pre_prep_kernel+" + proj + "+pre_mixsum_kernel+" + col, breakdown["pre_ms"], pre_b)
     if "post_ms" in breakdown:
-        cand.append(("mhc_post", breakdown["post_ms"], post_b))
+        calls["mhc_post"] = ("post_vec8_kernel" if H % 8 == 0 else "post_scalar_kernel", breakdown["post_ms"], post_b)
     if "sinkhorn_ms" in breakdown:
-        cand.append(("mhc_sinkhorn", breakdown["sinkhorn_ms"], step_bytes))
-    name, ms_k, bytes_k = max(cand, key=lambda c: c[1])
-    achieved = bytes_k / (ms_k * 1e-3) / 1e9
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": name,
-                "avg_ms": round(ms_k, 5), "algorithmic_bytes": bytes_k}
+        calls["mhc_sinkhorn"] = ("sinkhorn_kernel", breakdown["sinkhorn_ms"], step_bytes)
+    traffic = load_traffic(T, H)
+    per_call = {}
+    for name, (kern, ms_k, bytes_k) in calls.items():
+        achieved = bytes_k / (ms_k * 1e-3) / 1e9
+        per_call[name] = {"kernel": kern, "avg_ms": round(ms_k, 5), "algorithmic_bytes": bytes_k,
+                          "achieved": round(achieved, 1), "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                          "traffic": call_traffic(traffic, kern)}
+    # The dominant kernel: the longest single kernel launch of the step.  At
+    # T=8192, H=7168 that is the post-map (one launch, 64% of the bytes); the
+    # pre-map's longest kernel, the projection, is shorter.
+    dom = "mhc_post" if "mhc_post" in per_call else next(iter(per_call))
+    d = per_call[dom]
+    roofline = {"bound": "hbm", "achieved": d["achieved"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": d["frac"], "traffic": d["traffic"], "kernel": d["kernel"], "call": dom,
+                "avg_ms": d["avg_ms"], "algorithmic_bytes": d["algorithmic_bytes"]}
 
     copy_cal = None
     if args.copy_calibration:
-        n = 1 << 29  # 1 GiB of bf16
+        # A plain elementwise kernel of known size (reads 1 GiB, writes 1 GiB): the
+        # reference that scales the HBM byte counters of the kernels above.
+        n = 1 << 29
         src = torch.empty(n, dtype=torch.bfloat16, device=dev).normal_()
         dst = torch.empty_like(src)
-        ms_copy = timed(lambda: dst.copy_(src), 5)
-        copy_cal = {"bytes_read": 2 * n, "bytes_written": 2 * n, "ms": round(ms_copy, 4),
-                    "GBps": round(4 * n / (ms_copy * 1e-3) / 1e9, 1)}
+        ms_copy = timed(lambda: torch.neg(src, out=dst), 5)
+        copy_cal = {"kernel": "torch.neg (bf16, 2^29 elements)", "bytes_read": 2 * n, "bytes_written": 2 * n,
+                    "ms": round(ms_copy, 4), "GBps": round(4 * n / (ms_copy * 1e-3) / 1e9, 1)}
 
     cpu = None
     if not args.no_cpu_baseline and args.only in ("all",):
@@ -196,12 +218,103 @@ def main():
         "algorithmic_bytes_per_step": step_bytes,
         "breakdown_ms": {k: round(v, 5) for k, v in breakdown.items()},
         "roofline": roofline,
+        "calls": per_call,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),
     }
     if copy_cal:
         line["copy_calibration"] = copy_cal
     print(json.dumps(line), flush=True)
+
+
+PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "mhc_hyper_connection_amd", "csrc")
+
+
+def sources_digest() -> str:
+    """sha256 over the HIP sources (name + bytes), to tell whether stored counters are stale."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_path(T: int, H: int) -> str:
+    return os.path.join(PROFILES, f"hbm_traffic_T{T}_H{H}.json")
+
+
+def load_traffic(T: int, H: int):
+    """Per-kernel HBM bytes per launch from the stored counter runs, or None when
+    they are missing or were taken on different kernel sources."""
+    try:
+        with open(traffic_path(T, H)) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_sha256") != sources_digest():
+        return None
+    return {k: v["bytes"] for k, v in rec["kernels"].items()}
+
+
+def call_traffic(traffic, kernels: str):
+    """Summed HBM bytes of the '+'-joined kernels of one call, if all were measured."""
+    if not traffic:
+        return None
+    names = kernels.split("+")
+    if not all(n in traffic for n in names):
+        return None
+    return sum(traffic[n] for n in names)
+
+
+def _pmc_per_kernel(csv_dir: str, counter: str):
+    """Mean counter value (KiB) per dispatch, by kernel, from a rocprofv3 --pmc CSV run."""
+    import csv
+    import glob
+    import re
+    vals = {}
+    for path in glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                m = re.search(r"(\w+_kernel)\b", row["Kernel_Name"]) or re.search(r"([A-Za-z_]\w*)", row["Kernel_Name"])
+                name = m.group(1)
+                if "neg_kernel" in row["Kernel_Name"] or ("neg" in row["Kernel_Name"] and "elementwise" in row["Kernel_Name"]):
+                    name = "calibration_copy"
+                vals.setdefault(name, []).append(float(row["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in vals.items()}
+
+
+def write_traffic(fetch_dir: str, write_dir: str, T: int, H: int, command: str) -> None:
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) into bytes per launch,
+    each counter scaled by what it reads for the calibration copy kernel."""
+    fetch = _pmc_per_kernel(fetch_dir, "FETCH_SIZE")
+    write = _pmc_per_kernel(write_dir, "WRITE_SIZE")
+    cal_bytes = 2 * (1 << 29)
+    f_fetch = cal_bytes / (fetch["calibration_copy"] * 1024)
+    f_write = cal_bytes / (write["calibration_copy"] * 1024)
+    kernels = {}
+    for k in sorted(set(fetch) & set(write)):
+        if k == "calibration_copy":
+            continue
+        rb, wb = fetch[k] * 1024 * f_fetch, write[k] * 1024 * f_write
+        kernels[k] = {"fetch_kib": round(fetch[k], 1), "write_kib": round(write[k], 1),
+                      "read_bytes": round(rb), "write_bytes": round(wb), "bytes": round(rb + wb)}
+    rec = {"workload": f"T={T} H={H}", "command": command, "counters": ["FETCH_SIZE", "WRITE_SIZE"],
+           "calibration": {"kernel": "torch.neg bf16 2^29 elements", "bytes_read": cal_bytes,
+                           "bytes_written": cal_bytes, "fetch_kib": round(fetch["calibration_copy"], 1),
+                           "write_kib": round(write["calibration_copy"], 1), "fetch_factor": round(f_fetch, 4),
+                           "write_factor": round(f_write, 4)},
+           "sources_sha256": sources_digest(), "kernels": kernels}
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(traffic_path(T, H), "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec, indent=1))
 
 
 def cpu_baseline(inp, target_s: float):
