@@ -24,9 +24,10 @@
 //     y = sum_i pre_i * res_i with 16-byte loads.  The wavefront of each
 //     token's first tile also computes post and the 4x4 Sinkhorn of comb.
 //
-// The streams are read twice (passes 2 and 3).  A read-once variant that
-// holds the slice in VGPRs across per-tile workgroup barriers is correct on
-// this hardware but spends more time waiting at the barriers than it saves.
+// The streams are read twice (passes 2 and 4).  Reading them once needs the
+// collapse to wait for a cross-workgroup reduction while the data sits on
+// chip; a CU returns loads in order, so that reduction's round trips queue
+// behind the CU's own stream loads and cost more than the second read.
 #include "mhc_device.h"
 #include "mhc_internal.h"
 
@@ -145,11 +146,8 @@ __global__ __launch_bounds__(kPBlock, 2) void pre_proj_kernel(ProjArgs a)
     __shared__ float red[kPWaves][kPTok][kMix];
     __shared__ float sqp[kPWaves][4][kPTok];
 
-    // slice fastest: the workgroups in flight together read whole rows of a few
-    // tiles, and (with S a multiple of 8) each XCD only ever needs the weight
-    // fragments of one slice in eight.
-    const int tile = blockIdx.x / a.S;
-    const int slice = blockIdx.x - tile * a.S;
+    const int tile = blockIdx.x;
+    const int slice = blockIdx.y;
     const int tid = threadIdx.x;
     const int w = tid >> 6;
     const int lane = tid & (kWave - 1);
@@ -168,14 +166,16 @@ __global__ __launch_bounds__(kPBlock, 2) void pre_proj_kernel(ProjArgs a)
     for (int b = 0; b < kPNHB; ++b) {
         const int hb = (slice * kPNHB + b) * kPWaves + w;
         const int h = hb * kPHB + g * 8;
+        // past H (ragged last block): a column offset beyond the view reads zeros
+        // (one select up front; a select per load becomes branches and serialised loads)
+        const uint32_t colo = h < H ? (uint32_t)h * 2u : 0x80000000u;
 #pragma unroll
         for (int m = 0; m < kPMT; ++m) {
 #pragma unroll
             for (int i = 0; i < kHC; ++i) {
                 const int row = (m * 16 + c) * kHC + i;
                 if (kVec) {
-                    // past H (ragged last block): an offset beyond the view reads zeros
-                    const uint32_t off = h < H ? (uint32_t)(row * H + h) * 2u : 0xFFFFFFF0u;
+                    const uint32_t off = (uint32_t)(row * H) * 2u + colo;
                     d[b][m][i] =
                         __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vres, (int)off, 0, kNT));
                 } else {
@@ -511,7 +511,7 @@ hipError_t launch_pre(const uint16_t *res, const float *hc_fn, const float *hc_s
         a.nhb = g.nhb;
         a.S = g.slices;
         a.rec = reinterpret_cast<float *>(ws + g.off_rec);
-        const dim3 pgrid((unsigned)(tiles * g.slices));
+        const dim3 pgrid((unsigned)tiles, (unsigned)g.slices);
         if (vec8) {
             pre_proj_kernel<true><<<pgrid, dim3(kPBlock), 0, stream>>>(a);
         } else {

@@ -205,7 +205,9 @@ def _check_pre(inp, got, tokens=None, what=""):
 # (T, H): tile edges (T = 1, 63..65, 129), ragged H (H % 32 != 0, H % 8 != 0), one slice
 # (H <= 128), many slices, and H above the fused kernel's range (split-K fallback path).
 PRE_SHAPES = [(16, 256), (1, 64), (3, 8), (100, 512), (65, 7168), (32, 7168), (40, 127), (24, 1001),
-              (129, 1536), (7, 16392), (70, 96), (63, 200), (130, 4104), (3, 65544), (2, 65537)]
+              (129, 1536), (7, 16392), (70, 96), (63, 200), (130, 4104), (3, 65544), (2, 65537),
+              # many 64-token tiles per workgroup (odd and even counts), H % 32 != 0
+              (1100, 2048), (600, 7000), (1537, 4104), (1030, 7168), (700, 8)]
 
 
 @pytest.mark.parametrize("T,H", PRE_SHAPES)
@@ -262,7 +264,7 @@ def test_pre_zero_scale_selects_stream():
 
 
 def test_pre_deterministic():
-    inp = layer_inputs(200, 2048, cfg=333)
+    inp = layer_inputs(1100, 2048, cfg=333)
     a, b = _run_pre(inp), _run_pre(inp)
     for u, v in zip(a[:4], b[:4]):
         assert np.array_equal(u, v)
