@@ -44,7 +44,6 @@ constexpr int kPNHB = 1;         // blocks per wave
 constexpr int kPSliceH = kPWaves * kPNHB * kPHB;
 constexpr int kRec = kMix + 1;                    // partial record fields: 24 dots + sum of squares
 constexpr int kFragPerHbStream = 3 * 64 + 3 * 32; // hi/mid/lo of column tile 0 (64 lanes) and 1 (32 lanes)
-constexpr int kNT = 2;                            // cache policy nt: streaming
 constexpr int kBufWord3 = 0x00020000;
 
 constexpr int kColBlock = 256;
@@ -158,7 +157,9 @@ __global__ __launch_bounds__(kPBlock, 2) void pre_proj_kernel(ProjArgs a)
     const int t0 = tile * kPTok;
     const int ntok = min(kPTok, a.T - t0);
 
-    // ---------------- load the slice (buffer loads: rows past T read as zero)
+    // ---------------- load the slice (buffer loads: rows past T read as zero).
+    // Plain cached loads, not non-temporal: each 128-byte line is read in two 64-byte
+    // halves by neighbouring waves, and the collapse re-reads the same streams soon after.
     u32x4 d[kPNHB][kPMT][kHC];
     const __amdgpu_buffer_rsrc_t vres =
         buf_view(a.res + (size_t)t0 * kHC * H, (uint32_t)((size_t)ntok * kHC * H * sizeof(uint16_t)));
@@ -177,7 +178,7 @@ __global__ __launch_bounds__(kPBlock, 2) void pre_proj_kernel(ProjArgs a)
                 if (kVec) {
                     const uint32_t off = (uint32_t)(row * H) * 2u + colo;
                     d[b][m][i] =
-                        __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vres, (int)off, 0, kNT));
+                        __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vres, (int)off, 0, 0));
                 } else {
                     u32x4 v = {0u, 0u, 0u, 0u};
                     if (m * 16 + c < ntok) {
