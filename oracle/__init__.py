@@ -56,8 +56,9 @@ def _load():
     lib.orc_collapse.argtypes = [P, P, I64, I64, P]
     lib.orc_post.argtypes = [P, P, P, P, I64, I64, P]
     lib.orc_pre.argtypes = [P, P, P, P, I64, I64, D, D, D, D, ctypes.c_int, P, P, P, P, P, P]
+    lib.orc_pre_from_dots.argtypes = [P, P, I64, P, P, P, I64, I64, D, D, D, D, D, ctypes.c_int, P, P, P, P]
     for f in ("orc_round_bf16", "orc_rms", "orc_project", "orc_mix_activation", "orc_sinkhorn",
-              "orc_collapse", "orc_post", "orc_pre"):
+              "orc_collapse", "orc_post", "orc_pre", "orc_pre_from_dots"):
         getattr(lib, f).restype = None
     _lib = lib
     return lib
@@ -168,3 +169,31 @@ def pre(res, hc_fn, hc_scale, hc_base, rms_eps=1e-6, pre_eps=1e-6, sinkhorn_eps=
     _load().orc_pre(_p(res), _p(hc_fn), _p(hc_scale), _p(hc_base), T, H, rms_eps, pre_eps, sinkhorn_eps,
                     post_mult, int(num_iters), _p(y), _p(post_), _p(comb), _p(pre_), _p(dot), _p(rstd))
     return dict(y=y, post=post_, comb=comb, pre=pre_, dot=dot, rstd=rstd)
+
+
+def pre_from_dots(dot_mix, res, hc_scale, hc_base, sqrsum=None, k=None, rms_eps=1e-6, pre_eps=1e-6,
+                  sinkhorn_eps=1e-6, post_mult=1.0, num_iters=20):
+    """Pre-map from an external projection.  dot_mix [T,24] or [S,T,24] fp32, sqrsum None, [T] or [S,T]
+    fp32, k the RMS denominator (default 4H).  Returns dict of fp64 arrays: y, post, comb, pre."""
+    res = _c(res, np.uint16)
+    T, hc, H = res.shape
+    assert hc == HC
+    dm = _c(dot_mix, np.float32)
+    if dm.ndim == 2:
+        dm = dm.reshape(1, T, MIX)
+    S = dm.shape[0]
+    assert dm.shape == (S, T, MIX)
+    sq = None
+    if sqrsum is not None:
+        sq = _c(sqrsum, np.float32).reshape(S, T)
+    k = float(HC * H) if k is None else float(k)
+    y = np.empty((T, H))
+    post_ = np.empty((T, HC))
+    comb = np.empty((T, HC, HC))
+    pre_ = np.empty((T, HC))
+    _load().orc_pre_from_dots(_p(dm), _p(sq) if sq is not None else None, S, _p(res),
+                              _p(_c(hc_scale, np.float32)), _p(_c(hc_base, np.float32)), T, H, k, rms_eps,
+                              pre_eps, sinkhorn_eps, post_mult, int(num_iters), _p(y), _p(post_), _p(comb),
+                              _p(pre_))
+    return dict(y=y, post=post_, comb=comb, pre=pre_)
+

@@ -270,3 +270,44 @@ void orc_pre(const uint16_t *res, const float *hc_fn, const float *hc_scale, con
         }
     }
 }
+
+/* The pre-map from an external projection (FlashInfer mHC article, section 3.1
+ * to 3.3, mhc_pre_big_fuse: the dots arrive as input, optionally as num_splits
+ * partial sums over split K; section 4, mhc_pre_big_fuse_with_prenorm: the sum of
+ * squares is computed from the residual streams when it is not supplied):
+ *   d[r]  = sum over splits s of dot_mix[s][t][r]
+ *   S     = sum over splits of sqrsum[s][t], or sum_{i,h} res[t][i][h]^2 when sqrsum is NULL
+ *   rstd  = 1 / sqrt(S / k + rms_eps)
+ * then A3 -> A4 -> A5 exactly as in orc_pre.  dot_mix is [S][T][24] and sqrsum
+ * [S][T], fp32. */
+void orc_pre_from_dots(const float *dot_mix, const float *sqrsum, int64_t num_splits, const uint16_t *res,
+                       const float *hc_scale, const float *hc_base, int64_t T, int64_t H, double k, double rms_eps,
+                       double pre_eps, double sinkhorn_eps, double post_mult, int num_iters, double *y, double *post,
+                       double *comb, double *pre)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        const uint16_t *r = res + t * ORC_HC * H;
+        double dot[ORC_MIX], logits[ORC_HC * ORC_HC], S = 0.0;
+        for (int64_t c = 0; c < ORC_MIX; ++c) {
+            double acc = 0.0;
+            for (int64_t sp = 0; sp < num_splits; ++sp) {
+                acc += (double)dot_mix[(sp * T + t) * ORC_MIX + c];
+            }
+            dot[c] = acc;
+        }
+        if (sqrsum) {
+            for (int64_t sp = 0; sp < num_splits; ++sp) {
+                S += (double)sqrsum[sp * T + t];
+            }
+        } else {
+            double rstd_unused;
+            orc_rms(r, 1, H, rms_eps, &S, &rstd_unused); /* S = the sum of squares */
+        }
+        const double rstd = 1.0 / sqrt(S / k + rms_eps);
+        orc_mix_activation(dot, &rstd, hc_scale, hc_base, 1, pre_eps, post_mult, pre + t * ORC_HC,
+                           post + t * ORC_HC, logits);
+        orc_sinkhorn(logits, 1, num_iters, sinkhorn_eps, comb + t * ORC_HC * ORC_HC);
+        orc_collapse(r, pre + t * ORC_HC, 1, H, y + t * H);
+    }
+}
+

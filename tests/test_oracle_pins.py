@@ -372,3 +372,74 @@ def test_sinkhorn_subtracts_row_max_before_exp():
     out = oracle.sinkhorn(L, 20, 1e-6)
     assert np.all(np.isfinite(out))
     assert np.allclose(out, _sk_scaling(L, 20, 1e-6), atol=1e-13)
+
+
+# ---------------------------------------------------------------- pre-map from an external projection
+
+def _dots_f32(inp):
+    """fp32 dots from numpy's matmul on the row-major flatten (independent of the oracle)."""
+    r = _bf16_f64(inp.res)
+    T, _, H = r.shape
+    return (r.reshape(T, HC * H) @ inp.hc_fn.astype(np.float64).T).astype(np.float32)
+
+
+def test_pre_from_dots_matches_independent_composition():
+    """dots computed outside + sum of squares computed inside == the whole pre-map (FI sections 3 and 4)."""
+    inp = layer_inputs(12, 96, cfg=120)
+    y, post, comb, pre = _pre_numpy(inp)
+    o = oracle.pre_from_dots(_dots_f32(inp), inp.res, inp.hc_scale, inp.hc_base)
+    # the only difference is the fp32 rounding of the dots (relative 2^-24 of |dot| <= ~1)
+    assert np.abs(o["pre"] - pre).max() < 1e-7
+    assert np.abs(o["post"] - post).max() < 1e-7
+    assert np.abs(o["comb"] - comb).max() < 1e-6
+    assert np.abs(o["y"] - y).max() < 1e-6
+
+
+def test_pre_from_dots_split_partials_are_summed():
+    inp = layer_inputs(9, 64, cfg=121)
+    d = _dots_f32(inp)
+    one = oracle.pre_from_dots(d, inp.res, inp.hc_scale, inp.hc_base)
+    # four equal quarters sum back exactly (power-of-two scaling, fp64 accumulation)
+    four = oracle.pre_from_dots(np.stack([d / 4] * 4), inp.res, inp.hc_scale, inp.hc_base)
+    for key in ("y", "post", "comb", "pre"):
+        assert np.array_equal(one[key], four[key]), key
+    # an uneven partition agrees up to fp64 rounding
+    g = np.random.default_rng(5)
+    parts = g.standard_normal((3,) + d.shape).astype(np.float32)
+    parts[2] = (d.astype(np.float64) - parts[0] - parts[1]).astype(np.float32)
+    exact = parts.astype(np.float64).sum(axis=0).astype(np.float32)
+    a = oracle.pre_from_dots(parts, inp.res, inp.hc_scale, inp.hc_base)
+    b = oracle.pre_from_dots(exact, inp.res, inp.hc_scale, inp.hc_base)
+    assert np.abs(a["comb"] - b["comb"]).max() < 1e-6 and np.abs(a["pre"] - b["pre"]).max() < 1e-7
+
+
+def test_pre_from_dots_supplied_sum_of_squares_and_denominator():
+    inp = layer_inputs(7, 32, cfg=122)
+    d = _dots_f32(inp)
+    r = _bf16_f64(inp.res)
+    S = (r * r).sum(axis=(1, 2))
+    inside = oracle.pre_from_dots(d, inp.res, inp.hc_scale, inp.hc_base)
+    given = oracle.pre_from_dots(d, inp.res, inp.hc_scale, inp.hc_base, sqrsum=S.astype(np.float32))
+    assert np.abs(inside["pre"] - given["pre"]).max() < 1e-7
+    # S and k scaled together by 4: rstd, hence every output, is unchanged bit for bit
+    s4 = oracle.pre_from_dots(np.stack([d, d * 0]), inp.res, inp.hc_scale, inp.hc_base,
+                              sqrsum=np.stack([S * 4, S * 0]).astype(np.float32), k=4 * HC * 32)
+    s1 = oracle.pre_from_dots(d, inp.res, inp.hc_scale, inp.hc_base, sqrsum=S.astype(np.float32))
+    for key in ("y", "post", "comb", "pre"):
+        assert np.array_equal(s1[key], s4[key]), key
+
+
+def test_pre_from_dots_rms_denominator_closed_form():
+    """S = 3k gives rstd = 1/sqrt(3 + eps): the pre weight is sigmoid(d * rstd * s0 + b) + pre_eps."""
+    T, H = 2, 16
+    res = np.zeros((T, HC, H), np.uint16)
+    d = np.zeros((T, MIX), np.float32)
+    d[:, 0] = [1.5, -2.0]
+    k = 1000.0
+    sq = np.full(T, 3 * k, np.float32)
+    o = oracle.pre_from_dots(d, res, np.array([2.0, 1.0, 1.0], np.float32), np.zeros(MIX, np.float32),
+                             sqrsum=sq, k=k, rms_eps=0.25, pre_eps=0.0)
+    rstd = 1 / np.sqrt(3.25)
+    expect = 1 / (1 + np.exp(-(d[:, 0].astype(np.float64) * rstd * 2.0)))
+    assert np.allclose(o["pre"][:, 0], expect, rtol=0, atol=1e-15)
+    assert np.allclose(o["pre"][:, 1:], 0.5, rtol=0, atol=0)
