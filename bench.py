@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="layer_h7168", choices=sorted(WORKLOADS))
-    ap.add_argument("--only", default="all", choices=["all", "pre", "post", "sinkhorn"],
+    ap.add_argument("--only", default="all", choices=["all", "pre", "post", "sinkhorn", "pre_dots"],
                     help="run only one call in the timed loop (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
@@ -66,8 +66,8 @@ def main():
     import torch
 
     import mhc_hyper_connection_amd as mhc
-    from mhc_inputs import (algorithmic_bytes_post, algorithmic_bytes_pre, algorithmic_bytes_sinkhorn, layer_inputs,
-                            sinkhorn_logits)
+    from mhc_inputs import (algorithmic_bytes_post, algorithmic_bytes_pre, algorithmic_bytes_pre_dots,
+                            algorithmic_bytes_sinkhorn, layer_inputs, sinkhorn_logits)
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
@@ -106,6 +106,17 @@ def main():
     def call_post():
         mhc.mhc_post(x, res, post, comb, out=out)
 
+    dots = None
+    if args.only == "pre_dots":
+        # external projection logits of a realistic spread (|dot| ~ 0.02 * sqrt(4H)), one split,
+        # the sum of squares computed from the streams
+        g = np.random.default_rng(11)
+        dots = torch.from_numpy((g.standard_normal((T, 24)) * 0.02 * math.sqrt(4 * H)).astype(np.float32)).to(dev)
+
+    def call_pre_dots():
+        mhc.mhc_pre_from_dots(dots, res, hc_scale, hc_base, None, None, p["rms_eps"], p["pre_eps"],
+                              p["sinkhorn_eps"], p["post_mult"], p["num_iters"], y=y, post=post, comb=comb)
+
     def call_sinkhorn():
         mhc.mhc_sinkhorn(sk_logits, out=sk_out, num_iters=p["num_iters"], eps=p["sinkhorn_eps"])
 
@@ -116,6 +127,8 @@ def main():
             call_post()
         if args.only == "sinkhorn":
             call_sinkhorn()
+        if args.only == "pre_dots":
+            call_pre_dots()
 
     stream = torch.cuda.current_stream(dev)
 
@@ -149,9 +162,13 @@ def main():
         breakdown["post_ms"] = timed(call_post, max(args.steps, 1))
     if args.only == "sinkhorn":
         breakdown["sinkhorn_ms"] = ms_step
+    if args.only == "pre_dots":
+        breakdown["pre_dots_ms"] = ms_step
 
     if args.only == "sinkhorn":
         step_bytes = algorithmic_bytes_sinkhorn(sk_logits.shape[0])
+    elif args.only == "pre_dots":
+        step_bytes = algorithmic_bytes_pre_dots(T, H)
     else:
         step_bytes = (pre_b if args.only in ("all", "pre") else 0) + (post_b if args.only in ("all", "post") else 0)
     eff_gbps = step_bytes / (ms_step * 1e-3) / 1e9
@@ -167,6 +184,8 @@ def main():
         calls["mhc_post"] = ("post_vec8_kernel" if H % 8 == 0 else "post_scalar_kernel", breakdown["post_ms"], post_b)
     if "sinkhorn_ms" in breakdown:
         calls["mhc_sinkhorn"] = ("sinkhorn_kernel", breakdown["sinkhorn_ms"], step_bytes)
+    if "pre_dots_ms" in breakdown:
+        calls["mhc_pre_from_dots"] = ("pre_dots_kernel", breakdown["pre_dots_ms"], step_bytes)
     traffic = load_traffic(T, H)
     per_call = {}
     for name, (kern, ms_k, bytes_k) in calls.items():

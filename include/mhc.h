@@ -121,6 +121,34 @@ mhc_status mhc_pre_fused(const uint16_t *res, const float *hc_fn, const float *h
                          size_t workspace_bytes, void *stream);
 
 /*
+ * mhc_pre_from_dots -- the mHC pre-map from an external projection (FlashInfer mHC
+ * article, sections 3.1-3.3, mhc_pre_big_fuse, where the 24 dots and the sum of
+ * squares come from outside, optionally as split-K partial sums; section 4,
+ * mhc_pre_big_fuse_with_prenorm, where the sum of squares is computed from the
+ * streams):
+ *     d[t][r]  = sum over s < num_splits of dot_mix[s][t][r]          (in split order)
+ *     S_t      = sum over s of sqrsum[s][t], or sum_{i,h} res[t][i][h]^2 when sqrsum is NULL
+ *     rstd_t   = 1 / sqrt(S_t / k + rms_eps)
+ *     m_t[r]   = d[t][r] * rstd_t, then pre, post, comb and y exactly as in mhc_pre_fused
+ *
+ *   dot_mix     [num_splits, T, 24] fp32, device
+ *   sqrsum      [num_splits, T] fp32, device, or NULL
+ *   num_splits  1 <= num_splits <= 65536
+ *   res, hc_scale, hc_base   as in mhc_pre_fused
+ *   T >= 0, H >= 1
+ *   k           the RMS denominator (4H for the pre-map proper), finite and > 0
+ *   rms_eps, pre_eps, sinkhorn_eps, post_mult, num_iters   as in mhc_pre_fused
+ *   y [T,H], post [T,4], comb [T,4,4], pre [T,4] (nullable)   outputs, device; no output
+ *               may overlap an input or another output
+ * No workspace: the streams of a token are read once, into registers, when rows are
+ * 16-byte aligned and H is a multiple of 8 up to 16384; other shapes read them twice.
+ */
+mhc_status mhc_pre_from_dots(const float *dot_mix, const float *sqrsum, int32_t num_splits, const uint16_t *res,
+                             const float *hc_scale, const float *hc_base, int64_t T, int64_t H, float k,
+                             float rms_eps, float pre_eps, float sinkhorn_eps, float post_mult, int32_t num_iters,
+                             uint16_t *y, float *post, float *comb, float *pre, void *stream);
+
+/*
  * mhc_post -- the mHC post-map (FlashInfer mHC article, section 2.1; metrale
  * glm5next_mhc.rs, glm_hc_post):
  *     out[t][n][h] = bf16( x[t][h] * post[t][n] + sum_o res[t][o][h] * comb[t][o][n] )

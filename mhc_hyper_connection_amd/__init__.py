@@ -56,6 +56,8 @@ def lib() -> ctypes.CDLL:
     L.mhc_pre_fused.restype = ctypes.c_int
     L.mhc_post.argtypes = [P, P, P, P, I64, I64, P, P]
     L.mhc_post.restype = ctypes.c_int
+    L.mhc_pre_from_dots.argtypes = [P, P, I32, P, P, P, I64, I64, F, F, F, F, F, I32, P, P, P, P, P]
+    L.mhc_pre_from_dots.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -173,6 +175,66 @@ def mhc_pre_fused(res: torch.Tensor, hc_fn: torch.Tensor, hc_scale: torch.Tensor
     return y, post, comb
 
 
+def mhc_pre_from_dots(dot_mix: torch.Tensor, res: torch.Tensor, hc_scale: torch.Tensor, hc_base: torch.Tensor,
+                      sqrsum: torch.Tensor | None = None, k: float | None = None, rms_eps: float = 1e-6,
+                      pre_eps: float = 1e-6, sinkhorn_eps: float = 1e-6, post_mult: float = 1.0,
+                      num_iters: int = 20, *, y=None, post=None, comb=None, pre=None, return_pre: bool = False):
+    """The pre-map from an external projection.  dot_mix [..., 24] or [splits, ..., 24] fp32, res [..., 4, H]
+    bf16, sqrsum None (computed from res), [...] or [splits, ...] fp32, k the RMS denominator (default 4H)
+    -> (y [..., H], post [..., 4], comb [..., 4, 4] [, pre [..., 4]])."""
+    _need(res, "res", torch.bfloat16)
+    if res.dim() < 2 or res.shape[-2] != HC:
+        raise ValueError(f"res must be [..., 4, H], got {tuple(res.shape)}")
+    H = res.shape[-1]
+    outer = tuple(res.shape[:-2])
+    T = res.numel() // (HC * H) if H > 0 else 0
+    _need(dot_mix, "dot_mix", torch.float32)
+    if tuple(dot_mix.shape) == outer + (MIX,):
+        splits = 1
+    elif dot_mix.dim() == len(outer) + 2 and tuple(dot_mix.shape[1:]) == outer + (MIX,):
+        splits = dot_mix.shape[0]
+    else:
+        raise ValueError(f"dot_mix must be {outer + (MIX,)} or [splits, *{outer + (MIX,)}], "
+                         f"got {tuple(dot_mix.shape)}")
+    if sqrsum is not None:
+        _need(sqrsum, "sqrsum", torch.float32)
+        if sqrsum.numel() != splits * T:
+            raise ValueError(f"sqrsum must hold [splits, T] = [{splits}, {T}] values")
+    _need(hc_scale, "hc_scale", torch.float32)
+    if tuple(hc_scale.shape) != (3,):
+        raise ValueError("hc_scale must be [3] (pre, post, comb)")
+    _need(hc_base, "hc_base", torch.float32)
+    if tuple(hc_base.shape) != (MIX,):
+        raise ValueError("hc_base must be [24]")
+    dev = res.device
+    if y is None:
+        y = torch.empty(outer + (H,), dtype=torch.bfloat16, device=dev)
+    if post is None:
+        post = torch.empty(outer + (HC,), dtype=torch.float32, device=dev)
+    if comb is None:
+        comb = torch.empty(outer + (HC, HC), dtype=torch.float32, device=dev)
+    if pre is None and return_pre:
+        pre = torch.empty(outer + (HC,), dtype=torch.float32, device=dev)
+    _need(y, "y", torch.bfloat16)
+    _need(post, "post", torch.float32)
+    _need(comb, "comb", torch.float32)
+    if y.numel() != T * H or post.numel() != T * HC or comb.numel() != T * HC * HC:
+        raise ValueError("output sizes do not match res")
+    if pre is not None:
+        _need(pre, "pre", torch.float32)
+        if pre.numel() != T * HC:
+            raise ValueError("pre must hold [T, 4] values")
+    _same_device(dot_mix, sqrsum, res, hc_scale, hc_base, y, post, comb, pre)
+    kk = float(HC * H) if k is None else float(k)
+    _check("mhc_pre_from_dots", lib().mhc_pre_from_dots(
+        _ptr(dot_mix), _ptr(sqrsum), int(splits), _ptr(res), _ptr(hc_scale), _ptr(hc_base), T, H, kk,
+        float(rms_eps), float(pre_eps), float(sinkhorn_eps), float(post_mult), int(num_iters), _ptr(y), _ptr(post),
+        _ptr(comb), _ptr(pre), _stream(dev)))
+    if return_pre:
+        return y, post, comb, pre
+    return y, post, comb
+
+
 def mhc_post(x: torch.Tensor, res: torch.Tensor, post: torch.Tensor, comb: torch.Tensor,
              out: torch.Tensor | None = None) -> torch.Tensor:
     """The post-map.  x [..., H] bf16, res [..., 4, H] bf16, post [..., 4] or [..., 4, 1] fp32,
@@ -203,5 +265,6 @@ def mhc_post(x: torch.Tensor, res: torch.Tensor, post: torch.Tensor, comb: torch
     return out
 
 
-__all__ = ["mhc_sinkhorn", "mhc_pre_fused", "mhc_pre_fused_workspace_bytes", "mhc_post", "lib", "abi_version",
+__all__ = ["mhc_sinkhorn", "mhc_pre_fused", "mhc_pre_fused_workspace_bytes", "mhc_pre_from_dots", "mhc_post", "lib",
+           "abi_version",
            "status_string", "MHCError", "HC", "MIX"]

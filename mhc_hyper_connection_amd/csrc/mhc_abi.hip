@@ -133,6 +133,47 @@ mhc_status mhc_pre_fused(const uint16_t *res, const float *hc_fn, const float *h
                                          vec8));
 }
 
+mhc_status mhc_pre_from_dots(const float *dot_mix, const float *sqrsum, int32_t num_splits, const uint16_t *res,
+                             const float *hc_scale, const float *hc_base, int64_t T, int64_t H, float k,
+                             float rms_eps, float pre_eps, float sinkhorn_eps, float post_mult, int32_t num_iters,
+                             uint16_t *y, float *post, float *comb, float *pre, void *stream)
+{
+    if (!sizes_ok(T, H) || num_splits < 1 || num_splits > 65536 || num_iters < 1 || !finite(k) || !(k > 0.0f) ||
+        !finite(rms_eps) || !(rms_eps > 0.0f) || !finite(pre_eps) || pre_eps < 0.0f || !finite(sinkhorn_eps) ||
+        !(sinkhorn_eps > 0.0f) || !finite(post_mult)) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    if (T == 0) {
+        return MHC_SUCCESS;
+    }
+    if (!dot_mix || !res || !hc_scale || !hc_base || !y || !post || !comb) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    const size_t res_b = (size_t)T * 4 * H * 2, y_b = (size_t)T * H * 2;
+    const size_t post_b = (size_t)T * 4 * 4, comb_b = (size_t)T * 16 * 4, pre_b = pre ? (size_t)T * 4 * 4 : 0;
+    const size_t dm_b = (size_t)num_splits * T * 24 * 4, sq_b = sqrsum ? (size_t)num_splits * T * 4 : 0;
+    const void *outs[4] = {y, post, comb, pre};
+    const size_t outn[4] = {y_b, post_b, comb_b, pre_b};
+    const void *ins[5] = {res, dot_mix, sqrsum, hc_scale, hc_base};
+    const size_t inn[5] = {res_b, dm_b, sq_b, 3 * 4, 24 * 4};
+    for (int o = 0; o < 4; ++o) {
+        for (int i = 0; i < 5; ++i) {
+            if (overlaps(outs[o], outn[o], ins[i], inn[i])) {
+                return MHC_ERROR_INVALID_VALUE;
+            }
+        }
+        for (int o2 = o + 1; o2 < 4; ++o2) {
+            if (overlaps(outs[o], outn[o], outs[o2], outn[o2])) {
+                return MHC_ERROR_INVALID_VALUE;
+            }
+        }
+    }
+    const bool vec8 = (H % 8 == 0) && aligned16(res) && aligned16(y);
+    return launch_status(mhc::launch_pre_dots(dot_mix, sqrsum, num_splits, res, hc_scale, hc_base, T, H, k, rms_eps,
+                                              pre_eps, sinkhorn_eps, post_mult, num_iters, y, post, comb, pre,
+                                              (hipStream_t)stream, vec8));
+}
+
 mhc_status mhc_post(const uint16_t *x, const uint16_t *res, const float *post, const float *comb, int64_t T,
                     int64_t H, uint16_t *out, void *stream)
 {

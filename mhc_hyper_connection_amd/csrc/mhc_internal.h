@@ -36,4 +36,11 @@ hipError_t launch_pre(const uint16_t *res, const float *hc_fn, const float *hc_s
                       int iters, uint16_t *y, float *post, float *comb, float *pre, void *workspace,
                       hipStream_t stream, bool vec8);
 
+// Pre-map from external dots (one workgroup per token).  `vec8`: H % 8 == 0 and res/y
+// 16-byte aligned.
+hipError_t launch_pre_dots(const float *dot_mix, const float *sqrsum, int num_splits, const uint16_t *res,
+                           const float *hc_scale, const float *hc_base, int64_t T, int64_t H, float k,
+                           float rms_eps, float pre_eps, float sinkhorn_eps, float post_mult, int iters,
+                           uint16_t *y, float *post, float *comb, float *pre, hipStream_t stream, bool vec8);
+
 } // namespace mhc

@@ -1,0 +1,279 @@
+// mhc_pre_dots.hip -- the mHC pre-map from an external projection.
+//
+// ("FlashInfer mHC 模块深度解析", sections 3.1-3.4, mhc_pre_big_fuse: the 24 dots
+// come from outside, possibly as split-K partial sums; section 4,
+// mhc_pre_big_fuse_with_prenorm: the sum of squares is computed here from the
+// streams when the caller does not supply it.)
+//
+// One 256-thread workgroup per token.  On the 16-byte path each thread holds its
+// 8-element chunks of all 4 streams in VGPRs, so the streams are read from HBM
+// once: the sum of squares (when needed), the mixes and the collapse all use the
+// same registers.  Wavefront 0 sums the dot partials in split order, computes rstd
+// and the pre weights, and after the collapse the post weights and the 4x4
+// Sinkhorn of comb, one matrix entry per lane of a 16-lane row.
+#include "mhc_device.h"
+#include "mhc_internal.h"
+
+namespace mhc {
+
+namespace {
+
+constexpr int kDBlock = 256;
+constexpr int kDWaves = kDBlock / kWave;
+
+struct DotsArgs {
+    const float *dot_mix; // [S][T][24]
+    const float *sqrsum;  // [S][T], or null: computed from res
+    int S;
+    const uint16_t *res;
+    const float *hc_scale;
+    const float *hc_base;
+    int T, H;
+    float k, rms_eps, pre_eps, sk_eps, post_mult;
+    int iters;
+    uint16_t *y;
+    float *post, *comb, *pre_out;
+};
+
+__device__ __forceinline__ float dpp_quad_xor1(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_quad_xor2(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_row_ror4(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x124, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_row_ror8(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x128, 0xF, 0xF, false));
+}
+
+// Fixed-count Sinkhorn of a 4x4 matrix spread over a 16-lane row (lane e holds entry
+// (e / 4, e % 4)): row softmax (row maximum subtracted) plus eps, then `iters` rounds
+// of row then column normalisation.  Row sums combine the lane's quad; column sums
+// the lanes e, e +- 4, e +- 8 (rotations within the row).
+__device__ __forceinline__ float sinkhorn_row16(float L, int iters, float eps)
+{
+    float mx = fmaxf(L, dpp_quad_xor1(L));
+    mx = fmaxf(mx, dpp_quad_xor2(mx));
+    const float e = __expf(L - mx);
+    float s = e + dpp_quad_xor1(e);
+    s = s + dpp_quad_xor2(s);
+    float P = fmaf(e, fast_rcp(s), eps);
+    for (int it = 0; it < iters; ++it) {
+        float rs = P + dpp_quad_xor1(P);
+        rs = rs + dpp_quad_xor2(rs);
+        P *= fast_rcp(rs);
+        float cs = P + dpp_row_ror4(P);
+        cs = cs + dpp_row_ror8(cs);
+        P *= fast_rcp(cs);
+    }
+    return P;
+}
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        v += __shfl_xor(v, o);
+    }
+    return v;
+}
+
+// kCPT > 0: 16-byte path, kCPT chunks of 8 elements per thread and stream in VGPRs.
+// kCPT == 0: any H and alignment, two scalar passes over the token's streams.
+template <int kCPT>
+__global__ __launch_bounds__(kDBlock) void pre_dots_kernel(DotsArgs a)
+{
+    __shared__ float wsum[kDWaves];
+    __shared__ float dsum[kMix];
+    __shared__ float prew[kHC];
+    __shared__ float rstd_s;
+
+    const int t = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int w = uniform(tid >> 6);
+    const int lane = tid & (kWave - 1);
+    const int H = a.H;
+    const uint16_t *row = a.res + (size_t)t * kHC * H;
+    const bool need_sq = a.sqrsum == nullptr;
+
+    // the dots of this token, summed over the splits in split order
+    float dv = 0.0f;
+    if (w == 0 && lane < kMix) {
+        for (int s = 0; s < a.S; ++s) {
+            dv += a.dot_mix[((size_t)s * a.T + t) * kMix + lane];
+        }
+    }
+
+    float sq = 0.0f;
+    u32x4 r[kHC][kCPT > 0 ? kCPT : 1];
+    if constexpr (kCPT > 0) {
+        const int nch = H >> 3;
+#pragma unroll
+        for (int k = 0; k < kCPT; ++k) {
+            const int j = tid + k * kDBlock;
+#pragma unroll
+            for (int i = 0; i < kHC; ++i) {
+                r[i][k] = j < nch ? load16(row + (size_t)i * H + (size_t)j * 8) : u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+        if (need_sq) {
+#pragma unroll
+            for (int k = 0; k < kCPT; ++k) {
+#pragma unroll
+                for (int i = 0; i < kHC; ++i) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        // Copy to a scalar first: hipcc (clang 22) miscompiles __builtin_bit_cast
+                        // applied directly to an ext_vector element (it reads element 0 for every q).
+                        const uint32_t wq = r[i][k][q];
+                        const bf16x2 pr = __builtin_bit_cast(bf16x2, wq);
+                        sq = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, sq, false);
+                    }
+                }
+            }
+        }
+    } else {
+        if (need_sq) {
+            for (int h = tid; h < H; h += kDBlock) {
+#pragma unroll
+                for (int i = 0; i < kHC; ++i) {
+                    const float v = bf16_to_f32(row[(size_t)i * H + h]);
+                    sq = fmaf(v, v, sq);
+                }
+            }
+        }
+    }
+    if (need_sq) {
+        sq = wave_sum(sq);
+        if (lane == 0) {
+            wsum[w] = sq;
+        }
+    }
+    if (w == 0 && lane < kMix) {
+        dsum[lane] = dv;
+    }
+    __syncthreads();
+
+    // rstd and the pre weights (wavefront 0)
+    if (w == 0) {
+        float S = 0.0f;
+        if (need_sq) {
+            S = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+        } else {
+            for (int s = 0; s < a.S; ++s) {
+                S += a.sqrsum[(size_t)s * a.T + t];
+            }
+        }
+        const float rstd = 1.0f / sqrtf(S / a.k + a.rms_eps);
+        if (lane < kHC) {
+            prew[lane] = sigmoidf_fast(fmaf(dsum[lane] * rstd, a.hc_scale[0], a.hc_base[lane])) + a.pre_eps;
+        }
+        if (lane == 0) {
+            rstd_s = rstd;
+        }
+    }
+    __syncthreads();
+    const float p0 = prew[0], p1 = prew[1], p2 = prew[2], p3 = prew[3];
+
+    // collapse
+    uint16_t *yrow = a.y + (size_t)t * H;
+    if constexpr (kCPT > 0) {
+        const int nch = H >> 3;
+#pragma unroll
+        for (int k = 0; k < kCPT; ++k) {
+            const int j = tid + k * kDBlock;
+            if (j < nch) {
+                u32x4 yw;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float lo = bf16_lo(r[0][k][q]) * p0;
+                    float hi = bf16_hi(r[0][k][q]) * p0;
+                    lo = fmaf(bf16_lo(r[1][k][q]), p1, lo);
+                    hi = fmaf(bf16_hi(r[1][k][q]), p1, hi);
+                    lo = fmaf(bf16_lo(r[2][k][q]), p2, lo);
+                    hi = fmaf(bf16_hi(r[2][k][q]), p2, hi);
+                    lo = fmaf(bf16_lo(r[3][k][q]), p3, lo);
+                    hi = fmaf(bf16_hi(r[3][k][q]), p3, hi);
+                    yw[q] = pack_bf16x2(lo, hi);
+                }
+                store_nt16(yrow + (size_t)j * 8, yw);
+            }
+        }
+    } else {
+        for (int h = tid; h < H; h += kDBlock) {
+            float v = bf16_to_f32(row[h]) * p0;
+            v = fmaf(bf16_to_f32(row[(size_t)H + h]), p1, v);
+            v = fmaf(bf16_to_f32(row[(size_t)2 * H + h]), p2, v);
+            v = fmaf(bf16_to_f32(row[(size_t)3 * H + h]), p3, v);
+            yrow[h] = f32_to_bf16(v);
+        }
+    }
+
+    // post, comb and the optional pre output (wavefront 0)
+    if (w == 0) {
+        const float rstd = rstd_s;
+        const int e = lane & 15;
+        const float L = fmaf(dsum[2 * kHC + e] * rstd, a.hc_scale[2], a.hc_base[2 * kHC + e]);
+        const float P = sinkhorn_row16(L, a.iters, a.sk_eps);
+        if (lane < kHC * kHC) {
+            a.comb[(size_t)t * kHC * kHC + lane] = P;
+        }
+        if (lane < kHC) {
+            a.post[(size_t)t * kHC + lane] =
+                sigmoidf_fast(fmaf(dsum[kHC + lane] * rstd, a.hc_scale[1], a.hc_base[kHC + lane])) * a.post_mult;
+            if (a.pre_out) {
+                a.pre_out[(size_t)t * kHC + lane] = prew[lane];
+            }
+        }
+    }
+}
+
+} // namespace
+
+hipError_t launch_pre_dots(const float *dot_mix, const float *sqrsum, int num_splits, const uint16_t *res,
+                           const float *hc_scale, const float *hc_base, int64_t T, int64_t H, float k,
+                           float rms_eps, float pre_eps, float sinkhorn_eps, float post_mult, int iters,
+                           uint16_t *y, float *post, float *comb, float *pre, hipStream_t stream, bool vec8)
+{
+    DotsArgs a;
+    a.dot_mix = dot_mix;
+    a.sqrsum = sqrsum;
+    a.S = num_splits;
+    a.res = res;
+    a.hc_scale = hc_scale;
+    a.hc_base = hc_base;
+    a.T = (int)T;
+    a.H = (int)H;
+    a.k = k;
+    a.rms_eps = rms_eps;
+    a.pre_eps = pre_eps;
+    a.sk_eps = sinkhorn_eps;
+    a.post_mult = post_mult;
+    a.iters = iters;
+    a.y = y;
+    a.post = post;
+    a.comb = comb;
+    a.pre_out = pre;
+    const dim3 grid((unsigned)T), block(kDBlock);
+    const int64_t per = (H / 8 + kDBlock - 1) / kDBlock; // 16-byte chunks per thread and stream
+    if (vec8 && per <= 1) {
+        pre_dots_kernel<1><<<grid, block, 0, stream>>>(a);
+    } else if (vec8 && per <= 2) {
+        pre_dots_kernel<2><<<grid, block, 0, stream>>>(a);
+    } else if (vec8 && per <= 4) {
+        pre_dots_kernel<4><<<grid, block, 0, stream>>>(a);
+    } else if (vec8 && per <= 8) {
+        pre_dots_kernel<8><<<grid, block, 0, stream>>>(a);
+    } else {
+        pre_dots_kernel<0><<<grid, block, 0, stream>>>(a);
+    }
+    return hipGetLastError();
+}
+
+} // namespace mhc

@@ -176,5 +176,11 @@ def algorithmic_bytes_post(T: int, H: int) -> int:
     return T * (2 * H + 8 * H + 80 + 8 * H)
 
 
+def algorithmic_bytes_pre_dots(T: int, H: int, splits: int = 1, sqrsum: bool = False) -> int:
+    """Bytes the pre-map from external dots must move: the dot partials (and sum-of-squares
+    partials) read, res read, y written, post/comb written, scale/base read once."""
+    return T * (splits * 96 + (splits * 4 if sqrsum else 0) + 8 * H + 2 * H + 16 + 64) + 108
+
+
 def algorithmic_bytes_sinkhorn(n: int) -> int:
     return n * 64 * 2

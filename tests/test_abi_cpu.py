@@ -25,7 +25,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = mhc.lib()
     names = _declared()
-    assert {"mhc_sinkhorn", "mhc_pre_fused", "mhc_pre_fused_workspace_bytes", "mhc_post",
+    assert {"mhc_sinkhorn", "mhc_pre_fused", "mhc_pre_fused_workspace_bytes", "mhc_pre_from_dots", "mhc_post",
             "mhc_abi_version", "mhc_status_string"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -92,6 +92,34 @@ def test_pre_validation_workspace():
     assert _pre(lib, ws=None) == mhc.MHC_ERROR_WORKSPACE
     assert _pre(lib, ws=ctypes.c_void_p(0xC000000 + 8)) == mhc.MHC_ERROR_WORKSPACE  # not 256-byte aligned
     assert _pre(lib, T=0, res=None, y=None, ws=None) == mhc.MHC_SUCCESS  # empty: no-op
+
+
+def _dots(lib, **kw):
+    a = dict(dm=ctypes.c_void_p(0x1000000), sq=None, S=1, res=FAKE, sc=ctypes.c_void_p(0x8000000),
+             base=ctypes.c_void_p(0x8001000), T=16, H=256, k=1024.0, rms=1e-6, pe=1e-6, se=1e-6, pm=1.0, it=20,
+             y=ctypes.c_void_p(0x9000000), post=ctypes.c_void_p(0xA000000), comb=ctypes.c_void_p(0xB000000),
+             pre=None)
+    a.update(kw)
+    return lib.mhc_pre_from_dots(a["dm"], a["sq"], a["S"], a["res"], a["sc"], a["base"], a["T"], a["H"], a["k"],
+                                 a["rms"], a["pe"], a["se"], a["pm"], a["it"], a["y"], a["post"], a["comb"],
+                                 a["pre"], NULL)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(T=-1), dict(H=0), dict(S=0), dict(S=65537), dict(k=0.0), dict(k=float("inf")), dict(it=0),
+    dict(rms=0.0), dict(se=0.0), dict(pe=-1.0), dict(pm=float("nan")), dict(dm=None), dict(res=None),
+    dict(sc=None), dict(base=None), dict(y=None), dict(post=None), dict(comb=None),
+    dict(y=ctypes.c_void_p(0x10000 + 64)),                     # y overlaps res
+    dict(post=ctypes.c_void_p(0x1000000 + 32)),                # post overlaps dot_mix
+    dict(sq=ctypes.c_void_p(0xA000000 - 8), S=1),             # sqrsum overlaps post
+    dict(pre=ctypes.c_void_p(0xB000000 + 16)),                 # pre overlaps comb
+])
+def test_pre_from_dots_validation_invalid(kw):
+    assert _dots(mhc.lib(), **kw) == mhc.MHC_ERROR_INVALID_VALUE
+
+
+def test_pre_from_dots_empty_is_a_no_op():
+    assert _dots(mhc.lib(), T=0, dm=None, res=None, y=None, post=None, comb=None) == mhc.MHC_SUCCESS
 
 
 def test_post_validation():

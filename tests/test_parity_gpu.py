@@ -278,6 +278,112 @@ def test_pre_empty():
     assert y.shape == (0, 64) and post.shape == (0, 4) and comb.shape == (0, 4, 4)
 
 
+# ----------------------------------------------------------------------------- pre-map from external dots
+
+def _dots_inputs(inp, splits, cfg):
+    """fp32 dot partials: the exact fp64 projection, split into `splits` random parts (last part closes it)."""
+    d = oracle.project(inp.res, inp.hc_fn)
+    g = np.random.default_rng(cfg)
+    if splits == 1:
+        return d.astype(np.float32)[None]
+    parts = (g.standard_normal((splits - 1,) + d.shape) * 0.5).astype(np.float32)
+    last = (d - parts.astype(np.float64).sum(axis=0)).astype(np.float32)
+    return np.concatenate([parts, last[None]], axis=0)
+
+
+def _run_dots(inp, dm, sq=None, k=None, **kw):
+    mhc = _mhc()
+    p = dict(inp.params)
+    p.update(kw)
+    y, post, comb, pre = mhc.mhc_pre_from_dots(
+        to_dev_f32(dm), to_dev_bf16(inp.res), to_dev_f32(inp.hc_scale), to_dev_f32(inp.hc_base),
+        sqrsum=None if sq is None else to_dev_f32(sq), k=k, rms_eps=p["rms_eps"], pre_eps=p["pre_eps"],
+        sinkhorn_eps=p["sinkhorn_eps"], post_mult=p["post_mult"], num_iters=p["num_iters"], return_pre=True)
+    torch.cuda.synchronize()
+    ref = oracle.pre_from_dots(dm, inp.res, inp.hc_scale, inp.hc_base, sqrsum=sq, k=k, rms_eps=p["rms_eps"],
+                               pre_eps=p["pre_eps"], sinkhorn_eps=p["sinkhorn_eps"], post_mult=p["post_mult"],
+                               num_iters=p["num_iters"])
+    return (bits_of(y), f32_of(post), f32_of(comb), f32_of(pre)), ref
+
+
+def _check_dots(got, ref, what, tokens=None):
+    y, post, comb, pre = got
+    sel = (lambda a: a) if tokens is None else (lambda a: a[tokens])
+    assert_f32_close(sel(pre), sel(ref["pre"]), f"{what} pre")
+    assert_f32_close(sel(post), sel(ref["post"]), f"{what} post")
+    assert_f32_close(sel(comb), sel(ref["comb"]), f"{what} comb")
+    assert_bf16_close(sel(y), sel(ref["y"]), f"{what} y")
+
+
+# (T, H, splits): register path for 1, 2, 4 and 8 chunks per thread (H <= 2048, 4096, 8192, 16384), the
+# two-pass path (H % 8 != 0, H > 16384), one and several splits
+DOTS_SHAPES = [(16, 256, 1), (5, 8, 2), (33, 2048, 4), (9, 4096, 1), (7, 7168, 16), (3, 16384, 2),
+               (4, 16392, 1), (6, 127, 3), (5, 1001, 1), (2, 65537, 2), (70, 96, 8)]
+
+
+@pytest.mark.parametrize("T,H,splits", DOTS_SHAPES)
+def test_pre_from_dots_computed_sum_of_squares(T, H, splits):
+    inp = layer_inputs(T, H, cfg=400 + (T * 13 + H) % 71)
+    dm = _dots_inputs(inp, splits, cfg=T + H)
+    got, ref = _run_dots(inp, dm)
+    _check_dots(got, ref, f"dots T={T} H={H} S={splits}")
+
+
+@pytest.mark.parametrize("splits", [1, 4])
+def test_pre_from_dots_supplied_sum_of_squares_and_k(splits):
+    inp = layer_inputs(40, 1536, cfg=430)
+    dm = _dots_inputs(inp, splits, cfg=splits)
+    r = bf16_bits_to_f32(inp.res).astype(np.float64)
+    S = (r * r).sum(axis=(1, 2))
+    sq = np.stack([S / splits] * splits).astype(np.float32)
+    got, ref = _run_dots(inp, dm, sq=sq, k=2.0 * 4 * 1536, post_mult=2.0, num_iters=3)
+    _check_dots(got, ref, f"dots supplied S={splits}")
+
+
+def test_pre_from_dots_full_size_h7168_sampled():
+    """T=8192, H=7168 with one split and the sum of squares computed here (the measured launch)."""
+    mhc = _mhc()
+    inp = named_layer("layer_h7168")
+    toks = sample_tokens(inp.T, 32, seed=3)
+    d = np.zeros((inp.T, 24), np.float32)
+    d[toks] = oracle.project(inp.res[toks], inp.hc_fn).astype(np.float32)
+    y, post, comb, pre = mhc.mhc_pre_from_dots(to_dev_f32(d), to_dev_bf16(inp.res), to_dev_f32(inp.hc_scale),
+                                               to_dev_f32(inp.hc_base), return_pre=True)
+    torch.cuda.synchronize()
+    ref = oracle.pre_from_dots(d[toks], inp.res[toks], inp.hc_scale, inp.hc_base)
+    _check_dots((bits_of(y)[toks], f32_of(post)[toks], f32_of(comb)[toks], f32_of(pre)[toks]), ref,
+                "dots 8192x7168")
+    assert np.abs(f32_of(comb).sum(axis=-2) - 1).max() <= 1e-5
+
+
+def test_pre_from_dots_agrees_with_pre_fused():
+    """The external-projection path fed the projection of res gives the fused pre-map's outputs."""
+    mhc = _mhc()
+    inp = layer_inputs(64, 1024, cfg=431)
+    res = to_dev_bf16(inp.res)
+    fn, sc, base = to_dev_f32(inp.hc_fn), to_dev_f32(inp.hc_scale), to_dev_f32(inp.hc_base)
+    a = mhc.mhc_pre_fused(res, fn, sc, base, return_pre=True)
+    dm = torch.from_numpy(oracle.project(inp.res, inp.hc_fn).astype(np.float32)).cuda()
+    b = mhc.mhc_pre_from_dots(dm, res, sc, base, return_pre=True)
+    torch.cuda.synchronize()
+    for u, v, name in zip(a[1:], b[1:], ("post", "comb", "pre")):
+        assert np.abs(f32_of(u).astype(np.float64) - f32_of(v)).max() <= 2e-5, name
+
+
+def test_pre_from_dots_deterministic_and_empty():
+    mhc = _mhc()
+    inp = layer_inputs(50, 2048, cfg=432)
+    dm = _dots_inputs(inp, 2, cfg=1)
+    a, _ = _run_dots(inp, dm)
+    b, _ = _run_dots(inp, dm)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+    y, post, comb = mhc.mhc_pre_from_dots(torch.zeros(0, 24, device="cuda"),
+                                          torch.empty(0, 4, 64, dtype=torch.bfloat16, device="cuda"),
+                                          torch.ones(3, device="cuda"), torch.zeros(24, device="cuda"))
+    assert y.shape == (0, 64)
+
+
 # ----------------------------------------------------------------------------- whole layer
 
 def test_layer_pre_then_post_full_size_sampled():
