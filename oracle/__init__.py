@@ -57,8 +57,11 @@ def _load():
     lib.orc_post.argtypes = [P, P, P, P, I64, I64, P]
     lib.orc_pre.argtypes = [P, P, P, P, I64, I64, D, D, D, D, ctypes.c_int, P, P, P, P, P, P]
     lib.orc_pre_from_dots.argtypes = [P, P, I64, P, P, P, I64, I64, D, D, D, D, D, ctypes.c_int, P, P, P, P]
+    lib.orc_sinkhorn_backward.argtypes = [P, P, I64, ctypes.c_int, D, P]
+    lib.orc_post_backward.argtypes = [P, P, P, P, P, I64, I64, P, P, P, P]
     for f in ("orc_round_bf16", "orc_rms", "orc_project", "orc_mix_activation", "orc_sinkhorn",
-              "orc_collapse", "orc_post", "orc_pre", "orc_pre_from_dots"):
+              "orc_collapse", "orc_post", "orc_pre", "orc_pre_from_dots", "orc_sinkhorn_backward",
+              "orc_post_backward"):
         getattr(lib, f).restype = None
     _lib = lib
     return lib
@@ -196,4 +199,34 @@ def pre_from_dots(dot_mix, res, hc_scale, hc_base, sqrsum=None, k=None, rms_eps=
                               pre_eps, sinkhorn_eps, post_mult, int(num_iters), _p(y), _p(post_), _p(comb),
                               _p(pre_))
     return dict(y=y, post=post_, comb=comb, pre=pre_)
+
+
+def sinkhorn_backward(grad, logits, num_iters=20, eps=1e-6):
+    """d_logits [n,4,4] of the fixed-count Sinkhorn for the output gradient grad [n,4,4] (fp64)."""
+    g = _c(grad, np.float64)
+    lg = _c(logits, np.float64)
+    assert g.shape == lg.shape and lg.shape[-2:] == (HC, HC)
+    assert 1 <= int(num_iters) <= 1024
+    n = int(np.prod(lg.shape[:-2])) if lg.ndim > 2 else 1
+    out = np.empty(lg.shape)
+    _load().orc_sinkhorn_backward(_p(g), _p(lg), n, int(num_iters), eps, _p(out))
+    return out
+
+
+def post_backward(d_out, x, res, post, comb):
+    """Reverse mode of the post-map: (d_x [T,H], d_res [T,4,H], d_post [T,4], d_comb [T,4,4]), fp64."""
+    d_out = _c(d_out, np.uint16)
+    x = _c(x, np.uint16)
+    res = _c(res, np.uint16)
+    T, hc, H = res.shape
+    assert hc == HC and d_out.shape == res.shape and x.shape == (T, H)
+    post_ = _c(post, np.float64).reshape(T, HC)
+    comb = _c(comb, np.float64).reshape(T, HC, HC)
+    d_x = np.empty((T, H))
+    d_res = np.empty((T, HC, H))
+    d_post = np.empty((T, HC))
+    d_comb = np.empty((T, HC, HC))
+    _load().orc_post_backward(_p(d_out), _p(x), _p(res), _p(post_), _p(comb), T, H, _p(d_x), _p(d_res),
+                              _p(d_post), _p(d_comb))
+    return d_x, d_res, d_post, d_comb
 

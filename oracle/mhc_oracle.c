@@ -311,3 +311,152 @@ void orc_pre_from_dots(const float *dot_mix, const float *sqrsum, int64_t num_sp
     }
 }
 
+/* Reverse mode through the Sinkhorn steps of orc_sinkhorn (rwkv-ops mhu_jax.py,
+ * sinkhorn_knopp with its custom VJP SinkhornBwd: the gradient of the fixed-count
+ * iteration, not of its limit).  The forward is replayed keeping every
+ * intermediate matrix; then, from the last step back:
+ *   column step Q = A / c (c_j = sum_i A_ij):  dA_ij = (dQ_ij - sum_i' dQ_i'j Q_i'j) / c_j
+ *   row step    A = P / r (r_i = sum_j P_ij):  dP_ij = (dA_ij - sum_j' dA_ij' A_ij') / r_i
+ *   + eps:                                     dS = dP0
+ *   row softmax S = softmax(L):                dL_ij = S_ij (dS_ij - sum_j' dS_ij' S_ij')
+ * grad, logits and d_logits are [n, 4, 4]. */
+void orc_sinkhorn_backward(const double *grad, const double *logits, int64_t n, int num_iters, double eps,
+                           double *d_logits)
+{
+    for (int64_t b = 0; b < n; ++b) {
+        const double *L = logits + b * ORC_HC * ORC_HC;
+        /* hist[0] = softmax + eps; hist[2k-1] = after the k-th row step; hist[2k] = after the k-th column step */
+        double hist[2 * 1024 + 1][ORC_HC][ORC_HC];
+        double S[ORC_HC][ORC_HC];
+        if (num_iters > 1024) {
+            return;
+        }
+        for (int i = 0; i < ORC_HC; ++i) {
+            double mx = L[i * ORC_HC];
+            for (int j = 1; j < ORC_HC; ++j) {
+                mx = L[i * ORC_HC + j] > mx ? L[i * ORC_HC + j] : mx;
+            }
+            double s = 0.0;
+            for (int j = 0; j < ORC_HC; ++j) {
+                S[i][j] = exp(L[i * ORC_HC + j] - mx);
+                s += S[i][j];
+            }
+            for (int j = 0; j < ORC_HC; ++j) {
+                S[i][j] /= s;
+                hist[0][i][j] = S[i][j] + eps;
+            }
+        }
+        for (int k = 1; k <= num_iters; ++k) {
+            for (int i = 0; i < ORC_HC; ++i) {
+                double r = 0.0;
+                for (int j = 0; j < ORC_HC; ++j) {
+                    r += hist[2 * k - 2][i][j];
+                }
+                for (int j = 0; j < ORC_HC; ++j) {
+                    hist[2 * k - 1][i][j] = hist[2 * k - 2][i][j] / r;
+                }
+            }
+            for (int j = 0; j < ORC_HC; ++j) {
+                double c = 0.0;
+                for (int i = 0; i < ORC_HC; ++i) {
+                    c += hist[2 * k - 1][i][j];
+                }
+                for (int i = 0; i < ORC_HC; ++i) {
+                    hist[2 * k][i][j] = hist[2 * k - 1][i][j] / c;
+                }
+            }
+        }
+        double G[ORC_HC][ORC_HC];
+        for (int i = 0; i < ORC_HC; ++i) {
+            for (int j = 0; j < ORC_HC; ++j) {
+                G[i][j] = grad[b * ORC_HC * ORC_HC + i * ORC_HC + j];
+            }
+        }
+        for (int k = num_iters; k >= 1; --k) {
+            const double(*A)[ORC_HC] = hist[2 * k - 1];
+            const double(*Q)[ORC_HC] = hist[2 * k];
+            const double(*P)[ORC_HC] = hist[2 * k - 2];
+            double dA[ORC_HC][ORC_HC];
+            for (int j = 0; j < ORC_HC; ++j) {
+                double c = 0.0, gq = 0.0;
+                for (int i = 0; i < ORC_HC; ++i) {
+                    c += A[i][j];
+                    gq += G[i][j] * Q[i][j];
+                }
+                for (int i = 0; i < ORC_HC; ++i) {
+                    dA[i][j] = (G[i][j] - gq) / c;
+                }
+            }
+            for (int i = 0; i < ORC_HC; ++i) {
+                double r = 0.0, ga = 0.0;
+                for (int j = 0; j < ORC_HC; ++j) {
+                    r += P[i][j];
+                    ga += dA[i][j] * A[i][j];
+                }
+                for (int j = 0; j < ORC_HC; ++j) {
+                    G[i][j] = (dA[i][j] - ga) / r;
+                }
+            }
+        }
+        for (int i = 0; i < ORC_HC; ++i) {
+            double gs = 0.0;
+            for (int j = 0; j < ORC_HC; ++j) {
+                gs += G[i][j] * S[i][j];
+            }
+            for (int j = 0; j < ORC_HC; ++j) {
+                d_logits[b * ORC_HC * ORC_HC + i * ORC_HC + j] = S[i][j] * (G[i][j] - gs);
+            }
+        }
+    }
+}
+
+/* Reverse mode of the post-map orc_post (rwkv-ops mhu_jax.py, mhc_post_op with its
+ * custom VJP MhcPostOpBwd; the forward formula of the FlashInfer mHC article,
+ * section 2.1).  With dO = d_out [T, 4, H]:
+ *   d_x[t][h]       = sum_n dO[t][n][h] * post[t][n]
+ *   d_res[t][o][h]  = sum_n comb[t][o][n] * dO[t][n][h]
+ *   d_post[t][n]    = sum_h dO[t][n][h] * x[t][h]
+ *   d_comb[t][o][n] = sum_h res[t][o][h] * dO[t][n][h]
+ * d_out, x and res are bf16 bit patterns; post and comb fp64; every output fp64. */
+void orc_post_backward(const uint16_t *d_out, const uint16_t *x, const uint16_t *res, const double *post,
+                       const double *comb, int64_t T, int64_t H, double *d_x, double *d_res, double *d_post,
+                       double *d_comb)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        const uint16_t *g = d_out + t * ORC_HC * H;
+        const uint16_t *r = res + t * ORC_HC * H;
+        const double *p = post + t * ORC_HC;
+        const double *cm = comb + t * ORC_HC * ORC_HC;
+        for (int64_t h = 0; h < H; ++h) {
+            double a = 0.0;
+            for (int n = 0; n < ORC_HC; ++n) {
+                a += orc_bf16_to_f64(g[n * H + h]) * p[n];
+            }
+            d_x[t * H + h] = a;
+            for (int o = 0; o < ORC_HC; ++o) {
+                double v = 0.0;
+                for (int n = 0; n < ORC_HC; ++n) {
+                    v += cm[o * ORC_HC + n] * orc_bf16_to_f64(g[n * H + h]);
+                }
+                d_res[(t * ORC_HC + o) * H + h] = v;
+            }
+        }
+        for (int n = 0; n < ORC_HC; ++n) {
+            double v = 0.0;
+            for (int64_t h = 0; h < H; ++h) {
+                v += orc_bf16_to_f64(g[n * H + h]) * orc_bf16_to_f64(x[t * H + h]);
+            }
+            d_post[t * ORC_HC + n] = v;
+        }
+        for (int o = 0; o < ORC_HC; ++o) {
+            for (int n = 0; n < ORC_HC; ++n) {
+                double v = 0.0;
+                for (int64_t h = 0; h < H; ++h) {
+                    v += orc_bf16_to_f64(r[o * H + h]) * orc_bf16_to_f64(g[n * H + h]);
+                }
+                d_comb[(t * ORC_HC + o) * ORC_HC + n] = v;
+            }
+        }
+    }
+}
+

@@ -443,3 +443,77 @@ def test_pre_from_dots_rms_denominator_closed_form():
     expect = 1 / (1 + np.exp(-(d[:, 0].astype(np.float64) * rstd * 2.0)))
     assert np.allclose(o["pre"][:, 0], expect, rtol=0, atol=1e-15)
     assert np.allclose(o["pre"][:, 1:], 0.5, rtol=0, atol=0)
+
+
+# ---------------------------------------------------------------- backward passes
+
+def _fd_sinkhorn(L, G, iters, eps, h=1e-6):
+    """Central finite differences of sum(G * sinkhorn(L)) with respect to L (the forward oracle only)."""
+    out = np.empty_like(L)
+    for idx in np.ndindex(*L.shape):
+        a = L.copy()
+        b = L.copy()
+        a[idx] += h
+        b[idx] -= h
+        fa = (G * oracle.sinkhorn(a, iters, eps)).sum()
+        fb = (G * oracle.sinkhorn(b, iters, eps)).sum()
+        out[idx] = (fa - fb) / (2 * h)
+    return out
+
+
+@pytest.mark.parametrize("iters,eps,scale", [(1, 1e-6, 1.0), (3, 1e-3, 2.0), (20, 1e-6, 2.0), (20, 1e-6, 6.0)])
+def test_sinkhorn_backward_matches_finite_differences(iters, eps, scale):
+    g = np.random.default_rng(iters * 7 + int(scale))
+    L = g.standard_normal((3, 4, 4)) * scale
+    G = g.standard_normal((3, 4, 4))
+    d = oracle.sinkhorn_backward(G, L, iters, eps)
+    fd = _fd_sinkhorn(L, G, iters, eps)
+    assert np.abs(d - fd).max() < 1e-6 * max(1.0, np.abs(fd).max())
+
+
+def test_sinkhorn_backward_rows_sum_to_zero():
+    """Adding a constant to a row of the logits leaves the output unchanged, so each row of
+    d_logits sums to zero."""
+    g = np.random.default_rng(3)
+    L = g.standard_normal((50, 4, 4)) * 3
+    G = g.standard_normal((50, 4, 4))
+    d = oracle.sinkhorn_backward(G, L, 20, 1e-6)
+    assert np.abs(d.sum(axis=-1)).max() < 1e-13
+
+
+def test_post_backward_bilinear_identities():
+    """out is bilinear in (x, res) and (post, comb): <G, out> = <d_x, x> + <d_res, res>
+    = <d_post, post> + <d_comb, comb> (Euler's identity for each pair)."""
+    inp = layer_inputs(5, 40, cfg=130)
+    g = np.random.default_rng(8)
+    post = g.uniform(0, 2, (5, HC))
+    comb = g.uniform(0, 1, (5, HC, HC))
+    G16 = f32_to_bf16_bits(g.standard_normal((5, HC, 40)).astype(np.float32))
+    G = _bf16_f64(G16)
+    out = oracle.post(inp.x, inp.res, post, comb)
+    d_x, d_res, d_post, d_comb = oracle.post_backward(G16, inp.x, inp.res, post, comb)
+    inner = (G * out).sum()
+    assert abs(inner - ((d_x * _bf16_f64(inp.x)).sum() + (d_res * _bf16_f64(inp.res)).sum())) < 1e-10
+    assert abs(inner - ((d_post * post).sum() + (d_comb * comb).sum())) < 1e-10
+
+
+def test_post_backward_directional_derivatives_and_identity():
+    inp = layer_inputs(3, 16, cfg=131)
+    g = np.random.default_rng(9)
+    post = g.uniform(0, 2, (3, HC))
+    comb = g.uniform(0, 1, (3, HC, HC))
+    G16 = f32_to_bf16_bits(g.standard_normal((3, HC, 16)).astype(np.float32))
+    G = _bf16_f64(G16)
+    base = (G * oracle.post(inp.x, inp.res, post, comb)).sum()
+    _, _, d_post, d_comb = oracle.post_backward(G16, inp.x, inp.res, post, comb)
+    # out is linear in post and comb: a unit step gives the derivative exactly
+    p2 = post.copy()
+    p2[1, 2] += 1.0
+    assert abs(((G * oracle.post(inp.x, inp.res, p2, comb)).sum() - base) - d_post[1, 2]) < 1e-10
+    c2 = comb.copy()
+    c2[2, 0, 3] += 1.0
+    assert abs(((G * oracle.post(inp.x, inp.res, post, c2)).sum() - base) - d_comb[2, 0, 3]) < 1e-10
+    # identity comb, unit post: d_x = sum over new streams of G, d_res = G
+    eye = np.broadcast_to(np.eye(HC), (3, HC, HC))
+    d_x, d_res, _, _ = oracle.post_backward(G16, inp.x, inp.res, np.ones((3, HC)), eye)
+    assert np.array_equal(d_res, G) and np.allclose(d_x, G.sum(axis=1), rtol=0, atol=1e-12)
