@@ -40,7 +40,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="layer_h7168", choices=sorted(WORKLOADS))
-    ap.add_argument("--only", default="all", choices=["all", "pre", "post", "sinkhorn", "pre_dots"],
+    ap.add_argument("--only", default="all",
+                    choices=["all", "pre", "post", "sinkhorn", "pre_dots", "post_bwd", "sinkhorn_bwd"],
                     help="run only one call in the timed loop (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
@@ -66,8 +67,10 @@ def main():
     import torch
 
     import mhc_hyper_connection_amd as mhc
-    from mhc_inputs import (algorithmic_bytes_post, algorithmic_bytes_pre, algorithmic_bytes_pre_dots,
-                            algorithmic_bytes_sinkhorn, layer_inputs, sinkhorn_logits)
+    from mhc_inputs import (algorithmic_bytes_post, algorithmic_bytes_post_backward, algorithmic_bytes_pre,
+                            algorithmic_bytes_pre_dots, algorithmic_bytes_sinkhorn,
+                            algorithmic_bytes_sinkhorn_backward, layer_inputs, post_grad, sinkhorn_grad,
+                            sinkhorn_logits)
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
@@ -95,9 +98,17 @@ def main():
     ws = torch.empty(max(mhc.mhc_pre_fused_workspace_bytes(T, H), 1), dtype=torch.uint8, device=dev)
     p = inp.params
     sk_logits = None
-    if args.only == "sinkhorn":
+    if args.only in ("sinkhorn", "sinkhorn_bwd"):
         sk_logits = torch.from_numpy(sinkhorn_logits()).to(dev)
         sk_out = torch.empty_like(sk_logits)
+    if args.only == "sinkhorn_bwd":
+        sk_grad = torch.from_numpy(sinkhorn_grad()).to(dev)
+    if args.only == "post_bwd":
+        d_out = bf16(post_grad(T, H, cfg=cfg))
+        d_x = torch.empty_like(x)
+        d_res = torch.empty_like(res)
+        d_post = torch.empty_like(post)
+        d_comb = torch.empty_like(comb)
 
     def call_pre():
         mhc.mhc_pre_fused(res, hc_fn, hc_scale, hc_base, p["rms_eps"], p["pre_eps"], p["sinkhorn_eps"],
@@ -120,6 +131,16 @@ def main():
     def call_sinkhorn():
         mhc.mhc_sinkhorn(sk_logits, out=sk_out, num_iters=p["num_iters"], eps=p["sinkhorn_eps"])
 
+    def call_sinkhorn_bwd():
+        mhc.mhc_sinkhorn_backward(sk_grad, sk_logits, num_iters=p["num_iters"], eps=p["sinkhorn_eps"],
+                                  d_logits=sk_out)
+
+    def call_post_bwd():
+        mhc.mhc_post_backward(d_out, x, res, post, comb, d_x=d_x, d_res=d_res, d_post=d_post, d_comb=d_comb)
+
+    if args.only == "post_bwd":
+        call_pre()  # the forward's mixes (untimed)
+
     def step():
         if args.only in ("all", "pre"):
             call_pre()
@@ -129,6 +150,10 @@ def main():
             call_sinkhorn()
         if args.only == "pre_dots":
             call_pre_dots()
+        if args.only == "sinkhorn_bwd":
+            call_sinkhorn_bwd()
+        if args.only == "post_bwd":
+            call_post_bwd()
 
     stream = torch.cuda.current_stream(dev)
 
@@ -164,9 +189,17 @@ def main():
         breakdown["sinkhorn_ms"] = ms_step
     if args.only == "pre_dots":
         breakdown["pre_dots_ms"] = ms_step
+    if args.only == "sinkhorn_bwd":
+        breakdown["sinkhorn_bwd_ms"] = ms_step
+    if args.only == "post_bwd":
+        breakdown["post_bwd_ms"] = ms_step
 
     if args.only == "sinkhorn":
         step_bytes = algorithmic_bytes_sinkhorn(sk_logits.shape[0])
+    elif args.only == "sinkhorn_bwd":
+        step_bytes = algorithmic_bytes_sinkhorn_backward(sk_logits.shape[0])
+    elif args.only == "post_bwd":
+        step_bytes = algorithmic_bytes_post_backward(T, H)
     elif args.only == "pre_dots":
         step_bytes = algorithmic_bytes_pre_dots(T, H)
     else:
@@ -186,6 +219,10 @@ def main():
         calls["mhc_sinkhorn"] = ("sinkhorn_kernel", breakdown["sinkhorn_ms"], step_bytes)
     if "pre_dots_ms" in breakdown:
         calls["mhc_pre_from_dots"] = ("pre_dots_kernel", breakdown["pre_dots_ms"], step_bytes)
+    if "sinkhorn_bwd_ms" in breakdown:
+        calls["mhc_sinkhorn_backward"] = ("sinkhorn_bwd_kernel", breakdown["sinkhorn_bwd_ms"], step_bytes)
+    if "post_bwd_ms" in breakdown:
+        calls["mhc_post_backward"] = ("post_bwd_kernel", breakdown["post_bwd_ms"], step_bytes)
     traffic = load_traffic(T, H)
     per_call = {}
     for name, (kern, ms_k, bytes_k) in calls.items():
@@ -230,7 +267,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"mhc {args.only if args.only != 'all' else 'pre+post'} T={T} H={H} HC=4",
+        "config": {"workload": (f"mhc {args.only} 2^20 4x4 matrices" if args.only.startswith("sinkhorn") else
+                                f"mhc {args.only if args.only != 'all' else 'pre+post'} T={T} H={H} HC=4"),
                    "T": T, "H": H, "hc": 4, "num_iters": p["num_iters"], "inputs": "resident in HBM"},
         "effective_GBps": round(eff_gbps, 1),
         "hbm_frac": round(eff_gbps / HBM_PEAK_GBPS, 4),

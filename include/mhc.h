@@ -163,6 +163,58 @@ mhc_status mhc_pre_from_dots(const float *dot_mix, const float *sqrsum, int32_t 
 mhc_status mhc_post(const uint16_t *x, const uint16_t *res, const float *post, const float *comb, int64_t T,
                     int64_t H, uint16_t *out, void *stream);
 
+/*
+ * Reverse mode (backward pass).  Each entry point returns the gradients of the
+ * matching forward map for a given output gradient, as the custom VJPs of
+ * rwkv-ops mhu_jax.py do (sinkhorn_knopp / SinkhornBwd, mhc_post_op /
+ * MhcPostOpBwd).  The forward is recomputed from the saved inputs where needed;
+ * no state is kept between a forward and a backward call.
+ */
+
+#define MHC_SINKHORN_BWD_MAX_ITERS 255
+
+/*
+ * mhc_sinkhorn_backward -- gradient of mhc_sinkhorn with respect to its logits,
+ * through the fixed count of iterations (not the limit of the iteration):
+ *     d_logits = J(logits)^T grad,   J the Jacobian of the map computed by mhc_sinkhorn
+ * The forward is replayed per matrix, keeping the matrix after every iteration on
+ * chip; then, from the last iteration back, the column step Q = A / colsum(A) and
+ * the row step A = P / rowsum(P) are reversed, then + eps and the row softmax.
+ *
+ *   grad      [n_mats, 4, 4] fp32, device: gradient with respect to mhc_sinkhorn's out
+ *   logits    [n_mats, 4, 4] fp32, device: the forward's input
+ *   n_mats    0 <= n_mats <= 2^32
+ *   num_iters 1 <= num_iters <= MHC_SINKHORN_BWD_MAX_ITERS (the forward's count;
+ *             the history of one matrix takes 64 * (num_iters + 1) bytes of LDS)
+ *   eps       the forward's eps, finite and > 0
+ *   d_logits  [n_mats, 4, 4] fp32, device output; may equal `grad` or `logits` exactly,
+ *             must not overlap either otherwise
+ */
+mhc_status mhc_sinkhorn_backward(const float *grad, const float *logits, int64_t n_mats, int32_t num_iters,
+                                 float eps, float *d_logits, void *stream);
+
+/*
+ * mhc_post_backward -- gradients of mhc_post (FlashInfer mHC article, section 2.1,
+ * for the forward formula).  With dO = d_out:
+ *     d_x[t][h]       = bf16( sum_n dO[t][n][h] * post[t][n] )
+ *     d_res[t][o][h]  = bf16( sum_n comb[t][o][n] * dO[t][n][h] )
+ *     d_post[t][n]    = sum_h dO[t][n][h] * x[t][h]                 (fp32)
+ *     d_comb[t][o][n] = sum_h res[t][o][h] * dO[t][n][h]            (fp32)
+ *   (fp32 accumulation; the sums over h are reduced in a fixed order, so repeated
+ *   calls are bit-identical)
+ *
+ *   d_out [T,4,H] bf16   gradient with respect to mhc_post's out, device
+ *   x [T,H], res [T,4,H], post [T,4], comb [T,4,4]   the forward's inputs, device
+ *   T >= 0, H >= 1
+ *   d_x [T,H] bf16, d_res [T,4,H] bf16, d_post [T,4] fp32, d_comb [T,4,4] fp32
+ *             outputs, device.  d_res may equal d_out exactly (each element of d_out
+ *             is read before the d_res element at the same place is written); no
+ *             other overlap between an output and an input or another output is allowed.
+ */
+mhc_status mhc_post_backward(const uint16_t *d_out, const uint16_t *x, const uint16_t *res, const float *post,
+                             const float *comb, int64_t T, int64_t H, uint16_t *d_x, uint16_t *d_res,
+                             float *d_post, float *d_comb, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

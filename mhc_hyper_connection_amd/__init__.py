@@ -58,6 +58,10 @@ def lib() -> ctypes.CDLL:
     L.mhc_post.restype = ctypes.c_int
     L.mhc_pre_from_dots.argtypes = [P, P, I32, P, P, P, I64, I64, F, F, F, F, F, I32, P, P, P, P, P]
     L.mhc_pre_from_dots.restype = ctypes.c_int
+    L.mhc_sinkhorn_backward.argtypes = [P, P, I64, I32, F, P, P]
+    L.mhc_sinkhorn_backward.restype = ctypes.c_int
+    L.mhc_post_backward.argtypes = [P, P, P, P, P, I64, I64, P, P, P, P, P]
+    L.mhc_post_backward.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -265,6 +269,77 @@ def mhc_post(x: torch.Tensor, res: torch.Tensor, post: torch.Tensor, comb: torch
     return out
 
 
-__all__ = ["mhc_sinkhorn", "mhc_pre_fused", "mhc_pre_fused_workspace_bytes", "mhc_pre_from_dots", "mhc_post", "lib",
-           "abi_version",
-           "status_string", "MHCError", "HC", "MIX"]
+SINKHORN_BWD_MAX_ITERS = 255
+
+
+def mhc_sinkhorn_backward(grad: torch.Tensor, logits: torch.Tensor, num_iters: int = 20, eps: float = 1e-6,
+                          d_logits: torch.Tensor | None = None) -> torch.Tensor:
+    """Gradient of :func:`mhc_sinkhorn` with respect to its logits, for the output gradient
+    ``grad``; both [..., 4, 4] fp32.  ``d_logits`` may be ``grad`` or ``logits``."""
+    _need(logits, "logits", torch.float32)
+    if logits.dim() < 2 or tuple(logits.shape[-2:]) != (HC, HC):
+        raise ValueError(f"logits must be [..., 4, 4], got {tuple(logits.shape)}")
+    _need(grad, "grad", torch.float32)
+    if grad.shape != logits.shape:
+        raise ValueError("grad must have the shape of logits")
+    if d_logits is None:
+        d_logits = torch.empty_like(logits)
+    _need(d_logits, "d_logits", torch.float32)
+    if d_logits.shape != logits.shape:
+        raise ValueError("d_logits must have the shape of logits")
+    _same_device(grad, logits, d_logits)
+    n = logits.numel() // (HC * HC)
+    _check("mhc_sinkhorn_backward",
+           lib().mhc_sinkhorn_backward(_ptr(grad), _ptr(logits), n, int(num_iters), float(eps), _ptr(d_logits),
+                                       _stream(logits.device)))
+    return d_logits
+
+
+def mhc_post_backward(d_out: torch.Tensor, x: torch.Tensor, res: torch.Tensor, post: torch.Tensor,
+                      comb: torch.Tensor, *, d_x: torch.Tensor | None = None, d_res: torch.Tensor | None = None,
+                      d_post: torch.Tensor | None = None, d_comb: torch.Tensor | None = None):
+    """Gradients of :func:`mhc_post` for the output gradient ``d_out`` [..., 4, H] bf16:
+    returns (d_x [..., H] bf16, d_res [..., 4, H] bf16, d_post [..., 4] fp32, d_comb [..., 4, 4] fp32).
+    ``d_res`` may be ``d_out``; ``post`` may be [..., 4] or [..., 4, 1] (d_post takes its shape)."""
+    _need(res, "res", torch.bfloat16)
+    if res.dim() < 2 or res.shape[-2] != HC:
+        raise ValueError(f"residual.shape[-2] / HC must be 4, got {tuple(res.shape)}")
+    H = res.shape[-1]
+    outer = tuple(res.shape[:-2])
+    T = res.numel() // (HC * H) if H > 0 else 0
+    _need(d_out, "d_out", torch.bfloat16)
+    if d_out.shape != res.shape:
+        raise ValueError("d_out must have the shape of res")
+    _need(x, "x", torch.bfloat16)
+    if tuple(x.shape) != outer + (H,):
+        raise ValueError(f"x must be {outer + (H,)}, got {tuple(x.shape)}")
+    _need(post, "post", torch.float32)
+    if tuple(post.shape) not in (outer + (HC,), outer + (HC, 1)):
+        raise ValueError(f"post must be {outer + (HC,)} or {outer + (HC, 1)}, got {tuple(post.shape)}")
+    _need(comb, "comb", torch.float32)
+    if tuple(comb.shape) != outer + (HC, HC):
+        raise ValueError(f"comb must be {outer + (HC, HC)}, got {tuple(comb.shape)}")
+    if d_x is None:
+        d_x = torch.empty_like(x)
+    if d_res is None:
+        d_res = torch.empty_like(res)
+    if d_post is None:
+        d_post = torch.empty_like(post)
+    if d_comb is None:
+        d_comb = torch.empty_like(comb)
+    for t, name, dt, shape in ((d_x, "d_x", torch.bfloat16, x.shape), (d_res, "d_res", torch.bfloat16, res.shape),
+                               (d_post, "d_post", torch.float32, post.shape),
+                               (d_comb, "d_comb", torch.float32, comb.shape)):
+        _need(t, name, dt)
+        if t.shape != shape:
+            raise ValueError(f"{name} must be {tuple(shape)}, got {tuple(t.shape)}")
+    _same_device(d_out, x, res, post, comb, d_x, d_res, d_post, d_comb)
+    _check("mhc_post_backward",
+           lib().mhc_post_backward(_ptr(d_out), _ptr(x), _ptr(res), _ptr(post), _ptr(comb), T, H, _ptr(d_x),
+                                   _ptr(d_res), _ptr(d_post), _ptr(d_comb), _stream(res.device)))
+    return d_x, d_res, d_post, d_comb
+
+
+__all__ = ["mhc_sinkhorn", "mhc_pre_fused", "mhc_pre_fused_workspace_bytes", "mhc_pre_from_dots", "mhc_post",
+           "mhc_sinkhorn_backward", "mhc_post_backward", "lib", "abi_version", "status_string", "MHCError", "HC",
+           "MIX", "SINKHORN_BWD_MAX_ITERS"]

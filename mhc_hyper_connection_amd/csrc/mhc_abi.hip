@@ -198,4 +198,64 @@ mhc_status mhc_post(const uint16_t *x, const uint16_t *res, const float *post, c
     return launch_status(mhc::launch_post(x, res, post, comb, T, H, out, (hipStream_t)stream, vec8));
 }
 
+mhc_status mhc_sinkhorn_backward(const float *grad, const float *logits, int64_t n_mats, int32_t num_iters,
+                                 float eps, float *d_logits, void *stream)
+{
+    if (n_mats < 0 || n_mats > ((int64_t)1 << 32) || num_iters < 1 || num_iters > MHC_SINKHORN_BWD_MAX_ITERS ||
+        !finite(eps) || !(eps > 0.0f)) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    if (n_mats == 0) {
+        return MHC_SUCCESS;
+    }
+    if (!grad || !logits || !d_logits) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    const size_t bytes = (size_t)n_mats * 16 * sizeof(float);
+    if (((const void *)d_logits != (const void *)grad && overlaps(d_logits, bytes, grad, bytes)) ||
+        ((const void *)d_logits != (const void *)logits && overlaps(d_logits, bytes, logits, bytes))) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    return launch_status(
+        mhc::launch_sinkhorn_bwd(grad, logits, n_mats, num_iters, eps, d_logits, (hipStream_t)stream));
+}
+
+mhc_status mhc_post_backward(const uint16_t *d_out, const uint16_t *x, const uint16_t *res, const float *post,
+                             const float *comb, int64_t T, int64_t H, uint16_t *d_x, uint16_t *d_res,
+                             float *d_post, float *d_comb, void *stream)
+{
+    if (!sizes_ok(T, H)) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    if (T == 0) {
+        return MHC_SUCCESS;
+    }
+    if (!d_out || !x || !res || !post || !comb || !d_x || !d_res || !d_post || !d_comb) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    const size_t res_b = (size_t)T * 4 * H * 2, x_b = (size_t)T * H * 2;
+    const size_t post_b = (size_t)T * 4 * 4, comb_b = (size_t)T * 16 * 4;
+    const void *outs[4] = {d_x, d_res, d_post, d_comb};
+    const size_t outn[4] = {x_b, res_b, post_b, comb_b};
+    const void *ins[5] = {d_out, x, res, post, comb};
+    const size_t inn[5] = {res_b, x_b, res_b, post_b, comb_b};
+    for (int o = 0; o < 4; ++o) {
+        for (int i = 0; i < 5; ++i) {
+            const bool in_place = o == 1 && i == 0 && (const void *)d_res == (const void *)d_out;
+            if (!in_place && overlaps(outs[o], outn[o], ins[i], inn[i])) {
+                return MHC_ERROR_INVALID_VALUE;
+            }
+        }
+        for (int o2 = o + 1; o2 < 4; ++o2) {
+            if (overlaps(outs[o], outn[o], outs[o2], outn[o2])) {
+                return MHC_ERROR_INVALID_VALUE;
+            }
+        }
+    }
+    const bool vec8 = (H % 8 == 0) && aligned16(d_out) && aligned16(x) && aligned16(res) && aligned16(d_x) &&
+                      aligned16(d_res);
+    return launch_status(mhc::launch_post_bwd(d_out, x, res, post, comb, T, H, d_x, d_res, d_post, d_comb,
+                                              (hipStream_t)stream, vec8));
+}
+
 } // extern "C"

@@ -84,6 +84,52 @@ __device__ __forceinline__ void sinkhorn4x4(float *P, int iters, float eps)
     }
 }
 
+// Lane permutations within a 16-lane DPP row.  Every source lane exists for these
+// patterns, so bound_ctrl (zero for a missing source) never applies; setting it and
+// leaving `old` undefined lets the compiler fold the move into the consuming add.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_perm(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float dpp_quad_xor1(float v) { return dpp_perm<0xB1>(v); } // quad_perm [1,0,3,2]
+__device__ __forceinline__ float dpp_quad_xor2(float v) { return dpp_perm<0x4E>(v); } // quad_perm [2,3,0,1]
+__device__ __forceinline__ float dpp_row_ror4(float v) { return dpp_perm<0x124>(v); } // row_ror:4
+__device__ __forceinline__ float dpp_row_ror8(float v) { return dpp_perm<0x128>(v); } // row_ror:8
+
+// Fixed-count Sinkhorn of a 4x4 matrix spread over a 16-lane row (lane e holds entry
+// (e / 4, e % 4)): row softmax (row maximum subtracted) plus eps, then `iters` rounds
+// of row then column normalisation.  Row sums combine the lane's quad; column sums
+// the lanes e, e +- 4, e +- 8 (rotations within the row).
+__device__ __forceinline__ float sinkhorn_row16(float L, int iters, float eps)
+{
+    float mx = fmaxf(L, dpp_quad_xor1(L));
+    mx = fmaxf(mx, dpp_quad_xor2(mx));
+    const float e = __expf(L - mx);
+    float s = e + dpp_quad_xor1(e);
+    s = s + dpp_quad_xor2(s);
+    float P = fmaf(e, fast_rcp(s), eps);
+    for (int it = 0; it < iters; ++it) {
+        float rs = P + dpp_quad_xor1(P);
+        rs = rs + dpp_quad_xor2(rs);
+        P *= fast_rcp(rs);
+        float cs = P + dpp_row_ror4(P);
+        cs = cs + dpp_row_ror8(cs);
+        P *= fast_rcp(cs);
+    }
+    return P;
+}
+
+// Sum over the 64 lanes of a wavefront (butterfly: every lane gets the total).
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        v += __shfl_xor(v, o);
+    }
+    return v;
+}
+
 // Wave-uniform value (forces an SGPR so coefficient loads become scalar loads).
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 

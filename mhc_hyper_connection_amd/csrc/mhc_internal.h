@@ -43,4 +43,15 @@ hipError_t launch_pre_dots(const float *dot_mix, const float *sqrsum, int num_sp
                            float rms_eps, float pre_eps, float sinkhorn_eps, float post_mult, int iters,
                            uint16_t *y, float *post, float *comb, float *pre, hipStream_t stream, bool vec8);
 
+// Reverse mode of the standalone Sinkhorn (16 lanes per matrix, LDS history).
+size_t sinkhorn_bwd_lds_bytes(int iters);
+hipError_t launch_sinkhorn_bwd(const float *grad, const float *logits, int64_t n, int iters, float eps,
+                               float *d_logits, hipStream_t stream);
+
+// Reverse mode of the post-map (one workgroup per token).  `vec8`: H % 8 == 0 and
+// d_out/x/res/d_x/d_res 16-byte aligned.
+hipError_t launch_post_bwd(const uint16_t *d_out, const uint16_t *x, const uint16_t *res, const float *post,
+                           const float *comb, int64_t T, int64_t H, uint16_t *d_x, uint16_t *d_res, float *d_post,
+                           float *d_comb, hipStream_t stream, bool vec8);
+
 } // namespace mhc

@@ -35,55 +35,6 @@ struct DotsArgs {
     float *post, *comb, *pre_out;
 };
 
-__device__ __forceinline__ float dpp_quad_xor1(float v)
-{
-    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0xB1, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float dpp_quad_xor2(float v)
-{
-    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x4E, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float dpp_row_ror4(float v)
-{
-    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x124, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float dpp_row_ror8(float v)
-{
-    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x128, 0xF, 0xF, false));
-}
-
-// Fixed-count Sinkhorn of a 4x4 matrix spread over a 16-lane row (lane e holds entry
-// (e / 4, e % 4)): row softmax (row maximum subtracted) plus eps, then `iters` rounds
-// of row then column normalisation.  Row sums combine the lane's quad; column sums
-// the lanes e, e +- 4, e +- 8 (rotations within the row).
-__device__ __forceinline__ float sinkhorn_row16(float L, int iters, float eps)
-{
-    float mx = fmaxf(L, dpp_quad_xor1(L));
-    mx = fmaxf(mx, dpp_quad_xor2(mx));
-    const float e = __expf(L - mx);
-    float s = e + dpp_quad_xor1(e);
-    s = s + dpp_quad_xor2(s);
-    float P = fmaf(e, fast_rcp(s), eps);
-    for (int it = 0; it < iters; ++it) {
-        float rs = P + dpp_quad_xor1(P);
-        rs = rs + dpp_quad_xor2(rs);
-        P *= fast_rcp(rs);
-        float cs = P + dpp_row_ror4(P);
-        cs = cs + dpp_row_ror8(cs);
-        P *= fast_rcp(cs);
-    }
-    return P;
-}
-
-__device__ __forceinline__ float wave_sum(float v)
-{
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        v += __shfl_xor(v, o);
-    }
-    return v;
-}
-
 // kCPT > 0: 16-byte path, kCPT chunks of 8 elements per thread and stream in VGPRs.
 // kCPT == 0: any H and alignment, two scalar passes over the token's streams.
 template <int kCPT>

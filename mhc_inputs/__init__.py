@@ -35,6 +35,8 @@ _TID = {
     "comb_logits": 6,
     "logits": 7,
     "hc_scale": 8,
+    "grad": 9,
+    "d_out": 10,
 }
 
 
@@ -166,6 +168,16 @@ def sinkhorn_logits(n: int = SINKHORN_N, seed: int = 0, cfg: int = SINKHORN_CFG)
     return lg
 
 
+def sinkhorn_grad(n: int = SINKHORN_N, seed: int = 0, cfg: int = SINKHORN_CFG) -> np.ndarray:
+    """[n, 4, 4] fp32 output gradients ~ N(0, 1) for the Sinkhorn reverse mode."""
+    return normal_f32(seed, cfg, "grad", (n, HC, HC), 1.0)
+
+
+def post_grad(T: int, H: int, cfg: int = 2, seed: int = 0) -> np.ndarray:
+    """[T, 4, H] bf16 gradients ~ N(0, 1) of the post-map output."""
+    return normal_bf16(seed, cfg, "d_out", (T, HC, H))
+
+
 def algorithmic_bytes_pre(T: int, H: int) -> int:
     """Bytes the pre-map must move: res read, y written, post/comb written, hc_fn + scale/base read once."""
     return T * (8 * H + 2 * H + 16 + 64) + 384 * H + 108
@@ -184,3 +196,14 @@ def algorithmic_bytes_pre_dots(T: int, H: int, splits: int = 1, sqrsum: bool = F
 
 def algorithmic_bytes_sinkhorn(n: int) -> int:
     return n * 64 * 2
+
+
+def algorithmic_bytes_post_backward(T: int, H: int) -> int:
+    """Bytes the post-map reverse mode must move: d_out, x and res read, 80 B of mixes read,
+    d_x and d_res written, 80 B of mix gradients written."""
+    return T * (8 * H + 2 * H + 8 * H + 80 + 2 * H + 8 * H + 80)
+
+
+def algorithmic_bytes_sinkhorn_backward(n: int) -> int:
+    """grad and logits read, d_logits written: 64 B each per matrix."""
+    return n * 64 * 3

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     lib = mhc.lib()
     names = _declared()
     assert {"mhc_sinkhorn", "mhc_pre_fused", "mhc_pre_fused_workspace_bytes", "mhc_pre_from_dots", "mhc_post",
-            "mhc_abi_version", "mhc_status_string"} <= set(names)
+            "mhc_sinkhorn_backward", "mhc_post_backward", "mhc_abi_version", "mhc_status_string"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -137,6 +137,51 @@ def test_post_validation():
     assert call(T=0, x=None, res=None, post=None, comb=None, out=None) == mhc.MHC_SUCCESS
 
 
+def test_sinkhorn_backward_validation():
+    lib = mhc.lib()
+    g, lg, d = FAKE, FAKE2, ctypes.c_void_p(0x30000000)
+    E = mhc.MHC_ERROR_INVALID_VALUE
+    call = lambda **k: lib.mhc_sinkhorn_backward(k.get("g", g), k.get("lg", lg), k.get("n", 10), k.get("it", 20),
+                                                 k.get("eps", 1e-6), k.get("d", d), NULL)
+    assert call(n=-1) == E
+    assert call(n=(1 << 32) + 1) == E
+    assert call(it=0) == E
+    header_max = int(re.search(r"#define MHC_SINKHORN_BWD_MAX_ITERS (\d+)", HEADER.read_text()).group(1))
+    assert header_max == mhc.SINKHORN_BWD_MAX_ITERS
+    assert call(it=header_max + 1) == E
+    assert call(eps=0.0) == E
+    assert call(eps=float("inf")) == E
+    for name in ("g", "lg", "d"):
+        assert call(**{name: None}) == E
+    assert call(d=ctypes.c_void_p(0x10000 + 4)) == E          # partial overlap with grad
+    assert call(d=ctypes.c_void_p(0x20000000 - 64)) == E      # partial overlap with logits
+    assert call(n=0, g=None, lg=None, d=None) == mhc.MHC_SUCCESS
+
+
+def test_post_backward_validation():
+    lib = mhc.lib()
+    base = dict(go=0x100000, x=0x200000, res=0x300000, post=0x400000, comb=0x410000, dx=0x500000, dr=0x600000,
+                dp=0x700000, dc=0x710000)
+    E = mhc.MHC_ERROR_INVALID_VALUE
+
+    def call(T=8, H=64, **k):
+        a = {n: ctypes.c_void_p(v) if v is not None else None for n, v in {**base, **k}.items()}
+        return lib.mhc_post_backward(a["go"], a["x"], a["res"], a["post"], a["comb"], T, H, a["dx"], a["dr"],
+                                     a["dp"], a["dc"], NULL)
+
+    assert call(T=-1) == E
+    assert call(H=0) == E
+    for name in base:
+        assert call(**{name: None}) == E
+    assert call(dr=0x100000 + 2) == E      # d_res overlaps d_out without being it
+    assert call(dr=0x300000) == E          # d_res is res (only d_out may be updated in place)
+    assert call(dx=0x200000) == E          # d_x is x
+    assert call(dx=0x600000 + 128) == E    # d_x overlaps d_res
+    assert call(dp=0x710000 - 64) == E     # d_post overlaps d_comb
+    assert call(dc=0x410000) == E          # d_comb is comb
+    assert call(T=0, **{n: None for n in base}) == mhc.MHC_SUCCESS
+
+
 def test_binding_rejects_cpu_tensors_before_the_library():
     import torch
     with pytest.raises(ValueError):
@@ -144,3 +189,8 @@ def test_binding_rejects_cpu_tensors_before_the_library():
                      torch.zeros(2, 4), torch.zeros(2, 4, 4))
     with pytest.raises(ValueError):
         mhc.mhc_sinkhorn(torch.zeros(3, 4, 4))
+    with pytest.raises(ValueError):
+        mhc.mhc_sinkhorn_backward(torch.zeros(3, 4, 4), torch.zeros(3, 4, 4))
+    with pytest.raises(ValueError):
+        mhc.mhc_post_backward(torch.zeros(2, 4, 8, dtype=torch.bfloat16), torch.zeros(2, 8, dtype=torch.bfloat16),
+                              torch.zeros(2, 4, 8, dtype=torch.bfloat16), torch.zeros(2, 4), torch.zeros(2, 4, 4))
