@@ -23,6 +23,15 @@ import numpy as np
 
 METRIC = "mHC pre+post tokens/s and effective HBM GB/s (% of peak), T=8192 H=7168"
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+# VALU issue peak: 256 CUs x 4 SIMDs x 2.4 GHz, one wave64 fp32 VALU instruction per
+# 4 cycles per SIMD (16 lanes, non-packed) -> 614.4 G wave-instructions/s.
+VALU_PEAK_GIPS = 256 * 4 * 2.4 / 4
+
+
+def sinkhorn_valu_per_wave(iters: int) -> int:
+    """VALU instructions one wave of sinkhorn_kernel issues for its 64 matrices, counted
+    in the compiled gfx950 code: 105 outside the iteration loop plus 64 per iteration."""
+    return 105 + 64 * iters
 
 WORKLOADS = {
     # name: (cfg id, T, H)
@@ -238,6 +247,16 @@ def main():
     roofline = {"bound": "hbm", "achieved": d["achieved"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": d["frac"], "traffic": d["traffic"], "kernel": d["kernel"], "call": dom,
                 "avg_ms": d["avg_ms"], "algorithmic_bytes": d["algorithmic_bytes"]}
+    if dom == "mhc_sinkhorn":
+        # one lane per matrix: bound by VALU issue, not by its 128 B per matrix
+        waves = sk_logits.shape[0] // 64
+        instr = waves * sinkhorn_valu_per_wave(p["num_iters"])
+        achieved = instr / (d["avg_ms"] * 1e-3) / 1e9
+        roofline = {"bound": "alu", "achieved": round(achieved, 1), "peak": VALU_PEAK_GIPS,
+                    "unit": "G wave64 VALU instructions/s", "frac": round(achieved / VALU_PEAK_GIPS, 4),
+                    "traffic": d["traffic"], "kernel": d["kernel"], "call": dom, "avg_ms": d["avg_ms"],
+                    "valu_instructions": instr, "hbm": {"achieved": d["achieved"], "peak": HBM_PEAK_GBPS,
+                                                        "unit": "GB/s"}}
 
     copy_cal = None
     if args.copy_calibration:
