@@ -59,6 +59,9 @@ def _load():
     lib.orc_pre_from_dots.argtypes = [P, P, I64, P, P, P, I64, I64, D, D, D, D, D, ctypes.c_int, P, P, P, P]
     lib.orc_sinkhorn_backward.argtypes = [P, P, I64, ctypes.c_int, D, P]
     lib.orc_post_backward.argtypes = [P, P, P, P, P, I64, I64, P, P, P, P]
+    lib.orc_pre_from_dots_backward.argtypes = [P, P, P, P, P, P, P, P, I64, I64, D, D, D, D, D, ctypes.c_int,
+                                               P, P, P, P, P]
+    lib.orc_pre_backward.argtypes = [P, P, P, P, P, P, P, I64, I64, D, D, D, D, ctypes.c_int, P, P, P, P, P]
     for f in ("orc_round_bf16", "orc_rms", "orc_project", "orc_mix_activation", "orc_sinkhorn",
               "orc_collapse", "orc_post", "orc_pre", "orc_pre_from_dots", "orc_sinkhorn_backward",
               "orc_post_backward"):
@@ -230,3 +233,60 @@ def post_backward(d_out, x, res, post, comb):
                               _p(d_post), _p(d_comb))
     return d_x, d_res, d_post, d_comb
 
+
+
+def pre_from_dots_backward(dy, d_post, d_comb, dot, res, hc_scale, hc_base, sqrsum=None, k=None, rms_eps=1e-6,
+                           pre_eps=1e-6, sinkhorn_eps=1e-6, post_mult=1.0, num_iters=20):
+    """Reverse mode of the pre-map from external dots (one split).  dy [T,H] bf16 bits, d_post [T,4],
+    d_comb [T,4,4], dot [T,24] and sqrsum [T] or None (real values).  Returns dict of fp64 arrays:
+    d_res [T,4,H], d_dot [T,24], d_sqrsum [T] (None when sqrsum is None), d_hc_scale [3], d_hc_base [24]."""
+    res = _c(res, np.uint16)
+    T, hc, H = res.shape
+    assert hc == HC
+    dy = _c(dy, np.uint16)
+    assert dy.shape == (T, H)
+    d_post = _c(d_post, np.float64).reshape(T, HC)
+    d_comb = _c(d_comb, np.float64).reshape(T, HC, HC)
+    dot = _c(dot, np.float64).reshape(T, MIX)
+    sq = None if sqrsum is None else _c(sqrsum, np.float64).reshape(T)
+    hc_scale = _c(hc_scale, np.float32)
+    hc_base = _c(hc_base, np.float32)
+    assert 1 <= int(num_iters) <= 1024
+    k = float(HC * H) if k is None else float(k)
+    d_res = np.empty((T, HC, H))
+    d_dot = np.empty((T, MIX))
+    d_sq = np.empty(T) if sq is not None else None
+    d_scale = np.empty(3)
+    d_base = np.empty(MIX)
+    _load().orc_pre_from_dots_backward(_p(dy), _p(d_post), _p(d_comb), _p(dot), _p(sq) if sq is not None else None,
+                                       _p(res), _p(hc_scale), _p(hc_base), T, H, k, rms_eps, pre_eps, sinkhorn_eps,
+                                       post_mult, int(num_iters), _p(d_res), _p(d_dot),
+                                       _p(d_sq) if d_sq is not None else None, _p(d_scale), _p(d_base))
+    return dict(d_res=d_res, d_dot=d_dot, d_sqrsum=d_sq, d_hc_scale=d_scale, d_hc_base=d_base)
+
+
+def pre_backward(dy, d_post, d_comb, res, hc_fn, hc_scale, hc_base, rms_eps=1e-6, pre_eps=1e-6, sinkhorn_eps=1e-6,
+                 post_mult=1.0, num_iters=20):
+    """Reverse mode of the whole pre-map (projection inside).  Returns dict of fp64 arrays:
+    d_res [T,4,H], d_hc_fn [24,4H], d_hc_scale [3], d_hc_base [24]."""
+    res = _c(res, np.uint16)
+    T, hc, H = res.shape
+    assert hc == HC
+    dy = _c(dy, np.uint16)
+    assert dy.shape == (T, H)
+    d_post = _c(d_post, np.float64).reshape(T, HC)
+    d_comb = _c(d_comb, np.float64).reshape(T, HC, HC)
+    hc_fn = _c(hc_fn, np.float32)
+    assert hc_fn.shape == (MIX, HC * H)
+    hc_scale = _c(hc_scale, np.float32)
+    hc_base = _c(hc_base, np.float32)
+    assert 1 <= int(num_iters) <= 1024
+    d_res = np.empty((T, HC, H))
+    d_fn = np.empty((MIX, HC * H))
+    d_scale = np.empty(3)
+    d_base = np.empty(MIX)
+    scratch = np.empty(2 * MIX * max(T, 1))
+    _load().orc_pre_backward(_p(dy), _p(d_post), _p(d_comb), _p(res), _p(hc_fn), _p(hc_scale), _p(hc_base), T, H,
+                             rms_eps, pre_eps, sinkhorn_eps, post_mult, int(num_iters), _p(d_res), _p(d_fn),
+                             _p(d_scale), _p(d_base), _p(scratch))
+    return dict(d_res=d_res, d_hc_fn=d_fn, d_hc_scale=d_scale, d_hc_base=d_base)

@@ -460,3 +460,135 @@ void orc_post_backward(const uint16_t *d_out, const uint16_t *x, const uint16_t 
     }
 }
 
+
+/* Reverse mode of the pre-map from an external projection (orc_pre_from_dots with
+ * one split: the dots d[t][24] and, when supplied, the sum of squares S[t]).  It is
+ * the rwkv-ops mhc_pre_op custom VJP (MhcPreOpBwd: sigmoid weights, Sinkhorn and
+ * the stream aggregate), extended by the FlashInfer mixes in front of it
+ * (FlashInfer mHC article, section 5.2: m = d * rstd, per-group scale and base,
+ * pre_eps, post_mult).  Given dy [T,H] (bf16 bits), d_post [T,4] and d_comb
+ * [T,4,4], from the output back:
+ *   y = sum_i pre_i res_i:            d_pre_i = sum_h dy[h] res_i[h];  d_res_i[h] = pre_i dy[h]
+ *   pre_i = sigma(z_i) + pre_eps:     dz_i = d_pre_i sigma(z_i) (1 - sigma(z_i))
+ *   post_i = sigma(z_{4+i}) post_mult: dz_{4+i} = d_post_i post_mult sigma (1 - sigma)
+ *   comb = Sinkhorn(L), L = z_{8..23}: dz_{8..23} = the Sinkhorn reverse mode of d_comb
+ *   z_r = m_r s_g + b_r:              d_b_r += dz_r;  d_s_g += dz_r m_r;  dm_r = dz_r s_g
+ *   m_r = d_r rstd:                   dd_r = dm_r rstd;  d_rstd = sum_r dm_r d_r
+ *   rstd = (S / k + rms_eps)^(-1/2):  dS = -d_rstd rstd^3 / (2 k)
+ *   S = sum res^2 (sqrsum NULL):      d_res_i[h] += 2 res_i[h] dS;   else d_sqrsum[t] = dS
+ * dot is [T,24] fp64, sqrsum [T] fp64 or NULL.  d_res [T,4,H], d_dot [T,24],
+ * d_sqrsum [T] (ignored when sqrsum is NULL), d_hc_scale [3] and d_hc_base [24]
+ * (summed over the tokens in token order) are fp64 outputs. */
+void orc_pre_from_dots_backward(const uint16_t *dy, const double *d_post, const double *d_comb, const double *dot,
+                                const double *sqrsum, const uint16_t *res, const float *hc_scale,
+                                const float *hc_base, int64_t T, int64_t H, double k, double rms_eps,
+                                double pre_eps, double sinkhorn_eps, double post_mult, int num_iters, double *d_res,
+                                double *d_dot, double *d_sqrsum, double *d_hc_scale, double *d_hc_base)
+{
+    for (int g = 0; g < 3; ++g) {
+        d_hc_scale[g] = 0.0;
+    }
+    for (int r = 0; r < ORC_MIX; ++r) {
+        d_hc_base[r] = 0.0;
+    }
+    for (int64_t t = 0; t < T; ++t) {
+        const uint16_t *rr = res + t * ORC_HC * H;
+        const uint16_t *g = dy + t * H;
+        const double *d = dot + t * ORC_MIX;
+        /* forward values */
+        double S;
+        if (sqrsum) {
+            S = sqrsum[t];
+        } else {
+            double rstd_unused;
+            orc_rms(rr, 1, H, rms_eps, &S, &rstd_unused);
+        }
+        const double rstd = 1.0 / sqrt(S / k + rms_eps);
+        double m[ORC_MIX], z[ORC_MIX];
+        for (int r = 0; r < ORC_MIX; ++r) {
+            const int grp = r < ORC_HC ? 0 : (r < 2 * ORC_HC ? 1 : 2);
+            m[r] = d[r] * rstd;
+            z[r] = m[r] * (double)hc_scale[grp] + (double)hc_base[r];
+        }
+        /* reverse */
+        double dz[ORC_MIX];
+        for (int i = 0; i < ORC_HC; ++i) {
+            double dp = 0.0;
+            for (int64_t h = 0; h < H; ++h) {
+                dp += orc_bf16_to_f64(g[h]) * orc_bf16_to_f64(rr[i * H + h]);
+            }
+            const double s = orc_sigmoid(z[i]);
+            dz[i] = dp * s * (1.0 - s);
+            const double sp = orc_sigmoid(z[ORC_HC + i]);
+            dz[ORC_HC + i] = d_post[t * ORC_HC + i] * post_mult * sp * (1.0 - sp);
+        }
+        orc_sinkhorn_backward(d_comb + t * ORC_HC * ORC_HC, z + 2 * ORC_HC, 1, num_iters, sinkhorn_eps,
+                              dz + 2 * ORC_HC);
+        double d_rstd = 0.0;
+        for (int r = 0; r < ORC_MIX; ++r) {
+            const int grp = r < ORC_HC ? 0 : (r < 2 * ORC_HC ? 1 : 2);
+            d_hc_base[r] += dz[r];
+            d_hc_scale[grp] += dz[r] * m[r];
+            const double dm = dz[r] * (double)hc_scale[grp];
+            d_dot[t * ORC_MIX + r] = dm * rstd;
+            d_rstd += dm * d[r];
+        }
+        const double dS = -d_rstd * rstd * rstd * rstd / (2.0 * k);
+        if (sqrsum) {
+            d_sqrsum[t] = dS;
+        }
+        /* pre weights for the collapse term */
+        double pre[ORC_HC];
+        for (int i = 0; i < ORC_HC; ++i) {
+            pre[i] = orc_sigmoid(z[i]) + pre_eps;
+        }
+        for (int i = 0; i < ORC_HC; ++i) {
+            for (int64_t h = 0; h < H; ++h) {
+                double v = pre[i] * orc_bf16_to_f64(g[h]);
+                if (!sqrsum) {
+                    v += 2.0 * orc_bf16_to_f64(rr[i * H + h]) * dS;
+                }
+                d_res[(t * ORC_HC + i) * H + h] = v;
+            }
+        }
+    }
+}
+
+/* Reverse mode of the whole pre-map orc_pre (projection inside).  The dots and the
+ * sum of squares are recomputed from res (steps A1, A2), orc_pre_from_dots_backward
+ * runs with k = 4H and the sum of squares taken from res, and the projection
+ * dot[t][r] = sum_k hc_fn[r][k] res_flat[t][k] is reversed:
+ *   d_res_flat[t][k] += sum_r dd[t][r] hc_fn[r][k]
+ *   d_hc_fn[r][k]     = sum_t dd[t][r] res_flat[t][k]      (token order)
+ * d_res [T,4,H], d_hc_fn [24,4H], d_hc_scale [3], d_hc_base [24] are fp64 outputs.
+ * `scratch` holds 2 * 24 * T doubles. */
+void orc_pre_backward(const uint16_t *dy, const double *d_post, const double *d_comb, const uint16_t *res,
+                      const float *hc_fn, const float *hc_scale, const float *hc_base, int64_t T, int64_t H,
+                      double rms_eps, double pre_eps, double sinkhorn_eps, double post_mult, int num_iters,
+                      double *d_res, double *d_hc_fn, double *d_hc_scale, double *d_hc_base, double *scratch)
+{
+    const int64_t K = ORC_HC * H;
+    double *dot = scratch;
+    double *dd = scratch + ORC_MIX * T;
+    orc_project(res, hc_fn, T, H, dot);
+    orc_pre_from_dots_backward(dy, d_post, d_comb, dot, NULL, res, hc_scale, hc_base, T, H, (double)K, rms_eps,
+                               pre_eps, sinkhorn_eps, post_mult, num_iters, d_res, dd, NULL, d_hc_scale, d_hc_base);
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t kk = 0; kk < K; ++kk) {
+            double v = 0.0;
+            for (int r = 0; r < ORC_MIX; ++r) {
+                v += dd[t * ORC_MIX + r] * (double)hc_fn[r * K + kk];
+            }
+            d_res[t * K + kk] += v;
+        }
+    }
+    for (int r = 0; r < ORC_MIX; ++r) {
+        for (int64_t kk = 0; kk < K; ++kk) {
+            double v = 0.0;
+            for (int64_t t = 0; t < T; ++t) {
+                v += dd[t * ORC_MIX + r] * orc_bf16_to_f64(res[t * K + kk]);
+            }
+            d_hc_fn[r * K + kk] = v;
+        }
+    }
+}

@@ -517,3 +517,158 @@ def test_post_backward_directional_derivatives_and_identity():
     eye = np.broadcast_to(np.eye(HC), (3, HC, HC))
     d_x, d_res, _, _ = oracle.post_backward(G16, inp.x, inp.res, np.ones((3, HC)), eye)
     assert np.array_equal(d_res, G) and np.allclose(d_x, G.sum(axis=1), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- pre-map reverse mode
+#
+# The forward oracle is evaluated at inputs moved by +-d and +-2d along a random
+# direction; base values and steps are dyadic, so every moved input is exactly
+# representable in its dtype (bf16 streams, fp32 weights, scales, bases, dots).  The
+# Richardson combination (4 D(d) - D(2d)) / 3 of the central differences leaves an
+# O(d^4) truncation error.
+
+def _pre_bwd_case(seed, T=3, H=8):
+    g = np.random.default_rng(seed)
+    res_v = g.integers(-15, 16, (T, HC, H)) / 32.0      # |v| < 1/2: v +- 2^-9 and v +- 2^-8 are bf16
+    res = f32_to_bf16_bits(res_v.astype(np.float32))
+    hc_fn = (g.integers(-128, 129, (MIX, HC * H)) / 256.0).astype(np.float32)
+    hc_scale = np.array([0.75, 1.25, 1.5], np.float32)
+    hc_base = (g.integers(-64, 65, MIX) / 256.0).astype(np.float32)
+    dy = f32_to_bf16_bits(g.standard_normal((T, H)).astype(np.float32))
+    d_post = g.standard_normal((T, HC))
+    d_comb = g.standard_normal((T, HC, HC))
+    return res, hc_fn, hc_scale, hc_base, dy, d_post, d_comb
+
+
+def _pre_objective(out, dy, d_post, d_comb):
+    return (_bf16_f64(dy) * out["y"]).sum() + (d_post * out["post"]).sum() + (d_comb * out["comb"]).sum()
+
+
+def _richardson(J, step):
+    d1 = (J(step) - J(-step)) / (2 * step)
+    d2 = (J(2 * step) - J(-2 * step)) / (4 * step)
+    return (4 * d1 - d2) / 3
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_pre_backward_matches_finite_differences(seed):
+    res, hc_fn, hc_scale, hc_base, dy, d_post, d_comb = _pre_bwd_case(seed)
+    kw = dict(rms_eps=1e-3, pre_eps=1e-6, sinkhorn_eps=1e-6, post_mult=2.0, num_iters=20)
+    b = oracle.pre_backward(dy, d_post, d_comb, res, hc_fn, hc_scale, hc_base, **kw)
+    g = np.random.default_rng(100 + seed)
+    res_v = _bf16_f64(res)
+    v_res = g.integers(-1, 2, res.shape).astype(np.float64)
+    v_fn = g.integers(-1, 2, hc_fn.shape).astype(np.float64)
+    v_sc = np.array([1.0, -1.0, 1.0])
+    v_b = g.integers(-1, 2, MIX).astype(np.float64)
+
+    def J(dres=0.0, dfn=0.0, dsc=0.0, db=0.0):
+        r = f32_to_bf16_bits((res_v + dres * v_res).astype(np.float32))
+        assert np.array_equal(_bf16_f64(r), res_v + dres * v_res)  # the moved streams are exact
+        out = oracle.pre(r, (hc_fn + dfn * v_fn).astype(np.float32), (hc_scale + dsc * v_sc).astype(np.float32),
+                         (hc_base + db * v_b).astype(np.float32), **kw)
+        return _pre_objective(out, dy, d_post, d_comb)
+
+    checks = [
+        ((b["d_res"] * v_res).sum(), _richardson(lambda s: J(dres=s), 2.0 ** -9)),
+        ((b["d_hc_fn"] * v_fn).sum(), _richardson(lambda s: J(dfn=s), 2.0 ** -12)),
+        ((b["d_hc_scale"] * v_sc).sum(), _richardson(lambda s: J(dsc=s), 2.0 ** -10)),
+        ((b["d_hc_base"] * v_b).sum(), _richardson(lambda s: J(db=s), 2.0 ** -10)),
+    ]
+    for analytic, fd in checks:
+        assert abs(analytic - fd) < 1e-7 * max(1.0, abs(fd)), (analytic, fd)
+
+
+@pytest.mark.parametrize("supplied", [False, True])
+def test_pre_from_dots_backward_matches_finite_differences(supplied):
+    res, _, hc_scale, hc_base, dy, d_post, d_comb = _pre_bwd_case(5)
+    T, _, H = res.shape
+    g = np.random.default_rng(6)
+    dot = (g.integers(-512, 513, (T, MIX)) / 256.0).astype(np.float32)    # |d| <= 2, dyadic
+    sq = (g.integers(80, 240, T) / 16.0).astype(np.float32) if supplied else None
+    kw = dict(k=40.0, rms_eps=1e-3, pre_eps=1e-6, sinkhorn_eps=1e-6, post_mult=1.5, num_iters=20)
+    b = oracle.pre_from_dots_backward(dy, d_post, d_comb, dot, res, hc_scale, hc_base, sqrsum=sq, **kw)
+    res_v = _bf16_f64(res)
+    v_res = g.integers(-1, 2, res.shape).astype(np.float64)
+    v_dot = g.integers(-1, 2, dot.shape).astype(np.float64)
+    v_sq = g.integers(-1, 2, T).astype(np.float64)
+    v_sc = np.array([-1.0, 1.0, 1.0])
+    v_b = g.integers(-1, 2, MIX).astype(np.float64)
+
+    def J(dres=0.0, ddot=0.0, dsq=0.0, dsc=0.0, db=0.0):
+        r = f32_to_bf16_bits((res_v + dres * v_res).astype(np.float32))
+        assert np.array_equal(_bf16_f64(r), res_v + dres * v_res)
+        s = None if sq is None else (sq + dsq * v_sq).astype(np.float32)
+        out = oracle.pre_from_dots((dot + ddot * v_dot).astype(np.float32), r,
+                                   (hc_scale + dsc * v_sc).astype(np.float32),
+                                   (hc_base + db * v_b).astype(np.float32), sqrsum=s, **kw)
+        return _pre_objective(out, dy, d_post, d_comb)
+
+    checks = [
+        ((b["d_res"] * v_res).sum(), _richardson(lambda s: J(dres=s), 2.0 ** -9)),
+        ((b["d_dot"] * v_dot).sum(), _richardson(lambda s: J(ddot=s), 2.0 ** -10)),
+        ((b["d_hc_scale"] * v_sc).sum(), _richardson(lambda s: J(dsc=s), 2.0 ** -10)),
+        ((b["d_hc_base"] * v_b).sum(), _richardson(lambda s: J(db=s), 2.0 ** -10)),
+    ]
+    if supplied:
+        checks.append(((b["d_sqrsum"] * v_sq).sum(), _richardson(lambda s: J(dsq=s), 2.0 ** -8)))
+    else:
+        assert b["d_sqrsum"] is None
+    for analytic, fd in checks:
+        assert abs(analytic - fd) < 1e-7 * max(1.0, abs(fd)), (analytic, fd)
+
+
+def test_pre_backward_euler_homogeneity():
+    """With rms_eps = 0 the mixes are invariant to scaling the streams, and y is linear in
+    them, so d/dc J(c res) at c = 1 is <dy, y>: <d_res, res> = <dy, y> (projection, RMS and
+    collapse terms together)."""
+    res, hc_fn, hc_scale, hc_base, dy, d_post, d_comb = _pre_bwd_case(11, T=4, H=24)
+    kw = dict(rms_eps=0.0, pre_eps=1e-6, sinkhorn_eps=1e-6, post_mult=1.0, num_iters=20)
+    b = oracle.pre_backward(dy, d_post, d_comb, res, hc_fn, hc_scale, hc_base, **kw)
+    y = oracle.pre(res, hc_fn, hc_scale, hc_base, **kw)["y"]
+    lhs = (b["d_res"] * _bf16_f64(res)).sum()
+    rhs = (_bf16_f64(dy) * y).sum()
+    assert abs(lhs - rhs) < 1e-12 * max(1.0, abs(rhs))
+
+
+def test_pre_backward_scale_and_weight_rows_agree():
+    """Scaling the weight rows of group g by c equals scaling hc_scale[g] by c, so
+    sum over the group's rows of <d_hc_fn[r], hc_fn[r]> = d_hc_scale[g] * hc_scale[g]."""
+    res, hc_fn, hc_scale, hc_base, dy, d_post, d_comb = _pre_bwd_case(12, T=5, H=16)
+    b = oracle.pre_backward(dy, d_post, d_comb, res, hc_fn, hc_scale, hc_base)
+    for grp, rows in enumerate((slice(0, 4), slice(4, 8), slice(8, 24))):
+        lhs = (b["d_hc_fn"][rows] * hc_fn[rows].astype(np.float64)).sum()
+        assert abs(lhs - b["d_hc_scale"][grp] * float(hc_scale[grp])) < 1e-12 * max(1.0, abs(lhs))
+
+
+def test_pre_from_dots_backward_dot_and_square_scaling_invariance():
+    """With rms_eps = 0 and the sum of squares supplied, (dots * c, S * c^2) leaves every
+    mix unchanged: <d_dot, dot> + 2 <d_sqrsum, S> = 0."""
+    res, _, hc_scale, hc_base, dy, d_post, d_comb = _pre_bwd_case(13, T=6, H=8)
+    g = np.random.default_rng(14)
+    dot = g.standard_normal((6, MIX)) * 3
+    sq = g.uniform(5, 50, 6)
+    b = oracle.pre_from_dots_backward(dy, d_post, d_comb, dot, res, hc_scale, hc_base, sqrsum=sq, k=32.0,
+                                      rms_eps=0.0)
+    total = (b["d_dot"] * dot).sum() + 2 * (b["d_sqrsum"] * sq).sum()
+    assert abs(total) < 1e-12 * max(1.0, np.abs(b["d_dot"] * dot).sum())
+
+
+def test_pre_backward_zero_scale_reduces_to_the_logit_level_op():
+    """hc_scale = 0: the logits are hc_base alone, so the projection and the RMS statistic
+    receive no gradient, d_res = pre dy, and d_hc_base carries the sigmoid derivatives and
+    the Sinkhorn reverse mode of the logit-level pre-op."""
+    res, hc_fn, _, hc_base, dy, d_post, d_comb = _pre_bwd_case(15, T=4, H=16)
+    zero = np.zeros(3, np.float32)
+    b = oracle.pre_backward(dy, d_post, d_comb, res, hc_fn, zero, hc_base, post_mult=2.0)
+    assert np.array_equal(b["d_hc_fn"], np.zeros_like(b["d_hc_fn"]))
+    pre = 1 / (1 + np.exp(-hc_base[:4].astype(np.float64))) + 1e-6
+    dyv = _bf16_f64(dy)
+    assert np.allclose(b["d_res"], pre[None, :, None] * dyv[:, None, :], rtol=0, atol=1e-15)
+    s = 1 / (1 + np.exp(-hc_base.astype(np.float64)))
+    d_pre = np.einsum("th,tih->ti", dyv, _bf16_f64(res))
+    assert np.allclose(b["d_hc_base"][:4], (d_pre * (s[:4] * (1 - s[:4]))).sum(0), rtol=0, atol=1e-12)
+    assert np.allclose(b["d_hc_base"][4:8], (d_post * 2.0 * s[4:8] * (1 - s[4:8])).sum(0), rtol=0, atol=1e-12)
+    L = np.broadcast_to(hc_base[8:].astype(np.float64).reshape(HC, HC), (4, HC, HC))
+    dL = oracle.sinkhorn_backward(d_comb, L, 20, 1e-6).sum(0).reshape(-1)
+    assert np.allclose(b["d_hc_base"][8:], dL, rtol=0, atol=1e-12)
