@@ -50,7 +50,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="layer_h7168", choices=sorted(WORKLOADS))
     ap.add_argument("--only", default="all",
-                    choices=["all", "pre", "post", "sinkhorn", "pre_dots", "post_bwd", "sinkhorn_bwd"],
+                    choices=["all", "pre", "post", "sinkhorn", "pre_dots", "post_bwd", "sinkhorn_bwd", "pre_dots_bwd"],
                     help="run only one call in the timed loop (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
@@ -77,9 +77,9 @@ def main():
 
     import mhc_hyper_connection_amd as mhc
     from mhc_inputs import (algorithmic_bytes_post, algorithmic_bytes_post_backward, algorithmic_bytes_pre,
-                            algorithmic_bytes_pre_dots, algorithmic_bytes_sinkhorn,
-                            algorithmic_bytes_sinkhorn_backward, layer_inputs, post_grad, sinkhorn_grad,
-                            sinkhorn_logits)
+                            algorithmic_bytes_pre_dots, algorithmic_bytes_pre_dots_backward,
+                            algorithmic_bytes_sinkhorn, algorithmic_bytes_sinkhorn_backward, external_dots,
+                            layer_inputs, post_grad, pre_grads, sinkhorn_grad, sinkhorn_logits)
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
@@ -137,6 +137,20 @@ def main():
         mhc.mhc_pre_from_dots(dots, res, hc_scale, hc_base, None, None, p["rms_eps"], p["pre_eps"],
                               p["sinkhorn_eps"], p["post_mult"], p["num_iters"], y=y, post=post, comb=comb)
 
+    if args.only == "pre_dots_bwd":
+        g_dy, g_post, g_comb = pre_grads(T, H, cfg=cfg)
+        g_dy = bf16(g_dy)
+        g_post = torch.from_numpy(g_post).to(dev)
+        g_comb = torch.from_numpy(g_comb).to(dev)
+        bdots = torch.from_numpy(external_dots(T, H, cfg=cfg)[0]).to(dev)
+        d_res_b = torch.empty_like(res)
+        ws_b = torch.empty(max(mhc.mhc_pre_backward_workspace_bytes(T), 1), dtype=torch.uint8, device=dev)
+
+    def call_pre_dots_bwd():
+        mhc.mhc_pre_from_dots_backward(g_dy, g_post, g_comb, bdots, res, hc_scale, hc_base, None, None,
+                                       p["rms_eps"], p["pre_eps"], p["sinkhorn_eps"], p["post_mult"],
+                                       p["num_iters"], d_res=d_res_b, workspace=ws_b)
+
     def call_sinkhorn():
         mhc.mhc_sinkhorn(sk_logits, out=sk_out, num_iters=p["num_iters"], eps=p["sinkhorn_eps"])
 
@@ -163,6 +177,8 @@ def main():
             call_sinkhorn_bwd()
         if args.only == "post_bwd":
             call_post_bwd()
+        if args.only == "pre_dots_bwd":
+            call_pre_dots_bwd()
 
     stream = torch.cuda.current_stream(dev)
 
@@ -202,6 +218,8 @@ def main():
         breakdown["sinkhorn_bwd_ms"] = ms_step
     if args.only == "post_bwd":
         breakdown["post_bwd_ms"] = ms_step
+    if args.only == "pre_dots_bwd":
+        breakdown["pre_dots_bwd_ms"] = ms_step
 
     if args.only == "sinkhorn":
         step_bytes = algorithmic_bytes_sinkhorn(sk_logits.shape[0])
@@ -209,6 +227,8 @@ def main():
         step_bytes = algorithmic_bytes_sinkhorn_backward(sk_logits.shape[0])
     elif args.only == "post_bwd":
         step_bytes = algorithmic_bytes_post_backward(T, H)
+    elif args.only == "pre_dots_bwd":
+        step_bytes = algorithmic_bytes_pre_dots_backward(T, H)
     elif args.only == "pre_dots":
         step_bytes = algorithmic_bytes_pre_dots(T, H)
     else:
@@ -232,6 +252,9 @@ def main():
         calls["mhc_sinkhorn_backward"] = ("sinkhorn_bwd_kernel", breakdown["sinkhorn_bwd_ms"], step_bytes)
     if "post_bwd_ms" in breakdown:
         calls["mhc_post_backward"] = ("post_bwd_kernel", breakdown["post_bwd_ms"], step_bytes)
+    if "pre_dots_bwd_ms" in breakdown:
+        calls["mhc_pre_from_dots_backward"] = ("pre_dots_bwd_kernel+pre_bwd_partial_kernel+pre_bwd_final_kernel",
+                                               breakdown["pre_dots_bwd_ms"], step_bytes)
     traffic = load_traffic(T, H)
     per_call = {}
     for name, (kern, ms_k, bytes_k) in calls.items():

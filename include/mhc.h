@@ -215,6 +215,54 @@ mhc_status mhc_post_backward(const uint16_t *d_out, const uint16_t *x, const uin
                              const float *comb, int64_t T, int64_t H, uint16_t *d_x, uint16_t *d_res,
                              float *d_post, float *d_comb, void *stream);
 
+/*
+ * Size in bytes of the device workspace mhc_pre_from_dots_backward needs for T tokens:
+ * one row of 28 fp32 per token (24 logit gradients and 3 per-group scale terms) and
+ * one such row per 256 tokens for the partial sums over the tokens, each part rounded
+ * up to 256 bytes.  Returns 0 for T <= 0.
+ */
+size_t mhc_pre_backward_workspace_bytes(int64_t T);
+
+/*
+ * mhc_pre_from_dots_backward -- gradients of mhc_pre_from_dots: the rwkv-ops
+ * mhc_pre_op custom VJP (MhcPreOpBwd: sigmoid weights, Sinkhorn, stream aggregate),
+ * extended by the FlashInfer mixes in front of it (FlashInfer mHC article,
+ * section 5.2: m = d * rstd, per-group scale and base, pre_eps, post_mult).  The
+ * forward's mixes are recomputed from the same inputs.  With z_r = m_r * s_g + b_r:
+ *     d_pre_i   = sum_h dy[t][h] res[t][i][h];   dz_i = d_pre_i sigma'(z_i)            (i < 4)
+ *     dz_{4+i}  = d_post[t][i] post_mult sigma'(z_{4+i})
+ *     dz_{8..}  = Sinkhorn reverse mode of d_comb[t] at the comb logits (as mhc_sinkhorn_backward)
+ *     d_dot[t][r] = dz_r s_g rstd_t                          (the same for every split)
+ *     dS_t      = -(sum_r dz_r s_g d_r) rstd_t^3 / (2k)
+ *     d_res[t][i][h] = bf16( pre_i dy[t][h] + 2 dS_t res[t][i][h] )   (second term only when
+ *                      sqrsum is NULL, i.e. when the forward computed S from res)
+ *     d_sqrsum[s][t] = dS_t for every split s                 (only when sqrsum is given)
+ *     d_hc_base[r] = sum_t dz_r,  d_hc_scale[g] = sum_t sum_{r in group g} dz_r m_r
+ *   (token sums in a fixed order; repeated calls are bit-identical)
+ *
+ *   dy [T,H] bf16, d_post [T,4] fp32, d_comb [T,4,4] fp32   gradients of y, post, comb
+ *   dot_mix, sqrsum, num_splits, res, hc_scale, hc_base, T, H, k, rms_eps, pre_eps,
+ *   sinkhorn_eps, post_mult, num_iters   the forward's inputs, as in mhc_pre_from_dots;
+ *               here 1 <= num_iters <= MHC_SINKHORN_BWD_MAX_ITERS
+ *   d_res [T,4,H] bf16   output; may equal `res` exactly (every element is read before
+ *               it is written), no other overlap
+ *   d_dot [T,24] fp32    output: gradient of each split's partial dots
+ *   d_sqrsum [T] fp32    output, required when sqrsum is given (gradient of each split's
+ *               partial), ignored (may be NULL) otherwise
+ *   d_hc_scale [3], d_hc_base [24] fp32   outputs, overwritten (not accumulated).  For
+ *               T == 0 they are set to zero (one small launch) and nothing else runs.
+ *   workspace   device scratch of at least mhc_pre_backward_workspace_bytes(T) bytes,
+ *               256-byte aligned (may be NULL when T == 0); contents on entry ignored
+ * No output may overlap an input, the workspace or another output, except as stated.
+ */
+mhc_status mhc_pre_from_dots_backward(const uint16_t *dy, const float *d_post, const float *d_comb,
+                                      const float *dot_mix, const float *sqrsum, int32_t num_splits,
+                                      const uint16_t *res, const float *hc_scale, const float *hc_base, int64_t T,
+                                      int64_t H, float k, float rms_eps, float pre_eps, float sinkhorn_eps,
+                                      float post_mult, int32_t num_iters, uint16_t *d_res, float *d_dot,
+                                      float *d_sqrsum, float *d_hc_scale, float *d_hc_base, void *workspace,
+                                      size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

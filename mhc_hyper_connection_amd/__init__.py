@@ -62,6 +62,11 @@ def lib() -> ctypes.CDLL:
     L.mhc_sinkhorn_backward.restype = ctypes.c_int
     L.mhc_post_backward.argtypes = [P, P, P, P, P, I64, I64, P, P, P, P, P]
     L.mhc_post_backward.restype = ctypes.c_int
+    L.mhc_pre_backward_workspace_bytes.argtypes = [I64]
+    L.mhc_pre_backward_workspace_bytes.restype = SZ
+    L.mhc_pre_from_dots_backward.argtypes = [P, P, P, P, P, I32, P, P, P, I64, I64, F, F, F, F, F, I32, P, P, P, P,
+                                             P, P, SZ, P]
+    L.mhc_pre_from_dots_backward.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -340,6 +345,76 @@ def mhc_post_backward(d_out: torch.Tensor, x: torch.Tensor, res: torch.Tensor, p
     return d_x, d_res, d_post, d_comb
 
 
+def mhc_pre_backward_workspace_bytes(T: int) -> int:
+    return int(lib().mhc_pre_backward_workspace_bytes(int(T)))
+
+
+def mhc_pre_from_dots_backward(dy: torch.Tensor, d_post: torch.Tensor, d_comb: torch.Tensor,
+                               dot_mix: torch.Tensor, res: torch.Tensor, hc_scale: torch.Tensor,
+                               hc_base: torch.Tensor, sqrsum: torch.Tensor | None = None, k: float | None = None,
+                               rms_eps: float = 1e-6, pre_eps: float = 1e-6, sinkhorn_eps: float = 1e-6,
+                               post_mult: float = 1.0, num_iters: int = 20, *, d_res: torch.Tensor | None = None,
+                               workspace: torch.Tensor | None = None) -> dict:
+    """Gradients of :func:`mhc_pre_from_dots` for the output gradients dy [..., H] bf16,
+    d_post [..., 4] (or [..., 4, 1]) and d_comb [..., 4, 4] fp32.  dot_mix and sqrsum as in
+    the forward.  Returns a dict: d_res [..., 4, H] bf16, d_dot [..., 24] fp32 (the gradient
+    of every split's partial dots), d_sqrsum [...] fp32 or None, d_hc_scale [3], d_hc_base [24].
+    ``d_res`` may be ``res``."""
+    _need(res, "res", torch.bfloat16)
+    if res.dim() < 2 or res.shape[-2] != HC:
+        raise ValueError(f"residual.shape[-2] / HC must be 4, got {tuple(res.shape)}")
+    H = res.shape[-1]
+    outer = tuple(res.shape[:-2])
+    T = res.numel() // (HC * H) if H > 0 else 0
+    _need(dy, "dy", torch.bfloat16)
+    if tuple(dy.shape) != outer + (H,):
+        raise ValueError(f"dy must be {outer + (H,)}, got {tuple(dy.shape)}")
+    _need(d_post, "d_post", torch.float32)
+    if tuple(d_post.shape) not in (outer + (HC,), outer + (HC, 1)):
+        raise ValueError(f"d_post must be {outer + (HC,)} or {outer + (HC, 1)}, got {tuple(d_post.shape)}")
+    _need(d_comb, "d_comb", torch.float32)
+    if tuple(d_comb.shape) != outer + (HC, HC):
+        raise ValueError(f"d_comb must be {outer + (HC, HC)}, got {tuple(d_comb.shape)}")
+    _need(dot_mix, "dot_mix", torch.float32)
+    if tuple(dot_mix.shape) == outer + (MIX,):
+        splits = 1
+    elif dot_mix.dim() == len(outer) + 2 and tuple(dot_mix.shape[1:]) == outer + (MIX,):
+        splits = dot_mix.shape[0]
+    else:
+        raise ValueError(f"dot_mix must be {outer + (MIX,)} or [S, *{outer + (MIX,)}], got {tuple(dot_mix.shape)}")
+    if sqrsum is not None:
+        _need(sqrsum, "sqrsum", torch.float32)
+        if sqrsum.numel() != splits * T:
+            raise ValueError(f"sqrsum must hold num_splits * T = {splits * T} values, got {sqrsum.numel()}")
+    _need(hc_scale, "hc_scale", torch.float32)
+    _need(hc_base, "hc_base", torch.float32)
+    if hc_scale.numel() != 3 or hc_base.numel() != MIX:
+        raise ValueError("hc_scale must have 3 values and hc_base 24")
+    if d_res is None:
+        d_res = torch.empty_like(res)
+    _need(d_res, "d_res", torch.bfloat16)
+    if d_res.shape != res.shape:
+        raise ValueError("d_res must have the shape of res")
+    dev = res.device
+    d_dot = torch.empty(outer + (MIX,), dtype=torch.float32, device=dev)
+    d_sq = torch.empty(outer, dtype=torch.float32, device=dev) if sqrsum is not None else None
+    d_scale = torch.empty(3, dtype=torch.float32, device=dev)
+    d_base = torch.empty(MIX, dtype=torch.float32, device=dev)
+    need = mhc_pre_backward_workspace_bytes(T)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _same_device(dy, d_post, d_comb, dot_mix, sqrsum, res, hc_scale, hc_base, d_res, workspace)
+    kk = float(HC * H) if k is None else float(k)
+    _check("mhc_pre_from_dots_backward",
+           lib().mhc_pre_from_dots_backward(_ptr(dy), _ptr(d_post), _ptr(d_comb), _ptr(dot_mix), _ptr(sqrsum),
+                                            int(splits), _ptr(res), _ptr(hc_scale), _ptr(hc_base), T, H, kk,
+                                            float(rms_eps), float(pre_eps), float(sinkhorn_eps), float(post_mult),
+                                            int(num_iters), _ptr(d_res), _ptr(d_dot), _ptr(d_sq), _ptr(d_scale),
+                                            _ptr(d_base), _ptr(workspace), workspace.numel(), _stream(dev)))
+    return dict(d_res=d_res, d_dot=d_dot, d_sqrsum=d_sq, d_hc_scale=d_scale, d_hc_base=d_base)
+
+
 __all__ = ["mhc_sinkhorn", "mhc_pre_fused", "mhc_pre_fused_workspace_bytes", "mhc_pre_from_dots", "mhc_post",
-           "mhc_sinkhorn_backward", "mhc_post_backward", "lib", "abi_version", "status_string", "MHCError", "HC",
+           "mhc_sinkhorn_backward", "mhc_post_backward", "mhc_pre_from_dots_backward",
+           "mhc_pre_backward_workspace_bytes", "lib", "abi_version", "status_string", "MHCError", "HC",
            "MIX", "SINKHORN_BWD_MAX_ITERS"]

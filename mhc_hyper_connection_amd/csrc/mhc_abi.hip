@@ -258,4 +258,72 @@ mhc_status mhc_post_backward(const uint16_t *d_out, const uint16_t *x, const uin
                                               (hipStream_t)stream, vec8));
 }
 
+size_t mhc_pre_backward_workspace_bytes(int64_t T)
+{
+    if (T <= 0 || T > kMaxDim) {
+        return 0;
+    }
+    return mhc::pre_bwd_workspace_bytes(T);
+}
+
+mhc_status mhc_pre_from_dots_backward(const uint16_t *dy, const float *d_post, const float *d_comb,
+                                      const float *dot_mix, const float *sqrsum, int32_t num_splits,
+                                      const uint16_t *res, const float *hc_scale, const float *hc_base, int64_t T,
+                                      int64_t H, float k, float rms_eps, float pre_eps, float sinkhorn_eps,
+                                      float post_mult, int32_t num_iters, uint16_t *d_res, float *d_dot,
+                                      float *d_sqrsum, float *d_hc_scale, float *d_hc_base, void *workspace,
+                                      size_t workspace_bytes, void *stream)
+{
+    if (!sizes_ok(T, H) || num_splits < 1 || num_splits > 65536 || num_iters < 1 ||
+        num_iters > MHC_SINKHORN_BWD_MAX_ITERS || !finite(k) || !(k > 0.0f) || !finite(rms_eps) ||
+        !(rms_eps > 0.0f) || !finite(pre_eps) || pre_eps < 0.0f || !finite(sinkhorn_eps) || !(sinkhorn_eps > 0.0f) ||
+        !finite(post_mult)) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    if (!d_hc_scale || !d_hc_base || overlaps(d_hc_scale, 3 * 4, d_hc_base, 24 * 4)) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    if (T == 0) {
+        return launch_status(mhc::launch_pre_dots_bwd(nullptr, nullptr, nullptr, nullptr, nullptr, num_splits,
+                                                      nullptr, nullptr, nullptr, 0, H, k, rms_eps, pre_eps,
+                                                      sinkhorn_eps, post_mult, num_iters, nullptr, nullptr, nullptr,
+                                                      d_hc_scale, d_hc_base, nullptr, (hipStream_t)stream, false));
+    }
+    if (!dy || !d_post || !d_comb || !dot_mix || !res || !hc_scale || !hc_base || !d_res || !d_dot ||
+        (sqrsum && !d_sqrsum)) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    const size_t need = mhc::pre_bwd_workspace_bytes(T);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0) {
+        return MHC_ERROR_WORKSPACE;
+    }
+    if (!sqrsum) {
+        d_sqrsum = nullptr;
+    }
+    const size_t res_b = (size_t)T * 4 * H * 2, y_b = (size_t)T * H * 2;
+    const size_t dm_b = (size_t)num_splits * T * 24 * 4, sq_b = sqrsum ? (size_t)num_splits * T * 4 : 0;
+    const void *outs[6] = {d_res, d_dot, d_sqrsum, d_hc_scale, d_hc_base, workspace};
+    const size_t outn[6] = {res_b, (size_t)T * 24 * 4, d_sqrsum ? (size_t)T * 4 : 0, 3 * 4, 24 * 4, need};
+    const void *ins[8] = {dy, d_post, d_comb, dot_mix, sqrsum, res, hc_scale, hc_base};
+    const size_t inn[8] = {y_b, (size_t)T * 16, (size_t)T * 64, dm_b, sq_b, res_b, 3 * 4, 24 * 4};
+    for (int o = 0; o < 6; ++o) {
+        for (int i = 0; i < 8; ++i) {
+            const bool in_place = o == 0 && i == 5 && (const void *)d_res == (const void *)res;
+            if (!in_place && overlaps(outs[o], outn[o], ins[i], inn[i])) {
+                return MHC_ERROR_INVALID_VALUE;
+            }
+        }
+        for (int o2 = o + 1; o2 < 6; ++o2) {
+            if (overlaps(outs[o], outn[o], outs[o2], outn[o2])) {
+                return MHC_ERROR_INVALID_VALUE;
+            }
+        }
+    }
+    const bool vec8 = (H % 8 == 0) && aligned16(dy) && aligned16(res) && aligned16(d_res);
+    return launch_status(mhc::launch_pre_dots_bwd(dy, d_post, d_comb, dot_mix, sqrsum, num_splits, res, hc_scale,
+                                                  hc_base, T, H, k, rms_eps, pre_eps, sinkhorn_eps, post_mult,
+                                                  num_iters, d_res, d_dot, d_sqrsum, d_hc_scale, d_hc_base, workspace,
+                                                  (hipStream_t)stream, vec8));
+}
+
 } // extern "C"

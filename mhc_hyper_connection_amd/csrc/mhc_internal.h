@@ -48,6 +48,16 @@ size_t sinkhorn_bwd_lds_bytes(int iters);
 hipError_t launch_sinkhorn_bwd(const float *grad, const float *logits, int64_t n, int iters, float eps,
                                float *d_logits, hipStream_t stream);
 
+// Reverse mode of the pre-map from external dots (one workgroup per token), then the
+// fixed-order token sums of d_hc_scale and d_hc_base from a [T][28] fp32 workspace.
+size_t pre_bwd_workspace_bytes(int64_t T);
+hipError_t launch_pre_dots_bwd(const uint16_t *dy, const float *d_post, const float *d_comb, const float *dot_mix,
+                               const float *sqrsum, int num_splits, const uint16_t *res, const float *hc_scale,
+                               const float *hc_base, int64_t T, int64_t H, float k, float rms_eps, float pre_eps,
+                               float sinkhorn_eps, float post_mult, int iters, uint16_t *d_res, float *d_dot,
+                               float *d_sqrsum, float *d_hc_scale, float *d_hc_base, void *workspace,
+                               hipStream_t stream, bool vec8);
+
 // Reverse mode of the post-map (one workgroup per token).  `vec8`: H % 8 == 0 and
 // d_out/x/res/d_x/d_res 16-byte aligned.
 hipError_t launch_post_bwd(const uint16_t *d_out, const uint16_t *x, const uint16_t *res, const float *post,

@@ -37,6 +37,10 @@ _TID = {
     "hc_scale": 8,
     "grad": 9,
     "d_out": 10,
+    "dy": 11,
+    "d_post": 12,
+    "d_comb": 13,
+    "dots": 14,
 }
 
 
@@ -178,6 +182,23 @@ def post_grad(T: int, H: int, cfg: int = 2, seed: int = 0) -> np.ndarray:
     return normal_bf16(seed, cfg, "d_out", (T, HC, H))
 
 
+def pre_grads(T: int, H: int, cfg: int = 3, seed: int = 0):
+    """Output gradients of the pre-map: dy [T, H] bf16 ~ N(0, 1), d_post [T, 4] and
+    d_comb [T, 4, 4] fp32 ~ N(0, 1)."""
+    dy = normal_bf16(seed, cfg, "dy", (T, H))
+    d_post = normal_f32(seed, cfg, "d_post", (T, HC), 1.0)
+    d_comb = normal_f32(seed, cfg, "d_comb", (T, HC, HC), 1.0)
+    return dy, d_post, d_comb
+
+
+def external_dots(T: int, H: int, cfg: int = 3, seed: int = 0, splits: int = 1, hc_fn_std: float = 0.02):
+    """[splits, T, 24] fp32 partial dots with the spread of the layer workload's projection:
+    the full dot of N(0, 1) streams with N(0, hc_fn_std) weights has std hc_fn_std * sqrt(4H),
+    shared evenly between the splits."""
+    std = hc_fn_std * (HC * H) ** 0.5 / splits ** 0.5
+    return normal_f32(seed, cfg, "dots", (splits, T, MIX), std)
+
+
 def algorithmic_bytes_pre(T: int, H: int) -> int:
     """Bytes the pre-map must move: res read, y written, post/comb written, hc_fn + scale/base read once."""
     return T * (8 * H + 2 * H + 16 + 64) + 384 * H + 108
@@ -202,6 +223,12 @@ def algorithmic_bytes_post_backward(T: int, H: int) -> int:
     """Bytes the post-map reverse mode must move: d_out, x and res read, 80 B of mixes read,
     d_x and d_res written, 80 B of mix gradients written."""
     return T * (8 * H + 2 * H + 8 * H + 80 + 2 * H + 8 * H + 80)
+
+
+def algorithmic_bytes_pre_dots_backward(T: int, H: int, splits: int = 1, sqrsum: bool = False) -> int:
+    """Bytes the pre-map reverse mode (external dots) must move: dy, res, d_post, d_comb and the
+    dot partials read, d_res and d_dot written (plus the sum-of-squares partial and its gradient)."""
+    return T * (2 * H + 8 * H + 16 + 64 + splits * 96 + 8 * H + 96 + (splits * 4 + 4 if sqrsum else 0))
 
 
 def algorithmic_bytes_sinkhorn_backward(n: int) -> int:

@@ -26,7 +26,8 @@ def test_library_exports_every_declared_symbol():
     lib = mhc.lib()
     names = _declared()
     assert {"mhc_sinkhorn", "mhc_pre_fused", "mhc_pre_fused_workspace_bytes", "mhc_pre_from_dots", "mhc_post",
-            "mhc_sinkhorn_backward", "mhc_post_backward", "mhc_abi_version", "mhc_status_string"} <= set(names)
+            "mhc_sinkhorn_backward", "mhc_post_backward", "mhc_pre_from_dots_backward",
+            "mhc_pre_backward_workspace_bytes", "mhc_abi_version", "mhc_status_string"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -180,6 +181,43 @@ def test_post_backward_validation():
     assert call(dp=0x710000 - 64) == E     # d_post overlaps d_comb
     assert call(dc=0x410000) == E          # d_comb is comb
     assert call(T=0, **{n: None for n in base}) == mhc.MHC_SUCCESS
+
+
+def _dbwd(lib, **kw):
+    a = dict(dy=0x100000, dpost=0x200000, dcomb=0x210000, dm=0x300000, sq=None, S=1, res=0x400000,
+             sc=0x500000, base=0x500100, T=8, H=64, k=256.0, rms=1e-6, pe=1e-6, se=1e-6, pm=1.0, it=20,
+             dres=0x600000, ddot=0x700000, dsq=None, dsc=0x800000, dbase=0x800100, ws=0x900000, wsb=1 << 20)
+    a.update(kw)
+    v = lambda n: ctypes.c_void_p(a[n]) if a[n] is not None else None
+    return lib.mhc_pre_from_dots_backward(v("dy"), v("dpost"), v("dcomb"), v("dm"), v("sq"), a["S"], v("res"),
+                                          v("sc"), v("base"), a["T"], a["H"], a["k"], a["rms"], a["pe"], a["se"],
+                                          a["pm"], a["it"], v("dres"), v("ddot"), v("dsq"), v("dsc"), v("dbase"),
+                                          v("ws"), a["wsb"], NULL)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(T=-1), dict(H=0), dict(S=0), dict(S=65537), dict(it=0), dict(it=256), dict(k=0.0), dict(rms=0.0),
+    dict(se=0.0), dict(pe=-1.0), dict(pm=float("inf")), dict(dy=None), dict(dpost=None), dict(dcomb=None),
+    dict(dm=None), dict(res=None), dict(sc=None), dict(base=None), dict(dres=None), dict(ddot=None),
+    dict(dsc=None), dict(dbase=None), dict(T=0, dsc=None),
+    dict(sq=0x380000),                              # sqrsum given without d_sqrsum
+    dict(dres=0x400000 + 64),                       # d_res overlaps res without being it
+    dict(ddot=0x300000 + 32),                       # d_dot overlaps dot_mix
+    dict(dbase=0x800000 + 8),                       # d_hc_base overlaps d_hc_scale
+    dict(ws=0x600000 + 256),                        # workspace overlaps d_res
+])
+def test_pre_from_dots_backward_validation_invalid(kw):
+    assert _dbwd(mhc.lib(), **kw) == mhc.MHC_ERROR_INVALID_VALUE
+
+
+def test_pre_from_dots_backward_workspace():
+    lib = mhc.lib()
+    need = mhc.mhc_pre_backward_workspace_bytes(8)
+    assert need >= 8 * 28 * 4 and need % 256 == 0
+    assert mhc.mhc_pre_backward_workspace_bytes(0) == 0
+    assert _dbwd(lib, wsb=need - 1) == mhc.MHC_ERROR_WORKSPACE
+    assert _dbwd(lib, ws=None) == mhc.MHC_ERROR_WORKSPACE
+    assert _dbwd(lib, ws=0x900000 + 16) == mhc.MHC_ERROR_WORKSPACE
 
 
 def test_binding_rejects_cpu_tensors_before_the_library():

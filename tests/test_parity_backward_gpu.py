@@ -8,12 +8,16 @@ Tolerances (derived from the fp32 arithmetic of the kernels):
   * d_post, d_comb: |err| <= 1e-5 * sum_h |a_h b_h| + 1e-6: a sum of H products
     in fp32 with at most a few dozen roundings on any path of the reduction tree
     (about 40 * 2^-24 = 2.4e-6 relative to sum |a b|).
+  * pre-map reverse mode: each fp32 quantity within 1e-5 of its own magnitude, plus
+    the worst case of its one long reduction, d_pre_i = sum_h dy res_i (2.5e-6 *
+    sum_h |dy res_i|), carried through the chain (see _pre_bwd_tolerances).
 """
 import numpy as np
 import pytest
 
 import oracle
-from mhc_inputs import (HC, bf16_bits_to_f32, post_grad, post_inputs, sinkhorn_grad, sinkhorn_logits)
+from mhc_inputs import (HC, MIX, bf16_bits_to_f32, external_dots, layer_inputs, post_grad, post_inputs, pre_grads,
+                        sinkhorn_grad, sinkhorn_logits)
 from tests._helpers import assert_bf16_close, bits_of, f32_of, sample_tokens, to_dev_bf16, to_dev_f32
 
 pytestmark = pytest.mark.gpu
@@ -190,3 +194,145 @@ def test_post_backward_deterministic_and_empty():
     out = mhc.mhc_post_backward(z, torch.empty(0, 64, dtype=torch.bfloat16, device="cuda"), z,
                                 torch.empty(0, HC, device="cuda"), torch.empty(0, HC, HC, device="cuda"))
     assert all(o.numel() == 0 for o in out)
+
+
+# ----------------------------------------------------------------------------- pre-map reverse mode (external dots)
+
+def _pre_bwd_case(T, H, splits, supplied, cfg):
+    inp = layer_inputs(T, H, cfg=cfg, scale=(0.9, 1.1, 1.3))
+    dm = external_dots(T, H, cfg=cfg, splits=splits)
+    sq = None
+    if supplied:
+        full = (bf16_bits_to_f32(inp.res).astype(np.float64) ** 2).sum(axis=(1, 2))
+        sq = np.repeat((full / splits)[None, :], splits, axis=0).astype(np.float32)
+    dy, d_post, d_comb = pre_grads(T, H, cfg=cfg)
+    return inp, dm, sq, dy, d_post, d_comb
+
+
+def _pre_bwd_tolerances(inp, dm, sq, dy, d_post, d_comb, k, ref, post_mult=1.0):
+    """Per-element tolerances for the outputs of the pre-map reverse mode (fp32 arithmetic).
+
+    Besides 1e-5 of each value: the worst case of the d_pre reduction, and the sigmoid
+    derivative sigma (1 - sigma) formed from an fp32 sigma, whose absolute error is a few
+    ulp of 1 (bounded by 1e-6 here), times the gradient it multiplies."""
+    res = bf16_bits_to_f32(inp.res).astype(np.float64)
+    dyv = bf16_bits_to_f32(dy).astype(np.float64)
+    d = dm.astype(np.float64).sum(axis=0)
+    S = (res ** 2).sum(axis=(1, 2)) if sq is None else sq.astype(np.float64).sum(axis=0)
+    rstd = 1 / np.sqrt(S / k + 1e-6)
+    s = inp.hc_scale.astype(np.float64)
+    sg = np.concatenate([np.full(4, s[0]), np.full(4, s[1]), np.full(16, s[2])])
+    A = np.einsum("th,tih->ti", np.abs(dyv), np.abs(res))       # sum_h |dy res_i|
+    rel = 1e-5
+    tol_dot = rel * np.abs(ref["d_dot"])
+    tol_dot[:, :4] += (2.5e-6 * 0.25 + 1e-6) * rstd[:, None] * abs(s[0]) * A
+    tol_dot[:, 4:8] += 1e-6 * rstd[:, None] * abs(s[1]) * abs(post_mult) * np.abs(d_post) + 1e-7
+    tol_dot[:, 8:] += rel * abs(s[2]) * rstd[:, None] * np.abs(d_comb).reshape(-1, 16).max(axis=1)[:, None]
+    tol_dS = rstd ** 2 / (2 * k) * ((rel * np.abs(ref["d_dot"]) + tol_dot) * np.abs(d)).sum(axis=1)
+    tol_dz = tol_dot / (np.abs(sg)[None, :] * rstd[:, None])
+    dz = ref["d_dot"] / (sg[None, :] * rstd[:, None])
+    m = d * rstd[:, None]
+    tol_base = (tol_dz + rel * np.abs(dz)).sum(axis=0)
+    tz = (tol_dz * np.abs(m) + rel * np.abs(dz * m))
+    tol_scale = np.array([tz[:, :4].sum(), tz[:, 4:8].sum(), tz[:, 8:].sum()])
+    extra_res = (2 * tol_dS)[:, None, None] * np.abs(res) if sq is None else 0.0
+    return dict(d_dot=tol_dot, d_sqrsum=rel * np.abs(ref["d_sqrsum"] if ref["d_sqrsum"] is not None else 0) + tol_dS,
+                d_hc_base=tol_base, d_hc_scale=tol_scale, d_res_extra=extra_res)
+
+
+def _assert_within(got, ref, tol, what):
+    err = np.abs(np.asarray(got, np.float64) - ref)
+    bad = ~(err <= tol)
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside tolerance; first at {idx.tolist()}; "
+                             f"max err/tol {(err / np.maximum(tol, 1e-30)).max():.3e}")
+
+
+def _run_pre_bwd(case, k=None, **kw):
+    mhc = _mhc()
+    inp, dm, sq, dy, d_post, d_comb = case
+    T, _, H = inp.res.shape
+    dmd = to_dev_f32(dm if dm.shape[0] > 1 else dm[0])
+    out = mhc.mhc_pre_from_dots_backward(to_dev_bf16(dy), to_dev_f32(d_post), to_dev_f32(d_comb), dmd,
+                                         to_dev_bf16(inp.res), to_dev_f32(inp.hc_scale), to_dev_f32(inp.hc_base),
+                                         sqrsum=None if sq is None else to_dev_f32(sq), k=k, **kw)
+    torch.cuda.synchronize()
+    return dict(d_res=bits_of(out["d_res"]), d_dot=f32_of(out["d_dot"]),
+                d_sqrsum=None if out["d_sqrsum"] is None else f32_of(out["d_sqrsum"]),
+                d_hc_scale=f32_of(out["d_hc_scale"]), d_hc_base=f32_of(out["d_hc_base"]))
+
+
+def _check_pre_bwd(got, case, what, k=None, tokens=None):
+    inp, dm, sq, dy, d_post, d_comb = case
+    T, _, H = inp.res.shape
+    kk = float(4 * H) if k is None else k
+    ref = oracle.pre_from_dots_backward(dy, d_post, d_comb, dm.astype(np.float64).sum(axis=0), inp.res,
+                                        inp.hc_scale, inp.hc_base,
+                                        sqrsum=None if sq is None else sq.astype(np.float64).sum(axis=0), k=kk)
+    tol = _pre_bwd_tolerances(inp, dm, sq, dy, d_post, d_comb, kk, ref)
+    _assert_within(got["d_hc_base"], ref["d_hc_base"], tol["d_hc_base"], what + " d_hc_base")
+    _assert_within(got["d_hc_scale"], ref["d_hc_scale"], tol["d_hc_scale"], what + " d_hc_scale")
+    sel = slice(None) if tokens is None else tokens
+    _assert_within(got["d_dot"][sel], ref["d_dot"][sel], tol["d_dot"][sel], what + " d_dot")
+    if sq is not None:
+        _assert_within(got["d_sqrsum"][sel], ref["d_sqrsum"][sel], tol["d_sqrsum"][sel], what + " d_sqrsum")
+    gres = bf16_bits_to_f32(got["d_res"][sel]).astype(np.float64)
+    rres = ref["d_res"][sel]
+    extra = tol["d_res_extra"][sel] if sq is None else 0.0
+    _assert_within(gres, rres, 2.0 ** -7 * np.abs(rres) + 1e-3 + extra, what + " d_res")
+
+
+PRE_BWD_SHAPES = [(16, 256, 1, False), (5, 64, 1, True), (7, 127, 1, False), (3, 1001, 2, True),
+                  (37, 4096, 1, False), (21, 7168, 3, False), (9, 16392, 1, False), (1, 1, 1, False),
+                  (300, 1000, 1, True), (65, 2056, 4, False), (70, 96, 2, True)]
+
+
+@pytest.mark.parametrize("T,H,splits,supplied", PRE_BWD_SHAPES)
+def test_pre_from_dots_backward_matches_oracle(T, H, splits, supplied):
+    case = _pre_bwd_case(T, H, splits, supplied, cfg=400 + H % 83)
+    _check_pre_bwd(_run_pre_bwd(case), case, f"pre backward T={T} H={H} S={splits} sq={supplied}")
+
+
+@pytest.mark.parametrize("iters", [1, 3, 100])
+def test_pre_from_dots_backward_iterations_and_k(iters):
+    case = _pre_bwd_case(33, 512, 1, True, cfg=420 + iters)
+    got = _run_pre_bwd(case, k=700.0, num_iters=iters)
+    inp, dm, sq, dy, d_post, d_comb = case
+    ref = oracle.pre_from_dots_backward(dy, d_post, d_comb, dm[0].astype(np.float64), inp.res, inp.hc_scale,
+                                        inp.hc_base, sqrsum=sq[0].astype(np.float64), k=700.0, num_iters=iters)
+    tol = _pre_bwd_tolerances(inp, dm, sq, dy, d_post, d_comb, 700.0, ref)
+    _assert_within(got["d_dot"], ref["d_dot"], tol["d_dot"], f"d_dot iters={iters}")
+    _assert_within(got["d_hc_base"], ref["d_hc_base"], tol["d_hc_base"], f"d_hc_base iters={iters}")
+
+
+def test_pre_from_dots_backward_full_size_h7168_sampled():
+    """T=8192, H=7168: the token sums against the oracle over every token; the per-token
+    outputs on sampled tokens."""
+    case = _pre_bwd_case(8192, 7168, 1, False, cfg=3)
+    got = _run_pre_bwd(case)
+    _check_pre_bwd(got, case, "pre backward 8192x7168", tokens=sample_tokens(8192, 48))
+
+
+def test_pre_from_dots_backward_in_place_deterministic_and_empty():
+    mhc = _mhc()
+    case = _pre_bwd_case(40, 7168, 1, False, cfg=430)
+    a = _run_pre_bwd(case)
+    b = _run_pre_bwd(case)
+    for key in a:
+        if a[key] is not None:
+            assert np.array_equal(a[key], b[key]), key
+    inp, dm, sq, dy, d_post, d_comb = case
+    r = to_dev_bf16(inp.res)
+    out = mhc.mhc_pre_from_dots_backward(to_dev_bf16(dy), to_dev_f32(d_post), to_dev_f32(d_comb), to_dev_f32(dm[0]),
+                                         r, to_dev_f32(inp.hc_scale), to_dev_f32(inp.hc_base), d_res=r)
+    torch.cuda.synchronize()
+    assert out["d_res"].data_ptr() == r.data_ptr()
+    assert np.array_equal(bits_of(r), a["d_res"])
+    z = torch.empty(0, HC, 64, dtype=torch.bfloat16, device="cuda")
+    e = mhc.mhc_pre_from_dots_backward(torch.empty(0, 64, dtype=torch.bfloat16, device="cuda"),
+                                       torch.empty(0, HC, device="cuda"), torch.empty(0, HC, HC, device="cuda"),
+                                       torch.empty(0, MIX, device="cuda"), z, to_dev_f32(inp.hc_scale),
+                                       to_dev_f32(inp.hc_base))
+    torch.cuda.synchronize()
+    assert not f32_of(e["d_hc_base"]).any() and not f32_of(e["d_hc_scale"]).any()
