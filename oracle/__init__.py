@@ -61,6 +61,9 @@ def _load():
     lib.orc_post_backward.argtypes = [P, P, P, P, P, I64, I64, P, P, P, P]
     lib.orc_pre_from_dots_backward.argtypes = [P, P, P, P, P, P, P, P, I64, I64, D, D, D, D, D, ctypes.c_int,
                                                P, P, P, P, P]
+    lib.orc_expand.argtypes = [P, I64, I64, P]
+    lib.orc_head_mean.argtypes = [P, I64, I64, P]
+    lib.orc_head.argtypes = [P, P, P, P, I64, I64, D, D, P, P]
     lib.orc_pre_backward.argtypes = [P, P, P, P, P, P, P, I64, I64, D, D, D, D, ctypes.c_int, P, P, P, P, P]
     for f in ("orc_round_bf16", "orc_rms", "orc_project", "orc_mix_activation", "orc_sinkhorn",
               "orc_collapse", "orc_post", "orc_pre", "orc_pre_from_dots", "orc_sinkhorn_backward",
@@ -290,3 +293,39 @@ def pre_backward(dy, d_post, d_comb, res, hc_fn, hc_scale, hc_base, rms_eps=1e-6
                              rms_eps, pre_eps, sinkhorn_eps, post_mult, int(num_iters), _p(d_res), _p(d_fn),
                              _p(d_scale), _p(d_base), _p(scratch))
     return dict(d_res=d_res, d_hc_fn=d_fn, d_hc_scale=d_scale, d_hc_base=d_base)
+
+
+def expand(hidden):
+    """Model entry: [T,H] bf16 bits -> [T,4,H] bf16 bits, each stream a copy of the row."""
+    hidden = _c(hidden, np.uint16)
+    T, H = hidden.shape
+    out = np.empty((T, HC, H), np.uint16)
+    _load().orc_expand(_p(hidden), T, H, _p(out))
+    return out
+
+
+def head_mean(res):
+    """Model exit, unweighted: the mean of the 4 streams, [T,H] fp64 (unrounded)."""
+    res = _c(res, np.uint16)
+    T, hc, H = res.shape
+    assert hc == HC
+    y = np.empty((T, H))
+    _load().orc_head_mean(_p(res), T, H, _p(y))
+    return y
+
+
+def head(res, hc_fn, hc_scale, hc_base, norm_eps=1e-6, hc_eps=1e-6):
+    """Model exit, weighted: hc_fn [4,4H], hc_scale [1], hc_base [4] fp32.  Returns dict of fp64
+    arrays y [T,H], pre [T,4]."""
+    res = _c(res, np.uint16)
+    T, hc, H = res.shape
+    assert hc == HC
+    hc_fn = _c(hc_fn, np.float32)
+    assert hc_fn.shape == (HC, HC * H)
+    hc_scale = _c(hc_scale, np.float32).reshape(-1)
+    hc_base = _c(hc_base, np.float32).reshape(-1)
+    assert hc_scale.shape == (1,) and hc_base.shape == (HC,)
+    y = np.empty((T, H))
+    pre_ = np.empty((T, HC))
+    _load().orc_head(_p(res), _p(hc_fn), _p(hc_scale), _p(hc_base), T, H, norm_eps, hc_eps, _p(y), _p(pre_))
+    return dict(y=y, pre=pre_)

@@ -592,3 +592,57 @@ void orc_pre_backward(const uint16_t *dy, const double *d_post, const double *d_
         }
     }
 }
+
+/* Model entry (metrale glm5next_mhc.rs, glm_hc_expand: each hidden row is broadcast into
+ * its hc_mult streams): streams[t][i][h] = hidden[t][h] for every stream i.  bf16 in,
+ * bf16 out, an exact copy. */
+void orc_expand(const uint16_t *hidden, int64_t T, int64_t H, uint16_t *streams)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        for (int i = 0; i < ORC_HC; ++i) {
+            for (int64_t h = 0; h < H; ++h) {
+                streams[(t * ORC_HC + i) * H + h] = hidden[t * H + h];
+            }
+        }
+    }
+}
+
+/* Model exit, unweighted (metrale glm5next_mhc.rs, hc_head_mean: the mean of the
+ * hc_mult streams, no weights): y[t][h] = (1/4) sum_i res[t][i][h], fp64, unrounded. */
+void orc_head_mean(const uint16_t *res, int64_t T, int64_t H, double *y)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t h = 0; h < H; ++h) {
+            double acc = 0.0;
+            for (int i = 0; i < ORC_HC; ++i) {
+                acc += orc_bf16_to_f64(res[(t * ORC_HC + i) * H + h]);
+            }
+            y[t * H + h] = acc / ORC_HC;
+        }
+    }
+}
+
+/* Model exit, weighted (metrale hyper_connection_dispatch.rs, hc_head_site: the head
+ * takes its own hc_fn, hc_scale and hc_base with norm_eps and hc_eps and returns one
+ * row).  Read as the pre-map's pre group alone (steps A1, A2 for 4 rows, A3 for pre,
+ * A5): rstd = 1/sqrt(S/(4H) + norm_eps), m_i = rstd * sum_k hc_fn[i][k] res_flat[k],
+ * pre_i = sigmoid(m_i * s + b_i) + hc_eps, y = sum_i pre_i res_i.  hc_fn is [4, 4H],
+ * hc_scale [1], hc_base [4].  y [T,H] and pre [T,4] are fp64, unrounded. */
+void orc_head(const uint16_t *res, const float *hc_fn, const float *hc_scale, const float *hc_base, int64_t T,
+              int64_t H, double norm_eps, double hc_eps, double *y, double *pre)
+{
+    const int64_t K = ORC_HC * H;
+    for (int64_t t = 0; t < T; ++t) {
+        const uint16_t *r = res + t * K;
+        double rstd;
+        orc_rms(r, 1, H, norm_eps, NULL, &rstd);
+        for (int i = 0; i < ORC_HC; ++i) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                acc += (double)hc_fn[i * K + k] * orc_bf16_to_f64(r[k]);
+            }
+            pre[t * ORC_HC + i] = orc_sigmoid(acc * rstd * (double)hc_scale[0] + (double)hc_base[i]) + hc_eps;
+        }
+        orc_collapse(r, pre + t * ORC_HC, 1, H, y + t * H);
+    }
+}

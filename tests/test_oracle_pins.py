@@ -672,3 +672,42 @@ def test_pre_backward_zero_scale_reduces_to_the_logit_level_op():
     L = np.broadcast_to(hc_base[8:].astype(np.float64).reshape(HC, HC), (4, HC, HC))
     dL = oracle.sinkhorn_backward(d_comb, L, 20, 1e-6).sum(0).reshape(-1)
     assert np.allclose(b["d_hc_base"][8:], dL, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- model entry and exit
+
+def test_expand_is_a_broadcast_and_head_mean_undoes_it():
+    inp = layer_inputs(7, 33, cfg=140)
+    s = oracle.expand(inp.x)
+    assert np.array_equal(s, np.repeat(inp.x[:, None, :], HC, axis=1))
+    assert np.array_equal(oracle.round_bf16(oracle.head_mean(s)), inp.x)
+
+
+def test_head_mean_matches_numpy_mean():
+    inp = layer_inputs(9, 40, cfg=141)
+    assert np.allclose(oracle.head_mean(inp.res), _bf16_f64(inp.res).mean(axis=1), rtol=0, atol=1e-15)
+
+
+def test_head_agrees_with_the_pre_groups_of_the_pre_map():
+    """The weighted head is the pre-map's pre group alone: with the same 4 weight rows,
+    scale, bases and eps, y and pre agree with the (pinned) whole pre-map."""
+    inp = layer_inputs(6, 48, cfg=142, scale=(1.3, 0.7, 0.9))
+    full = oracle.pre(inp.res, inp.hc_fn, inp.hc_scale, inp.hc_base, rms_eps=1e-5, pre_eps=3e-3)
+    hd = oracle.head(inp.res, inp.hc_fn[:HC], inp.hc_scale[:1], inp.hc_base[:HC], norm_eps=1e-5, hc_eps=3e-3)
+    assert np.allclose(hd["pre"], full["pre"], rtol=0, atol=1e-15)
+    assert np.allclose(hd["y"], full["y"], rtol=0, atol=1e-13)
+
+
+def test_head_zero_scale_and_stream_permutation():
+    inp = layer_inputs(5, 24, cfg=143)
+    b = np.array([0.5, -1.0, 2.0, 0.0], np.float32)
+    hd = oracle.head(inp.res, inp.hc_fn[:HC], np.zeros(1, np.float32), b, hc_eps=1e-3)
+    assert np.allclose(hd["pre"], 1 / (1 + np.exp(-b.astype(np.float64))) + 1e-3, rtol=0, atol=1e-15)
+    perm = [2, 0, 3, 1]
+    H = 24
+    fn = inp.hc_fn[:HC].reshape(HC, HC, H)              # [row][stream][h]
+    fn_p = fn[perm][:, perm].reshape(HC, HC * H)        # rows and stream blocks permuted alike
+    a = oracle.head(inp.res, inp.hc_fn[:HC], np.ones(1, np.float32), b)
+    p = oracle.head(inp.res[:, perm], fn_p, np.ones(1, np.float32), b[perm])
+    assert np.allclose(p["y"], a["y"], rtol=0, atol=1e-12)
+    assert np.allclose(p["pre"], a["pre"][:, perm], rtol=0, atol=1e-14)
