@@ -50,7 +50,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="layer_h7168", choices=sorted(WORKLOADS))
     ap.add_argument("--only", default="all",
-                    choices=["all", "pre", "post", "sinkhorn", "pre_dots", "post_bwd", "sinkhorn_bwd", "pre_dots_bwd"],
+                    choices=["all", "pre", "post", "sinkhorn", "pre_dots", "post_bwd", "sinkhorn_bwd", "pre_dots_bwd",
+                             "pre_bf16", "expand", "head", "head_mean"],
                     help="run only one call in the timed loop (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
@@ -76,7 +77,9 @@ def main():
     import torch
 
     import mhc_hyper_connection_amd as mhc
-    from mhc_inputs import (algorithmic_bytes_post, algorithmic_bytes_post_backward, algorithmic_bytes_pre,
+    from mhc_inputs import (algorithmic_bytes_expand, algorithmic_bytes_head, algorithmic_bytes_head_mean,
+                            algorithmic_bytes_pre_bf16,
+                            algorithmic_bytes_post, algorithmic_bytes_post_backward, algorithmic_bytes_pre,
                             algorithmic_bytes_pre_dots, algorithmic_bytes_pre_dots_backward,
                             algorithmic_bytes_sinkhorn, algorithmic_bytes_sinkhorn_backward, external_dots,
                             layer_inputs, post_grad, pre_grads, sinkhorn_grad, sinkhorn_logits)
@@ -151,6 +154,28 @@ def main():
                                        p["rms_eps"], p["pre_eps"], p["sinkhorn_eps"], p["post_mult"],
                                        p["num_iters"], d_res=d_res_b, workspace=ws_b)
 
+    if args.only == "pre_bf16":
+        hc_fn16 = hc_fn.to(torch.bfloat16)
+    if args.only == "head":
+        head_fn = hc_fn[:4].contiguous()
+        head_scale = hc_scale[:1].contiguous()
+        head_base = hc_base[:4].contiguous()
+    if args.only == "expand":
+        streams_out = torch.empty_like(res)
+
+    def call_pre_bf16():
+        mhc.mhc_pre_fused_bf16(res, hc_fn16, hc_scale, hc_base, p["rms_eps"], p["pre_eps"], p["sinkhorn_eps"],
+                               p["post_mult"], p["num_iters"], y=y, post=post, comb=comb, workspace=ws)
+
+    def call_expand():
+        mhc.mhc_expand(x, streams=streams_out)
+
+    def call_head():
+        mhc.mhc_head(res, head_fn, head_scale, head_base, p["rms_eps"], p["pre_eps"], y=y, workspace=ws)
+
+    def call_head_mean():
+        mhc.mhc_head_mean(res, y=y)
+
     def call_sinkhorn():
         mhc.mhc_sinkhorn(sk_logits, out=sk_out, num_iters=p["num_iters"], eps=p["sinkhorn_eps"])
 
@@ -179,6 +204,14 @@ def main():
             call_post_bwd()
         if args.only == "pre_dots_bwd":
             call_pre_dots_bwd()
+        if args.only == "pre_bf16":
+            call_pre_bf16()
+        if args.only == "expand":
+            call_expand()
+        if args.only == "head":
+            call_head()
+        if args.only == "head_mean":
+            call_head_mean()
 
     stream = torch.cuda.current_stream(dev)
 
@@ -220,6 +253,9 @@ def main():
         breakdown["post_bwd_ms"] = ms_step
     if args.only == "pre_dots_bwd":
         breakdown["pre_dots_bwd_ms"] = ms_step
+    for mode in ("pre_bf16", "expand", "head", "head_mean"):
+        if args.only == mode:
+            breakdown[mode + "_ms"] = ms_step
 
     if args.only == "sinkhorn":
         step_bytes = algorithmic_bytes_sinkhorn(sk_logits.shape[0])
@@ -229,6 +265,14 @@ def main():
         step_bytes = algorithmic_bytes_post_backward(T, H)
     elif args.only == "pre_dots_bwd":
         step_bytes = algorithmic_bytes_pre_dots_backward(T, H)
+    elif args.only == "pre_bf16":
+        step_bytes = algorithmic_bytes_pre_bf16(T, H)
+    elif args.only == "expand":
+        step_bytes = algorithmic_bytes_expand(T, H)
+    elif args.only == "head":
+        step_bytes = algorithmic_bytes_head(T, H)
+    elif args.only == "head_mean":
+        step_bytes = algorithmic_bytes_head_mean(T, H)
     elif args.only == "pre_dots":
         step_bytes = algorithmic_bytes_pre_dots(T, H)
     else:
@@ -252,6 +296,17 @@ def main():
         calls["mhc_sinkhorn_backward"] = ("sinkhorn_bwd_kernel", breakdown["sinkhorn_bwd_ms"], step_bytes)
     if "post_bwd_ms" in breakdown:
         calls["mhc_post_backward"] = ("post_bwd_kernel", breakdown["post_bwd_ms"], step_bytes)
+    col = "pre_collapse_vec8_kernel" if H % 8 == 0 else "pre_collapse_scalar_kernel"
+    if "pre_bf16_ms" in breakdown:
+        calls["mhc_pre_fused_bf16"] = ("pre_prep_kernel+pre_proj_kernel+pre_mixsum_kernel+" + col,
+                                       breakdown["pre_bf16_ms"], step_bytes)
+    if "head_ms" in breakdown:
+        calls["mhc_head"] = ("pre_prep_kernel+pre_proj_kernel+pre_mixsum_kernel+" + col, breakdown["head_ms"],
+                             step_bytes)
+    if "expand_ms" in breakdown:
+        calls["mhc_expand"] = ("expand_kernel", breakdown["expand_ms"], step_bytes)
+    if "head_mean_ms" in breakdown:
+        calls["mhc_head_mean"] = ("head_mean_kernel", breakdown["head_mean_ms"], step_bytes)
     if "pre_dots_bwd_ms" in breakdown:
         calls["mhc_pre_from_dots_backward"] = ("pre_dots_bwd_kernel+pre_bwd_partial_kernel+pre_bwd_final_kernel",
                                                breakdown["pre_dots_bwd_ms"], step_bytes)

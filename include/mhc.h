@@ -121,6 +121,17 @@ mhc_status mhc_pre_fused(const uint16_t *res, const float *hc_fn, const float *h
                          size_t workspace_bytes, void *stream);
 
 /*
+ * mhc_pre_fused_bf16 -- mhc_pre_fused with bf16 weights (metrale glm5next_mhc.rs,
+ * glm5next_hc_mix_bf16: widening bf16 to fp32 is exact, so the result is the fp32
+ * pre-map's on the widened weights).  hc_fn is [24, 4H] bf16 bit patterns; every other
+ * argument, output, limit and the workspace are as in mhc_pre_fused.
+ */
+mhc_status mhc_pre_fused_bf16(const uint16_t *res, const uint16_t *hc_fn, const float *hc_scale,
+                              const float *hc_base, int64_t T, int64_t H, float rms_eps, float pre_eps,
+                              float sinkhorn_eps, float post_mult, int32_t num_iters, uint16_t *y, float *post,
+                              float *comb, float *pre, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * mhc_pre_from_dots -- the mHC pre-map from an external projection (FlashInfer mHC
  * article, sections 3.1-3.3, mhc_pre_big_fuse, where the 24 dots and the sum of
  * squares come from outside, optionally as split-K partial sums; section 4,
@@ -162,6 +173,40 @@ mhc_status mhc_pre_from_dots(const float *dot_mix, const float *sqrsum, int32_t 
  */
 mhc_status mhc_post(const uint16_t *x, const uint16_t *res, const float *post, const float *comb, int64_t T,
                     int64_t H, uint16_t *out, void *stream);
+
+/*
+ * mhc_expand -- model entry (metrale glm5next_mhc.rs, glm_hc_expand): each hidden row is
+ * copied into the 4 residual streams, streams[t][i][h] = hidden[t][h] (bf16, exact).
+ *   hidden [T,H] bf16 input, streams [T,4,H] bf16 output, device; no overlap.  T >= 0, H >= 1.
+ */
+mhc_status mhc_expand(const uint16_t *hidden, int64_t T, int64_t H, uint16_t *streams, void *stream);
+
+/*
+ * mhc_head_mean -- model exit, unweighted (metrale glm5next_mhc.rs, hc_head_mean):
+ *     y[t][h] = bf16( (res[t][0][h] + res[t][1][h] + res[t][2][h] + res[t][3][h]) / 4 )
+ *   (fp32 sum in that order, one rounding)
+ *   res [T,4,H] bf16 input, y [T,H] bf16 output, device; no overlap.  T >= 0, H >= 1.
+ */
+mhc_status mhc_head_mean(const uint16_t *res, int64_t T, int64_t H, uint16_t *y, void *stream);
+
+/*
+ * mhc_head -- model exit, weighted (metrale hyper_connection_dispatch.rs, hc_head_site:
+ * the head's own hc_fn, hc_scale and hc_base, norm_eps and hc_eps, one output row), taken
+ * as the pre-map's pre group alone:
+ *     rstd_t  = 1 / sqrt(S_t / (4H) + norm_eps),   S_t = sum_{i,h} res[t][i][h]^2
+ *     m_t[i]  = rstd_t * sum_k hc_fn[i][k] * res_flat[t][k]            (i < 4, k = i'*H + h)
+ *     pre[t][i] = sigmoid(m_t[i] * hc_scale[0] + hc_base[i]) + hc_eps
+ *     y[t][h] = bf16( sum_i pre[t][i] * res[t][i][h] )
+ *   res [T,4,H] bf16, hc_fn [4, 4H] fp32, hc_scale [1] fp32, hc_base [4] fp32   inputs, device
+ *   T >= 0, 1 <= H <= 2097152; norm_eps finite and > 0, hc_eps finite and >= 0
+ *   y [T,H] bf16 output; pre [T,4] fp32 optional output (may be NULL)
+ *   workspace   as for mhc_pre_fused: at least mhc_pre_fused_workspace_bytes(T, H) bytes,
+ *               256-byte aligned
+ * No output may overlap an input, the workspace or another output.
+ */
+mhc_status mhc_head(const uint16_t *res, const float *hc_fn, const float *hc_scale, const float *hc_base, int64_t T,
+                    int64_t H, float norm_eps, float hc_eps, uint16_t *y, float *pre, void *workspace,
+                    size_t workspace_bytes, void *stream);
 
 /*
  * Reverse mode (backward pass).  Each entry point returns the gradients of the

@@ -62,6 +62,14 @@ def lib() -> ctypes.CDLL:
     L.mhc_sinkhorn_backward.restype = ctypes.c_int
     L.mhc_post_backward.argtypes = [P, P, P, P, P, I64, I64, P, P, P, P, P]
     L.mhc_post_backward.restype = ctypes.c_int
+    L.mhc_pre_fused_bf16.argtypes = [P, P, P, P, I64, I64, F, F, F, F, I32, P, P, P, P, P, SZ, P]
+    L.mhc_pre_fused_bf16.restype = ctypes.c_int
+    L.mhc_expand.argtypes = [P, I64, I64, P, P]
+    L.mhc_expand.restype = ctypes.c_int
+    L.mhc_head_mean.argtypes = [P, I64, I64, P, P]
+    L.mhc_head_mean.restype = ctypes.c_int
+    L.mhc_head.argtypes = [P, P, P, P, I64, I64, F, F, P, P, P, SZ, P]
+    L.mhc_head.restype = ctypes.c_int
     L.mhc_pre_backward_workspace_bytes.argtypes = [I64]
     L.mhc_pre_backward_workspace_bytes.restype = SZ
     L.mhc_pre_from_dots_backward.argtypes = [P, P, P, P, P, I32, P, P, P, I64, I64, F, F, F, F, F, I32, P, P, P, P,
@@ -137,13 +145,28 @@ def mhc_pre_fused(res: torch.Tensor, hc_fn: torch.Tensor, hc_scale: torch.Tensor
                   return_pre: bool = False, workspace: torch.Tensor | None = None):
     """The pre-map.  res [..., 4, H] bf16 -> (y [..., H] bf16, post [..., 4] fp32, comb [..., 4, 4] fp32
     [, pre [..., 4] fp32]).  Outputs may be passed in (contiguous, right shape) to be written in place."""
+    return _pre_fused("mhc_pre_fused", torch.float32, res, hc_fn, hc_scale, hc_base, rms_eps, pre_eps,
+                      sinkhorn_eps, post_mult, num_iters, y, post, comb, pre, return_pre, workspace)
+
+
+def mhc_pre_fused_bf16(res: torch.Tensor, hc_fn: torch.Tensor, hc_scale: torch.Tensor, hc_base: torch.Tensor,
+                       rms_eps: float = 1e-6, pre_eps: float = 1e-6, sinkhorn_eps: float = 1e-6,
+                       post_mult: float = 1.0, num_iters: int = 20, *, y=None, post=None, comb=None, pre=None,
+                       return_pre: bool = False, workspace: torch.Tensor | None = None):
+    """:func:`mhc_pre_fused` with hc_fn [24, 4H] in bf16."""
+    return _pre_fused("mhc_pre_fused_bf16", torch.bfloat16, res, hc_fn, hc_scale, hc_base, rms_eps, pre_eps,
+                      sinkhorn_eps, post_mult, num_iters, y, post, comb, pre, return_pre, workspace)
+
+
+def _pre_fused(name, fn_dtype, res, hc_fn, hc_scale, hc_base, rms_eps, pre_eps, sinkhorn_eps, post_mult, num_iters,
+               y, post, comb, pre, return_pre, workspace):
     _need(res, "res", torch.bfloat16)
     if res.dim() < 2 or res.shape[-2] != HC:
         raise ValueError(f"res must be [..., 4, H], got {tuple(res.shape)}")
     H = res.shape[-1]
     outer = tuple(res.shape[:-2])
     T = res.numel() // (HC * H) if H > 0 else 0
-    _need(hc_fn, "hc_fn", torch.float32)
+    _need(hc_fn, "hc_fn", fn_dtype)
     if tuple(hc_fn.shape) != (MIX, HC * H):
         raise ValueError(f"hc_fn must be [24, 4H] = [24, {HC * H}], got {tuple(hc_fn.shape)}")
     _need(hc_scale, "hc_scale", torch.float32)
@@ -175,7 +198,7 @@ def mhc_pre_fused(res: torch.Tensor, hc_fn: torch.Tensor, hc_scale: torch.Tensor
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _need(workspace, "workspace", torch.uint8)
-    _check("mhc_pre_fused", lib().mhc_pre_fused(
+    _check(name, getattr(lib(), name)(
         _ptr(res), _ptr(hc_fn), _ptr(hc_scale), _ptr(hc_base), T, H, float(rms_eps), float(pre_eps),
         float(sinkhorn_eps), float(post_mult), int(num_iters), _ptr(y), _ptr(post), _ptr(comb), _ptr(pre),
         _ptr(workspace), workspace.numel(), _stream(dev)))
@@ -345,6 +368,84 @@ def mhc_post_backward(d_out: torch.Tensor, x: torch.Tensor, res: torch.Tensor, p
     return d_x, d_res, d_post, d_comb
 
 
+def mhc_expand(hidden: torch.Tensor, streams: torch.Tensor | None = None) -> torch.Tensor:
+    """Model entry: hidden [..., H] bf16 -> streams [..., 4, H] bf16, each stream a copy of the row."""
+    _need(hidden, "hidden", torch.bfloat16)
+    if hidden.dim() < 1:
+        raise ValueError("hidden must be [..., H]")
+    H = hidden.shape[-1]
+    outer = tuple(hidden.shape[:-1])
+    T = hidden.numel() // H if H > 0 else 0
+    if streams is None:
+        streams = torch.empty(outer + (HC, H), dtype=torch.bfloat16, device=hidden.device)
+    _need(streams, "streams", torch.bfloat16)
+    if tuple(streams.shape) != outer + (HC, H):
+        raise ValueError(f"streams must be {outer + (HC, H)}, got {tuple(streams.shape)}")
+    _same_device(hidden, streams)
+    _check("mhc_expand", lib().mhc_expand(_ptr(hidden), T, H, _ptr(streams), _stream(hidden.device)))
+    return streams
+
+
+def mhc_head_mean(res: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
+    """Model exit, unweighted: res [..., 4, H] bf16 -> the mean of the 4 streams [..., H] bf16."""
+    _need(res, "res", torch.bfloat16)
+    if res.dim() < 2 or res.shape[-2] != HC:
+        raise ValueError(f"res must be [..., 4, H], got {tuple(res.shape)}")
+    H = res.shape[-1]
+    outer = tuple(res.shape[:-2])
+    T = res.numel() // (HC * H) if H > 0 else 0
+    if y is None:
+        y = torch.empty(outer + (H,), dtype=torch.bfloat16, device=res.device)
+    _need(y, "y", torch.bfloat16)
+    if tuple(y.shape) != outer + (H,):
+        raise ValueError(f"y must be {outer + (H,)}, got {tuple(y.shape)}")
+    _same_device(res, y)
+    _check("mhc_head_mean", lib().mhc_head_mean(_ptr(res), T, H, _ptr(y), _stream(res.device)))
+    return y
+
+
+def mhc_head(res: torch.Tensor, hc_fn: torch.Tensor, hc_scale: torch.Tensor, hc_base: torch.Tensor,
+             norm_eps: float = 1e-6, hc_eps: float = 1e-6, *, y: torch.Tensor | None = None,
+             pre: torch.Tensor | None = None, return_pre: bool = False,
+             workspace: torch.Tensor | None = None):
+    """Model exit, weighted: res [..., 4, H] bf16, hc_fn [4, 4H], hc_scale [1], hc_base [4] fp32 ->
+    y [..., H] bf16 (and pre [..., 4] fp32 with ``return_pre``)."""
+    _need(res, "res", torch.bfloat16)
+    if res.dim() < 2 or res.shape[-2] != HC:
+        raise ValueError(f"res must be [..., 4, H], got {tuple(res.shape)}")
+    H = res.shape[-1]
+    outer = tuple(res.shape[:-2])
+    T = res.numel() // (HC * H) if H > 0 else 0
+    _need(hc_fn, "hc_fn", torch.float32)
+    if tuple(hc_fn.shape) != (HC, HC * H):
+        raise ValueError(f"hc_fn must be [4, 4H] = [4, {HC * H}], got {tuple(hc_fn.shape)}")
+    _need(hc_scale, "hc_scale", torch.float32)
+    _need(hc_base, "hc_base", torch.float32)
+    if hc_scale.numel() != 1 or hc_base.numel() != HC:
+        raise ValueError("hc_scale must hold 1 value and hc_base 4")
+    dev = res.device
+    if y is None:
+        y = torch.empty(outer + (H,), dtype=torch.bfloat16, device=dev)
+    _need(y, "y", torch.bfloat16)
+    if y.numel() != T * H:
+        raise ValueError("y must hold [T, H] values")
+    if pre is None and return_pre:
+        pre = torch.empty(outer + (HC,), dtype=torch.float32, device=dev)
+    if pre is not None:
+        _need(pre, "pre", torch.float32)
+        if pre.numel() != T * HC:
+            raise ValueError("pre must hold [T, 4] values")
+    need = mhc_pre_fused_workspace_bytes(T, H)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8)
+    _same_device(res, hc_fn, hc_scale, hc_base, y, pre, workspace)
+    _check("mhc_head", lib().mhc_head(_ptr(res), _ptr(hc_fn), _ptr(hc_scale), _ptr(hc_base), T, H, float(norm_eps),
+                                      float(hc_eps), _ptr(y), _ptr(pre), _ptr(workspace), workspace.numel(),
+                                      _stream(dev)))
+    return (y, pre) if return_pre else y
+
+
 def mhc_pre_backward_workspace_bytes(T: int) -> int:
     return int(lib().mhc_pre_backward_workspace_bytes(int(T)))
 
@@ -414,7 +515,8 @@ def mhc_pre_from_dots_backward(dy: torch.Tensor, d_post: torch.Tensor, d_comb: t
     return dict(d_res=d_res, d_dot=d_dot, d_sqrsum=d_sq, d_hc_scale=d_scale, d_hc_base=d_base)
 
 
-__all__ = ["mhc_sinkhorn", "mhc_pre_fused", "mhc_pre_fused_workspace_bytes", "mhc_pre_from_dots", "mhc_post",
+__all__ = ["mhc_sinkhorn", "mhc_pre_fused", "mhc_pre_fused_bf16", "mhc_expand", "mhc_head_mean", "mhc_head",
+           "mhc_pre_fused_workspace_bytes", "mhc_pre_from_dots", "mhc_post",
            "mhc_sinkhorn_backward", "mhc_post_backward", "mhc_pre_from_dots_backward",
            "mhc_pre_backward_workspace_bytes", "lib", "abi_version", "status_string", "MHCError", "HC",
            "MIX", "SINKHORN_BWD_MAX_ITERS"]

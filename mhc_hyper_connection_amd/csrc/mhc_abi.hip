@@ -40,6 +40,56 @@ bool sizes_ok(int64_t T, int64_t H)
 
 mhc_status launch_status(hipError_t e) { return e == hipSuccess ? MHC_SUCCESS : MHC_ERROR_LAUNCH; }
 
+constexpr int kMixRows = 24;
+
+// Shared validation and launch of the pre-map forms: the full pre-map (24 weight
+// rows, fp32 or bf16) and the weighted head (4 rows, pre weights and y only).
+mhc_status pre_common(const uint16_t *res, const void *hc_fn, bool fn_bf16, int fn_rows, const float *hc_scale,
+                      int n_scale, const float *hc_base, int64_t T, int64_t H, float rms_eps, float pre_eps,
+                      float sinkhorn_eps, float post_mult, int32_t num_iters, bool head, uint16_t *y, float *post,
+                      float *comb, float *pre, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!sizes_ok(T, H) || H > kPreMaxH || num_iters < 1 || !finite(rms_eps) || !(rms_eps > 0.0f) || !finite(pre_eps) ||
+        pre_eps < 0.0f || !finite(sinkhorn_eps) || !(sinkhorn_eps > 0.0f) || !finite(post_mult)) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    if (T == 0) {
+        return MHC_SUCCESS;
+    }
+    if (!res || !hc_fn || !hc_scale || !hc_base || !y || (!head && (!post || !comb))) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    const PreGeom g = mhc::pre_geometry(T, H);
+    if (!workspace || workspace_bytes < g.total_bytes || ((uintptr_t)workspace & 255u) != 0) {
+        return MHC_ERROR_WORKSPACE;
+    }
+    const size_t res_b = (size_t)T * 4 * H * 2, y_b = (size_t)T * H * 2;
+    const size_t post_b = head ? 0 : (size_t)T * 4 * 4, comb_b = head ? 0 : (size_t)T * 16 * 4;
+    const size_t pre_b = pre ? (size_t)T * 4 * 4 : 0;
+    const size_t fn_b = (size_t)fn_rows * 4 * H * (fn_bf16 ? 2 : 4);
+    // Outputs must not overlap inputs, each other, or the workspace.
+    const void *outs[5] = {y, post, comb, pre, workspace};
+    const size_t outn[5] = {y_b, post_b, comb_b, pre_b, g.total_bytes};
+    const void *ins[4] = {res, hc_fn, hc_scale, hc_base};
+    const size_t inn[4] = {res_b, fn_b, (size_t)n_scale * 4, (size_t)fn_rows * 4};
+    for (int a = 0; a < 5; ++a) {
+        for (int b = 0; b < 4; ++b) {
+            if (overlaps(outs[a], outn[a], ins[b], inn[b])) {
+                return MHC_ERROR_INVALID_VALUE;
+            }
+        }
+        for (int b = a + 1; b < 5; ++b) {
+            if (overlaps(outs[a], outn[a], outs[b], outn[b])) {
+                return MHC_ERROR_INVALID_VALUE;
+            }
+        }
+    }
+    const bool vec8 = (H % 8 == 0) && aligned16(res) && aligned16(y);
+    return launch_status(mhc::launch_pre(res, hc_fn, fn_bf16, fn_rows, hc_scale, hc_base, g, rms_eps, pre_eps,
+                                         sinkhorn_eps, post_mult, num_iters, head, y, post, comb, pre, workspace,
+                                         (hipStream_t)stream, vec8));
+}
+
 } // namespace
 
 extern "C" {
@@ -93,44 +143,55 @@ mhc_status mhc_pre_fused(const uint16_t *res, const float *hc_fn, const float *h
                          int32_t num_iters, uint16_t *y, float *post, float *comb, float *pre, void *workspace,
                          size_t workspace_bytes, void *stream)
 {
-    if (!sizes_ok(T, H) || H > kPreMaxH || num_iters < 1 || !finite(rms_eps) || !(rms_eps > 0.0f) || !finite(pre_eps) ||
-        pre_eps < 0.0f || !finite(sinkhorn_eps) || !(sinkhorn_eps > 0.0f) || !finite(post_mult)) {
+    return pre_common(res, hc_fn, false, kMixRows, hc_scale, 3, hc_base, T, H, rms_eps, pre_eps, sinkhorn_eps,
+                      post_mult, num_iters, false, y, post, comb, pre, workspace, workspace_bytes, stream);
+}
+
+mhc_status mhc_pre_fused_bf16(const uint16_t *res, const uint16_t *hc_fn, const float *hc_scale,
+                              const float *hc_base, int64_t T, int64_t H, float rms_eps, float pre_eps,
+                              float sinkhorn_eps, float post_mult, int32_t num_iters, uint16_t *y, float *post,
+                              float *comb, float *pre, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return pre_common(res, hc_fn, true, kMixRows, hc_scale, 3, hc_base, T, H, rms_eps, pre_eps, sinkhorn_eps,
+                      post_mult, num_iters, false, y, post, comb, pre, workspace, workspace_bytes, stream);
+}
+
+mhc_status mhc_head(const uint16_t *res, const float *hc_fn, const float *hc_scale, const float *hc_base, int64_t T,
+                    int64_t H, float norm_eps, float hc_eps, uint16_t *y, float *pre, void *workspace,
+                    size_t workspace_bytes, void *stream)
+{
+    return pre_common(res, hc_fn, false, 4, hc_scale, 1, hc_base, T, H, norm_eps, hc_eps, 1.0f, 1.0f, 1, true, y,
+                      nullptr, nullptr, pre, workspace, workspace_bytes, stream);
+}
+
+mhc_status mhc_head_mean(const uint16_t *res, int64_t T, int64_t H, uint16_t *y, void *stream)
+{
+    if (!sizes_ok(T, H)) {
         return MHC_ERROR_INVALID_VALUE;
     }
     if (T == 0) {
         return MHC_SUCCESS;
     }
-    if (!res || !hc_fn || !hc_scale || !hc_base || !y || !post || !comb) {
+    if (!res || !y || overlaps(y, (size_t)T * H * 2, res, (size_t)T * 4 * H * 2)) {
         return MHC_ERROR_INVALID_VALUE;
     }
-    const PreGeom g = mhc::pre_geometry(T, H);
-    if (!workspace || workspace_bytes < g.total_bytes || ((uintptr_t)workspace & 255u) != 0) {
-        return MHC_ERROR_WORKSPACE;
-    }
-    const size_t res_b = (size_t)T * 4 * H * 2, y_b = (size_t)T * H * 2;
-    const size_t post_b = (size_t)T * 4 * 4, comb_b = (size_t)T * 16 * 4, pre_b = pre ? (size_t)T * 4 * 4 : 0;
-    const size_t fn_b = (size_t)24 * 4 * H * 4;
-    // Outputs must not overlap inputs, each other, or the workspace.
-    const void *outs[5] = {y, post, comb, pre, workspace};
-    const size_t outn[5] = {y_b, post_b, comb_b, pre_b, g.total_bytes};
-    const void *ins[4] = {res, hc_fn, hc_scale, hc_base};
-    const size_t inn[4] = {res_b, fn_b, 3 * 4, 24 * 4};
-    for (int a = 0; a < 5; ++a) {
-        for (int b = 0; b < 4; ++b) {
-            if (overlaps(outs[a], outn[a], ins[b], inn[b])) {
-                return MHC_ERROR_INVALID_VALUE;
-            }
-        }
-        for (int b = a + 1; b < 5; ++b) {
-            if (overlaps(outs[a], outn[a], outs[b], outn[b])) {
-                return MHC_ERROR_INVALID_VALUE;
-            }
-        }
-    }
     const bool vec8 = (H % 8 == 0) && aligned16(res) && aligned16(y);
-    return launch_status(mhc::launch_pre(res, hc_fn, hc_scale, hc_base, g, rms_eps, pre_eps, sinkhorn_eps,
-                                         post_mult, num_iters, y, post, comb, pre, workspace, (hipStream_t)stream,
-                                         vec8));
+    return launch_status(mhc::launch_head_mean(res, T, H, y, (hipStream_t)stream, vec8));
+}
+
+mhc_status mhc_expand(const uint16_t *hidden, int64_t T, int64_t H, uint16_t *streams, void *stream)
+{
+    if (!sizes_ok(T, H)) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    if (T == 0) {
+        return MHC_SUCCESS;
+    }
+    if (!hidden || !streams || overlaps(streams, (size_t)T * 4 * H * 2, hidden, (size_t)T * H * 2)) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    const bool vec8 = (H % 8 == 0) && aligned16(hidden) && aligned16(streams);
+    return launch_status(mhc::launch_expand(hidden, T, H, streams, (hipStream_t)stream, vec8));
 }
 
 mhc_status mhc_pre_from_dots(const float *dot_mix, const float *sqrsum, int32_t num_splits, const uint16_t *res,

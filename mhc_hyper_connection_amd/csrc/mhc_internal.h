@@ -31,10 +31,18 @@ struct PreGeom {
 };
 PreGeom pre_geometry(int64_t T, int64_t H);
 
-hipError_t launch_pre(const uint16_t *res, const float *hc_fn, const float *hc_scale, const float *hc_base,
-                      const PreGeom &g, float rms_eps, float pre_eps, float sinkhorn_eps, float post_mult,
-                      int iters, uint16_t *y, float *post, float *comb, float *pre, void *workspace,
-                      hipStream_t stream, bool vec8);
+// The pre-map (and, with `head`, the weighted head: `fn_rows` = 4 weight rows, pre
+// weights and y only).  `hc_fn` is fp32, or bf16 bit patterns when `fn_bf16`.
+hipError_t launch_pre(const uint16_t *res, const void *hc_fn, bool fn_bf16, int fn_rows, const float *hc_scale,
+                      const float *hc_base, const PreGeom &g, float rms_eps, float pre_eps, float sinkhorn_eps,
+                      float post_mult, int iters, bool head, uint16_t *y, float *post, float *comb, float *pre,
+                      void *workspace, hipStream_t stream, bool vec8);
+
+// Model entry (each hidden row copied into the 4 streams) and the unweighted head (the
+// mean of the 4 streams).  `vec8`: H % 8 == 0 and both pointers 16-byte aligned.
+hipError_t launch_expand(const uint16_t *hidden, int64_t T, int64_t H, uint16_t *streams, hipStream_t stream,
+                         bool vec8);
+hipError_t launch_head_mean(const uint16_t *res, int64_t T, int64_t H, uint16_t *y, hipStream_t stream, bool vec8);
 
 // Pre-map from external dots (one workgroup per token).  `vec8`: H % 8 == 0 and res/y
 // 16-byte aligned.

@@ -83,7 +83,13 @@ __device__ __forceinline__ void split3x8(const float *v, u32x4 &ph, u32x4 &pm, u
 // One thread per (h block, stream, operand slot).  Slot < 64: column tile 0,
 // MFMA lane = slot (weight row = slot % 16).  Slot >= 64: column tile 1, rows
 // 16..23 only; entry g*8 + c stands for MFMA lane 16g + c (c < 8).
-__global__ __launch_bounds__(256) void pre_prep_kernel(const float *__restrict__ hc_fn, int H, int nhb,
+// Weight rows at or past `rows` are zero (the weighted head has 4 rows).  bf16
+// weights widen exactly to fp32, so their mid and lo terms come out zero.
+__device__ __forceinline__ float weight_at(const float *w, size_t i) { return w[i]; }
+__device__ __forceinline__ float weight_at(const uint16_t *w, size_t i) { return bf16_to_f32(w[i]); }
+
+template <typename W>
+__global__ __launch_bounds__(256) void pre_prep_kernel(const W *__restrict__ hc_fn, int H, int nhb, int rows,
                                                        u32x4 *__restrict__ frag)
 {
     const int gid = blockIdx.x * 256 + threadIdx.x;
@@ -108,10 +114,10 @@ __global__ __launch_bounds__(256) void pre_prep_kernel(const float *__restrict__
     const int r = n * 16 + c;
     const int h = hb * kPHB + g * 8;
     float v[8];
-    const float *src = hc_fn + (size_t)r * kHC * H + (size_t)i * H + h;
+    const size_t base = (size_t)r * kHC * H + (size_t)i * H + h;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        v[j] = (h + j < H) ? src[j] : 0.0f;
+        v[j] = (r < rows && h + j < H) ? weight_at(hc_fn, base + j) : 0.0f;
     }
     u32x4 ph, pm, pl;
     split3x8(v, ph, pm, pl);
@@ -338,6 +344,7 @@ struct MixArgs {
     const float *hc_base;
     float k_denom, rms_eps, pre_eps, sk_eps, post_mult;
     int iters;
+    int head; // the weighted head: pre weights and y only
     float *post, *comb, *pre_out;
 };
 
@@ -355,6 +362,15 @@ __device__ __forceinline__ void token_pre(const MixArgs &m, int t, float *p, flo
 // post, comb (Sinkhorn) and the optional pre output of token t (one lane writes).
 __device__ __forceinline__ void token_mix_outputs(const MixArgs &m, int t, const float *p, float rstd, bool writer)
 {
+    if (m.head) {
+        if (writer && m.pre_out) {
+#pragma unroll
+            for (int i = 0; i < kHC; ++i) {
+                m.pre_out[(size_t)t * kHC + i] = p[i];
+            }
+        }
+        return;
+    }
     const float *d = m.sums + (size_t)t * kSumStride;
     float post[kHC];
 #pragma unroll
@@ -485,17 +501,24 @@ PreGeom pre_geometry(int64_t T, int64_t H)
     return g;
 }
 
-hipError_t launch_pre(const uint16_t *res, const float *hc_fn, const float *hc_scale, const float *hc_base,
-                      const PreGeom &g, float rms_eps, float pre_eps, float sinkhorn_eps, float post_mult,
-                      int iters, uint16_t *y, float *post, float *comb, float *pre, void *workspace,
-                      hipStream_t stream, bool vec8)
+hipError_t launch_pre(const uint16_t *res, const void *hc_fn, bool fn_bf16, int fn_rows, const float *hc_scale,
+                      const float *hc_base, const PreGeom &g, float rms_eps, float pre_eps, float sinkhorn_eps,
+                      float post_mult, int iters, bool head, uint16_t *y, float *post, float *comb, float *pre,
+                      void *workspace, hipStream_t stream, bool vec8)
 {
     char *ws = reinterpret_cast<char *>(workspace);
     u32x4 *frag = reinterpret_cast<u32x4 *>(ws + g.off_frag);
     const int H = (int)g.H;
 
     const int prep_threads = g.nhb * kHC * (kFragPerHbStream / 3);
-    pre_prep_kernel<<<dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, stream>>>(hc_fn, H, g.nhb, frag);
+    const dim3 prep_grid((unsigned)((prep_threads + 255) / 256));
+    if (fn_bf16) {
+        pre_prep_kernel<uint16_t><<<prep_grid, dim3(256), 0, stream>>>(reinterpret_cast<const uint16_t *>(hc_fn), H,
+                                                                       g.nhb, fn_rows, frag);
+    } else {
+        pre_prep_kernel<float><<<prep_grid, dim3(256), 0, stream>>>(reinterpret_cast<const float *>(hc_fn), H, g.nhb,
+                                                                    fn_rows, frag);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
         return e;
@@ -537,8 +560,9 @@ hipError_t launch_pre(const uint16_t *res, const float *hc_fn, const float *hc_s
         mx.sk_eps = sinkhorn_eps;
         mx.post_mult = post_mult;
         mx.iters = iters;
-        mx.post = post + (size_t)c0 * kHC;
-        mx.comb = comb + (size_t)c0 * kHC * kHC;
+        mx.head = head ? 1 : 0;
+        mx.post = head ? nullptr : post + (size_t)c0 * kHC;
+        mx.comb = head ? nullptr : comb + (size_t)c0 * kHC * kHC;
         mx.pre_out = pre ? pre + (size_t)c0 * kHC : nullptr;
         const int tile = vec8 ? kColVecTile : kWave;
         const int64_t htiles = (g.H + tile - 1) / tile;

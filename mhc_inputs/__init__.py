@@ -204,6 +204,26 @@ def algorithmic_bytes_pre(T: int, H: int) -> int:
     return T * (8 * H + 2 * H + 16 + 64) + 384 * H + 108
 
 
+def algorithmic_bytes_pre_bf16(T: int, H: int) -> int:
+    """The pre-map with bf16 weights: as algorithmic_bytes_pre, with 192 H bytes of weights."""
+    return T * (8 * H + 2 * H + 16 + 64) + 192 * H + 108
+
+
+def algorithmic_bytes_expand(T: int, H: int) -> int:
+    """Model entry: the hidden row read, 4 streams written."""
+    return T * (2 * H + 8 * H)
+
+
+def algorithmic_bytes_head_mean(T: int, H: int) -> int:
+    """Unweighted head: 4 streams read, one row written."""
+    return T * (8 * H + 2 * H)
+
+
+def algorithmic_bytes_head(T: int, H: int) -> int:
+    """Weighted head: 4 streams read, one row written, 4 x 4H fp32 weights and 5 scalars read once."""
+    return T * (8 * H + 2 * H) + 64 * H + 20
+
+
 def algorithmic_bytes_post(T: int, H: int) -> int:
     """Bytes the post-map must move: x and res read, 80 B of mixes, out written."""
     return T * (2 * H + 8 * H + 80 + 8 * H)

@@ -27,7 +27,8 @@ def test_library_exports_every_declared_symbol():
     names = _declared()
     assert {"mhc_sinkhorn", "mhc_pre_fused", "mhc_pre_fused_workspace_bytes", "mhc_pre_from_dots", "mhc_post",
             "mhc_sinkhorn_backward", "mhc_post_backward", "mhc_pre_from_dots_backward",
-            "mhc_pre_backward_workspace_bytes", "mhc_abi_version", "mhc_status_string"} <= set(names)
+            "mhc_pre_backward_workspace_bytes", "mhc_pre_fused_bf16", "mhc_expand", "mhc_head_mean", "mhc_head",
+            "mhc_abi_version", "mhc_status_string"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -218,6 +219,57 @@ def test_pre_from_dots_backward_workspace():
     assert _dbwd(lib, wsb=need - 1) == mhc.MHC_ERROR_WORKSPACE
     assert _dbwd(lib, ws=None) == mhc.MHC_ERROR_WORKSPACE
     assert _dbwd(lib, ws=0x900000 + 16) == mhc.MHC_ERROR_WORKSPACE
+
+
+def test_expand_and_head_mean_validation():
+    lib = mhc.lib()
+    E = mhc.MHC_ERROR_INVALID_VALUE
+    a, b = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000)
+    for fn in (lib.mhc_expand, lib.mhc_head_mean):
+        assert fn(a, -1, 64, b, NULL) == E
+        assert fn(a, 8, 0, b, NULL) == E
+        assert fn(None, 8, 64, b, NULL) == E
+        assert fn(a, 8, 64, None, NULL) == E
+        assert fn(None, 0, 64, None, NULL) == mhc.MHC_SUCCESS
+    assert lib.mhc_expand(a, 8, 64, ctypes.c_void_p(0x100000 + 512), NULL) == E     # streams overlap hidden
+    assert lib.mhc_head_mean(a, 8, 64, ctypes.c_void_p(0x100000 + 512), NULL) == E  # y overlaps res
+
+
+def _head(lib, **kw):
+    a = dict(res=0x100000, fn=0x4000000, sc=0x8000000, base=0x8001000, T=16, H=256, ne=1e-6, he=1e-6,
+             y=0x9000000, pre=None, ws=0xC000000, wsb=1 << 30)
+    a.update(kw)
+    v = lambda n: ctypes.c_void_p(a[n]) if a[n] is not None else None
+    return lib.mhc_head(v("res"), v("fn"), v("sc"), v("base"), a["T"], a["H"], a["ne"], a["he"], v("y"), v("pre"),
+                        v("ws"), a["wsb"], NULL)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(T=-1), dict(H=0), dict(H=(1 << 21) + 8), dict(ne=0.0), dict(he=-1.0), dict(ne=float("nan")),
+    dict(res=None), dict(fn=None), dict(sc=None), dict(base=None), dict(y=None),
+    dict(y=0x100000 + 64),                  # y overlaps res
+    dict(pre=0x8001000 + 4),                # pre overlaps hc_base (4 floats)
+    dict(y=0x4000000 + 1024),               # y overlaps hc_fn ([4, 4H] fp32 = 16 KB)
+])
+def test_head_validation_invalid(kw):
+    assert _head(mhc.lib(), **kw) == mhc.MHC_ERROR_INVALID_VALUE
+
+
+def test_head_workspace_and_bf16_pre_validation():
+    lib = mhc.lib()
+    need = mhc.mhc_pre_fused_workspace_bytes(16, 256)
+    assert _head(lib, wsb=need - 1) == mhc.MHC_ERROR_WORKSPACE
+    assert _head(lib, ws=None) == mhc.MHC_ERROR_WORKSPACE
+    assert _head(lib, T=0, res=None, y=None, ws=None) == mhc.MHC_SUCCESS
+    # mhc_pre_fused_bf16 shares mhc_pre_fused's checks; bf16 weights are [24, 4H] x 2 bytes
+    f = lambda **k: lib.mhc_pre_fused_bf16(ctypes.c_void_p(0x10000), ctypes.c_void_p(k.get("fn", 0x4000000)),
+                                           ctypes.c_void_p(0x8000000), ctypes.c_void_p(0x8001000), 16, 256, 1e-6,
+                                           1e-6, 1e-6, 1.0, k.get("it", 20), ctypes.c_void_p(k.get("y", 0x9000000)),
+                                           ctypes.c_void_p(0xA000000), ctypes.c_void_p(0xB000000), None,
+                                           ctypes.c_void_p(0xC000000), k.get("wsb", 1 << 30), NULL)
+    assert f(it=0) == mhc.MHC_ERROR_INVALID_VALUE
+    assert f(y=0x4000000 + 24 * 1024 * 2 - 64) == mhc.MHC_ERROR_INVALID_VALUE   # y overlaps the bf16 weights
+    assert f(wsb=need - 1) == mhc.MHC_ERROR_WORKSPACE
 
 
 def test_binding_rejects_cpu_tensors_before_the_library():
