@@ -70,6 +70,16 @@ def normal_f32(seed: int, cfg: int, tensor: str, shape, std: float) -> np.ndarra
     return (g.standard_normal(size=shape, dtype=np.float32) * np.float32(std)).astype(np.float32)
 
 
+def device_normal_bf16(seed: int, cfg: int, tensor: str, shape, device="cuda", std: float = 1.0):
+    """A large seeded bf16 tensor drawn directly on the device (torch's generator, fp32
+    normals rounded to bf16 nearest-even), for shapes too big to draw on the host.  The
+    caller copies the rows it checks back to the host."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed((seed * 1_000_003 + cfg) * 1_000_003 + _TID[tensor])
+    return (torch.randn(shape, generator=g, device=device, dtype=torch.float32) * std).to(torch.bfloat16)
+
+
 def normal_bf16(seed: int, cfg: int, tensor: str, shape, std: float = 1.0) -> np.ndarray:
     return f32_to_bf16_bits(normal_f32(seed, cfg, tensor, shape, std))
 

@@ -1,0 +1,97 @@
+"""GPU parity at the size limits: the pre-map's token chunking (a batch whose partial
+sums pass 2^31 bytes is processed in chunks) and the largest accepted hidden size.
+Sampled tokens against the fp64 oracle, with the tolerances of the other parity tests."""
+import numpy as np
+import pytest
+
+import oracle
+from mhc_inputs import HC, MIX, device_normal_bf16, normal_f32, post_inputs
+from tests._helpers import assert_bf16_close, assert_f32_close, bits_of, f32_of, to_dev_bf16, to_dev_f32
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+PRE_MAX_H = 1 << 21
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mhc_hyper_connection_amd as mhc
+    mhc.lib()
+    yield
+
+
+def _mhc():
+    import mhc_hyper_connection_amd as mhc
+    return mhc
+
+
+def _bits_rows(t, rows):
+    return bits_of(t[torch.as_tensor(rows, device=t.device)])
+
+
+def _check_pre(res_rows, hc_fn, hc_scale, hc_base, y, post, comb, what):
+    ref = oracle.pre(res_rows, hc_fn, hc_scale, hc_base)
+    assert_f32_close(post, ref["post"], what + " post")
+    assert_f32_close(comb, ref["comb"], what + " comb")
+    assert_bf16_close(y, ref["y"], what + " y")
+
+
+def test_pre_token_chunking():
+    """H = 8: one 128-wide slice, 6400 bytes of partial sums per 64-token tile, so the
+    first chunk ends after floor(2^31 / 6400) tiles; T runs 3000 tokens into a second,
+    ragged chunk."""
+    mhc = _mhc()
+    H = 8
+    chunk = (2 ** 31 // (1 * 100 * 64)) * 64
+    T = chunk + 3000
+    res = device_normal_bf16(0, 600, "res", (T, HC, H))
+    hc_fn = normal_f32(0, 600, "hc_fn", (MIX, HC * H), 0.02)
+    hc_scale = np.ones(3, np.float32)
+    hc_base = normal_f32(0, 600, "hc_base", (MIX,), 0.1)
+    y, post, comb = mhc.mhc_pre_fused(res, to_dev_f32(hc_fn), to_dev_f32(hc_scale), to_dev_f32(hc_base))
+    torch.cuda.synchronize()
+    rows = sorted({0, 1, 63, 64, chunk - 65, chunk - 64, chunk - 1, chunk, chunk + 1, chunk + 63, chunk + 64,
+                   chunk + 2999, T // 2, 12345678})
+    _check_pre(_bits_rows(res, rows), hc_fn, hc_scale, hc_base, _bits_rows(y, rows),
+               f32_of(post[torch.as_tensor(rows, device="cuda")]), f32_of(comb[torch.as_tensor(rows, device="cuda")]),
+               f"pre chunked T={T}")
+
+
+@pytest.mark.parametrize("fn", ["pre_fused", "pre_from_dots", "post"])
+def test_largest_hidden_size(fn):
+    """H = 2^21, the pre-map's limit (its 64-token tiles are addressed with 32-bit byte
+    offsets), with a ragged T of 3."""
+    mhc = _mhc()
+    T, H = 3, PRE_MAX_H
+    res = device_normal_bf16(0, 610, "res", (T, HC, H))
+    rows = list(range(T))
+    if fn == "pre_fused":
+        hc_fn = normal_f32(0, 610, "hc_fn", (MIX, HC * H), 0.02)
+        hc_scale = np.ones(3, np.float32)
+        hc_base = normal_f32(0, 610, "hc_base", (MIX,), 0.1)
+        y, post, comb = mhc.mhc_pre_fused(res, to_dev_f32(hc_fn), to_dev_f32(hc_scale), to_dev_f32(hc_base))
+        torch.cuda.synchronize()
+        _check_pre(bits_of(res), hc_fn, hc_scale, hc_base, bits_of(y), f32_of(post), f32_of(comb), "pre H=2^21")
+    elif fn == "pre_from_dots":
+        dm = normal_f32(0, 610, "logits", (T, MIX), 5.0)
+        hc_scale = np.ones(3, np.float32)
+        hc_base = normal_f32(0, 610, "hc_base", (MIX,), 0.1)
+        y, post, comb = mhc.mhc_pre_from_dots(to_dev_f32(dm), res, to_dev_f32(hc_scale), to_dev_f32(hc_base))
+        torch.cuda.synchronize()
+        ref = oracle.pre_from_dots(dm, bits_of(res), hc_scale, hc_base)
+        assert_f32_close(f32_of(post), ref["post"], "pre_from_dots H=2^21 post")
+        assert_f32_close(f32_of(comb), ref["comb"], "pre_from_dots H=2^21 comb")
+        assert_bf16_close(bits_of(y), ref["y"], "pre_from_dots H=2^21 y")
+    else:
+        x = device_normal_bf16(0, 610, "x", (T, H))
+        g = np.random.default_rng(610)
+        post = g.uniform(0, 2, (T, HC)).astype(np.float32)
+        comb = oracle.sinkhorn(g.standard_normal((T, HC, HC)), 20, 1e-6).astype(np.float32)
+        out = mhc.mhc_post(x, res, to_dev_f32(post), to_dev_f32(comb))
+        torch.cuda.synchronize()
+        ref = oracle.post(bits_of(x), bits_of(res), post.astype(np.float64), comb.astype(np.float64))
+        assert_bf16_close(bits_of(out), ref, "post H=2^21")
