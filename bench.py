@@ -51,9 +51,11 @@ def parse():
     ap.add_argument("--workload", default="layer_h7168", choices=sorted(WORKLOADS))
     ap.add_argument("--only", default="all",
                     choices=["all", "pre", "post", "sinkhorn", "pre_dots", "post_bwd", "sinkhorn_bwd", "pre_dots_bwd",
-                             "pre_bf16", "expand", "head", "head_mean"],
+                             "pre_bf16", "expand", "head", "head_mean", "pre_bwd"],
                     help="run only one call in the timed loop (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the steps as replays of one captured HIP graph (no host launch cost)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="(no GPU) turn two rocprofv3 --pmc CSV runs into the stored per-kernel HBM traffic")
@@ -80,7 +82,8 @@ def main():
     from mhc_inputs import (algorithmic_bytes_expand, algorithmic_bytes_head, algorithmic_bytes_head_mean,
                             algorithmic_bytes_pre_bf16,
                             algorithmic_bytes_post, algorithmic_bytes_post_backward, algorithmic_bytes_pre,
-                            algorithmic_bytes_pre_dots, algorithmic_bytes_pre_dots_backward,
+                            algorithmic_bytes_pre_backward, algorithmic_bytes_pre_dots,
+                            algorithmic_bytes_pre_dots_backward,
                             algorithmic_bytes_sinkhorn, algorithmic_bytes_sinkhorn_backward, external_dots,
                             layer_inputs, post_grad, pre_grads, sinkhorn_grad, sinkhorn_logits)
 
@@ -154,6 +157,18 @@ def main():
                                        p["rms_eps"], p["pre_eps"], p["sinkhorn_eps"], p["post_mult"],
                                        p["num_iters"], d_res=d_res_b, workspace=ws_b)
 
+    if args.only == "pre_bwd":
+        f_dy, f_post, f_comb = pre_grads(T, H, cfg=cfg)
+        f_dy = bf16(f_dy)
+        f_post = torch.from_numpy(f_post).to(dev)
+        f_comb = torch.from_numpy(f_comb).to(dev)
+        f_dres = torch.empty_like(res)
+        f_ws = torch.empty(max(mhc.mhc_pre_fused_backward_workspace_bytes(T, H), 1), dtype=torch.uint8, device=dev)
+
+    def call_pre_bwd():
+        mhc.mhc_pre_fused_backward(f_dy, f_post, f_comb, res, hc_fn, hc_scale, hc_base, p["rms_eps"], p["pre_eps"],
+                                   p["sinkhorn_eps"], p["post_mult"], p["num_iters"], d_res=f_dres, workspace=f_ws)
+
     if args.only == "pre_bf16":
         hc_fn16 = hc_fn.to(torch.bfloat16)
     if args.only == "head":
@@ -212,6 +227,8 @@ def main():
             call_head()
         if args.only == "head_mean":
             call_head_mean()
+        if args.only == "pre_bwd":
+            call_pre_bwd()
 
     stream = torch.cuda.current_stream(dev)
 
@@ -231,9 +248,27 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    run_step = step
+    if args.graph:
+        # capture one step on a side stream (after a warm-up there), then replay it
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        run_step = graph.replay
+        for _ in range(args.warmup):
+            run_step()
+        torch.cuda.synchronize()
+
+    print(f"[bench] timing {args.steps} steps{' (graph replays)' if args.graph else ''}", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
-    ms_step = timed(step, args.steps)
+    ms_step = timed(run_step, args.steps)
     wall = time.perf_counter() - t0
 
     pre_b = algorithmic_bytes_pre(T, H)
@@ -253,7 +288,7 @@ def main():
         breakdown["post_bwd_ms"] = ms_step
     if args.only == "pre_dots_bwd":
         breakdown["pre_dots_bwd_ms"] = ms_step
-    for mode in ("pre_bf16", "expand", "head", "head_mean"):
+    for mode in ("pre_bf16", "expand", "head", "head_mean", "pre_bwd"):
         if args.only == mode:
             breakdown[mode + "_ms"] = ms_step
 
@@ -273,6 +308,8 @@ def main():
         step_bytes = algorithmic_bytes_head(T, H)
     elif args.only == "head_mean":
         step_bytes = algorithmic_bytes_head_mean(T, H)
+    elif args.only == "pre_bwd":
+        step_bytes = algorithmic_bytes_pre_backward(T, H)
     elif args.only == "pre_dots":
         step_bytes = algorithmic_bytes_pre_dots(T, H)
     else:
@@ -303,6 +340,10 @@ def main():
     if "head_ms" in breakdown:
         calls["mhc_head"] = ("pre_prep_kernel+pre_proj_kernel+pre_mixsum_kernel+" + col, breakdown["head_ms"],
                              step_bytes)
+    if "pre_bwd_ms" in breakdown:
+        calls["mhc_pre_fused_backward"] = ("pre_prep_kernel+pre_proj_kernel+pre_mixsum_kernel+pre_dots_bwd_kernel+"
+                                           "pre_bwd_partial_kernel+pre_bwd_final_kernel+proj_bwd_wfrag_kernel+"
+                                           "proj_bwd_kernel+dw_reduce_kernel", breakdown["pre_bwd_ms"], step_bytes)
     if "expand_ms" in breakdown:
         calls["mhc_expand"] = ("expand_kernel", breakdown["expand_ms"], step_bytes)
     if "head_mean_ms" in breakdown:
@@ -366,6 +407,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": (f"mhc {args.only} 2^20 4x4 matrices" if args.only.startswith("sinkhorn") else
                                 f"mhc {args.only if args.only != 'all' else 'pre+post'} T={T} H={H} HC=4"),
+                   "launch": "HIP graph replay" if args.graph else "eager",
                    "T": T, "H": H, "hc": 4, "num_iters": p["num_iters"], "inputs": "resident in HBM"},
         "effective_GBps": round(eff_gbps, 1),
         "hbm_frac": round(eff_gbps / HBM_PEAK_GBPS, 4),

@@ -308,6 +308,43 @@ mhc_status mhc_pre_from_dots_backward(const uint16_t *dy, const float *d_post, c
                                       float *d_sqrsum, float *d_hc_scale, float *d_hc_base, void *workspace,
                                       size_t workspace_bytes, void *stream);
 
+/*
+ * Size in bytes of the device workspace mhc_pre_fused_backward needs for (T, H): the
+ * forward's projection workspace, the weights split for the reverse products, per-token
+ * values (pre, dS, the logit gradients as bf16 halves, row-major and transposed), the
+ * token-sum rows and per-token-range partial sums of d_hc_fn.  Returns 0 for T <= 0,
+ * H <= 0, H % 8 != 0 or H beyond the pre-map limit.
+ */
+size_t mhc_pre_fused_backward_workspace_bytes(int64_t T, int64_t H);
+
+/*
+ * mhc_pre_fused_backward -- gradients of mhc_pre_fused (the whole pre-map, projection
+ * inside).  The forward's dots and sum of squares are recomputed from res and hc_fn;
+ * then the reverse of mhc_pre_from_dots_backward's chain with the sum of squares taken
+ * from the streams (k = 4H), and the projection's reverse:
+ *     d_res[t][i][h] = bf16( pre_i dy[t][h] + 2 dS_t res[t][i][h] + sum_r dd[t][r] hc_fn[r][i*H+h] )
+ *     d_hc_fn[r][k]  = sum_t dd[t][r] res_flat[t][k]            (dd = d_dot of the dots)
+ *     d_hc_scale, d_hc_base as in mhc_pre_from_dots_backward
+ *   (the weight products use bf16 hi + lo halves of both factors, three products,
+ *   fp32 accumulation; every sum over tokens runs in a fixed order)
+ *
+ *   dy [T,H] bf16, d_post [T,4] fp32, d_comb [T,4,4] fp32   gradients of y, post, comb
+ *   res, hc_fn, hc_scale, hc_base, rms_eps, pre_eps, sinkhorn_eps, post_mult   as in
+ *               mhc_pre_fused; 1 <= num_iters <= MHC_SINKHORN_BWD_MAX_ITERS
+ *   T >= 0; 8 <= H <= 2097152 with H % 8 == 0; dy, res and d_res 16-byte aligned
+ *   d_res [T,4,H] bf16   output; may equal `res` exactly
+ *   d_hc_fn [24,4H] fp32, d_hc_scale [3], d_hc_base [24]   outputs, overwritten.  For
+ *               T == 0 they are set to zero and nothing else runs.
+ *   workspace   at least mhc_pre_fused_backward_workspace_bytes(T, H) bytes, 256-byte
+ *               aligned (may be NULL when T == 0)
+ * No output may overlap an input, the workspace or another output, except as stated.
+ */
+mhc_status mhc_pre_fused_backward(const uint16_t *dy, const float *d_post, const float *d_comb, const uint16_t *res,
+                                  const float *hc_fn, const float *hc_scale, const float *hc_base, int64_t T,
+                                  int64_t H, float rms_eps, float pre_eps, float sinkhorn_eps, float post_mult,
+                                  int32_t num_iters, uint16_t *d_res, float *d_hc_fn, float *d_hc_scale,
+                                  float *d_hc_base, void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -70,6 +70,10 @@ def lib() -> ctypes.CDLL:
     L.mhc_head_mean.restype = ctypes.c_int
     L.mhc_head.argtypes = [P, P, P, P, I64, I64, F, F, P, P, P, SZ, P]
     L.mhc_head.restype = ctypes.c_int
+    L.mhc_pre_fused_backward_workspace_bytes.argtypes = [I64, I64]
+    L.mhc_pre_fused_backward_workspace_bytes.restype = SZ
+    L.mhc_pre_fused_backward.argtypes = [P, P, P, P, P, P, P, I64, I64, F, F, F, F, I32, P, P, P, P, P, SZ, P]
+    L.mhc_pre_fused_backward.restype = ctypes.c_int
     L.mhc_pre_backward_workspace_bytes.argtypes = [I64]
     L.mhc_pre_backward_workspace_bytes.restype = SZ
     L.mhc_pre_from_dots_backward.argtypes = [P, P, P, P, P, I32, P, P, P, I64, I64, F, F, F, F, F, I32, P, P, P, P,
@@ -515,8 +519,64 @@ def mhc_pre_from_dots_backward(dy: torch.Tensor, d_post: torch.Tensor, d_comb: t
     return dict(d_res=d_res, d_dot=d_dot, d_sqrsum=d_sq, d_hc_scale=d_scale, d_hc_base=d_base)
 
 
+def mhc_pre_fused_backward_workspace_bytes(T: int, H: int) -> int:
+    return int(lib().mhc_pre_fused_backward_workspace_bytes(int(T), int(H)))
+
+
+def mhc_pre_fused_backward(dy: torch.Tensor, d_post: torch.Tensor, d_comb: torch.Tensor, res: torch.Tensor,
+                           hc_fn: torch.Tensor, hc_scale: torch.Tensor, hc_base: torch.Tensor,
+                           rms_eps: float = 1e-6, pre_eps: float = 1e-6, sinkhorn_eps: float = 1e-6,
+                           post_mult: float = 1.0, num_iters: int = 20, *, d_res: torch.Tensor | None = None,
+                           workspace: torch.Tensor | None = None) -> dict:
+    """Gradients of :func:`mhc_pre_fused` for dy [..., H] bf16, d_post [..., 4] and d_comb [..., 4, 4]
+    fp32: a dict with d_res [..., 4, H] bf16, d_hc_fn [24, 4H], d_hc_scale [3], d_hc_base [24] fp32.
+    ``d_res`` may be ``res``.  H must be a multiple of 8."""
+    _need(res, "res", torch.bfloat16)
+    if res.dim() < 2 or res.shape[-2] != HC:
+        raise ValueError(f"res must be [..., 4, H], got {tuple(res.shape)}")
+    H = res.shape[-1]
+    outer = tuple(res.shape[:-2])
+    T = res.numel() // (HC * H) if H > 0 else 0
+    _need(dy, "dy", torch.bfloat16)
+    if tuple(dy.shape) != outer + (H,):
+        raise ValueError(f"dy must be {outer + (H,)}, got {tuple(dy.shape)}")
+    _need(d_post, "d_post", torch.float32)
+    if d_post.numel() != T * HC:
+        raise ValueError("d_post must hold [T, 4] values")
+    _need(d_comb, "d_comb", torch.float32)
+    if tuple(d_comb.shape) != outer + (HC, HC):
+        raise ValueError(f"d_comb must be {outer + (HC, HC)}, got {tuple(d_comb.shape)}")
+    _need(hc_fn, "hc_fn", torch.float32)
+    if tuple(hc_fn.shape) != (MIX, HC * H):
+        raise ValueError(f"hc_fn must be [24, 4H] = [24, {HC * H}], got {tuple(hc_fn.shape)}")
+    _need(hc_scale, "hc_scale", torch.float32)
+    _need(hc_base, "hc_base", torch.float32)
+    if hc_scale.numel() != 3 or hc_base.numel() != MIX:
+        raise ValueError("hc_scale must have 3 values and hc_base 24")
+    dev = res.device
+    if d_res is None:
+        d_res = torch.empty_like(res)
+    _need(d_res, "d_res", torch.bfloat16)
+    if d_res.shape != res.shape:
+        raise ValueError("d_res must have the shape of res")
+    d_fn = torch.empty(MIX, HC * H, dtype=torch.float32, device=dev)
+    d_scale = torch.empty(3, dtype=torch.float32, device=dev)
+    d_base = torch.empty(MIX, dtype=torch.float32, device=dev)
+    need = mhc_pre_fused_backward_workspace_bytes(T, H)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _same_device(dy, d_post, d_comb, res, hc_fn, hc_scale, hc_base, d_res, workspace)
+    _check("mhc_pre_fused_backward",
+           lib().mhc_pre_fused_backward(_ptr(dy), _ptr(d_post), _ptr(d_comb), _ptr(res), _ptr(hc_fn), _ptr(hc_scale),
+                                        _ptr(hc_base), T, H, float(rms_eps), float(pre_eps), float(sinkhorn_eps),
+                                        float(post_mult), int(num_iters), _ptr(d_res), _ptr(d_fn), _ptr(d_scale),
+                                        _ptr(d_base), _ptr(workspace), workspace.numel(), _stream(dev)))
+    return dict(d_res=d_res, d_hc_fn=d_fn, d_hc_scale=d_scale, d_hc_base=d_base)
+
+
 __all__ = ["mhc_sinkhorn", "mhc_pre_fused", "mhc_pre_fused_bf16", "mhc_expand", "mhc_head_mean", "mhc_head",
            "mhc_pre_fused_workspace_bytes", "mhc_pre_from_dots", "mhc_post",
            "mhc_sinkhorn_backward", "mhc_post_backward", "mhc_pre_from_dots_backward",
-           "mhc_pre_backward_workspace_bytes", "lib", "abi_version", "status_string", "MHCError", "HC",
+           "mhc_pre_backward_workspace_bytes", "mhc_pre_fused_backward", "mhc_pre_fused_backward_workspace_bytes",
+           "lib", "abi_version", "status_string", "MHCError", "HC",
            "MIX", "SINKHORN_BWD_MAX_ITERS"]

@@ -387,4 +387,67 @@ mhc_status mhc_pre_from_dots_backward(const uint16_t *dy, const float *d_post, c
                                                   (hipStream_t)stream, vec8));
 }
 
+size_t mhc_pre_fused_backward_workspace_bytes(int64_t T, int64_t H)
+{
+    if (T <= 0 || H <= 0 || H > kPreMaxH || H % 8 != 0 || !sizes_ok(T, H)) {
+        return 0;
+    }
+    return mhc::pre_fused_bwd_workspace_bytes(T, H);
+}
+
+mhc_status mhc_pre_fused_backward(const uint16_t *dy, const float *d_post, const float *d_comb, const uint16_t *res,
+                                  const float *hc_fn, const float *hc_scale, const float *hc_base, int64_t T,
+                                  int64_t H, float rms_eps, float pre_eps, float sinkhorn_eps, float post_mult,
+                                  int32_t num_iters, uint16_t *d_res, float *d_hc_fn, float *d_hc_scale,
+                                  float *d_hc_base, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!sizes_ok(T, H) || H > kPreMaxH || H % 8 != 0 || num_iters < 1 || num_iters > MHC_SINKHORN_BWD_MAX_ITERS ||
+        !finite(rms_eps) || !(rms_eps > 0.0f) || !finite(pre_eps) || pre_eps < 0.0f || !finite(sinkhorn_eps) ||
+        !(sinkhorn_eps > 0.0f) || !finite(post_mult)) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    const size_t fn_b = (size_t)24 * 4 * H * 4;
+    if (!d_hc_fn || !d_hc_scale || !d_hc_base || overlaps(d_hc_fn, fn_b, d_hc_scale, 3 * 4) ||
+        overlaps(d_hc_fn, fn_b, d_hc_base, 24 * 4) || overlaps(d_hc_scale, 3 * 4, d_hc_base, 24 * 4)) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    if (T == 0) {
+        return launch_status(mhc::launch_pre_fused_bwd(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                                       0, H, rms_eps, pre_eps, sinkhorn_eps, post_mult, num_iters,
+                                                       nullptr, d_hc_fn, d_hc_scale, d_hc_base, nullptr,
+                                                       (hipStream_t)stream));
+    }
+    if (!dy || !d_post || !d_comb || !res || !hc_fn || !hc_scale || !hc_base || !d_res) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    if (!aligned16(dy) || !aligned16(res) || !aligned16(d_res)) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    const size_t need = mhc::pre_fused_bwd_workspace_bytes(T, H);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0) {
+        return MHC_ERROR_WORKSPACE;
+    }
+    const size_t res_b = (size_t)T * 4 * H * 2, y_b = (size_t)T * H * 2;
+    const void *outs[5] = {d_res, d_hc_fn, d_hc_scale, d_hc_base, workspace};
+    const size_t outn[5] = {res_b, fn_b, 3 * 4, 24 * 4, need};
+    const void *ins[7] = {dy, d_post, d_comb, res, hc_fn, hc_scale, hc_base};
+    const size_t inn[7] = {y_b, (size_t)T * 16, (size_t)T * 64, res_b, fn_b, 3 * 4, 24 * 4};
+    for (int o = 0; o < 5; ++o) {
+        for (int i = 0; i < 7; ++i) {
+            const bool in_place = o == 0 && i == 3 && (const void *)d_res == (const void *)res;
+            if (!in_place && overlaps(outs[o], outn[o], ins[i], inn[i])) {
+                return MHC_ERROR_INVALID_VALUE;
+            }
+        }
+        for (int o2 = o + 1; o2 < 5; ++o2) {
+            if (overlaps(outs[o], outn[o], outs[o2], outn[o2])) {
+                return MHC_ERROR_INVALID_VALUE;
+            }
+        }
+    }
+    return launch_status(mhc::launch_pre_fused_bwd(dy, d_post, d_comb, res, hc_fn, hc_scale, hc_base, T, H, rms_eps,
+                                                   pre_eps, sinkhorn_eps, post_mult, num_iters, d_res, d_hc_fn,
+                                                   d_hc_scale, d_hc_base, workspace, (hipStream_t)stream));
+}
+
 } // extern "C"

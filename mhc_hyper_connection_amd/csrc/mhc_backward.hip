@@ -10,6 +10,11 @@ namespace mhc {
 
 namespace {
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_view_b(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+
 // ---------------------------------------------------------------- Sinkhorn backward
 //
 // 16 lanes per matrix (lane e holds entry (e / 4, e % 4)), 4 matrices per 64-thread
@@ -111,7 +116,19 @@ struct DotsBwdArgs {
     uint16_t *d_res;
     float *d_dot, *d_sqrsum;
     float *ws; // [T][kWsRow]
+    // Projection inside (the reverse of the whole pre-map): the dots and the sum of
+    // squares come from the projection's per-token fields, and instead of d_res the
+    // kernel writes pre and 2 dS ([T][8]) and d_dot as bf16 hi and lo halves, both
+    // row-major [T][32] and transposed [32][ldT] (rows 24..31 zero).
+    const float *sums; // [T][32], or null
+    float *tok;
+    uint16_t *dd_hi, *dd_lo, *ddT_hi, *ddT_lo;
+    int ldT;
 };
+
+// The projection's per-token fields: pre dots 0..3, the sum of squares at 4, then
+// post and comb dots.
+__device__ __forceinline__ int sums_field(int col) { return col < kHC ? col : col + 1; }
 
 template <int kCPT>
 __global__ __launch_bounds__(kDBBlock) void pre_dots_bwd_kernel(DotsBwdArgs a)
@@ -128,12 +145,18 @@ __global__ __launch_bounds__(kDBBlock) void pre_dots_bwd_kernel(DotsBwdArgs a)
     const int H = a.H;
     const uint16_t *row = a.res + (size_t)t * kHC * H;
     const uint16_t *grow = a.dy + (size_t)t * H;
-    const bool need_sq = a.sqrsum == nullptr;
+    const bool fused = a.sums != nullptr;
+    // S computed here from the streams (the RMS term of d_res applies), or supplied
+    const bool need_sq = a.sqrsum == nullptr && !fused;
 
     float dv = 0.0f;
     if (w == 0 && lane < kMix) {
-        for (int s = 0; s < a.S; ++s) {
-            dv += a.dot_mix[((size_t)s * a.T + t) * kMix + lane];
+        if (fused) {
+            dv = a.sums[(size_t)t * 32 + sums_field(lane)];
+        } else {
+            for (int s = 0; s < a.S; ++s) {
+                dv += a.dot_mix[((size_t)s * a.T + t) * kMix + lane];
+            }
         }
     }
 
@@ -200,7 +223,9 @@ __global__ __launch_bounds__(kDBBlock) void pre_dots_bwd_kernel(DotsBwdArgs a)
 
     if (w == 0) {
         float S = 0.0f;
-        if (need_sq) {
+        if (fused) {
+            S = a.sums[(size_t)t * 32 + kHC];
+        } else if (need_sq) {
             S = (part[0][kHC] + part[1][kHC]) + (part[2][kHC] + part[3][kHC]);
         } else {
             for (int s = 0; s < a.S; ++s) {
@@ -234,7 +259,19 @@ __global__ __launch_bounds__(kDBBlock) void pre_dots_bwd_kernel(DotsBwdArgs a)
                 dz = dLmine;
             }
             dm = dz * a.hc_scale[grp];
-            a.d_dot[(size_t)t * kMix + lane] = dm * rstd;
+            if (!fused) {
+                a.d_dot[(size_t)t * kMix + lane] = dm * rstd;
+            }
+        }
+        if (fused && lane < 32) {
+            // d_dot as bf16 hi + lo (the lo half carries the rounding error of the hi)
+            const float v = lane < kMix ? dm * rstd : 0.0f;
+            const uint16_t hi = f32_to_bf16(v);
+            const uint16_t lo = f32_to_bf16(v - bf16_to_f32(hi));
+            a.dd_hi[(size_t)t * 32 + lane] = hi;
+            a.dd_lo[(size_t)t * 32 + lane] = lo;
+            a.ddT_hi[(size_t)lane * a.ldT + t] = hi;
+            a.ddT_lo[(size_t)lane * a.ldT + t] = lo;
         }
         const float d_rstd = wave_sum(dm * d);
         const float dS = -d_rstd * rstd * rstd * rstd / (2.0f * a.k);
@@ -254,11 +291,18 @@ __global__ __launch_bounds__(kDBBlock) void pre_dots_bwd_kernel(DotsBwdArgs a)
             wrow[kMix + 3] = 0.0f;
             if (need_sq) {
                 bc[kHC] = 2.0f * dS;
-            } else {
+            } else if (!fused) {
                 bc[kHC] = 0.0f;
                 a.d_sqrsum[t] = dS;
             }
         }
+        if (fused && lane < 8) {
+            // pre weights (lanes 0..3 hold them in bc), then 2 dS, then padding
+            a.tok[(size_t)t * 8 + lane] = lane < kHC ? bc[lane] : (lane == kHC ? 2.0f * dS : 0.0f);
+        }
+    }
+    if (fused) {
+        return; // d_res is written by the projection's reverse, with the weight term
     }
     __syncthreads();
     const float p0 = bc[0], p1 = bc[1], p2 = bc[2], p3 = bc[3], cr = bc[kHC];
@@ -373,6 +417,357 @@ __global__ __launch_bounds__(64) void pre_bwd_final_kernel(const float *__restri
     } else {
         d_hc_scale[c - kMix] = v;
     }
+}
+
+// ---------------------------------------------------------------- the projection's reverse
+//
+// dot[t][r] = sum_k W[r][k] res_flat[t][k] (k = i*H + h) gives
+//   d_res_flat[t][k] += sum_r dd[t][r] W[r][k]      and      d_W[r][k] = sum_t dd[t][r] res_flat[t][k].
+// One workgroup owns one stream i, a strip of 256 consecutive h and a range of tokens,
+// walked in 32-token chunks.  Each chunk's streams, dy, dd, dd^T and token scalars come
+// in with whole-row 16-byte loads (512 contiguous bytes per row) and go to LDS; the 4
+// wavefronts then do the MFMA work on 64 columns each, reading their operands from LDS,
+// and the d_res tile leaves through LDS as whole rows again.  The next chunk's loads
+// are in flight (in registers) while the current chunk is worked on.
+//   d_res: v_mfma_f32_16x16x32_bf16 with A = W^T (64 columns x 32 logit rows, rows
+//     24..31 zero) and B = dd (logit rows x 16 tokens); W and dd each as bf16 hi + lo,
+//     three products (hi hi, hi lo, lo hi).  The MFMA row order inside a 64-column block
+//     is permuted so that result register q of tile j in lane (g, c) is h = 16g + 4j + q
+//     of token c: each lane ends with 16 consecutive h of one token, which it combines
+//     with pre_i dy + 2 dS res and writes back over dy in LDS.
+//   d_W: A = dd^T (logit rows x 32 tokens, hi and lo), B = res (32 tokens x 16 columns),
+//     read transposed from the LDS tile; the accumulators stay in VGPRs over the token
+//     range and give one partial per (column block, token range), summed over the
+//     ranges in order by a second kernel.
+// The 16-byte pieces of an LDS tile row are XOR-swizzled by a function of the row, so
+// that the 16-byte MFMA-operand reads (16 rows, one piece each) and the transposed
+// 2-byte reads (rows 8g + r over g, 2 pieces) both fall on distinct banks.
+constexpr int kPBCols = 64;                 // columns per wavefront
+constexpr int kPBStrip = 4 * kPBCols;       // columns per workgroup
+constexpr int kPBChunk = 32;                // tokens per step
+constexpr int kPBRowB = kPBStrip * 2;       // bytes per LDS tile row
+constexpr int kPBTile = kPBChunk * kPBRowB; // 16 KiB
+constexpr int kPBSmallRow = 80;             // bytes per LDS dd / dd^T row (64 + 16: conflict-free 16-byte reads)
+constexpr int kPBSmall = kPBChunk * kPBSmallRow;
+constexpr int kPBOffRes = 0;                      // streams tile
+constexpr int kPBOffDy = kPBOffRes + kPBTile;     // 2 dy tiles (d_res written over them)
+constexpr int kPBOffDd = kPBOffDy + 2 * kPBTile;  // dd hi, dd lo: [token][32 rows]
+constexpr int kPBOffDdT = kPBOffDd + 2 * kPBSmall; // dd^T hi, lo: [row][32 tokens]
+constexpr int kPBOffTok = kPBOffDdT + 2 * kPBSmall; // [token][8] floats
+constexpr int kPBSmem = kPBOffTok + kPBChunk * 8 * 4;
+constexpr int kPBTargetBlocks = 1024; // about 2 rounds of 2 workgroups per CU
+
+struct ProjBwdArgs {
+    const uint16_t *dy, *res;
+    const float *tok;              // [T][8]: pre[4], 2 dS
+    const uint16_t *dd_hi, *dd_lo;   // [T][32]
+    const uint16_t *ddT_hi, *ddT_lo; // [32][ldT]
+    const u32x4 *wfrag;            // [blocks][4 tiles][2 terms][64 lanes]
+    int T, H, ldT, nbh, nstrip, nblocks, tok_per_split;
+    uint16_t *d_res;
+    float *dw_part;                // [splits][24][4H]
+};
+
+// W^T fragments in the permuted MFMA row order: one thread per (block, tile, lane);
+// term 0 = hi, term 1 = lo of the fp32 weight.  The same threads also zero the
+// dd^T columns T .. ldT - 1, so that the main kernel reads whole 8-token pieces of
+// dd^T with no tail test (the pad multiplies zero streams; it must only be finite).
+__global__ __launch_bounds__(256) void proj_bwd_wfrag_kernel(const float *__restrict__ hc_fn, int H, int nbh,
+                                                             u32x4 *__restrict__ wfrag, int T, int ldT,
+                                                             uint16_t *__restrict__ ddT_hi,
+                                                             uint16_t *__restrict__ ddT_lo)
+{
+    const int gid = blockIdx.x * 256 + threadIdx.x;
+    const int pad = ldT - T; // 0 .. 31
+    if (gid < 32 * pad) {
+        const size_t at = (size_t)(gid / pad) * ldT + T + gid % pad;
+        ddT_hi[at] = 0;
+        ddT_lo[at] = 0;
+    }
+    const int nblk = kHC * nbh;
+    if (gid >= nblk * 4 * kWave) {
+        return;
+    }
+    const int l = gid & (kWave - 1);
+    const int j = (gid >> 6) & 3;
+    const int b = gid >> 8;
+    const int i = b / nbh, h0 = (b - i * nbh) * kPBCols;
+    const int m = l & 15, rg = l >> 4;
+    const int h = h0 + 16 * (m >> 2) + 4 * j + (m & 3);
+    u32x4 hi, lo;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        float v[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int r = 8 * rg + 2 * q + e;
+            v[e] = (r < kMix && h < H) ? hc_fn[(size_t)r * kHC * H + (size_t)i * H + h] : 0.0f;
+        }
+        const uint16_t h0b = f32_to_bf16(v[0]), h1b = f32_to_bf16(v[1]);
+        hi[q] = (uint32_t)h0b | ((uint32_t)h1b << 16);
+        lo[q] = (uint32_t)f32_to_bf16(v[0] - bf16_to_f32(h0b)) |
+                ((uint32_t)f32_to_bf16(v[1] - bf16_to_f32(h1b)) << 16);
+    }
+    wfrag[((size_t)(b * 4 + j) * 2 + 0) * kWave + l] = hi;
+    wfrag[((size_t)(b * 4 + j) * 2 + 1) * kWave + l] = lo;
+}
+
+// Byte offset of 16-byte piece `ch` (0..31) of row t in an LDS tile.  Over any 16
+// consecutive rows from a multiple of 16 the swizzle takes every value 0..15 once, and
+// over rows 8g + r (g = 0..3, r fixed) its top three bits differ.
+__device__ __forceinline__ int pb_at(int t, int ch)
+{
+    const int swz = (t & 15) ^ (2 * ((t >> 3) & 3));
+    return t * kPBRowB + ((ch ^ swz) << 4);
+}
+
+__device__ __forceinline__ u32x4 lds16(const unsigned char *smem, int off)
+{
+    return *reinterpret_cast<const u32x4 *>(smem + off);
+}
+
+// One chunk's loads, held in registers until they go to LDS.  Thread tid takes piece
+// tid & 31 of tile rows (tid >> 5) + 8k; piece tid & 127 of dd and of dd^T (hi for
+// wavefronts 0 and 1, lo for 2 and 3); piece tid & 63 of the token scalars.
+struct ProjBwdStage {
+    u32x4 r[4], d[4];
+    u32x4 dd, ddT, tk;
+};
+
+__device__ __forceinline__ void pb_issue(const ProjBwdArgs &a, int t0, int te, int i, int tid, int w, uint32_t colo,
+                                         ProjBwdStage &P)
+{
+    const int H = a.H;
+    const int ntok = min(kPBChunk, te - t0);
+    const __amdgpu_buffer_rsrc_t vres =
+        buf_view_b(a.res + (size_t)t0 * kHC * H, (uint32_t)((size_t)ntok * kHC * H * 2));
+    const __amdgpu_buffer_rsrc_t vdy = buf_view_b(a.dy + (size_t)t0 * H, (uint32_t)((size_t)ntok * H * 2));
+    const int row0 = tid >> 5;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int row = row0 + 8 * k;
+        P.r[k] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(vres, (int)((uint32_t)((row * kHC + i) * H) * 2u + colo), 0, 0));
+        P.d[k] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(vdy, (int)((uint32_t)(row * H) * 2u + colo), 0, 0));
+    }
+    const int hl = w >> 1, pc = tid & 127;
+    // past the range dd and the token scalars read as zero; dd^T columns up to ldT exist
+    // (t0 is a multiple of 32 below T) and are zero past T
+    const __amdgpu_buffer_rsrc_t vdd = buf_view_b((hl ? a.dd_lo : a.dd_hi) + (size_t)t0 * 32, (uint32_t)(ntok * 64));
+    P.dd = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vdd, pc * 16, 0, 0));
+    P.ddT = *reinterpret_cast<const u32x4 *>((hl ? a.ddT_lo : a.ddT_hi) + (size_t)(pc >> 2) * a.ldT + t0 +
+                                              8 * (pc & 3));
+    const __amdgpu_buffer_rsrc_t vtok = buf_view_b(a.tok + (size_t)t0 * 8, (uint32_t)(ntok * 32));
+    P.tk = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vtok, (tid & 63) * 16, 0, 0));
+}
+
+__device__ __forceinline__ void pb_commit(unsigned char *smem, const ProjBwdStage &P, int slot, int tid, int w)
+{
+    const int row0 = tid >> 5, ch = tid & 31;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int at = pb_at(row0 + 8 * k, ch);
+        *reinterpret_cast<u32x4 *>(smem + kPBOffRes + at) = P.r[k];
+        *reinterpret_cast<u32x4 *>(smem + kPBOffDy + slot * kPBTile + at) = P.d[k];
+    }
+    const int hl = w >> 1, pc = tid & 127;
+    const int so = hl * kPBSmall + (pc >> 2) * kPBSmallRow + (pc & 3) * 16;
+    *reinterpret_cast<u32x4 *>(smem + kPBOffDd + so) = P.dd;
+    *reinterpret_cast<u32x4 *>(smem + kPBOffDdT + so) = P.ddT;
+    if (w == 0) {
+        *reinterpret_cast<u32x4 *>(smem + kPBOffTok + tid * 16) = P.tk;
+    }
+}
+
+// Workgroup barrier over LDS only: waits for this wavefront's LDS accesses, not for
+// its global loads, which stay in flight across it.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__global__ __launch_bounds__(256, 2) void proj_bwd_kernel(ProjBwdArgs a)
+{
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kPBSmem];
+
+    const int tid = threadIdx.x;
+    const int w = uniform(tid >> 6);
+    const int lane = tid & (kWave - 1);
+    const int g = lane >> 4, c = lane & 15;
+    // workgroup -> (stream i, unit u = strip + nstrip * range); blocks are dealt to the 8
+    // XCDs in turn, so this sends the four streams of a unit to one XCD back to back,
+    // where they share its dy and dd reads in L2
+    const int L = blockIdx.x;
+    const int n32 = a.nblocks & ~31;
+    int u, i;
+    if (L < n32) {
+        u = (L >> 5) * 8 + (L & 7);
+        i = (L >> 3) & 3;
+    } else {
+        u = (n32 >> 2) + ((L - n32) >> 2);
+        i = (L - n32) & 3;
+    }
+    const int hb = u % a.nstrip, split = u / a.nstrip;
+    const int H = a.H;
+    const int hs = hb * kPBStrip;
+    const int tb = split * a.tok_per_split;
+    const int te = min(a.T, tb + a.tok_per_split);
+    // this thread's 16-byte piece of every tile row it moves (past H: loads read zero,
+    // stores are dropped)
+    const int hp = hs + 8 * (tid & 31);
+    const uint32_t colo = hp < H ? (uint32_t)hp * 2u : 0x80000000u;
+
+    const int b = i * a.nbh + hb * 4 + w; // fragment block of this wavefront's 64 columns
+    u32x4 wf[4][2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int tm = 0; tm < 2; ++tm) {
+            wf[j][tm] = a.wfrag[((size_t)(b * 4 + j) * 2 + tm) * kWave + lane];
+        }
+    }
+    f32x4 dw[2][4];
+#pragma unroll
+    for (int rtile = 0; rtile < 2; ++rtile) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            dw[rtile][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+
+    ProjBwdStage P;
+    int t0 = tb;
+    if (t0 < te) {
+        pb_issue(a, t0, te, i, tid, w, colo, P);
+        pb_commit(smem, P, 0, tid, w);
+        if (t0 + kPBChunk < te) {
+            pb_issue(a, t0 + kPBChunk, te, i, tid, w, colo, P);
+        }
+    }
+    const float *tokf = reinterpret_cast<const float *>(smem + kPBOffTok);
+    for (int k = 0; t0 < te; ++k, t0 += kPBChunk) {
+        const int dyo = kPBOffDy + (k & 1) * kPBTile;
+        lds_barrier(); // the chunk is in LDS
+        // ---- d_res for the 2 token tiles of the chunk, written over dy
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            const int row = mt * 16 + c;
+            const float pre = tokf[row * 8 + i], cr = tokf[row * 8 + kHC];
+            const u32x4 bh = lds16(smem, kPBOffDd + row * kPBSmallRow + g * 16);
+            const u32x4 bl = lds16(smem, kPBOffDd + kPBSmall + row * kPBSmallRow + g * 16);
+            f32x4 acc[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wf[j][0]),
+                                                                __builtin_bit_cast(bf16x8, bh), acc[j], 0, 0, 0);
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wf[j][0]),
+                                                                __builtin_bit_cast(bf16x8, bl), acc[j], 0, 0, 0);
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wf[j][1]),
+                                                                __builtin_bit_cast(bf16x8, bh), acc[j], 0, 0, 0);
+            }
+            // lane (g, c): acc[j][q] is h = 16g + 4j + q; piece hf holds tiles 2hf, 2hf + 1
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int at = pb_at(row, 8 * w + 2 * g + hf);
+                const u32x4 rv = lds16(smem, kPBOffRes + at), gv = lds16(smem, dyo + at);
+                u32x4 o;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    // element pair (2q, 2q + 1) of the piece: tile 2hf + (q >> 1), registers 2(q & 1), +1
+                    const int j = 2 * hf + (q >> 1), e = 2 * (q & 1);
+                    const float lo = fmaf(bf16_lo(rv[q]), cr, fmaf(bf16_lo(gv[q]), pre, acc[j][e]));
+                    const float hi = fmaf(bf16_hi(rv[q]), cr, fmaf(bf16_hi(gv[q]), pre, acc[j][e + 1]));
+                    o[q] = pack_bf16x2(lo, hi);
+                }
+                *reinterpret_cast<u32x4 *>(smem + dyo + at) = o;
+            }
+        }
+        // ---- d_W: B = the chunk's streams read transposed (tokens 8g .. 8g + 7 of column 16 jj + c)
+        u32x4 ah[2], al[2];
+#pragma unroll
+        for (int rtile = 0; rtile < 2; ++rtile) {
+            ah[rtile] = lds16(smem, kPBOffDdT + (c + 16 * rtile) * kPBSmallRow + g * 16);
+            al[rtile] = lds16(smem, kPBOffDdT + kPBSmall + (c + 16 * rtile) * kPBSmallRow + g * 16);
+        }
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int ch = 8 * w + 2 * jj + (c >> 3);
+            uint32_t bw[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r0 = 8 * g + 2 * q;
+                const uint32_t e0 =
+                    *reinterpret_cast<const uint16_t *>(smem + kPBOffRes + pb_at(r0, ch) + 2 * (c & 7));
+                const uint32_t e1 =
+                    *reinterpret_cast<const uint16_t *>(smem + kPBOffRes + pb_at(r0 + 1, ch) + 2 * (c & 7));
+                bw[q] = e0 | (e1 << 16);
+            }
+            const bf16x8 B = __builtin_bit_cast(bf16x8, u32x4{bw[0], bw[1], bw[2], bw[3]});
+#pragma unroll
+            for (int rtile = 0; rtile < 2; ++rtile) {
+                dw[rtile][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ah[rtile]), B,
+                                                                       dw[rtile][jj], 0, 0, 0);
+                dw[rtile][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, al[rtile]), B,
+                                                                       dw[rtile][jj], 0, 0, 0);
+            }
+        }
+        lds_barrier(); // d_res of the chunk is in LDS; every wavefront is done with the chunk's operands
+        // ---- d_res rows out (t0 is uniform; saying so keeps the descriptor in SGPRs)
+        const int tu = uniform(t0);
+        const int ntok = min(kPBChunk, te - tu);
+        const __amdgpu_buffer_rsrc_t vout =
+            buf_view_b(a.d_res + (size_t)tu * kHC * H, (uint32_t)((size_t)ntok * kHC * H * 2));
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int row = (tid >> 5) + 8 * kk;
+            __builtin_amdgcn_raw_buffer_store_b128(lds16(smem, dyo + pb_at(row, tid & 31)), vout,
+                                                   (int)((uint32_t)((row * kHC + i) * H) * 2u + colo), 0, 0);
+        }
+        // ---- the next chunk to LDS (streams, dd, dd^T, scalars: single copies, free since
+        // the barrier; dy: the other slot, free since the previous chunk's rows went out),
+        // and the one after it in flight
+        if (t0 + kPBChunk < te) {
+            pb_commit(smem, P, (k + 1) & 1, tid, w);
+            if (t0 + 2 * kPBChunk < te) {
+                pb_issue(a, t0 + 2 * kPBChunk, te, i, tid, w, colo, P);
+            }
+        }
+    }
+    // ---- d_W partial of this (stream, 64 columns, token range): dw[rtile][jj][q] is
+    // logit row 16 rtile + 4g + q, column hs + 64w + 16 jj + c
+#pragma unroll
+    for (int rtile = 0; rtile < 2; ++rtile) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int h = hs + kPBCols * w + 16 * jj + c;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = 16 * rtile + 4 * g + q;
+                if (r < kMix && h < H) {
+                    a.dw_part[((size_t)split * kMix + r) * kHC * H + (size_t)i * H + h] = dw[rtile][jj][q];
+                }
+            }
+        }
+    }
+}
+
+// d_W[r][k] = sum over the token ranges of the partials, in range order.
+__global__ __launch_bounds__(256) void dw_reduce_kernel(const float *__restrict__ part, int splits, int64_t n,
+                                                        float *__restrict__ d_w)
+{
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= n) {
+        return;
+    }
+    float v = 0.0f;
+    for (int s = 0; s < splits; ++s) {
+        v += part[(size_t)s * n + e];
+    }
+    d_w[e] = v;
 }
 
 // ---------------------------------------------------------------- post-map backward
@@ -566,7 +961,7 @@ hipError_t launch_pre_dots_bwd(const uint16_t *dy, const float *d_post, const fl
 {
     float *ws = reinterpret_cast<float *>(workspace);
     if (T > 0) {
-        DotsBwdArgs a;
+        DotsBwdArgs a{};
         a.dy = dy;
         a.d_post = d_post;
         a.d_comb = d_comb;
@@ -620,11 +1015,190 @@ hipError_t launch_pre_dots_bwd(const uint16_t *dy, const float *d_post, const fl
     return hipGetLastError();
 }
 
+// Workspace of the whole pre-map's reverse, all parts 256-byte aligned.
+struct PreBwdLayout {
+    PreGeom g;
+    int nbh, nstrip, splits, tok_per_split, ldT;
+    size_t off_wfrag, off_tok, off_ddh, off_ddl, off_ddTh, off_ddTl, off_rows, off_dw, total;
+};
+
+static size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+static PreBwdLayout pre_bwd_layout(int64_t T, int64_t H)
+{
+    PreBwdLayout L{};
+    L.g = pre_geometry(T, H);
+    L.nstrip = (int)((H + kPBStrip - 1) / kPBStrip);
+    L.nbh = 4 * L.nstrip; // 64-column fragment blocks per stream, whole strips
+    const int nb = kHC * L.nbh;
+    const int64_t steps = (T + kPBChunk - 1) / kPBChunk; // 32-token steps
+    int64_t splits = kPBTargetBlocks / (kHC * L.nstrip);
+    splits = splits > steps ? steps : splits;
+    splits = splits < 1 ? 1 : splits;
+    const int64_t per_steps = (steps + splits - 1) / splits;
+    L.tok_per_split = (int)(per_steps * kPBChunk);
+    L.splits = (int)((T + L.tok_per_split - 1) / L.tok_per_split);
+    if (L.splits < 1) {
+        L.splits = 1;
+    }
+    L.ldT = (int)((T + 31) & ~(int64_t)31);
+    size_t off = up256(L.g.total_bytes);
+    L.off_wfrag = off;
+    off += up256((size_t)nb * 4 * 2 * kWave * sizeof(u32x4));
+    L.off_tok = off;
+    off += up256((size_t)T * 8 * sizeof(float));
+    L.off_ddh = off;
+    off += up256((size_t)T * 32 * 2);
+    L.off_ddl = off;
+    off += up256((size_t)T * 32 * 2);
+    L.off_ddTh = off;
+    off += up256((size_t)32 * L.ldT * 2);
+    L.off_ddTl = off;
+    off += up256((size_t)32 * L.ldT * 2);
+    L.off_rows = off;
+    off += up256(pre_bwd_workspace_bytes(T));
+    L.off_dw = off;
+    off += up256((size_t)L.splits * kMix * kHC * H * sizeof(float));
+    L.total = off;
+    return L;
+}
+
+size_t pre_fused_bwd_workspace_bytes(int64_t T, int64_t H) { return pre_bwd_layout(T, H).total; }
+
+hipError_t launch_pre_fused_bwd(const uint16_t *dy, const float *d_post, const float *d_comb, const uint16_t *res,
+                                const float *hc_fn, const float *hc_scale, const float *hc_base, int64_t T,
+                                int64_t H, float rms_eps, float pre_eps, float sinkhorn_eps, float post_mult,
+                                int iters, uint16_t *d_res, float *d_hc_fn, float *d_hc_scale, float *d_hc_base,
+                                void *workspace, hipStream_t stream)
+{
+    if (T == 0) { // gradients summed over no tokens: zeros
+        pre_bwd_final_kernel<<<dim3(1), dim3(64), 0, stream>>>(nullptr, 0, d_hc_scale, d_hc_base);
+        hipError_t e0 = hipGetLastError();
+        if (e0 != hipSuccess) {
+            return e0;
+        }
+        const int64_t n0 = (int64_t)kMix * kHC * H;
+        dw_reduce_kernel<<<dim3((unsigned)((n0 + 255) / 256)), dim3(256), 0, stream>>>(nullptr, 0, n0, d_hc_fn);
+        return hipGetLastError();
+    }
+    const PreBwdLayout L = pre_bwd_layout(T, H);
+    char *ws = reinterpret_cast<char *>(workspace);
+    float *tok = reinterpret_cast<float *>(ws + L.off_tok);
+    uint16_t *ddh = reinterpret_cast<uint16_t *>(ws + L.off_ddh);
+    uint16_t *ddl = reinterpret_cast<uint16_t *>(ws + L.off_ddl);
+    uint16_t *ddTh = reinterpret_cast<uint16_t *>(ws + L.off_ddTh);
+    uint16_t *ddTl = reinterpret_cast<uint16_t *>(ws + L.off_ddTl);
+    float *rows = reinterpret_cast<float *>(ws + L.off_rows);
+    hipError_t e = launch_pre_split(hc_fn, L.g, workspace, stream);
+    if (e != hipSuccess) {
+        return e;
+    }
+    // forward fields, then the per-token reverse, chunk by chunk
+    for (int64_t c0 = 0; c0 < T; c0 += L.g.chunk) {
+        const int Tc = (int)(T - c0 < L.g.chunk ? T - c0 : L.g.chunk);
+        e = launch_pre_sums(res, L.g, c0, Tc, workspace, stream, true);
+        if (e != hipSuccess) {
+            return e;
+        }
+        DotsBwdArgs a{};
+        a.dy = dy + (size_t)c0 * H;
+        a.d_post = d_post + (size_t)c0 * kHC;
+        a.d_comb = d_comb + (size_t)c0 * kHC * kHC;
+        a.S = 1;
+        a.res = res + (size_t)c0 * kHC * H;
+        a.hc_scale = hc_scale;
+        a.hc_base = hc_base;
+        a.T = Tc;
+        a.H = (int)H;
+        a.k = (float)(kHC * H);
+        a.rms_eps = rms_eps;
+        a.pre_eps = pre_eps;
+        a.sk_eps = sinkhorn_eps;
+        a.post_mult = post_mult;
+        a.iters = iters;
+        a.ws = rows + (size_t)c0 * kWsRow;
+        a.sums = reinterpret_cast<const float *>(ws + L.g.off_prew);
+        a.tok = tok + (size_t)c0 * 8;
+        a.dd_hi = ddh + (size_t)c0 * 32;
+        a.dd_lo = ddl + (size_t)c0 * 32;
+        a.ddT_hi = ddTh + c0;
+        a.ddT_lo = ddTl + c0;
+        a.ldT = L.ldT;
+        const size_t lds = (size_t)(iters + 1) * kWave * sizeof(float);
+        const int64_t per = (H / 8 + kDBBlock - 1) / kDBBlock;
+        const dim3 grid((unsigned)Tc), block(kDBBlock);
+        if (per <= 1) {
+            pre_dots_bwd_kernel<1><<<grid, block, lds, stream>>>(a);
+        } else if (per <= 2) {
+            pre_dots_bwd_kernel<2><<<grid, block, lds, stream>>>(a);
+        } else if (per <= 4) {
+            pre_dots_bwd_kernel<4><<<grid, block, lds, stream>>>(a);
+        } else if (per <= 8) {
+            pre_dots_bwd_kernel<8><<<grid, block, lds, stream>>>(a);
+        } else {
+            pre_dots_bwd_kernel<0><<<grid, block, lds, stream>>>(a);
+        }
+        e = hipGetLastError();
+        if (e != hipSuccess) {
+            return e;
+        }
+    }
+    // token sums of d_hc_scale and d_hc_base
+    const int64_t nblk = (T + kRedTok - 1) / kRedTok;
+    float *part = reinterpret_cast<float *>(reinterpret_cast<char *>(rows) + pre_bwd_rows_bytes(T));
+    pre_bwd_partial_kernel<<<dim3((unsigned)nblk), dim3(kRedTok), 0, stream>>>(rows, T, part);
+    e = hipGetLastError();
+    if (e != hipSuccess) {
+        return e;
+    }
+    pre_bwd_final_kernel<<<dim3(1), dim3(64), 0, stream>>>(part, nblk, d_hc_scale, d_hc_base);
+    e = hipGetLastError();
+    if (e != hipSuccess) {
+        return e;
+    }
+    // the projection's reverse
+    const int nb = kHC * L.nbh;
+    u32x4 *wfrag = reinterpret_cast<u32x4 *>(ws + L.off_wfrag);
+    // nb >= 16, so the grid's 4096+ threads cover the 32 x 31 dd^T pad entries at most
+    proj_bwd_wfrag_kernel<<<dim3((unsigned)((nb * 4 * kWave + 255) / 256)), dim3(256), 0, stream>>>(
+        hc_fn, (int)H, L.nbh, wfrag, (int)T, L.ldT, ddTh, ddTl);
+    e = hipGetLastError();
+    if (e != hipSuccess) {
+        return e;
+    }
+    ProjBwdArgs pa{};
+    pa.dy = dy;
+    pa.res = res;
+    pa.tok = tok;
+    pa.dd_hi = ddh;
+    pa.dd_lo = ddl;
+    pa.ddT_hi = ddTh;
+    pa.ddT_lo = ddTl;
+    pa.wfrag = wfrag;
+    pa.T = (int)T;
+    pa.H = (int)H;
+    pa.ldT = L.ldT;
+    pa.nbh = L.nbh;
+    pa.nstrip = L.nstrip;
+    pa.nblocks = kHC * L.nstrip * L.splits;
+    pa.tok_per_split = L.tok_per_split;
+    pa.d_res = d_res;
+    pa.dw_part = reinterpret_cast<float *>(ws + L.off_dw);
+    proj_bwd_kernel<<<dim3((unsigned)pa.nblocks), dim3(kHC * kWave), 0, stream>>>(pa);
+    e = hipGetLastError();
+    if (e != hipSuccess) {
+        return e;
+    }
+    const int64_t n = (int64_t)kMix * kHC * H;
+    dw_reduce_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(pa.dw_part, L.splits, n, d_hc_fn);
+    return hipGetLastError();
+}
+
 hipError_t launch_post_bwd(const uint16_t *d_out, const uint16_t *x, const uint16_t *res, const float *post,
                            const float *comb, int64_t T, int64_t H, uint16_t *d_x, uint16_t *d_res, float *d_post,
                            float *d_comb, hipStream_t stream, bool vec8)
 {
-    PostBwdArgs a;
+    PostBwdArgs a{};
     a.d_out = d_out;
     a.x = x;
     a.res = res;

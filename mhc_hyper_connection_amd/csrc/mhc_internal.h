@@ -38,6 +38,14 @@ hipError_t launch_pre(const uint16_t *res, const void *hc_fn, bool fn_bf16, int 
                       float post_mult, int iters, bool head, uint16_t *y, float *post, float *comb, float *pre,
                       void *workspace, hipStream_t stream, bool vec8);
 
+// The pre-map's first stages on their own: the weight split (once), then for the token
+// chunk [c0, c0 + Tc) the projection and the slice sums, which leave the per-token
+// fields in the workspace at g.off_prew ([Tc][32] fp32: pre dots 0..3, the sum of
+// squares at 4, post dots 5..8, comb dots 9..24).
+hipError_t launch_pre_split(const float *hc_fn, const PreGeom &g, void *workspace, hipStream_t stream);
+hipError_t launch_pre_sums(const uint16_t *res, const PreGeom &g, int64_t c0, int Tc, void *workspace,
+                           hipStream_t stream, bool vec8);
+
 // Model entry (each hidden row copied into the 4 streams) and the unweighted head (the
 // mean of the 4 streams).  `vec8`: H % 8 == 0 and both pointers 16-byte aligned.
 hipError_t launch_expand(const uint16_t *hidden, int64_t T, int64_t H, uint16_t *streams, hipStream_t stream,
@@ -65,6 +73,16 @@ hipError_t launch_pre_dots_bwd(const uint16_t *dy, const float *d_post, const fl
                                float sinkhorn_eps, float post_mult, int iters, uint16_t *d_res, float *d_dot,
                                float *d_sqrsum, float *d_hc_scale, float *d_hc_base, void *workspace,
                                hipStream_t stream, bool vec8);
+
+// Reverse mode of the whole pre-map (projection inside): forward fields recomputed,
+// the per-token reverse, token sums, then the projection's reverse (d_res with the
+// weight term, d_hc_fn over token ranges).  Needs H % 8 == 0 and 16-byte aligned rows.
+size_t pre_fused_bwd_workspace_bytes(int64_t T, int64_t H);
+hipError_t launch_pre_fused_bwd(const uint16_t *dy, const float *d_post, const float *d_comb, const uint16_t *res,
+                                const float *hc_fn, const float *hc_scale, const float *hc_base, int64_t T,
+                                int64_t H, float rms_eps, float pre_eps, float sinkhorn_eps, float post_mult,
+                                int iters, uint16_t *d_res, float *d_hc_fn, float *d_hc_scale, float *d_hc_base,
+                                void *workspace, hipStream_t stream);
 
 // Reverse mode of the post-map (one workgroup per token).  `vec8`: H % 8 == 0 and
 // d_out/x/res/d_x/d_res 16-byte aligned.

@@ -501,6 +501,44 @@ PreGeom pre_geometry(int64_t T, int64_t H)
     return g;
 }
 
+hipError_t launch_pre_split(const float *hc_fn, const PreGeom &g, void *workspace, hipStream_t stream)
+{
+    u32x4 *frag = reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(workspace) + g.off_frag);
+    const int prep_threads = g.nhb * kHC * (kFragPerHbStream / 3);
+    pre_prep_kernel<float><<<dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, stream>>>(
+        hc_fn, (int)g.H, g.nhb, kMix, frag);
+    return hipGetLastError();
+}
+
+hipError_t launch_pre_sums(const uint16_t *res, const PreGeom &g, int64_t c0, int Tc, void *workspace,
+                           hipStream_t stream, bool vec8)
+{
+    char *ws = reinterpret_cast<char *>(workspace);
+    const int H = (int)g.H;
+    const int tiles = (Tc + kPTok - 1) / kPTok;
+    ProjArgs a{};
+    a.res = res + (size_t)c0 * kHC * H;
+    a.frag = reinterpret_cast<const u32x4 *>(ws + g.off_frag);
+    a.T = Tc;
+    a.H = H;
+    a.nhb = g.nhb;
+    a.S = g.slices;
+    a.rec = reinterpret_cast<float *>(ws + g.off_rec);
+    const dim3 pgrid((unsigned)tiles, (unsigned)g.slices);
+    if (vec8) {
+        pre_proj_kernel<true><<<pgrid, dim3(kPBlock), 0, stream>>>(a);
+    } else {
+        pre_proj_kernel<false><<<pgrid, dim3(kPBlock), 0, stream>>>(a);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        return e;
+    }
+    pre_mixsum_kernel<<<dim3((unsigned)(tiles * kRec)), dim3(256), 0, stream>>>(
+        a.rec, Tc, g.slices, reinterpret_cast<float *>(ws + g.off_prew));
+    return hipGetLastError();
+}
+
 hipError_t launch_pre(const uint16_t *res, const void *hc_fn, bool fn_bf16, int fn_rows, const float *hc_scale,
                       const float *hc_base, const PreGeom &g, float rms_eps, float pre_eps, float sinkhorn_eps,
                       float post_mult, int iters, bool head, uint16_t *y, float *post, float *comb, float *pre,
@@ -527,7 +565,7 @@ hipError_t launch_pre(const uint16_t *res, const void *hc_fn, bool fn_bf16, int 
     for (int64_t c0 = 0; c0 < g.T; c0 += g.chunk) {
         const int Tc = (int)(g.T - c0 < g.chunk ? g.T - c0 : g.chunk);
         const int tiles = (Tc + kPTok - 1) / kPTok;
-        ProjArgs a;
+        ProjArgs a{};
         a.res = res + (size_t)c0 * kHC * H;
         a.frag = frag;
         a.T = Tc;
@@ -550,7 +588,7 @@ hipError_t launch_pre(const uint16_t *res, const void *hc_fn, bool fn_bf16, int 
         if (e != hipSuccess) {
             return e;
         }
-        MixArgs mx;
+        MixArgs mx{};
         mx.sums = sums;
         mx.hc_scale = hc_scale;
         mx.hc_base = hc_base;

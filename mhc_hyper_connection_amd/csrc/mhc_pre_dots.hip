@@ -192,7 +192,7 @@ hipError_t launch_pre_dots(const float *dot_mix, const float *sqrsum, int num_sp
                            float rms_eps, float pre_eps, float sinkhorn_eps, float post_mult, int iters,
                            uint16_t *y, float *post, float *comb, float *pre, hipStream_t stream, bool vec8)
 {
-    DotsArgs a;
+    DotsArgs a{};
     a.dot_mix = dot_mix;
     a.sqrsum = sqrsum;
     a.S = num_splits;

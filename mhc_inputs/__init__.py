@@ -261,6 +261,12 @@ def algorithmic_bytes_pre_dots_backward(T: int, H: int, splits: int = 1, sqrsum:
     return T * (2 * H + 8 * H + 16 + 64 + splits * 96 + 8 * H + 96 + (splits * 4 + 4 if sqrsum else 0))
 
 
+def algorithmic_bytes_pre_backward(T: int, H: int) -> int:
+    """Bytes the whole pre-map's reverse mode must move: dy, res, d_post and d_comb read,
+    d_res written, the fp32 weights read and their gradient written."""
+    return T * (2 * H + 8 * H + 80 + 8 * H) + 2 * 384 * H + 108
+
+
 def algorithmic_bytes_sinkhorn_backward(n: int) -> int:
     """grad and logits read, d_logits written: 64 B each per matrix."""
     return n * 64 * 3

@@ -272,6 +272,43 @@ def test_head_workspace_and_bf16_pre_validation():
     assert f(wsb=need - 1) == mhc.MHC_ERROR_WORKSPACE
 
 
+def _fbwd(lib, **kw):
+    a = dict(dy=0x100000, dpost=0x200000, dcomb=0x210000, res=0x400000, fn=0x1000000, sc=0x500000,
+             base=0x500100, T=8, H=64, rms=1e-6, pe=1e-6, se=1e-6, pm=1.0, it=20, dres=0x600000,
+             dfn=0x2000000, dsc=0x800000, dbase=0x800100, ws=0x9000000, wsb=1 << 30)
+    a.update(kw)
+    v = lambda n: ctypes.c_void_p(a[n]) if a[n] is not None else None
+    return lib.mhc_pre_fused_backward(v("dy"), v("dpost"), v("dcomb"), v("res"), v("fn"), v("sc"), v("base"),
+                                      a["T"], a["H"], a["rms"], a["pe"], a["se"], a["pm"], a["it"], v("dres"),
+                                      v("dfn"), v("dsc"), v("dbase"), v("ws"), a["wsb"], NULL)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(T=-1), dict(H=0), dict(H=60), dict(H=(1 << 21) + 8), dict(it=0), dict(it=256), dict(rms=0.0),
+    dict(se=0.0), dict(pe=-1.0), dict(pm=float("nan")), dict(dy=None), dict(dpost=None), dict(dcomb=None),
+    dict(res=None), dict(fn=None), dict(sc=None), dict(base=None), dict(dres=None), dict(dfn=None),
+    dict(dsc=None), dict(dbase=None), dict(T=0, dfn=None),
+    dict(dy=0x100000 + 8),                  # dy not 16-byte aligned
+    dict(dres=0x400000 + 64),               # d_res overlaps res without being it
+    dict(dfn=0x1000000 + 1024),             # d_hc_fn overlaps hc_fn
+    dict(dbase=0x800000 + 4),               # d_hc_base overlaps d_hc_scale
+    dict(ws=0x600000 + 256),                # workspace overlaps d_res
+])
+def test_pre_fused_backward_validation_invalid(kw):
+    assert _fbwd(mhc.lib(), **kw) == mhc.MHC_ERROR_INVALID_VALUE
+
+
+def test_pre_fused_backward_workspace():
+    lib = mhc.lib()
+    need = mhc.mhc_pre_fused_backward_workspace_bytes(8, 64)
+    assert need > mhc.mhc_pre_fused_workspace_bytes(8, 64) and need % 256 == 0
+    assert mhc.mhc_pre_fused_backward_workspace_bytes(8, 60) == 0
+    assert mhc.mhc_pre_fused_backward_workspace_bytes(0, 64) == 0
+    assert _fbwd(lib, wsb=need - 1) == mhc.MHC_ERROR_WORKSPACE
+    assert _fbwd(lib, ws=None) == mhc.MHC_ERROR_WORKSPACE
+    assert _fbwd(lib, ws=0x9000000 + 16) == mhc.MHC_ERROR_WORKSPACE
+
+
 def test_binding_rejects_cpu_tensors_before_the_library():
     import torch
     with pytest.raises(ValueError):

@@ -336,3 +336,81 @@ def test_pre_from_dots_backward_in_place_deterministic_and_empty():
                                        to_dev_f32(inp.hc_base))
     torch.cuda.synchronize()
     assert not f32_of(e["d_hc_base"]).any() and not f32_of(e["d_hc_scale"]).any()
+
+
+# ----------------------------------------------------------------------------- whole pre-map reverse mode
+
+def _full_pre_bwd_check(inp, dy, d_post, d_comb, got, what, tokens=None):
+    """got: dict of host arrays from mhc_pre_fused_backward.  The oracle's reverse mode on the
+    (sampled) tokens; d_hc_fn, d_hc_scale and d_hc_base need every token, so `tokens` may only
+    be given for the per-token outputs when the sums are checked separately."""
+    T, _, H = inp.res.shape
+    K = HC * H
+    kw = dict()
+    fwd = oracle.pre(inp.res, inp.hc_fn, inp.hc_scale, inp.hc_base)
+    dm = fwd["dot"][None].astype(np.float64)
+    ref_fd = oracle.pre_from_dots_backward(dy, d_post, d_comb, fwd["dot"], inp.res, inp.hc_scale, inp.hc_base,
+                                           k=float(K))
+    tol = _pre_bwd_tolerances(inp, dm, None, dy, d_post, d_comb, float(K), ref_fd)
+    ref = oracle.pre_backward(dy, d_post, d_comb, inp.res, inp.hc_fn, inp.hc_scale, inp.hc_base)
+    W = np.abs(inp.hc_fn.astype(np.float64))
+    dd_err = tol["d_dot"] + 2.0 ** -15 * np.abs(ref_fd["d_dot"])          # d_dot and its hi/lo halves
+    resv = np.abs(bf16_bits_to_f32(inp.res).astype(np.float64)).reshape(T, K)
+    tol_fn = dd_err.T @ resv + 1e-5 * (np.abs(ref_fd["d_dot"]).T @ resv) + 1e-6
+    _assert_within(got["d_hc_fn"], ref["d_hc_fn"], tol_fn, what + " d_hc_fn")
+    _assert_within(got["d_hc_base"], ref["d_hc_base"], tol["d_hc_base"], what + " d_hc_base")
+    _assert_within(got["d_hc_scale"], ref["d_hc_scale"], tol["d_hc_scale"], what + " d_hc_scale")
+    sel = slice(None) if tokens is None else tokens
+    proj_tol = (dd_err[sel] @ W).reshape(-1, HC, H) + 2.0 ** -15 * (np.abs(ref_fd["d_dot"][sel]) @ W).reshape(-1, HC, H)
+    rres = ref["d_res"][sel]
+    gres = bf16_bits_to_f32(got["d_res"][sel]).astype(np.float64)
+    _assert_within(gres, rres, 2.0 ** -7 * np.abs(rres) + 1e-3 + tol["d_res_extra"][sel] + proj_tol, what + " d_res")
+
+
+def _run_full_pre_bwd(inp, dy, d_post, d_comb, **kw):
+    mhc = _mhc()
+    out = mhc.mhc_pre_fused_backward(to_dev_bf16(dy), to_dev_f32(d_post), to_dev_f32(d_comb), to_dev_bf16(inp.res),
+                                     to_dev_f32(inp.hc_fn), to_dev_f32(inp.hc_scale), to_dev_f32(inp.hc_base), **kw)
+    torch.cuda.synchronize()
+    return dict(d_res=bits_of(out["d_res"]), d_hc_fn=f32_of(out["d_hc_fn"]), d_hc_scale=f32_of(out["d_hc_scale"]),
+                d_hc_base=f32_of(out["d_hc_base"]))
+
+
+@pytest.mark.parametrize("T,H", [(16, 256), (5, 64), (33, 1000), (70, 96), (130, 4096), (21, 7168), (300, 1024),
+                                 (1, 8), (65, 2056)])
+def test_pre_fused_backward_matches_oracle(T, H):
+    inp = layer_inputs(T, H, cfg=800 + H % 79, scale=(0.9, 1.1, 1.3))
+    dy, d_post, d_comb = pre_grads(T, H, cfg=800 + H % 79)
+    got = _run_full_pre_bwd(inp, dy, d_post, d_comb)
+    _full_pre_bwd_check(inp, dy, d_post, d_comb, got, f"pre_fused backward T={T} H={H}")
+
+
+def test_pre_fused_backward_many_tokens_h4096():
+    """T=2048, H=4096: several token ranges per column block, the d_hc_fn sums over all of them."""
+    inp = layer_inputs(2048, 4096, cfg=820)
+    dy, d_post, d_comb = pre_grads(2048, 4096, cfg=820)
+    got = _run_full_pre_bwd(inp, dy, d_post, d_comb)
+    _full_pre_bwd_check(inp, dy, d_post, d_comb, got, "pre_fused backward 2048x4096")
+
+
+def test_pre_fused_backward_in_place_deterministic_and_empty():
+    mhc = _mhc()
+    inp = layer_inputs(40, 1024, cfg=830)
+    dy, d_post, d_comb = pre_grads(40, 1024, cfg=830)
+    a = _run_full_pre_bwd(inp, dy, d_post, d_comb)
+    b = _run_full_pre_bwd(inp, dy, d_post, d_comb)
+    for key in a:
+        assert np.array_equal(a[key], b[key]), key
+    r = to_dev_bf16(inp.res)
+    out = mhc.mhc_pre_fused_backward(to_dev_bf16(dy), to_dev_f32(d_post), to_dev_f32(d_comb), r,
+                                     to_dev_f32(inp.hc_fn), to_dev_f32(inp.hc_scale), to_dev_f32(inp.hc_base), d_res=r)
+    torch.cuda.synchronize()
+    assert out["d_res"].data_ptr() == r.data_ptr() and np.array_equal(bits_of(r), a["d_res"])
+    assert np.array_equal(f32_of(out["d_hc_fn"]), a["d_hc_fn"])
+    z = torch.empty(0, HC, 64, dtype=torch.bfloat16, device="cuda")
+    e = mhc.mhc_pre_fused_backward(torch.empty(0, 64, dtype=torch.bfloat16, device="cuda"),
+                                   torch.empty(0, HC, device="cuda"), torch.empty(0, HC, HC, device="cuda"), z,
+                                   torch.ones(MIX, HC * 64, device="cuda"), to_dev_f32(inp.hc_scale),
+                                   to_dev_f32(inp.hc_base))
+    torch.cuda.synchronize()
+    assert not f32_of(e["d_hc_fn"]).any() and not f32_of(e["d_hc_base"]).any() and not f32_of(e["d_hc_scale"]).any()
