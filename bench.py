@@ -319,9 +319,9 @@ def main():
     # Per-call rooflines.  mhc_post and mhc_sinkhorn are one kernel launch each;
     # mhc_pre_fused is four (weight split, projection, slice sums, collapse).
     calls = {}
+    proj = "pre_proj_stream_kernel" if H % 8 == 0 else "pre_proj_kernel"
     if "pre_ms" in breakdown:
         col = "pre_collapse_vec8_kernel" if H % 8 == 0 else "pre_collapse_scalar_kernel"
-        proj = "pre_proj_kernel"
         calls["mhc_pre_fused"] = ("pre_prep_kernel+" + proj + "+pre_mixsum_kernel+" + col, breakdown["pre_ms"], pre_b)
     if "post_ms" in breakdown:
         calls["mhc_post"] = ("post_vec8_kernel" if H % 8 == 0 else "post_scalar_kernel", breakdown["post_ms"], post_b)
@@ -335,13 +335,13 @@ def main():
         calls["mhc_post_backward"] = ("post_bwd_kernel", breakdown["post_bwd_ms"], step_bytes)
     col = "pre_collapse_vec8_kernel" if H % 8 == 0 else "pre_collapse_scalar_kernel"
     if "pre_bf16_ms" in breakdown:
-        calls["mhc_pre_fused_bf16"] = ("pre_prep_kernel+pre_proj_kernel+pre_mixsum_kernel+" + col,
+        calls["mhc_pre_fused_bf16"] = ("pre_prep_kernel+" + proj + "+pre_mixsum_kernel+" + col,
                                        breakdown["pre_bf16_ms"], step_bytes)
     if "head_ms" in breakdown:
-        calls["mhc_head"] = ("pre_prep_kernel+pre_proj_kernel+pre_mixsum_kernel+" + col, breakdown["head_ms"],
+        calls["mhc_head"] = ("pre_prep_kernel+" + proj + "+pre_mixsum_kernel+" + col, breakdown["head_ms"],
                              step_bytes)
     if "pre_bwd_ms" in breakdown:
-        calls["mhc_pre_fused_backward"] = ("pre_prep_kernel+pre_proj_kernel+pre_mixsum_kernel+pre_dots_bwd_kernel+"
+        calls["mhc_pre_fused_backward"] = ("pre_prep_kernel+" + proj + "+pre_mixsum_kernel+pre_dots_bwd_kernel+"
                                            "pre_bwd_partial_kernel+pre_bwd_final_kernel+proj_bwd_wfrag_kernel+"
                                            "proj_bwd_kernel+dw_reduce_kernel", breakdown["pre_bwd_ms"], step_bytes)
     if "expand_ms" in breakdown:
@@ -351,7 +351,7 @@ def main():
     if "pre_dots_bwd_ms" in breakdown:
         calls["mhc_pre_from_dots_backward"] = ("pre_dots_bwd_kernel+pre_bwd_partial_kernel+pre_bwd_final_kernel",
                                                breakdown["pre_dots_bwd_ms"], step_bytes)
-    traffic = load_traffic(T, H)
+    traffic = load_traffic(T, H, args.only)
     per_call = {}
     for name, (kern, ms_k, bytes_k) in calls.items():
         achieved = bytes_k / (ms_k * 1e-3) / 1e9
@@ -443,9 +443,12 @@ def traffic_path(T: int, H: int) -> str:
     return os.path.join(PROFILES, f"hbm_traffic_T{T}_H{H}.json")
 
 
-def load_traffic(T: int, H: int):
-    """Per-kernel HBM bytes per launch from the stored counter runs, or None when
-    they are missing or were taken on different kernel sources."""
+def load_traffic(T: int, H: int, mode: str):
+    """Per-kernel HBM bytes per launch in bench mode `mode`, from the stored counter runs,
+    or None when they are missing or were taken on different kernel sources.  Counters
+    are kept per mode: one kernel can move different bytes in different calls (the
+    per-token reverse writes d_res on its own, only per-token values inside the fused
+    reverse)."""
     try:
         with open(traffic_path(T, H)) as f:
             rec = json.load(f)
@@ -453,7 +456,10 @@ def load_traffic(T: int, H: int):
         return None
     if rec.get("sources_sha256") != sources_digest():
         return None
-    return {k: v["bytes"] for k, v in rec["kernels"].items()}
+    kernels = rec.get("modes", {}).get(mode)
+    if not kernels:
+        return None
+    return {k: v["bytes"] for k, v in kernels.items()}
 
 
 def call_traffic(traffic, kernels: str):
@@ -486,26 +492,35 @@ def _pmc_per_kernel(csv_dir: str, counter: str):
 
 
 def write_traffic(fetch_dir: str, write_dir: str, T: int, H: int, command: str) -> None:
-    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) into bytes per launch,
-    each counter scaled by what it reads for the calibration copy kernel."""
-    fetch = _pmc_per_kernel(fetch_dir, "FETCH_SIZE")
-    write = _pmc_per_kernel(write_dir, "WRITE_SIZE")
+    """Turn two sets of rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; one
+    subdirectory per bench mode) into bytes per launch, per mode and kernel, each counter
+    scaled by what it reads for the calibration copy kernel of the same run."""
     cal_bytes = 2 * (1 << 29)
-    f_fetch = cal_bytes / (fetch["calibration_copy"] * 1024)
-    f_write = cal_bytes / (write["calibration_copy"] * 1024)
-    kernels = {}
-    for k in sorted(set(fetch) & set(write)):
-        if k == "calibration_copy":
+    modes, cals = {}, {}
+    for mode in sorted(os.listdir(fetch_dir)):
+        fd, wd = os.path.join(fetch_dir, mode), os.path.join(write_dir, mode)
+        if not (os.path.isdir(fd) and os.path.isdir(wd)):
             continue
-        rb, wb = fetch[k] * 1024 * f_fetch, write[k] * 1024 * f_write
-        kernels[k] = {"fetch_kib": round(fetch[k], 1), "write_kib": round(write[k], 1),
-                      "read_bytes": round(rb), "write_bytes": round(wb), "bytes": round(rb + wb)}
+        fetch = _pmc_per_kernel(fd, "FETCH_SIZE")
+        write = _pmc_per_kernel(wd, "WRITE_SIZE")
+        if "calibration_copy" not in fetch or "calibration_copy" not in write:
+            continue
+        f_fetch = cal_bytes / (fetch["calibration_copy"] * 1024)
+        f_write = cal_bytes / (write["calibration_copy"] * 1024)
+        cals[mode] = {"fetch_kib": round(fetch["calibration_copy"], 1), "write_kib": round(write["calibration_copy"], 1),
+                      "fetch_factor": round(f_fetch, 4), "write_factor": round(f_write, 4)}
+        kernels = {}
+        for k in sorted(set(fetch) & set(write)):
+            if k == "calibration_copy":
+                continue
+            rb, wb = fetch[k] * 1024 * f_fetch, write[k] * 1024 * f_write
+            kernels[k] = {"fetch_kib": round(fetch[k], 1), "write_kib": round(write[k], 1),
+                          "read_bytes": round(rb), "write_bytes": round(wb), "bytes": round(rb + wb)}
+        modes[mode] = kernels
     rec = {"workload": f"T={T} H={H}", "command": command, "counters": ["FETCH_SIZE", "WRITE_SIZE"],
            "calibration": {"kernel": "torch.neg bf16 2^29 elements", "bytes_read": cal_bytes,
-                           "bytes_written": cal_bytes, "fetch_kib": round(fetch["calibration_copy"], 1),
-                           "write_kib": round(write["calibration_copy"], 1), "fetch_factor": round(f_fetch, 4),
-                           "write_factor": round(f_write, 4)},
-           "sources_sha256": sources_digest(), "kernels": kernels}
+                           "bytes_written": cal_bytes, "per_mode": cals},
+           "sources_sha256": sources_digest(), "modes": modes}
     os.makedirs(PROFILES, exist_ok=True)
     with open(traffic_path(T, H), "w") as f:
         json.dump(rec, f, indent=1)

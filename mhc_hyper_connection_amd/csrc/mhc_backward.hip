@@ -580,15 +580,6 @@ __device__ __forceinline__ void pb_commit(unsigned char *smem, const ProjBwdStag
     }
 }
 
-// Workgroup barrier over LDS only: waits for this wavefront's LDS accesses, not for
-// its global loads, which stay in flight across it.
-__device__ __forceinline__ void lds_barrier()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 __global__ __launch_bounds__(256, 2) void proj_bwd_kernel(ProjBwdArgs a)
 {
     __shared__ __attribute__((aligned(16))) unsigned char smem[kPBSmem];

@@ -130,7 +130,30 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
+// Workgroup barrier over LDS only: waits for this wavefront's LDS accesses, not for
+// its global loads, which stay in flight across it.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Wave-uniform value (forces an SGPR so coefficient loads become scalar loads).
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// A raw buffer view of `bytes` bytes at `base` (stride 0; offsets past the end read
+// zero and drop stores).  Every piece goes through readfirstlane: the caller promises
+// that base and bytes are the same in every lane, and the descriptor then stays in
+// SGPRs even where the compiler would otherwise route it through VGPRs.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_view_uniform(const void *base, uint32_t bytes)
+{
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));
+    const uint32_t n = (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes);
+    void *q = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(q, 0, (int)n, 0x00020000);
+}
 
 } // namespace mhc

@@ -12,11 +12,13 @@
 //     projection loop issues only 16-byte loads and MFMAs.  Three bf16
 //     products accumulated in fp32 reproduce the fp32 weight without rounding
 //     it.
-//  2. pre_proj_kernel -- the 24 x 4H projection and the sum of squares.  A
-//     workgroup owns (64 tokens, a 128-wide slice of H across all 4 streams):
-//     the bf16 streams feed v_mfma_f32_16x16x32_bf16 unchanged, the sum of
-//     squares rides on v_dot2_f32_bf16 from the same registers, and each
-//     workgroup writes one 25-float partial record per token.
+//  2. pre_proj_stream_kernel -- the 24 x 4H projection and the sum of squares.  A
+//     workgroup owns a 128-wide slice of H across all 4 streams and a range of
+//     tokens, walked 32 tokens at a time through an LDS tile (whole-row loads,
+//     the next step in flight): the bf16 streams feed v_mfma_f32_16x16x32_bf16
+//     unchanged, the sum of squares rides on v_dot2_f32_bf16 from the same
+//     registers, and each step writes one 25-float partial record per token.
+//     (pre_proj_kernel, one 64-token tile per workgroup, serves H % 8 != 0.)
 //  3. pre_mixsum_kernel -- sums every record field of every token over the
 //     slices in a fixed order, so the result does not depend on timing.
 //  4. pre_collapse_kernel -- one wavefront per (token, 512-wide H tile): rstd
@@ -145,7 +147,8 @@ struct ProjArgs {
 // k-values of lane group g = l / 16; result register q of lane l is row 4g + q,
 // column l % 16.  A k-step here is one stream i and 32 consecutive h (lane group
 // g takes h = 32*hb + 8g .. +8), identically for A (tokens) and B (weights).
-template <bool kVec>
+// This one-tile-per-workgroup form serves H % 8 != 0 (element loads); for H % 8 == 0
+// pre_proj_stream_kernel below does the same work.
 __global__ __launch_bounds__(kPBlock, 2) void pre_proj_kernel(ProjArgs a)
 {
     __shared__ float red[kPWaves][kPTok][kMix];
@@ -163,29 +166,18 @@ __global__ __launch_bounds__(kPBlock, 2) void pre_proj_kernel(ProjArgs a)
     const int t0 = tile * kPTok;
     const int ntok = min(kPTok, a.T - t0);
 
-    // ---------------- load the slice (buffer loads: rows past T read as zero).
-    // Plain cached loads, not non-temporal: each 128-byte line is read in two 64-byte
-    // halves by neighbouring waves, and the collapse re-reads the same streams soon after.
+    // ---------------- load the slice (elements past T or H read as zero)
     u32x4 d[kPNHB][kPMT][kHC];
-    const __amdgpu_buffer_rsrc_t vres =
-        buf_view(a.res + (size_t)t0 * kHC * H, (uint32_t)((size_t)ntok * kHC * H * sizeof(uint16_t)));
 #pragma unroll
     for (int b = 0; b < kPNHB; ++b) {
         const int hb = (slice * kPNHB + b) * kPWaves + w;
         const int h = hb * kPHB + g * 8;
-        // past H (ragged last block): a column offset beyond the view reads zeros
-        // (one select up front; a select per load becomes branches and serialised loads)
-        const uint32_t colo = h < H ? (uint32_t)h * 2u : 0x80000000u;
 #pragma unroll
         for (int m = 0; m < kPMT; ++m) {
 #pragma unroll
             for (int i = 0; i < kHC; ++i) {
                 const int row = (m * 16 + c) * kHC + i;
-                if (kVec) {
-                    const uint32_t off = (uint32_t)(row * H) * 2u + colo;
-                    d[b][m][i] =
-                        __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vres, (int)off, 0, 0));
-                } else {
+                {
                     u32x4 v = {0u, 0u, 0u, 0u};
                     if (m * 16 + c < ntok) {
                         const uint16_t *p = a.res + ((size_t)t0 * kHC + row) * H + h;
@@ -299,6 +291,231 @@ __global__ __launch_bounds__(kPBlock, 2) void pre_proj_kernel(ProjArgs a)
         }
         rec[kFSq * kPTok + tid] = v;
     }
+}
+
+// Streaming form of the projection (H % 8 == 0).  A workgroup owns one 128-wide
+// slice and a range of tokens: it loads the slice's weight fragments once, keeps them
+// in VGPRs, and walks the range in 32-token steps.  A step's streams come in with
+// whole 256-byte row pieces (row = token * 4 + stream) into an LDS tile, whose 16-byte
+// pieces are XOR-swizzled by the token so that the MFMA operand reads (16 tokens of one
+// stream, one piece each) fall on distinct banks.  The next step's loads are in flight
+// in registers while the current step is multiplied and reduced, across LDS-only
+// barriers.  The products, their order and the reduction order are those of
+// pre_proj_kernel, so the records are bit-identical to its.
+constexpr int kPSTok = 32;                       // tokens per step
+constexpr int kPSMT = kPSTok / 16;               // MFMA row tiles per step
+constexpr int kPSRowB = kPSliceH * 2;            // 256 bytes per tile row
+constexpr int kPSRows = kPSTok * kHC;            // 128 rows per step
+constexpr int kPSLoads = kPSRows / (kPBlock / 16); // row pieces per thread per step (8)
+constexpr int kPSTargetBlocks = 512;             // one round of two workgroups per CU
+// Row stride (floats) of the per-wave partial dots in LDS.  36 = 4 (mod 16): a write of
+// lanes (g, c) at token 4g + k, column c lands on 64 distinct banks, and the reduction's
+// reads of 32 tokens of one column meet at most two to a bank.
+constexpr int kPSRedStride = 36;
+
+struct ProjStreamArgs {
+    const uint16_t *res;
+    const u32x4 *frag;
+    int T, H, nhb, S, tok_per_range;
+    float *rec; // [64-token tiles][S][25][64]
+    uint32_t rec_bytes;
+};
+
+__device__ __forceinline__ int pstile_at(int row, int piece)
+{
+    return row * kPSRowB + ((piece ^ ((row >> 2) & 15)) << 4);
+}
+
+// Thread tid moves piece tid & 15 of rows (tid >> 4) + 16k of the step at t0.  A step
+// past the range gets an empty view: its loads read zero and touch no memory, so every
+// step issues the same loads and the wait counts stay exact across the loop.
+__device__ __forceinline__ void pre_stream_load(const ProjStreamArgs &a, int t0, int te, int tid, uint32_t colq,
+                                                u32x4 (&d)[kPSLoads])
+{
+    const int H = a.H;
+    const int ntok = max(0, min(kPSTok, te - t0));
+    const __amdgpu_buffer_rsrc_t v =
+        buf_view_uniform(a.res + (size_t)t0 * kHC * H, (uint32_t)((size_t)ntok * kHC * H * sizeof(uint16_t)));
+#pragma unroll
+    for (int k = 0; k < kPSLoads; ++k) {
+        const int row = (tid >> 4) + 16 * k;
+        d[k] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(v, (int)((uint32_t)(row * H) * 2u + colq), 0, 0));
+    }
+}
+
+struct PreStreamCtx {
+    int tid, w, lane, g, c, slice, S, te;
+    uint32_t colq;
+    __amdgpu_buffer_rsrc_t vrec; // the chunk's records (under 2 GiB)
+};
+
+// One 32-token step at t0 (its streams in the LDS tile): products, sum of squares and
+// the workgroup reduction into the records.  Between the two barriers the tile takes
+// the streams of step t0 + 32 from `commit`, whose registers then load step t0 + 96.
+__device__ __forceinline__ void pre_stream_step(const ProjStreamArgs &a, const PreStreamCtx &x, int tu,
+                                                unsigned char *tile, float (*red)[kPSTok][kPSRedStride],
+                                                float (*sqp)[kPSTok][4], const u32x4 (&b0)[kHC][3],
+                                                const u32x4 (&b1)[kHC][3], u32x4 (&commit)[kPSLoads])
+{
+    const int w = x.w, g = x.g, c = x.c, tid = x.tid;
+    lds_barrier(); // the step's streams are in LDS
+    f32x4 acc[kPSMT][2];
+    float sq[kPSMT];
+#pragma unroll
+    for (int m = 0; m < kPSMT; ++m) {
+        acc[m][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        sq[m] = 0.0f;
+    }
+    // stream by stream (the operands of one stream read from LDS when needed); each
+    // token's sum of squares still runs stream-major, as in pre_proj_kernel
+#pragma unroll
+    for (int i = 0; i < kHC; ++i) {
+        u32x4 dc[kPSMT];
+#pragma unroll
+        for (int m = 0; m < kPSMT; ++m) {
+            dc[m] = *reinterpret_cast<const u32x4 *>(tile + pstile_at((m * 16 + c) * kHC + i, 4 * w + g));
+        }
+#pragma unroll
+        for (int s = 0; s < 3; ++s) {
+            const bf16x8 B0 = __builtin_bit_cast(bf16x8, b0[i][s]);
+            const bf16x8 B1 = __builtin_bit_cast(bf16x8, b1[i][s]);
+#pragma unroll
+            for (int m = 0; m < kPSMT; ++m) {
+                const bf16x8 A = __builtin_bit_cast(bf16x8, dc[m]);
+                acc[m][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B0, acc[m][0], 0, 0, 0);
+                acc[m][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B1, acc[m][1], 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < kPSMT; ++m) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                // a scalar copy first (see pre_proj_kernel)
+                const uint32_t wk = dc[m][k];
+                const bf16x2 pr = __builtin_bit_cast(bf16x2, wk);
+                sq[m] = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, sq[m], false);
+            }
+        }
+    }
+    // ---- workgroup reduction -> the slice's partial records of these 32 tokens
+#pragma unroll
+    for (int m = 0; m < kPSMT; ++m) {
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            const int col = n * 16 + c;
+            if (col < kMix) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    red[w][m * 16 + 4 * g + k][col] = acc[m][n][k];
+                }
+            }
+        }
+        sqp[w][m * 16 + c][g] = sq[m];
+    }
+    lds_barrier(); // the partial dots are in LDS; every wave is done with the tile
+    // step t0 + 32 to the tile (zeros past the range), step t0 + 96 into the registers
+#pragma unroll
+    for (int k = 0; k < kPSLoads; ++k) {
+        *reinterpret_cast<u32x4 *>(tile + pstile_at((tid >> 4) + 16 * k, tid & 15)) = commit[k];
+    }
+    pre_stream_load(a, tu + 3 * kPSTok, x.te, tid, x.colq, commit);
+    // records are per 64-token tile; t0 is a multiple of 32, so these are entries
+    // (t0 & 63) .. + 31 of tile t0 >> 6.  Every thread issues the same stores (the sum
+    // of squares from threads 0..31; the others' offset is past the view: dropped).
+    const uint32_t rec0 = (uint32_t)((((size_t)(tu >> 6) * x.S + x.slice) * (kRec * kPTok) + (tu & (kPTok - 1))) * 4);
+    const int tok = tid & (kPSTok - 1);
+#pragma unroll
+    for (int j = 0; j < kMix / (kPBlock / kPSTok); ++j) {
+        const int col = (tid >> 5) + j * (kPBlock / kPSTok);
+        float v = red[0][tok][col];
+#pragma unroll
+        for (int ww = 1; ww < kPWaves; ++ww) {
+            v += red[ww][tok][col];
+        }
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), x.vrec,
+                                              (int)(rec0 + (uint32_t)(field_of_col(col) * kPTok + tok) * 4u), 0, 0);
+    }
+    float v = 0.0f;
+#pragma unroll
+    for (int ww = 0; ww < kPWaves; ++ww) {
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+            v += sqp[ww][tok][gg];
+        }
+    }
+    const uint32_t sqo = tid < kPSTok ? rec0 + (uint32_t)(kFSq * kPTok + tok) * 4u : 0x80000000u;
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), x.vrec, (int)sqo, 0, 0);
+}
+
+__global__ __launch_bounds__(kPBlock, 2) void pre_proj_stream_kernel(ProjStreamArgs a)
+{
+    __shared__ __attribute__((aligned(16))) unsigned char tile[kPSRows * kPSRowB];
+    __shared__ float red[kPWaves][kPSTok][kPSRedStride];
+    __shared__ float sqp[kPWaves][kPSTok][4];
+
+    PreStreamCtx x;
+    x.tid = threadIdx.x;
+    x.w = uniform(x.tid >> 6);
+    x.lane = x.tid & (kWave - 1);
+    x.g = x.lane >> 4;
+    x.c = x.lane & 15;
+    x.slice = blockIdx.x;
+    x.S = a.S;
+    const int H = a.H;
+    const int tb = blockIdx.y * a.tok_per_range;
+    x.te = min(a.T, tb + a.tok_per_range);
+    const int hb = x.slice * kPWaves + x.w;
+    // this thread's 16-byte piece of each row it moves (past H: loads read zero)
+    const int hq = x.slice * kPSliceH + 8 * (x.tid & 15);
+    x.colq = hq < H ? (uint32_t)hq * 2u : 0x80000000u;
+    x.vrec = buf_view_uniform(a.rec, a.rec_bytes);
+
+    // the weight fragments of this wave's 32 h of the 4 streams; lanes with c >= 8
+    // stand for weight rows >= 24 in column tile 1 and hold zero; past H all zero
+    u32x4 b0[kHC][3], b1[kHC][3];
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const u32x4 *fp = a.frag + (size_t)hb * kHC * kFragPerHbStream;
+#pragma unroll
+    for (int i = 0; i < kHC; ++i) {
+#pragma unroll
+        for (int s = 0; s < 3; ++s) {
+            b0[i][s] = hb < a.nhb ? fp[i * kFragPerHbStream + s * 64 + x.lane] : z;
+            b1[i][s] = hb < a.nhb && x.c < 8 ? fp[i * kFragPerHbStream + 192 + s * 32 + ((x.g * 8 + x.c) & 31)] : z;
+        }
+    }
+
+    // step t0's streams in the tile; steps t0 + 32 and t0 + 64 in flight in two register sets
+    u32x4 lda[kPSLoads], ldb[kPSLoads];
+    if (tb >= x.te) {
+        return;
+    }
+    pre_stream_load(a, uniform(tb), x.te, x.tid, x.colq, lda);
+#pragma unroll
+    for (int k = 0; k < kPSLoads; ++k) {
+        *reinterpret_cast<u32x4 *>(tile + pstile_at((x.tid >> 4) + 16 * k, x.tid & 15)) = lda[k];
+    }
+    pre_stream_load(a, uniform(tb + kPSTok), x.te, x.tid, x.colq, lda);
+    pre_stream_load(a, uniform(tb + 2 * kPSTok), x.te, x.tid, x.colq, ldb);
+    for (int t0 = tb; t0 < x.te; t0 += 2 * kPSTok) {
+        const int tu = uniform(t0);
+        pre_stream_step(a, x, tu, tile, red, sqp, b0, b1, lda);
+        if (tu + kPSTok >= x.te) {
+            break;
+        }
+        pre_stream_step(a, x, tu + kPSTok, tile, red, sqp, b0, b1, ldb);
+    }
+}
+
+// Token ranges of the streaming projection for Tc tokens and S slices.
+static void pre_stream_ranges(int Tc, int S, int &ranges, int &tok_per_range)
+{
+    const int steps = (Tc + kPSTok - 1) / kPSTok;
+    int r = kPSTargetBlocks / S;
+    r = r < 1 ? 1 : (r > steps ? steps : r);
+    tok_per_range = ((steps + r - 1) / r) * kPSTok;
+    ranges = (Tc + tok_per_range - 1) / tok_per_range;
 }
 
 // Per-token sums of the 25 record fields over the slices.  Block = (tile,
@@ -524,11 +741,21 @@ hipError_t launch_pre_sums(const uint16_t *res, const PreGeom &g, int64_t c0, in
     a.nhb = g.nhb;
     a.S = g.slices;
     a.rec = reinterpret_cast<float *>(ws + g.off_rec);
-    const dim3 pgrid((unsigned)tiles, (unsigned)g.slices);
     if (vec8) {
-        pre_proj_kernel<true><<<pgrid, dim3(kPBlock), 0, stream>>>(a);
+        ProjStreamArgs sa{};
+        sa.res = a.res;
+        sa.frag = a.frag;
+        sa.T = a.T;
+        sa.H = H;
+        sa.nhb = g.nhb;
+        sa.S = g.slices;
+        sa.rec = a.rec;
+        sa.rec_bytes = (uint32_t)g.rec_bytes;
+        int ranges = 1;
+        pre_stream_ranges(a.T, g.slices, ranges, sa.tok_per_range);
+        pre_proj_stream_kernel<<<dim3((unsigned)g.slices, (unsigned)ranges), dim3(kPBlock), 0, stream>>>(sa);
     } else {
-        pre_proj_kernel<false><<<pgrid, dim3(kPBlock), 0, stream>>>(a);
+        pre_proj_kernel<<<dim3((unsigned)tiles, (unsigned)g.slices), dim3(kPBlock), 0, stream>>>(a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
@@ -573,11 +800,21 @@ hipError_t launch_pre(const uint16_t *res, const void *hc_fn, bool fn_bf16, int 
         a.nhb = g.nhb;
         a.S = g.slices;
         a.rec = reinterpret_cast<float *>(ws + g.off_rec);
-        const dim3 pgrid((unsigned)tiles, (unsigned)g.slices);
         if (vec8) {
-            pre_proj_kernel<true><<<pgrid, dim3(kPBlock), 0, stream>>>(a);
+            ProjStreamArgs sa{};
+            sa.res = a.res;
+            sa.frag = a.frag;
+            sa.T = a.T;
+            sa.H = H;
+            sa.nhb = g.nhb;
+            sa.S = g.slices;
+            sa.rec = a.rec;
+            sa.rec_bytes = (uint32_t)g.rec_bytes;
+            int ranges = 1;
+            pre_stream_ranges(a.T, g.slices, ranges, sa.tok_per_range);
+            pre_proj_stream_kernel<<<dim3((unsigned)g.slices, (unsigned)ranges), dim3(kPBlock), 0, stream>>>(sa);
         } else {
-            pre_proj_kernel<false><<<pgrid, dim3(kPBlock), 0, stream>>>(a);
+            pre_proj_kernel<<<dim3((unsigned)tiles, (unsigned)g.slices), dim3(kPBlock), 0, stream>>>(a);
         }
         e = hipGetLastError();
         if (e != hipSuccess) {
