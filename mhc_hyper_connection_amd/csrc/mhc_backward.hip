@@ -116,11 +116,11 @@ struct DotsBwdArgs {
     uint16_t *d_res;
     float *d_dot, *d_sqrsum;
     float *ws; // [T][kWsRow]
-    // Projection inside (the reverse of the whole pre-map): the dots and the sum of
-    // squares come from the projection's per-token fields, and instead of d_res the
-    // kernel writes pre and 2 dS ([T][8]) and d_dot as bf16 hi and lo halves, both
-    // row-major [T][32] and transposed [32][ldT] (rows 24..31 zero).
-    const float *sums; // [T][32], or null
+    // pre_tok_bwd_kernel (the reverse of the whole pre-map): the per-token fields come
+    // from the projection's recompute, and instead of d_res it writes pre and 2 dS
+    // ([T][8]) and d_dot as bf16 hi and lo halves, both row-major [T][32] and
+    // transposed [32][ldT] (rows 24..31 zero).
+    const float *sums; // [T][32]
     float *tok;
     uint16_t *dd_hi, *dd_lo, *ddT_hi, *ddT_lo;
     int ldT;
@@ -145,18 +145,13 @@ __global__ __launch_bounds__(kDBBlock) void pre_dots_bwd_kernel(DotsBwdArgs a)
     const int H = a.H;
     const uint16_t *row = a.res + (size_t)t * kHC * H;
     const uint16_t *grow = a.dy + (size_t)t * H;
-    const bool fused = a.sums != nullptr;
     // S computed here from the streams (the RMS term of d_res applies), or supplied
-    const bool need_sq = a.sqrsum == nullptr && !fused;
+    const bool need_sq = a.sqrsum == nullptr;
 
     float dv = 0.0f;
     if (w == 0 && lane < kMix) {
-        if (fused) {
-            dv = a.sums[(size_t)t * 32 + sums_field(lane)];
-        } else {
-            for (int s = 0; s < a.S; ++s) {
-                dv += a.dot_mix[((size_t)s * a.T + t) * kMix + lane];
-            }
+        for (int s = 0; s < a.S; ++s) {
+            dv += a.dot_mix[((size_t)s * a.T + t) * kMix + lane];
         }
     }
 
@@ -223,9 +218,7 @@ __global__ __launch_bounds__(kDBBlock) void pre_dots_bwd_kernel(DotsBwdArgs a)
 
     if (w == 0) {
         float S = 0.0f;
-        if (fused) {
-            S = a.sums[(size_t)t * 32 + kHC];
-        } else if (need_sq) {
+        if (need_sq) {
             S = (part[0][kHC] + part[1][kHC]) + (part[2][kHC] + part[3][kHC]);
         } else {
             for (int s = 0; s < a.S; ++s) {
@@ -259,19 +252,7 @@ __global__ __launch_bounds__(kDBBlock) void pre_dots_bwd_kernel(DotsBwdArgs a)
                 dz = dLmine;
             }
             dm = dz * a.hc_scale[grp];
-            if (!fused) {
-                a.d_dot[(size_t)t * kMix + lane] = dm * rstd;
-            }
-        }
-        if (fused && lane < 32) {
-            // d_dot as bf16 hi + lo (the lo half carries the rounding error of the hi)
-            const float v = lane < kMix ? dm * rstd : 0.0f;
-            const uint16_t hi = f32_to_bf16(v);
-            const uint16_t lo = f32_to_bf16(v - bf16_to_f32(hi));
-            a.dd_hi[(size_t)t * 32 + lane] = hi;
-            a.dd_lo[(size_t)t * 32 + lane] = lo;
-            a.ddT_hi[(size_t)lane * a.ldT + t] = hi;
-            a.ddT_lo[(size_t)lane * a.ldT + t] = lo;
+            a.d_dot[(size_t)t * kMix + lane] = dm * rstd;
         }
         const float d_rstd = wave_sum(dm * d);
         const float dS = -d_rstd * rstd * rstd * rstd / (2.0f * a.k);
@@ -291,18 +272,11 @@ __global__ __launch_bounds__(kDBBlock) void pre_dots_bwd_kernel(DotsBwdArgs a)
             wrow[kMix + 3] = 0.0f;
             if (need_sq) {
                 bc[kHC] = 2.0f * dS;
-            } else if (!fused) {
+            } else {
                 bc[kHC] = 0.0f;
                 a.d_sqrsum[t] = dS;
             }
         }
-        if (fused && lane < 8) {
-            // pre weights (lanes 0..3 hold them in bc), then 2 dS, then padding
-            a.tok[(size_t)t * 8 + lane] = lane < kHC ? bc[lane] : (lane == kHC ? 2.0f * dS : 0.0f);
-        }
-    }
-    if (fused) {
-        return; // d_res is written by the projection's reverse, with the weight term
     }
     __syncthreads();
     const float p0 = bc[0], p1 = bc[1], p2 = bc[2], p3 = bc[3], cr = bc[kHC];
@@ -338,6 +312,80 @@ __global__ __launch_bounds__(kDBBlock) void pre_dots_bwd_kernel(DotsBwdArgs a)
                 drow[(size_t)i * H + h] = f32_to_bf16(fmaf(v, cr, gv * pw[i]));
             }
         }
+    }
+}
+
+// The whole pre-map's per-token reverse.  One 64-thread workgroup per token, after the
+// projection's recompute left the token's fields in `sums` ([T][32]: pre dots 0..3, S
+// at 4, post dots 5..8, comb dots 9..24, <dy, res_i> at 25..28).  The chain is that of
+// pre_dots_bwd_kernel's wavefront 0 with S taken from the streams (the RMS term of
+// d_res applies); it writes pre and 2 dS, the dot gradients as bf16 hi + lo halves
+// (row-major and transposed) for the projection's reverse, and the token's row of the
+// d_hc_scale / d_hc_base sums.  No stream is read here.
+constexpr int kSumsDy = kMix + 1; // first <dy, res_i> field in the sums
+__global__ __launch_bounds__(kWave) void pre_tok_bwd_kernel(DotsBwdArgs a)
+{
+    extern __shared__ float hist[]; // [iters + 1][64]: the Sinkhorn history
+    const int t = blockIdx.x;
+    const int lane = threadIdx.x;
+    const float *sm = a.sums + (size_t)t * 32;
+    const float rstd = 1.0f / sqrtf(sm[kHC] / a.k + a.rms_eps);
+    // comb: Sinkhorn reverse mode, entry e = lane & 15 on every 16-lane row (each row
+    // computes the same matrix); lane 8 + e then takes entry e from lane e
+    const int e = lane & 15;
+    const float Lc = fmaf(sm[sums_field(2 * kHC + e)] * rstd, a.hc_scale[2], a.hc_base[2 * kHC + e]);
+    const float Gc = a.d_comb[(size_t)t * kHC * kHC + e];
+    const float dLc = sinkhorn_row16_backward(Lc, Gc, a.iters, a.sk_eps, hist + lane);
+    const float dLmine = __shfl(dLc, (lane - 2 * kHC) & 15);
+    // lanes 0..23: one mix each
+    const int grp = lane < kHC ? 0 : (lane < 2 * kHC ? 1 : 2);
+    float dz = 0.0f, m = 0.0f, dm = 0.0f, d = 0.0f, pw = 0.0f;
+    if (lane < kMix) {
+        d = sm[sums_field(lane)];
+        m = d * rstd;
+        if (lane < 2 * kHC) {
+            const float sg = sigmoidf_fast(fmaf(m, a.hc_scale[grp], a.hc_base[lane]));
+            if (lane < kHC) {
+                dz = sm[kSumsDy + lane] * sg * (1.0f - sg);
+                pw = sg + a.pre_eps;
+            } else {
+                dz = a.d_post[(size_t)t * kHC + lane - kHC] * a.post_mult * sg * (1.0f - sg);
+            }
+        } else {
+            dz = dLmine;
+        }
+        dm = dz * a.hc_scale[grp];
+    }
+    if (lane < 32) {
+        // d_dot as bf16 hi + lo (the lo half carries the rounding error of the hi)
+        const float v = lane < kMix ? dm * rstd : 0.0f;
+        const uint16_t hi = f32_to_bf16(v);
+        const uint16_t lo = f32_to_bf16(v - bf16_to_f32(hi));
+        a.dd_hi[(size_t)t * 32 + lane] = hi;
+        a.dd_lo[(size_t)t * 32 + lane] = lo;
+        a.ddT_hi[(size_t)lane * a.ldT + t] = hi;
+        a.ddT_lo[(size_t)lane * a.ldT + t] = lo;
+    }
+    const float d_rstd = wave_sum(dm * d);
+    const float dS = -d_rstd * rstd * rstd * rstd / (2.0f * a.k);
+    float *wrow = a.ws + (size_t)t * kWsRow;
+    const float zm = dz * m;
+    // per-group sums of dz * m over lanes 0..3, 4..7 and 8..23 (fixed order)
+    const float g0 = wave_sum(lane < kHC ? zm : 0.0f);
+    const float g1 = wave_sum(lane >= kHC && lane < 2 * kHC ? zm : 0.0f);
+    const float g2 = wave_sum(lane >= 2 * kHC && lane < kMix ? zm : 0.0f);
+    if (lane < kMix) {
+        wrow[lane] = dz;
+    }
+    if (lane == 0) {
+        wrow[kMix] = g0;
+        wrow[kMix + 1] = g1;
+        wrow[kMix + 2] = g2;
+        wrow[kMix + 3] = 0.0f;
+    }
+    if (lane < 8) {
+        // pre weights (lanes 0..3), then 2 dS, then padding
+        a.tok[(size_t)t * 8 + lane] = lane < kHC ? pw : (lane == kHC ? 2.0f * dS : 0.0f);
     }
 }
 
@@ -1018,7 +1066,7 @@ static size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 static PreBwdLayout pre_bwd_layout(int64_t T, int64_t H)
 {
     PreBwdLayout L{};
-    L.g = pre_geometry(T, H);
+    L.g = pre_geometry(T, H, true);
     L.nstrip = (int)((H + kPBStrip - 1) / kPBStrip);
     L.nbh = 4 * L.nstrip; // 64-column fragment blocks per stream, whole strips
     const int nb = kHC * L.nbh;
@@ -1084,19 +1132,16 @@ hipError_t launch_pre_fused_bwd(const uint16_t *dy, const float *d_post, const f
     if (e != hipSuccess) {
         return e;
     }
-    // forward fields, then the per-token reverse, chunk by chunk
+    // forward fields and <dy, res_i>, then the per-token reverse, chunk by chunk
     for (int64_t c0 = 0; c0 < T; c0 += L.g.chunk) {
         const int Tc = (int)(T - c0 < L.g.chunk ? T - c0 : L.g.chunk);
-        e = launch_pre_sums(res, L.g, c0, Tc, workspace, stream, true);
+        e = launch_pre_sums(res, dy, L.g, c0, Tc, workspace, stream, true);
         if (e != hipSuccess) {
             return e;
         }
         DotsBwdArgs a{};
-        a.dy = dy + (size_t)c0 * H;
         a.d_post = d_post + (size_t)c0 * kHC;
         a.d_comb = d_comb + (size_t)c0 * kHC * kHC;
-        a.S = 1;
-        a.res = res + (size_t)c0 * kHC * H;
         a.hc_scale = hc_scale;
         a.hc_base = hc_base;
         a.T = Tc;
@@ -1116,19 +1161,7 @@ hipError_t launch_pre_fused_bwd(const uint16_t *dy, const float *d_post, const f
         a.ddT_lo = ddTl + c0;
         a.ldT = L.ldT;
         const size_t lds = (size_t)(iters + 1) * kWave * sizeof(float);
-        const int64_t per = (H / 8 + kDBBlock - 1) / kDBBlock;
-        const dim3 grid((unsigned)Tc), block(kDBBlock);
-        if (per <= 1) {
-            pre_dots_bwd_kernel<1><<<grid, block, lds, stream>>>(a);
-        } else if (per <= 2) {
-            pre_dots_bwd_kernel<2><<<grid, block, lds, stream>>>(a);
-        } else if (per <= 4) {
-            pre_dots_bwd_kernel<4><<<grid, block, lds, stream>>>(a);
-        } else if (per <= 8) {
-            pre_dots_bwd_kernel<8><<<grid, block, lds, stream>>>(a);
-        } else {
-            pre_dots_bwd_kernel<0><<<grid, block, lds, stream>>>(a);
-        }
+        pre_tok_bwd_kernel<<<dim3((unsigned)Tc), dim3(kWave), lds, stream>>>(a);
         e = hipGetLastError();
         if (e != hipSuccess) {
             return e;

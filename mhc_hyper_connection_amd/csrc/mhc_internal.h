@@ -23,13 +23,14 @@ struct PreGeom {
     int tiles;         // 64-token tiles in one chunk
     int nhb;           // ceil(H / 32)
     int slices;        // workgroups per 64-token tile in the projection
+    int nrec;          // fields per record: 25, or 29 with the reverse's <dy, res_i>
     size_t off_frag;   // split weights in MFMA operand order
     size_t off_rec;    // partial records of one chunk
     size_t rec_bytes;
     size_t off_prew;   // per-token field sums of one chunk
     size_t total_bytes;
 };
-PreGeom pre_geometry(int64_t T, int64_t H);
+PreGeom pre_geometry(int64_t T, int64_t H, bool with_dy = false);
 
 // The pre-map (and, with `head`, the weighted head: `fn_rows` = 4 weight rows, pre
 // weights and y only).  `hc_fn` is fp32, or bf16 bit patterns when `fn_bf16`.
@@ -41,10 +42,11 @@ hipError_t launch_pre(const uint16_t *res, const void *hc_fn, bool fn_bf16, int 
 // The pre-map's first stages on their own: the weight split (once), then for the token
 // chunk [c0, c0 + Tc) the projection and the slice sums, which leave the per-token
 // fields in the workspace at g.off_prew ([Tc][32] fp32: pre dots 0..3, the sum of
-// squares at 4, post dots 5..8, comb dots 9..24).
+// squares at 4, post dots 5..8, comb dots 9..24; with `dy` (the reverse's recompute,
+// g from pre_geometry(T, H, true), vec8 only) also <dy, res_i> at 25..28).
 hipError_t launch_pre_split(const float *hc_fn, const PreGeom &g, void *workspace, hipStream_t stream);
-hipError_t launch_pre_sums(const uint16_t *res, const PreGeom &g, int64_t c0, int Tc, void *workspace,
-                           hipStream_t stream, bool vec8);
+hipError_t launch_pre_sums(const uint16_t *res, const uint16_t *dy, const PreGeom &g, int64_t c0, int Tc,
+                           void *workspace, hipStream_t stream, bool vec8);
 
 // Model entry (each hidden row copied into the 4 streams) and the unweighted head (the
 // mean of the 4 streams).  `vec8`: H % 8 == 0 and both pointers 16-byte aligned.

@@ -46,7 +46,6 @@ constexpr int kPNHB = 1;         // blocks per wave
 constexpr int kPSliceH = kPWaves * kPNHB * kPHB;
 constexpr int kRec = kMix + 1;                    // partial record fields: 24 dots + sum of squares
 constexpr int kFragPerHbStream = 3 * 64 + 3 * 32; // hi/mid/lo of column tile 0 (64 lanes) and 1 (32 lanes)
-constexpr int kBufWord3 = 0x00020000;
 
 constexpr int kColBlock = 256;
 constexpr int kColWaves = kColBlock / kWave;
@@ -57,11 +56,6 @@ constexpr int kColVecTile = kWave * 8;
 // field of the 64 tokens is 256 contiguous bytes.
 constexpr int kFSq = kHC;
 __device__ __forceinline__ int field_of_col(int col) { return col < kHC ? col : col + 1; }
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_view(const void *base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kBufWord3);
-}
 
 // v == hi + mid + lo exactly for normal fp32 v (three successive bf16 truncations).
 __device__ __forceinline__ void split3x8(const float *v, u32x4 &ph, u32x4 &pm, u32x4 &pl)
@@ -315,11 +309,15 @@ constexpr int kPSRedStride = 36;
 
 struct ProjStreamArgs {
     const uint16_t *res;
+    const uint16_t *dy; // the reverse's recompute: the layer input's gradient [T][H], else null
     const u32x4 *frag;
     int T, H, nhb, S, tok_per_range;
-    float *rec; // [64-token tiles][S][25][64]
+    float *rec; // [64-token tiles][S][nrec][64]
     uint32_t rec_bytes;
 };
+// Record fields: 24 dots + the sum of squares; with dy also <dy, res_i> at 25 .. 28.
+constexpr int kRecDy = kRec + kHC;
+constexpr int kFDy = kRec;
 
 __device__ __forceinline__ int pstile_at(int row, int piece)
 {
@@ -344,19 +342,43 @@ __device__ __forceinline__ void pre_stream_load(const ProjStreamArgs &a, int t0,
     }
 }
 
+// dy of the step at t0 for this slice: 32 rows (tokens) of 16 pieces; thread tid moves
+// piece tid & 15 of rows (tid >> 4) + 16k, k < 2 (empty view past the range).
+constexpr int kPSDyLoads = kPSTok / (kPBlock / 16);
+__device__ __forceinline__ void pre_stream_load_dy(const ProjStreamArgs &a, int t0, int te, int tid, uint32_t colq,
+                                                   u32x4 (&d)[kPSDyLoads])
+{
+    const int H = a.H;
+    const int ntok = max(0, min(kPSTok, te - t0));
+    const __amdgpu_buffer_rsrc_t v =
+        buf_view_uniform(a.dy + (size_t)t0 * H, (uint32_t)((size_t)ntok * H * sizeof(uint16_t)));
+#pragma unroll
+    for (int k = 0; k < kPSDyLoads; ++k) {
+        const int row = (tid >> 4) + 16 * k;
+        d[k] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(v, (int)((uint32_t)(row * H) * 2u + colq), 0, 0));
+    }
+}
+
+// Byte offset of piece p of dy row (token) r in its LDS tile: the same swizzle by token.
+__device__ __forceinline__ int psdy_at(int row, int piece) { return row * kPSRowB + ((piece ^ (row & 15)) << 4); }
+
 struct PreStreamCtx {
     int tid, w, lane, g, c, slice, S, te;
     uint32_t colq;
     __amdgpu_buffer_rsrc_t vrec; // the chunk's records (under 2 GiB)
 };
 
-// One 32-token step at t0 (its streams in the LDS tile): products, sum of squares and
-// the workgroup reduction into the records.  Between the two barriers the tile takes
-// the streams of step t0 + 32 from `commit`, whose registers then load step t0 + 96.
+// One 32-token step at t0 (its streams, and with kDy its dy, in the LDS tiles):
+// products, sum of squares (and <dy, res_i>), and the workgroup reduction into the
+// records.  After the second barrier the tiles take step t0 + 32 from the registers,
+// which then load step t0 + 64.
+template <bool kDy>
 __device__ __forceinline__ void pre_stream_step(const ProjStreamArgs &a, const PreStreamCtx &x, int tu,
-                                                unsigned char *tile, float (*red)[kPSTok][kPSRedStride],
-                                                float (*sqp)[kPSTok][4], const u32x4 (&b0)[kHC][3],
-                                                const u32x4 (&b1)[kHC][3], u32x4 (&commit)[kPSLoads])
+                                                unsigned char *tile, unsigned char *dyt,
+                                                float (*red)[kPSTok][kPSRedStride], float (*sqp)[kPSTok][4],
+                                                const u32x4 (&b0)[kHC][3], const u32x4 (&b1)[kHC][3],
+                                                u32x4 (&ld)[kPSLoads], u32x4 (&ldy)[kPSDyLoads])
 {
     const int w = x.w, g = x.g, c = x.c, tid = x.tid;
     lds_barrier(); // the step's streams are in LDS
@@ -367,6 +389,15 @@ __device__ __forceinline__ void pre_stream_step(const ProjStreamArgs &a, const P
         acc[m][0] = f32x4{0.f, 0.f, 0.f, 0.f};
         acc[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
         sq[m] = 0.0f;
+    }
+    // this lane's 8 h of dy for its two tokens (the same h as its stream operands)
+    u32x4 gy[kPSMT];
+    float pd[kPSMT][kHC];
+    if (kDy) {
+#pragma unroll
+        for (int m = 0; m < kPSMT; ++m) {
+            gy[m] = *reinterpret_cast<const u32x4 *>(dyt + psdy_at(m * 16 + c, 4 * w + g));
+        }
     }
     // stream by stream (the operands of one stream read from LDS when needed); each
     // token's sum of squares still runs stream-major, as in pre_proj_kernel
@@ -390,12 +421,19 @@ __device__ __forceinline__ void pre_stream_step(const ProjStreamArgs &a, const P
         }
 #pragma unroll
         for (int m = 0; m < kPSMT; ++m) {
+            if (kDy) {
+                pd[m][i] = 0.0f;
+            }
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 // a scalar copy first (see pre_proj_kernel)
                 const uint32_t wk = dc[m][k];
                 const bf16x2 pr = __builtin_bit_cast(bf16x2, wk);
                 sq[m] = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, sq[m], false);
+                if (kDy) {
+                    const uint32_t yk = gy[m][k];
+                    pd[m][i] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, yk), pr, pd[m][i], false);
+                }
             }
         }
     }
@@ -413,18 +451,40 @@ __device__ __forceinline__ void pre_stream_step(const ProjStreamArgs &a, const P
             }
         }
         sqp[w][m * 16 + c][g] = sq[m];
+        if (kDy) {
+            // over the 4 lane groups of token m*16 + c: (g0 + g1) + (g2 + g3), every lane
+#pragma unroll
+            for (int i = 0; i < kHC; ++i) {
+                float v = pd[m][i];
+                v += __shfl_xor(v, 16);
+                v += __shfl_xor(v, 32);
+                if (g == 0) {
+                    red[w][m * 16 + c][kMix + i] = v;
+                }
+            }
+        }
     }
-    lds_barrier(); // the partial dots are in LDS; every wave is done with the tile
-    // step t0 + 32 to the tile (zeros past the range), step t0 + 96 into the registers
+    lds_barrier(); // the partial dots are in LDS; every wave is done with the tiles
+    // step t0 + 32 to the tiles (zeros past the range), step t0 + 64 into the registers
 #pragma unroll
     for (int k = 0; k < kPSLoads; ++k) {
-        *reinterpret_cast<u32x4 *>(tile + pstile_at((tid >> 4) + 16 * k, tid & 15)) = commit[k];
+        *reinterpret_cast<u32x4 *>(tile + pstile_at((tid >> 4) + 16 * k, tid & 15)) = ld[k];
     }
-    pre_stream_load(a, tu + 3 * kPSTok, x.te, tid, x.colq, commit);
+    if (kDy) {
+#pragma unroll
+        for (int k = 0; k < kPSDyLoads; ++k) {
+            *reinterpret_cast<u32x4 *>(dyt + psdy_at((tid >> 4) + 16 * k, tid & 15)) = ldy[k];
+        }
+    }
+    pre_stream_load(a, tu + 2 * kPSTok, x.te, tid, x.colq, ld);
+    if (kDy) {
+        pre_stream_load_dy(a, tu + 2 * kPSTok, x.te, tid, x.colq, ldy);
+    }
     // records are per 64-token tile; t0 is a multiple of 32, so these are entries
-    // (t0 & 63) .. + 31 of tile t0 >> 6.  Every thread issues the same stores (the sum
-    // of squares from threads 0..31; the others' offset is past the view: dropped).
-    const uint32_t rec0 = (uint32_t)((((size_t)(tu >> 6) * x.S + x.slice) * (kRec * kPTok) + (tu & (kPTok - 1))) * 4);
+    // (t0 & 63) .. + 31 of tile t0 >> 6.  Every thread issues the same stores (a lane
+    // with nothing to store gets an offset past the view: the store is dropped).
+    constexpr int nrec = kDy ? kRecDy : kRec;
+    const uint32_t rec0 = (uint32_t)((((size_t)(tu >> 6) * x.S + x.slice) * (nrec * kPTok) + (tu & (kPTok - 1))) * 4);
     const int tok = tid & (kPSTok - 1);
 #pragma unroll
     for (int j = 0; j < kMix / (kPBlock / kPSTok); ++j) {
@@ -447,11 +507,24 @@ __device__ __forceinline__ void pre_stream_step(const ProjStreamArgs &a, const P
     }
     const uint32_t sqo = tid < kPSTok ? rec0 + (uint32_t)(kFSq * kPTok + tok) * 4u : 0x80000000u;
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), x.vrec, (int)sqo, 0, 0);
+    if (kDy) {
+        // <dy, res_i> of the slice: threads 0..127 take stream tid >> 5 of token tok
+        const int i = (tid >> 5) & (kHC - 1);
+        float u = red[0][tok][kMix + i];
+#pragma unroll
+        for (int ww = 1; ww < kPWaves; ++ww) {
+            u += red[ww][tok][kMix + i];
+        }
+        const uint32_t o = tid < kHC * kPSTok ? rec0 + (uint32_t)((kFDy + i) * kPTok + tok) * 4u : 0x80000000u;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(u), x.vrec, (int)o, 0, 0);
+    }
 }
 
+template <bool kDy>
 __global__ __launch_bounds__(kPBlock, 2) void pre_proj_stream_kernel(ProjStreamArgs a)
 {
     __shared__ __attribute__((aligned(16))) unsigned char tile[kPSRows * kPSRowB];
+    __shared__ __attribute__((aligned(16))) unsigned char dyt[kDy ? kPSTok * kPSRowB : 16];
     __shared__ float red[kPWaves][kPSTok][kPSRedStride];
     __shared__ float sqp[kPWaves][kPSTok][4];
 
@@ -486,25 +559,31 @@ __global__ __launch_bounds__(kPBlock, 2) void pre_proj_stream_kernel(ProjStreamA
         }
     }
 
-    // step t0's streams in the tile; steps t0 + 32 and t0 + 64 in flight in two register sets
-    u32x4 lda[kPSLoads], ldb[kPSLoads];
+    // step t0 in the tiles, step t0 + 32 in flight in registers
+    u32x4 ld[kPSLoads], ldy[kPSDyLoads];
     if (tb >= x.te) {
         return;
     }
-    pre_stream_load(a, uniform(tb), x.te, x.tid, x.colq, lda);
+    pre_stream_load(a, uniform(tb), x.te, x.tid, x.colq, ld);
+    if (kDy) {
+        pre_stream_load_dy(a, uniform(tb), x.te, x.tid, x.colq, ldy);
+    }
 #pragma unroll
     for (int k = 0; k < kPSLoads; ++k) {
-        *reinterpret_cast<u32x4 *>(tile + pstile_at((x.tid >> 4) + 16 * k, x.tid & 15)) = lda[k];
+        *reinterpret_cast<u32x4 *>(tile + pstile_at((x.tid >> 4) + 16 * k, x.tid & 15)) = ld[k];
     }
-    pre_stream_load(a, uniform(tb + kPSTok), x.te, x.tid, x.colq, lda);
-    pre_stream_load(a, uniform(tb + 2 * kPSTok), x.te, x.tid, x.colq, ldb);
-    for (int t0 = tb; t0 < x.te; t0 += 2 * kPSTok) {
-        const int tu = uniform(t0);
-        pre_stream_step(a, x, tu, tile, red, sqp, b0, b1, lda);
-        if (tu + kPSTok >= x.te) {
-            break;
+    if (kDy) {
+#pragma unroll
+        for (int k = 0; k < kPSDyLoads; ++k) {
+            *reinterpret_cast<u32x4 *>(dyt + psdy_at((x.tid >> 4) + 16 * k, x.tid & 15)) = ldy[k];
         }
-        pre_stream_step(a, x, tu + kPSTok, tile, red, sqp, b0, b1, ldb);
+    }
+    pre_stream_load(a, uniform(tb + kPSTok), x.te, x.tid, x.colq, ld);
+    if (kDy) {
+        pre_stream_load_dy(a, uniform(tb + kPSTok), x.te, x.tid, x.colq, ldy);
+    }
+    for (int t0 = tb; t0 < x.te; t0 += kPSTok) {
+        pre_stream_step<kDy>(a, x, uniform(t0), tile, dyt, red, sqp, b0, b1, ld, ldy);
     }
 }
 
@@ -522,29 +601,29 @@ static void pre_stream_ranges(int Tc, int S, int &ranges, int &tok_per_range)
 // field): thread (token, slice group k) adds slices k, k+4, ... (independent
 // loads in flight), then the four group sums are added in a fixed order.
 constexpr int kSumStride = 32; // floats per token in the sums array (25 used)
-__global__ __launch_bounds__(256) void pre_mixsum_kernel(const float *__restrict__ rec, int T, int S,
+__global__ __launch_bounds__(256) void pre_mixsum_kernel(const float *__restrict__ rec, int T, int S, int nrec,
                                                          float *__restrict__ sums)
 {
     __shared__ float part[4][kPTok];
-    const int tile = blockIdx.x / kRec;
-    const int f = blockIdx.x - tile * kRec;
+    const int tile = blockIdx.x / nrec;
+    const int f = blockIdx.x - tile * nrec;
     const int tok = threadIdx.x & (kPTok - 1);
     const int k = threadIdx.x >> 6;
-    const float *src = rec + (size_t)tile * S * (kRec * kPTok) + f * kPTok + tok;
+    const float *src = rec + (size_t)tile * S * (nrec * kPTok) + f * kPTok + tok;
     float v = 0.0f;
     int s = k;
     for (; s + 12 < S; s += 16) {
-        const float e0 = src[(size_t)s * (kRec * kPTok)];
-        const float e1 = src[(size_t)(s + 4) * (kRec * kPTok)];
-        const float e2 = src[(size_t)(s + 8) * (kRec * kPTok)];
-        const float e3 = src[(size_t)(s + 12) * (kRec * kPTok)];
+        const float e0 = src[(size_t)s * (nrec * kPTok)];
+        const float e1 = src[(size_t)(s + 4) * (nrec * kPTok)];
+        const float e2 = src[(size_t)(s + 8) * (nrec * kPTok)];
+        const float e3 = src[(size_t)(s + 12) * (nrec * kPTok)];
         v += e0;
         v += e1;
         v += e2;
         v += e3;
     }
     for (; s < S; s += 4) {
-        v += src[(size_t)s * (kRec * kPTok)];
+        v += src[(size_t)s * (nrec * kPTok)];
     }
     part[k][tok] = v;
     __syncthreads();
@@ -688,18 +767,19 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 } // namespace
 
-PreGeom pre_geometry(int64_t T, int64_t H)
+PreGeom pre_geometry(int64_t T, int64_t H, bool with_dy)
 {
     PreGeom g{};
     g.T = T;
     g.H = H;
+    g.nrec = with_dy ? kRecDy : kRec;
     if (T <= 0 || H <= 0) {
         return g;
     }
     g.nhb = (int)((H + kPHB - 1) / kPHB);
     g.slices = (int)((H + kPSliceH - 1) / kPSliceH);
     const int64_t tiles_total = (T + kPTok - 1) / kPTok;
-    const size_t rec_per_tile = (size_t)g.slices * kRec * kPTok * sizeof(float);
+    const size_t rec_per_tile = (size_t)g.slices * g.nrec * kPTok * sizeof(float);
     int64_t max_tiles = (int64_t)(((size_t)1 << 31) / rec_per_tile);
     if (max_tiles < 1) {
         max_tiles = 1;
@@ -727,9 +807,12 @@ hipError_t launch_pre_split(const float *hc_fn, const PreGeom &g, void *workspac
     return hipGetLastError();
 }
 
-hipError_t launch_pre_sums(const uint16_t *res, const PreGeom &g, int64_t c0, int Tc, void *workspace,
-                           hipStream_t stream, bool vec8)
+hipError_t launch_pre_sums(const uint16_t *res, const uint16_t *dy, const PreGeom &g, int64_t c0, int Tc,
+                           void *workspace, hipStream_t stream, bool vec8)
 {
+    if (dy != nullptr && (!vec8 || g.nrec != kRecDy)) {
+        return hipErrorInvalidValue;
+    }
     char *ws = reinterpret_cast<char *>(workspace);
     const int H = (int)g.H;
     const int tiles = (Tc + kPTok - 1) / kPTok;
@@ -744,6 +827,7 @@ hipError_t launch_pre_sums(const uint16_t *res, const PreGeom &g, int64_t c0, in
     if (vec8) {
         ProjStreamArgs sa{};
         sa.res = a.res;
+        sa.dy = dy != nullptr ? dy + (size_t)c0 * H : nullptr;
         sa.frag = a.frag;
         sa.T = a.T;
         sa.H = H;
@@ -753,7 +837,12 @@ hipError_t launch_pre_sums(const uint16_t *res, const PreGeom &g, int64_t c0, in
         sa.rec_bytes = (uint32_t)g.rec_bytes;
         int ranges = 1;
         pre_stream_ranges(a.T, g.slices, ranges, sa.tok_per_range);
-        pre_proj_stream_kernel<<<dim3((unsigned)g.slices, (unsigned)ranges), dim3(kPBlock), 0, stream>>>(sa);
+        const dim3 sgrid((unsigned)g.slices, (unsigned)ranges);
+        if (dy != nullptr) {
+            pre_proj_stream_kernel<true><<<sgrid, dim3(kPBlock), 0, stream>>>(sa);
+        } else {
+            pre_proj_stream_kernel<false><<<sgrid, dim3(kPBlock), 0, stream>>>(sa);
+        }
     } else {
         pre_proj_kernel<<<dim3((unsigned)tiles, (unsigned)g.slices), dim3(kPBlock), 0, stream>>>(a);
     }
@@ -761,8 +850,8 @@ hipError_t launch_pre_sums(const uint16_t *res, const PreGeom &g, int64_t c0, in
     if (e != hipSuccess) {
         return e;
     }
-    pre_mixsum_kernel<<<dim3((unsigned)(tiles * kRec)), dim3(256), 0, stream>>>(
-        a.rec, Tc, g.slices, reinterpret_cast<float *>(ws + g.off_prew));
+    pre_mixsum_kernel<<<dim3((unsigned)(tiles * g.nrec)), dim3(256), 0, stream>>>(
+        a.rec, Tc, g.slices, g.nrec, reinterpret_cast<float *>(ws + g.off_prew));
     return hipGetLastError();
 }
 
@@ -812,7 +901,7 @@ hipError_t launch_pre(const uint16_t *res, const void *hc_fn, bool fn_bf16, int 
             sa.rec_bytes = (uint32_t)g.rec_bytes;
             int ranges = 1;
             pre_stream_ranges(a.T, g.slices, ranges, sa.tok_per_range);
-            pre_proj_stream_kernel<<<dim3((unsigned)g.slices, (unsigned)ranges), dim3(kPBlock), 0, stream>>>(sa);
+            pre_proj_stream_kernel<false><<<dim3((unsigned)g.slices, (unsigned)ranges), dim3(kPBlock), 0, stream>>>(sa);
         } else {
             pre_proj_kernel<<<dim3((unsigned)tiles, (unsigned)g.slices), dim3(kPBlock), 0, stream>>>(a);
         }
@@ -820,7 +909,8 @@ hipError_t launch_pre(const uint16_t *res, const void *hc_fn, bool fn_bf16, int 
         if (e != hipSuccess) {
             return e;
         }
-        pre_mixsum_kernel<<<dim3((unsigned)(tiles * kRec)), dim3(256), 0, stream>>>(a.rec, Tc, g.slices, sums);
+        pre_mixsum_kernel<<<dim3((unsigned)(tiles * g.nrec)), dim3(256), 0, stream>>>(a.rec, Tc, g.slices, g.nrec,
+                                                                                    sums);
         e = hipGetLastError();
         if (e != hipSuccess) {
             return e;
