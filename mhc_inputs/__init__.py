@@ -80,6 +80,15 @@ def device_normal_bf16(seed: int, cfg: int, tensor: str, shape, device="cuda", s
     return (torch.randn(shape, generator=g, device=device, dtype=torch.float32) * std).to(torch.bfloat16)
 
 
+def device_normal_f32(seed: int, cfg: int, tensor: str, shape, device="cuda", std: float = 1.0):
+    """A large seeded fp32 tensor drawn directly on the device (torch's generator), as
+    device_normal_bf16 without the rounding."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed((seed * 1_000_003 + cfg) * 1_000_003 + _TID[tensor])
+    return torch.randn(shape, generator=g, device=device, dtype=torch.float32) * std
+
+
 def normal_bf16(seed: int, cfg: int, tensor: str, shape, std: float = 1.0) -> np.ndarray:
     return f32_to_bf16_bits(normal_f32(seed, cfg, tensor, shape, std))
 

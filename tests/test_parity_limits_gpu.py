@@ -1,11 +1,12 @@
 """GPU parity at the size limits: the pre-map's token chunking (a batch whose partial
-sums pass 2^31 bytes is processed in chunks) and the largest accepted hidden size.
+sums pass 2^31 bytes is processed in chunks, in the forward and in the reverse's
+recompute) and the largest accepted hidden size.
 Sampled tokens against the fp64 oracle, with the tolerances of the other parity tests."""
 import numpy as np
 import pytest
 
 import oracle
-from mhc_inputs import HC, MIX, device_normal_bf16, normal_f32, post_inputs
+from mhc_inputs import HC, MIX, device_normal_bf16, device_normal_f32, normal_f32, post_inputs
 from tests._helpers import assert_bf16_close, assert_f32_close, bits_of, f32_of, to_dev_bf16, to_dev_f32
 
 pytestmark = pytest.mark.gpu
@@ -59,6 +60,35 @@ def test_pre_token_chunking():
     _check_pre(_bits_rows(res, rows), hc_fn, hc_scale, hc_base, _bits_rows(y, rows),
                f32_of(post[torch.as_tensor(rows, device="cuda")]), f32_of(comb[torch.as_tensor(rows, device="cuda")]),
                f"pre chunked T={T}")
+
+
+def test_pre_fused_backward_token_chunking():
+    """The reverse's recompute keeps 29 fields per record (the 25 of the forward and the
+    four <dy, res_i>): at H = 8 that is 7424 bytes per 64-token tile, so the recompute and
+    the per-token reverse run in chunks of floor(2^31 / 7424) tiles, and T runs 3000
+    tokens into a second, ragged chunk.  A token's d_res depends on its own inputs only,
+    so sampled rows are checked against the oracle run on those rows alone (the sums
+    over tokens are covered by the smaller parity tests)."""
+    mhc = _mhc()
+    H = 8
+    chunk = (2 ** 31 // (1 * 29 * 64 * 4)) * 64
+    T = chunk + 3000
+    res = device_normal_bf16(0, 620, "res", (T, HC, H))
+    dy = device_normal_bf16(0, 620, "dy", (T, H))
+    d_post = device_normal_f32(0, 620, "d_post", (T, HC))
+    d_comb = device_normal_f32(0, 620, "d_comb", (T, HC, HC))
+    hc_fn = normal_f32(0, 620, "hc_fn", (MIX, HC * H), 0.02)
+    hc_scale = np.ones(3, np.float32)
+    hc_base = normal_f32(0, 620, "hc_base", (MIX,), 0.1)
+    out = mhc.mhc_pre_fused_backward(dy, d_post, d_comb, res, to_dev_f32(hc_fn), to_dev_f32(hc_scale),
+                                     to_dev_f32(hc_base))
+    torch.cuda.synchronize()
+    rows = sorted({0, 1, 31, 32, 63, 64, chunk - 65, chunk - 33, chunk - 1, chunk, chunk + 1, chunk + 31, chunk + 32,
+                   chunk + 2999, T // 2, 12345678})
+    idx = torch.as_tensor(rows, device="cuda")
+    ref = oracle.pre_backward(_bits_rows(dy, rows), f32_of(d_post[idx]), f32_of(d_comb[idx]), _bits_rows(res, rows),
+                              hc_fn, hc_scale, hc_base)
+    assert_bf16_close(_bits_rows(out["d_res"], rows), ref["d_res"], f"pre_fused backward chunked T={T} d_res")
 
 
 @pytest.mark.parametrize("fn", ["pre_fused", "pre_from_dots", "post"])
