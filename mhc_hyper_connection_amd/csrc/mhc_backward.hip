@@ -315,77 +315,97 @@ __global__ __launch_bounds__(kDBBlock) void pre_dots_bwd_kernel(DotsBwdArgs a)
     }
 }
 
-// The whole pre-map's per-token reverse.  One 64-thread workgroup per token, after the
-// projection's recompute left the token's fields in `sums` ([T][32]: pre dots 0..3, S
-// at 4, post dots 5..8, comb dots 9..24, <dy, res_i> at 25..28).  The chain is that of
-// pre_dots_bwd_kernel's wavefront 0 with S taken from the streams (the RMS term of
-// d_res applies); it writes pre and 2 dS, the dot gradients as bf16 hi + lo halves
-// (row-major and transposed) for the projection's reverse, and the token's row of the
-// d_hc_scale / d_hc_base sums.  No stream is read here.
+// The whole pre-map's per-token reverse, after the projection's recompute left each
+// token's fields in `sums` ([T][32]: pre dots 0..3, S at 4, post dots 5..8, comb dots
+// 9..24, <dy, res_i> at 25..28).  The chain is that of pre_dots_bwd_kernel's wavefront
+// 0 with S taken from the streams (the RMS term of d_res applies).  Four tokens per
+// wavefront, one per 16-lane row: lane e of a row takes comb entry e (its Sinkhorn
+// reverse on the row), and lanes e < 4 also pre_e and post_e; sums over a token's mixes
+// are DPP sums over its row.  It writes pre and 2 dS, the dot gradients as bf16 hi + lo
+// halves (row-major and transposed) for the projection's reverse, and the token's row
+// of the d_hc_scale / d_hc_base sums.  No stream is read here.
 constexpr int kSumsDy = kMix + 1; // first <dy, res_i> field in the sums
+
+// Sum over the 16 lanes of a DPP row (every lane gets it): quads, then across them.
+__device__ __forceinline__ float row16_sum(float v) { return col_sum4(row_sum4(v)); }
+
+__device__ __forceinline__ void put_dd(const DotsBwdArgs &a, int t, int col, float v)
+{
+    const uint16_t hi = f32_to_bf16(v);
+    const uint16_t lo = f32_to_bf16(v - bf16_to_f32(hi));
+    a.dd_hi[(size_t)t * 32 + col] = hi;
+    a.dd_lo[(size_t)t * 32 + col] = lo;
+    a.ddT_hi[(size_t)col * a.ldT + t] = hi;
+    a.ddT_lo[(size_t)col * a.ldT + t] = lo;
+}
+
 __global__ __launch_bounds__(kWave) void pre_tok_bwd_kernel(DotsBwdArgs a)
 {
     extern __shared__ float hist[]; // [iters + 1][64]: the Sinkhorn history
-    const int t = blockIdx.x;
     const int lane = threadIdx.x;
+    const int e = lane & 15;
+    const int t_row = blockIdx.x * 4 + (lane >> 4);
+    const bool live = t_row < a.T; // uniform within each row
+    const int t = live ? t_row : a.T - 1;
     const float *sm = a.sums + (size_t)t * 32;
     const float rstd = 1.0f / sqrtf(sm[kHC] / a.k + a.rms_eps);
-    // comb: Sinkhorn reverse mode, entry e = lane & 15 on every 16-lane row (each row
-    // computes the same matrix); lane 8 + e then takes entry e from lane e
-    const int e = lane & 15;
-    const float Lc = fmaf(sm[sums_field(2 * kHC + e)] * rstd, a.hc_scale[2], a.hc_base[2 * kHC + e]);
+    const float s0 = a.hc_scale[0], s1 = a.hc_scale[1], s2 = a.hc_scale[2];
+    // comb entry e (mix 8 + e)
+    const float dc = sm[sums_field(2 * kHC + e)];
+    const float mc = dc * rstd;
+    const float Lc = fmaf(mc, s2, a.hc_base[2 * kHC + e]);
     const float Gc = a.d_comb[(size_t)t * kHC * kHC + e];
-    const float dLc = sinkhorn_row16_backward(Lc, Gc, a.iters, a.sk_eps, hist + lane);
-    const float dLmine = __shfl(dLc, (lane - 2 * kHC) & 15);
-    // lanes 0..23: one mix each
-    const int grp = lane < kHC ? 0 : (lane < 2 * kHC ? 1 : 2);
-    float dz = 0.0f, m = 0.0f, dm = 0.0f, d = 0.0f, pw = 0.0f;
-    if (lane < kMix) {
-        d = sm[sums_field(lane)];
-        m = d * rstd;
-        if (lane < 2 * kHC) {
-            const float sg = sigmoidf_fast(fmaf(m, a.hc_scale[grp], a.hc_base[lane]));
-            if (lane < kHC) {
-                dz = sm[kSumsDy + lane] * sg * (1.0f - sg);
-                pw = sg + a.pre_eps;
-            } else {
-                dz = a.d_post[(size_t)t * kHC + lane - kHC] * a.post_mult * sg * (1.0f - sg);
-            }
-        } else {
-            dz = dLmine;
+    const float dzc = sinkhorn_row16_backward(Lc, Gc, a.iters, a.sk_eps, hist + lane);
+    const float dmc = dzc * s2;
+    // pre_e and post_e on lanes e < 4
+    float dzp = 0.0f, mp = 0.0f, dmp = 0.0f, dp = 0.0f, pw = 0.0f;
+    float dzq = 0.0f, mq = 0.0f, dmq = 0.0f, dq = 0.0f;
+    const int eq = e & (kHC - 1);
+    {
+        dp = sm[sums_field(eq)];
+        mp = dp * rstd;
+        const float sg = sigmoidf_fast(fmaf(mp, s0, a.hc_base[eq]));
+        dzp = sm[kSumsDy + eq] * sg * (1.0f - sg);
+        pw = sg + a.pre_eps;
+        dq = sm[sums_field(kHC + eq)];
+        mq = dq * rstd;
+        const float sq = sigmoidf_fast(fmaf(mq, s1, a.hc_base[kHC + eq]));
+        dzq = a.d_post[(size_t)t * kHC + eq] * a.post_mult * sq * (1.0f - sq);
+        if (e >= kHC) {
+            dzp = 0.0f;
+            dzq = 0.0f;
         }
-        dm = dz * a.hc_scale[grp];
+        dmp = dzp * s0;
+        dmq = dzq * s1;
     }
-    if (lane < 32) {
-        // d_dot as bf16 hi + lo (the lo half carries the rounding error of the hi)
-        const float v = lane < kMix ? dm * rstd : 0.0f;
-        const uint16_t hi = f32_to_bf16(v);
-        const uint16_t lo = f32_to_bf16(v - bf16_to_f32(hi));
-        a.dd_hi[(size_t)t * 32 + lane] = hi;
-        a.dd_lo[(size_t)t * 32 + lane] = lo;
-        a.ddT_hi[(size_t)lane * a.ldT + t] = hi;
-        a.ddT_lo[(size_t)lane * a.ldT + t] = lo;
-    }
-    const float d_rstd = wave_sum(dm * d);
+    // d_rstd = sum over the 24 mixes of dm * dot; the group sums of dz * m
+    const float d_rstd = row16_sum(dmc * dc + (dmp * dp + dmq * dq));
+    const float g0 = row16_sum(dzp * mp);
+    const float g1 = row16_sum(dzq * mq);
+    const float g2 = row16_sum(dzc * mc);
     const float dS = -d_rstd * rstd * rstd * rstd / (2.0f * a.k);
-    float *wrow = a.ws + (size_t)t * kWsRow;
-    const float zm = dz * m;
-    // per-group sums of dz * m over lanes 0..3, 4..7 and 8..23 (fixed order)
-    const float g0 = wave_sum(lane < kHC ? zm : 0.0f);
-    const float g1 = wave_sum(lane >= kHC && lane < 2 * kHC ? zm : 0.0f);
-    const float g2 = wave_sum(lane >= 2 * kHC && lane < kMix ? zm : 0.0f);
-    if (lane < kMix) {
-        wrow[lane] = dz;
+    if (!live) {
+        return;
     }
-    if (lane == 0) {
+    put_dd(a, t, 2 * kHC + e, dmc * rstd);
+    float *wrow = a.ws + (size_t)t * kWsRow;
+    wrow[2 * kHC + e] = dzc;
+    if (e < kHC) {
+        put_dd(a, t, e, dmp * rstd);
+        put_dd(a, t, kHC + e, dmq * rstd);
+        wrow[e] = dzp;
+        wrow[kHC + e] = dzq;
+        a.tok[(size_t)t * 8 + e] = pw;
+    } else if (e < 2 * kHC) {
+        a.tok[(size_t)t * 8 + e] = e == kHC ? 2.0f * dS : 0.0f;
+    } else {
+        put_dd(a, t, kMix + e - 2 * kHC, 0.0f); // d_dot rows 24..31 of the MFMA tiles: zero
+    }
+    if (e == 0) {
         wrow[kMix] = g0;
         wrow[kMix + 1] = g1;
         wrow[kMix + 2] = g2;
         wrow[kMix + 3] = 0.0f;
-    }
-    if (lane < 8) {
-        // pre weights (lanes 0..3), then 2 dS, then padding
-        a.tok[(size_t)t * 8 + lane] = lane < kHC ? pw : (lane == kHC ? 2.0f * dS : 0.0f);
     }
 }
 
@@ -1161,7 +1181,7 @@ hipError_t launch_pre_fused_bwd(const uint16_t *dy, const float *d_post, const f
         a.ddT_lo = ddTl + c0;
         a.ldT = L.ldT;
         const size_t lds = (size_t)(iters + 1) * kWave * sizeof(float);
-        pre_tok_bwd_kernel<<<dim3((unsigned)Tc), dim3(kWave), lds, stream>>>(a);
+        pre_tok_bwd_kernel<<<dim3((unsigned)((Tc + 3) / 4)), dim3(kWave), lds, stream>>>(a);
         e = hipGetLastError();
         if (e != hipSuccess) {
             return e;
