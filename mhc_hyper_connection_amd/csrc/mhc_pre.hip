@@ -306,6 +306,12 @@ constexpr int kPSTargetBlocks = 512;             // one round of two workgroups 
 // lanes (g, c) at token 4g + k, column c lands on 64 distinct banks, and the reduction's
 // reads of 32 tokens of one column meet at most two to a bank.
 constexpr int kPSRedStride = 36;
+// With <dy, res_i> each lane also leaves its 4 lane-group partials (columns 24 + 4i + g):
+// 44 = 12 (mod 16) keeps those writes, the dot writes and the reads as conflict-free.
+constexpr int kPSRedStrideDy = 44;
+template <bool kDy> struct PSRed {
+    static constexpr int stride = kDy ? kPSRedStrideDy : kPSRedStride;
+};
 
 struct ProjStreamArgs {
     const uint16_t *res;
@@ -376,7 +382,7 @@ struct PreStreamCtx {
 template <bool kDy>
 __device__ __forceinline__ void pre_stream_step(const ProjStreamArgs &a, const PreStreamCtx &x, int tu,
                                                 unsigned char *tile, unsigned char *dyt,
-                                                float (*red)[kPSTok][kPSRedStride], float (*sqp)[kPSTok][4],
+                                                float (*red)[kPSTok][PSRed<kDy>::stride], float (*sqp)[kPSTok][4],
                                                 const u32x4 (&b0)[kHC][3], const u32x4 (&b1)[kHC][3],
                                                 u32x4 (&ld)[kPSLoads], u32x4 (&ldy)[kPSDyLoads])
 {
@@ -452,15 +458,11 @@ __device__ __forceinline__ void pre_stream_step(const ProjStreamArgs &a, const P
         }
         sqp[w][m * 16 + c][g] = sq[m];
         if (kDy) {
-            // over the 4 lane groups of token m*16 + c: (g0 + g1) + (g2 + g3), every lane
+            // this lane's partial of token m*16 + c over its 8 h; the 4 lane groups are
+            // summed with the 4 waves below
 #pragma unroll
             for (int i = 0; i < kHC; ++i) {
-                float v = pd[m][i];
-                v += __shfl_xor(v, 16);
-                v += __shfl_xor(v, 32);
-                if (g == 0) {
-                    red[w][m * 16 + c][kMix + i] = v;
-                }
+                red[w][m * 16 + c][kMix + 4 * i + g] = pd[m][i];
             }
         }
     }
@@ -508,12 +510,16 @@ __device__ __forceinline__ void pre_stream_step(const ProjStreamArgs &a, const P
     const uint32_t sqo = tid < kPSTok ? rec0 + (uint32_t)(kFSq * kPTok + tok) * 4u : 0x80000000u;
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), x.vrec, (int)sqo, 0, 0);
     if (kDy) {
-        // <dy, res_i> of the slice: threads 0..127 take stream tid >> 5 of token tok
+        // <dy, res_i> of the slice: threads 0..127 take stream tid >> 5 of token tok,
+        // summing wave by wave, lane group by lane group
         const int i = (tid >> 5) & (kHC - 1);
-        float u = red[0][tok][kMix + i];
+        float u = 0.0f;
 #pragma unroll
-        for (int ww = 1; ww < kPWaves; ++ww) {
-            u += red[ww][tok][kMix + i];
+        for (int ww = 0; ww < kPWaves; ++ww) {
+#pragma unroll
+            for (int gg = 0; gg < 4; ++gg) {
+                u += red[ww][tok][kMix + 4 * i + gg];
+            }
         }
         const uint32_t o = tid < kHC * kPSTok ? rec0 + (uint32_t)((kFDy + i) * kPTok + tok) * 4u : 0x80000000u;
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(u), x.vrec, (int)o, 0, 0);
@@ -525,7 +531,7 @@ __global__ __launch_bounds__(kPBlock, 2) void pre_proj_stream_kernel(ProjStreamA
 {
     __shared__ __attribute__((aligned(16))) unsigned char tile[kPSRows * kPSRowB];
     __shared__ __attribute__((aligned(16))) unsigned char dyt[kDy ? kPSTok * kPSRowB : 16];
-    __shared__ float red[kPWaves][kPSTok][kPSRedStride];
+    __shared__ float red[kPWaves][kPSTok][PSRed<kDy>::stride];
     __shared__ float sqp[kPWaves][kPSTok][4];
 
     PreStreamCtx x;
