@@ -54,6 +54,9 @@ def parse():
                              "pre_bf16", "expand", "head", "head_mean", "pre_bwd"],
                     help="run only one call in the timed loop (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flush-mb", type=int, default=-1,
+                    help="overwrite a buffer of this many MiB before every timed rep (0: never); by default 512 "
+                         "when a step moves less than 512 MB, so no rep starts with its data in the caches")
     ap.add_argument("--graph", action="store_true",
                     help="time the steps as replays of one captured HIP graph (no host launch cost)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -244,6 +247,25 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / n
 
+    flush_buf = None
+
+    def timed_reps(fn, n):
+        """As timed(), or with the flush buffer overwritten before each rep (HIP events
+        around each rep only; the flush is not counted)."""
+        if flush_buf is None:
+            return timed(fn, n)
+        torch.cuda.synchronize()
+        evs = []
+        for _ in range(n):
+            flush_buf.fill_(1)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs) / n
+
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
@@ -267,18 +289,24 @@ def main():
             run_step()
         torch.cuda.synchronize()
 
-    print(f"[bench] timing {args.steps} steps{' (graph replays)' if args.graph else ''}", file=sys.stderr, flush=True)
-    t0 = time.perf_counter()
-    ms_step = timed(run_step, args.steps)
-    wall = time.perf_counter() - t0
-
     pre_b = algorithmic_bytes_pre(T, H)
     post_b = algorithmic_bytes_post(T, H)
+    step_bytes = step_algorithmic_bytes(args.only, T, H, sk_logits)
+    flush_mb = args.flush_mb if args.flush_mb >= 0 else (512 if step_bytes < 512 * 10 ** 6 else 0)
+    if flush_mb > 0:
+        flush_buf = torch.empty(flush_mb << 18, dtype=torch.float32, device=dev)
+
+    print(f"[bench] timing {args.steps} steps{' (graph replays)' if args.graph else ''}"
+          f"{f', {flush_mb} MiB flushed before each' if flush_mb else ''}", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    ms_step = timed_reps(run_step, args.steps)
+    wall = time.perf_counter() - t0
+
     breakdown = {}
     if args.only in ("all", "pre"):
-        breakdown["pre_ms"] = timed(call_pre, max(args.steps, 1))
+        breakdown["pre_ms"] = timed_reps(call_pre, max(args.steps, 1))
     if args.only in ("all", "post"):
-        breakdown["post_ms"] = timed(call_post, max(args.steps, 1))
+        breakdown["post_ms"] = timed_reps(call_post, max(args.steps, 1))
     if args.only == "sinkhorn":
         breakdown["sinkhorn_ms"] = ms_step
     if args.only == "pre_dots":
@@ -293,28 +321,6 @@ def main():
         if args.only == mode:
             breakdown[mode + "_ms"] = ms_step
 
-    if args.only == "sinkhorn":
-        step_bytes = algorithmic_bytes_sinkhorn(sk_logits.shape[0])
-    elif args.only == "sinkhorn_bwd":
-        step_bytes = algorithmic_bytes_sinkhorn_backward(sk_logits.shape[0])
-    elif args.only == "post_bwd":
-        step_bytes = algorithmic_bytes_post_backward(T, H)
-    elif args.only == "pre_dots_bwd":
-        step_bytes = algorithmic_bytes_pre_dots_backward(T, H)
-    elif args.only == "pre_bf16":
-        step_bytes = algorithmic_bytes_pre_bf16(T, H)
-    elif args.only == "expand":
-        step_bytes = algorithmic_bytes_expand(T, H)
-    elif args.only == "head":
-        step_bytes = algorithmic_bytes_head(T, H)
-    elif args.only == "head_mean":
-        step_bytes = algorithmic_bytes_head_mean(T, H)
-    elif args.only == "pre_bwd":
-        step_bytes = algorithmic_bytes_pre_backward(T, H)
-    elif args.only == "pre_dots":
-        step_bytes = algorithmic_bytes_pre_dots(T, H)
-    else:
-        step_bytes = (pre_b if args.only in ("all", "pre") else 0) + (post_b if args.only in ("all", "post") else 0)
     eff_gbps = step_bytes / (ms_step * 1e-3) / 1e9
 
     # Per-call rooflines.  mhc_post and mhc_sinkhorn are one kernel launch each;
@@ -378,6 +384,25 @@ def main():
                     "valu_instructions": instr, "hbm": {"achieved": d["achieved"], "peak": HBM_PEAK_GBPS,
                                                         "unit": "GB/s"}}
 
+    # Sanity figures: the launch floor of the step's kernel count (one-element fills,
+    # launched the same way), and what a plain elementwise copy sustains here.
+    nker = {"all": 5, "pre": 4, "post": 1}.get(args.only)
+    launch_floor_ms = None
+    if nker:
+        one = torch.zeros(1, device=dev)
+
+        def floor_step():
+            for _ in range(nker):
+                one.fill_(0.0)
+        launch_floor_ms = timed(floor_step, max(args.steps, 1))
+    nc = 1 << 29
+    csrc = torch.empty(nc, dtype=torch.bfloat16, device=dev).normal_()
+    cdst = torch.empty_like(csrc)
+    torch.neg(csrc, out=cdst)  # the first call loads the kernel
+    ms_c = timed(lambda: torch.neg(csrc, out=cdst), 10)
+    copy_gbps = round(4 * nc / (ms_c * 1e-3) / 1e9, 1)
+    del csrc, cdst
+
     copy_cal = None
     if args.copy_calibration:
         # A plain elementwise kernel of known size (reads 1 GiB, writes 1 GiB): the
@@ -385,6 +410,7 @@ def main():
         n = 1 << 29
         src = torch.empty(n, dtype=torch.bfloat16, device=dev).normal_()
         dst = torch.empty_like(src)
+        torch.neg(src, out=dst)  # the first call loads the kernel
         ms_copy = timed(lambda: torch.neg(src, out=dst), 5)
         copy_cal = {"kernel": "torch.neg (bf16, 2^29 elements)", "bytes_read": 2 * n, "bytes_written": 2 * n,
                     "ms": round(ms_copy, 4), "GBps": round(4 * n / (ms_copy * 1e-3) / 1e9, 1)}
@@ -409,6 +435,7 @@ def main():
         "config": {"workload": (f"mhc {args.only} 2^20 4x4 matrices" if args.only.startswith("sinkhorn") else
                                 f"mhc {args.only if args.only != 'all' else 'pre+post'} T={T} H={H} HC=4"),
                    "launch": "HIP graph replay" if args.graph else "eager",
+                   "cache_flush_mib": flush_mb,
                    "T": T, "H": H, "hc": 4, "num_iters": p["num_iters"], "inputs": "resident in HBM"},
         "effective_GBps": round(eff_gbps, 1),
         "hbm_frac": round(eff_gbps / HBM_PEAK_GBPS, 4),
@@ -417,6 +444,9 @@ def main():
         "roofline": roofline,
         "calls": per_call,
         "cpu_baseline": cpu,
+        "launch_floor_ms": None if launch_floor_ms is None else round(launch_floor_ms, 5),
+        "kernels_per_step": nker,
+        "copy_GBps": copy_gbps,
         "wall_s_timed": round(wall, 3),
     }
     if copy_cal:
@@ -442,6 +472,31 @@ def sources_digest() -> str:
 
 def traffic_path(T: int, H: int) -> str:
     return os.path.join(PROFILES, f"hbm_traffic_T{T}_H{H}.json")
+
+
+def step_algorithmic_bytes(only: str, T: int, H: int, sk_logits) -> int:
+    """What one timed step must move (each tensor counted once)."""
+    from mhc_inputs import (algorithmic_bytes_expand, algorithmic_bytes_head, algorithmic_bytes_head_mean,
+                            algorithmic_bytes_post, algorithmic_bytes_post_backward, algorithmic_bytes_pre,
+                            algorithmic_bytes_pre_backward, algorithmic_bytes_pre_bf16, algorithmic_bytes_pre_dots,
+                            algorithmic_bytes_pre_dots_backward, algorithmic_bytes_sinkhorn,
+                            algorithmic_bytes_sinkhorn_backward)
+    per_mode = {
+        "sinkhorn": lambda: algorithmic_bytes_sinkhorn(sk_logits.shape[0]),
+        "sinkhorn_bwd": lambda: algorithmic_bytes_sinkhorn_backward(sk_logits.shape[0]),
+        "post_bwd": lambda: algorithmic_bytes_post_backward(T, H),
+        "pre_dots_bwd": lambda: algorithmic_bytes_pre_dots_backward(T, H),
+        "pre_bf16": lambda: algorithmic_bytes_pre_bf16(T, H),
+        "expand": lambda: algorithmic_bytes_expand(T, H),
+        "head": lambda: algorithmic_bytes_head(T, H),
+        "head_mean": lambda: algorithmic_bytes_head_mean(T, H),
+        "pre_bwd": lambda: algorithmic_bytes_pre_backward(T, H),
+        "pre_dots": lambda: algorithmic_bytes_pre_dots(T, H),
+        "pre": lambda: algorithmic_bytes_pre(T, H),
+        "post": lambda: algorithmic_bytes_post(T, H),
+        "all": lambda: algorithmic_bytes_pre(T, H) + algorithmic_bytes_post(T, H),
+    }
+    return per_mode[only]()
 
 
 def load_traffic(T: int, H: int, mode: str):
@@ -559,7 +614,20 @@ def cpu_baseline(inp, target_s: float):
         for _ in range(reps):
             list(ex.map(lambda k: run(k * chunk, (k + 1) * chunk), range(threads)))
     wall = time.perf_counter() - t0
+    # one thread, about 3 CPU-seconds
+    n1 = int(min(T, max(1, 3.0 / max(per_tok, 1e-9))))
+    t1 = time.perf_counter()
+    run(0, n1)
+    wall1 = time.perf_counter() - t1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), model)
+    except OSError:
+        pass
     return {"value": round(reps * n / wall, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "single_thread": {"value": round(n1 / wall1, 2), "unit": "tokens/s", "sample": f"{n1} tokens"},
+            "cpu_model": model, "logical_cpus": os.cpu_count(),
             "sample": (f"{reps} pass{'es' if reps > 1 else ''} over {n} of {T} tokens of the T={T} H={H} pre+post "
                        f"step, fp64 oracle, {threads} threads (about {reps * n * per_tok:.0f} CPU-seconds)"),
             "wall_s": round(wall, 2)}
