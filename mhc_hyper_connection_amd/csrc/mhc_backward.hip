@@ -1,8 +1,11 @@
-// mhc_backward.hip -- reverse mode of the Sinkhorn projection and of the post-map.
+// mhc_backward.hip -- reverse mode of the mHC path: the Sinkhorn projection, the
+// post-map, the pre-map from external dots, and the whole pre-map with its projection
+// inside (the projection's fields recomputed together with <dy, res_i>, the per-token
+// chain, then the projection's reverse products).
 //
-// (rwkv-ops mhu_jax.py: sinkhorn_knopp and mhc_post_op with their custom VJPs,
-// SinkhornBwd and MhcPostOpBwd; the forward formulas are those of the FlashInfer
-// mHC article, sections 2.1 and 5.2.)
+// (rwkv-ops mhu_jax.py: sinkhorn_knopp, mhc_pre_op and mhc_post_op with their custom
+// VJPs, SinkhornBwd, MhcPreOpBwd and MhcPostOpBwd; the forward formulas are those of the
+// FlashInfer mHC article, sections 2.1, 3.2 and 5.2.)
 #include "mhc_device.h"
 #include "mhc_internal.h"
 
