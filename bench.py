@@ -51,7 +51,7 @@ def parse():
     ap.add_argument("--workload", default="layer_h7168", choices=sorted(WORKLOADS))
     ap.add_argument("--only", default="all",
                     choices=["all", "pre", "post", "sinkhorn", "pre_dots", "post_bwd", "sinkhorn_bwd", "pre_dots_bwd",
-                             "pre_bf16", "expand", "head", "head_mean", "pre_bwd"],
+                             "pre_bf16", "expand", "head", "head_mean", "pre_bwd", "post_project", "fused"],
                     help="run only one call in the timed loop (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush-mb", type=int, default=-1,
@@ -208,6 +208,27 @@ def main():
     if args.only == "post_bwd":
         call_pre()  # the forward's mixes (untimed)
 
+    if args.only in ("post_project", "fused"):
+        # the post-map with the next sublayer's projection fused in (the next weights are
+        # hc_fn again); "fused" is the steady-state sublayer step: the pre-map from the
+        # previous post-map's partials, then the post-map updating the streams in place
+        pp_S = mhc.mhc_post_project_splits(H)
+        pp_dm = torch.empty(pp_S, T, 24, dtype=torch.float32, device=dev)
+        pp_sq = torch.empty(pp_S, T, dtype=torch.float32, device=dev)
+        pp_ws = torch.empty(mhc.mhc_post_project_workspace_bytes(H), dtype=torch.uint8, device=dev)
+        streams = res.clone()
+        call_pre()  # mixes for the first post-map (untimed)
+        mhc.mhc_post_project(x, streams, post, comb, hc_fn, out=out, dot_mix=pp_dm, sqrsum=pp_sq, workspace=pp_ws)
+
+    def call_post_project():
+        mhc.mhc_post_project(x, res, post, comb, hc_fn, out=out, dot_mix=pp_dm, sqrsum=pp_sq, workspace=pp_ws)
+
+    def call_fused():
+        mhc.mhc_pre_from_dots(pp_dm, streams, hc_scale, hc_base, pp_sq, None, p["rms_eps"], p["pre_eps"],
+                              p["sinkhorn_eps"], p["post_mult"], p["num_iters"], y=y, post=post, comb=comb)
+        mhc.mhc_post_project(x, streams, post, comb, hc_fn, out=streams, dot_mix=pp_dm, sqrsum=pp_sq,
+                             workspace=pp_ws)
+
     def step():
         if args.only in ("all", "pre"):
             call_pre()
@@ -233,6 +254,10 @@ def main():
             call_head_mean()
         if args.only == "pre_bwd":
             call_pre_bwd()
+        if args.only == "post_project":
+            call_post_project()
+        if args.only == "fused":
+            call_fused()
 
     stream = torch.cuda.current_stream(dev)
 
@@ -317,7 +342,7 @@ def main():
         breakdown["post_bwd_ms"] = ms_step
     if args.only == "pre_dots_bwd":
         breakdown["pre_dots_bwd_ms"] = ms_step
-    for mode in ("pre_bf16", "expand", "head", "head_mean", "pre_bwd"):
+    for mode in ("pre_bf16", "expand", "head", "head_mean", "pre_bwd", "post_project", "fused"):
         if args.only == mode:
             breakdown[mode + "_ms"] = ms_step
 
@@ -358,6 +383,12 @@ def main():
     if "pre_dots_bwd_ms" in breakdown:
         calls["mhc_pre_from_dots_backward"] = ("pre_dots_bwd_kernel+pre_bwd_partial_kernel+pre_bwd_final_kernel",
                                                breakdown["pre_dots_bwd_ms"], step_bytes)
+    if "post_project_ms" in breakdown:
+        calls["mhc_post_project"] = ("pre_prep_kernel+post_proj_stream_kernel", breakdown["post_project_ms"],
+                                     step_bytes)
+    if "fused_ms" in breakdown:
+        calls["mhc_pre_from_dots+mhc_post_project"] = (
+            "pre_dots_kernel+pre_prep_kernel+post_proj_stream_kernel", breakdown["fused_ms"], step_bytes)
     traffic = load_traffic(T, H, args.only)
     per_call = {}
     for name, (kern, ms_k, bytes_k) in calls.items():
@@ -386,7 +417,7 @@ def main():
 
     # Sanity figures: the launch floor of the step's kernel count (one-element fills,
     # launched the same way), and what a plain elementwise copy sustains here.
-    nker = {"all": 5, "pre": 4, "post": 1}.get(args.only)
+    nker = {"all": 5, "pre": 4, "post": 1, "post_project": 2, "fused": 3}.get(args.only)
     launch_floor_ms = None
     if nker:
         one = torch.zeros(1, device=dev)
@@ -480,8 +511,11 @@ def step_algorithmic_bytes(only: str, T: int, H: int, sk_logits) -> int:
                             algorithmic_bytes_post, algorithmic_bytes_post_backward, algorithmic_bytes_pre,
                             algorithmic_bytes_pre_backward, algorithmic_bytes_pre_bf16, algorithmic_bytes_pre_dots,
                             algorithmic_bytes_pre_dots_backward, algorithmic_bytes_sinkhorn,
-                            algorithmic_bytes_sinkhorn_backward)
+                            algorithmic_bytes_sinkhorn_backward, algorithmic_bytes_post_project)
+    S = (H + 127) // 128  # splits of the fused post-map (128-wide h slices)
     per_mode = {
+        "post_project": lambda: algorithmic_bytes_post_project(T, H, S),
+        "fused": lambda: algorithmic_bytes_pre_dots(T, H, splits=S, sqrsum=True) + algorithmic_bytes_post_project(T, H, S),
         "sinkhorn": lambda: algorithmic_bytes_sinkhorn(sk_logits.shape[0]),
         "sinkhorn_bwd": lambda: algorithmic_bytes_sinkhorn_backward(sk_logits.shape[0]),
         "post_bwd": lambda: algorithmic_bytes_post_backward(T, H),

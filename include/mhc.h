@@ -137,8 +137,10 @@ mhc_status mhc_pre_fused_bf16(const uint16_t *res, const uint16_t *hc_fn, const 
  * squares come from outside, optionally as split-K partial sums; section 4,
  * mhc_pre_big_fuse_with_prenorm, where the sum of squares is computed from the
  * streams):
- *     d[t][r]  = sum over s < num_splits of dot_mix[s][t][r]          (in split order)
+ *     d[t][r]  = sum over s < num_splits of dot_mix[s][t][r]
  *     S_t      = sum over s of sqrsum[s][t], or sum_{i,h} res[t][i][h]^2 when sqrsum is NULL
+ *   Both split sums take a fixed order (four interleaved running sums over s mod 4,
+ *   then (0 + 1) + (2 + 3)), so the results do not depend on the launch.
  *     rstd_t   = 1 / sqrt(S_t / k + rms_eps)
  *     m_t[r]   = d[t][r] * rstd_t, then pre, post, comb and y exactly as in mhc_pre_fused
  *
@@ -217,6 +219,36 @@ mhc_status mhc_head(const uint16_t *res, const float *hc_fn, const float *hc_sca
  */
 
 #define MHC_SINKHORN_BWD_MAX_ITERS 255
+
+/*
+ * mhc_post_project -- the post-map fused with the next sublayer's projection
+ * (FlashInfer mHC article, sections 3.1-3.3: the pre-map that takes split-K partial dots
+ * and sums of squares, dot_mix and sqrsum with num_splits; here the post-map that writes
+ * the streams also produces them).  One call computes
+ *     out[t][n][h] = bf16( x[t][h] post[t][n] + sum_o res[t][o][h] comb[t][o][n] )
+ * exactly as mhc_post does (the same bits), and, over the bf16 `out` it writes, the
+ * next pre-map's split partials, one split per 128-wide slice s of h:
+ *     dot_mix[s][t][r] = sum_{i, h in slice s} hc_fn_next[r][i*H + h] out[t][i][h]
+ *     sqrsum[s][t]     = sum_{i, h in slice s} out[t][i][h]^2
+ * (the weights as three exact bf16 terms on MFMA, fp32 accumulation).  Passing them to
+ * mhc_pre_from_dots with num_splits = mhc_post_project_splits(H) and res = out runs the
+ * next pre-map without reading the streams for its projection.
+ *
+ *   x [T,H], res [T,4,H] bf16; post [T,4], comb [T,4,4] fp32   as in mhc_post
+ *   hc_fn_next [24,4H] fp32   the next pre-map's weights
+ *   T >= 0; 8 <= H <= 2097152 with H % 8 == 0; x, res and out 16-byte aligned
+ *   out [T,4,H] bf16   output; may equal `res` exactly
+ *   dot_mix [S][T][24], sqrsum [S][T] fp32   outputs, S = mhc_post_project_splits(H)
+ *   workspace   at least mhc_post_project_workspace_bytes(H) bytes (the next weights
+ *               split for the MFMA), 256-byte aligned; contents on entry ignored
+ * No output may overlap an input, the workspace or another output, except as stated.
+ * T == 0 is a no-op.
+ */
+int32_t mhc_post_project_splits(int64_t H); /* ceil(H / 128); 0 for an unsupported H */
+size_t mhc_post_project_workspace_bytes(int64_t H); /* 0 for an unsupported H */
+mhc_status mhc_post_project(const uint16_t *x, const uint16_t *res, const float *post, const float *comb,
+                            const float *hc_fn_next, int64_t T, int64_t H, uint16_t *out, float *dot_mix,
+                            float *sqrsum, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * mhc_sinkhorn_backward -- gradient of mhc_sinkhorn with respect to its logits,

@@ -79,6 +79,12 @@ def lib() -> ctypes.CDLL:
     L.mhc_pre_from_dots_backward.argtypes = [P, P, P, P, P, I32, P, P, P, I64, I64, F, F, F, F, F, I32, P, P, P, P,
                                              P, P, SZ, P]
     L.mhc_pre_from_dots_backward.restype = ctypes.c_int
+    L.mhc_post_project_splits.argtypes = [I64]
+    L.mhc_post_project_splits.restype = ctypes.c_int32
+    L.mhc_post_project_workspace_bytes.argtypes = [I64]
+    L.mhc_post_project_workspace_bytes.restype = SZ
+    L.mhc_post_project.argtypes = [P, P, P, P, P, I64, I64, P, P, P, P, SZ, P]
+    L.mhc_post_project.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -299,6 +305,70 @@ def mhc_post(x: torch.Tensor, res: torch.Tensor, post: torch.Tensor, comb: torch
     _check("mhc_post", lib().mhc_post(_ptr(x), _ptr(res), _ptr(post), _ptr(comb), T, H, _ptr(out),
                                       _stream(res.device)))
     return out
+
+
+def mhc_post_project_splits(H: int) -> int:
+    return int(lib().mhc_post_project_splits(int(H)))
+
+
+def mhc_post_project_workspace_bytes(H: int) -> int:
+    return int(lib().mhc_post_project_workspace_bytes(int(H)))
+
+
+def mhc_post_project(x: torch.Tensor, res: torch.Tensor, post: torch.Tensor, comb: torch.Tensor,
+                     hc_fn_next: torch.Tensor, *, out: torch.Tensor | None = None,
+                     dot_mix: torch.Tensor | None = None, sqrsum: torch.Tensor | None = None,
+                     workspace: torch.Tensor | None = None):
+    """The post-map fused with the next sublayer's projection: out as :func:`mhc_post`
+    writes it, and the next pre-map's split partials over out, dot_mix [S, ..., 24] and
+    sqrsum [S, ...] fp32 with S = :func:`mhc_post_project_splits` (H).  Returns
+    (out, dot_mix, sqrsum); pass the partials to :func:`mhc_pre_from_dots` with res=out.
+    H must be a multiple of 8; ``out`` may be ``res``."""
+    _need(res, "res", torch.bfloat16)
+    if res.dim() < 2 or res.shape[-2] != HC:
+        raise ValueError(f"residual.shape[-2] / HC must be 4, got {tuple(res.shape)}")
+    H = res.shape[-1]
+    outer = tuple(res.shape[:-2])
+    T = res.numel() // (HC * H) if H > 0 else 0
+    if H % 8 != 0:
+        raise ValueError(f"H must be a multiple of 8, got {H}")
+    _need(x, "x", torch.bfloat16)
+    if tuple(x.shape) != outer + (H,):
+        raise ValueError(f"x must be {outer + (H,)}, got {tuple(x.shape)}")
+    _need(post, "post", torch.float32)
+    if tuple(post.shape) not in (outer + (HC,), outer + (HC, 1)):
+        raise ValueError(f"post must be {outer + (HC,)} or {outer + (HC, 1)}, got {tuple(post.shape)}")
+    _need(comb, "comb", torch.float32)
+    if tuple(comb.shape) != outer + (HC, HC):
+        raise ValueError(f"comb must be {outer + (HC, HC)}, got {tuple(comb.shape)}")
+    _need(hc_fn_next, "hc_fn_next", torch.float32)
+    if tuple(hc_fn_next.shape) != (MIX, HC * H):
+        raise ValueError(f"hc_fn_next must be {(MIX, HC * H)}, got {tuple(hc_fn_next.shape)}")
+    S = mhc_post_project_splits(H)
+    dev = res.device
+    if out is None:
+        out = torch.empty_like(res)
+    _need(out, "out", torch.bfloat16)
+    if out.shape != res.shape:
+        raise ValueError("out must have the shape of res")
+    if dot_mix is None:
+        dot_mix = torch.empty((S,) + outer + (MIX,), dtype=torch.float32, device=dev)
+    _need(dot_mix, "dot_mix", torch.float32)
+    if tuple(dot_mix.shape) != (S,) + outer + (MIX,):
+        raise ValueError(f"dot_mix must be {(S,) + outer + (MIX,)}, got {tuple(dot_mix.shape)}")
+    if sqrsum is None:
+        sqrsum = torch.empty((S,) + outer, dtype=torch.float32, device=dev)
+    _need(sqrsum, "sqrsum", torch.float32)
+    if tuple(sqrsum.shape) != (S,) + outer:
+        raise ValueError(f"sqrsum must be {(S,) + outer}, got {tuple(sqrsum.shape)}")
+    need = mhc_post_project_workspace_bytes(H)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _same_device(x, res, post, comb, hc_fn_next, out, dot_mix, sqrsum, workspace)
+    _check("mhc_post_project", lib().mhc_post_project(_ptr(x), _ptr(res), _ptr(post), _ptr(comb), _ptr(hc_fn_next),
+                                                      T, H, _ptr(out), _ptr(dot_mix), _ptr(sqrsum), _ptr(workspace),
+                                                      workspace.numel(), _stream(dev)))
+    return out, dot_mix, sqrsum
 
 
 SINKHORN_BWD_MAX_ITERS = 255
@@ -578,5 +648,6 @@ __all__ = ["mhc_sinkhorn", "mhc_pre_fused", "mhc_pre_fused_bf16", "mhc_expand", 
            "mhc_pre_fused_workspace_bytes", "mhc_pre_from_dots", "mhc_post",
            "mhc_sinkhorn_backward", "mhc_post_backward", "mhc_pre_from_dots_backward",
            "mhc_pre_backward_workspace_bytes", "mhc_pre_fused_backward", "mhc_pre_fused_backward_workspace_bytes",
+           "mhc_post_project", "mhc_post_project_splits", "mhc_post_project_workspace_bytes",
            "lib", "abi_version", "status_string", "MHCError", "HC",
            "MIX", "SINKHORN_BWD_MAX_ITERS"]

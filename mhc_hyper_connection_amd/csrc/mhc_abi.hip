@@ -259,6 +259,65 @@ mhc_status mhc_post(const uint16_t *x, const uint16_t *res, const float *post, c
     return launch_status(mhc::launch_post(x, res, post, comb, T, H, out, (hipStream_t)stream, vec8));
 }
 
+int32_t mhc_post_project_splits(int64_t H)
+{
+    if (H < 8 || H % 8 != 0 || H > kPreMaxH) {
+        return 0;
+    }
+    return (int32_t)mhc::post_project_splits(H);
+}
+
+size_t mhc_post_project_workspace_bytes(int64_t H)
+{
+    if (H < 8 || H % 8 != 0 || H > kPreMaxH) {
+        return 0;
+    }
+    return mhc::post_project_workspace_bytes(H);
+}
+
+mhc_status mhc_post_project(const uint16_t *x, const uint16_t *res, const float *post, const float *comb,
+                            const float *hc_fn_next, int64_t T, int64_t H, uint16_t *out, float *dot_mix,
+                            float *sqrsum, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!sizes_ok(T, H) || H % 8 != 0 || H > kPreMaxH) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    if (T == 0) {
+        return MHC_SUCCESS;
+    }
+    if (!x || !res || !post || !comb || !hc_fn_next || !out || !dot_mix || !sqrsum) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    if (!aligned16(x) || !aligned16(res) || !aligned16(out)) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    const size_t need = mhc::post_project_workspace_bytes(H);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0) {
+        return MHC_ERROR_WORKSPACE;
+    }
+    const size_t S = (size_t)mhc::post_project_splits(H);
+    const size_t res_b = (size_t)T * 4 * H * 2, x_b = (size_t)T * H * 2, fn_b = (size_t)24 * 4 * H * 4;
+    const void *outs[4] = {out, dot_mix, sqrsum, workspace};
+    const size_t outn[4] = {res_b, S * T * 24 * 4, S * T * 4, need};
+    const void *ins[5] = {res, x, post, comb, hc_fn_next};
+    const size_t inn[5] = {res_b, x_b, (size_t)T * 16, (size_t)T * 64, fn_b};
+    for (int o = 0; o < 4; ++o) {
+        for (int i = 0; i < 5; ++i) {
+            const bool in_place = o == 0 && i == 0 && (const void *)out == (const void *)res;
+            if (!in_place && overlaps(outs[o], outn[o], ins[i], inn[i])) {
+                return MHC_ERROR_INVALID_VALUE;
+            }
+        }
+        for (int o2 = o + 1; o2 < 4; ++o2) {
+            if (overlaps(outs[o], outn[o], outs[o2], outn[o2])) {
+                return MHC_ERROR_INVALID_VALUE;
+            }
+        }
+    }
+    return launch_status(mhc::launch_post_project(x, res, post, comb, hc_fn_next, T, H, out, dot_mix, sqrsum,
+                                                  workspace, (hipStream_t)stream));
+}
+
 mhc_status mhc_sinkhorn_backward(const float *grad, const float *logits, int64_t n_mats, int32_t num_iters,
                                  float eps, float *d_logits, void *stream)
 {

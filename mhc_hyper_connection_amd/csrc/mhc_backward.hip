@@ -138,10 +138,12 @@ __global__ __launch_bounds__(kDBBlock) void pre_dots_bwd_kernel(DotsBwdArgs a)
 {
     extern __shared__ float hist[]; // [iters + 1][64], wavefront 0's Sinkhorn history
     __shared__ float part[kDBWaves][kHC + 1];
-    __shared__ float dsum[kMix];
+    __shared__ float dsum[kSplitFields]; // the summed dots, then the supplied sum of squares
+    __shared__ float stage[kSplitStage * kSplitFields];
+    __shared__ float wpart[4 * kSplitFields];
     __shared__ float bc[kHC + 1]; // pre weights, then the coefficient of res in d_res
 
-    const int t = blockIdx.x;
+    const int t = xcd_contiguous((int)blockIdx.x, (int)gridDim.x); // one token per workgroup
     const int tid = threadIdx.x;
     const int w = uniform(tid >> 6);
     const int lane = tid & (kWave - 1);
@@ -150,13 +152,6 @@ __global__ __launch_bounds__(kDBBlock) void pre_dots_bwd_kernel(DotsBwdArgs a)
     const uint16_t *grow = a.dy + (size_t)t * H;
     // S computed here from the streams (the RMS term of d_res applies), or supplied
     const bool need_sq = a.sqrsum == nullptr;
-
-    float dv = 0.0f;
-    if (w == 0 && lane < kMix) {
-        for (int s = 0; s < a.S; ++s) {
-            dv += a.dot_mix[((size_t)s * a.T + t) * kMix + lane];
-        }
-    }
 
     float dp[kHC] = {0.0f, 0.0f, 0.0f, 0.0f};
     float sq = 0.0f;
@@ -173,6 +168,8 @@ __global__ __launch_bounds__(kDBBlock) void pre_dots_bwd_kernel(DotsBwdArgs a)
                 r[i][k] = in ? load16(row + (size_t)i * H + (size_t)j * 8) : u32x4{0u, 0u, 0u, 0u};
             }
         }
+        // the split partials, loaded while the streams are in flight
+        sum_split_partials(a.dot_mix, a.sqrsum, a.S, a.T, t, stage, wpart, dsum);
 #pragma unroll
         for (int k = 0; k < kCPT; ++k) {
 #pragma unroll
@@ -192,6 +189,7 @@ __global__ __launch_bounds__(kDBBlock) void pre_dots_bwd_kernel(DotsBwdArgs a)
             }
         }
     } else {
+        sum_split_partials(a.dot_mix, a.sqrsum, a.S, a.T, t, stage, wpart, dsum);
         for (int h = tid; h < H; h += kDBBlock) {
             const float gv = bf16_to_f32(grow[h]);
 #pragma unroll
@@ -214,9 +212,6 @@ __global__ __launch_bounds__(kDBBlock) void pre_dots_bwd_kernel(DotsBwdArgs a)
         }
         part[w][kHC] = sq;
     }
-    if (w == 0 && lane < kMix) {
-        dsum[lane] = dv;
-    }
     __syncthreads();
 
     if (w == 0) {
@@ -224,9 +219,7 @@ __global__ __launch_bounds__(kDBBlock) void pre_dots_bwd_kernel(DotsBwdArgs a)
         if (need_sq) {
             S = (part[0][kHC] + part[1][kHC]) + (part[2][kHC] + part[3][kHC]);
         } else {
-            for (int s = 0; s < a.S; ++s) {
-                S += a.sqrsum[(size_t)s * a.T + t];
-            }
+            S = dsum[kMix];
         }
         const float rstd = 1.0f / sqrtf(S / a.k + a.rms_eps);
         // comb: Sinkhorn reverse mode, entry e = lane & 15 on every 16-lane row (each row

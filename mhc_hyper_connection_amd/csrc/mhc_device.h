@@ -156,4 +156,68 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_view_uniform(const void *b
     return __builtin_amdgcn_make_buffer_rsrc(q, 0, (int)n, 0x00020000);
 }
 
+// Workgroups are dealt to the chip's 8 XCDs (each with its own L2) round robin.
+// For a grid of n workgroups, one per item, this maps workgroup b to an item such that
+// XCD b mod 8 walks a contiguous run of items: neighbouring items, whose small rows
+// share cache lines, then meet in the same L2.  A bijection on [0, n).
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_contiguous(int b, int n)
+{
+    const int q = n / kXcds, r = n - kXcds * q;
+    const int x = b & (kXcds - 1), i = b / kXcds;
+    return x * q + min(x, r) + i;
+}
+
+// A token's split partials summed by a whole 256-thread workgroup: dots [S][T][24] into
+// out[0..23] and, when sqrsum is given, sums of squares [S][T] into out[24] (LDS).
+// Splits are staged 64 at a time, every thread loading some of them, so the loads are
+// in flight together instead of one after another.  Wave w adds the splits s = w mod 4
+// in increasing order, and the four wave sums combine as (w0 + w1) + (w2 + w3): a fixed
+// order, so the result is deterministic.  stage: 64 * 25 floats, wpart: 4 * 25 floats.
+// Every thread of the workgroup must call it; out is valid after it returns.
+constexpr int kSplitStage = 64;
+constexpr int kSplitFields = kMix + 1;
+__device__ __forceinline__ void sum_split_partials(const float *dot_mix, const float *sqrsum, int S, int T, int t,
+                                                   float *stage, float *wpart, float *out)
+{
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int lane = tid & (kWave - 1);
+    float acc = 0.0f;
+    for (int s0 = 0; s0 < S; s0 += kSplitStage) {
+        const int ns = min(kSplitStage, S - s0);
+#pragma unroll
+        for (int k = 0; k < (kSplitStage * kSplitFields + 255) / 256; ++k) {
+            const int e = tid + 256 * k;
+            const int s = e / kSplitFields, f = e - kSplitFields * s;
+            float v = 0.0f;
+            if (s < ns) {
+                if (f < kMix) {
+                    v = dot_mix[((size_t)(s0 + s) * T + t) * kMix + f];
+                } else if (sqrsum != nullptr) {
+                    v = sqrsum[(size_t)(s0 + s) * T + t];
+                }
+            }
+            if (e < kSplitStage * kSplitFields) {
+                stage[e] = v;
+            }
+        }
+        __syncthreads();
+        if (lane < kSplitFields) {
+            for (int s = w; s < ns; s += 4) {
+                acc += stage[s * kSplitFields + lane];
+            }
+        }
+        __syncthreads();
+    }
+    if (lane < kSplitFields) {
+        wpart[w * kSplitFields + lane] = acc;
+    }
+    __syncthreads();
+    if (tid < kSplitFields) {
+        out[tid] = (wpart[tid] + wpart[kSplitFields + tid]) + (wpart[2 * kSplitFields + tid] + wpart[3 * kSplitFields + tid]);
+    }
+    __syncthreads();
+}
+
 } // namespace mhc

@@ -48,6 +48,17 @@ hipError_t launch_pre_split(const float *hc_fn, const PreGeom &g, void *workspac
 hipError_t launch_pre_sums(const uint16_t *res, const uint16_t *dy, const PreGeom &g, int64_t c0, int Tc,
                            void *workspace, hipStream_t stream, bool vec8);
 
+// The post-map fused with the next sublayer's projection (H % 8 == 0, 16-byte aligned
+// rows): out as launch_post writes it, plus the split partials of the next pre-map's
+// dots and sum of squares over out, one split per 128-wide slice of H
+// (dot_mix [post_project_splits(H)][T][24], sqrsum [..][T]).  The workspace holds the
+// next weights split for the MFMA (post_project_workspace_bytes(H)).
+int post_project_splits(int64_t H);
+size_t post_project_workspace_bytes(int64_t H);
+hipError_t launch_post_project(const uint16_t *x, const uint16_t *res, const float *post, const float *comb,
+                               const float *hc_fn_next, int64_t T, int64_t H, uint16_t *out, float *dot_mix,
+                               float *sqrsum, void *workspace, hipStream_t stream);
+
 // Model entry (each hidden row copied into the 4 streams) and the unweighted head (the
 // mean of the 4 streams).  `vec8`: H % 8 == 0 and both pointers 16-byte aligned.
 hipError_t launch_expand(const uint16_t *hidden, int64_t T, int64_t H, uint16_t *streams, hipStream_t stream,

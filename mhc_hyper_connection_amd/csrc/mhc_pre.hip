@@ -593,6 +593,248 @@ __global__ __launch_bounds__(kPBlock, 2) void pre_proj_stream_kernel(ProjStreamA
     }
 }
 
+// ---------------------------------------------------------------- post-map fused with the next projection
+//
+// A post-map whose output feeds the next sublayer's pre-map, and that sublayer's
+// projection and sum of squares on the way.  One 256-thread workgroup per (128-wide
+// slice of H across the 4 streams, token range), walked in 32-token steps as in
+// pre_proj_stream_kernel.  In a step each thread takes two (token, 16-byte piece)
+// pairs: it loads x, the four old streams and the token's coefficients, computes the
+// four new streams with the arithmetic of post_vec8_kernel (so they are the same bits),
+// stores them and writes them to the LDS tile.  The waves then project the tile with the
+// next weights and reduce the slice's 24 dots and sum of squares into split partials of
+// the form the external-dots pre-map takes: dot_mix[slice][t][24], sqrsum[slice][t].
+// The next step's loads are in flight meanwhile.  out may equal res: each pair's old
+// streams are read, by the thread that writes them, before they are written.
+struct PostProjArgs {
+    const uint16_t *x, *res;
+    const float *post, *comb;
+    const u32x4 *frag; // the next weights, split by pre_prep_kernel
+    int T, H, nhb, S, tok_per_range;
+    uint16_t *out;
+    float *dot_mix; // [S][T][24]
+    float *sqrsum;  // [S][T]
+};
+
+constexpr int kPPPairs = kPSTok * (kPSliceH / 8) / kPBlock; // (token, piece) pairs per thread per step (2)
+constexpr int kPPCoef = kHC + kHC * kHC;                     // post (4) and comb (16) of a token
+constexpr int kPPCoefPieces = kPSTok * kPPCoef / 4;          // 16-byte pieces per step (160)
+
+// What a thread loads for a step: x and the four old streams of its two pairs (token
+// (tid >> 4) + 16k, piece tid & 15), and piece tid of the step's coefficient block
+// ([32 tokens][20] fp32; threads past 160 load nothing).
+struct PostStepIn {
+    u32x4 x[kPPPairs], r[kPPPairs][kHC], cf;
+};
+
+// Past the range the views are empty and read zero.
+__device__ __forceinline__ void post_proj_load(const PostProjArgs &a, int t0, int te, int tid, uint32_t colq,
+                                               PostStepIn &in)
+{
+    const int H = a.H;
+    const int ntok = max(0, min(kPSTok, te - t0));
+    const __amdgpu_buffer_rsrc_t vx = buf_view_uniform(a.x + (size_t)t0 * H, (uint32_t)((size_t)ntok * H * 2));
+    const __amdgpu_buffer_rsrc_t vr =
+        buf_view_uniform(a.res + (size_t)t0 * kHC * H, (uint32_t)((size_t)ntok * kHC * H * 2));
+#pragma unroll
+    for (int k = 0; k < kPPPairs; ++k) {
+        const int tl = (tid >> 4) + 16 * k;
+        in.x[k] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(vx, (int)((uint32_t)(tl * H) * 2u + colq), 0, 0));
+#pragma unroll
+        for (int o = 0; o < kHC; ++o) {
+            in.r[k][o] = __builtin_bit_cast(
+                u32x4,
+                __builtin_amdgcn_raw_buffer_load_b128(vr, (int)((uint32_t)((tl * kHC + o) * H) * 2u + colq), 0, 0));
+        }
+    }
+    // coefficient piece tid: token tid / 5, word 4 (tid % 5) of its 20 (post, then comb)
+    const int ct = tid / 5, cq = tid - 5 * (tid / 5);
+    const __amdgpu_buffer_rsrc_t vp = buf_view_uniform(a.post + (size_t)t0 * kHC, (uint32_t)(ntok * kHC * 4));
+    const __amdgpu_buffer_rsrc_t vc =
+        buf_view_uniform(a.comb + (size_t)t0 * kHC * kHC, (uint32_t)(ntok * kHC * kHC * 4));
+    const int off = tid < kPPCoefPieces ? (cq == 0 ? ct * 16 : ct * 64 + (cq - 1) * 16) : (int)0x80000000;
+    const u32x4 pv = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vp, cq == 0 ? off : (int)0x80000000, 0, 0));
+    const u32x4 cv = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vc, cq != 0 ? off : (int)0x80000000, 0, 0));
+    in.cf = cq == 0 ? pv : cv;
+}
+
+// The pairs' new streams: stored to `out` and written to the LDS tile (row token*4 + n).
+// coef: [32][20] fp32 in LDS.
+__device__ __forceinline__ void post_proj_emit(const PostProjArgs &a, int t0, int te, int tid, uint32_t colq,
+                                               const PostStepIn &in, const float *coef, unsigned char *tile)
+{
+    const int H = a.H;
+    const int ntok = max(0, min(kPSTok, te - t0));
+    const __amdgpu_buffer_rsrc_t vo =
+        buf_view_uniform(a.out + (size_t)t0 * kHC * H, (uint32_t)((size_t)ntok * kHC * H * 2));
+#pragma unroll
+    for (int k = 0; k < kPPPairs; ++k) {
+        const int tl = (tid >> 4) + 16 * k;
+        const float *cf = coef + tl * kPPCoef; // post[n] at n, comb[o][n] at 4 + 4o + n
+        float xf[8], rf[kHC][8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            xf[2 * q] = bf16_lo(in.x[k][q]);
+            xf[2 * q + 1] = bf16_hi(in.x[k][q]);
+#pragma unroll
+            for (int o = 0; o < kHC; ++o) {
+                rf[o][2 * q] = bf16_lo(in.r[k][o][q]);
+                rf[o][2 * q + 1] = bf16_hi(in.r[k][o][q]);
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < kHC; ++n) {
+            const float pn = cf[n];
+            const float c0 = cf[kHC + n], c1 = cf[2 * kHC + n], c2 = cf[3 * kHC + n], c3 = cf[4 * kHC + n];
+            u32x4 ow;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float v[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int j = 2 * q + e;
+                    float acc = xf[j] * pn;
+                    acc = fmaf(rf[0][j], c0, acc);
+                    acc = fmaf(rf[1][j], c1, acc);
+                    acc = fmaf(rf[2][j], c2, acc);
+                    acc = fmaf(rf[3][j], c3, acc);
+                    v[e] = acc;
+                }
+                ow[q] = pack_bf16x2(v[0], v[1]);
+            }
+            __builtin_amdgcn_raw_buffer_store_b128(ow, vo, (int)((uint32_t)((tl * kHC + n) * H) * 2u + colq), 0, 0);
+            *reinterpret_cast<u32x4 *>(tile + pstile_at(tl * kHC + n, tid & 15)) = ow;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kPBlock, 2) void post_proj_stream_kernel(PostProjArgs a)
+{
+    __shared__ __attribute__((aligned(16))) unsigned char tile[kPSRows * kPSRowB];
+    __shared__ __attribute__((aligned(16))) float coef[kPSTok * kPPCoef];
+    __shared__ float red[kPWaves][kPSTok][kPSRedStride];
+    __shared__ float sqp[kPWaves][kPSTok][4];
+
+    const int tid = threadIdx.x;
+    const int w = uniform(tid >> 6);
+    const int lane = tid & (kWave - 1);
+    const int g = lane >> 4, c = lane & 15;
+    const int slice = blockIdx.x;
+    const int H = a.H;
+    const int tb = blockIdx.y * a.tok_per_range;
+    const int te = min(a.T, tb + a.tok_per_range);
+    const int hb = slice * kPWaves + w;
+    const int hq = slice * kPSliceH + 8 * (tid & 15);
+    const uint32_t colq = hq < H ? (uint32_t)hq * 2u : 0x80000000u;
+
+    u32x4 b0[kHC][3], b1[kHC][3];
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const u32x4 *fp = a.frag + (size_t)hb * kHC * kFragPerHbStream;
+#pragma unroll
+    for (int i = 0; i < kHC; ++i) {
+#pragma unroll
+        for (int s = 0; s < 3; ++s) {
+            b0[i][s] = hb < a.nhb ? fp[i * kFragPerHbStream + s * 64 + lane] : z;
+            b1[i][s] = hb < a.nhb && c < 8 ? fp[i * kFragPerHbStream + 192 + s * 32 + ((g * 8 + c) & 31)] : z;
+        }
+    }
+    if (tb >= te) {
+        return;
+    }
+    PostStepIn in;
+    post_proj_load(a, uniform(tb), te, tid, colq, in);
+    for (int t0 = tb; t0 < te; t0 += kPSTok) {
+        const int tu = uniform(t0);
+        // the step's coefficients to LDS (free since the last step's second barrier)
+        if (tid < kPPCoefPieces) {
+            *reinterpret_cast<u32x4 *>(coef + 4 * tid) = in.cf;
+        }
+        lds_barrier(); // coefficients in; the tile is free
+        // the step's new streams out and into the tile, then the next step's loads
+        post_proj_emit(a, tu, te, tid, colq, in, coef, tile);
+        post_proj_load(a, tu + kPSTok, te, tid, colq, in);
+        lds_barrier(); // the tile holds the step's new streams
+        f32x4 acc[kPSMT][2];
+        float sq[kPSMT];
+#pragma unroll
+        for (int m = 0; m < kPSMT; ++m) {
+            acc[m][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+            acc[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+            sq[m] = 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < kHC; ++i) {
+            u32x4 dc[kPSMT];
+#pragma unroll
+            for (int m = 0; m < kPSMT; ++m) {
+                dc[m] = *reinterpret_cast<const u32x4 *>(tile + pstile_at((m * 16 + c) * kHC + i, 4 * w + g));
+            }
+#pragma unroll
+            for (int s = 0; s < 3; ++s) {
+                const bf16x8 B0 = __builtin_bit_cast(bf16x8, b0[i][s]);
+                const bf16x8 B1 = __builtin_bit_cast(bf16x8, b1[i][s]);
+#pragma unroll
+                for (int m = 0; m < kPSMT; ++m) {
+                    const bf16x8 A = __builtin_bit_cast(bf16x8, dc[m]);
+                    acc[m][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B0, acc[m][0], 0, 0, 0);
+                    acc[m][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B1, acc[m][1], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < kPSMT; ++m) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t wk = dc[m][k];
+                    const bf16x2 pr = __builtin_bit_cast(bf16x2, wk);
+                    sq[m] = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, sq[m], false);
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < kPSMT; ++m) {
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                const int col = n * 16 + c;
+                if (col < kMix) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        red[w][m * 16 + 4 * g + k][col] = acc[m][n][k];
+                    }
+                }
+            }
+            sqp[w][m * 16 + c][g] = sq[m];
+        }
+        lds_barrier(); // the partial dots are in LDS; every wave is done with the tile and the coefficients
+        // the slice's split partials of these 32 tokens (past the range: dropped)
+        const int ntok = max(0, min(kPSTok, te - tu));
+        const __amdgpu_buffer_rsrc_t vd =
+            buf_view_uniform(a.dot_mix + ((size_t)slice * a.T + tu) * kMix, (uint32_t)(ntok * kMix * 4));
+        const __amdgpu_buffer_rsrc_t vs =
+            buf_view_uniform(a.sqrsum + (size_t)slice * a.T + tu, (uint32_t)(ntok * 4));
+        const int tok = tid & (kPSTok - 1);
+#pragma unroll
+        for (int j = 0; j < kMix / (kPBlock / kPSTok); ++j) {
+            const int col = (tid >> 5) + j * (kPBlock / kPSTok);
+            float v = red[0][tok][col];
+#pragma unroll
+            for (int ww = 1; ww < kPWaves; ++ww) {
+                v += red[ww][tok][col];
+            }
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), vd, (tok * kMix + col) * 4, 0, 0);
+        }
+        float v = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < kPWaves; ++ww) {
+#pragma unroll
+            for (int gg = 0; gg < 4; ++gg) {
+                v += sqp[ww][tok][gg];
+            }
+        }
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), vs, tid < kPSTok ? tok * 4 : (int)0x80000000, 0, 0);
+    }
+}
+
 // Token ranges of the streaming projection for Tc tokens and S slices.
 static void pre_stream_ranges(int Tc, int S, int &ranges, int &tok_per_range)
 {
@@ -810,6 +1052,47 @@ hipError_t launch_pre_split(const float *hc_fn, const PreGeom &g, void *workspac
     const int prep_threads = g.nhb * kHC * (kFragPerHbStream / 3);
     pre_prep_kernel<float><<<dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, stream>>>(
         hc_fn, (int)g.H, g.nhb, kMix, frag);
+    return hipGetLastError();
+}
+
+int post_project_splits(int64_t H) { return (int)((H + kPSliceH - 1) / kPSliceH); }
+
+size_t post_project_workspace_bytes(int64_t H)
+{
+    const int64_t nhb = (H + kPHB - 1) / kPHB;
+    return align256((size_t)nhb * kHC * kFragPerHbStream * sizeof(u32x4));
+}
+
+hipError_t launch_post_project(const uint16_t *x, const uint16_t *res, const float *post, const float *comb,
+                               const float *hc_fn_next, int64_t T, int64_t H, uint16_t *out, float *dot_mix,
+                               float *sqrsum, void *workspace, hipStream_t stream)
+{
+    PreGeom g{};
+    g.T = T;
+    g.H = H;
+    g.nhb = (int)((H + kPHB - 1) / kPHB);
+    g.slices = post_project_splits(H);
+    g.off_frag = 0;
+    hipError_t e = launch_pre_split(hc_fn_next, g, workspace, stream);
+    if (e != hipSuccess) {
+        return e;
+    }
+    PostProjArgs a{};
+    a.x = x;
+    a.res = res;
+    a.post = post;
+    a.comb = comb;
+    a.frag = reinterpret_cast<const u32x4 *>(workspace);
+    a.T = (int)T;
+    a.H = (int)H;
+    a.nhb = g.nhb;
+    a.S = g.slices;
+    a.out = out;
+    a.dot_mix = dot_mix;
+    a.sqrsum = sqrsum;
+    int ranges = 1;
+    pre_stream_ranges((int)T, g.slices, ranges, a.tok_per_range);
+    post_proj_stream_kernel<<<dim3((unsigned)g.slices, (unsigned)ranges), dim3(kPBlock), 0, stream>>>(a);
     return hipGetLastError();
 }
 

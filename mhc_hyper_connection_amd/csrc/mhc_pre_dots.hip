@@ -8,8 +8,8 @@
 // One 256-thread workgroup per token.  On the 16-byte path each thread holds its
 // 8-element chunks of all 4 streams in VGPRs, so the streams are read from HBM
 // once: the sum of squares (when needed), the mixes and the collapse all use the
-// same registers.  Wavefront 0 sums the dot partials in split order, computes rstd
-// and the pre weights, and after the collapse the post weights and the 4x4
+// same registers.  The whole workgroup sums the dot partials (staged through LDS,
+// 64 splits at a time, in a fixed order), wavefront 0 computes rstd and the pre weights, and after the collapse the post weights and the 4x4
 // Sinkhorn of comb, one matrix entry per lane of a 16-lane row.
 #include "mhc_device.h"
 #include "mhc_internal.h"
@@ -41,25 +41,19 @@ template <int kCPT>
 __global__ __launch_bounds__(kDBlock) void pre_dots_kernel(DotsArgs a)
 {
     __shared__ float wsum[kDWaves];
-    __shared__ float dsum[kMix];
+    __shared__ float dsum[kSplitFields]; // the summed dots, then the supplied sum of squares
+    __shared__ float stage[kSplitStage * kSplitFields];
+    __shared__ float wpart[4 * kSplitFields];
     __shared__ float prew[kHC];
     __shared__ float rstd_s;
 
-    const int t = blockIdx.x;
+    const int t = xcd_contiguous((int)blockIdx.x, (int)gridDim.x); // one token per workgroup
     const int tid = threadIdx.x;
     const int w = uniform(tid >> 6);
     const int lane = tid & (kWave - 1);
     const int H = a.H;
     const uint16_t *row = a.res + (size_t)t * kHC * H;
     const bool need_sq = a.sqrsum == nullptr;
-
-    // the dots of this token, summed over the splits in split order
-    float dv = 0.0f;
-    if (w == 0 && lane < kMix) {
-        for (int s = 0; s < a.S; ++s) {
-            dv += a.dot_mix[((size_t)s * a.T + t) * kMix + lane];
-        }
-    }
 
     float sq = 0.0f;
     u32x4 r[kHC][kCPT > 0 ? kCPT : 1];
@@ -73,6 +67,8 @@ __global__ __launch_bounds__(kDBlock) void pre_dots_kernel(DotsArgs a)
                 r[i][k] = j < nch ? load16(row + (size_t)i * H + (size_t)j * 8) : u32x4{0u, 0u, 0u, 0u};
             }
         }
+        // the split partials, loaded while the streams are in flight
+        sum_split_partials(a.dot_mix, a.sqrsum, a.S, a.T, t, stage, wpart, dsum);
         if (need_sq) {
 #pragma unroll
             for (int k = 0; k < kCPT; ++k) {
@@ -90,6 +86,7 @@ __global__ __launch_bounds__(kDBlock) void pre_dots_kernel(DotsArgs a)
             }
         }
     } else {
+        sum_split_partials(a.dot_mix, a.sqrsum, a.S, a.T, t, stage, wpart, dsum);
         if (need_sq) {
             for (int h = tid; h < H; h += kDBlock) {
 #pragma unroll
@@ -106,9 +103,6 @@ __global__ __launch_bounds__(kDBlock) void pre_dots_kernel(DotsArgs a)
             wsum[w] = sq;
         }
     }
-    if (w == 0 && lane < kMix) {
-        dsum[lane] = dv;
-    }
     __syncthreads();
 
     // rstd and the pre weights (wavefront 0)
@@ -117,9 +111,7 @@ __global__ __launch_bounds__(kDBlock) void pre_dots_kernel(DotsArgs a)
         if (need_sq) {
             S = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
         } else {
-            for (int s = 0; s < a.S; ++s) {
-                S += a.sqrsum[(size_t)s * a.T + t];
-            }
+            S = dsum[kMix];
         }
         const float rstd = 1.0f / sqrtf(S / a.k + a.rms_eps);
         if (lane < kHC) {

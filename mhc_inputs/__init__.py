@@ -248,6 +248,13 @@ def algorithmic_bytes_post(T: int, H: int) -> int:
     return T * (2 * H + 8 * H + 80 + 8 * H)
 
 
+def algorithmic_bytes_post_project(T: int, H: int, splits: int) -> int:
+    """The post-map fused with the next projection: the post-map's bytes, the next fp32
+    weights read once, and the split partials written (24 dots and a sum of squares, 100 B
+    per token and split)."""
+    return algorithmic_bytes_post(T, H) + 384 * H + T * splits * 100
+
+
 def algorithmic_bytes_pre_dots(T: int, H: int, splits: int = 1, sqrsum: bool = False) -> int:
     """Bytes the pre-map from external dots must move: the dot partials (and sum-of-squares
     partials) read, res read, y written, post/comb written, scale/base read once."""

@@ -309,11 +309,50 @@ def test_pre_fused_backward_workspace():
     assert _fbwd(lib, ws=0x9000000 + 16) == mhc.MHC_ERROR_WORKSPACE
 
 
+def _pproj(lib, **kw):
+    # every case below turns one argument invalid: validation fails before any launch
+    a = dict(x=0x100000, res=0x400000, post=0x200000, comb=0x210000, fn=0x1000000, T=8, H=64, out=0x600000,
+             dm=0x2000000, sq=0x800000, ws=0x9000000, wsb=1 << 30)
+    a.update(kw)
+    v = lambda n: ctypes.c_void_p(a[n]) if a[n] is not None else None
+    return lib.mhc_post_project(v("x"), v("res"), v("post"), v("comb"), v("fn"), a["T"], a["H"], v("out"), v("dm"),
+                                v("sq"), v("ws"), a["wsb"], NULL)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(T=-1), dict(H=0), dict(H=60), dict(H=(1 << 21) + 8), dict(x=None), dict(res=None), dict(post=None),
+    dict(comb=None), dict(fn=None), dict(out=None), dict(dm=None), dict(sq=None), dict(x=0x100000 + 8),
+    dict(res=0x400000 + 8), dict(out=0x600000 + 8), dict(out=0x400000 + 16), dict(out=0x100000),
+    dict(dm=0x400000), dict(sq=0x2000000 + 16), dict(dm=0x1000000), dict(ws=0x600000),
+])
+def test_post_project_validation_invalid(kw):
+    assert _pproj(mhc.lib(), **kw) == mhc.MHC_ERROR_INVALID_VALUE
+
+
+def test_post_project_workspace_and_splits():
+    lib = mhc.lib()
+    assert mhc.mhc_post_project_splits(64) == 1 and mhc.mhc_post_project_splits(7168) == 56
+    assert mhc.mhc_post_project_splits(1000) == 8 and mhc.mhc_post_project_splits(60) == 0
+    need = mhc.mhc_post_project_workspace_bytes(64)
+    assert need > 0 and need % 256 == 0 and mhc.mhc_post_project_workspace_bytes(60) == 0
+    # the split weights take 576 bytes per h, as the pre-map's: 288 16-byte fragments per 32 h and stream
+    assert mhc.mhc_post_project_workspace_bytes(7168) == 576 * 7168
+    assert _pproj(lib, wsb=need - 1) == mhc.MHC_ERROR_WORKSPACE
+    assert _pproj(lib, ws=None) == mhc.MHC_ERROR_WORKSPACE
+    assert _pproj(lib, ws=0x9000000 + 16) == mhc.MHC_ERROR_WORKSPACE
+    # T == 0: nothing to do, no pointer is looked at
+    assert _pproj(lib, T=0, x=None, res=None, post=None, comb=None, fn=None, out=None, dm=None, sq=None,
+                  ws=None, wsb=0) == mhc.MHC_SUCCESS
+
+
 def test_binding_rejects_cpu_tensors_before_the_library():
     import torch
     with pytest.raises(ValueError):
         mhc.mhc_post(torch.zeros(2, 8, dtype=torch.bfloat16), torch.zeros(2, 4, 8, dtype=torch.bfloat16),
                      torch.zeros(2, 4), torch.zeros(2, 4, 4))
+    with pytest.raises(ValueError):
+        mhc.mhc_post_project(torch.zeros(2, 8, dtype=torch.bfloat16), torch.zeros(2, 4, 8, dtype=torch.bfloat16),
+                             torch.zeros(2, 4), torch.zeros(2, 4, 4), torch.zeros(24, 32))
     with pytest.raises(ValueError):
         mhc.mhc_sinkhorn(torch.zeros(3, 4, 4))
     with pytest.raises(ValueError):
