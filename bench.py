@@ -212,10 +212,9 @@ def main():
         # the post-map with the next sublayer's projection fused in (the next weights are
         # hc_fn again); "fused" is the steady-state sublayer step: the pre-map from the
         # previous post-map's partials, then the post-map updating the streams in place
-        pp_S = mhc.mhc_post_project_splits(H)
-        pp_dm = torch.empty(pp_S, T, 24, dtype=torch.float32, device=dev)
-        pp_sq = torch.empty(pp_S, T, dtype=torch.float32, device=dev)
-        pp_ws = torch.empty(mhc.mhc_post_project_workspace_bytes(H), dtype=torch.uint8, device=dev)
+        pp_dm = torch.empty(T, 24, dtype=torch.float32, device=dev)
+        pp_sq = torch.empty(T, dtype=torch.float32, device=dev)
+        pp_ws = torch.empty(mhc.mhc_post_project_workspace_bytes(T, H), dtype=torch.uint8, device=dev)
         streams = res.clone()
         call_pre()  # mixes for the first post-map (untimed)
         mhc.mhc_post_project(x, streams, post, comb, hc_fn, out=out, dot_mix=pp_dm, sqrsum=pp_sq, workspace=pp_ws)
@@ -384,11 +383,12 @@ def main():
         calls["mhc_pre_from_dots_backward"] = ("pre_dots_bwd_kernel+pre_bwd_partial_kernel+pre_bwd_final_kernel",
                                                breakdown["pre_dots_bwd_ms"], step_bytes)
     if "post_project_ms" in breakdown:
-        calls["mhc_post_project"] = ("pre_prep_kernel+post_proj_stream_kernel", breakdown["post_project_ms"],
-                                     step_bytes)
+        calls["mhc_post_project"] = ("pre_prep_kernel+post_proj_stream_kernel+pre_mixsum_kernel",
+                                     breakdown["post_project_ms"], step_bytes)
     if "fused_ms" in breakdown:
         calls["mhc_pre_from_dots+mhc_post_project"] = (
-            "pre_dots_kernel+pre_prep_kernel+post_proj_stream_kernel", breakdown["fused_ms"], step_bytes)
+            "pre_collapse_vec8_kernel+pre_prep_kernel+post_proj_stream_kernel+pre_mixsum_kernel", breakdown["fused_ms"],
+            step_bytes)
     traffic = load_traffic(T, H, args.only)
     per_call = {}
     for name, (kern, ms_k, bytes_k) in calls.items():
@@ -417,7 +417,7 @@ def main():
 
     # Sanity figures: the launch floor of the step's kernel count (one-element fills,
     # launched the same way), and what a plain elementwise copy sustains here.
-    nker = {"all": 5, "pre": 4, "post": 1, "post_project": 2, "fused": 3}.get(args.only)
+    nker = {"all": 5, "pre": 4, "post": 1, "post_project": 3, "fused": 4}.get(args.only)
     launch_floor_ms = None
     if nker:
         one = torch.zeros(1, device=dev)
@@ -512,10 +512,9 @@ def step_algorithmic_bytes(only: str, T: int, H: int, sk_logits) -> int:
                             algorithmic_bytes_pre_backward, algorithmic_bytes_pre_bf16, algorithmic_bytes_pre_dots,
                             algorithmic_bytes_pre_dots_backward, algorithmic_bytes_sinkhorn,
                             algorithmic_bytes_sinkhorn_backward, algorithmic_bytes_post_project)
-    S = (H + 127) // 128  # splits of the fused post-map (128-wide h slices)
     per_mode = {
-        "post_project": lambda: algorithmic_bytes_post_project(T, H, S),
-        "fused": lambda: algorithmic_bytes_pre_dots(T, H, splits=S, sqrsum=True) + algorithmic_bytes_post_project(T, H, S),
+        "post_project": lambda: algorithmic_bytes_post_project(T, H),
+        "fused": lambda: algorithmic_bytes_pre_dots(T, H, splits=1, sqrsum=True) + algorithmic_bytes_post_project(T, H),
         "sinkhorn": lambda: algorithmic_bytes_sinkhorn(sk_logits.shape[0]),
         "sinkhorn_bwd": lambda: algorithmic_bytes_sinkhorn_backward(sk_logits.shape[0]),
         "post_bwd": lambda: algorithmic_bytes_post_backward(T, H),

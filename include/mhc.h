@@ -153,7 +153,10 @@ mhc_status mhc_pre_fused_bf16(const uint16_t *res, const uint16_t *hc_fn, const 
  *   rms_eps, pre_eps, sinkhorn_eps, post_mult, num_iters   as in mhc_pre_fused
  *   y [T,H], post [T,4], comb [T,4,4], pre [T,4] (nullable)   outputs, device; no output
  *               may overlap an input or another output
- * No workspace: the streams of a token are read once, into registers, when rows are
+ * No workspace.  The streams of a token are read once.  With num_splits = 1, sqrsum
+ * given and 16-byte rows (H % 8 == 0, res and y 16-byte aligned), the mixes need no
+ * reduction and each 512-wide piece of a token's streams is read by its own wavefront.
+ * Otherwise one workgroup per token holds the streams in registers when rows are
  * 16-byte aligned and H is a multiple of 8 up to 16384; other shapes read them twice.
  */
 mhc_status mhc_pre_from_dots(const float *dot_mix, const float *sqrsum, int32_t num_splits, const uint16_t *res,
@@ -222,30 +225,31 @@ mhc_status mhc_head(const uint16_t *res, const float *hc_fn, const float *hc_sca
 
 /*
  * mhc_post_project -- the post-map fused with the next sublayer's projection
- * (FlashInfer mHC article, sections 3.1-3.3: the pre-map that takes split-K partial dots
- * and sums of squares, dot_mix and sqrsum with num_splits; here the post-map that writes
- * the streams also produces them).  One call computes
+ * (FlashInfer mHC article, sections 3.1-3.3: the pre-map that takes its 24 dots and the
+ * sum of squares from outside, dot_mix and sqrsum; here the post-map that writes the
+ * streams also produces them).  One call computes
  *     out[t][n][h] = bf16( x[t][h] post[t][n] + sum_o res[t][o][h] comb[t][o][n] )
  * exactly as mhc_post does (the same bits), and, over the bf16 `out` it writes, the
- * next pre-map's split partials, one split per 128-wide slice s of h:
- *     dot_mix[s][t][r] = sum_{i, h in slice s} hc_fn_next[r][i*H + h] out[t][i][h]
- *     sqrsum[s][t]     = sum_{i, h in slice s} out[t][i][h]^2
- * (the weights as three exact bf16 terms on MFMA, fp32 accumulation).  Passing them to
- * mhc_pre_from_dots with num_splits = mhc_post_project_splits(H) and res = out runs the
- * next pre-map without reading the streams for its projection.
+ * next pre-map's projection and sum of squares:
+ *     dot_mix[t][r] = sum_{i,h} hc_fn_next[r][i*H + h] out[t][i][h]
+ *     sqrsum[t]     = sum_{i,h} out[t][i][h]^2
+ * (the weights as three exact bf16 terms on MFMA, fp32 partial sums per 128-wide slice
+ * of h, added over the slices in a fixed order).  Passing them to mhc_pre_from_dots
+ * with num_splits = 1 and res = out runs the next pre-map without reading the streams
+ * for its projection.
  *
  *   x [T,H], res [T,4,H] bf16; post [T,4], comb [T,4,4] fp32   as in mhc_post
  *   hc_fn_next [24,4H] fp32   the next pre-map's weights
  *   T >= 0; 8 <= H <= 2097152 with H % 8 == 0; x, res and out 16-byte aligned
  *   out [T,4,H] bf16   output; may equal `res` exactly
- *   dot_mix [S][T][24], sqrsum [S][T] fp32   outputs, S = mhc_post_project_splits(H)
- *   workspace   at least mhc_post_project_workspace_bytes(H) bytes (the next weights
- *               split for the MFMA), 256-byte aligned; contents on entry ignored
+ *   dot_mix [T][24], sqrsum [T] fp32   outputs
+ *   workspace   at least mhc_post_project_workspace_bytes(T, H) bytes (the next weights
+ *               split for the MFMA and the per-slice partial sums), 256-byte aligned;
+ *               contents on entry ignored
  * No output may overlap an input, the workspace or another output, except as stated.
  * T == 0 is a no-op.
  */
-int32_t mhc_post_project_splits(int64_t H); /* ceil(H / 128); 0 for an unsupported H */
-size_t mhc_post_project_workspace_bytes(int64_t H); /* 0 for an unsupported H */
+size_t mhc_post_project_workspace_bytes(int64_t T, int64_t H); /* 0 for T == 0 or an unsupported H */
 mhc_status mhc_post_project(const uint16_t *x, const uint16_t *res, const float *post, const float *comb,
                             const float *hc_fn_next, int64_t T, int64_t H, uint16_t *out, float *dot_mix,
                             float *sqrsum, void *workspace, size_t workspace_bytes, void *stream);

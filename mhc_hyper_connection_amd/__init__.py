@@ -79,9 +79,7 @@ def lib() -> ctypes.CDLL:
     L.mhc_pre_from_dots_backward.argtypes = [P, P, P, P, P, I32, P, P, P, I64, I64, F, F, F, F, F, I32, P, P, P, P,
                                              P, P, SZ, P]
     L.mhc_pre_from_dots_backward.restype = ctypes.c_int
-    L.mhc_post_project_splits.argtypes = [I64]
-    L.mhc_post_project_splits.restype = ctypes.c_int32
-    L.mhc_post_project_workspace_bytes.argtypes = [I64]
+    L.mhc_post_project_workspace_bytes.argtypes = [I64, I64]
     L.mhc_post_project_workspace_bytes.restype = SZ
     L.mhc_post_project.argtypes = [P, P, P, P, P, I64, I64, P, P, P, P, SZ, P]
     L.mhc_post_project.restype = ctypes.c_int
@@ -307,12 +305,8 @@ def mhc_post(x: torch.Tensor, res: torch.Tensor, post: torch.Tensor, comb: torch
     return out
 
 
-def mhc_post_project_splits(H: int) -> int:
-    return int(lib().mhc_post_project_splits(int(H)))
-
-
-def mhc_post_project_workspace_bytes(H: int) -> int:
-    return int(lib().mhc_post_project_workspace_bytes(int(H)))
+def mhc_post_project_workspace_bytes(T: int, H: int) -> int:
+    return int(lib().mhc_post_project_workspace_bytes(int(T), int(H)))
 
 
 def mhc_post_project(x: torch.Tensor, res: torch.Tensor, post: torch.Tensor, comb: torch.Tensor,
@@ -320,10 +314,10 @@ def mhc_post_project(x: torch.Tensor, res: torch.Tensor, post: torch.Tensor, com
                      dot_mix: torch.Tensor | None = None, sqrsum: torch.Tensor | None = None,
                      workspace: torch.Tensor | None = None):
     """The post-map fused with the next sublayer's projection: out as :func:`mhc_post`
-    writes it, and the next pre-map's split partials over out, dot_mix [S, ..., 24] and
-    sqrsum [S, ...] fp32 with S = :func:`mhc_post_project_splits` (H).  Returns
-    (out, dot_mix, sqrsum); pass the partials to :func:`mhc_pre_from_dots` with res=out.
-    H must be a multiple of 8; ``out`` may be ``res``."""
+    writes it, and the next pre-map's dots and sum of squares over out, dot_mix [..., 24]
+    and sqrsum [...] fp32.  Returns (out, dot_mix, sqrsum); pass them to
+    :func:`mhc_pre_from_dots` with res=out.  H must be a multiple of 8; ``out`` may be
+    ``res``."""
     _need(res, "res", torch.bfloat16)
     if res.dim() < 2 or res.shape[-2] != HC:
         raise ValueError(f"residual.shape[-2] / HC must be 4, got {tuple(res.shape)}")
@@ -344,7 +338,6 @@ def mhc_post_project(x: torch.Tensor, res: torch.Tensor, post: torch.Tensor, com
     _need(hc_fn_next, "hc_fn_next", torch.float32)
     if tuple(hc_fn_next.shape) != (MIX, HC * H):
         raise ValueError(f"hc_fn_next must be {(MIX, HC * H)}, got {tuple(hc_fn_next.shape)}")
-    S = mhc_post_project_splits(H)
     dev = res.device
     if out is None:
         out = torch.empty_like(res)
@@ -352,16 +345,16 @@ def mhc_post_project(x: torch.Tensor, res: torch.Tensor, post: torch.Tensor, com
     if out.shape != res.shape:
         raise ValueError("out must have the shape of res")
     if dot_mix is None:
-        dot_mix = torch.empty((S,) + outer + (MIX,), dtype=torch.float32, device=dev)
+        dot_mix = torch.empty(outer + (MIX,), dtype=torch.float32, device=dev)
     _need(dot_mix, "dot_mix", torch.float32)
-    if tuple(dot_mix.shape) != (S,) + outer + (MIX,):
-        raise ValueError(f"dot_mix must be {(S,) + outer + (MIX,)}, got {tuple(dot_mix.shape)}")
+    if tuple(dot_mix.shape) != outer + (MIX,):
+        raise ValueError(f"dot_mix must be {outer + (MIX,)}, got {tuple(dot_mix.shape)}")
     if sqrsum is None:
-        sqrsum = torch.empty((S,) + outer, dtype=torch.float32, device=dev)
+        sqrsum = torch.empty(outer, dtype=torch.float32, device=dev)
     _need(sqrsum, "sqrsum", torch.float32)
-    if tuple(sqrsum.shape) != (S,) + outer:
-        raise ValueError(f"sqrsum must be {(S,) + outer}, got {tuple(sqrsum.shape)}")
-    need = mhc_post_project_workspace_bytes(H)
+    if tuple(sqrsum.shape) != outer:
+        raise ValueError(f"sqrsum must be {outer}, got {tuple(sqrsum.shape)}")
+    need = mhc_post_project_workspace_bytes(T, H)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _same_device(x, res, post, comb, hc_fn_next, out, dot_mix, sqrsum, workspace)
@@ -648,6 +641,6 @@ __all__ = ["mhc_sinkhorn", "mhc_pre_fused", "mhc_pre_fused_bf16", "mhc_expand", 
            "mhc_pre_fused_workspace_bytes", "mhc_pre_from_dots", "mhc_post",
            "mhc_sinkhorn_backward", "mhc_post_backward", "mhc_pre_from_dots_backward",
            "mhc_pre_backward_workspace_bytes", "mhc_pre_fused_backward", "mhc_pre_fused_backward_workspace_bytes",
-           "mhc_post_project", "mhc_post_project_splits", "mhc_post_project_workspace_bytes",
+           "mhc_post_project", "mhc_post_project_workspace_bytes",
            "lib", "abi_version", "status_string", "MHCError", "HC",
            "MIX", "SINKHORN_BWD_MAX_ITERS"]

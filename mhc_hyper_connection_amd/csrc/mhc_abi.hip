@@ -259,20 +259,12 @@ mhc_status mhc_post(const uint16_t *x, const uint16_t *res, const float *post, c
     return launch_status(mhc::launch_post(x, res, post, comb, T, H, out, (hipStream_t)stream, vec8));
 }
 
-int32_t mhc_post_project_splits(int64_t H)
+size_t mhc_post_project_workspace_bytes(int64_t T, int64_t H)
 {
-    if (H < 8 || H % 8 != 0 || H > kPreMaxH) {
+    if (T <= 0 || H < 8 || H % 8 != 0 || H > kPreMaxH || !sizes_ok(T, H)) {
         return 0;
     }
-    return (int32_t)mhc::post_project_splits(H);
-}
-
-size_t mhc_post_project_workspace_bytes(int64_t H)
-{
-    if (H < 8 || H % 8 != 0 || H > kPreMaxH) {
-        return 0;
-    }
-    return mhc::post_project_workspace_bytes(H);
+    return mhc::post_project_workspace_bytes(T, H);
 }
 
 mhc_status mhc_post_project(const uint16_t *x, const uint16_t *res, const float *post, const float *comb,
@@ -291,14 +283,13 @@ mhc_status mhc_post_project(const uint16_t *x, const uint16_t *res, const float 
     if (!aligned16(x) || !aligned16(res) || !aligned16(out)) {
         return MHC_ERROR_INVALID_VALUE;
     }
-    const size_t need = mhc::post_project_workspace_bytes(H);
+    const size_t need = mhc::post_project_workspace_bytes(T, H);
     if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0) {
         return MHC_ERROR_WORKSPACE;
     }
-    const size_t S = (size_t)mhc::post_project_splits(H);
     const size_t res_b = (size_t)T * 4 * H * 2, x_b = (size_t)T * H * 2, fn_b = (size_t)24 * 4 * H * 4;
     const void *outs[4] = {out, dot_mix, sqrsum, workspace};
-    const size_t outn[4] = {res_b, S * T * 24 * 4, S * T * 4, need};
+    const size_t outn[4] = {res_b, (size_t)T * 24 * 4, (size_t)T * 4, need};
     const void *ins[5] = {res, x, post, comb, hc_fn_next};
     const size_t inn[5] = {res_b, x_b, (size_t)T * 16, (size_t)T * 64, fn_b};
     for (int o = 0; o < 4; ++o) {

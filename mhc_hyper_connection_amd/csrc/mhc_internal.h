@@ -49,12 +49,11 @@ hipError_t launch_pre_sums(const uint16_t *res, const uint16_t *dy, const PreGeo
                            void *workspace, hipStream_t stream, bool vec8);
 
 // The post-map fused with the next sublayer's projection (H % 8 == 0, 16-byte aligned
-// rows): out as launch_post writes it, plus the split partials of the next pre-map's
-// dots and sum of squares over out, one split per 128-wide slice of H
-// (dot_mix [post_project_splits(H)][T][24], sqrsum [..][T]).  The workspace holds the
-// next weights split for the MFMA (post_project_workspace_bytes(H)).
-int post_project_splits(int64_t H);
-size_t post_project_workspace_bytes(int64_t H);
+// rows): out as launch_post writes it, plus the next pre-map's 24 dots and sum of
+// squares over out (dot_mix [T][24], sqrsum [T]).  The workspace is laid out as the
+// pre-map's (pre_geometry(T, H)): the next weights split for the MFMA and one token
+// chunk's partial records.
+size_t post_project_workspace_bytes(int64_t T, int64_t H);
 hipError_t launch_post_project(const uint16_t *x, const uint16_t *res, const float *post, const float *comb,
                                const float *hc_fn_next, int64_t T, int64_t H, uint16_t *out, float *dot_mix,
                                float *sqrsum, void *workspace, hipStream_t stream);
@@ -66,11 +65,20 @@ hipError_t launch_expand(const uint16_t *hidden, int64_t T, int64_t H, uint16_t 
 hipError_t launch_head_mean(const uint16_t *res, int64_t T, int64_t H, uint16_t *y, hipStream_t stream, bool vec8);
 
 // Pre-map from external dots (one workgroup per token).  `vec8`: H % 8 == 0 and res/y
-// 16-byte aligned.
+// 16-byte aligned.  One split with a supplied sum of squares and vec8 goes to
+// launch_collapse_dots instead.
 hipError_t launch_pre_dots(const float *dot_mix, const float *sqrsum, int num_splits, const uint16_t *res,
                            const float *hc_scale, const float *hc_base, int64_t T, int64_t H, float k,
                            float rms_eps, float pre_eps, float sinkhorn_eps, float post_mult, int iters,
                            uint16_t *y, float *post, float *comb, float *pre, hipStream_t stream, bool vec8);
+
+// The pre-map's collapse kernel fed external dots: one split, dots [T][24] and the sum
+// of squares [T] supplied, H % 8 == 0 and res/y 16-byte aligned.  One wavefront per
+// (token, 512-wide h tile), the first tile's also writing post, comb and pre.
+hipError_t launch_collapse_dots(const float *dots, const float *sq, const uint16_t *res, const float *hc_scale,
+                                const float *hc_base, int64_t T, int64_t H, float k, float rms_eps, float pre_eps,
+                                float sinkhorn_eps, float post_mult, int iters, uint16_t *y, float *post,
+                                float *comb, float *pre, hipStream_t stream);
 
 // Reverse mode of the standalone Sinkhorn (16 lanes per matrix, LDS history).
 size_t sinkhorn_bwd_lds_bytes(int iters);

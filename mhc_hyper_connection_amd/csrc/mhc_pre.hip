@@ -602,9 +602,10 @@ __global__ __launch_bounds__(kPBlock, 2) void pre_proj_stream_kernel(ProjStreamA
 // pairs: it loads x, the four old streams and the token's coefficients, computes the
 // four new streams with the arithmetic of post_vec8_kernel (so they are the same bits),
 // stores them and writes them to the LDS tile.  The waves then project the tile with the
-// next weights and reduce the slice's 24 dots and sum of squares into split partials of
-// the form the external-dots pre-map takes: dot_mix[slice][t][24], sqrsum[slice][t].
-// The next step's loads are in flight meanwhile.  out may equal res: each pair's old
+// next weights and reduce the slice's 24 dots and sum of squares into the projection's
+// partial records ([64-token tile][slice][25][64], as pre_proj_stream_kernel writes
+// them), which pre_mixsum_kernel sums over the slices.  The next step's loads are in
+// flight meanwhile.  out may equal res: each pair's old
 // streams are read, by the thread that writes them, before they are written.
 struct PostProjArgs {
     const uint16_t *x, *res;
@@ -612,8 +613,8 @@ struct PostProjArgs {
     const u32x4 *frag; // the next weights, split by pre_prep_kernel
     int T, H, nhb, S, tok_per_range;
     uint16_t *out;
-    float *dot_mix; // [S][T][24]
-    float *sqrsum;  // [S][T]
+    float *rec; // [64-token tiles][S][25][64]
+    uint32_t rec_bytes;
 };
 
 constexpr int kPPPairs = kPSTok * (kPSliceH / 8) / kPBlock; // (token, piece) pairs per thread per step (2)
@@ -742,6 +743,7 @@ __global__ __launch_bounds__(kPBlock, 2) void post_proj_stream_kernel(PostProjAr
     if (tb >= te) {
         return;
     }
+    const __amdgpu_buffer_rsrc_t vrec = buf_view_uniform(a.rec, a.rec_bytes);
     PostStepIn in;
     post_proj_load(a, uniform(tb), te, tid, colq, in);
     for (int t0 = tb; t0 < te; t0 += kPSTok) {
@@ -806,12 +808,10 @@ __global__ __launch_bounds__(kPBlock, 2) void post_proj_stream_kernel(PostProjAr
             sqp[w][m * 16 + c][g] = sq[m];
         }
         lds_barrier(); // the partial dots are in LDS; every wave is done with the tile and the coefficients
-        // the slice's split partials of these 32 tokens (past the range: dropped)
-        const int ntok = max(0, min(kPSTok, te - tu));
-        const __amdgpu_buffer_rsrc_t vd =
-            buf_view_uniform(a.dot_mix + ((size_t)slice * a.T + tu) * kMix, (uint32_t)(ntok * kMix * 4));
-        const __amdgpu_buffer_rsrc_t vs =
-            buf_view_uniform(a.sqrsum + (size_t)slice * a.T + tu, (uint32_t)(ntok * 4));
+        // the slice's records of these 32 tokens: entries (tu & 63) .. + 31 of tile tu >> 6
+        // (tokens past the end land in the last tile's unused entries)
+        const uint32_t rec0 =
+            (uint32_t)((((size_t)(tu >> 6) * a.S + slice) * (kRec * kPTok) + (tu & (kPTok - 1))) * 4);
         const int tok = tid & (kPSTok - 1);
 #pragma unroll
         for (int j = 0; j < kMix / (kPBlock / kPSTok); ++j) {
@@ -821,7 +821,8 @@ __global__ __launch_bounds__(kPBlock, 2) void post_proj_stream_kernel(PostProjAr
             for (int ww = 1; ww < kPWaves; ++ww) {
                 v += red[ww][tok][col];
             }
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), vd, (tok * kMix + col) * 4, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), vrec,
+                                                  (int)(rec0 + (uint32_t)(field_of_col(col) * kPTok + tok) * 4u), 0, 0);
         }
         float v = 0.0f;
 #pragma unroll
@@ -831,7 +832,8 @@ __global__ __launch_bounds__(kPBlock, 2) void post_proj_stream_kernel(PostProjAr
                 v += sqp[ww][tok][gg];
             }
         }
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), vs, tid < kPSTok ? tok * 4 : (int)0x80000000, 0, 0);
+        const uint32_t sqo = tid < kPSTok ? rec0 + (uint32_t)(kFSq * kPTok + tok) * 4u : 0x80000000u;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), vrec, (int)sqo, 0, 0);
     }
 }
 
@@ -850,7 +852,8 @@ static void pre_stream_ranges(int Tc, int S, int &ranges, int &tok_per_range)
 // loads in flight), then the four group sums are added in a fixed order.
 constexpr int kSumStride = 32; // floats per token in the sums array (25 used)
 __global__ __launch_bounds__(256) void pre_mixsum_kernel(const float *__restrict__ rec, int T, int S, int nrec,
-                                                         float *__restrict__ sums)
+                                                         float *__restrict__ sums, float *__restrict__ dots,
+                                                         float *__restrict__ sq)
 {
     __shared__ float part[4][kPTok];
     const int tile = blockIdx.x / nrec;
@@ -877,13 +880,25 @@ __global__ __launch_bounds__(256) void pre_mixsum_kernel(const float *__restrict
     __syncthreads();
     const int t = tile * kPTok + threadIdx.x;
     if (threadIdx.x < kPTok && t < T) {
-        sums[(size_t)t * kSumStride + f] =
-            ((part[0][threadIdx.x] + part[1][threadIdx.x]) + part[2][threadIdx.x]) + part[3][threadIdx.x];
+        const float v = ((part[0][threadIdx.x] + part[1][threadIdx.x]) + part[2][threadIdx.x]) + part[3][threadIdx.x];
+        if (dots == nullptr) {
+            sums[(size_t)t * kSumStride + f] = v;
+        } else if (f == kFSq) { // external form: dot_mix [T][24] and sqrsum [T]
+            sq[t] = v;
+        } else {
+            dots[(size_t)t * kMix + (f < kFSq ? f : f - 1)] = v;
+        }
     }
 }
 
 struct MixArgs {
-    const float *sums; // [T][32]: 4 pre logits, sum of squares, 4 post logits, 16 comb logits
+    // Per token `stride` floats: the 4 pre dots at 0..3, the post and comb dots from
+    // `off_post` on; the sum of squares at kFSq, or in `sq` [T] when that is given.
+    // The projection's sums are [T][32] with off_post = 5; external dots [T][24] with
+    // off_post = 4 and `sq`.
+    const float *sums;
+    int stride, off_post;
+    const float *sq;
     const float *hc_scale;
     const float *hc_base;
     float k_denom, rms_eps, pre_eps, sk_eps, post_mult;
@@ -895,8 +910,9 @@ struct MixArgs {
 // pre weights of token t from its sums (wave-uniform).
 __device__ __forceinline__ void token_pre(const MixArgs &m, int t, float *p, float &rstd)
 {
-    const float *d = m.sums + (size_t)t * kSumStride;
-    rstd = 1.0f / sqrtf(d[kFSq] / m.k_denom + m.rms_eps);
+    const float *d = m.sums + (size_t)t * m.stride;
+    const float S = m.sq != nullptr ? m.sq[t] : d[kFSq];
+    rstd = 1.0f / sqrtf(S / m.k_denom + m.rms_eps);
 #pragma unroll
     for (int i = 0; i < kHC; ++i) {
         p[i] = sigmoidf_fast(fmaf(d[i] * rstd, m.hc_scale[0], m.hc_base[i])) + m.pre_eps;
@@ -915,16 +931,16 @@ __device__ __forceinline__ void token_mix_outputs(const MixArgs &m, int t, const
         }
         return;
     }
-    const float *d = m.sums + (size_t)t * kSumStride;
+    const float *d = m.sums + (size_t)t * m.stride;
     float post[kHC];
 #pragma unroll
     for (int i = 0; i < kHC; ++i) {
-        post[i] = sigmoidf_fast(fmaf(d[kFSq + 1 + i] * rstd, m.hc_scale[1], m.hc_base[kHC + i])) * m.post_mult;
+        post[i] = sigmoidf_fast(fmaf(d[m.off_post + i] * rstd, m.hc_scale[1], m.hc_base[kHC + i])) * m.post_mult;
     }
     float P16[kHC * kHC];
 #pragma unroll
     for (int e = 0; e < kHC * kHC; ++e) {
-        P16[e] = fmaf(d[kFSq + 1 + kHC + e] * rstd, m.hc_scale[2], m.hc_base[2 * kHC + e]);
+        P16[e] = fmaf(d[m.off_post + kHC + e] * rstd, m.hc_scale[2], m.hc_base[2 * kHC + e]);
     }
     sinkhorn4x4(P16, m.iters, m.sk_eps);
     if (writer) {
@@ -1055,45 +1071,86 @@ hipError_t launch_pre_split(const float *hc_fn, const PreGeom &g, void *workspac
     return hipGetLastError();
 }
 
-int post_project_splits(int64_t H) { return (int)((H + kPSliceH - 1) / kPSliceH); }
-
-size_t post_project_workspace_bytes(int64_t H)
-{
-    const int64_t nhb = (H + kPHB - 1) / kPHB;
-    return align256((size_t)nhb * kHC * kFragPerHbStream * sizeof(u32x4));
-}
+size_t post_project_workspace_bytes(int64_t T, int64_t H) { return pre_geometry(T, H).total_bytes; }
 
 hipError_t launch_post_project(const uint16_t *x, const uint16_t *res, const float *post, const float *comb,
                                const float *hc_fn_next, int64_t T, int64_t H, uint16_t *out, float *dot_mix,
                                float *sqrsum, void *workspace, hipStream_t stream)
 {
-    PreGeom g{};
-    g.T = T;
-    g.H = H;
-    g.nhb = (int)((H + kPHB - 1) / kPHB);
-    g.slices = post_project_splits(H);
-    g.off_frag = 0;
+    const PreGeom g = pre_geometry(T, H);
     hipError_t e = launch_pre_split(hc_fn_next, g, workspace, stream);
     if (e != hipSuccess) {
         return e;
     }
-    PostProjArgs a{};
-    a.x = x;
-    a.res = res;
-    a.post = post;
-    a.comb = comb;
-    a.frag = reinterpret_cast<const u32x4 *>(workspace);
-    a.T = (int)T;
-    a.H = (int)H;
-    a.nhb = g.nhb;
-    a.S = g.slices;
-    a.out = out;
-    a.dot_mix = dot_mix;
-    a.sqrsum = sqrsum;
-    int ranges = 1;
-    pre_stream_ranges((int)T, g.slices, ranges, a.tok_per_range);
-    post_proj_stream_kernel<<<dim3((unsigned)g.slices, (unsigned)ranges), dim3(kPBlock), 0, stream>>>(a);
-    return hipGetLastError();
+    char *ws = reinterpret_cast<char *>(workspace);
+    for (int64_t c0 = 0; c0 < T; c0 += g.chunk) {
+        const int Tc = (int)(T - c0 < g.chunk ? T - c0 : g.chunk);
+        const int tiles = (Tc + kPTok - 1) / kPTok;
+        PostProjArgs a{};
+        a.x = x + (size_t)c0 * H;
+        a.res = res + (size_t)c0 * kHC * H;
+        a.post = post + (size_t)c0 * kHC;
+        a.comb = comb + (size_t)c0 * kHC * kHC;
+        a.frag = reinterpret_cast<const u32x4 *>(ws + g.off_frag);
+        a.T = Tc;
+        a.H = (int)H;
+        a.nhb = g.nhb;
+        a.S = g.slices;
+        a.out = out + (size_t)c0 * kHC * H;
+        a.rec = reinterpret_cast<float *>(ws + g.off_rec);
+        a.rec_bytes = (uint32_t)((size_t)tiles * g.slices * kRec * kPTok * sizeof(float));
+        int ranges = 1;
+        pre_stream_ranges(Tc, g.slices, ranges, a.tok_per_range);
+        post_proj_stream_kernel<<<dim3((unsigned)g.slices, (unsigned)ranges), dim3(kPBlock), 0, stream>>>(a);
+        e = hipGetLastError();
+        if (e != hipSuccess) {
+            return e;
+        }
+        pre_mixsum_kernel<<<dim3((unsigned)(tiles * kRec)), dim3(256), 0, stream>>>(
+            a.rec, Tc, g.slices, kRec, nullptr, dot_mix + (size_t)c0 * kMix, sqrsum + c0);
+        e = hipGetLastError();
+        if (e != hipSuccess) {
+            return e;
+        }
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_collapse_dots(const float *dots, const float *sq, const uint16_t *res, const float *hc_scale,
+                                const float *hc_base, int64_t T, int64_t H, float k, float rms_eps, float pre_eps,
+                                float sinkhorn_eps, float post_mult, int iters, uint16_t *y, float *post,
+                                float *comb, float *pre, hipStream_t stream)
+{
+    const int64_t htiles = (H + kColVecTile - 1) / kColVecTile;
+    const int64_t max_tok = ((int64_t)1 << 30) / htiles; // waves per launch stay below 2^30
+    for (int64_t c0 = 0; c0 < T; c0 += max_tok) {
+        const int64_t Tc = T - c0 < max_tok ? T - c0 : max_tok;
+        MixArgs mx{};
+        mx.sums = dots + (size_t)c0 * kMix;
+        mx.stride = kMix;
+        mx.off_post = kHC;
+        mx.sq = sq + c0;
+        mx.hc_scale = hc_scale;
+        mx.hc_base = hc_base;
+        mx.k_denom = k;
+        mx.rms_eps = rms_eps;
+        mx.pre_eps = pre_eps;
+        mx.sk_eps = sinkhorn_eps;
+        mx.post_mult = post_mult;
+        mx.iters = iters;
+        mx.head = 0;
+        mx.post = post + (size_t)c0 * kHC;
+        mx.comb = comb + (size_t)c0 * kHC * kHC;
+        mx.pre_out = pre ? pre + (size_t)c0 * kHC : nullptr;
+        const int64_t blocks = (Tc * htiles + kColWaves - 1) / kColWaves;
+        pre_collapse_vec8_kernel<<<dim3((unsigned)blocks), dim3(kColBlock), 0, stream>>>(
+            res + (size_t)c0 * kHC * H, mx, (int)Tc, (int)H, (int)htiles, y + (size_t)c0 * H);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) {
+            return e;
+        }
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_pre_sums(const uint16_t *res, const uint16_t *dy, const PreGeom &g, int64_t c0, int Tc,
@@ -1140,7 +1197,7 @@ hipError_t launch_pre_sums(const uint16_t *res, const uint16_t *dy, const PreGeo
         return e;
     }
     pre_mixsum_kernel<<<dim3((unsigned)(tiles * g.nrec)), dim3(256), 0, stream>>>(
-        a.rec, Tc, g.slices, g.nrec, reinterpret_cast<float *>(ws + g.off_prew));
+        a.rec, Tc, g.slices, g.nrec, reinterpret_cast<float *>(ws + g.off_prew), nullptr, nullptr);
     return hipGetLastError();
 }
 
@@ -1199,13 +1256,16 @@ hipError_t launch_pre(const uint16_t *res, const void *hc_fn, bool fn_bf16, int 
             return e;
         }
         pre_mixsum_kernel<<<dim3((unsigned)(tiles * g.nrec)), dim3(256), 0, stream>>>(a.rec, Tc, g.slices, g.nrec,
-                                                                                    sums);
+                                                                                    sums, nullptr, nullptr);
         e = hipGetLastError();
         if (e != hipSuccess) {
             return e;
         }
         MixArgs mx{};
         mx.sums = sums;
+        mx.stride = kSumStride;
+        mx.off_post = kFSq + 1;
+        mx.sq = nullptr;
         mx.hc_scale = hc_scale;
         mx.hc_base = hc_base;
         mx.k_denom = (float)(kHC * g.H);

@@ -5,7 +5,10 @@
 // mhc_pre_big_fuse_with_prenorm: the sum of squares is computed here from the
 // streams when the caller does not supply it.)
 //
-// One 256-thread workgroup per token.  On the 16-byte path each thread holds its
+// With one split, a supplied sum of squares and 16-byte rows, the per-token mixes need
+// no reduction and the pre-map's collapse kernel runs instead (one wavefront per token
+// and 512-wide h tile, launch_collapse_dots).  Otherwise: one 256-thread workgroup per
+// token.  On the 16-byte path each thread holds its
 // 8-element chunks of all 4 streams in VGPRs, so the streams are read from HBM
 // once: the sum of squares (when needed), the mixes and the collapse all use the
 // same registers.  The whole workgroup sums the dot partials (staged through LDS,
@@ -184,6 +187,11 @@ hipError_t launch_pre_dots(const float *dot_mix, const float *sqrsum, int num_sp
                            float rms_eps, float pre_eps, float sinkhorn_eps, float post_mult, int iters,
                            uint16_t *y, float *post, float *comb, float *pre, hipStream_t stream, bool vec8)
 {
+    if (vec8 && num_splits == 1 && sqrsum != nullptr) {
+        // nothing to reduce per token: the collapse kernel's one-wave-per-tile layout
+        return launch_collapse_dots(dot_mix, sqrsum, res, hc_scale, hc_base, T, H, k, rms_eps, pre_eps,
+                                    sinkhorn_eps, post_mult, iters, y, post, comb, pre, stream);
+    }
     DotsArgs a{};
     a.dot_mix = dot_mix;
     a.sqrsum = sqrsum;

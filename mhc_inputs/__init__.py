@@ -248,11 +248,10 @@ def algorithmic_bytes_post(T: int, H: int) -> int:
     return T * (2 * H + 8 * H + 80 + 8 * H)
 
 
-def algorithmic_bytes_post_project(T: int, H: int, splits: int) -> int:
+def algorithmic_bytes_post_project(T: int, H: int) -> int:
     """The post-map fused with the next projection: the post-map's bytes, the next fp32
-    weights read once, and the split partials written (24 dots and a sum of squares, 100 B
-    per token and split)."""
-    return algorithmic_bytes_post(T, H) + 384 * H + T * splits * 100
+    weights read once, and 24 dots and a sum of squares written (100 B per token)."""
+    return algorithmic_bytes_post(T, H) + 384 * H + T * 100
 
 
 def algorithmic_bytes_pre_dots(T: int, H: int, splits: int = 1, sqrsum: bool = False) -> int:

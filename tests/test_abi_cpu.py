@@ -329,14 +329,14 @@ def test_post_project_validation_invalid(kw):
     assert _pproj(mhc.lib(), **kw) == mhc.MHC_ERROR_INVALID_VALUE
 
 
-def test_post_project_workspace_and_splits():
+def test_post_project_workspace():
     lib = mhc.lib()
-    assert mhc.mhc_post_project_splits(64) == 1 and mhc.mhc_post_project_splits(7168) == 56
-    assert mhc.mhc_post_project_splits(1000) == 8 and mhc.mhc_post_project_splits(60) == 0
-    need = mhc.mhc_post_project_workspace_bytes(64)
-    assert need > 0 and need % 256 == 0 and mhc.mhc_post_project_workspace_bytes(60) == 0
-    # the split weights take 576 bytes per h, as the pre-map's: 288 16-byte fragments per 32 h and stream
-    assert mhc.mhc_post_project_workspace_bytes(7168) == 576 * 7168
+    need = mhc.mhc_post_project_workspace_bytes(8, 64)
+    assert need > 0 and need % 256 == 0
+    assert mhc.mhc_post_project_workspace_bytes(8, 60) == 0 and mhc.mhc_post_project_workspace_bytes(0, 64) == 0
+    # laid out as the pre-map's: the split weights and one token chunk's partial records
+    for T, H in ((8, 64), (3000, 1000), (8192, 7168)):
+        assert mhc.mhc_post_project_workspace_bytes(T, H) == mhc.mhc_pre_fused_workspace_bytes(T, H)
     assert _pproj(lib, wsb=need - 1) == mhc.MHC_ERROR_WORKSPACE
     assert _pproj(lib, ws=None) == mhc.MHC_ERROR_WORKSPACE
     assert _pproj(lib, ws=0x9000000 + 16) == mhc.MHC_ERROR_WORKSPACE

@@ -340,6 +340,24 @@ def test_pre_from_dots_supplied_sum_of_squares_and_k(splits):
     _check_dots(got, ref, f"dots supplied S={splits}")
 
 
+# one split with the sum of squares supplied: the collapse-kernel path when H % 8 == 0
+# (any H, including past the register path's 16384), the workgroup-per-token path otherwise
+ONE_SPLIT_SHAPES = [(16, 256), (5, 8), (33, 2048), (7, 7168), (3, 16384), (4, 16392), (6, 127), (2, 65544),
+                    (70, 96), (1, 1000), (130, 520)]
+
+
+@pytest.mark.parametrize("T,H", ONE_SPLIT_SHAPES)
+def test_pre_from_dots_one_split_supplied_sum_of_squares(T, H):
+    inp = layer_inputs(T, H, cfg=440 + (T * 11 + H) % 67)
+    dm = _dots_inputs(inp, 1, cfg=T * 3 + H)
+    r = bf16_bits_to_f32(inp.res).astype(np.float64)
+    sq = (r * r).sum(axis=(1, 2)).astype(np.float32)[None]
+    got, ref = _run_dots(inp, dm, sq=sq)
+    _check_dots(got, ref, f"one split T={T} H={H}")
+    got, ref = _run_dots(inp, dm, sq=sq, k=3.0 * H, post_mult=1.5, num_iters=7, pre_eps=1e-3)
+    _check_dots(got, ref, f"one split, parameters T={T} H={H}")
+
+
 def test_pre_from_dots_full_size_h7168_sampled():
     """T=8192, H=7168 with one split and the sum of squares computed here (the measured launch)."""
     mhc = _mhc()
