@@ -208,10 +208,12 @@ def main():
     if args.only == "post_bwd":
         call_pre()  # the forward's mixes (untimed)
 
-    if args.only in ("post_project", "fused"):
+    steady_state = args.only == "all" and H % 8 == 0
+    if args.only in ("post_project", "fused") or steady_state:
         # the post-map with the next sublayer's projection fused in (the next weights are
         # hc_fn again); "fused" is the steady-state sublayer step: the pre-map from the
-        # previous post-map's partials, then the post-map updating the streams in place
+        # previous post-map's dots, then the post-map updating the streams in place.  The
+        # default run times it too, after the headline step, as a separate figure.
         pp_dm = torch.empty(T, 24, dtype=torch.float32, device=dev)
         pp_sq = torch.empty(T, dtype=torch.float32, device=dev)
         pp_ws = torch.empty(mhc.mhc_post_project_workspace_bytes(T, H), dtype=torch.uint8, device=dev)
@@ -347,6 +349,22 @@ def main():
 
     eff_gbps = step_bytes / (ms_step * 1e-3) / 1e9
 
+    steady = None
+    if steady_state:
+        # The same layer computed as a steady-state sublayer step: the pre-map (A1, A3-A5)
+        # from the dots and sum of squares the previous post-map produced, then the post-map
+        # (A6) that also computes the next pre-map's projection (A1-A2).  Every row of the
+        # method runs once per step; a model's first sublayer still needs mhc_pre_fused.
+        print("[bench] timing the steady-state sublayer step", file=sys.stderr, flush=True)
+        for _ in range(max(args.warmup, 1)):
+            call_fused()
+        ms_f = timed_reps(call_fused, max(args.steps, 1))
+        eff_f = step_bytes / (ms_f * 1e-3) / 1e9
+        steady = {"calls": "mhc_pre_from_dots (one split, sqrsum supplied) + mhc_post_project (in place)",
+                  "ms_per_step": round(ms_f, 5), "tokens_per_s": round(T / (ms_f * 1e-3), 1),
+                  "effective_GBps": round(eff_f, 1), "hbm_frac": round(eff_f / HBM_PEAK_GBPS, 4),
+                  "algorithmic_bytes": step_bytes}
+
     # Per-call rooflines.  mhc_post and mhc_sinkhorn are one kernel launch each;
     # mhc_pre_fused is four (weight split, projection, slice sums, collapse).
     calls = {}
@@ -478,6 +496,7 @@ def main():
         "launch_floor_ms": None if launch_floor_ms is None else round(launch_floor_ms, 5),
         "kernels_per_step": nker,
         "copy_GBps": copy_gbps,
+        "steady_state": steady,
         "wall_s_timed": round(wall, 3),
     }
     if copy_cal:

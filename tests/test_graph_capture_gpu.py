@@ -126,3 +126,31 @@ def test_reverse_mode_graph_replays_match_eager(T, H):
     eager = [t.clone() for t in step()]
     torch.cuda.synchronize()
     _replays_match(step, eager)
+
+
+@pytest.mark.parametrize("T,H", [(32, 7168), (300, 1000)])
+def test_fused_sublayer_graph_replays_match_eager(T, H):
+    """The steady-state sublayer step under capture: mhc_post_project (the post-map and
+    the next projection), then mhc_pre_from_dots on its dots and sum of squares."""
+    import mhc_hyper_connection_amd as mhc
+    inp = layer_inputs(T, H, cfg=720 + H % 7)
+    res, x = to_dev_bf16(inp.res), to_dev_bf16(inp.x)
+    fn, sc, base = to_dev_f32(inp.hc_fn), to_dev_f32(inp.hc_scale), to_dev_f32(inp.hc_base)
+    _, post0, comb0 = mhc.mhc_pre_fused(res, fn, sc, base)
+    ws = torch.empty(mhc.mhc_post_project_workspace_bytes(T, H), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(res)
+    dm = torch.empty(T, 24, device="cuda")
+    sq = torch.empty(T, device="cuda")
+    y = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
+    post = torch.empty(T, 4, device="cuda")
+    comb = torch.empty(T, 4, 4, device="cuda")
+    pre = torch.empty(T, 4, device="cuda")
+
+    def step():
+        mhc.mhc_post_project(x, res, post0, comb0, fn, out=out, dot_mix=dm, sqrsum=sq, workspace=ws)
+        mhc.mhc_pre_from_dots(dm, out, sc, base, sqrsum=sq, y=y, post=post, comb=comb, pre=pre, return_pre=True)
+        return [out, dm, sq, y, post, comb, pre]
+
+    eager = [t.clone() for t in step()]
+    torch.cuda.synchronize()
+    _replays_match(step, eager)
