@@ -30,8 +30,10 @@ VALU_PEAK_GIPS = 256 * 4 * 2.4 / 4
 
 def sinkhorn_valu_per_wave(iters: int) -> int:
     """VALU instructions one wave of sinkhorn_kernel issues for its 64 matrices, counted
-    in the compiled gfx950 code: 105 outside the iteration loop plus 64 per iteration."""
-    return 105 + 64 * iters
+    in the compiled gfx950 code (iters >= 1): 141 outside the iteration loop (loads,
+    softmax, the final scaling) plus 40 per iteration (4 row and 4 column scales, each
+    one multiply, three FMAs and a reciprocal)."""
+    return 141 + 40 * iters
 
 WORKLOADS = {
     # name: (cfg id, T, H)
@@ -55,7 +57,7 @@ def parse():
                     help="run only one call in the timed loop (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush-mb", type=int, default=-1,
-                    help="overwrite a buffer of this many MiB before every timed rep (0: never); by default 512 "
+                    help="read a buffer of this many MiB before every timed rep (0: never); by default 512 "
                          "when a step moves less than 512 MB, so no rep starts with its data in the caches")
     ap.add_argument("--graph", action="store_true",
                     help="time the steps as replays of one captured HIP graph (no host launch cost)")
@@ -276,14 +278,15 @@ def main():
     flush_buf = None
 
     def timed_reps(fn, n):
-        """As timed(), or with the flush buffer overwritten before each rep (HIP events
-        around each rep only; the flush is not counted)."""
+        """As timed(), or with the flush buffer read before each rep (HIP events around
+        each rep only; the flush is not counted).  A read evicts the caches and leaves
+        clean lines: a fill would leave dirty ones, written back during the timed rep."""
         if flush_buf is None:
             return timed(fn, n)
         torch.cuda.synchronize()
         evs = []
         for _ in range(n):
-            flush_buf.fill_(1)
+            flush_buf.sum()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             fn()
@@ -320,10 +323,12 @@ def main():
     step_bytes = step_algorithmic_bytes(args.only, T, H, sk_logits)
     flush_mb = args.flush_mb if args.flush_mb >= 0 else (512 if step_bytes < 512 * 10 ** 6 else 0)
     if flush_mb > 0:
-        flush_buf = torch.empty(flush_mb << 18, dtype=torch.float32, device=dev)
+        flush_buf = torch.ones(flush_mb << 18, dtype=torch.float32, device=dev)
+        flush_buf.sum()  # write back the fill's own dirty lines before timing
+        torch.cuda.synchronize()
 
     print(f"[bench] timing {args.steps} steps{' (graph replays)' if args.graph else ''}"
-          f"{f', {flush_mb} MiB flushed before each' if flush_mb else ''}", file=sys.stderr, flush=True)
+          f"{f', {flush_mb} MiB read before each' if flush_mb else ''}", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
     ms_step = timed_reps(run_step, args.steps)
     wall = time.perf_counter() - t0
