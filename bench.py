@@ -56,6 +56,9 @@ def parse():
                              "pre_bf16", "expand", "head", "head_mean", "pre_bwd", "post_project", "fused"],
                     help="run only one call in the timed loop (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-steady-state", action="store_true",
+                    help="skip the steady-state sublayer step of the default run (for per-kernel profiles of the "
+                         "headline step alone: both steps launch the collapse kernel)")
     ap.add_argument("--flush-mb", type=int, default=-1,
                     help="read a buffer of this many MiB before every timed rep (0: never); by default 512 "
                          "when a step moves less than 512 MB, so no rep starts with its data in the caches")
@@ -210,7 +213,7 @@ def main():
     if args.only == "post_bwd":
         call_pre()  # the forward's mixes (untimed)
 
-    steady_state = args.only == "all" and H % 8 == 0
+    steady_state = args.only == "all" and H % 8 == 0 and not args.no_steady_state
     if args.only in ("post_project", "fused") or steady_state:
         # the post-map with the next sublayer's projection fused in (the next weights are
         # hc_fn again); "fused" is the steady-state sublayer step: the pre-map from the
