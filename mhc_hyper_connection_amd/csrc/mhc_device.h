@@ -188,13 +188,23 @@ __device__ __forceinline__ int xcd_contiguous(int b, int n)
 // in flight together instead of one after another.  Wave w adds the splits s = w mod 4
 // in increasing order, and the four wave sums combine as (w0 + w1) + (w2 + w3): a fixed
 // order, so the result is deterministic.  stage: 64 * 25 floats, wpart: 4 * 25 floats.
-// Every thread of the workgroup must call it; out is valid after it returns.
+// Every thread of the workgroup must call it.  With one split there is nothing to
+// reduce: threads 0..24 copy their field, and out is valid after the caller's next
+// workgroup barrier; with several, out is valid when it returns.
 constexpr int kSplitStage = 64;
 constexpr int kSplitFields = kMix + 1;
 __device__ __forceinline__ void sum_split_partials(const float *dot_mix, const float *sqrsum, int S, int T, int t,
                                                    float *stage, float *wpart, float *out)
 {
     const int tid = threadIdx.x;
+    if (S == 1) {
+        if (tid < kMix) {
+            out[tid] = dot_mix[(size_t)t * kMix + tid];
+        } else if (tid == kMix && sqrsum != nullptr) {
+            out[kMix] = sqrsum[t];
+        }
+        return;
+    }
     const int w = tid >> 6;
     const int lane = tid & (kWave - 1);
     float acc = 0.0f;
