@@ -60,7 +60,8 @@ mhc_status pre_common(const uint16_t *res, const void *hc_fn, bool fn_bf16, int 
         return MHC_ERROR_INVALID_VALUE;
     }
     const PreGeom g = mhc::pre_geometry(T, H);
-    if (!workspace || workspace_bytes < g.total_bytes || ((uintptr_t)workspace & 255u) != 0) {
+    const size_t ws_need = mhc::pre_fused_workspace_bytes(T, H);
+    if (!workspace || workspace_bytes < ws_need || ((uintptr_t)workspace & 255u) != 0) {
         return MHC_ERROR_WORKSPACE;
     }
     const size_t res_b = (size_t)T * 4 * H * 2, y_b = (size_t)T * H * 2;
@@ -69,7 +70,7 @@ mhc_status pre_common(const uint16_t *res, const void *hc_fn, bool fn_bf16, int 
     const size_t fn_b = (size_t)fn_rows * 4 * H * (fn_bf16 ? 2 : 4);
     // Outputs must not overlap inputs, each other, or the workspace.
     const void *outs[5] = {y, post, comb, pre, workspace};
-    const size_t outn[5] = {y_b, post_b, comb_b, pre_b, g.total_bytes};
+    const size_t outn[5] = {y_b, post_b, comb_b, pre_b, ws_need};
     const void *ins[4] = {res, hc_fn, hc_scale, hc_base};
     const size_t inn[4] = {res_b, fn_b, (size_t)n_scale * 4, (size_t)fn_rows * 4};
     for (int a = 0; a < 5; ++a) {
@@ -135,7 +136,7 @@ size_t mhc_pre_fused_workspace_bytes(int64_t T, int64_t H)
     if (T <= 0 || H <= 0 || H > kPreMaxH || !sizes_ok(T, H)) {
         return 0;
     }
-    return mhc::pre_geometry(T, H).total_bytes;
+    return mhc::pre_fused_workspace_bytes(T, H);
 }
 
 mhc_status mhc_pre_fused(const uint16_t *res, const float *hc_fn, const float *hc_scale, const float *hc_base,

@@ -98,6 +98,26 @@ __device__ __forceinline__ void sinkhorn4x4(float *P, int iters, float eps)
     }
 }
 
+// Eight fp32 values split into three bf16 terms, packed in pairs: v == hi + mid + lo exactly
+// for normal fp32 v (three successive bf16 truncations: 8 + 8 + 8 significant bits).
+__device__ __forceinline__ void split3x8(const float *v, u32x4 &ph, u32x4 &pm, u32x4 &pl)
+{
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t h0 = __float_as_uint(v[2 * q]) & 0xFFFF0000u;
+        const uint32_t h1 = __float_as_uint(v[2 * q + 1]) & 0xFFFF0000u;
+        const float r0 = v[2 * q] - __uint_as_float(h0);
+        const float r1 = v[2 * q + 1] - __uint_as_float(h1);
+        const uint32_t m0 = __float_as_uint(r0) & 0xFFFF0000u;
+        const uint32_t m1 = __float_as_uint(r1) & 0xFFFF0000u;
+        const float l0 = r0 - __uint_as_float(m0);
+        const float l1 = r1 - __uint_as_float(m1);
+        ph[q] = (h0 >> 16) | h1;
+        pm[q] = (m0 >> 16) | m1;
+        pl[q] = (__float_as_uint(l0) >> 16) | (__float_as_uint(l1) & 0xFFFF0000u);
+    }
+}
+
 // Lane permutations within a 16-lane DPP row.  Every source lane exists for these
 // patterns, so bound_ctrl (zero for a missing source) never applies; setting it and
 // leaving `old` undefined lets the compiler fold the move into the consuming add.

@@ -39,6 +39,21 @@ hipError_t launch_pre(const uint16_t *res, const void *hc_fn, bool fn_bf16, int 
                       float post_mult, int iters, bool head, uint16_t *y, float *post, float *comb, float *pre,
                       void *workspace, hipStream_t stream, bool vec8);
 
+// The pre-map with one read of the streams: on each of the 8 XCDs a group of 32
+// workgroups splits K, holds 16-token steps of the streams in LDS and exchanges partial
+// sums through the XCD's L2 (mhc_pre_coop.hip).  Usable for 16-byte rows with
+// 2 <= ceil(ceil(H / 32) / 32) <= 8 (1024 < H <= 8192) and T >= 1024, on a 256-CU gfx950.
+// Its workspace is a ring of exchange records, pre_coop_workspace_bytes(H) bytes.
+size_t pre_coop_workspace_bytes(int64_t H);
+bool pre_coop_shape_ok(int64_t T, int64_t H); // the shape alone (no device or alignment check)
+bool pre_coop_usable(int64_t T, int64_t H, bool vec8);
+hipError_t launch_pre_coop(const uint16_t *res, const void *hc_fn, bool fn_bf16, int fn_rows, const float *hc_scale,
+                           const float *hc_base, int64_t T, int64_t H, float rms_eps, float pre_eps,
+                           float sinkhorn_eps, float post_mult, int iters, bool head, uint16_t *y, float *post,
+                           float *comb, float *pre, void *workspace, hipStream_t stream);
+// Workspace of the pre-map entry points: enough for either form.
+size_t pre_fused_workspace_bytes(int64_t T, int64_t H);
+
 // The pre-map's first stages on their own: the weight split (once), then for the token
 // chunk [c0, c0 + Tc) the projection and the slice sums, which leave the per-token
 // fields in the workspace at g.off_prew ([Tc][32] fp32: pre dots 0..3, the sum of

@@ -1,10 +1,12 @@
-// mhc_pre.hip -- the mHC pre-map on gfx950.
+// mhc_pre.hip -- the mHC pre-map on gfx950: the two-pass form and the dispatch.
 //
 // ("FlashInfer mHC 模块深度解析", sections 3.4 and 5.2; metrale
 // hyper_connection_dispatch.rs, hc_pre_site; metrale glm5next_mhc.rs, the
 // hc_mix / hc_finish split.)
 //
-// Four kernels on one stream:
+// launch_pre takes the one-read form (mhc_pre_coop.hip) when the shape and the
+// device allow it: 16-byte rows, 1024 < H <= 8192, T >= 1024, a 256-CU gfx950.
+// Everything else runs the two-pass form here, four kernels on one stream:
 //
 //  1. pre_prep_kernel -- splits every fp32 weight of hc_fn exactly into three
 //     bf16 terms hi + mid + lo (successive truncations: 8 + 8 + 8 significant
@@ -26,10 +28,7 @@
 //     y = sum_i pre_i * res_i with 16-byte loads.  The wavefront of each
 //     token's first tile also computes post and the 4x4 Sinkhorn of comb.
 //
-// The streams are read twice (passes 2 and 4).  Reading them once needs the
-// collapse to wait for a cross-workgroup reduction while the data sits on
-// chip; a CU returns loads in order, so that reduction's round trips queue
-// behind the CU's own stream loads and cost more than the second read.
+// The two-pass form reads the streams twice (passes 2 and 4).
 #include "mhc_device.h"
 #include "mhc_internal.h"
 
@@ -56,25 +55,6 @@ constexpr int kColVecTile = kWave * 8;
 // field of the 64 tokens is 256 contiguous bytes.
 constexpr int kFSq = kHC;
 __device__ __forceinline__ int field_of_col(int col) { return col < kHC ? col : col + 1; }
-
-// v == hi + mid + lo exactly for normal fp32 v (three successive bf16 truncations).
-__device__ __forceinline__ void split3x8(const float *v, u32x4 &ph, u32x4 &pm, u32x4 &pl)
-{
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const uint32_t h0 = __float_as_uint(v[2 * q]) & 0xFFFF0000u;
-        const uint32_t h1 = __float_as_uint(v[2 * q + 1]) & 0xFFFF0000u;
-        const float r0 = v[2 * q] - __uint_as_float(h0);
-        const float r1 = v[2 * q + 1] - __uint_as_float(h1);
-        const uint32_t m0 = __float_as_uint(r0) & 0xFFFF0000u;
-        const uint32_t m1 = __float_as_uint(r1) & 0xFFFF0000u;
-        const float l0 = r0 - __uint_as_float(m0);
-        const float l1 = r1 - __uint_as_float(m1);
-        ph[q] = (h0 >> 16) | h1;
-        pm[q] = (m0 >> 16) | m1;
-        pl[q] = (__float_as_uint(l0) >> 16) | (__float_as_uint(l1) & 0xFFFF0000u);
-    }
-}
 
 // One thread per (h block, stream, operand slot).  Slot < 64: column tile 0,
 // MFMA lane = slot (weight row = slot % 16).  Slot >= 64: column tile 1, rows
@@ -1073,6 +1053,13 @@ hipError_t launch_pre_split(const float *hc_fn, const PreGeom &g, void *workspac
 
 size_t post_project_workspace_bytes(int64_t T, int64_t H) { return pre_geometry(T, H).total_bytes; }
 
+size_t pre_fused_workspace_bytes(int64_t T, int64_t H)
+{
+    const size_t two_pass = pre_geometry(T, H).total_bytes;
+    const size_t coop = pre_coop_shape_ok(T, H) ? pre_coop_workspace_bytes(H) : 0;
+    return coop > two_pass ? coop : two_pass;
+}
+
 hipError_t launch_post_project(const uint16_t *x, const uint16_t *res, const float *post, const float *comb,
                                const float *hc_fn_next, int64_t T, int64_t H, uint16_t *out, float *dot_mix,
                                float *sqrsum, void *workspace, hipStream_t stream)
@@ -1206,6 +1193,10 @@ hipError_t launch_pre(const uint16_t *res, const void *hc_fn, bool fn_bf16, int 
                       float post_mult, int iters, bool head, uint16_t *y, float *post, float *comb, float *pre,
                       void *workspace, hipStream_t stream, bool vec8)
 {
+    if (pre_coop_usable(g.T, g.H, vec8)) {
+        return launch_pre_coop(res, hc_fn, fn_bf16, fn_rows, hc_scale, hc_base, g.T, g.H, rms_eps, pre_eps,
+                               sinkhorn_eps, post_mult, iters, head, y, post, comb, pre, workspace, stream);
+    }
     char *ws = reinterpret_cast<char *>(workspace);
     u32x4 *frag = reinterpret_cast<u32x4 *>(ws + g.off_frag);
     const int H = (int)g.H;

@@ -1,0 +1,735 @@
+// mhc_pre_coop.hip -- the mHC pre-map with one read of the streams (gfx950).
+//
+// ("FlashInfer mHC 模块深度解析", section 3.4: per token, the RMS statistic and the
+// projection, then the mixes and the Sinkhorn, then the collapse, from one read of the
+// residual; section 5.2 for the arithmetic.)
+//
+// A token's pre weights need all 4H products of the projection before its collapse can
+// start, and no workgroup can hold the 24 x 4H weights, so the reduction over K is
+// split across workgroups and the token's streams are held on chip until it is done.
+//
+//  * One group of 32 workgroups per XCD (workgroup b runs on XCD b mod 8 under the
+//    hardware's round-robin dispatch; the grid is 256 workgroups, one per CU).  Workgroup
+//    s of a group owns a slice of W x 32 h across the four streams and keeps that slice of
+//    the weights in VGPRs, split exactly into three bf16 terms for the MFMA.
+//  * The group walks its tokens in 16-token steps (group x takes steps x, x + 8, ...).
+//    A step's slice of the streams is loaded two steps ahead, written into a ring of LDS
+//    slots, projected with v_mfma_f32_16x16x32_bf16 (the sum of squares rides on
+//    v_dot2_f32_bf16), and reduced over the workgroup's waves into one record: 24 partial
+//    dots and the partial sum of squares of its 16 tokens.
+//  * Records go through the XCD's L2 as 16-byte chunks of three values and a tag that
+//    names the call (its dispatch id) and the step.  L iterations after producing a step,
+//    every workgroup loads the pre dots and the sums of squares of that step from all 32
+//    slices (device-scope loads: they miss the CU's L1), sums them over the slices in a
+//    fixed order, forms rstd and the pre weights, and collapses its slice of the step
+//    from the LDS ring: the streams are read from HBM once.  A chunk whose tag does not
+//    match has not landed yet and is loaded again (bounded).
+//  * Each token's post weights and Sinkhorn are finished by one workgroup: workgroup s
+//    takes token s mod 16 of the steps whose parity is s / 16.
+//
+// Reduction orders are fixed (waves in order, slices by a butterfly over 32 lanes), so a
+// result does not depend on timing.  Every iteration issues the same memory operations
+// (empty buffer views stand for steps outside the range), which keeps the compiler's
+// in-order wait counts exact, so the loads of the next two steps stay in flight.
+#include "mhc_device.h"
+#include "mhc_internal.h"
+
+#include <string.h>
+
+namespace mhc {
+
+namespace {
+
+extern "C" __device__ uint64_t mhc_coop_dispatch_id() __asm("llvm.amdgcn.dispatch.id");
+
+constexpr int kQTok = 16;                                           // tokens per step
+constexpr int kQGroups = 8;                                         // one group per XCD
+constexpr int kQSlices = 32;                                        // workgroups per group
+constexpr int kQUrgVals = 5 * kQTok;                                // pre dots 0..3 and the sum of squares
+constexpr int kQUrgChunks = (kQUrgVals + 2) / 3;                    // 27
+constexpr int kQDefFields = kMix - kHC;                             // post and comb dots
+constexpr int kQDefChunks = (kQDefFields + 2) / 3;                  // 7
+constexpr int kQChunks = kQUrgChunks + kQTok * kQDefChunks;         // chunks of one record (139)
+constexpr int kQRedStride = 28;                                     // 24 dots + 4 lane-group sums of squares
+constexpr int kQMaxRetry = 1 << 14;                                 // reloads of a step's records before giving up
+constexpr uint32_t kOob = 0x80000000u;
+constexpr int64_t kCoopMinTokens = 1024; // below this the pipeline's fill and drain dominate
+
+struct CoopArgs {
+    const uint16_t *res;
+    const void *hc_fn;
+    const float *hc_scale, *hc_base;
+    int T, H, nhb, fn_rows;
+    int L, R, RR; // collapse lag in iterations, LDS ring slots, record ring slots
+    float inv_k, rms_eps, pre_eps, sk_eps, post_mult; // inv_k = 1 / (4H)
+    int iters, head;
+    uint16_t *y;
+    float *post, *comb, *pre;
+    u32x4 *rec;
+    uint32_t rec_bytes;
+};
+
+__device__ __forceinline__ uint32_t coop_key()
+{
+    uint64_t z = mhc_coop_dispatch_id() + 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(z >> 32));
+}
+// Distinct steps of one call get distinct tags (an odd multiplier is a bijection).
+__device__ __forceinline__ uint32_t coop_tag(uint32_t key, int gs) { return key ^ ((uint32_t)gs * 0x85EBCA6Bu + 1u); }
+
+__device__ __forceinline__ float weight_elem(const float *w, uint32_t i, __amdgpu_buffer_rsrc_t v)
+{
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(v, (int)(i * 4u), 0, 0));
+}
+__device__ __forceinline__ float weight_elem(const uint16_t *w, uint32_t i, __amdgpu_buffer_rsrc_t v)
+{
+    return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(v, (int)(i * 2u), 0, 0));
+}
+
+// Sum of v over the 32 lanes of each half-wave, on DPP moves: within each quad (lanes
+// xor 1, 2), the two quads of each 8-lane half row (mirror), the two halves of each
+// 16-lane row (mirror), then row 0 into row 1 and row 2 into row 3 (row_bcast:15).  The
+// total of lanes 0..31 lands in lanes 16..31 and that of lanes 32..63 in lanes 48..63;
+// the order of the additions is fixed.
+__device__ __forceinline__ float half_sum(float v)
+{
+    v += dpp_perm<0xB1>(v);  // quad_perm [1,0,3,2]
+    v += dpp_perm<0x4E>(v);  // quad_perm [2,3,0,1]
+    v += dpp_perm<0x141>(v); // row_half_mirror
+    v += dpp_perm<0x140>(v); // row_mirror
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+}
+constexpr int kHalfSumLane = 16; // the lane of each half-wave (mod 32) that holds its sum
+
+// rstd and sigmoid on the hardware reciprocal square root and reciprocal (1 ulp each, far
+// inside the 1e-5 tolerance of the mixes); they are for this kernel's per-step path.
+__device__ __forceinline__ float rstd_of(float S, float inv_k, float eps) { return __builtin_amdgcn_rsqf(fmaf(S, inv_k, eps)); }
+__device__ __forceinline__ float sigmoid_rcp(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
+
+// Sum over the four 16-lane rows of the wave, same bits in every lane: rows (0 + 1) and
+// (2 + 3) by v_permlane16_swap, then the two halves by v_permlane32_swap.
+__device__ __forceinline__ float rows_sum(float v)
+{
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
+template <int W, typename WT>
+__global__ __launch_bounds__(W * 64) void pre_coop_kernel(CoopArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    constexpr int kTh = W * 64;
+    constexpr int kPieces = 4 * W;        // 16-byte pieces of one stream row of the slice
+    constexpr int kRowB = 64 * W;         // bytes of one stream row of the slice
+    constexpr int kTokB = 4 * kRowB + 16; // token pitch in a slot: (16W + 1) x 16 bytes
+    constexpr int kSlotB = kQTok * kTokB;
+    constexpr int kHW = 2 * W;            // half-waves
+    constexpr int kUR = (kQUrgChunks + kHW - 1) / kHW;
+    constexpr int kDR = (kQDefChunks + kHW - 1) / kHW;
+    constexpr int kRS = (kQChunks + kTh - 1) / kTh;
+
+    const int R = a.R, RR = a.RR, L = a.L;
+    // the wave that computes the pre weights and this workgroup's token: wave 3 sits alone on
+    // its SIMD when W < 8 (waves go to SIMDs round robin)
+    constexpr int kAux = W >= 4 ? 3 : W - 1;
+    unsigned char *ring = smem;
+    float *red = reinterpret_cast<float *>(smem + R * kSlotB); // [W][16][28]
+    float *sums = red + W * kQTok * kQRedStride;               // [81]: value f * 16 + token
+    float *dsum = sums + 96;                                   // [21]: the designated token's post and comb dots
+    float *prel = dsum + 32;                                   // [16][4]
+    int *badf = reinterpret_cast<int *>(prel + 64);
+    float *dummy = prel + 64 + 4; // [64]: writes of lanes with nothing to write (no divergent branches)
+
+    const int tid = threadIdx.x;
+    const int w = uniform(tid >> 6);
+    const int lane = tid & (kWave - 1);
+    const int g = lane >> 4, c = lane & 15;
+    const int hw = tid >> 5, sl = tid & 31;
+    const int x = (int)blockIdx.x & (kQGroups - 1);
+    const int s = (int)blockIdx.x >> 3;
+    const int T = a.T, H = a.H;
+    const int steps_total = (T + kQTok - 1) / kQTok;
+    const int nst = steps_total > x ? (steps_total - x + kQGroups - 1) / kQGroups : 0;
+    if (nst == 0) {
+        return; // the whole group
+    }
+    const uint32_t key = coop_key();
+    const float s0 = a.hc_scale[0];
+    const float s1 = a.head ? 0.0f : a.hc_scale[1];
+    const float s2 = a.head ? 0.0f : a.hc_scale[2];
+
+    // ---- this wave's slice of the weights: 32 h of the 4 streams, rows 0..23, as three
+    // bf16 terms in the MFMA B layout (lane (g, c): k = hb*32 + 8g .. +8 of stream i).  Column
+    // tile 0 holds rows 0..15 (lane c: row c), one operand per term.  Rows 16..23 take two
+    // operands: lanes c < 8 hold the hi term of row 16 + c and lanes c >= 8 the mid term of
+    // row 8 + c in the first, lanes c < 8 the lo term of row 16 + c in the second; the
+    // columns c and c + 8 of the first are added after the products.
+    const int hb = s * W + w;
+    u32x4 b0[kHC][3], b1[kHC][2];
+    {
+        const __amdgpu_buffer_rsrc_t vw =
+            buf_view_uniform(a.hc_fn, (uint32_t)((size_t)a.fn_rows * kHC * H * sizeof(WT)));
+        const int h = hb * 32 + 8 * g;
+        const bool hok = hb < a.nhb && h < H;
+        const WT *wt = reinterpret_cast<const WT *>(a.hc_fn);
+        const int r1 = 16 + (c & 7);
+#pragma unroll
+        for (int i = 0; i < kHC; ++i) {
+            float v0[8], v1[8];
+            const uint32_t i0 = hok ? (uint32_t)c * kHC * H + (uint32_t)i * H + h : kOob / 4;
+            const uint32_t i1 = hok ? (uint32_t)r1 * kHC * H + (uint32_t)i * H + h : kOob / 4;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                v0[e] = weight_elem(wt, i0 + e, vw);
+                v1[e] = weight_elem(wt, i1 + e, vw);
+            }
+            split3x8(v0, b0[i][0], b0[i][1], b0[i][2]);
+            u32x4 hi, mid, lo;
+            split3x8(v1, hi, mid, lo);
+            b1[i][0] = c < 8 ? hi : mid;
+            b1[i][1] = c < 8 ? lo : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    // hc_base per lane: the pre entry lane / 16; with e = lane mod 16 the comb entry e and the
+    // post entry e mod 4 (the designated token's row of lanes)
+    const float bpre = a.hc_base[lane >> 4]; // lane = 16 k + token computes pre weight k
+    const float bcomb = a.head ? 0.0f : a.hc_base[2 * kHC + (lane & 15)];
+    const float bpost = a.head ? 0.0f : a.hc_base[kHC + (lane & 3)];
+
+    // ---- geometry of this thread's loads and of the record chunks
+    const int piece = tid % kPieces;
+    const int prow = tid / kPieces; // 0..15: rows prow + 16k of a step (row = token * 4 + stream)
+    const int hq = s * (32 * W) + piece * 8;
+    const uint32_t colq = hq < H ? (uint32_t)hq * 2u : kOob;
+    const __amdgpu_buffer_rsrc_t vrec = buf_view_uniform(a.rec, a.rec_bytes);
+    const uint32_t def0 = (uint32_t)kQGroups * RR * kQUrgChunks * kQSlices; // first deferred chunk
+    const int td = s & 15;                                                  // the token this workgroup finishes
+    auto urg_chunk = [&](int q, int k, int sli) -> uint32_t {
+        return (((uint32_t)(x * RR + q) * kQUrgChunks + k) * kQSlices + sli) * 16u;
+    };
+    auto def_chunk = [&](int q, int tok, int k, int sli) -> uint32_t {
+        return (def0 + (((uint32_t)(x * RR + q) * kQTok + tok) * kQDefChunks + k) * kQSlices + sli) * 16u;
+    };
+    auto wrap = [](int v, int n) { return v >= n ? v - n : v; }; // v in [0, 2n)
+    auto designated = [&](int j) { return j >= 0 && j < nst && (s >> 4) == (j & 1); };
+
+    auto load_step = [&](int j, u32x4(&d)[4]) {
+        const int t0 = (j * kQGroups + x) * kQTok;
+        const int ntok = (j >= 0 && j < nst) ? min(kQTok, T - t0) : 0;
+        const __amdgpu_buffer_rsrc_t v = buf_view_uniform(a.res + (size_t)(ntok > 0 ? t0 : 0) * kHC * H,
+                                                          (uint32_t)((size_t)ntok * kHC * H * sizeof(uint16_t)));
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int row = prow + 16 * k;
+            d[k] = __builtin_bit_cast(u32x4,
+                                      __builtin_amdgcn_raw_buffer_load_b128(v, (int)((uint32_t)(row * H) * 2u + colq), 0, 0));
+        }
+    };
+    // the records of step j this thread reads: chunk k of slice sl for its half-wave's k
+    auto load_recs = [&](int j, int q, u32x4(&ru)[kUR], u32x4(&rd)[kDR]) {
+        const bool ok = j >= 0 && j < nst;
+#pragma unroll
+        for (int r = 0; r < kUR; ++r) {
+            const int k = r * kHW + hw;
+            const uint32_t o = ok && k < kQUrgChunks ? urg_chunk(q, k, sl) : kOob;
+            ru[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrec, (int)o, 0, 16));
+        }
+        const bool dz = designated(j);
+#pragma unroll
+        for (int r = 0; r < kDR; ++r) {
+            const int k = r * kHW + hw;
+            const uint32_t o = dz && k < kQDefChunks ? def_chunk(q, td, k, sl) : kOob;
+            rd[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrec, (int)o, 0, 16));
+        }
+    };
+    // tags of the loaded records of step j (0 if they all match), and their slice sums into LDS
+    auto take_recs = [&](int j, const u32x4(&ru)[kUR], const u32x4(&rd)[kDR], int *flag) {
+        const bool ok = j >= 0 && j < nst;
+        const uint32_t tag = coop_tag(key, j * kQGroups + x);
+        const bool dz = designated(j);
+        int bad = 0;
+#pragma unroll
+        for (int r = 0; r < kUR; ++r) {
+            const int k = r * kHW + hw;
+            if (ok && k < kQUrgChunks && ru[r][3] != tag) {
+                bad = 1;
+            }
+            float v0 = half_sum(__uint_as_float(ru[r][0]));
+            float v1 = half_sum(__uint_as_float(ru[r][1]));
+            float v2 = half_sum(__uint_as_float(ru[r][2]));
+            float *dst = sl == kHalfSumLane && k < kQUrgChunks ? sums + 3 * k : dummy + (lane & 0x3C);
+            dst[0] = v0;
+            dst[1] = v1;
+            dst[2] = v2;
+        }
+#pragma unroll
+        for (int r = 0; r < kDR; ++r) {
+            const int k = r * kHW + hw;
+            if (dz && k < kQDefChunks && rd[r][3] != tag) {
+                bad = 1;
+            }
+            float v0 = half_sum(__uint_as_float(rd[r][0]));
+            float v1 = half_sum(__uint_as_float(rd[r][1]));
+            float v2 = half_sum(__uint_as_float(rd[r][2]));
+            float *dst = sl == kHalfSumLane && k < kQDefChunks ? dsum + 3 * k : dummy + (lane & 0x3C);
+            dst[0] = v0;
+            dst[1] = v1;
+            dst[2] = v2;
+        }
+        if (bad) {
+            *flag = 1;
+        }
+    };
+
+    // The record chunks this thread writes: chunk ch = tid + rs * kTh of kQChunks (27 urgent
+    // chunks: value 3ch + e is field (3ch + e) / 16 of token (3ch + e) mod 16, field 4 being
+    // the sum of squares in column 24; then 16 tokens x 7 chunks of the 20 post and comb
+    // dots, columns 4..23).  rc_off: the value's offset in a wave's [16][28] partials;
+    // rc_base + q * rc_qstride: the chunk's byte offset in record slot q.
+    int rc_off[kRS][3];
+    int rc_valid[kRS];
+    uint32_t rc_base[kRS], rc_qstride[kRS];
+#pragma unroll
+    for (int rs = 0; rs < kRS; ++rs) {
+        const int ch = tid + rs * kTh;
+        rc_valid[rs] = 0;
+        rc_base[rs] = kOob;
+        rc_qstride[rs] = 0;
+#pragma unroll
+        for (int e = 0; e < 3; ++e) {
+            rc_off[rs][e] = 0;
+        }
+        if (ch < kQUrgChunks) {
+#pragma unroll
+            for (int e = 0; e < 3; ++e) {
+                const int val = 3 * ch + e;
+                if (val < kQUrgVals) {
+                    const int f = val >> 4, tok = val & 15;
+                    rc_off[rs][e] = tok * kQRedStride + (f < kHC ? f : kMix);
+                    rc_valid[rs] |= 1 << e;
+                }
+            }
+            rc_base[rs] = urg_chunk(0, ch, s);
+            rc_qstride[rs] = (uint32_t)kQUrgChunks * kQSlices * 16u;
+        } else if (ch < kQChunks) {
+            const int dch = ch - kQUrgChunks;
+            const int tok = dch / kQDefChunks, k = dch - kQDefChunks * (dch / kQDefChunks);
+#pragma unroll
+            for (int e = 0; e < 3; ++e) {
+                const int f = 3 * k + e;
+                if (f < kQDefFields) {
+                    rc_off[rs][e] = tok * kQRedStride + kHC + f;
+                    rc_valid[rs] |= 1 << e;
+                }
+            }
+            rc_base[rs] = def_chunk(0, tok, k, s);
+            rc_qstride[rs] = (uint32_t)kQTok * kQDefChunks * kQSlices * 16u;
+        }
+    }
+
+    // ---- one iteration: produce step i, collapse step i - L
+    // ri = i mod R (the LDS slot of step i), qi = i mod RR (its record slot), kept as counters.
+    // One iteration: sum the records of step cu = i - L; write step i to its slot; projection
+    // of step i and collapse of step cu - 1 (from registers, so that its arithmetic overlaps
+    // the products); the record of step i; step cu's slot and pre weights into registers.
+    auto iteration = [&](int i, int ri, int qi, u32x4(&cur)[4], u32x4(&ru)[kUR], u32x4(&rd)[kDR],
+                         u32x4(&hold)[kHC], float(&holdp)[kHC]) {
+        const int cu = i - L;
+        const int cc = cu - 1;                    // collapsed this iteration
+        const int rcs = wrap(ri + 2, R);          // slot of step cu: i - L = i + 2 (mod R = L + 2)
+        const int qc = wrap(qi + RR - L, RR);     // record slot of step cu
+        const int ql = wrap(qi + RR - L + 1, RR); // record slot of step cu + 1
+        const bool cu_ok = cu >= 0 && cu < nst;
+        const bool p_ok = i >= 0 && i < nst;
+        // records of step cu (loaded last iteration): check and sum over the slices.  The
+        // flag alternates with the iteration's parity, so its reset after B2 cannot race
+        // with the next iteration's writes.
+        int *bf = badf + (i & 1);
+        take_recs(cu, ru, rd, bf);
+        // step i into its slot
+        unsigned char *slot = ring + ri * kSlotB;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int row = prow + 16 * k;
+            *reinterpret_cast<u32x4 *>(slot + (row >> 2) * kTokB + (row & 3) * kRowB + piece * 16) = cur[k];
+        }
+        // the next loads: records of step cu + 1 first (they return before the streams)
+        load_recs(cu + 1, ql, ru, rd);
+        load_step(i + 2, cur);
+        lds_barrier(); // B1: slot i and the slice sums are in LDS
+
+        const int bad_now = *bf; // read before the products; tested after them
+        // projection of step i (this wave's 32 h, all 4 streams): streams 0, 1 and 2, 3 in two
+        // chains per column tile; a step outside the range projects zeros and stores nothing
+        {
+            u32x4 A[kHC];
+#pragma unroll
+            for (int st = 0; st < kHC; ++st) {
+                A[st] = *reinterpret_cast<const u32x4 *>(slot + c * kTokB + st * kRowB + (4 * w + g) * 16);
+            }
+            f32x4 acc0[2], acc1[2], acc2[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                acc0[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+                acc1[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+                acc2[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+            float sq = 0.0f;
+#pragma unroll
+            for (int st = 0; st < kHC; ++st) {
+                const int u = st >> 1;
+                const bf16x8 Ab = __builtin_bit_cast(bf16x8, A[st]);
+#pragma unroll
+                for (int t3 = 0; t3 < 3; ++t3) {
+                    acc0[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ab, __builtin_bit_cast(bf16x8, b0[st][t3]), acc0[u], 0, 0, 0);
+                }
+                acc1[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ab, __builtin_bit_cast(bf16x8, b1[st][0]), acc1[u], 0, 0, 0);
+                acc2[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ab, __builtin_bit_cast(bf16x8, b1[st][1]), acc2[u], 0, 0, 0);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    // a scalar copy first: hipcc (clang 22) miscompiles __builtin_bit_cast applied
+                    // directly to an ext_vector element (it reads element 0 for every k)
+                    const uint32_t wk = A[st][k];
+                    const bf16x2 pr = __builtin_bit_cast(bf16x2, wk);
+                    sq = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, sq, false);
+                }
+            }
+            // the token's sum of squares over the 4 lane groups: (g0 + g1) + (g2 + g3)
+            sq = rows_sum(sq);
+            float *rw = red + w * (kQTok * kQRedStride);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float d0 = acc0[0][k] + acc0[1][k];
+                // rows 16..23: (hi + mid) + lo, the mid partial coming from column c + 8
+                const float p1 = acc1[0][k] + acc1[1][k];
+                const float d1 = (p1 + dpp_row_ror8(p1)) + (acc2[0][k] + acc2[1][k]);
+                rw[(4 * g + k) * kQRedStride + c] = d0;
+                *(c < 8 ? rw + (4 * g + k) * kQRedStride + 16 + c : dummy + lane) = d1;
+            }
+            rw[c * kQRedStride + kMix] = sq; // the same bits from all 4 lane groups
+        }
+        // collapse of step cc: y = sum_i pre_i * res_i for this thread's (token, piece)
+        {
+            u32x4 yw;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float lo = bf16_lo(hold[0][q]) * holdp[0];
+                float hi = bf16_hi(hold[0][q]) * holdp[0];
+#pragma unroll
+                for (int st = 1; st < kHC; ++st) {
+                    lo = fmaf(bf16_lo(hold[st][q]), holdp[st], lo);
+                    hi = fmaf(bf16_hi(hold[st][q]), holdp[st], hi);
+                }
+                yw[q] = pack_bf16x2(lo, hi);
+            }
+            const bool cc_ok = cc >= 0 && cc < nst;
+            const int t0 = (cc * kQGroups + x) * kQTok;
+            const int ntok = cc_ok ? min(kQTok, T - t0) : 0;
+            const __amdgpu_buffer_rsrc_t vy =
+                buf_view_uniform(a.y + (size_t)(ntok > 0 ? t0 : 0) * H, (uint32_t)((size_t)ntok * H * sizeof(uint16_t)));
+            __builtin_amdgcn_raw_buffer_store_b128(yw, vy, (int)((uint32_t)(prow * H) * 2u + colq), 0, 2);
+        }
+        if (bad_now) { // a record had not landed: load the step's records again
+            for (int tries = 0; tries < kQMaxRetry; ++tries) {
+                __syncthreads();
+                if (tid == 0) {
+                    *bf = 0;
+                }
+                __syncthreads();
+                u32x4 qu[kUR], qd[kDR];
+                asm volatile("" ::: "memory");
+                load_recs(cu, qc, qu, qd);
+                take_recs(cu, qu, qd, bf);
+                __syncthreads();
+                if (!*bf) {
+                    break;
+                }
+            }
+        }
+
+        // pre weights of step cu (the auxiliary wave: lane = 16 k + token, one sigmoid each)
+        if (w == kAux && cu_ok) {
+            const int tok = lane & 15, k = lane >> 4;
+            const float rstd = rstd_of(sums[4 * kQTok + tok], a.inv_k, a.rms_eps);
+            prel[tok * kHC + k] = sigmoid_rcp(fmaf(sums[k * kQTok + tok] * rstd, s0, bpre)) + a.pre_eps;
+        }
+        // this workgroup's token of step cu: its comb logits (lane e of the auxiliary wave) and post
+        // pre-activations (lanes 0..3), stored raw into comb and post; the Sinkhorn and the
+        // sigmoids run after the loop, off the per-step path
+        const bool dz = designated(cu) && !a.head;
+        const int tdz = (cu * kQGroups + x) * kQTok + td;
+        {
+            float Lg = 0.0f, zp = 0.0f;
+            if (w == kAux && dz) {
+                const float rstd = rstd_of(sums[4 * kQTok + td], a.inv_k, a.rms_eps);
+                const int e = lane & 15;
+                Lg = fmaf(dsum[kHC + e] * rstd, s2, bcomb);
+                zp = fmaf(dsum[e & 3] * rstd, s1, bpost);
+            }
+            const bool tin = dz && tdz < T && w == kAux;
+            const __amdgpu_buffer_rsrc_t vc =
+                buf_view_uniform(a.comb + (size_t)(tin ? tdz : 0) * kHC * kHC, tin ? kHC * kHC * 4 : 0);
+            const __amdgpu_buffer_rsrc_t vp =
+                buf_view_uniform(a.post + (size_t)(tin ? tdz : 0) * kHC, tin ? kHC * 4 : 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(Lg), vc, lane < 16 ? lane * 4 : (int)kOob, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(zp), vp, lane < 4 ? lane * 4 : (int)kOob, 0, 0);
+        }
+        lds_barrier(); // B2: partial dots and the pre weights of step cu are in LDS
+        if (tid == 0) {
+            *bf = 0;
+        }
+
+        // the record of step i: this thread's chunk(s), three slice sums over the waves each
+        // (waves holding no chunk skip it)
+        if (w * kWave < kQChunks) {
+            const uint32_t tag = coop_tag(key, i * kQGroups + x);
+            const uint32_t q = (uint32_t)qi;
+#pragma unroll
+            for (int rs = 0; rs < kRS; ++rs) {
+                float v[3];
+#pragma unroll
+                for (int e = 0; e < 3; ++e) {
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int ww = 0; ww < W; ++ww) {
+                        acc += red[ww * (kQTok * kQRedStride) + rc_off[rs][e]];
+                    }
+                    v[e] = (rc_valid[rs] >> e) & 1 ? acc : 0.0f;
+                }
+                const uint32_t o = p_ok && rc_base[rs] != kOob ? rc_base[rs] + q * rc_qstride[rs] : kOob;
+                const u32x4 chunk = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), tag};
+                __builtin_amdgcn_raw_buffer_store_b128(chunk, vrec, (int)o, 0, 0);
+            }
+        }
+
+        // step cu's slot (this thread's token prow and piece, 4 streams) and pre weights into
+        // registers for the next iteration's collapse; the slot is free once B1 has passed
+        {
+            const unsigned char *cs = ring + rcs * kSlotB + prow * kTokB + piece * 16;
+#pragma unroll
+            for (int st = 0; st < kHC; ++st) {
+                hold[st] = *reinterpret_cast<const u32x4 *>(cs + st * kRowB);
+            }
+#pragma unroll
+            for (int k = 0; k < kHC; ++k) {
+                holdp[k] = prel[prow * kHC + k];
+            }
+        }
+        // the optional pre output of this workgroup's token (the auxiliary wave's lanes 0..3;
+        // every wave issues the store, elsewhere into an empty view)
+        {
+            const bool tin = designated(cu) && tdz < T && a.pre != nullptr && w == kAux;
+            const __amdgpu_buffer_rsrc_t vq =
+                buf_view_uniform(tin ? (const void *)(a.pre + (size_t)tdz * kHC) : (const void *)a.y, tin ? kHC * 4 : 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(prel[td * kHC + (lane & 3)]), vq,
+                                                  lane < 4 ? lane * 4 : (int)kOob, 0, 0);
+        }
+    };
+
+    // Two warm-up iterations (steps -2 and -1: every memory operation out of range) load
+    // steps 0 and 1, so every trip of the loop, the first included, issues the same
+    // operations and the compiler's wait counts stay exact.
+    u32x4 bufA[4], bufB[4], hold[kHC];
+    float holdp[kHC];
+    u32x4 ru[kUR], rd[kDR];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        bufA[k] = u32x4{0u, 0u, 0u, 0u};
+        bufB[k] = u32x4{0u, 0u, 0u, 0u};
+        hold[k] = u32x4{0u, 0u, 0u, 0u};
+        holdp[k] = 0.0f;
+    }
+#pragma unroll
+    for (int r = 0; r < kUR; ++r) {
+        ru[r] = u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int r = 0; r < kDR; ++r) {
+        rd[r] = u32x4{0u, 0u, 0u, 0u};
+    }
+    if (tid < 2) {
+        badf[tid] = 0;
+    }
+    __syncthreads();
+    const int iend = nst + L + 1; // the last collapse (of step nst - 1) is in iteration nst + L
+    int ri = R - 2, qi = RR - 2;  // step -2
+    for (int i = -2; i < iend; i += 2) {
+        iteration(i, ri, qi, bufA, ru, rd, hold, holdp);
+        ri = wrap(ri + 1, R);
+        qi = wrap(qi + 1, RR);
+        iteration(i + 1, ri, qi, bufB, ru, rd, hold, holdp);
+        ri = wrap(ri + 1, R);
+        qi = wrap(qi + 1, RR);
+    }
+    if (a.head) {
+        return;
+    }
+    // Post weights and the Sinkhorn of this workgroup's tokens: token td of the steps j with
+    // j mod 2 == s / 16, whose raw comb logits and post pre-activations the loop stored.
+    // Row r of wave w takes the ((round * W + w) * 4 + r)-th of them.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const int e = lane & 15;
+    const int nmine = (nst - (s >> 4) + 1) / 2;
+    for (int base = 0; base < nmine; base += 4 * W) {
+        const int m = base + 4 * w + (lane >> 4);
+        const int j = 2 * m + (s >> 4);
+        const int t = (j * kQGroups + x) * kQTok + td;
+        const bool ok = m < nmine && t < T;
+        float *pc = a.comb + (size_t)(ok ? t : 0) * kHC * kHC + e;
+        float *pp = a.post + (size_t)(ok ? t : 0) * kHC + (e & 3);
+        // device-scope loads: the auxiliary wave stored these, and they must not come from a stale L1 line
+        const float Lg = ok ? __hip_atomic_load(pc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.0f;
+        const float zp = ok && e < kHC ? __hip_atomic_load(pp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.0f;
+        const float P = sinkhorn_row16(Lg, a.iters, a.sk_eps);
+        const float pv = sigmoidf_fast(zp) * a.post_mult;
+        if (ok) {
+            *pc = P;
+            if (e < kHC) {
+                *pp = pv;
+            }
+        }
+    }
+}
+
+int coop_waves(int64_t H) { return (int)((((H + 31) / 32) + kQSlices - 1) / kQSlices); }
+
+struct CoopCfg {
+    int W, L, R, RR;
+    size_t lds;
+};
+
+CoopCfg coop_config(int64_t H)
+{
+    CoopCfg k{};
+    k.W = coop_waves(H);
+    const size_t slot = (size_t)kQTok * (256 * k.W + 16);
+    const size_t scratch = (size_t)k.W * kQTok * kQRedStride * 4 + (96 + 32 + 64 + 4 + 64) * 4;
+    const size_t lds_max = 160 * 1024;
+    k.L = 3;
+    while (k.L > 1 && (size_t)(k.L + 2) * slot + scratch > lds_max) {
+        --k.L;
+    }
+    k.R = k.L + 2;
+    k.RR = 2 * k.L + 2;
+    k.lds = (size_t)k.R * slot + scratch;
+    return k;
+}
+
+int g_coop_device_ok[64]; // per device: 0 unknown, 1 usable (256 CUs on gfx950), 2 not
+
+bool coop_device_ok()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        return false;
+    }
+    if (g_coop_device_ok[dev] == 0) {
+        int cus = 0;
+        hipDeviceProp_t prop;
+        const bool ok = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+                        hipGetDeviceProperties(&prop, dev) == hipSuccess && cus == kQGroups * kQSlices &&
+                        strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        g_coop_device_ok[dev] = ok ? 1 : 2;
+    }
+    return g_coop_device_ok[dev] == 1;
+}
+
+template <int W, typename WT>
+hipError_t launch_coop_w(const CoopArgs &a, size_t lds, hipStream_t stream)
+{
+    static bool attr_set = false;
+    if (!attr_set) {
+        const hipError_t e =
+            hipFuncSetAttribute((const void *)pre_coop_kernel<W, WT>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) {
+            return e;
+        }
+        attr_set = true;
+    }
+    pre_coop_kernel<W, WT><<<dim3(kQGroups * kQSlices), dim3(W * 64), lds, stream>>>(a);
+    return hipGetLastError();
+}
+
+template <typename WT>
+hipError_t launch_coop_t(const CoopArgs &a, int W, size_t lds, hipStream_t stream)
+{
+    switch (W) {
+    case 2:
+        return launch_coop_w<2, WT>(a, lds, stream);
+    case 3:
+        return launch_coop_w<3, WT>(a, lds, stream);
+    case 4:
+        return launch_coop_w<4, WT>(a, lds, stream);
+    case 5:
+        return launch_coop_w<5, WT>(a, lds, stream);
+    case 6:
+        return launch_coop_w<6, WT>(a, lds, stream);
+    case 7:
+        return launch_coop_w<7, WT>(a, lds, stream);
+    case 8:
+        return launch_coop_w<8, WT>(a, lds, stream);
+    default:
+        return hipErrorInvalidValue;
+    }
+}
+
+} // namespace
+
+size_t pre_coop_workspace_bytes(int64_t H)
+{
+    const CoopCfg k = coop_config(H);
+    return (size_t)kQGroups * k.RR * kQSlices * kQChunks * sizeof(u32x4);
+}
+
+bool pre_coop_shape_ok(int64_t T, int64_t H)
+{
+    if (T < kCoopMinTokens || H > (int64_t)kQSlices * 8 * 32) {
+        return false;
+    }
+    const int W = coop_waves(H);
+    return W >= 2 && W <= 8;
+}
+
+bool pre_coop_usable(int64_t T, int64_t H, bool vec8) { return vec8 && pre_coop_shape_ok(T, H) && coop_device_ok(); }
+
+hipError_t launch_pre_coop(const uint16_t *res, const void *hc_fn, bool fn_bf16, int fn_rows, const float *hc_scale,
+                           const float *hc_base, int64_t T, int64_t H, float rms_eps, float pre_eps,
+                           float sinkhorn_eps, float post_mult, int iters, bool head, uint16_t *y, float *post,
+                           float *comb, float *pre, void *workspace, hipStream_t stream)
+{
+    const CoopCfg k = coop_config(H);
+    CoopArgs a{};
+    a.res = res;
+    a.hc_fn = hc_fn;
+    a.hc_scale = hc_scale;
+    a.hc_base = hc_base;
+    a.T = (int)T;
+    a.H = (int)H;
+    a.nhb = (int)((H + 31) / 32);
+    a.fn_rows = fn_rows;
+    a.L = k.L;
+    a.R = k.R;
+    a.RR = k.RR;
+    a.inv_k = 1.0f / (float)(kHC * H);
+    a.rms_eps = rms_eps;
+    a.pre_eps = pre_eps;
+    a.sk_eps = sinkhorn_eps;
+    a.post_mult = post_mult;
+    a.iters = iters;
+    a.head = head ? 1 : 0;
+    a.y = y;
+    a.post = post;
+    a.comb = comb;
+    a.pre = pre;
+    a.rec = reinterpret_cast<u32x4 *>(workspace);
+    a.rec_bytes = (uint32_t)pre_coop_workspace_bytes(H);
+    return fn_bf16 ? launch_coop_t<uint16_t>(a, k.W, k.lds, stream) : launch_coop_t<float>(a, k.W, k.lds, stream);
+}
+
+} // namespace mhc

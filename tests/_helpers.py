@@ -62,3 +62,39 @@ def sample_tokens(T: int, n: int, seed: int = 123) -> np.ndarray:
     while len(pick) < min(n, T):
         pick.add(int(g.integers(0, T)))
     return np.array(sorted(pick))
+
+
+def oracle_threads() -> int:
+    import os
+    return max(1, min(os.cpu_count() or 1, 16))
+
+
+def check_pre_all_tokens(inp, got, what, params=None, chunk=256, x=None, out=None):
+    """Every token of a pre-map call (y, post, comb, pre) against the oracle, and with `x`/`out`
+    the post-map that followed it.  The oracle runs on token chunks over threads (its ctypes
+    calls release the GIL), comparing each chunk as it finishes, so memory stays bounded."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    y, post, comb, pre = got
+    p = dict(inp.params)
+    if params:
+        p.update(params)
+    T = inp.res.shape[0]
+
+    def one(t0):
+        t1 = min(T, t0 + chunk)
+        r = inp.res[t0:t1]
+        ref = oracle.pre(r, inp.hc_fn, inp.hc_scale, inp.hc_base, rms_eps=p["rms_eps"], pre_eps=p["pre_eps"],
+                         sinkhorn_eps=p["sinkhorn_eps"], post_mult=p["post_mult"], num_iters=p["num_iters"])
+        if pre is not None:
+            assert_f32_close(pre[t0:t1], ref["pre"], f"{what} pre [{t0}:{t1}]")
+        assert_f32_close(post[t0:t1], ref["post"], f"{what} post [{t0}:{t1}]")
+        assert_f32_close(comb[t0:t1], ref["comb"], f"{what} comb [{t0}:{t1}]")
+        assert_bf16_close(y[t0:t1], ref["y"], f"{what} y [{t0}:{t1}]")
+        if out is not None:
+            ref_out = oracle.post(x[t0:t1], r, ref["post"], ref["comb"])
+            assert_bf16_close(out[t0:t1], ref_out, f"{what} out [{t0}:{t1}]")
+
+    with ThreadPoolExecutor(oracle_threads()) as ex:
+        list(ex.map(one, range(0, T, chunk)))

@@ -10,8 +10,8 @@ import pytest
 import oracle
 from mhc_inputs import (HC, bf16_bits_to_f32, layer_inputs, named_layer, post_inputs, sinkhorn_logits,
                         SINKHORN_N)
-from tests._helpers import (assert_bf16_close, assert_f32_close, bits_of, f32_of, sample_tokens, to_dev_bf16,
-                            to_dev_f32)
+from tests._helpers import (assert_bf16_close, assert_f32_close, bits_of, check_pre_all_tokens, f32_of, sample_tokens,
+                            to_dev_bf16, to_dev_f32)
 
 pytestmark = pytest.mark.gpu
 
@@ -243,14 +243,13 @@ def test_pre_decode_h7168_full():
     _check_pre(inp, _run_pre(inp), what="pre 32x7168")
 
 
-def test_pre_full_size_h7168_sampled():
-    """T=8192, H=7168 (the measured layer): GPU runs the full call, the oracle checks sampled tokens."""
+def test_pre_full_size_h7168_all_tokens():
+    """T=8192, H=7168 (the measured layer, in the launch the benchmark times): every token of
+    y, post, comb and pre against the oracle."""
     inp = named_layer("layer_h7168")
-    got = _run_pre(inp)
-    toks = sample_tokens(inp.T, 48)
-    _check_pre(inp, got, tokens=toks, what="pre 8192x7168")
-    y, post, comb, pre, _ = got
-    assert np.abs(comb.sum(axis=-2) - 1).max() <= 1e-5  # property at every token
+    y, post, comb, pre, _ = _run_pre(inp)
+    check_pre_all_tokens(inp, (y, post, comb, pre), "pre 8192x7168")
+    assert np.abs(comb.sum(axis=-2) - 1).max() <= 1e-5
     assert np.all(pre > 0) and np.all(pre <= 1 + 2e-6) and np.all(post >= 0) and np.all(post <= 1)
 
 
@@ -404,8 +403,9 @@ def test_pre_from_dots_deterministic_and_empty():
 
 # ----------------------------------------------------------------------------- whole layer
 
-def test_layer_pre_then_post_full_size_sampled():
-    """T=8192, H=7168 pre-map then post-map with x as the sublayer output, sampled tokens."""
+def test_layer_pre_then_post_full_size_all_tokens():
+    """T=8192, H=7168 pre-map then post-map with x as the sublayer output: every token of y
+    and out against the oracle (out from the oracle's own post and comb)."""
     mhc = _mhc()
     inp = named_layer("layer_h7168")
     res_d = to_dev_bf16(inp.res)
@@ -413,8 +413,4 @@ def test_layer_pre_then_post_full_size_sampled():
                                       to_dev_f32(inp.hc_base))
     out = mhc.mhc_post(to_dev_bf16(inp.x), res_d, post, comb)
     torch.cuda.synchronize()
-    toks = sample_tokens(inp.T, 32, seed=7)
-    ref = oracle.pre(inp.res[toks], inp.hc_fn, inp.hc_scale, inp.hc_base)
-    ref_out = oracle.post(inp.x[toks], inp.res[toks], ref["post"], ref["comb"])
-    assert_bf16_close(bits_of(out)[toks], ref_out, "layer out")
-    assert_bf16_close(bits_of(y)[toks], ref["y"], "layer y")
+    check_pre_all_tokens(inp, (bits_of(y), f32_of(post), f32_of(comb), None), "layer", x=inp.x, out=bits_of(out))
