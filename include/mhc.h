@@ -81,12 +81,15 @@ mhc_status mhc_sinkhorn(const float *logits, float *out, int64_t n_mats, int32_t
                         void *stream);
 
 /*
- * Size in bytes of the device workspace mhc_pre_fused needs for (T, H): the
- * projection weights split into bf16 terms in MFMA operand order (384 * H
- * bytes, rounded up), the per-slice partial sums of the projection (100 bytes
- * per token per 128-wide slice of H) and the per-token totals (128 bytes per
- * token).  Tokens beyond 2^31 bytes of partial sums are processed in chunks
- * that reuse the same space.  Returns 0 for T <= 0, H <= 0 or H beyond the
+ * Size in bytes of the device workspace mhc_pre_fused needs for (T, H): enough for
+ * either form of the pre-map.  The one-read form (16-byte rows, 1024 < H <= 8192,
+ * T >= 1024, on a 256-CU gfx950) keeps a ring of exchange records: 16-byte chunks of
+ * partial sums for a few 16-token steps of every workgroup, at most 4.6 MB and
+ * independent of T.  The two-pass form keeps the projection weights split into bf16
+ * terms in MFMA operand order (384 * H bytes, rounded up), the per-slice partial sums of
+ * the projection (100 bytes per token per 128-wide slice of H) and the per-token totals
+ * (128 bytes per token); tokens beyond 2^31 bytes of partial sums are processed in
+ * chunks that reuse the same space.  Returns 0 for T <= 0, H <= 0 or H beyond the
  * pre-map limit.
  */
 size_t mhc_pre_fused_workspace_bytes(int64_t T, int64_t H);
@@ -119,6 +122,28 @@ mhc_status mhc_pre_fused(const uint16_t *res, const float *hc_fn, const float *h
                          int64_t T, int64_t H, float rms_eps, float pre_eps, float sinkhorn_eps, float post_mult,
                          int32_t num_iters, uint16_t *y, float *post, float *comb, float *pre, void *workspace,
                          size_t workspace_bytes, void *stream);
+
+/*
+ * mhc_pre_fused_noalloc -- mhc_pre_fused for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * no workspace argument.  Its scratch is a file-scope device array of
+ * MHC_PRE_FUSED_NOALLOC_MAX_BYTES inside the library, one per GPU, held until the
+ * process ends; the first call on a device resolves its address there.  The call
+ * allocates and frees nothing.  Arguments, outputs and limits are those of
+ * mhc_pre_fused, and so are the results (bit for bit).  A call whose form needs more
+ * workspace than MHC_PRE_FUSED_NOALLOC_MAX_BYTES is rejected with MHC_ERROR_WORKSPACE
+ * before anything is enqueued.  The one-read form (16-byte aligned res and y, H a multiple
+ * of 8, T >= 1024, 1024 < H <= 8192, on a 256-CU gfx950) needs at most 4.6 MB whatever T,
+ * so it always fits; the two-pass form's partial sums take roughly 1 to 1.5 KB per token
+ * and 1024 of H (mhc_pre_fused_workspace_bytes(T, H) bounds either form).  Every call on one
+ * GPU shares the array: calls that may overlap in time on one GPU (different streams,
+ * concurrent host threads) race and give undefined results; order them on one stream.
+ */
+#define MHC_PRE_FUSED_NOALLOC_MAX_BYTES ((size_t)16 << 20)
+mhc_status mhc_pre_fused_noalloc(const uint16_t *res, const float *hc_fn, const float *hc_scale,
+                                 const float *hc_base, int64_t T, int64_t H, float rms_eps, float pre_eps,
+                                 float sinkhorn_eps, float post_mult, int32_t num_iters, uint16_t *y, float *post,
+                                 float *comb, float *pre, void *stream);
 
 /*
  * mhc_pre_fused_bf16 -- mhc_pre_fused with bf16 weights (metrale glm5next_mhc.rs,

@@ -25,6 +25,7 @@ MHC_SUCCESS = 0
 MHC_ERROR_INVALID_VALUE = 1
 MHC_ERROR_WORKSPACE = 2
 MHC_ERROR_LAUNCH = 3
+MHC_PRE_FUSED_NOALLOC_MAX_BYTES = 16 << 20  # the static scratch of mhc_pre_fused_noalloc
 
 _lib = None
 
@@ -64,6 +65,8 @@ def lib() -> ctypes.CDLL:
     L.mhc_post_backward.restype = ctypes.c_int
     L.mhc_pre_fused_bf16.argtypes = [P, P, P, P, I64, I64, F, F, F, F, I32, P, P, P, P, P, SZ, P]
     L.mhc_pre_fused_bf16.restype = ctypes.c_int
+    L.mhc_pre_fused_noalloc.argtypes = [P, P, P, P, I64, I64, F, F, F, F, I32, P, P, P, P, P]
+    L.mhc_pre_fused_noalloc.restype = ctypes.c_int
     L.mhc_expand.argtypes = [P, I64, I64, P, P]
     L.mhc_expand.restype = ctypes.c_int
     L.mhc_head_mean.argtypes = [P, I64, I64, P, P]
@@ -166,8 +169,19 @@ def mhc_pre_fused_bf16(res: torch.Tensor, hc_fn: torch.Tensor, hc_scale: torch.T
                       sinkhorn_eps, post_mult, num_iters, y, post, comb, pre, return_pre, workspace)
 
 
+def mhc_pre_fused_noalloc(res: torch.Tensor, hc_fn: torch.Tensor, hc_scale: torch.Tensor, hc_base: torch.Tensor,
+                          rms_eps: float = 1e-6, pre_eps: float = 1e-6, sinkhorn_eps: float = 1e-6,
+                          post_mult: float = 1.0, num_iters: int = 20, *, y=None, post=None, comb=None, pre=None,
+                          return_pre: bool = False):
+    """:func:`mhc_pre_fused` with the library's static scratch instead of a workspace (for callers
+    that cannot allocate device memory).  Outputs given here are written in place; ones left as
+    None are allocated by this Python wrapper, not by the library."""
+    return _pre_fused("mhc_pre_fused_noalloc", torch.float32, res, hc_fn, hc_scale, hc_base, rms_eps, pre_eps,
+                      sinkhorn_eps, post_mult, num_iters, y, post, comb, pre, return_pre, None, noalloc=True)
+
+
 def _pre_fused(name, fn_dtype, res, hc_fn, hc_scale, hc_base, rms_eps, pre_eps, sinkhorn_eps, post_mult, num_iters,
-               y, post, comb, pre, return_pre, workspace):
+               y, post, comb, pre, return_pre, workspace, noalloc=False):
     _need(res, "res", torch.bfloat16)
     if res.dim() < 2 or res.shape[-2] != HC:
         raise ValueError(f"res must be [..., 4, H], got {tuple(res.shape)}")
@@ -202,6 +216,12 @@ def _pre_fused(name, fn_dtype, res, hc_fn, hc_scale, hc_base, rms_eps, pre_eps, 
         if pre.numel() != T * HC:
             raise ValueError("pre must hold [T, 4] values")
     _same_device(res, hc_fn, hc_scale, hc_base, y, post, comb, pre)
+    if noalloc:
+        _check(name, getattr(lib(), name)(
+            _ptr(res), _ptr(hc_fn), _ptr(hc_scale), _ptr(hc_base), T, H, float(rms_eps), float(pre_eps),
+            float(sinkhorn_eps), float(post_mult), int(num_iters), _ptr(y), _ptr(post), _ptr(comb), _ptr(pre),
+            _stream(dev)))
+        return (y, post, comb, pre) if return_pre else (y, post, comb)
     need = mhc_pre_fused_workspace_bytes(T, H)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -637,10 +657,10 @@ def mhc_pre_fused_backward(dy: torch.Tensor, d_post: torch.Tensor, d_comb: torch
     return dict(d_res=d_res, d_hc_fn=d_fn, d_hc_scale=d_scale, d_hc_base=d_base)
 
 
-__all__ = ["mhc_sinkhorn", "mhc_pre_fused", "mhc_pre_fused_bf16", "mhc_expand", "mhc_head_mean", "mhc_head",
+__all__ = ["mhc_sinkhorn", "mhc_pre_fused", "mhc_pre_fused_noalloc", "mhc_pre_fused_bf16", "mhc_expand", "mhc_head_mean", "mhc_head",
            "mhc_pre_fused_workspace_bytes", "mhc_pre_from_dots", "mhc_post",
            "mhc_sinkhorn_backward", "mhc_post_backward", "mhc_pre_from_dots_backward",
            "mhc_pre_backward_workspace_bytes", "mhc_pre_fused_backward", "mhc_pre_fused_backward_workspace_bytes",
            "mhc_post_project", "mhc_post_project_workspace_bytes",
            "lib", "abi_version", "status_string", "MHCError", "HC",
-           "MIX", "SINKHORN_BWD_MAX_ITERS"]
+           "MIX", "SINKHORN_BWD_MAX_ITERS", "MHC_PRE_FUSED_NOALLOC_MAX_BYTES"]

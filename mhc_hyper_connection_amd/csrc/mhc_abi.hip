@@ -4,6 +4,7 @@
 #include "mhc.h"
 #include "mhc_internal.h"
 
+#include <atomic>
 #include <math.h>
 
 namespace {
@@ -44,10 +45,14 @@ constexpr int kMixRows = 24;
 
 // Shared validation and launch of the pre-map forms: the full pre-map (24 weight
 // rows, fp32 or bf16) and the weighted head (4 rows, pre weights and y only).
+// 16-byte rows: the pre-map's wide loads and its one-read form need them
+bool pre_vec8(const uint16_t *res, const uint16_t *y, int64_t H) { return (H % 8 == 0) && aligned16(res) && aligned16(y); }
+
 mhc_status pre_common(const uint16_t *res, const void *hc_fn, bool fn_bf16, int fn_rows, const float *hc_scale,
                       int n_scale, const float *hc_base, int64_t T, int64_t H, float rms_eps, float pre_eps,
                       float sinkhorn_eps, float post_mult, int32_t num_iters, bool head, uint16_t *y, float *post,
-                      float *comb, float *pre, void *workspace, size_t workspace_bytes, void *stream)
+                      float *comb, float *pre, void *workspace, size_t workspace_bytes, void *stream,
+                      bool validate_only = false)
 {
     if (!sizes_ok(T, H) || H > kPreMaxH || num_iters < 1 || !finite(rms_eps) || !(rms_eps > 0.0f) || !finite(pre_eps) ||
         pre_eps < 0.0f || !finite(sinkhorn_eps) || !(sinkhorn_eps > 0.0f) || !finite(post_mult)) {
@@ -60,8 +65,10 @@ mhc_status pre_common(const uint16_t *res, const void *hc_fn, bool fn_bf16, int 
         return MHC_ERROR_INVALID_VALUE;
     }
     const PreGeom g = mhc::pre_geometry(T, H);
-    const size_t ws_need = mhc::pre_fused_workspace_bytes(T, H);
-    if (!workspace || workspace_bytes < ws_need || ((uintptr_t)workspace & 255u) != 0) {
+    const bool vec8 = pre_vec8(res, y, H);
+    // the need of the form this call takes (never above mhc_pre_fused_workspace_bytes)
+    const size_t ws_need = mhc::pre_path_workspace_bytes(T, H, vec8);
+    if (!validate_only && (!workspace || workspace_bytes < ws_need || ((uintptr_t)workspace & 255u) != 0)) {
         return MHC_ERROR_WORKSPACE;
     }
     const size_t res_b = (size_t)T * 4 * H * 2, y_b = (size_t)T * H * 2;
@@ -85,10 +92,45 @@ mhc_status pre_common(const uint16_t *res, const void *hc_fn, bool fn_bf16, int 
             }
         }
     }
-    const bool vec8 = (H % 8 == 0) && aligned16(res) && aligned16(y);
+    if (validate_only) {
+        return MHC_SUCCESS;
+    }
     return launch_status(mhc::launch_pre(res, hc_fn, fn_bf16, fn_rows, hc_scale, hc_base, g, rms_eps, pre_eps,
                                          sinkhorn_eps, post_mult, num_iters, head, y, post, comb, pre, workspace,
                                          (hipStream_t)stream, vec8));
+}
+
+// The no-allocation pre-map's scratch: a file-scope device array.  In host code the name
+// stands for a host-side handle, not a device address: the address on each device comes
+// from hipGetSymbolAddress with that device current, once, and only that pointer is
+// passed to kernels.
+static __device__ __align__(256) unsigned char scratch[MHC_PRE_FUSED_NOALLOC_MAX_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+
+// The array's address on the current device (resolved on the first call there), or
+// nullptr with the HIP error in `err`.
+void *scratch_on_current_device(hipError_t &err)
+{
+    int dev = -1;
+    err = hipGetDevice(&dev);
+    if (err != hipSuccess) {
+        return nullptr;
+    }
+    if (dev < 0 || dev >= kMaxDevices) {
+        err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess || p == nullptr) {
+            return nullptr;
+        }
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    return p;
 }
 
 } // namespace
@@ -105,7 +147,7 @@ const char *mhc_status_string(mhc_status status)
     case MHC_ERROR_INVALID_VALUE:
         return "invalid argument";
     case MHC_ERROR_WORKSPACE:
-        return "workspace missing or too small";
+        return "workspace missing, misaligned or too small (or above the no-allocation scratch)";
     case MHC_ERROR_LAUNCH:
         return "kernel launch failed";
     }
@@ -146,6 +188,30 @@ mhc_status mhc_pre_fused(const uint16_t *res, const float *hc_fn, const float *h
 {
     return pre_common(res, hc_fn, false, kMixRows, hc_scale, 3, hc_base, T, H, rms_eps, pre_eps, sinkhorn_eps,
                       post_mult, num_iters, false, y, post, comb, pre, workspace, workspace_bytes, stream);
+}
+
+mhc_status mhc_pre_fused_noalloc(const uint16_t *res, const float *hc_fn, const float *hc_scale,
+                                 const float *hc_base, int64_t T, int64_t H, float rms_eps, float pre_eps,
+                                 float sinkhorn_eps, float post_mult, int32_t num_iters, uint16_t *y, float *post,
+                                 float *comb, float *pre, void *stream)
+{
+    // every check of mhc_pre_fused except the workspace, before the device is touched
+    const mhc_status v = pre_common(res, hc_fn, false, kMixRows, hc_scale, 3, hc_base, T, H, rms_eps, pre_eps,
+                                    sinkhorn_eps, post_mult, num_iters, false, y, post, comb, pre, nullptr, 0,
+                                    stream, true);
+    if (v != MHC_SUCCESS || T == 0) {
+        return v;
+    }
+    if (mhc::pre_path_workspace_bytes(T, H, pre_vec8(res, y, H)) > MHC_PRE_FUSED_NOALLOC_MAX_BYTES) {
+        return MHC_ERROR_WORKSPACE;
+    }
+    hipError_t e = hipSuccess;
+    void *ws = scratch_on_current_device(e);
+    if (ws == nullptr) {
+        return MHC_ERROR_LAUNCH;
+    }
+    return pre_common(res, hc_fn, false, kMixRows, hc_scale, 3, hc_base, T, H, rms_eps, pre_eps, sinkhorn_eps,
+                      post_mult, num_iters, false, y, post, comb, pre, ws, MHC_PRE_FUSED_NOALLOC_MAX_BYTES, stream);
 }
 
 mhc_status mhc_pre_fused_bf16(const uint16_t *res, const uint16_t *hc_fn, const float *hc_scale,

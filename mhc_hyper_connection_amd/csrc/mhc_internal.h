@@ -53,6 +53,9 @@ hipError_t launch_pre_coop(const uint16_t *res, const void *hc_fn, bool fn_bf16,
                            float *comb, float *pre, void *workspace, hipStream_t stream);
 // Workspace of the pre-map entry points: enough for either form.
 size_t pre_fused_workspace_bytes(int64_t T, int64_t H);
+// Workspace of the form a call with these sizes and 16-byte rows (vec8) or not takes on the
+// current device; at most pre_fused_workspace_bytes.
+size_t pre_path_workspace_bytes(int64_t T, int64_t H, bool vec8);
 
 // The pre-map's first stages on their own: the weight split (once), then for the token
 // chunk [c0, c0 + Tc) the projection and the slice sums, which leave the per-token

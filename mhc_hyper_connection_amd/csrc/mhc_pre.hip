@@ -1060,6 +1060,11 @@ size_t pre_fused_workspace_bytes(int64_t T, int64_t H)
     return coop > two_pass ? coop : two_pass;
 }
 
+size_t pre_path_workspace_bytes(int64_t T, int64_t H, bool vec8)
+{
+    return pre_coop_usable(T, H, vec8) ? pre_coop_workspace_bytes(H) : pre_geometry(T, H).total_bytes;
+}
+
 hipError_t launch_post_project(const uint16_t *x, const uint16_t *res, const float *post, const float *comb,
                                const float *hc_fn_next, int64_t T, int64_t H, uint16_t *out, float *dot_mix,
                                float *sqrsum, void *workspace, hipStream_t stream)

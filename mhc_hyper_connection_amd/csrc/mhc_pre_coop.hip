@@ -34,6 +34,7 @@
 #include "mhc_device.h"
 #include "mhc_internal.h"
 
+#include <atomic>
 #include <string.h>
 
 namespace mhc {
@@ -643,14 +644,19 @@ bool coop_device_ok()
 template <int W, typename WT>
 hipError_t launch_coop_w(const CoopArgs &a, size_t lds, hipStream_t stream)
 {
-    static bool attr_set = false;
-    if (!attr_set) {
-        const hipError_t e =
-            hipFuncSetAttribute((const void *)pre_coop_kernel<W, WT>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    // the dynamic-LDS limit is a per-device attribute: raised once on each device
+    static std::atomic<bool> attr_set[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= 64) {
+        return e != hipSuccess ? e : hipErrorInvalidDevice;
+    }
+    if (!attr_set[dev].load(std::memory_order_acquire)) {
+        e = hipFuncSetAttribute((const void *)pre_coop_kernel<W, WT>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) {
             return e;
         }
-        attr_set = true;
+        attr_set[dev].store(true, std::memory_order_release);
     }
     pre_coop_kernel<W, WT><<<dim3(kQGroups * kQSlices), dim3(W * 64), lds, stream>>>(a);
     return hipGetLastError();

@@ -96,6 +96,40 @@ def test_pre_validation_workspace():
     assert _pre(lib, T=0, res=None, y=None, ws=None) == mhc.MHC_SUCCESS  # empty: no-op
 
 
+def _pre_noalloc(lib, **kw):
+    G = 1 << 40  # fake addresses 1 TiB apart: no overlap at any size used here
+    a = dict(res=ctypes.c_void_p(G), fn=ctypes.c_void_p(2 * G), sc=ctypes.c_void_p(3 * G), base=ctypes.c_void_p(4 * G),
+             T=16, H=256, rms=1e-6, pe=1e-6, se=1e-6, pm=1.0, it=20, y=ctypes.c_void_p(5 * G),
+             post=ctypes.c_void_p(6 * G), comb=ctypes.c_void_p(7 * G), pre=None)
+    a.update(kw)
+    return lib.mhc_pre_fused_noalloc(a["res"], a["fn"], a["sc"], a["base"], a["T"], a["H"], a["rms"], a["pe"],
+                                     a["se"], a["pm"], a["it"], a["y"], a["post"], a["comb"], a["pre"], NULL)
+
+
+def test_pre_noalloc_limit_matches_header():
+    m = re.search(r"#define\s+MHC_PRE_FUSED_NOALLOC_MAX_BYTES\s+\(\(size_t\)(\d+)\s*<<\s*(\d+)\)", HEADER.read_text())
+    assert m and int(m.group(1)) << int(m.group(2)) == mhc.MHC_PRE_FUSED_NOALLOC_MAX_BYTES
+
+
+@pytest.mark.parametrize("kw", [
+    dict(T=-1), dict(H=0), dict(it=0), dict(rms=0.0), dict(se=0.0), dict(pe=-1.0), dict(pm=float("nan")),
+    dict(res=None), dict(fn=None), dict(y=None), dict(post=None), dict(comb=None),
+    dict(y=ctypes.c_void_p((1 << 40) + 64)),           # y overlaps res
+])
+def test_pre_noalloc_validation_invalid(kw):
+    assert _pre_noalloc(mhc.lib(), **kw) == mhc.MHC_ERROR_INVALID_VALUE
+
+
+def test_pre_noalloc_rejects_shapes_beyond_the_scratch():
+    """Checked before any HIP call: these shapes always take the two-pass form (H above the
+    one-read form's range, or a single-wave slice), whose workspace exceeds the scratch."""
+    lib = mhc.lib()
+    for T, H in [(2000, 16384), (20000, 1024)]:
+        assert mhc.mhc_pre_fused_workspace_bytes(T, H) > mhc.MHC_PRE_FUSED_NOALLOC_MAX_BYTES
+        assert _pre_noalloc(lib, T=T, H=H) == mhc.MHC_ERROR_WORKSPACE
+    assert _pre_noalloc(lib, T=0, res=None, y=None) == mhc.MHC_SUCCESS  # empty: no-op
+
+
 def _dots(lib, **kw):
     a = dict(dm=ctypes.c_void_p(0x1000000), sq=None, S=1, res=FAKE, sc=ctypes.c_void_p(0x8000000),
              base=ctypes.c_void_p(0x8001000), T=16, H=256, k=1024.0, rms=1e-6, pe=1e-6, se=1e-6, pm=1.0, it=20,
