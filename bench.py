@@ -28,6 +28,12 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 VALU_PEAK_GIPS = 256 * 4 * 2.4 / 4
 
 
+def pre_one_read(T: int, H: int) -> bool:
+    """Whether the library's pre-map takes its one-read form at these sizes (the bench's
+    buffers are 16-byte aligned and the machine's GPU is a 256-CU gfx950)."""
+    return H % 8 == 0 and T >= 1024 and 1024 < H <= 8192
+
+
 def sinkhorn_valu_per_wave(iters: int) -> int:
     """VALU instructions one wave of sinkhorn_kernel issues for its 64 matrices, counted
     in the compiled gfx950 code (iters >= 1): 141 outside the iteration loop (loads,
@@ -374,12 +380,14 @@ def main():
                   "algorithmic_bytes": step_bytes}
 
     # Per-call rooflines.  mhc_post and mhc_sinkhorn are one kernel launch each;
-    # mhc_pre_fused is four (weight split, projection, slice sums, collapse).
+    # mhc_pre_fused is one in its one-read form (16-byte rows, T >= 1024, 1024 < H <= 8192
+    # on a 256-CU gfx950) and four otherwise (weight split, projection, slice sums, collapse).
     calls = {}
     proj = "pre_proj_stream_kernel" if H % 8 == 0 else "pre_proj_kernel"
+    col = "pre_collapse_vec8_kernel" if H % 8 == 0 else "pre_collapse_scalar_kernel"
+    pre_kernels = "pre_coop_kernel" if pre_one_read(T, H) else "pre_prep_kernel+" + proj + "+pre_mixsum_kernel+" + col
     if "pre_ms" in breakdown:
-        col = "pre_collapse_vec8_kernel" if H % 8 == 0 else "pre_collapse_scalar_kernel"
-        calls["mhc_pre_fused"] = ("pre_prep_kernel+" + proj + "+pre_mixsum_kernel+" + col, breakdown["pre_ms"], pre_b)
+        calls["mhc_pre_fused"] = (pre_kernels, breakdown["pre_ms"], pre_b)
     if "post_ms" in breakdown:
         calls["mhc_post"] = ("post_vec8_kernel" if H % 8 == 0 else "post_scalar_kernel", breakdown["post_ms"], post_b)
     if "sinkhorn_ms" in breakdown:
@@ -390,13 +398,10 @@ def main():
         calls["mhc_sinkhorn_backward"] = ("sinkhorn_bwd_kernel", breakdown["sinkhorn_bwd_ms"], step_bytes)
     if "post_bwd_ms" in breakdown:
         calls["mhc_post_backward"] = ("post_bwd_kernel", breakdown["post_bwd_ms"], step_bytes)
-    col = "pre_collapse_vec8_kernel" if H % 8 == 0 else "pre_collapse_scalar_kernel"
     if "pre_bf16_ms" in breakdown:
-        calls["mhc_pre_fused_bf16"] = ("pre_prep_kernel+" + proj + "+pre_mixsum_kernel+" + col,
-                                       breakdown["pre_bf16_ms"], step_bytes)
+        calls["mhc_pre_fused_bf16"] = (pre_kernels, breakdown["pre_bf16_ms"], step_bytes)
     if "head_ms" in breakdown:
-        calls["mhc_head"] = ("pre_prep_kernel+" + proj + "+pre_mixsum_kernel+" + col, breakdown["head_ms"],
-                             step_bytes)
+        calls["mhc_head"] = (pre_kernels, breakdown["head_ms"], step_bytes)
     if "pre_bwd_ms" in breakdown:
         calls["mhc_pre_fused_backward"] = ("pre_prep_kernel+" + proj + "+pre_mixsum_kernel+pre_dots_bwd_kernel+"
                                            "pre_bwd_partial_kernel+pre_bwd_final_kernel+proj_bwd_wfrag_kernel+"
@@ -443,7 +448,8 @@ def main():
 
     # Sanity figures: the launch floor of the step's kernel count (one-element fills,
     # launched the same way), and what a plain elementwise copy sustains here.
-    nker = {"all": 5, "pre": 4, "post": 1, "post_project": 3, "fused": 4}.get(args.only)
+    npre = 1 if pre_one_read(T, H) else 4
+    nker = {"all": npre + 1, "pre": npre, "post": 1, "post_project": 3, "fused": 4}.get(args.only)
     launch_floor_ms = None
     if nker:
         one = torch.zeros(1, device=dev)

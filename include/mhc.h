@@ -26,7 +26,12 @@
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Work is enqueued asynchronously on it; no call synchronises the host.
  *  - Ownership: the caller owns every buffer.  The library never allocates,
- *    frees or retains device memory; outputs are written in place.
+ *    frees or retains device memory, apart from the static scratch array of
+ *    mhc_pre_fused_noalloc; outputs are written in place.
+ *  - Large calls: token-parallel kernels are launched over token chunks, so that
+ *    every launch covers fewer than 2^31 work-items and at most 2^24 tokens (a HIP
+ *    grid dimension holds fewer than 2^32 work-items); mhc_launch_plan reports
+ *    the split.
  *  - Errors: arguments are validated on the host before anything is enqueued.
  *    On any error nothing is launched and no output is touched.  T == 0 is a
  *    successful no-op.  MHC_ERROR_LAUNCH reports a failed enqueue
@@ -62,6 +67,23 @@ int mhc_abi_version(void);
 
 /* Static, NUL-terminated description of a status code. */
 const char *mhc_status_string(mhc_status status);
+
+/*
+ * mhc_launch_plan -- diagnostics, host only (no HIP call, nothing enqueued): how an entry
+ * point splits a call into launches of its token-parallel kernel.  `entry` names the
+ * entry point without the mhc_ prefix: "post", "expand", "head_mean", "pre_fused" (its
+ * two-pass form; the collapse and the slice sums are its widest grids), "collapse" (the
+ * collapse of pre_from_dots with one split and a supplied sum of squares on 16-byte
+ * rows), "pre_from_dots" (its other forms), "pre_from_dots_backward", "post_backward",
+ * "sinkhorn", "sinkhorn_backward".  T is the
+ * token count (the matrix count for the Sinkhorn entry points), H the hidden size (unused
+ * for the Sinkhorn entry points), vec8 != 0 for 16-byte rows.  Writes the number of
+ * launches, the tokens per launch (the last launch may hold fewer) and the work-items of
+ * the widest launch (grid blocks times block size), which stays below 2^31.  Returns
+ * MHC_ERROR_INVALID_VALUE for an unknown name, a null output pointer, T < 0 or H < 1.
+ */
+mhc_status mhc_launch_plan(const char *entry, int64_t T, int64_t H, int32_t vec8, int64_t *launches,
+                           int64_t *tokens_per_launch, int64_t *max_items);
 
 /*
  * mhc_sinkhorn -- fixed-iteration Sinkhorn-Knopp projection of 4x4 logit
@@ -107,7 +129,10 @@ size_t mhc_pre_fused_workspace_bytes(int64_t T, int64_t H);
  *   res, hc_fn, hc_scale, hc_base   inputs (layouts above), device
  *   T >= 0, 1 <= H <= 2097152 (the streams of a 64-token tile are addressed with
  *                     32-bit byte offsets)
- *   rms_eps, pre_eps, sinkhorn_eps  finite; rms_eps and sinkhorn_eps > 0, pre_eps >= 0
+ *   rms_eps, pre_eps, sinkhorn_eps  finite; rms_eps and sinkhorn_eps > 0, pre_eps >= 0 (the
+ *                     FlashInfer article's parameter table of mhc_pre_big_fuse asks for a
+ *                     positive pre_eps; 0 is accepted here, since no later step divides by
+ *                     pre: it is then the plain sigmoid, in (0, 1))
  *   post_mult                       finite
  *   num_iters                       >= 1
  *   y [T,H], post [T,4], comb [T,4,4]   outputs, device; y must not overlap res

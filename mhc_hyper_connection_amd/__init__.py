@@ -49,6 +49,9 @@ def lib() -> ctypes.CDLL:
     L.mhc_abi_version.restype = ctypes.c_int
     L.mhc_status_string.argtypes = [ctypes.c_int]
     L.mhc_status_string.restype = ctypes.c_char_p
+    L.mhc_launch_plan.argtypes = [ctypes.c_char_p, I64, I64, I32, ctypes.POINTER(I64), ctypes.POINTER(I64),
+                                  ctypes.POINTER(I64)]
+    L.mhc_launch_plan.restype = ctypes.c_int
     L.mhc_sinkhorn.argtypes = [P, P, I64, I32, F, P]
     L.mhc_sinkhorn.restype = ctypes.c_int
     L.mhc_pre_fused_workspace_bytes.argtypes = [I64, I64]
@@ -92,6 +95,15 @@ def lib() -> ctypes.CDLL:
 
 def status_string(status: int) -> str:
     return lib().mhc_status_string(int(status)).decode()
+
+
+def launch_plan(entry: str, T: int, H: int, vec8: bool = True) -> dict:
+    """How `entry` (an entry point's name without the mhc_ prefix) splits a call at these
+    sizes into launches of its token-parallel kernel (host arithmetic only, no GPU call)."""
+    n, per, items = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check("mhc_launch_plan", lib().mhc_launch_plan(entry.encode(), int(T), int(H), int(bool(vec8)),
+                                                    ctypes.byref(n), ctypes.byref(per), ctypes.byref(items)))
+    return {"launches": n.value, "tokens_per_launch": per.value, "max_items": items.value}
 
 
 def abi_version() -> int:
@@ -662,5 +674,5 @@ __all__ = ["mhc_sinkhorn", "mhc_pre_fused", "mhc_pre_fused_noalloc", "mhc_pre_fu
            "mhc_sinkhorn_backward", "mhc_post_backward", "mhc_pre_from_dots_backward",
            "mhc_pre_backward_workspace_bytes", "mhc_pre_fused_backward", "mhc_pre_fused_backward_workspace_bytes",
            "mhc_post_project", "mhc_post_project_workspace_bytes",
-           "lib", "abi_version", "status_string", "MHCError", "HC",
+           "lib", "abi_version", "status_string", "launch_plan", "MHCError", "HC",
            "MIX", "SINKHORN_BWD_MAX_ITERS", "MHC_PRE_FUSED_NOALLOC_MAX_BYTES"]

@@ -6,6 +6,7 @@
 
 #include <atomic>
 #include <math.h>
+#include <string.h>
 
 namespace {
 
@@ -152,6 +153,49 @@ const char *mhc_status_string(mhc_status status)
         return "kernel launch failed";
     }
     return "unknown status";
+}
+
+mhc_status mhc_launch_plan(const char *entry, int64_t T, int64_t H, int32_t vec8, int64_t *launches,
+                           int64_t *tokens_per_launch, int64_t *max_items)
+{
+    if (!entry || !launches || !tokens_per_launch || !max_items || T < 0 || H < 1) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    const bool v = vec8 != 0;
+    int64_t per_tok = 0, block = 256, per_launch = 0;
+    if (!strcmp(entry, "post")) {
+        per_tok = mhc::post_items_per_token(H, v);
+    } else if (!strcmp(entry, "expand") || !strcmp(entry, "head_mean")) {
+        per_tok = mhc::stream_copy_items_per_token(H, v);
+    } else if (!strcmp(entry, "pre_fused")) {
+        const PreGeom g = mhc::pre_geometry(T > 0 ? T : 1, H);
+        per_tok = mhc::collapse_items_per_token(H, v);
+        per_tok = per_tok > (int64_t)g.nrec * 4 ? per_tok : (int64_t)g.nrec * 4; // slice sums: nrec * 256 per 64
+        per_launch = g.chunk;
+    } else if (!strcmp(entry, "collapse")) {
+        per_tok = mhc::collapse_items_per_token(H, v);
+    } else if (!strcmp(entry, "pre_from_dots")) {
+        per_tok = mhc::pre_dots_items_per_token();
+    } else if (!strcmp(entry, "pre_from_dots_backward")) {
+        per_tok = mhc::pre_dots_bwd_items_per_token();
+    } else if (!strcmp(entry, "post_backward")) {
+        per_tok = mhc::post_bwd_items_per_token();
+    } else if (!strcmp(entry, "sinkhorn")) {
+        per_tok = mhc::sinkhorn_items_per_matrix();
+    } else if (!strcmp(entry, "sinkhorn_backward")) {
+        per_tok = mhc::sinkhorn_bwd_items_per_matrix();
+        block = 64;
+    } else {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    if (per_launch == 0) {
+        per_launch = mhc::launch_tokens(per_tok);
+    }
+    const int64_t n = T < per_launch ? T : per_launch;
+    *launches = (T + per_launch - 1) / per_launch;
+    *tokens_per_launch = per_launch;
+    *max_items = (n * per_tok + block - 1) / block * block;
+    return MHC_SUCCESS;
 }
 
 mhc_status mhc_sinkhorn(const float *logits, float *out, int64_t n_mats, int32_t num_iters, float eps, void *stream)

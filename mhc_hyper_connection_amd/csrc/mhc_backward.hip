@@ -108,12 +108,12 @@ constexpr int kWsRow = 28; // floats per token in the workspace: 24 dz, 3 group 
 struct DotsBwdArgs {
     const uint16_t *dy;
     const float *d_post, *d_comb;
-    const float *dot_mix; // [S][T][24]
-    const float *sqrsum;  // [S][T] or null
+    const float *dot_mix; // [S][T][24], advanced to the launch's first token
+    const float *sqrsum;  // [S][T] or null (advanced likewise)
     int S;
     const uint16_t *res;
     const float *hc_scale, *hc_base;
-    int T, H;
+    int T, H; // T: tokens of the whole call, the split arrays' split stride
     float k, rms_eps, pre_eps, sk_eps, post_mult;
     int iters;
     uint16_t *d_res;
@@ -992,11 +992,13 @@ size_t sinkhorn_bwd_lds_bytes(int iters) { return (size_t)(iters + 1) * kSBBlock
 hipError_t launch_sinkhorn_bwd(const float *grad, const float *logits, int64_t n, int iters, float eps,
                                float *d_logits, hipStream_t stream)
 {
-    const int64_t threads = n * 16;
-    const int64_t blocks = (threads + kSBBlock - 1) / kSBBlock;
-    sinkhorn_bwd_kernel<<<dim3((unsigned)blocks), dim3(kSBBlock), sinkhorn_bwd_lds_bytes(iters), stream>>>(
-        grad, logits, n, iters, eps, d_logits);
-    return hipGetLastError();
+    return for_token_chunks(n, sinkhorn_bwd_items_per_matrix(), [&](int64_t c0, int64_t nc) {
+        const int64_t blocks = (nc * 16 + kSBBlock - 1) / kSBBlock;
+        const size_t o = (size_t)c0 * 16;
+        sinkhorn_bwd_kernel<<<dim3((unsigned)blocks), dim3(kSBBlock), sinkhorn_bwd_lds_bytes(iters), stream>>>(
+            grad + o, logits + o, nc, iters, eps, d_logits + o);
+        return hipGetLastError();
+    });
 }
 
 // Workspace: the [T][28] token rows, then the [ceil(T / 256)][28] block partials.
@@ -1015,15 +1017,17 @@ hipError_t launch_pre_dots_bwd(const uint16_t *dy, const float *d_post, const fl
                                hipStream_t stream, bool vec8)
 {
     float *ws = reinterpret_cast<float *>(workspace);
-    if (T > 0) {
+    const int64_t per = (H / 8 + kDBBlock - 1) / kDBBlock;
+    const size_t lds = (size_t)(iters + 1) * kWave * sizeof(float);
+    const hipError_t ec = for_token_chunks(T, pre_dots_bwd_items_per_token(), [&](int64_t c0, int64_t Tc) {
         DotsBwdArgs a{};
-        a.dy = dy;
-        a.d_post = d_post;
-        a.d_comb = d_comb;
-        a.dot_mix = dot_mix;
-        a.sqrsum = sqrsum;
+        a.dy = dy + (size_t)c0 * H;
+        a.d_post = d_post + (size_t)c0 * kHC;
+        a.d_comb = d_comb + (size_t)c0 * kHC * kHC;
+        a.dot_mix = dot_mix + (size_t)c0 * kMix; // split s of token c0 + t at ((s * T) + t) * 24
+        a.sqrsum = sqrsum ? sqrsum + c0 : nullptr;
         a.S = num_splits;
-        a.res = res;
+        a.res = res + (size_t)c0 * kHC * H;
         a.hc_scale = hc_scale;
         a.hc_base = hc_base;
         a.T = (int)T;
@@ -1034,13 +1038,11 @@ hipError_t launch_pre_dots_bwd(const uint16_t *dy, const float *d_post, const fl
         a.sk_eps = sinkhorn_eps;
         a.post_mult = post_mult;
         a.iters = iters;
-        a.d_res = d_res;
-        a.d_dot = d_dot;
-        a.d_sqrsum = d_sqrsum;
-        a.ws = ws;
-        const dim3 grid((unsigned)T), block(kDBBlock);
-        const size_t lds = (size_t)(iters + 1) * kWave * sizeof(float);
-        const int64_t per = (H / 8 + kDBBlock - 1) / kDBBlock;
+        a.d_res = d_res + (size_t)c0 * kHC * H;
+        a.d_dot = d_dot + (size_t)c0 * kMix;
+        a.d_sqrsum = d_sqrsum ? d_sqrsum + c0 : nullptr;
+        a.ws = ws + (size_t)c0 * kWsRow;
+        const dim3 grid((unsigned)Tc), block(kDBBlock);
         if (vec8 && per <= 1) {
             pre_dots_bwd_kernel<1><<<grid, block, lds, stream>>>(a);
         } else if (vec8 && per <= 2) {
@@ -1052,10 +1054,10 @@ hipError_t launch_pre_dots_bwd(const uint16_t *dy, const float *d_post, const fl
         } else {
             pre_dots_bwd_kernel<0><<<grid, block, lds, stream>>>(a);
         }
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) {
-            return e;
-        }
+        return hipGetLastError();
+    });
+    if (ec != hipSuccess) {
+        return ec;
     }
     const int64_t nblk = (T + kRedTok - 1) / kRedTok;
     float *part = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + pre_bwd_rows_bytes(T));
@@ -1238,34 +1240,41 @@ hipError_t launch_post_bwd(const uint16_t *d_out, const uint16_t *x, const uint1
                            const float *comb, int64_t T, int64_t H, uint16_t *d_x, uint16_t *d_res, float *d_post,
                            float *d_comb, hipStream_t stream, bool vec8)
 {
-    PostBwdArgs a{};
-    a.d_out = d_out;
-    a.x = x;
-    a.res = res;
-    a.post = post;
-    a.comb = comb;
-    a.T = (int)T;
-    a.H = (int)H;
-    a.d_x = d_x;
-    a.d_res = d_res;
-    a.d_post = d_post;
-    a.d_comb = d_comb;
     // 256 threads, kCPT 8-element chunks per thread and stream on the 16-byte path
     // (128- and 64-thread groups with exact chunk counts measured no faster at H=7168).
-    const dim3 grid((unsigned)T), block(256);
     const int64_t per = (H / 8 + 255) / 256;
-    if (vec8 && per <= 1) {
-        post_bwd_kernel<256, 1><<<grid, block, 0, stream>>>(a);
-    } else if (vec8 && per <= 2) {
-        post_bwd_kernel<256, 2><<<grid, block, 0, stream>>>(a);
-    } else if (vec8 && per <= 4) {
-        post_bwd_kernel<256, 4><<<grid, block, 0, stream>>>(a);
-    } else if (vec8 && per <= 8) {
-        post_bwd_kernel<256, 8><<<grid, block, 0, stream>>>(a);
-    } else {
-        post_bwd_kernel<256, 0><<<grid, block, 0, stream>>>(a);
-    }
-    return hipGetLastError();
+    return for_token_chunks(T, post_bwd_items_per_token(), [&](int64_t c0, int64_t Tc) {
+        PostBwdArgs a{};
+        const size_t s = (size_t)c0 * kHC * H;
+        a.d_out = d_out + s;
+        a.x = x + (size_t)c0 * H;
+        a.res = res + s;
+        a.post = post + (size_t)c0 * kHC;
+        a.comb = comb + (size_t)c0 * kHC * kHC;
+        a.T = (int)Tc;
+        a.H = (int)H;
+        a.d_x = d_x + (size_t)c0 * H;
+        a.d_res = d_res + s;
+        a.d_post = d_post + (size_t)c0 * kHC;
+        a.d_comb = d_comb + (size_t)c0 * kHC * kHC;
+        const dim3 grid((unsigned)Tc), block(256);
+        if (vec8 && per <= 1) {
+            post_bwd_kernel<256, 1><<<grid, block, 0, stream>>>(a);
+        } else if (vec8 && per <= 2) {
+            post_bwd_kernel<256, 2><<<grid, block, 0, stream>>>(a);
+        } else if (vec8 && per <= 4) {
+            post_bwd_kernel<256, 4><<<grid, block, 0, stream>>>(a);
+        } else if (vec8 && per <= 8) {
+            post_bwd_kernel<256, 8><<<grid, block, 0, stream>>>(a);
+        } else {
+            post_bwd_kernel<256, 0><<<grid, block, 0, stream>>>(a);
+        }
+        return hipGetLastError();
+    });
 }
+
+int64_t pre_dots_bwd_items_per_token() { return kDBBlock; }
+int64_t post_bwd_items_per_token() { return 256; }
+int64_t sinkhorn_bwd_items_per_matrix() { return 16; }
 
 } // namespace mhc

@@ -91,39 +91,47 @@ __global__ __launch_bounds__(kHBlock) void head_mean_kernel(const uint16_t *__re
     }
 }
 
-dim3 stream_grid(int64_t T, int64_t H, bool vec8, int &tiles)
+} // namespace
+
+int64_t stream_copy_items_per_token(int64_t H, bool vec8)
 {
     const int tile = vec8 ? kHVecTile : kWave;
-    tiles = (int)((H + tile - 1) / tile);
-    const int64_t waves = T * tiles;
-    return dim3((unsigned)((waves + kHWaves - 1) / kHWaves));
+    return (H + tile - 1) / tile * kWave;
 }
-
-} // namespace
 
 hipError_t launch_expand(const uint16_t *hidden, int64_t T, int64_t H, uint16_t *streams, hipStream_t stream,
                          bool vec8)
 {
-    int tiles;
-    const dim3 grid = stream_grid(T, H, vec8, tiles);
-    if (vec8) {
-        expand_kernel<true><<<grid, dim3(kHBlock), 0, stream>>>(hidden, (int)T, (int)H, tiles, streams);
-    } else {
-        expand_kernel<false><<<grid, dim3(kHBlock), 0, stream>>>(hidden, (int)T, (int)H, tiles, streams);
-    }
-    return hipGetLastError();
+    const int tile = vec8 ? kHVecTile : kWave;
+    const int tiles = (int)((H + tile - 1) / tile);
+    return for_token_chunks(T, stream_copy_items_per_token(H, vec8), [&](int64_t c0, int64_t Tc) {
+        const dim3 grid((unsigned)((Tc * tiles + kHWaves - 1) / kHWaves));
+        const uint16_t *hc = hidden + (size_t)c0 * H;
+        uint16_t *sc = streams + (size_t)c0 * kHC * H;
+        if (vec8) {
+            expand_kernel<true><<<grid, dim3(kHBlock), 0, stream>>>(hc, (int)Tc, (int)H, tiles, sc);
+        } else {
+            expand_kernel<false><<<grid, dim3(kHBlock), 0, stream>>>(hc, (int)Tc, (int)H, tiles, sc);
+        }
+        return hipGetLastError();
+    });
 }
 
 hipError_t launch_head_mean(const uint16_t *res, int64_t T, int64_t H, uint16_t *y, hipStream_t stream, bool vec8)
 {
-    int tiles;
-    const dim3 grid = stream_grid(T, H, vec8, tiles);
-    if (vec8) {
-        head_mean_kernel<true><<<grid, dim3(kHBlock), 0, stream>>>(res, (int)T, (int)H, tiles, y);
-    } else {
-        head_mean_kernel<false><<<grid, dim3(kHBlock), 0, stream>>>(res, (int)T, (int)H, tiles, y);
-    }
-    return hipGetLastError();
+    const int tile = vec8 ? kHVecTile : kWave;
+    const int tiles = (int)((H + tile - 1) / tile);
+    return for_token_chunks(T, stream_copy_items_per_token(H, vec8), [&](int64_t c0, int64_t Tc) {
+        const dim3 grid((unsigned)((Tc * tiles + kHWaves - 1) / kHWaves));
+        const uint16_t *rc = res + (size_t)c0 * kHC * H;
+        uint16_t *yc = y + (size_t)c0 * H;
+        if (vec8) {
+            head_mean_kernel<true><<<grid, dim3(kHBlock), 0, stream>>>(rc, (int)Tc, (int)H, tiles, yc);
+        } else {
+            head_mean_kernel<false><<<grid, dim3(kHBlock), 0, stream>>>(rc, (int)Tc, (int)H, tiles, yc);
+        }
+        return hipGetLastError();
+    });
 }
 
 } // namespace mhc

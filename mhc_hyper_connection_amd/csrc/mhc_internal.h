@@ -7,6 +7,46 @@
 
 namespace mhc {
 
+// Token-parallel launches are split into token chunks so that every launch covers fewer
+// than kLaunchItems work-items (a grid dimension holds fewer than 2^32; below 2^31 every
+// int index a kernel forms from its block and thread ids is exact) and at most
+// kLaunchTokens tokens (per-token offsets such as t * 24 stay far below 2^31).  Each
+// chunk is launched on pointers advanced to its first token.
+constexpr int64_t kLaunchItems = (int64_t)1 << 31;
+constexpr int64_t kLaunchTokens = (int64_t)1 << 24;
+
+// Tokens per launch of a grid with `items_per_token` work-items per token (a grid rounded
+// up to whole blocks adds fewer than one block).
+inline int64_t launch_tokens(int64_t items_per_token)
+{
+    const int64_t n = (kLaunchItems - 1024) / (items_per_token > 0 ? items_per_token : 1);
+    return n < 1 ? 1 : (n < kLaunchTokens ? n : kLaunchTokens);
+}
+
+// Calls f(c0, Tc) for the chunks [c0, c0 + Tc) of [0, T), stopping at the first error.
+template <typename F> hipError_t for_token_chunks(int64_t T, int64_t items_per_token, F &&f)
+{
+    const int64_t per = launch_tokens(items_per_token);
+    for (int64_t c0 = 0; c0 < T; c0 += per) {
+        const hipError_t e = f(c0, T - c0 < per ? T - c0 : per);
+        if (e != hipSuccess) {
+            return e;
+        }
+    }
+    return hipSuccess;
+}
+
+// Work-items per token (per matrix for the Sinkhorn kernels) of each token-parallel
+// kernel, as its launcher sizes the grid and its token chunks.
+int64_t post_items_per_token(int64_t H, bool vec8);
+int64_t stream_copy_items_per_token(int64_t H, bool vec8); // expand and head_mean
+int64_t collapse_items_per_token(int64_t H, bool vec8);    // the pre-map's collapse
+int64_t pre_dots_items_per_token();
+int64_t pre_dots_bwd_items_per_token();
+int64_t post_bwd_items_per_token();
+int64_t sinkhorn_items_per_matrix();
+int64_t sinkhorn_bwd_items_per_matrix();
+
 // Post-map.  `vec8`: H % 8 == 0 and x/res/out 16-byte aligned.
 hipError_t launch_post(const uint16_t *x, const uint16_t *res, const float *post, const float *comb, int64_t T,
                        int64_t H, uint16_t *out, hipStream_t stream, bool vec8);

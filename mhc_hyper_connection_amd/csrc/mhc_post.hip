@@ -49,11 +49,11 @@ __global__ __launch_bounds__(kPostBlock) void post_vec8_kernel(const uint16_t *_
     float p[kHC], c[kHC * kHC];
 #pragma unroll
     for (int n = 0; n < kHC; ++n) {
-        p[n] = post[t * kHC + n];
+        p[n] = post[(size_t)t * kHC + n];
     }
 #pragma unroll
     for (int e = 0; e < kHC * kHC; ++e) {
-        c[e] = comb[t * kHC * kHC + e];
+        c[e] = comb[(size_t)t * kHC * kHC + e];
     }
     const size_t row = (size_t)t * kHC * H + h;
     const u32x4 xw = load_nt16(x + (size_t)t * H + h);
@@ -116,10 +116,10 @@ __global__ __launch_bounds__(kPostBlock) void post_scalar_kernel(const uint16_t 
     }
 #pragma unroll
     for (int n = 0; n < kHC; ++n) {
-        float a = xf * post[t * kHC + n];
+        float a = xf * post[(size_t)t * kHC + n];
 #pragma unroll
         for (int o = 0; o < kHC; ++o) {
-            a = fmaf(rf[o], comb[t * kHC * kHC + o * kHC + n], a);
+            a = fmaf(rf[o], comb[(size_t)t * kHC * kHC + o * kHC + n], a);
         }
         out[row + (size_t)n * H] = f32_to_bf16(a);
     }
@@ -127,21 +127,31 @@ __global__ __launch_bounds__(kPostBlock) void post_scalar_kernel(const uint16_t 
 
 } // namespace
 
+int64_t post_items_per_token(int64_t H, bool vec8)
+{
+    const int tile = vec8 ? kVecTile : kWave;
+    return (H + tile - 1) / tile * kWave;
+}
+
 hipError_t launch_post(const uint16_t *x, const uint16_t *res, const float *post, const float *comb, int64_t T,
                        int64_t H, uint16_t *out, hipStream_t stream, bool vec8)
 {
     const int tile = vec8 ? kVecTile : kWave;
     const int64_t tiles = (H + tile - 1) / tile;
-    const int64_t waves = T * tiles;
-    const int64_t blocks = (waves + kPostWavesPerBlock - 1) / kPostWavesPerBlock;
-    if (vec8) {
-        post_vec8_kernel<<<dim3((unsigned)blocks), dim3(kPostBlock), 0, stream>>>(x, res, post, comb, (int)T, (int)H,
-                                                                                   (int)tiles, out);
-    } else {
-        post_scalar_kernel<<<dim3((unsigned)blocks), dim3(kPostBlock), 0, stream>>>(x, res, post, comb, (int)T,
-                                                                                     (int)H, (int)tiles, out);
-    }
-    return hipGetLastError();
+    return for_token_chunks(T, post_items_per_token(H, vec8), [&](int64_t c0, int64_t Tc) {
+        const int64_t blocks = (Tc * tiles + kPostWavesPerBlock - 1) / kPostWavesPerBlock;
+        const size_t s = (size_t)c0 * kHC * H;
+        if (vec8) {
+            post_vec8_kernel<<<dim3((unsigned)blocks), dim3(kPostBlock), 0, stream>>>(
+                x + (size_t)c0 * H, res + s, post + (size_t)c0 * kHC, comb + (size_t)c0 * kHC * kHC, (int)Tc,
+                (int)H, (int)tiles, out + s);
+        } else {
+            post_scalar_kernel<<<dim3((unsigned)blocks), dim3(kPostBlock), 0, stream>>>(
+                x + (size_t)c0 * H, res + s, post + (size_t)c0 * kHC, comb + (size_t)c0 * kHC * kHC, (int)Tc,
+                (int)H, (int)tiles, out + s);
+        }
+        return hipGetLastError();
+    });
 }
 
 } // namespace mhc

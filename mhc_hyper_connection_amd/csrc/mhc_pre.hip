@@ -32,6 +32,8 @@
 #include "mhc_device.h"
 #include "mhc_internal.h"
 
+#include <algorithm>
+
 namespace mhc {
 
 namespace {
@@ -1028,6 +1030,11 @@ PreGeom pre_geometry(int64_t T, int64_t H, bool with_dy)
     if (max_tiles < 1) {
         max_tiles = 1;
     }
+    // and every launch of a chunk stays within the launch limits: the collapse (at most a
+    // wave per 64 h of a token) and the slice sums (nrec blocks of 256 per tile) are its
+    // widest grids
+    const int64_t per_tok = std::max((H + kWave - 1) / kWave * kWave, (int64_t)g.nrec * 256 / kPTok);
+    max_tiles = std::min(max_tiles, std::max<int64_t>(1, launch_tokens(per_tok) / kPTok));
     g.tiles = (int)(tiles_total < max_tiles ? tiles_total : max_tiles);
     g.chunk = (int64_t)g.tiles * kPTok;
     size_t off = 0;
@@ -1114,9 +1121,7 @@ hipError_t launch_collapse_dots(const float *dots, const float *sq, const uint16
                                 float *comb, float *pre, hipStream_t stream)
 {
     const int64_t htiles = (H + kColVecTile - 1) / kColVecTile;
-    const int64_t max_tok = ((int64_t)1 << 30) / htiles; // waves per launch stay below 2^30
-    for (int64_t c0 = 0; c0 < T; c0 += max_tok) {
-        const int64_t Tc = T - c0 < max_tok ? T - c0 : max_tok;
+    return for_token_chunks(T, collapse_items_per_token(H, true), [&](int64_t c0, int64_t Tc) {
         MixArgs mx{};
         mx.sums = dots + (size_t)c0 * kMix;
         mx.stride = kMix;
@@ -1137,12 +1142,14 @@ hipError_t launch_collapse_dots(const float *dots, const float *sq, const uint16
         const int64_t blocks = (Tc * htiles + kColWaves - 1) / kColWaves;
         pre_collapse_vec8_kernel<<<dim3((unsigned)blocks), dim3(kColBlock), 0, stream>>>(
             res + (size_t)c0 * kHC * H, mx, (int)Tc, (int)H, (int)htiles, y + (size_t)c0 * H);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) {
-            return e;
-        }
-    }
-    return hipSuccess;
+        return hipGetLastError();
+    });
+}
+
+int64_t collapse_items_per_token(int64_t H, bool vec8)
+{
+    const int tile = vec8 ? kColVecTile : kWave;
+    return (H + tile - 1) / tile * kWave;
 }
 
 hipError_t launch_pre_sums(const uint16_t *res, const uint16_t *dy, const PreGeom &g, int64_t c0, int Tc,

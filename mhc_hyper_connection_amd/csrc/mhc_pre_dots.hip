@@ -25,13 +25,13 @@ constexpr int kDBlock = 256;
 constexpr int kDWaves = kDBlock / kWave;
 
 struct DotsArgs {
-    const float *dot_mix; // [S][T][24]
-    const float *sqrsum;  // [S][T], or null: computed from res
+    const float *dot_mix; // [S][T][24], advanced to the launch's first token
+    const float *sqrsum;  // [S][T], or null: computed from res (advanced likewise)
     int S;
     const uint16_t *res;
     const float *hc_scale;
     const float *hc_base;
-    int T, H;
+    int T, H; // T: tokens of the whole call, the split arrays' split stride
     float k, rms_eps, pre_eps, sk_eps, post_mult;
     int iters;
     uint16_t *y;
@@ -192,39 +192,43 @@ hipError_t launch_pre_dots(const float *dot_mix, const float *sqrsum, int num_sp
         return launch_collapse_dots(dot_mix, sqrsum, res, hc_scale, hc_base, T, H, k, rms_eps, pre_eps,
                                     sinkhorn_eps, post_mult, iters, y, post, comb, pre, stream);
     }
-    DotsArgs a{};
-    a.dot_mix = dot_mix;
-    a.sqrsum = sqrsum;
-    a.S = num_splits;
-    a.res = res;
-    a.hc_scale = hc_scale;
-    a.hc_base = hc_base;
-    a.T = (int)T;
-    a.H = (int)H;
-    a.k = k;
-    a.rms_eps = rms_eps;
-    a.pre_eps = pre_eps;
-    a.sk_eps = sinkhorn_eps;
-    a.post_mult = post_mult;
-    a.iters = iters;
-    a.y = y;
-    a.post = post;
-    a.comb = comb;
-    a.pre_out = pre;
-    const dim3 grid((unsigned)T), block(kDBlock);
     const int64_t per = (H / 8 + kDBlock - 1) / kDBlock; // 16-byte chunks per thread and stream
-    if (vec8 && per <= 1) {
-        pre_dots_kernel<1><<<grid, block, 0, stream>>>(a);
-    } else if (vec8 && per <= 2) {
-        pre_dots_kernel<2><<<grid, block, 0, stream>>>(a);
-    } else if (vec8 && per <= 4) {
-        pre_dots_kernel<4><<<grid, block, 0, stream>>>(a);
-    } else if (vec8 && per <= 8) {
-        pre_dots_kernel<8><<<grid, block, 0, stream>>>(a);
-    } else {
-        pre_dots_kernel<0><<<grid, block, 0, stream>>>(a);
-    }
-    return hipGetLastError();
+    return for_token_chunks(T, pre_dots_items_per_token(), [&](int64_t c0, int64_t Tc) {
+        DotsArgs a{};
+        a.dot_mix = dot_mix + (size_t)c0 * kMix; // split s of token c0 + t at ((s * T) + t) * 24
+        a.sqrsum = sqrsum ? sqrsum + c0 : nullptr;
+        a.S = num_splits;
+        a.res = res + (size_t)c0 * kHC * H;
+        a.hc_scale = hc_scale;
+        a.hc_base = hc_base;
+        a.T = (int)T;
+        a.H = (int)H;
+        a.k = k;
+        a.rms_eps = rms_eps;
+        a.pre_eps = pre_eps;
+        a.sk_eps = sinkhorn_eps;
+        a.post_mult = post_mult;
+        a.iters = iters;
+        a.y = y + (size_t)c0 * H;
+        a.post = post + (size_t)c0 * kHC;
+        a.comb = comb + (size_t)c0 * kHC * kHC;
+        a.pre_out = pre ? pre + (size_t)c0 * kHC : nullptr;
+        const dim3 grid((unsigned)Tc), block(kDBlock);
+        if (vec8 && per <= 1) {
+            pre_dots_kernel<1><<<grid, block, 0, stream>>>(a);
+        } else if (vec8 && per <= 2) {
+            pre_dots_kernel<2><<<grid, block, 0, stream>>>(a);
+        } else if (vec8 && per <= 4) {
+            pre_dots_kernel<4><<<grid, block, 0, stream>>>(a);
+        } else if (vec8 && per <= 8) {
+            pre_dots_kernel<8><<<grid, block, 0, stream>>>(a);
+        } else {
+            pre_dots_kernel<0><<<grid, block, 0, stream>>>(a);
+        }
+        return hipGetLastError();
+    });
 }
+
+int64_t pre_dots_items_per_token() { return kDBlock; }
 
 } // namespace mhc

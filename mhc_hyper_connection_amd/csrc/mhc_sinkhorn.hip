@@ -62,13 +62,20 @@ __global__ __launch_bounds__(kSkBlock) void sinkhorn_kernel(const float *logits,
 hipError_t launch_sinkhorn(const float *logits, float *out, int64_t n, int iters, float eps, hipStream_t stream,
                            bool vec4)
 {
-    const int64_t blocks = (n + kSkBlock - 1) / kSkBlock;
-    if (vec4) {
-        sinkhorn_kernel<true><<<dim3((unsigned)blocks), dim3(kSkBlock), 0, stream>>>(logits, out, n, iters, eps);
-    } else {
-        sinkhorn_kernel<false><<<dim3((unsigned)blocks), dim3(kSkBlock), 0, stream>>>(logits, out, n, iters, eps);
-    }
-    return hipGetLastError();
+    return for_token_chunks(n, sinkhorn_items_per_matrix(), [&](int64_t c0, int64_t nc) {
+        const int64_t blocks = (nc + kSkBlock - 1) / kSkBlock;
+        const size_t o = (size_t)c0 * 16;
+        if (vec4) {
+            sinkhorn_kernel<true><<<dim3((unsigned)blocks), dim3(kSkBlock), 0, stream>>>(logits + o, out + o, nc, iters,
+                                                                                         eps);
+        } else {
+            sinkhorn_kernel<false><<<dim3((unsigned)blocks), dim3(kSkBlock), 0, stream>>>(logits + o, out + o, nc,
+                                                                                          iters, eps);
+        }
+        return hipGetLastError();
+    });
 }
+
+int64_t sinkhorn_items_per_matrix() { return 1; }
 
 } // namespace mhc

@@ -394,3 +394,57 @@ def test_binding_rejects_cpu_tensors_before_the_library():
     with pytest.raises(ValueError):
         mhc.mhc_post_backward(torch.zeros(2, 4, 8, dtype=torch.bfloat16), torch.zeros(2, 8, dtype=torch.bfloat16),
                               torch.zeros(2, 4, 8, dtype=torch.bfloat16), torch.zeros(2, 4), torch.zeros(2, 4, 4))
+
+
+PLAN_ENTRIES = ["post", "expand", "head_mean", "pre_fused", "collapse", "pre_from_dots", "pre_from_dots_backward",
+                "post_backward", "sinkhorn", "sinkhorn_backward"]
+
+
+@pytest.mark.parametrize("entry", PLAN_ENTRIES)
+@pytest.mark.parametrize("vec8", [True, False])
+def test_launch_plan_keeps_every_launch_below_the_grid_limit(entry, vec8):
+    """Host grid arithmetic only (no GPU): at the largest sizes validation accepts, every
+    launch covers fewer than 2^31 work-items (a grid dimension must stay below 2^32) and
+    at most 2^24 tokens, and the launches cover all T tokens."""
+    sizes = [(1 << 27, 8), ((1 << 29) - 1, 64), (1 << 22, 1000), (825_000, 6400), (8192, 7168), (300, 1 << 21),
+             (1, 1 << 21), (1, 1), (0, 64)]
+    if entry.startswith("sinkhorn"):
+        sizes = [(1 << 32, 1), ((1 << 40), 1), (1 << 20, 1), (1, 1), (0, 1)]
+    for T, H in sizes:
+        p = mhc.launch_plan(entry, T, H, vec8)
+        assert p["max_items"] < 1 << 31, (entry, T, H, p)
+        assert 1 <= p["tokens_per_launch"] <= 1 << 24, (entry, T, H, p)
+        assert p["launches"] * p["tokens_per_launch"] >= T > (p["launches"] - 1) * p["tokens_per_launch"] or T == 0, \
+            (entry, T, H, p)
+        # per-token offsets of 24 fp32 (t * 24) inside one launch stay int-exact
+        assert p["tokens_per_launch"] * 24 < 1 << 31
+
+
+def test_launch_plan_cases_from_the_review():
+    """T = 2^27 at H = 8 splits the post-map into launches of 2^24 tokens (its coefficient
+    offsets t * 16 stay below 2^28), and 2^32 Sinkhorn matrices into 256 launches."""
+    p = mhc.launch_plan("post", 1 << 27, 8, True)
+    assert p == {"launches": 8, "tokens_per_launch": 1 << 24, "max_items": (1 << 24) * 64}
+    p = mhc.launch_plan("post", 1 << 27, 8, False)
+    assert p["launches"] == 8 and p["max_items"] == (1 << 24) * 64
+    p = mhc.launch_plan("sinkhorn", 1 << 32, 1, True)
+    assert p == {"launches": 256, "tokens_per_launch": 1 << 24, "max_items": 1 << 24}
+    p = mhc.launch_plan("sinkhorn_backward", 1 << 32, 1, True)
+    assert p["launches"] == 256 and p["max_items"] == (1 << 24) * 16
+    # a scalar collapse at T = 825 000, H = 6400 (42 GB of streams) would need 5.3e9
+    # work-items in one launch; the pre-map's chunks keep it below 2^31
+    p = mhc.launch_plan("pre_fused", 825_000, 6400, False)
+    assert p["launches"] >= 3 and p["max_items"] < 1 << 31
+
+
+def test_launch_plan_rejects_bad_arguments():
+    lib = mhc.lib()
+    n = ctypes.c_int64()
+    assert lib.mhc_launch_plan(b"nope", 1, 1, 1, ctypes.byref(n), ctypes.byref(n), ctypes.byref(n)) == \
+        mhc.MHC_ERROR_INVALID_VALUE
+    assert lib.mhc_launch_plan(b"post", -1, 1, 1, ctypes.byref(n), ctypes.byref(n), ctypes.byref(n)) == \
+        mhc.MHC_ERROR_INVALID_VALUE
+    assert lib.mhc_launch_plan(b"post", 1, 0, 1, ctypes.byref(n), ctypes.byref(n), ctypes.byref(n)) == \
+        mhc.MHC_ERROR_INVALID_VALUE
+    assert lib.mhc_launch_plan(b"post", 1, 1, 1, None, ctypes.byref(n), ctypes.byref(n)) == \
+        mhc.MHC_ERROR_INVALID_VALUE
