@@ -40,9 +40,15 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not _LIB_PATH.exists() or _LIB_PATH.stat().st_mtime < _SRC.stat().st_mtime:
-        build()
-    lib = ctypes.CDLL(str(_LIB_PATH))
+    # MHC_ORACLE_LIB names another build of this source to load instead: the planted-mistake
+    # test builds mutated copies and runs the pins against each.
+    alt = os.environ.get("MHC_ORACLE_LIB")
+    if alt:
+        lib = ctypes.CDLL(alt)
+    else:
+        if not _LIB_PATH.exists() or _LIB_PATH.stat().st_mtime < _SRC.stat().st_mtime:
+            build()
+        lib = ctypes.CDLL(str(_LIB_PATH))
     P = ctypes.c_void_p
     I64 = ctypes.c_int64
     D = ctypes.c_double
