@@ -139,6 +139,19 @@ def layer_inputs(T: int, H: int, cfg: int, seed: int = 0, *, hc_fn_std: float = 
     return LayerInputs(T, H, res, x, hc_fn, hc_scale, hc_base, dict(DEFAULT_PARAMS))
 
 
+def f32_streams(T: int, H: int, cfg: int, seed: int = 0, std: float = 1.0) -> np.ndarray:
+    """FP32 residual streams [T, 4, H] ~ N(0, std): full fp32 values (almost none are bf16
+    values), for the fp32-stream entry points."""
+    return normal_f32(seed, cfg, "res", (T, HC, H), std)
+
+
+def layer_inputs_f32s(T: int, H: int, cfg: int, seed: int = 0, **kw) -> LayerInputs:
+    """layer_inputs with FP32 streams (res float32 [T, 4, H]); x stays bf16."""
+    inp = layer_inputs(T, H, cfg, seed, **kw)
+    inp.res = f32_streams(T, H, cfg, seed)
+    return inp
+
+
 def named_layer(name: str, seed: int = 0) -> LayerInputs:
     cfg, T, H = LAYER_SHAPES[name]
     return layer_inputs(T, H, cfg, seed)

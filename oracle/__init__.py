@@ -71,9 +71,17 @@ def _load():
     lib.orc_head_mean.argtypes = [P, I64, I64, P]
     lib.orc_head.argtypes = [P, P, P, P, I64, I64, D, D, P, P]
     lib.orc_pre_backward.argtypes = [P, P, P, P, P, P, P, I64, I64, D, D, D, D, ctypes.c_int, P, P, P, P, P]
+    lib.orc_rms_f32s.argtypes = [P, I64, I64, D, P, P]
+    lib.orc_project_f32s.argtypes = [P, P, I64, I64, P]
+    lib.orc_collapse_f32s.argtypes = [P, P, I64, I64, P]
+    lib.orc_pre_f32s.argtypes = [P, P, P, P, I64, I64, D, D, D, D, ctypes.c_int, P, P, P, P]
+    lib.orc_post_f32s.argtypes = [P, P, P, P, I64, I64, P]
+    lib.orc_expand_f32s.argtypes = [P, I64, I64, P]
+    lib.orc_head_mean_f32s.argtypes = [P, I64, I64, P]
     for f in ("orc_round_bf16", "orc_rms", "orc_project", "orc_mix_activation", "orc_sinkhorn",
               "orc_collapse", "orc_post", "orc_pre", "orc_pre_from_dots", "orc_sinkhorn_backward",
-              "orc_post_backward"):
+              "orc_post_backward", "orc_rms_f32s", "orc_project_f32s", "orc_collapse_f32s", "orc_pre_f32s",
+              "orc_post_f32s", "orc_expand_f32s", "orc_head_mean_f32s"):
         getattr(lib, f).restype = None
     _lib = lib
     return lib
@@ -335,3 +343,93 @@ def head(res, hc_fn, hc_scale, hc_base, norm_eps=1e-6, hc_eps=1e-6):
     pre_ = np.empty((T, HC))
     _load().orc_head(_p(res), _p(hc_fn), _p(hc_scale), _p(hc_base), T, H, norm_eps, hc_eps, _p(y), _p(pre_))
     return dict(y=y, pre=pre_)
+
+
+# ---------------------------------------------------------------- fp32 residual streams
+# The same steps on FP32 [T, 4, H] streams (metrale hyper_connection_dispatch.rs, module
+# header; glm5next_mhc.rs, glm_hc_expand / glm_hc_pre / glm_hc_post).  res is float32.
+
+def rms_f32s(res: np.ndarray, rms_eps: float):
+    """Step A1 on fp32 streams: (sqsum [T], rstd [T])."""
+    res = _c(res, np.float32)
+    T, hc, H = res.shape
+    assert hc == HC
+    sq = np.empty(T)
+    rstd = np.empty(T)
+    _load().orc_rms_f32s(_p(res), T, H, float(rms_eps), _p(sq), _p(rstd))
+    return sq, rstd
+
+
+def project_f32s(res: np.ndarray, hc_fn: np.ndarray) -> np.ndarray:
+    """Step A2 on fp32 streams: dot [T,24]."""
+    res = _c(res, np.float32)
+    T, hc, H = res.shape
+    assert hc == HC
+    hc_fn = _c(hc_fn, np.float32)
+    assert hc_fn.shape == (MIX, HC * H)
+    dot = np.empty((T, MIX))
+    _load().orc_project_f32s(_p(res), _p(hc_fn), T, H, _p(dot))
+    return dot
+
+
+def collapse_f32s(res: np.ndarray, pre: np.ndarray) -> np.ndarray:
+    """Step A5 on fp32 streams: y [T,H] fp64 (unrounded)."""
+    res = _c(res, np.float32)
+    T, hc, H = res.shape
+    assert hc == HC
+    pre = _c(pre, np.float64).reshape(T, HC)
+    y = np.empty((T, H))
+    _load().orc_collapse_f32s(_p(res), _p(pre), T, H, _p(y))
+    return y
+
+
+def pre_f32s(res, hc_fn, hc_scale, hc_base, rms_eps=1e-6, pre_eps=1e-6, sinkhorn_eps=1e-6, post_mult=1.0,
+             num_iters=20):
+    """The pre-map on fp32 streams res [T,4,H].  Returns dict of fp64 arrays: y, post, comb, pre."""
+    res = _c(res, np.float32)
+    T, hc, H = res.shape
+    assert hc == HC
+    hc_fn = _c(hc_fn, np.float32)
+    assert hc_fn.shape == (MIX, HC * H)
+    y = np.empty((T, H))
+    post_ = np.empty((T, HC))
+    comb = np.empty((T, HC, HC))
+    pre_ = np.empty((T, HC))
+    _load().orc_pre_f32s(_p(res), _p(hc_fn), _p(_c(hc_scale, np.float32)), _p(_c(hc_base, np.float32)), T, H,
+                         rms_eps, pre_eps, sinkhorn_eps, post_mult, int(num_iters), _p(y), _p(post_), _p(comb),
+                         _p(pre_))
+    return dict(y=y, post=post_, comb=comb, pre=pre_)
+
+
+def post_f32s(x: np.ndarray, res: np.ndarray, post: np.ndarray, comb: np.ndarray) -> np.ndarray:
+    """Step A6 on fp32 streams: x [T,H] bf16 bits, res [T,4,H] fp32, post [T,4], comb [T,4,4]
+    (real values) -> out [T,4,H] fp64 (unrounded)."""
+    res = _c(res, np.float32)
+    T, hc, H = res.shape
+    assert hc == HC
+    x = _c(x, np.uint16)
+    assert x.shape == (T, H)
+    post = _c(post, np.float64).reshape(T, HC)
+    comb = _c(comb, np.float64).reshape(T, HC, HC)
+    out = np.empty((T, HC, H))
+    _load().orc_post_f32s(_p(x), _p(res), _p(post), _p(comb), T, H, _p(out))
+    return out
+
+
+def expand_f32s(hidden):
+    """Model entry on fp32 streams: [T,H] bf16 bits -> [T,4,H] float32 (exact widening)."""
+    hidden = _c(hidden, np.uint16)
+    T, H = hidden.shape
+    out = np.empty((T, HC, H), np.float32)
+    _load().orc_expand_f32s(_p(hidden), T, H, _p(out))
+    return out
+
+
+def head_mean_f32s(res):
+    """Model exit, unweighted, on fp32 streams: [T,H] fp64 (unrounded)."""
+    res = _c(res, np.float32)
+    T, hc, H = res.shape
+    assert hc == HC
+    y = np.empty((T, H))
+    _load().orc_head_mean_f32s(_p(res), T, H, _p(y))
+    return y

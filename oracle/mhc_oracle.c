@@ -646,3 +646,127 @@ void orc_head(const uint16_t *res, const float *hc_fn, const float *hc_scale, co
         orc_collapse(r, pre + t * ORC_HC, 1, H, y + t * H);
     }
 }
+
+/* ---------------------------------------------------------------------------------------
+ * FP32 residual streams (metrale hyper_connection_dispatch.rs, module header: both mixer
+ * families run over FP32 [T, hc_mult, H] streams; metrale glm5next_mhc.rs: glm_hc_expand
+ * broadcasts each BF16 hidden row into its FP32 highway streams, glm_hc_pre collapses the
+ * FP32 streams to one BF16 row and writes post and comb, glm_hc_post writes the new
+ * streams with the same formula).  Every step is the one of the bf16-stream functions
+ * above, with the streams read as fp32 (widened exactly to fp64).
+ * ------------------------------------------------------------------------------------- */
+
+/* Step A1 on fp32 streams: S = sum_{i,h} res^2, rstd = 1 / sqrt(S / (4H) + rms_eps). */
+void orc_rms_f32s(const float *res, int64_t T, int64_t H, double rms_eps, double *sqsum, double *rstd)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        double s = 0.0;
+        for (int64_t i = 0; i < ORC_HC; ++i) {
+            for (int64_t h = 0; h < H; ++h) {
+                double v = (double)res[(t * ORC_HC + i) * H + h];
+                s += v * v;
+            }
+        }
+        if (sqsum) {
+            sqsum[t] = s;
+        }
+        rstd[t] = 1.0 / sqrt(s / (double)(ORC_HC * H) + rms_eps);
+    }
+}
+
+/* Step A2 on fp32 streams: dot[t][r] = sum_k hc_fn[r][k] * res_flat[t][k], k = i*H + h. */
+void orc_project_f32s(const float *res, const float *hc_fn, int64_t T, int64_t H, double *dot)
+{
+    const int64_t K = ORC_HC * H;
+    for (int64_t t = 0; t < T; ++t) {
+        const float *row = res + t * K;
+        for (int64_t r = 0; r < ORC_MIX; ++r) {
+            const float *w = hc_fn + r * K;
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                acc += (double)w[k] * (double)row[k];
+            }
+            dot[t * ORC_MIX + r] = acc;
+        }
+    }
+}
+
+/* Step A5 on fp32 streams: y[t][h] = sum_i pre[t][i] * res[t][i][h] (fp64, unrounded;
+ * the layer input is a BF16 row, so callers round it once). */
+void orc_collapse_f32s(const float *res, const double *pre, int64_t T, int64_t H, double *y)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t h = 0; h < H; ++h) {
+            double acc = 0.0;
+            for (int i = 0; i < ORC_HC; ++i) {
+                acc += pre[t * ORC_HC + i] * (double)res[(t * ORC_HC + i) * H + h];
+            }
+            y[t * H + h] = acc;
+        }
+    }
+}
+
+/* The whole pre-map on fp32 streams, one token at a time: A1 -> A2 -> A3 -> A4 -> A5.
+ * y [T,H], post [T,4], comb [T,4,4], pre [T,4] are fp64, unrounded. */
+void orc_pre_f32s(const float *res, const float *hc_fn, const float *hc_scale, const float *hc_base, int64_t T,
+                  int64_t H, double rms_eps, double pre_eps, double sinkhorn_eps, double post_mult, int num_iters,
+                  double *y, double *post, double *comb, double *pre)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        const float *r = res + t * ORC_HC * H;
+        double rstd, dot[ORC_MIX], logits[ORC_HC * ORC_HC];
+        orc_rms_f32s(r, 1, H, rms_eps, NULL, &rstd);
+        orc_project_f32s(r, hc_fn, 1, H, dot);
+        orc_mix_activation(dot, &rstd, hc_scale, hc_base, 1, pre_eps, post_mult, pre + t * ORC_HC,
+                           post + t * ORC_HC, logits);
+        orc_sinkhorn(logits, 1, num_iters, sinkhorn_eps, comb + t * ORC_HC * ORC_HC);
+        orc_collapse_f32s(r, pre + t * ORC_HC, 1, H, y + t * H);
+    }
+}
+
+/* Step A6 on fp32 streams: out[t][n][h] = x[t][h] * post[t][n] + sum_o res[t][o][h] *
+ * comb[t][o][n], with x the BF16 sublayer output and res the fp32 streams; fp64,
+ * unrounded (the new streams are fp32, so callers round them once). */
+void orc_post_f32s(const uint16_t *x, const float *res, const double *post, const double *comb, int64_t T,
+                   int64_t H, double *out)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        for (int n = 0; n < ORC_HC; ++n) {
+            for (int64_t h = 0; h < H; ++h) {
+                double acc = orc_bf16_to_f64(x[t * H + h]) * post[t * ORC_HC + n];
+                for (int o = 0; o < ORC_HC; ++o) {
+                    acc += (double)res[(t * ORC_HC + o) * H + h] * comb[(t * ORC_HC + o) * ORC_HC + n];
+                }
+                out[(t * ORC_HC + n) * H + h] = acc;
+            }
+        }
+    }
+}
+
+/* Model entry on fp32 streams (glm_hc_expand): streams[t][i][h] = hidden[t][h], the BF16
+ * value widened exactly to fp32. */
+void orc_expand_f32s(const uint16_t *hidden, int64_t T, int64_t H, float *streams)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        for (int i = 0; i < ORC_HC; ++i) {
+            for (int64_t h = 0; h < H; ++h) {
+                streams[(t * ORC_HC + i) * H + h] = (float)orc_bf16_to_f64(hidden[t * H + h]);
+            }
+        }
+    }
+}
+
+/* Model exit, unweighted, on fp32 streams (hc_head_mean): y[t][h] = (1/4) sum_i res[t][i][h],
+ * fp64, unrounded. */
+void orc_head_mean_f32s(const float *res, int64_t T, int64_t H, double *y)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t h = 0; h < H; ++h) {
+            double acc = 0.0;
+            for (int i = 0; i < ORC_HC; ++i) {
+                acc += (double)res[(t * ORC_HC + i) * H + h];
+            }
+            y[t * H + h] = acc / ORC_HC;
+        }
+    }
+}

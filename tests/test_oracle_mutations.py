@@ -22,10 +22,10 @@ PINS = ["tests/test_oracle_pins.py", "tests/test_golden_layout.py"]
 # (name, text in mhc_oracle.c (must occur exactly once), replacement)
 MUTANTS = [
     ("bf16 rounding ties away from zero", "double qr = nearbyint(q);", "double qr = floor(q + 0.5);"),
-    ("RMS over H instead of 4H", "rstd[t] = 1.0 / sqrt(s / (double)(ORC_HC * H) + rms_eps);",
-     "rstd[t] = 1.0 / sqrt(s / (double)(H) + rms_eps);"),
-    ("RMS without eps", "rstd[t] = 1.0 / sqrt(s / (double)(ORC_HC * H) + rms_eps);",
-     "rstd[t] = 1.0 / sqrt(s / (double)(ORC_HC * H));"),
+    ("RMS over H instead of 4H", "rstd[t] = 1.0 / sqrt(s / (double)(ORC_HC * H) + rms_eps);\n    }\n}\n\n/* Step A2:",
+     "rstd[t] = 1.0 / sqrt(s / (double)(H) + rms_eps);\n    }\n}\n\n/* Step A2:"),
+    ("RMS without eps", "rstd[t] = 1.0 / sqrt(s / (double)(ORC_HC * H) + rms_eps);\n    }\n}\n\n/* Step A2:",
+     "rstd[t] = 1.0 / sqrt(s / (double)(ORC_HC * H));\n    }\n}\n\n/* Step A2:"),
     ("projection flattens h-major", "acc += (double)w[k] * orc_bf16_to_f64(row[k]);",
      "acc += (double)w[k] * orc_bf16_to_f64(row[(k % H) * ORC_HC + k / H]);"),
     ("pre and post scales swapped", "const double s_pre = hc_scale[0], s_post = hc_scale[1], s_comb = hc_scale[2];",
@@ -78,7 +78,24 @@ MUTANTS = [
      "v += dd[t * ORC_MIX + r] * orc_bf16_to_f64(res[((t + 1) % T) * K + kk]);"),
     ("expand reverses h", "streams[(t * ORC_HC + i) * H + h] = hidden[t * H + h];",
      "streams[(t * ORC_HC + i) * H + h] = hidden[t * H + (H - 1 - h)];"),
-    ("head mean over 3", "y[t * H + h] = acc / ORC_HC;", "y[t * H + h] = acc / (ORC_HC - 1);"),
+    ("head mean over 3", "y[t * H + h] = acc / ORC_HC;\n        }\n    }\n}\n\n/* Model exit, weighted",
+     "y[t * H + h] = acc / (ORC_HC - 1);\n        }\n    }\n}\n\n/* Model exit, weighted"),
+    ("fp32 streams: RMS over H", "rstd[t] = 1.0 / sqrt(s / (double)(ORC_HC * H) + rms_eps);\n    }\n}\n\n/* Step A2 on fp32",
+     "rstd[t] = 1.0 / sqrt(s / (double)(H) + rms_eps);\n    }\n}\n\n/* Step A2 on fp32"),
+    ("fp32 streams: projection flattens h-major", "acc += (double)w[k] * (double)row[k];",
+     "acc += (double)w[k] * (double)row[(k % H) * ORC_HC + k / H];"),
+    ("fp32 streams: collapse with the streams reversed",
+     "acc += pre[t * ORC_HC + i] * (double)res[(t * ORC_HC + i) * H + h];",
+     "acc += pre[t * ORC_HC + i] * (double)res[(t * ORC_HC + (ORC_HC - 1 - i)) * H + h];"),
+    ("fp32 streams: post-map with comb transposed",
+     "acc += (double)res[(t * ORC_HC + o) * H + h] * comb[(t * ORC_HC + o) * ORC_HC + n];",
+     "acc += (double)res[(t * ORC_HC + o) * H + h] * comb[(t * ORC_HC + n) * ORC_HC + o];"),
+    ("fp32 streams: expand rounds through bf16 twice",
+     "streams[(t * ORC_HC + i) * H + h] = (float)orc_bf16_to_f64(hidden[t * H + h]);",
+     "streams[(t * ORC_HC + i) * H + h] = (float)orc_bf16_to_f64(hidden[t * H + h]) * (1.0f + 0x1p-20f);"),
+    ("fp32 streams: head mean over 3",
+     "acc += (double)res[(t * ORC_HC + i) * H + h];\n            }\n            y[t * H + h] = acc / ORC_HC;",
+     "acc += (double)res[(t * ORC_HC + i) * H + h];\n            }\n            y[t * H + h] = acc / (ORC_HC - 1);"),
     ("weighted head without hc_eps",
      "pre[t * ORC_HC + i] = orc_sigmoid(acc * rstd * (double)hc_scale[0] + (double)hc_base[i]) + hc_eps;",
      "pre[t * ORC_HC + i] = orc_sigmoid(acc * rstd * (double)hc_scale[0] + (double)hc_base[i]);"),

@@ -15,8 +15,8 @@ import numpy as np
 import pytest
 
 import oracle
-from mhc_inputs import (HC, MIX, bf16_bits_to_f32, f32_to_bf16_bits, layer_inputs, sinkhorn_logits,
-                        stress_logits)
+from mhc_inputs import (HC, MIX, bf16_bits_to_f32, f32_to_bf16_bits, layer_inputs, layer_inputs_f32s,
+                        sinkhorn_logits, stress_logits)
 
 pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
 
@@ -711,3 +711,109 @@ def test_head_zero_scale_and_stream_permutation():
     p = oracle.head(inp.res[:, perm], fn_p, np.ones(1, np.float32), b[perm])
     assert np.allclose(p["y"], a["y"], rtol=0, atol=1e-12)
     assert np.allclose(p["pre"], a["pre"][:, perm], rtol=0, atol=1e-14)
+
+
+# ---------------------------------------------------------------- fp32 residual streams
+
+def test_f32_streams_holding_bf16_values_reduce_to_the_bf16_oracle():
+    """fp32 streams whose values are bf16 values: every fp32-stream function equals its
+    (pinned) bf16-stream counterpart bit for bit."""
+    inp = layer_inputs(6, 40, cfg=150, scale=(0.8, 1.2, 1.1))
+    wide = bf16_bits_to_f32(inp.res)
+    a = oracle.pre(inp.res, inp.hc_fn, inp.hc_scale, inp.hc_base, post_mult=2.0)
+    b = oracle.pre_f32s(wide, inp.hc_fn, inp.hc_scale, inp.hc_base, post_mult=2.0)
+    for k in ("y", "post", "comb", "pre"):
+        assert np.array_equal(a[k], b[k]), k
+    g = np.random.default_rng(5)
+    post = g.uniform(0, 2, (6, HC))
+    comb = g.uniform(0, 1, (6, HC, HC))
+    assert np.array_equal(oracle.post(inp.x, inp.res, post, comb), oracle.post_f32s(inp.x, wide, post, comb))
+    assert np.array_equal(oracle.head_mean(inp.res), oracle.head_mean_f32s(wide))
+    assert np.array_equal(oracle.rms(inp.res, 1e-6)[1], oracle.rms_f32s(wide, 1e-6)[1])
+    assert np.array_equal(oracle.project(inp.res, inp.hc_fn), oracle.project_f32s(wide, inp.hc_fn))
+
+
+def test_f32_streams_keep_their_low_bits():
+    """Values below bf16 resolution reach the result: 1 + 2^-20 in every stream element
+    gives sum squares 4H (1 + 2^-20)^2 exactly in fp64, and a collapse that sees them."""
+    H = 16
+    res = np.full((1, HC, H), 1.0 + 2.0 ** -20, np.float32)
+    sq, rstd = oracle.rms_f32s(res, 0.0)
+    assert sq[0] == 4 * H * (1.0 + 2.0 ** -20) ** 2
+    assert rstd[0] == 1.0 / (1.0 + 2.0 ** -20)
+    y = oracle.collapse_f32s(res, np.array([[0.25, 0.25, 0.25, 0.25]]))
+    assert np.all(y == 1.0 + 2.0 ** -20)
+
+
+def test_f32_stream_steps_match_numpy():
+    inp = layer_inputs_f32s(5, 48, cfg=151)
+    r = inp.res.astype(np.float64)
+    T, _, H = r.shape
+    flat = r.reshape(T, HC * H)
+    sq, rstd = oracle.rms_f32s(inp.res, 1e-6)
+    assert np.allclose(sq, (flat * flat).sum(axis=1), rtol=1e-14, atol=0)
+    assert np.allclose(rstd, 1 / np.sqrt(sq / (HC * H) + 1e-6), rtol=1e-15, atol=0)
+    assert np.allclose(oracle.project_f32s(inp.res, inp.hc_fn), flat @ inp.hc_fn.astype(np.float64).T,
+                       rtol=1e-12, atol=1e-13)
+    pre = np.random.default_rng(3).uniform(0, 1, (T, HC))
+    assert np.allclose(oracle.collapse_f32s(inp.res, pre), np.einsum("ti,tih->th", pre, r), rtol=1e-14, atol=1e-14)
+    g = np.random.default_rng(4)
+    post = g.uniform(0, 2, (T, HC))
+    comb = g.uniform(0, 1, (T, HC, HC))
+    out = oracle.post_f32s(inp.x, inp.res, post, comb)
+    ref = _bf16_f64(inp.x)[:, None, :] * post[:, :, None] + np.einsum("toh,ton->tnh", r, comb)
+    assert np.allclose(out, ref, rtol=1e-14, atol=1e-14)
+    assert np.allclose(oracle.head_mean_f32s(inp.res), r.mean(axis=1), rtol=0, atol=1e-15)
+
+
+def test_f32_stream_post_orientation_and_identity():
+    """Identity comb with post = 0 returns the streams exactly; a permutation comb sends
+    old stream o to new stream perm[o]."""
+    inp = layer_inputs_f32s(3, 20, cfg=152)
+    eye = np.broadcast_to(np.eye(HC), (3, HC, HC))
+    out = oracle.post_f32s(inp.x, inp.res, np.zeros((3, HC)), eye)
+    assert np.array_equal(out, inp.res.astype(np.float64))
+    perm = [1, 3, 0, 2]
+    P = np.zeros((3, HC, HC))
+    for o, n in enumerate(perm):
+        P[:, o, n] = 1.0
+    out = oracle.post_f32s(inp.x, inp.res, np.zeros((3, HC)), P)
+    for o, n in enumerate(perm):
+        assert np.array_equal(out[:, n], inp.res[:, o].astype(np.float64))
+
+
+def test_f32_stream_pre_matches_independent_composition():
+    inp = layer_inputs_f32s(8, 64, cfg=153, scale=(1.1, 0.9, 1.3))
+    o = oracle.pre_f32s(inp.res, inp.hc_fn, inp.hc_scale, inp.hc_base, post_mult=2.0)
+    r = inp.res.astype(np.float64)
+    T, _, H = r.shape
+    flat = r.reshape(T, HC * H)
+    rstd = 1.0 / np.sqrt((flat * flat).sum(axis=1) / (HC * H) + 1e-6)
+    m = (flat @ inp.hc_fn.astype(np.float64).T) * rstd[:, None]
+    s, b = inp.hc_scale.astype(np.float64), inp.hc_base.astype(np.float64)
+    pre = _sig(m[:, 0:4] * s[0] + b[0:4]) + 1e-6
+    post = _sig(m[:, 4:8] * s[1] + b[4:8]) * 2.0
+    comb = _sk_scaling((m[:, 8:24] * s[2] + b[8:24]).reshape(T, 4, 4), 20, 1e-6)
+    assert np.allclose(o["pre"], pre, atol=1e-13)
+    assert np.allclose(o["post"], post, atol=1e-13)
+    assert np.allclose(o["comb"], comb, atol=1e-12)
+    assert np.allclose(o["y"], np.einsum("ti,tih->th", pre, r), atol=1e-12)
+
+
+def test_f32_stream_pre_is_scale_invariant_without_eps():
+    """With rms_eps = 0 the mixes see res / rms(res) only: scaling the streams by 8 leaves
+    pre, post and comb unchanged and scales y by 8."""
+    inp = layer_inputs_f32s(4, 32, cfg=154)
+    a = oracle.pre_f32s(inp.res, inp.hc_fn, inp.hc_scale, inp.hc_base, rms_eps=0.0)
+    b = oracle.pre_f32s(inp.res * np.float32(8), inp.hc_fn, inp.hc_scale, inp.hc_base, rms_eps=0.0)
+    for k in ("pre", "post", "comb"):
+        assert np.allclose(a[k], b[k], rtol=0, atol=1e-14), k
+    assert np.allclose(b["y"], 8 * a["y"], rtol=1e-14, atol=0)
+
+
+def test_f32_stream_expand_widens_exactly():
+    inp = layer_inputs(4, 24, cfg=155)
+    s = oracle.expand_f32s(inp.x)
+    assert s.dtype == np.float32
+    assert np.array_equal(s, np.repeat(bf16_bits_to_f32(inp.x)[:, None, :], HC, axis=1))
+    assert np.array_equal(oracle.round_bf16(oracle.head_mean_f32s(s)), inp.x)
