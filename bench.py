@@ -59,7 +59,8 @@ def parse():
     ap.add_argument("--workload", default="layer_h7168", choices=sorted(WORKLOADS))
     ap.add_argument("--only", default="all",
                     choices=["all", "pre", "post", "sinkhorn", "pre_dots", "post_bwd", "sinkhorn_bwd", "pre_dots_bwd",
-                             "pre_bf16", "expand", "head", "head_mean", "pre_bwd", "post_project", "fused"],
+                             "pre_bf16", "expand", "head", "head_mean", "pre_bwd", "post_project", "fused",
+                             "f32", "pre_f32", "post_f32", "expand_f32", "head_mean_f32"],
                     help="run only one call in the timed loop (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-steady-state", action="store_true",
@@ -94,6 +95,8 @@ def main():
     import torch
 
     import mhc_hyper_connection_amd as mhc
+    from mhc_inputs import (algorithmic_bytes_expand_f32, algorithmic_bytes_head_mean_f32,
+                            algorithmic_bytes_post_f32, algorithmic_bytes_pre_f32)
     from mhc_inputs import (algorithmic_bytes_expand, algorithmic_bytes_head, algorithmic_bytes_head_mean,
                             algorithmic_bytes_pre_bf16,
                             algorithmic_bytes_post, algorithmic_bytes_post_backward, algorithmic_bytes_pre,
@@ -216,7 +219,26 @@ def main():
     def call_post_bwd():
         mhc.mhc_post_backward(d_out, x, res, post, comb, d_x=d_x, d_res=d_res, d_post=d_post, d_comb=d_comb)
 
-    if args.only == "post_bwd":
+    if args.only in ("f32", "pre_f32", "post_f32", "expand_f32", "head_mean_f32"):
+        # fp32 residual streams [T, 4, H] (full fp32 N(0,1) values), the same weights and x
+        from mhc_inputs import f32_streams
+        res32 = torch.from_numpy(f32_streams(T, H, cfg)).to(dev)
+        out32 = torch.empty_like(res32)
+
+    def call_pre_f32():
+        mhc.mhc_pre_fused_f32(res32, hc_fn, hc_scale, hc_base, p["rms_eps"], p["pre_eps"], p["sinkhorn_eps"],
+                              p["post_mult"], p["num_iters"], y=y, post=post, comb=comb, workspace=ws)
+
+    def call_post_f32():
+        mhc.mhc_post_f32(x, res32, post, comb, out=out32)
+
+    def call_expand_f32():
+        mhc.mhc_expand_f32(x, streams=out32)
+
+    def call_head_mean_f32():
+        mhc.mhc_head_mean_f32(res32, y=y)
+
+    if args.only in ("post_bwd", "post_f32"):
         call_pre()  # the forward's mixes (untimed)
 
     steady_state = args.only == "all" and H % 8 == 0 and not args.no_steady_state
@@ -270,6 +292,14 @@ def main():
             call_post_project()
         if args.only == "fused":
             call_fused()
+        if args.only in ("f32", "pre_f32"):
+            call_pre_f32()
+        if args.only in ("f32", "post_f32"):
+            call_post_f32()
+        if args.only == "expand_f32":
+            call_expand_f32()
+        if args.only == "head_mean_f32":
+            call_head_mean_f32()
 
     stream = torch.cuda.current_stream(dev)
 
@@ -357,9 +387,14 @@ def main():
         breakdown["post_bwd_ms"] = ms_step
     if args.only == "pre_dots_bwd":
         breakdown["pre_dots_bwd_ms"] = ms_step
-    for mode in ("pre_bf16", "expand", "head", "head_mean", "pre_bwd", "post_project", "fused"):
+    for mode in ("pre_bf16", "expand", "head", "head_mean", "pre_bwd", "post_project", "fused", "expand_f32",
+                 "head_mean_f32"):
         if args.only == mode:
             breakdown[mode + "_ms"] = ms_step
+    if args.only in ("f32", "pre_f32"):
+        breakdown["pre_f32_ms"] = timed_reps(call_pre_f32, max(args.steps, 1))
+    if args.only in ("f32", "post_f32"):
+        breakdown["post_f32_ms"] = timed_reps(call_post_f32, max(args.steps, 1))
 
     eff_gbps = step_bytes / (ms_step * 1e-3) / 1e9
 
@@ -416,6 +451,15 @@ def main():
     if "post_project_ms" in breakdown:
         calls["mhc_post_project"] = ("pre_prep_kernel+post_proj_stream_kernel+pre_mixsum_kernel",
                                      breakdown["post_project_ms"], step_bytes)
+    if "pre_f32_ms" in breakdown:
+        proj32 = "pre_proj_f32s_kernel+pre_mixsum_kernel+pre_collapse_f32s_kernel"
+        calls["mhc_pre_fused_f32"] = (proj32, breakdown["pre_f32_ms"], algorithmic_bytes_pre_f32(T, H))
+    if "post_f32_ms" in breakdown:
+        calls["mhc_post_f32"] = ("post_f32s_kernel", breakdown["post_f32_ms"], algorithmic_bytes_post_f32(T, H))
+    if "expand_f32_ms" in breakdown:
+        calls["mhc_expand_f32"] = ("expand_f32s_kernel", breakdown["expand_f32_ms"], step_bytes)
+    if "head_mean_f32_ms" in breakdown:
+        calls["mhc_head_mean_f32"] = ("head_mean_f32s_kernel", breakdown["head_mean_f32_ms"], step_bytes)
     if "fused_ms" in breakdown:
         calls["mhc_pre_from_dots+mhc_post_project"] = (
             "pre_collapse_vec8_kernel+pre_prep_kernel+post_proj_stream_kernel+pre_mixsum_kernel", breakdown["fused_ms"],
@@ -449,7 +493,8 @@ def main():
     # Sanity figures: the launch floor of the step's kernel count (one-element fills,
     # launched the same way), and what a plain elementwise copy sustains here.
     npre = 1 if pre_one_read(T, H) else 4
-    nker = {"all": npre + 1, "pre": npre, "post": 1, "post_project": 3, "fused": 4}.get(args.only)
+    nker = {"all": npre + 1, "pre": npre, "post": 1, "post_project": 3, "fused": 4, "f32": 4, "pre_f32": 3,
+            "post_f32": 1}.get(args.only)
     launch_floor_ms = None
     if nker:
         one = torch.zeros(1, device=dev)
@@ -493,7 +538,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f32" if args.only.endswith("f32") or args.only == "f32" else "bf16",
         "data": "synthetic",
         "config": {"workload": (f"mhc {args.only} 2^20 4x4 matrices" if args.only.startswith("sinkhorn") else
                                 f"mhc {args.only if args.only != 'all' else 'pre+post'} T={T} H={H} HC=4"),
@@ -540,6 +585,8 @@ def traffic_path(T: int, H: int) -> str:
 
 def step_algorithmic_bytes(only: str, T: int, H: int, sk_logits) -> int:
     """What one timed step must move (each tensor counted once)."""
+    from mhc_inputs import (algorithmic_bytes_expand_f32, algorithmic_bytes_head_mean_f32,
+                            algorithmic_bytes_post_f32, algorithmic_bytes_pre_f32)
     from mhc_inputs import (algorithmic_bytes_expand, algorithmic_bytes_head, algorithmic_bytes_head_mean,
                             algorithmic_bytes_post, algorithmic_bytes_post_backward, algorithmic_bytes_pre,
                             algorithmic_bytes_pre_backward, algorithmic_bytes_pre_bf16, algorithmic_bytes_pre_dots,
@@ -561,6 +608,11 @@ def step_algorithmic_bytes(only: str, T: int, H: int, sk_logits) -> int:
         "pre": lambda: algorithmic_bytes_pre(T, H),
         "post": lambda: algorithmic_bytes_post(T, H),
         "all": lambda: algorithmic_bytes_pre(T, H) + algorithmic_bytes_post(T, H),
+        "f32": lambda: algorithmic_bytes_pre_f32(T, H) + algorithmic_bytes_post_f32(T, H),
+        "pre_f32": lambda: algorithmic_bytes_pre_f32(T, H),
+        "post_f32": lambda: algorithmic_bytes_post_f32(T, H),
+        "expand_f32": lambda: algorithmic_bytes_expand_f32(T, H),
+        "head_mean_f32": lambda: algorithmic_bytes_head_mean_f32(T, H),
     }
     return per_mode[only]()
 

@@ -75,7 +75,7 @@ const char *mhc_status_string(mhc_status status);
  * two-pass form; the collapse and the slice sums are its widest grids), "collapse" (the
  * collapse of pre_from_dots with one split and a supplied sum of squares on 16-byte
  * rows), "pre_from_dots" (its other forms), "pre_from_dots_backward", "post_backward",
- * "sinkhorn", "sinkhorn_backward".  T is the
+ * "sinkhorn", "sinkhorn_backward", "post_f32", "expand_f32", "head_mean_f32".  T is the
  * token count (the matrix count for the Sinkhorn entry points), H the hidden size (unused
  * for the Sinkhorn entry points), vec8 != 0 for 16-byte rows.  Writes the number of
  * launches, the tokens per launch (the last launch may hold fewer) and the work-items of
@@ -243,6 +243,52 @@ mhc_status mhc_expand(const uint16_t *hidden, int64_t T, int64_t H, uint16_t *st
  *   res [T,4,H] bf16 input, y [T,H] bf16 output, device; no overlap.  T >= 0, H >= 1.
  */
 mhc_status mhc_head_mean(const uint16_t *res, int64_t T, int64_t H, uint16_t *y, void *stream);
+
+/*
+ * FP32 residual streams.  The metrale dispatch page (hyper_connection_dispatch.rs, module
+ * header) runs both mixer families over FP32 [T, hc_mult, H] streams, and glm5next_mhc.rs
+ * expands each BF16 hidden row into its FP32 highway streams (glm_hc_expand), collapses
+ * them to one BF16 row (glm_hc_pre) and writes new FP32 streams (glm_hc_post).  These entry
+ * points are the bf16-stream ones with `res`, `out` and `streams` as float [T, 4, H]; x,
+ * hidden and y stay bf16 and the mixing coefficients fp32.  1 <= H <= 1048576 (the
+ * projection addresses a 64-token tile of fp32 streams with 32-bit byte offsets).  Rows
+ * take a vector path when H % 4 == 0, the fp32 arrays are 16-byte aligned and the bf16
+ * rows 8-byte aligned, and a scalar path otherwise; both give the same results.
+ */
+
+/*
+ * mhc_pre_fused_f32 -- the pre-map over fp32 streams: steps and outputs of mhc_pre_fused,
+ * with the sum of squares, the 24 dots and the collapse taken over the fp32 values
+ * (fp32 arithmetic; y rounded once to bf16).  The workspace is mhc_pre_fused's: at least
+ * mhc_pre_fused_workspace_bytes(T, H) bytes, 256-byte aligned, contents on entry ignored.
+ */
+mhc_status mhc_pre_fused_f32(const float *res, const float *hc_fn, const float *hc_scale, const float *hc_base,
+                             int64_t T, int64_t H, float rms_eps, float pre_eps, float sinkhorn_eps, float post_mult,
+                             int32_t num_iters, uint16_t *y, float *post, float *comb, float *pre, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/*
+ * mhc_post_f32 -- the post-map over fp32 streams (metrale glm5next_mhc.rs, glm_hc_post):
+ *     out[t][n][h] = x[t][h] * post[t][n] + sum_o res[t][o][h] * comb[t][o][n]
+ *   fp32 arithmetic in that order (one rounding per fused multiply-add), out fp32.
+ *   x [T,H] bf16; res, out [T,4,H] fp32; post [T,4], comb [T,4,4] fp32.  `out` may equal
+ *   `res` exactly (in place); no other overlap.
+ */
+mhc_status mhc_post_f32(const uint16_t *x, const float *res, const float *post, const float *comb, int64_t T,
+                        int64_t H, float *out, void *stream);
+
+/*
+ * mhc_expand_f32 -- model entry onto fp32 streams (glm_hc_expand): streams[t][i][h] =
+ * hidden[t][h] widened exactly.  hidden [T,H] bf16, streams [T,4,H] fp32; no overlap.
+ */
+mhc_status mhc_expand_f32(const uint16_t *hidden, int64_t T, int64_t H, float *streams, void *stream);
+
+/*
+ * mhc_head_mean_f32 -- the unweighted head over fp32 streams (hc_head_mean):
+ *     y[t][h] = bf16( (res[t][0][h] + res[t][1][h] + res[t][2][h] + res[t][3][h]) / 4 )
+ *   (fp32 sum in that order, one rounding).  res [T,4,H] fp32, y [T,H] bf16; no overlap.
+ */
+mhc_status mhc_head_mean_f32(const float *res, int64_t T, int64_t H, uint16_t *y, void *stream);
 
 /*
  * mhc_head -- model exit, weighted (metrale hyper_connection_dispatch.rs, hc_head_site:

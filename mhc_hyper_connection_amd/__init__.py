@@ -70,6 +70,14 @@ def lib() -> ctypes.CDLL:
     L.mhc_pre_fused_bf16.restype = ctypes.c_int
     L.mhc_pre_fused_noalloc.argtypes = [P, P, P, P, I64, I64, F, F, F, F, I32, P, P, P, P, P]
     L.mhc_pre_fused_noalloc.restype = ctypes.c_int
+    L.mhc_pre_fused_f32.argtypes = [P, P, P, P, I64, I64, F, F, F, F, I32, P, P, P, P, P, SZ, P]
+    L.mhc_pre_fused_f32.restype = ctypes.c_int
+    L.mhc_post_f32.argtypes = [P, P, P, P, I64, I64, P, P]
+    L.mhc_post_f32.restype = ctypes.c_int
+    L.mhc_expand_f32.argtypes = [P, I64, I64, P, P]
+    L.mhc_expand_f32.restype = ctypes.c_int
+    L.mhc_head_mean_f32.argtypes = [P, I64, I64, P, P]
+    L.mhc_head_mean_f32.restype = ctypes.c_int
     L.mhc_expand.argtypes = [P, I64, I64, P, P]
     L.mhc_expand.restype = ctypes.c_int
     L.mhc_head_mean.argtypes = [P, I64, I64, P, P]
@@ -192,9 +200,20 @@ def mhc_pre_fused_noalloc(res: torch.Tensor, hc_fn: torch.Tensor, hc_scale: torc
                       sinkhorn_eps, post_mult, num_iters, y, post, comb, pre, return_pre, None, noalloc=True)
 
 
+def mhc_pre_fused_f32(res: torch.Tensor, hc_fn: torch.Tensor, hc_scale: torch.Tensor, hc_base: torch.Tensor,
+                      rms_eps: float = 1e-6, pre_eps: float = 1e-6, sinkhorn_eps: float = 1e-6,
+                      post_mult: float = 1.0, num_iters: int = 20, *, y=None, post=None, comb=None, pre=None,
+                      return_pre: bool = False, workspace: torch.Tensor | None = None):
+    """:func:`mhc_pre_fused` over fp32 streams: res [..., 4, H] float32 -> (y [..., H] bf16,
+    post [..., 4], comb [..., 4, 4] [, pre [..., 4]])."""
+    return _pre_fused("mhc_pre_fused_f32", torch.float32, res, hc_fn, hc_scale, hc_base, rms_eps, pre_eps,
+                      sinkhorn_eps, post_mult, num_iters, y, post, comb, pre, return_pre, workspace,
+                      res_dtype=torch.float32)
+
+
 def _pre_fused(name, fn_dtype, res, hc_fn, hc_scale, hc_base, rms_eps, pre_eps, sinkhorn_eps, post_mult, num_iters,
-               y, post, comb, pre, return_pre, workspace, noalloc=False):
-    _need(res, "res", torch.bfloat16)
+               y, post, comb, pre, return_pre, workspace, noalloc=False, res_dtype=torch.bfloat16):
+    _need(res, "res", res_dtype)
     if res.dim() < 2 or res.shape[-2] != HC:
         raise ValueError(f"res must be [..., 4, H], got {tuple(res.shape)}")
     H = res.shape[-1]
@@ -334,6 +353,36 @@ def mhc_post(x: torch.Tensor, res: torch.Tensor, post: torch.Tensor, comb: torch
     _same_device(x, res, post, comb, out)
     _check("mhc_post", lib().mhc_post(_ptr(x), _ptr(res), _ptr(post), _ptr(comb), T, H, _ptr(out),
                                       _stream(res.device)))
+    return out
+
+
+def mhc_post_f32(x: torch.Tensor, res: torch.Tensor, post: torch.Tensor, comb: torch.Tensor,
+                 out: torch.Tensor | None = None) -> torch.Tensor:
+    """:func:`mhc_post` over fp32 streams: x [..., H] bf16, res [..., 4, H] float32 ->
+    out [..., 4, H] float32 (``out`` may be ``res``)."""
+    _need(res, "res", torch.float32)
+    if res.dim() < 2 or res.shape[-2] != HC:
+        raise ValueError(f"res must be [..., 4, H], got {tuple(res.shape)}")
+    H = res.shape[-1]
+    outer = tuple(res.shape[:-2])
+    T = res.numel() // (HC * H) if H > 0 else 0
+    _need(x, "x", torch.bfloat16)
+    if tuple(x.shape) != outer + (H,):
+        raise ValueError(f"x must be {outer + (H,)}, got {tuple(x.shape)}")
+    _need(post, "post", torch.float32)
+    if tuple(post.shape) not in (outer + (HC,), outer + (HC, 1)):
+        raise ValueError(f"post must be {outer + (HC,)} or {outer + (HC, 1)}, got {tuple(post.shape)}")
+    _need(comb, "comb", torch.float32)
+    if tuple(comb.shape) != outer + (HC, HC):
+        raise ValueError(f"comb must be {outer + (HC, HC)}, got {tuple(comb.shape)}")
+    if out is None:
+        out = torch.empty_like(res)
+    _need(out, "out", torch.float32)
+    if out.shape != res.shape:
+        raise ValueError("out must have the shape of res")
+    _same_device(x, res, post, comb, out)
+    _check("mhc_post_f32", lib().mhc_post_f32(_ptr(x), _ptr(res), _ptr(post), _ptr(comb), T, H, _ptr(out),
+                                              _stream(res.device)))
     return out
 
 
@@ -503,6 +552,42 @@ def mhc_head_mean(res: torch.Tensor, y: torch.Tensor | None = None) -> torch.Ten
     return y
 
 
+def mhc_expand_f32(hidden: torch.Tensor, streams: torch.Tensor | None = None) -> torch.Tensor:
+    """Model entry onto fp32 streams: hidden [..., H] bf16 -> streams [..., 4, H] float32."""
+    _need(hidden, "hidden", torch.bfloat16)
+    if hidden.dim() < 1:
+        raise ValueError("hidden must be [..., H]")
+    H = hidden.shape[-1]
+    outer = tuple(hidden.shape[:-1])
+    T = hidden.numel() // H if H > 0 else 0
+    if streams is None:
+        streams = torch.empty(outer + (HC, H), dtype=torch.float32, device=hidden.device)
+    _need(streams, "streams", torch.float32)
+    if tuple(streams.shape) != outer + (HC, H):
+        raise ValueError(f"streams must be {outer + (HC, H)}, got {tuple(streams.shape)}")
+    _same_device(hidden, streams)
+    _check("mhc_expand_f32", lib().mhc_expand_f32(_ptr(hidden), T, H, _ptr(streams), _stream(hidden.device)))
+    return streams
+
+
+def mhc_head_mean_f32(res: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
+    """Model exit, unweighted, over fp32 streams: res [..., 4, H] float32 -> y [..., H] bf16."""
+    _need(res, "res", torch.float32)
+    if res.dim() < 2 or res.shape[-2] != HC:
+        raise ValueError(f"res must be [..., 4, H], got {tuple(res.shape)}")
+    H = res.shape[-1]
+    outer = tuple(res.shape[:-2])
+    T = res.numel() // (HC * H) if H > 0 else 0
+    if y is None:
+        y = torch.empty(outer + (H,), dtype=torch.bfloat16, device=res.device)
+    _need(y, "y", torch.bfloat16)
+    if tuple(y.shape) != outer + (H,):
+        raise ValueError(f"y must be {outer + (H,)}, got {tuple(y.shape)}")
+    _same_device(res, y)
+    _check("mhc_head_mean_f32", lib().mhc_head_mean_f32(_ptr(res), T, H, _ptr(y), _stream(res.device)))
+    return y
+
+
 def mhc_head(res: torch.Tensor, hc_fn: torch.Tensor, hc_scale: torch.Tensor, hc_base: torch.Tensor,
              norm_eps: float = 1e-6, hc_eps: float = 1e-6, *, y: torch.Tensor | None = None,
              pre: torch.Tensor | None = None, return_pre: bool = False,
@@ -669,7 +754,8 @@ def mhc_pre_fused_backward(dy: torch.Tensor, d_post: torch.Tensor, d_comb: torch
     return dict(d_res=d_res, d_hc_fn=d_fn, d_hc_scale=d_scale, d_hc_base=d_base)
 
 
-__all__ = ["mhc_sinkhorn", "mhc_pre_fused", "mhc_pre_fused_noalloc", "mhc_pre_fused_bf16", "mhc_expand", "mhc_head_mean", "mhc_head",
+__all__ = ["mhc_sinkhorn", "mhc_pre_fused", "mhc_pre_fused_noalloc", "mhc_pre_fused_bf16", "mhc_pre_fused_f32",
+           "mhc_post_f32", "mhc_expand_f32", "mhc_head_mean_f32", "mhc_expand", "mhc_head_mean", "mhc_head",
            "mhc_pre_fused_workspace_bytes", "mhc_pre_from_dots", "mhc_post",
            "mhc_sinkhorn_backward", "mhc_post_backward", "mhc_pre_from_dots_backward",
            "mhc_pre_backward_workspace_bytes", "mhc_pre_fused_backward", "mhc_pre_fused_backward_workspace_bytes",

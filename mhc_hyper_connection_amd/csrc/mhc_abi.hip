@@ -17,6 +17,11 @@ constexpr int64_t kMaxDim = (int64_t)1 << 30;
 constexpr int64_t kPreMaxH = (int64_t)1 << 21;
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned8(const void *p) { return ((uintptr_t)p & 7u) == 0; }
+
+// FP32 streams: the projection addresses a 64-token tile ([64][4][H] fp32) with 32-bit
+// byte offsets.
+constexpr int64_t kF32MaxH = (int64_t)1 << 20;
 
 // Do [a, a + an) and [b, b + bn) share a byte?
 bool overlaps(const void *a, size_t an, const void *b, size_t bn)
@@ -172,6 +177,10 @@ mhc_status mhc_launch_plan(const char *entry, int64_t T, int64_t H, int32_t vec8
         per_tok = mhc::collapse_items_per_token(H, v);
         per_tok = per_tok > (int64_t)g.nrec * 4 ? per_tok : (int64_t)g.nrec * 4; // slice sums: nrec * 256 per 64
         per_launch = g.chunk;
+    } else if (!strcmp(entry, "post_f32")) {
+        per_tok = mhc::post_f32s_items_per_token(H, v);
+    } else if (!strcmp(entry, "expand_f32") || !strcmp(entry, "head_mean_f32")) {
+        per_tok = mhc::stream_copy_f32s_items_per_token(H, v);
     } else if (!strcmp(entry, "collapse")) {
         per_tok = mhc::collapse_items_per_token(H, v);
     } else if (!strcmp(entry, "pre_from_dots")) {
@@ -368,6 +377,106 @@ mhc_status mhc_post(const uint16_t *x, const uint16_t *res, const float *post, c
     }
     const bool vec8 = (H % 8 == 0) && aligned16(x) && aligned16(res) && aligned16(out);
     return launch_status(mhc::launch_post(x, res, post, comb, T, H, out, (hipStream_t)stream, vec8));
+}
+
+// ---------------------------------------------------------------- FP32 residual streams
+
+mhc_status mhc_post_f32(const uint16_t *x, const float *res, const float *post, const float *comb, int64_t T,
+                        int64_t H, float *out, void *stream)
+{
+    if (!sizes_ok(T, H) || H > kF32MaxH) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    if (T == 0) {
+        return MHC_SUCCESS;
+    }
+    if (!x || !res || !post || !comb || !out) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    const size_t res_b = (size_t)T * 4 * H * 4, x_b = (size_t)T * H * 2;
+    const size_t post_b = (size_t)T * 4 * 4, comb_b = (size_t)T * 16 * 4;
+    if ((const void *)out != (const void *)res && overlaps(out, res_b, res, res_b)) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    if (overlaps(out, res_b, x, x_b) || overlaps(out, res_b, post, post_b) || overlaps(out, res_b, comb, comb_b)) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    const bool vec4 = (H % 4 == 0) && aligned8(x) && aligned16(res) && aligned16(out);
+    return launch_status(mhc::launch_post_f32s(x, res, post, comb, T, H, out, (hipStream_t)stream, vec4));
+}
+
+mhc_status mhc_expand_f32(const uint16_t *hidden, int64_t T, int64_t H, float *streams, void *stream)
+{
+    if (!sizes_ok(T, H) || H > kF32MaxH) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    if (T == 0) {
+        return MHC_SUCCESS;
+    }
+    if (!hidden || !streams || overlaps(streams, (size_t)T * 4 * H * 4, hidden, (size_t)T * H * 2)) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    const bool vec4 = (H % 4 == 0) && aligned8(hidden) && aligned16(streams);
+    return launch_status(mhc::launch_expand_f32s(hidden, T, H, streams, (hipStream_t)stream, vec4));
+}
+
+mhc_status mhc_head_mean_f32(const float *res, int64_t T, int64_t H, uint16_t *y, void *stream)
+{
+    if (!sizes_ok(T, H) || H > kF32MaxH) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    if (T == 0) {
+        return MHC_SUCCESS;
+    }
+    if (!res || !y || overlaps(y, (size_t)T * H * 2, res, (size_t)T * 4 * H * 4)) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    const bool vec4 = (H % 4 == 0) && aligned16(res) && aligned8(y);
+    return launch_status(mhc::launch_head_mean_f32s(res, T, H, y, (hipStream_t)stream, vec4));
+}
+
+mhc_status mhc_pre_fused_f32(const float *res, const float *hc_fn, const float *hc_scale, const float *hc_base,
+                             int64_t T, int64_t H, float rms_eps, float pre_eps, float sinkhorn_eps, float post_mult,
+                             int32_t num_iters, uint16_t *y, float *post, float *comb, float *pre, void *workspace,
+                             size_t workspace_bytes, void *stream)
+{
+    if (!sizes_ok(T, H) || H > kF32MaxH || num_iters < 1 || !finite(rms_eps) || !(rms_eps > 0.0f) ||
+        !finite(pre_eps) || pre_eps < 0.0f || !finite(sinkhorn_eps) || !(sinkhorn_eps > 0.0f) || !finite(post_mult)) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    if (T == 0) {
+        return MHC_SUCCESS;
+    }
+    if (!res || !hc_fn || !hc_scale || !hc_base || !y || !post || !comb) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    const PreGeom g = mhc::pre_geometry(T, H);
+    if (!workspace || workspace_bytes < g.total_bytes || ((uintptr_t)workspace & 255u) != 0) {
+        return MHC_ERROR_WORKSPACE;
+    }
+    const size_t res_b = (size_t)T * 4 * H * 4, y_b = (size_t)T * H * 2;
+    const size_t post_b = (size_t)T * 4 * 4, comb_b = (size_t)T * 16 * 4, pre_b = pre ? (size_t)T * 4 * 4 : 0;
+    const size_t fn_b = (size_t)kMixRows * 4 * H * 4;
+    const void *outs[5] = {y, post, comb, pre, workspace};
+    const size_t outn[5] = {y_b, post_b, comb_b, pre_b, g.total_bytes};
+    const void *ins[4] = {res, hc_fn, hc_scale, hc_base};
+    const size_t inn[4] = {res_b, fn_b, 3 * 4, (size_t)kMixRows * 4};
+    for (int a = 0; a < 5; ++a) {
+        for (int b = 0; b < 4; ++b) {
+            if (overlaps(outs[a], outn[a], ins[b], inn[b])) {
+                return MHC_ERROR_INVALID_VALUE;
+            }
+        }
+        for (int b = a + 1; b < 5; ++b) {
+            if (overlaps(outs[a], outn[a], outs[b], outn[b])) {
+                return MHC_ERROR_INVALID_VALUE;
+            }
+        }
+    }
+    const bool vec4 = (H % 4 == 0) && aligned16(res) && aligned8(y);
+    return launch_status(mhc::launch_pre_f32s(res, hc_fn, hc_scale, hc_base, g, rms_eps, pre_eps, sinkhorn_eps,
+                                              post_mult, num_iters, y, post, comb, pre, workspace,
+                                              (hipStream_t)stream, vec4));
 }
 
 size_t mhc_post_project_workspace_bytes(int64_t T, int64_t H)

@@ -116,6 +116,21 @@ hipError_t launch_post_project(const uint16_t *x, const uint16_t *res, const flo
                                const float *hc_fn_next, int64_t T, int64_t H, uint16_t *out, float *dot_mix,
                                float *sqrsum, void *workspace, hipStream_t stream);
 
+// FP32 residual streams [T][4][H] (x, hidden and y stay bf16).  `vec4`: H % 4 == 0, the
+// fp32 arrays 16-byte and the bf16 rows 8-byte aligned.  The pre-map takes the two-pass
+// form with the workspace layout of pre_geometry(T, H) (its weight-fragment area unused).
+hipError_t launch_pre_f32s(const float *res, const float *hc_fn, const float *hc_scale, const float *hc_base,
+                           const PreGeom &g, float rms_eps, float pre_eps, float sinkhorn_eps, float post_mult,
+                           int iters, uint16_t *y, float *post, float *comb, float *pre, void *workspace,
+                           hipStream_t stream, bool vec4);
+hipError_t launch_post_f32s(const uint16_t *x, const float *res, const float *post, const float *comb, int64_t T,
+                            int64_t H, float *out, hipStream_t stream, bool vec4);
+hipError_t launch_expand_f32s(const uint16_t *hidden, int64_t T, int64_t H, float *streams, hipStream_t stream,
+                              bool vec4);
+hipError_t launch_head_mean_f32s(const float *res, int64_t T, int64_t H, uint16_t *y, hipStream_t stream, bool vec4);
+int64_t post_f32s_items_per_token(int64_t H, bool vec4);
+int64_t stream_copy_f32s_items_per_token(int64_t H, bool vec4);
+
 // Model entry (each hidden row copied into the 4 streams) and the unweighted head (the
 // mean of the 4 streams).  `vec8`: H % 8 == 0 and both pointers 16-byte aligned.
 hipError_t launch_expand(const uint16_t *hidden, int64_t T, int64_t H, uint16_t *streams, hipStream_t stream,

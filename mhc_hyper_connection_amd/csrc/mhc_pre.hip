@@ -1009,6 +1009,222 @@ __global__ __launch_bounds__(kColBlock) void pre_collapse_scalar_kernel(const ui
     }
 }
 
+// ---------------------------------------------------------------- FP32 residual streams
+// The pre-map over fp32 streams (the same steps; y is still a bf16 row).  The projection
+// runs on the fp32 MFMA (16x16x4: one fp32 value per lane and step), so neither operand
+// needs splitting: A holds 16 tokens, B 16 weight rows, and the 4 k of a step are one
+// stream's h = h0 + 16u + 4g + e of lane group g.  A workgroup takes one 64-token tile and
+// one 128-wide slice (a wave per 32-wide block, all 4 streams), keeps the block's weights
+// in VGPRs, and leaves the same 25-field partial records as the bf16 projection, which
+// pre_mixsum_kernel sums and the fp32 collapse below finishes.
+struct ProjF32Args {
+    const float *res;   // the chunk's streams [T][4][H]
+    const float *hc_fn; // [24][4H]
+    int T, H, S;
+    float *rec; // [tiles][S][25][64]
+};
+
+template <bool kVec>
+__global__ __launch_bounds__(kPBlock, 2) void pre_proj_f32s_kernel(ProjF32Args a)
+{
+    __shared__ float red[kPWaves][kPTok][kMix];
+    __shared__ float sqp[kPWaves][4][kPTok];
+    const int tile = blockIdx.x;
+    const int slice = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int lane = tid & (kWave - 1);
+    const int g = lane >> 4;
+    const int c = lane & 15;
+    const int H = a.H;
+    const int S = a.S;
+    const int h0 = (slice * kPWaves + w) * kPHB;
+    const size_t K = (size_t)kHC * H;
+
+    // B operands: weight row n * 16 + c (rows 24..31 zero) at stream i, h = h0 + 16u + 4g + e
+    float wv[kHC][2][4][2];
+#pragma unroll
+    for (int i = 0; i < kHC; ++i) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int h = h0 + 16 * u + 4 * g + e;
+#pragma unroll
+                for (int n = 0; n < 2; ++n) {
+                    const int r = n * 16 + c;
+                    wv[i][u][e][n] = (r < kMix && h < H) ? a.hc_fn[(size_t)r * K + (size_t)i * H + h] : 0.0f;
+                }
+            }
+        }
+    }
+
+    const int t0 = tile * kPTok;
+    const int ntok = min(kPTok, a.T - t0);
+    // the tile's streams; tokens past the chunk and h past H read zero
+    const __amdgpu_buffer_rsrc_t v =
+        buf_view_uniform(a.res + (size_t)t0 * K, (uint32_t)((size_t)ntok * K * sizeof(float)));
+    auto load = [&](int m, float (&d)[kHC][2][4]) {
+        const int tok = m * 16 + c;
+#pragma unroll
+        for (int i = 0; i < kHC; ++i) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int h = h0 + 16 * u + 4 * g;
+                const uint32_t base = ((uint32_t)(tok * kHC + i) * (uint32_t)H) * 4u;
+                if constexpr (kVec) {
+                    const uint32_t off = h < H ? base + (uint32_t)h * 4u : 0x80000000u;
+                    const f32x4 q = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(v, (int)off, 0, 0));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        d[i][u][e] = q[e];
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t off = h + e < H ? base + (uint32_t)(h + e) * 4u : 0x80000000u;
+                        d[i][u][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(v, (int)off, 0, 0));
+                    }
+                }
+            }
+        }
+    };
+
+    f32x4 acc[kPMT][2];
+    float sq[kPMT];
+    float cur[kHC][2][4], nxt[kHC][2][4];
+    load(0, cur);
+#pragma unroll
+    for (int m = 0; m < kPMT; ++m) {
+        if (m + 1 < kPMT) {
+            load(m + 1, nxt);
+        }
+        acc[m][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        sq[m] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kHC; ++i) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float x = cur[i][u][e];
+                    sq[m] = fmaf(x, x, sq[m]);
+                    acc[m][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(x, wv[i][u][e][0], acc[m][0], 0, 0, 0);
+                    acc[m][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(x, wv[i][u][e][1], acc[m][1], 0, 0, 0);
+                }
+            }
+        }
+        if (m + 1 < kPMT) {
+#pragma unroll
+            for (int i = 0; i < kHC; ++i) {
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        cur[i][u][e] = nxt[i][u][e];
+                    }
+                }
+            }
+        }
+    }
+
+    // workgroup reduction -> this slice's partial record (the order of pre_proj_kernel)
+#pragma unroll
+    for (int m = 0; m < kPMT; ++m) {
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            const int col = n * 16 + c;
+            if (col < kMix) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    red[w][m * 16 + 4 * g + k][col] = acc[m][n][k];
+                }
+            }
+        }
+        sqp[w][g][m * 16 + c] = sq[m];
+    }
+    __syncthreads();
+    float *rec = a.rec + ((size_t)tile * S + slice) * (kRec * kPTok);
+    const int tok = tid & (kPTok - 1);
+    for (int col = tid >> 6; col < kMix; col += kPWaves) {
+        float s = red[0][tok][col];
+#pragma unroll
+        for (int ww = 1; ww < kPWaves; ++ww) {
+            s += red[ww][tok][col];
+        }
+        rec[field_of_col(col) * kPTok + tok] = s;
+    }
+    if (tid < kPTok) {
+        float s = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < kPWaves; ++ww) {
+#pragma unroll
+            for (int gg = 0; gg < 4; ++gg) {
+                s += sqp[ww][gg][tid];
+            }
+        }
+        rec[kFSq * kPTok + tid] = s;
+    }
+}
+
+// y = sum_i pre_i * res_i over fp32 streams, and the token's post and comb (first tile).
+// Vector path: a wave per (token, 256-wide tile), 4 h per lane, 16-byte loads and an
+// 8-byte bf16 store; scalar path: a lane per h.
+constexpr int kColVecTileF = kWave * 4;
+
+template <bool kVec>
+__global__ __launch_bounds__(kColBlock) void pre_collapse_f32s_kernel(const float *__restrict__ res, MixArgs mx, int T,
+                                                                      int H, int tiles_per_token,
+                                                                      uint16_t *__restrict__ y)
+{
+    const int wave = uniform(blockIdx.x * kColWaves + (threadIdx.x >> 6));
+    const int lane = threadIdx.x & (kWave - 1);
+    const int t = uniform(wave / tiles_per_token);
+    const int tile = uniform(wave - t * tiles_per_token);
+    if (t >= T) {
+        return;
+    }
+    float p[kHC], rstd;
+    token_pre(mx, t, p, rstd);
+    if constexpr (kVec) {
+        const int h = tile * kColVecTileF + lane * 4;
+        if (h < H) {
+            const size_t row = (size_t)t * kHC * H + h;
+            f32x4 r[kHC];
+#pragma unroll
+            for (int i = 0; i < kHC; ++i) {
+                r[i] = __builtin_bit_cast(f32x4, load_nt16(res + row + (size_t)i * H));
+            }
+            float o[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float s = r[0][j] * p[0];
+#pragma unroll
+                for (int i = 1; i < kHC; ++i) {
+                    s = fmaf(r[i][j], p[i], s);
+                }
+                o[j] = s;
+            }
+            *reinterpret_cast<uint2 *>(y + (size_t)t * H + h) = uint2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+        }
+    } else {
+        const int h = tile * kWave + lane;
+        if (h < H) {
+            const size_t row = (size_t)t * kHC * H + h;
+            float s = res[row] * p[0];
+#pragma unroll
+            for (int i = 1; i < kHC; ++i) {
+                s = fmaf(res[row + (size_t)i * H], p[i], s);
+            }
+            y[(size_t)t * H + h] = f32_to_bf16(s);
+        }
+    }
+    if (tile == 0) {
+        token_mix_outputs(mx, t, p, rstd, lane == 0);
+    }
+}
+
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 } // namespace
@@ -1292,6 +1508,76 @@ hipError_t launch_pre(const uint16_t *res, const void *hc_fn, bool fn_bf16, int 
         } else {
             pre_collapse_scalar_kernel<<<dim3((unsigned)blocks), dim3(kColBlock), 0, stream>>>(rc, mx, Tc, H,
                                                                                                (int)htiles, yc);
+        }
+        e = hipGetLastError();
+        if (e != hipSuccess) {
+            return e;
+        }
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_pre_f32s(const float *res, const float *hc_fn, const float *hc_scale, const float *hc_base,
+                           const PreGeom &g, float rms_eps, float pre_eps, float sinkhorn_eps, float post_mult,
+                           int iters, uint16_t *y, float *post, float *comb, float *pre, void *workspace,
+                           hipStream_t stream, bool vec4)
+{
+    char *ws = reinterpret_cast<char *>(workspace);
+    float *sums = reinterpret_cast<float *>(ws + g.off_prew);
+    const int H = (int)g.H;
+    for (int64_t c0 = 0; c0 < g.T; c0 += g.chunk) {
+        const int Tc = (int)(g.T - c0 < g.chunk ? g.T - c0 : g.chunk);
+        const int tiles = (Tc + kPTok - 1) / kPTok;
+        ProjF32Args a{};
+        a.res = res + (size_t)c0 * kHC * H;
+        a.hc_fn = hc_fn;
+        a.T = Tc;
+        a.H = H;
+        a.S = g.slices;
+        a.rec = reinterpret_cast<float *>(ws + g.off_rec);
+        if (vec4) {
+            pre_proj_f32s_kernel<true><<<dim3((unsigned)tiles, (unsigned)g.slices), dim3(kPBlock), 0, stream>>>(a);
+        } else {
+            pre_proj_f32s_kernel<false><<<dim3((unsigned)tiles, (unsigned)g.slices), dim3(kPBlock), 0, stream>>>(a);
+        }
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) {
+            return e;
+        }
+        pre_mixsum_kernel<<<dim3((unsigned)(tiles * kRec)), dim3(256), 0, stream>>>(a.rec, Tc, g.slices, kRec, sums,
+                                                                                  nullptr, nullptr);
+        e = hipGetLastError();
+        if (e != hipSuccess) {
+            return e;
+        }
+        MixArgs mx{};
+        mx.sums = sums;
+        mx.stride = kSumStride;
+        mx.off_post = kFSq + 1;
+        mx.sq = nullptr;
+        mx.hc_scale = hc_scale;
+        mx.hc_base = hc_base;
+        mx.k_denom = (float)(kHC * g.H);
+        mx.rms_eps = rms_eps;
+        mx.pre_eps = pre_eps;
+        mx.sk_eps = sinkhorn_eps;
+        mx.post_mult = post_mult;
+        mx.iters = iters;
+        mx.head = 0;
+        mx.post = post + (size_t)c0 * kHC;
+        mx.comb = comb + (size_t)c0 * kHC * kHC;
+        mx.pre_out = pre ? pre + (size_t)c0 * kHC : nullptr;
+        const int tile = vec4 ? kColVecTileF : kWave;
+        const int64_t htiles = (g.H + tile - 1) / tile;
+        const int64_t blocks = ((int64_t)Tc * htiles + kColWaves - 1) / kColWaves;
+        const float *rc = res + (size_t)c0 * kHC * H;
+        uint16_t *yc = y + (size_t)c0 * H;
+        if (vec4) {
+            pre_collapse_f32s_kernel<true><<<dim3((unsigned)blocks), dim3(kColBlock), 0, stream>>>(rc, mx, Tc, H,
+                                                                                                 (int)htiles, yc);
+        } else {
+            pre_collapse_f32s_kernel<false><<<dim3((unsigned)blocks), dim3(kColBlock), 0, stream>>>(rc, mx, Tc, H,
+                                                                                                  (int)htiles, yc);
         }
         e = hipGetLastError();
         if (e != hipSuccess) {

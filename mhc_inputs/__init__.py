@@ -145,11 +145,15 @@ def f32_streams(T: int, H: int, cfg: int, seed: int = 0, std: float = 1.0) -> np
     return normal_f32(seed, cfg, "res", (T, HC, H), std)
 
 
-def layer_inputs_f32s(T: int, H: int, cfg: int, seed: int = 0, **kw) -> LayerInputs:
-    """layer_inputs with FP32 streams (res float32 [T, 4, H]); x stays bf16."""
-    inp = layer_inputs(T, H, cfg, seed, **kw)
-    inp.res = f32_streams(T, H, cfg, seed)
-    return inp
+def layer_inputs_f32s(T: int, H: int, cfg: int, seed: int = 0, *, hc_fn_std: float = 0.02,
+                      base_std: float = 0.1, scale=(1.0, 1.0, 1.0)) -> LayerInputs:
+    """layer_inputs with FP32 streams (res float32 [T, 4, H] ~ N(0,1)); x stays bf16."""
+    res = f32_streams(T, H, cfg, seed)
+    x = normal_bf16(seed, cfg, "x", (T, H))
+    hc_fn = normal_f32(seed, cfg, "hc_fn", (MIX, HC * H), hc_fn_std)
+    hc_base = normal_f32(seed, cfg, "hc_base", (MIX,), base_std)
+    hc_scale = np.asarray(scale, dtype=np.float32)
+    return LayerInputs(T, H, res, x, hc_fn, hc_scale, hc_base, dict(DEFAULT_PARAMS))
 
 
 def named_layer(name: str, seed: int = 0) -> LayerInputs:
@@ -239,6 +243,27 @@ def algorithmic_bytes_pre(T: int, H: int) -> int:
 def algorithmic_bytes_pre_bf16(T: int, H: int) -> int:
     """The pre-map with bf16 weights: as algorithmic_bytes_pre, with 192 H bytes of weights."""
     return T * (8 * H + 2 * H + 16 + 64) + 192 * H + 108
+
+
+def algorithmic_bytes_pre_f32(T: int, H: int) -> int:
+    """The pre-map over fp32 streams: 16 H bytes of streams read per token, the rest as
+    algorithmic_bytes_pre."""
+    return T * (16 * H + 2 * H + 16 + 64) + 384 * H + 108
+
+
+def algorithmic_bytes_post_f32(T: int, H: int) -> int:
+    """The post-map over fp32 streams: x (bf16) and res (fp32) read, 80 B of mixes, out (fp32) written."""
+    return T * (2 * H + 16 * H + 80 + 16 * H)
+
+
+def algorithmic_bytes_expand_f32(T: int, H: int) -> int:
+    """Model entry onto fp32 streams: the hidden row read, 4 fp32 streams written."""
+    return T * (2 * H + 16 * H)
+
+
+def algorithmic_bytes_head_mean_f32(T: int, H: int) -> int:
+    """Unweighted head over fp32 streams: 4 fp32 streams read, one bf16 row written."""
+    return T * (16 * H + 2 * H)
 
 
 def algorithmic_bytes_expand(T: int, H: int) -> int:

@@ -69,10 +69,39 @@ def oracle_threads() -> int:
     return max(1, min(os.cpu_count() or 1, 16))
 
 
+# fp32 outputs of an fp32 multiply-add chain (the fp32-stream post-map): within 2^-21 of
+# the sum of the absolute terms (five roundings of at most 2^-24 of it each, with margin).
+F32_CHAIN_REL = 2.0 ** -21
+
+
+def assert_f32_chain_close(got, ref, scale, what, rel: float = F32_CHAIN_REL):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    err = np.abs(got - ref)
+    tol = rel * np.asarray(scale, dtype=np.float64) + 1e-30
+    bad = ~(err <= tol)
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside tolerance; first at {idx.tolist()}; "
+                             f"max err/tol {(err / tol).max():.3e}")
+
+
+def post_f32s_scale(x_bits, res, post, comb):
+    """Sum of the absolute terms of each fp32-stream post-map output: |x post| + sum_o |res comb|."""
+    xa = np.abs(bf16_bits_to_f32(x_bits).astype(np.float64))
+    ra = np.abs(np.asarray(res, np.float64))
+    pa = np.abs(np.asarray(post, np.float64)).reshape(ra.shape[0], 4)
+    ca = np.abs(np.asarray(comb, np.float64)).reshape(ra.shape[0], 4, 4)
+    return xa[:, None, :] * pa[:, :, None] + np.einsum("toh,ton->tnh", ra, ca)
+
+
 def check_pre_all_tokens(inp, got, what, params=None, chunk=256, x=None, out=None):
     """Every token of a pre-map call (y, post, comb, pre) against the oracle, and with `x`/`out`
     the post-map that followed it.  The oracle runs on token chunks over threads (its ctypes
-    calls release the GIL), comparing each chunk as it finishes, so memory stays bounded."""
+    calls release the GIL), comparing each chunk as it finishes, so memory stays bounded.
+    fp32 streams (inp.res float32) are checked against the fp32-stream oracle; their post-map
+    against the oracle on the kernel's own post and comb (fp32), within F32_CHAIN_REL."""
     from concurrent.futures import ThreadPoolExecutor
 
     import oracle
@@ -81,18 +110,25 @@ def check_pre_all_tokens(inp, got, what, params=None, chunk=256, x=None, out=Non
     if params:
         p.update(params)
     T = inp.res.shape[0]
+    f32 = inp.res.dtype == np.float32
+    pre_fn = oracle.pre_f32s if f32 else oracle.pre
 
     def one(t0):
         t1 = min(T, t0 + chunk)
         r = inp.res[t0:t1]
-        ref = oracle.pre(r, inp.hc_fn, inp.hc_scale, inp.hc_base, rms_eps=p["rms_eps"], pre_eps=p["pre_eps"],
-                         sinkhorn_eps=p["sinkhorn_eps"], post_mult=p["post_mult"], num_iters=p["num_iters"])
+        ref = pre_fn(r, inp.hc_fn, inp.hc_scale, inp.hc_base, rms_eps=p["rms_eps"], pre_eps=p["pre_eps"],
+                     sinkhorn_eps=p["sinkhorn_eps"], post_mult=p["post_mult"], num_iters=p["num_iters"])
         if pre is not None:
             assert_f32_close(pre[t0:t1], ref["pre"], f"{what} pre [{t0}:{t1}]")
         assert_f32_close(post[t0:t1], ref["post"], f"{what} post [{t0}:{t1}]")
         assert_f32_close(comb[t0:t1], ref["comb"], f"{what} comb [{t0}:{t1}]")
         assert_bf16_close(y[t0:t1], ref["y"], f"{what} y [{t0}:{t1}]")
-        if out is not None:
+        if out is not None and f32:
+            gp, gc = post[t0:t1].astype(np.float64), comb[t0:t1].astype(np.float64)
+            ref_out = oracle.post_f32s(x[t0:t1], r, gp, gc)
+            assert_f32_chain_close(out[t0:t1], ref_out, post_f32s_scale(x[t0:t1], r, gp, gc),
+                                   f"{what} out [{t0}:{t1}]")
+        elif out is not None:
             ref_out = oracle.post(x[t0:t1], r, ref["post"], ref["comb"])
             assert_bf16_close(out[t0:t1], ref_out, f"{what} out [{t0}:{t1}]")
 

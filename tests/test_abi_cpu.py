@@ -397,7 +397,7 @@ def test_binding_rejects_cpu_tensors_before_the_library():
 
 
 PLAN_ENTRIES = ["post", "expand", "head_mean", "pre_fused", "collapse", "pre_from_dots", "pre_from_dots_backward",
-                "post_backward", "sinkhorn", "sinkhorn_backward"]
+                "post_backward", "sinkhorn", "sinkhorn_backward", "post_f32", "expand_f32", "head_mean_f32"]
 
 
 @pytest.mark.parametrize("entry", PLAN_ENTRIES)
@@ -448,3 +448,55 @@ def test_launch_plan_rejects_bad_arguments():
         mhc.MHC_ERROR_INVALID_VALUE
     assert lib.mhc_launch_plan(b"post", 1, 1, 1, None, ctypes.byref(n), ctypes.byref(n)) == \
         mhc.MHC_ERROR_INVALID_VALUE
+
+
+def _pre_f32(lib, **kw):
+    G = 1 << 40
+    a = dict(res=ctypes.c_void_p(G), fn=ctypes.c_void_p(2 * G), sc=ctypes.c_void_p(3 * G), base=ctypes.c_void_p(4 * G),
+             T=16, H=256, rms=1e-6, pe=1e-6, se=1e-6, pm=1.0, it=20, y=ctypes.c_void_p(5 * G),
+             post=ctypes.c_void_p(6 * G), comb=ctypes.c_void_p(7 * G), pre=None, ws=ctypes.c_void_p(8 * G),
+             wsb=1 << 30)
+    a.update(kw)
+    return lib.mhc_pre_fused_f32(a["res"], a["fn"], a["sc"], a["base"], a["T"], a["H"], a["rms"], a["pe"], a["se"],
+                                 a["pm"], a["it"], a["y"], a["post"], a["comb"], a["pre"], a["ws"], a["wsb"], NULL)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(T=-1), dict(H=0), dict(H=(1 << 20) + 4), dict(it=0), dict(rms=0.0), dict(se=-1e-6), dict(pe=-1.0),
+    dict(pm=float("nan")), dict(res=None), dict(fn=None), dict(sc=None), dict(base=None), dict(y=None),
+    dict(post=None), dict(comb=None),
+    dict(y=ctypes.c_void_p((1 << 40) + 16 * 4 * 256 * 4 - 8)),   # y overlaps the fp32 streams' last bytes
+    dict(pre=ctypes.c_void_p(7 << 40)),                          # pre overlaps comb
+])
+def test_pre_f32_validation_invalid(kw):
+    assert _pre_f32(mhc.lib(), **kw) == mhc.MHC_ERROR_INVALID_VALUE
+
+
+def test_pre_f32_validation_workspace_and_empty():
+    lib = mhc.lib()
+    need = mhc.mhc_pre_fused_workspace_bytes(16, 256)
+    assert _pre_f32(lib, wsb=need // 8) == mhc.MHC_ERROR_WORKSPACE
+    assert _pre_f32(lib, ws=None) == mhc.MHC_ERROR_WORKSPACE
+    assert _pre_f32(lib, ws=ctypes.c_void_p((8 << 40) + 64)) == mhc.MHC_ERROR_WORKSPACE  # not 256-byte aligned
+    assert _pre_f32(lib, T=0, res=None, y=None, ws=None) == mhc.MHC_SUCCESS
+
+
+def test_f32_stream_post_expand_head_validation():
+    lib = mhc.lib()
+    G = 1 << 40
+    x, res, post, comb, out = (ctypes.c_void_p(k * G) for k in range(1, 6))
+    assert lib.mhc_post_f32(x, res, post, comb, -1, 64, out, NULL) == mhc.MHC_ERROR_INVALID_VALUE
+    assert lib.mhc_post_f32(x, res, post, comb, 8, (1 << 20) + 1, out, NULL) == mhc.MHC_ERROR_INVALID_VALUE
+    assert lib.mhc_post_f32(None, res, post, comb, 8, 64, out, NULL) == mhc.MHC_ERROR_INVALID_VALUE
+    # out overlapping res partly (not exactly) is rejected; x overlapping out too
+    assert lib.mhc_post_f32(x, res, post, comb, 8, 64, ctypes.c_void_p(G * 2 + 4), NULL) == \
+        mhc.MHC_ERROR_INVALID_VALUE
+    assert lib.mhc_post_f32(ctypes.c_void_p(5 * G + 8), res, post, comb, 8, 64, out, NULL) == \
+        mhc.MHC_ERROR_INVALID_VALUE
+    assert lib.mhc_post_f32(None, None, None, None, 0, 64, None, NULL) == mhc.MHC_SUCCESS
+    assert lib.mhc_expand_f32(x, 8, 0, out, NULL) == mhc.MHC_ERROR_INVALID_VALUE
+    assert lib.mhc_expand_f32(None, 8, 64, out, NULL) == mhc.MHC_ERROR_INVALID_VALUE
+    assert lib.mhc_expand_f32(ctypes.c_void_p(5 * G + 16), 8, 64, out, NULL) == mhc.MHC_ERROR_INVALID_VALUE
+    assert lib.mhc_head_mean_f32(res, 8, 64, None, NULL) == mhc.MHC_ERROR_INVALID_VALUE
+    assert lib.mhc_head_mean_f32(res, 8, 64, ctypes.c_void_p(2 * G + 8), NULL) == mhc.MHC_ERROR_INVALID_VALUE
+    assert lib.mhc_head_mean_f32(None, 0, 64, None, NULL) == mhc.MHC_SUCCESS

@@ -183,3 +183,28 @@ def test_pre_from_dots_backward_chunks():
     torch.cuda.synchronize()
     assert np.array_equal(got["d_res"], bits_of(small["d_res"]))
     assert np.array_equal(got["d_dot"], f32_of(small["d_dot"]))
+
+
+def test_f32_stream_post_expand_head_mean_chunks():
+    """The fp32-stream post-map, model entry and unweighted head across a chunk edge."""
+    from tests._helpers import assert_f32_chain_close, post_f32s_scale
+    mhc = _mhc()
+    T, rows = _plan("post_f32")
+    assert _plan("expand_f32")[0] == T and _plan("head_mean_f32")[0] == T
+    x = device_normal_bf16(0, 908, "x", (T, H))
+    res = device_normal_f32(0, 908, "res", (T, HC, H))
+    post = device_normal_f32(0, 908, "post", (T, HC))
+    comb = device_normal_f32(0, 908, "comb_logits", (T, HC, HC), std=0.5)
+    out = mhc.mhc_post_f32(x, res, post, comb)
+    torch.cuda.synchronize()
+    xr, rr, pr, cr = bits_of(_at(x, rows)), f32_of(_at(res, rows)), f32_of(_at(post, rows)), f32_of(_at(comb, rows))
+    ref = oracle.post_f32s(xr, rr, pr.astype(np.float64), cr.astype(np.float64))
+    assert_f32_chain_close(f32_of(_at(out, rows)), ref, post_f32s_scale(xr, rr, pr, cr), f"post f32 T={T}")
+    del out, post, comb
+    y = mhc.mhc_head_mean_f32(res)
+    torch.cuda.synchronize()
+    assert_bf16_close(bits_of(_at(y, rows)), oracle.head_mean_f32s(rr), f"head_mean f32 T={T}")
+    del res, y
+    streams = mhc.mhc_expand_f32(x)
+    torch.cuda.synchronize()
+    assert np.array_equal(f32_of(_at(streams, rows)), oracle.expand_f32s(xr))
