@@ -1013,14 +1013,15 @@ __global__ __launch_bounds__(kColBlock) void pre_collapse_scalar_kernel(const ui
 // The pre-map over fp32 streams (the same steps; y is still a bf16 row).  The projection
 // runs on the fp32 MFMA (16x16x4: one fp32 value per lane and step), so neither operand
 // needs splitting: A holds 16 tokens, B 16 weight rows, and the 4 k of a step are one
-// stream's h = h0 + 16u + 4g + e of lane group g.  A workgroup takes one 64-token tile and
-// one 128-wide slice (a wave per 32-wide block, all 4 streams), keeps the block's weights
-// in VGPRs, and leaves the same 25-field partial records as the bf16 projection, which
-// pre_mixsum_kernel sums and the fp32 collapse below finishes.
+// stream's h = h0 + 16u + 4g + e of lane group g.  A workgroup owns one 128-wide slice (a
+// wave per 32-wide block, all 4 streams) and walks a range of 64-token tiles with the
+// block's weights in VGPRs; the streams of the next two 16-token row tiles are in flight
+// while one is multiplied.  Each tile leaves the same 25-field partial record as the bf16
+// projection, which pre_mixsum_kernel sums and the fp32 collapse below finishes.
 struct ProjF32Args {
     const float *res;   // the chunk's streams [T][4][H]
     const float *hc_fn; // [24][4H]
-    int T, H, S;
+    int T, H, S, tiles_per_range, ntiles;
     float *rec; // [tiles][S][25][64]
 };
 
@@ -1029,8 +1030,12 @@ __global__ __launch_bounds__(kPBlock, 2) void pre_proj_f32s_kernel(ProjF32Args a
 {
     __shared__ float red[kPWaves][kPTok][kMix];
     __shared__ float sqp[kPWaves][4][kPTok];
-    const int tile = blockIdx.x;
-    const int slice = blockIdx.y;
+    const int slice = blockIdx.x;
+    const int tile0 = blockIdx.y * a.tiles_per_range;
+    const int tile1 = min(a.ntiles, tile0 + a.tiles_per_range);
+    if (tile0 >= tile1) {
+        return; // the whole workgroup
+    }
     const int tid = threadIdx.x;
     const int w = tid >> 6;
     const int lane = tid & (kWave - 1);
@@ -1043,41 +1048,57 @@ __global__ __launch_bounds__(kPBlock, 2) void pre_proj_f32s_kernel(ProjF32Args a
 
     // B operands: weight row n * 16 + c (rows 24..31 zero) at stream i, h = h0 + 16u + 4g + e
     float wv[kHC][2][4][2];
-#pragma unroll
-    for (int i = 0; i < kHC; ++i) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int h = h0 + 16 * u + 4 * g + e;
-#pragma unroll
-                for (int n = 0; n < 2; ++n) {
-                    const int r = n * 16 + c;
-                    wv[i][u][e][n] = (r < kMix && h < H) ? a.hc_fn[(size_t)r * K + (size_t)i * H + h] : 0.0f;
-                }
-            }
-        }
-    }
-
-    const int t0 = tile * kPTok;
-    const int ntok = min(kPTok, a.T - t0);
-    // the tile's streams; tokens past the chunk and h past H read zero
-    const __amdgpu_buffer_rsrc_t v =
-        buf_view_uniform(a.res + (size_t)t0 * K, (uint32_t)((size_t)ntok * K * sizeof(float)));
-    auto load = [&](int m, float (&d)[kHC][2][4]) {
-        const int tok = m * 16 + c;
+    {
+        const __amdgpu_buffer_rsrc_t vw = buf_view_uniform(a.hc_fn, (uint32_t)((size_t)kMix * K * sizeof(float)));
 #pragma unroll
         for (int i = 0; i < kHC; ++i) {
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int h = h0 + 16 * u + 4 * g;
-                const uint32_t base = ((uint32_t)(tok * kHC + i) * (uint32_t)H) * 4u;
+#pragma unroll
+                for (int n = 0; n < 2; ++n) {
+                    const int r = n * 16 + c;
+                    const uint32_t base = r < kMix ? (uint32_t)((size_t)r * K + (size_t)i * H) * 4u : 0x80000000u;
+                    if constexpr (kVec) {
+                        const uint32_t off = h < H ? base + (uint32_t)h * 4u : 0x80000000u;
+                        const f32x4 q = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(vw, (int)off, 0, 0));
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            wv[i][u][e][n] = q[e];
+                        }
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const uint32_t off = h + e < H ? base + (uint32_t)(h + e) * 4u : 0x80000000u;
+                            wv[i][u][e][n] =
+                                __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vw, (int)off, 0, 0));
+                        }
+                    }
+                }
+            }
+        }
+    }
+
+    // row tile q of the range: 16 tokens (token c for this lane) of every stream at this
+    // lane's h; tiles past the range or tokens past the chunk, and h past H, read zero
+    const int nq = (tile1 - tile0) * kPMT;
+    auto load = [&](int q, float (&d)[kHC][2][4]) {
+        const int tok0 = tile0 * kPTok + q * 16;
+        const int ntok = q < nq ? max(0, min(16, a.T - tok0)) : 0;
+        const __amdgpu_buffer_rsrc_t v = buf_view_uniform(a.res + (size_t)(ntok > 0 ? tok0 : 0) * K,
+                                                          (uint32_t)((size_t)ntok * K * sizeof(float)));
+#pragma unroll
+        for (int i = 0; i < kHC; ++i) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int h = h0 + 16 * u + 4 * g;
+                const uint32_t base = ((uint32_t)(c * kHC + i) * (uint32_t)H) * 4u;
                 if constexpr (kVec) {
                     const uint32_t off = h < H ? base + (uint32_t)h * 4u : 0x80000000u;
-                    const f32x4 q = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(v, (int)off, 0, 0));
+                    const f32x4 q4 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(v, (int)off, 0, 0));
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        d[i][u][e] = q[e];
+                        d[i][u][e] = q4[e];
                     }
                 } else {
 #pragma unroll
@@ -1090,81 +1111,69 @@ __global__ __launch_bounds__(kPBlock, 2) void pre_proj_f32s_kernel(ProjF32Args a
         }
     };
 
-    f32x4 acc[kPMT][2];
-    float sq[kPMT];
-    float cur[kHC][2][4], nxt[kHC][2][4];
-    load(0, cur);
+    float buf[2][kHC][2][4];
+    load(0, buf[0]);
+    load(1, buf[1]);
+    for (int q0 = 0; q0 < nq; q0 += kPMT) {
 #pragma unroll
-    for (int m = 0; m < kPMT; ++m) {
-        if (m + 1 < kPMT) {
-            load(m + 1, nxt);
-        }
-        acc[m][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-        acc[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-        sq[m] = 0.0f;
-#pragma unroll
-        for (int i = 0; i < kHC; ++i) {
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float x = cur[i][u][e];
-                    sq[m] = fmaf(x, x, sq[m]);
-                    acc[m][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(x, wv[i][u][e][0], acc[m][0], 0, 0, 0);
-                    acc[m][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(x, wv[i][u][e][1], acc[m][1], 0, 0, 0);
-                }
-            }
-        }
-        if (m + 1 < kPMT) {
+        for (int m = 0; m < kPMT; ++m) {
+            float (&cur)[kHC][2][4] = buf[m & 1];
+            f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+            float sq = 0.0f;
 #pragma unroll
             for (int i = 0; i < kHC; ++i) {
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        cur[i][u][e] = nxt[i][u][e];
+                        const float x = cur[i][u][e];
+                        sq = fmaf(x, x, sq);
+                        acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(x, wv[i][u][e][0], acc[0], 0, 0, 0);
+                        acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(x, wv[i][u][e][1], acc[1], 0, 0, 0);
                     }
                 }
             }
-        }
-    }
-
-    // workgroup reduction -> this slice's partial record (the order of pre_proj_kernel)
+            load(q0 + m + 2, cur); // two row tiles ahead, into the registers just consumed
+            // this row tile's partials (the order of pre_proj_kernel: waves summed after the barrier)
 #pragma unroll
-    for (int m = 0; m < kPMT; ++m) {
+            for (int n = 0; n < 2; ++n) {
+                const int col = n * 16 + c;
+                if (col < kMix) {
 #pragma unroll
-        for (int n = 0; n < 2; ++n) {
-            const int col = n * 16 + c;
-            if (col < kMix) {
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    red[w][m * 16 + 4 * g + k][col] = acc[m][n][k];
+                    for (int k = 0; k < 4; ++k) {
+                        red[w][m * 16 + 4 * g + k][col] = acc[n][k];
+                    }
                 }
             }
+            sqp[w][g][m * 16 + c] = sq;
         }
-        sqp[w][g][m * 16 + c] = sq[m];
-    }
-    __syncthreads();
-    float *rec = a.rec + ((size_t)tile * S + slice) * (kRec * kPTok);
-    const int tok = tid & (kPTok - 1);
-    for (int col = tid >> 6; col < kMix; col += kPWaves) {
-        float s = red[0][tok][col];
+
+        // workgroup reduction -> this slice's partial record of the tile; LDS-only barriers
+        // keep the next loads in flight
+        lds_barrier();
+        const int tile = tile0 + q0 / kPMT;
+        float *rec = a.rec + ((size_t)tile * S + slice) * (kRec * kPTok);
+        const int tok = tid & (kPTok - 1);
+        for (int col = tid >> 6; col < kMix; col += kPWaves) {
+            float s = red[0][tok][col];
 #pragma unroll
-        for (int ww = 1; ww < kPWaves; ++ww) {
-            s += red[ww][tok][col];
-        }
-        rec[field_of_col(col) * kPTok + tok] = s;
-    }
-    if (tid < kPTok) {
-        float s = 0.0f;
-#pragma unroll
-        for (int ww = 0; ww < kPWaves; ++ww) {
-#pragma unroll
-            for (int gg = 0; gg < 4; ++gg) {
-                s += sqp[ww][gg][tid];
+            for (int ww = 1; ww < kPWaves; ++ww) {
+                s += red[ww][tok][col];
             }
+            rec[field_of_col(col) * kPTok + tok] = s;
         }
-        rec[kFSq * kPTok + tid] = s;
+        if (tid < kPTok) {
+            float s = 0.0f;
+#pragma unroll
+            for (int ww = 0; ww < kPWaves; ++ww) {
+#pragma unroll
+                for (int gg = 0; gg < 4; ++gg) {
+                    s += sqp[ww][gg][tid];
+                }
+            }
+            rec[kFSq * kPTok + tid] = s;
+        }
+        lds_barrier(); // the partials are read before the next tile writes them
     }
 }
 
@@ -1534,11 +1543,17 @@ hipError_t launch_pre_f32s(const float *res, const float *hc_fn, const float *hc
         a.T = Tc;
         a.H = H;
         a.S = g.slices;
+        a.ntiles = tiles;
         a.rec = reinterpret_cast<float *>(ws + g.off_rec);
+        // about two workgroups per CU over all slices, each walking a range of tiles
+        int ranges = kPSTargetBlocks / g.slices;
+        ranges = ranges < 1 ? 1 : (ranges > tiles ? tiles : ranges);
+        a.tiles_per_range = (tiles + ranges - 1) / ranges;
+        ranges = (tiles + a.tiles_per_range - 1) / a.tiles_per_range;
         if (vec4) {
-            pre_proj_f32s_kernel<true><<<dim3((unsigned)tiles, (unsigned)g.slices), dim3(kPBlock), 0, stream>>>(a);
+            pre_proj_f32s_kernel<true><<<dim3((unsigned)g.slices, (unsigned)ranges), dim3(kPBlock), 0, stream>>>(a);
         } else {
-            pre_proj_f32s_kernel<false><<<dim3((unsigned)tiles, (unsigned)g.slices), dim3(kPBlock), 0, stream>>>(a);
+            pre_proj_f32s_kernel<false><<<dim3((unsigned)g.slices, (unsigned)ranges), dim3(kPBlock), 0, stream>>>(a);
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) {
