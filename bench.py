@@ -62,6 +62,9 @@ def parse():
                              "pre_bf16", "expand", "head", "head_mean", "pre_bwd", "post_project", "fused",
                              "f32", "pre_f32", "post_f32", "expand_f32", "head_mean_f32"],
                     help="run only one call in the timed loop (for profiling)")
+    ap.add_argument("--presplit", action="store_true",
+                    help="split the fixed weights once before timing and time mhc_pre_fused_presplit (a decode "
+                         "loop's form: the weights do not change between steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-steady-state", action="store_true",
                     help="skip the steady-state sublayer step of the default run (for per-kernel profiles of the "
@@ -143,7 +146,14 @@ def main():
         d_post = torch.empty_like(post)
         d_comb = torch.empty_like(comb)
 
+    if args.presplit:
+        mhc.mhc_pre_split_weights(hc_fn, ws)  # once, outside the timed steps
+
     def call_pre():
+        if args.presplit:
+            mhc.mhc_pre_fused_presplit(res, hc_fn, hc_scale, hc_base, p["rms_eps"], p["pre_eps"], p["sinkhorn_eps"],
+                                       p["post_mult"], p["num_iters"], y=y, post=post, comb=comb, workspace=ws)
+            return
         mhc.mhc_pre_fused(res, hc_fn, hc_scale, hc_base, p["rms_eps"], p["pre_eps"], p["sinkhorn_eps"],
                           p["post_mult"], p["num_iters"], y=y, post=post, comb=comb, workspace=ws)
 
@@ -420,7 +430,13 @@ def main():
     calls = {}
     proj = "pre_proj_stream_kernel" if H % 8 == 0 else "pre_proj_kernel"
     col = "pre_collapse_vec8_kernel" if H % 8 == 0 else "pre_collapse_scalar_kernel"
-    pre_kernels = "pre_coop_kernel" if pre_one_read(T, H) else "pre_prep_kernel+" + proj + "+pre_mixsum_kernel+" + col
+    # the two-pass form: the weight split (unless done before the steps), the projection, the
+    # slice sums (above 64 tokens; below, the collapse sums the slices) and the collapse
+    sums = [] if T <= 64 else ["pre_mixsum_kernel"]
+    one_read = pre_one_read(T, H)
+    pre_kernels = "pre_coop_kernel" if one_read else "+".join(
+        ([] if args.presplit else ["pre_prep_kernel"]) + [proj] + sums + [col])
+    split_kernels = "pre_coop_kernel" if one_read else "+".join(["pre_prep_kernel", proj] + sums + [col])
     if "pre_ms" in breakdown:
         calls["mhc_pre_fused"] = (pre_kernels, breakdown["pre_ms"], pre_b)
     if "post_ms" in breakdown:
@@ -434,9 +450,9 @@ def main():
     if "post_bwd_ms" in breakdown:
         calls["mhc_post_backward"] = ("post_bwd_kernel", breakdown["post_bwd_ms"], step_bytes)
     if "pre_bf16_ms" in breakdown:
-        calls["mhc_pre_fused_bf16"] = (pre_kernels, breakdown["pre_bf16_ms"], step_bytes)
+        calls["mhc_pre_fused_bf16"] = (split_kernels, breakdown["pre_bf16_ms"], step_bytes)
     if "head_ms" in breakdown:
-        calls["mhc_head"] = (pre_kernels, breakdown["head_ms"], step_bytes)
+        calls["mhc_head"] = (split_kernels, breakdown["head_ms"], step_bytes)
     if "pre_bwd_ms" in breakdown:
         calls["mhc_pre_fused_backward"] = ("pre_prep_kernel+" + proj + "+pre_mixsum_kernel+pre_dots_bwd_kernel+"
                                            "pre_bwd_partial_kernel+pre_bwd_final_kernel+proj_bwd_wfrag_kernel+"
@@ -452,7 +468,7 @@ def main():
         calls["mhc_post_project"] = ("pre_prep_kernel+post_proj_stream_kernel+pre_mixsum_kernel",
                                      breakdown["post_project_ms"], step_bytes)
     if "pre_f32_ms" in breakdown:
-        proj32 = "pre_proj_f32s_kernel+pre_mixsum_kernel+pre_collapse_f32s_kernel"
+        proj32 = "+".join(["pre_proj_f32s_kernel"] + sums + ["pre_collapse_f32s_kernel"])
         calls["mhc_pre_fused_f32"] = (proj32, breakdown["pre_f32_ms"], algorithmic_bytes_pre_f32(T, H))
     if "post_f32_ms" in breakdown:
         calls["mhc_post_f32"] = ("post_f32s_kernel", breakdown["post_f32_ms"], algorithmic_bytes_post_f32(T, H))
@@ -492,9 +508,10 @@ def main():
 
     # Sanity figures: the launch floor of the step's kernel count (one-element fills,
     # launched the same way), and what a plain elementwise copy sustains here.
-    npre = 1 if pre_one_read(T, H) else 4
-    nker = {"all": npre + 1, "pre": npre, "post": 1, "post_project": 3, "fused": 4, "f32": 4, "pre_f32": 3,
-            "post_f32": 1}.get(args.only)
+    npre = 1 if pre_one_read(T, H) else 2 + (0 if args.presplit else 1) + (0 if T <= 64 else 1)
+    npre32 = 2 + (0 if T <= 64 else 1)
+    nker = {"all": npre + 1, "pre": npre, "post": 1, "post_project": 3, "fused": 4, "f32": npre32 + 1,
+            "pre_f32": npre32, "post_f32": 1}.get(args.only)
     launch_floor_ms = None
     if nker:
         one = torch.zeros(1, device=dev)
@@ -543,6 +560,7 @@ def main():
         "config": {"workload": (f"mhc {args.only} 2^20 4x4 matrices" if args.only.startswith("sinkhorn") else
                                 f"mhc {args.only if args.only != 'all' else 'pre+post'} T={T} H={H} HC=4"),
                    "launch": "HIP graph replay" if args.graph else "eager",
+                   "weights": "split once before the timed steps" if args.presplit else "split in every step",
                    "cache_flush_mib": flush_mb,
                    "T": T, "H": H, "hc": 4, "num_iters": p["num_iters"], "inputs": "resident in HBM"},
         "effective_GBps": round(eff_gbps, 1),

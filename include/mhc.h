@@ -149,6 +149,34 @@ mhc_status mhc_pre_fused(const uint16_t *res, const float *hc_fn, const float *h
                          size_t workspace_bytes, void *stream);
 
 /*
+ * mhc_pre_split_weights / mhc_pre_fused_presplit -- mhc_pre_fused with its weight split
+ * done once ahead of the calls, for weights that stay fixed over many calls (a decode
+ * loop; metrale glm5next_mhc.rs, Glm5NextMhcSiteWeights: a site's weights are uploaded
+ * once by the loader and every call reuses them).
+ *
+ * mhc_pre_split_weights writes the split of hc_fn ([24, 4H] fp32: three bf16 terms per
+ * weight, in the projection's MFMA operand order) into the first mhc_pre_split_bytes(H)
+ * bytes of `workspace` (256-byte aligned, device; must not overlap hc_fn).  1 <= H <=
+ * 2097152.
+ *
+ * mhc_pre_fused_presplit takes mhc_pre_fused's arguments, with a workspace that holds the
+ * split of this hc_fn: mhc_pre_split_weights ran on it, ordered before this call (same
+ * stream or synchronised), and neither hc_fn nor the workspace's first
+ * mhc_pre_split_bytes(H) bytes changed since (mhc_pre_fused calls on the same workspace
+ * rewrite them with the same values, so they keep it valid).  The two-pass form then skips
+ * its weight-split launch; the one-read form (16-byte rows, T >= 1024, 1024 < H <= 8192)
+ * splits in-kernel and ignores the stored split.  Results equal mhc_pre_fused's bit for
+ * bit; a stale split gives the results of the weights it was made from.
+ */
+size_t mhc_pre_split_bytes(int64_t H);
+mhc_status mhc_pre_split_weights(const float *hc_fn, int64_t H, void *workspace, size_t workspace_bytes,
+                                 void *stream);
+mhc_status mhc_pre_fused_presplit(const uint16_t *res, const float *hc_fn, const float *hc_scale,
+                                  const float *hc_base, int64_t T, int64_t H, float rms_eps, float pre_eps,
+                                  float sinkhorn_eps, float post_mult, int32_t num_iters, uint16_t *y, float *post,
+                                  float *comb, float *pre, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * mhc_pre_fused_noalloc -- mhc_pre_fused for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
  * no workspace argument.  Its scratch is a file-scope device array of

@@ -70,6 +70,12 @@ def lib() -> ctypes.CDLL:
     L.mhc_pre_fused_bf16.restype = ctypes.c_int
     L.mhc_pre_fused_noalloc.argtypes = [P, P, P, P, I64, I64, F, F, F, F, I32, P, P, P, P, P]
     L.mhc_pre_fused_noalloc.restype = ctypes.c_int
+    L.mhc_pre_split_bytes.argtypes = [I64]
+    L.mhc_pre_split_bytes.restype = SZ
+    L.mhc_pre_split_weights.argtypes = [P, I64, P, SZ, P]
+    L.mhc_pre_split_weights.restype = ctypes.c_int
+    L.mhc_pre_fused_presplit.argtypes = [P, P, P, P, I64, I64, F, F, F, F, I32, P, P, P, P, P, SZ, P]
+    L.mhc_pre_fused_presplit.restype = ctypes.c_int
     L.mhc_pre_fused_f32.argtypes = [P, P, P, P, I64, I64, F, F, F, F, I32, P, P, P, P, P, SZ, P]
     L.mhc_pre_fused_f32.restype = ctypes.c_int
     L.mhc_post_f32.argtypes = [P, P, P, P, I64, I64, P, P]
@@ -198,6 +204,34 @@ def mhc_pre_fused_noalloc(res: torch.Tensor, hc_fn: torch.Tensor, hc_scale: torc
     None are allocated by this Python wrapper, not by the library."""
     return _pre_fused("mhc_pre_fused_noalloc", torch.float32, res, hc_fn, hc_scale, hc_base, rms_eps, pre_eps,
                       sinkhorn_eps, post_mult, num_iters, y, post, comb, pre, return_pre, None, noalloc=True)
+
+
+def mhc_pre_split_bytes(H: int) -> int:
+    return int(lib().mhc_pre_split_bytes(int(H)))
+
+
+def mhc_pre_split_weights(hc_fn: torch.Tensor, workspace: torch.Tensor) -> torch.Tensor:
+    """Split hc_fn [24, 4H] fp32 into the start of a pre-map workspace (uint8, device), for
+    :func:`mhc_pre_fused_presplit` calls with the same weights.  Returns the workspace."""
+    _need(hc_fn, "hc_fn", torch.float32)
+    if hc_fn.dim() != 2 or hc_fn.shape[0] != MIX or hc_fn.shape[1] % HC != 0:
+        raise ValueError(f"hc_fn must be [24, 4H], got {tuple(hc_fn.shape)}")
+    H = hc_fn.shape[1] // HC
+    _need(workspace, "workspace", torch.uint8)
+    _same_device(hc_fn, workspace)
+    _check("mhc_pre_split_weights", lib().mhc_pre_split_weights(_ptr(hc_fn), H, _ptr(workspace), workspace.numel(),
+                                                                _stream(hc_fn.device)))
+    return workspace
+
+
+def mhc_pre_fused_presplit(res: torch.Tensor, hc_fn: torch.Tensor, hc_scale: torch.Tensor, hc_base: torch.Tensor,
+                           rms_eps: float = 1e-6, pre_eps: float = 1e-6, sinkhorn_eps: float = 1e-6,
+                           post_mult: float = 1.0, num_iters: int = 20, *, workspace: torch.Tensor, y=None,
+                           post=None, comb=None, pre=None, return_pre: bool = False):
+    """:func:`mhc_pre_fused` on a workspace that :func:`mhc_pre_split_weights` prepared with
+    this hc_fn (the two-pass form skips its weight split)."""
+    return _pre_fused("mhc_pre_fused_presplit", torch.float32, res, hc_fn, hc_scale, hc_base, rms_eps, pre_eps,
+                      sinkhorn_eps, post_mult, num_iters, y, post, comb, pre, return_pre, workspace)
 
 
 def mhc_pre_fused_f32(res: torch.Tensor, hc_fn: torch.Tensor, hc_scale: torch.Tensor, hc_base: torch.Tensor,
@@ -755,6 +789,7 @@ def mhc_pre_fused_backward(dy: torch.Tensor, d_post: torch.Tensor, d_comb: torch
 
 
 __all__ = ["mhc_sinkhorn", "mhc_pre_fused", "mhc_pre_fused_noalloc", "mhc_pre_fused_bf16", "mhc_pre_fused_f32",
+           "mhc_pre_split_bytes", "mhc_pre_split_weights", "mhc_pre_fused_presplit",
            "mhc_post_f32", "mhc_expand_f32", "mhc_head_mean_f32", "mhc_expand", "mhc_head_mean", "mhc_head",
            "mhc_pre_fused_workspace_bytes", "mhc_pre_from_dots", "mhc_post",
            "mhc_sinkhorn_backward", "mhc_post_backward", "mhc_pre_from_dots_backward",

@@ -58,7 +58,7 @@ mhc_status pre_common(const uint16_t *res, const void *hc_fn, bool fn_bf16, int 
                       int n_scale, const float *hc_base, int64_t T, int64_t H, float rms_eps, float pre_eps,
                       float sinkhorn_eps, float post_mult, int32_t num_iters, bool head, uint16_t *y, float *post,
                       float *comb, float *pre, void *workspace, size_t workspace_bytes, void *stream,
-                      bool validate_only = false)
+                      bool validate_only = false, bool presplit = false)
 {
     if (!sizes_ok(T, H) || H > kPreMaxH || num_iters < 1 || !finite(rms_eps) || !(rms_eps > 0.0f) || !finite(pre_eps) ||
         pre_eps < 0.0f || !finite(sinkhorn_eps) || !(sinkhorn_eps > 0.0f) || !finite(post_mult)) {
@@ -103,7 +103,7 @@ mhc_status pre_common(const uint16_t *res, const void *hc_fn, bool fn_bf16, int 
     }
     return launch_status(mhc::launch_pre(res, hc_fn, fn_bf16, fn_rows, hc_scale, hc_base, g, rms_eps, pre_eps,
                                          sinkhorn_eps, post_mult, num_iters, head, y, post, comb, pre, workspace,
-                                         (hipStream_t)stream, vec8));
+                                         (hipStream_t)stream, vec8, presplit));
 }
 
 // The no-allocation pre-map's scratch: a file-scope device array.  In host code the name
@@ -241,6 +241,40 @@ mhc_status mhc_pre_fused(const uint16_t *res, const float *hc_fn, const float *h
 {
     return pre_common(res, hc_fn, false, kMixRows, hc_scale, 3, hc_base, T, H, rms_eps, pre_eps, sinkhorn_eps,
                       post_mult, num_iters, false, y, post, comb, pre, workspace, workspace_bytes, stream);
+}
+
+size_t mhc_pre_split_bytes(int64_t H)
+{
+    if (H <= 0 || H > kPreMaxH) {
+        return 0;
+    }
+    return mhc::pre_split_bytes(H);
+}
+
+mhc_status mhc_pre_split_weights(const float *hc_fn, int64_t H, void *workspace, size_t workspace_bytes,
+                                 void *stream)
+{
+    if (H <= 0 || H > kPreMaxH || !hc_fn) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    const size_t need = mhc::pre_split_bytes(H);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0) {
+        return MHC_ERROR_WORKSPACE;
+    }
+    if (overlaps(workspace, need, hc_fn, (size_t)kMixRows * 4 * H * 4)) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    return launch_status(mhc::launch_pre_split_any(hc_fn, false, kMixRows, H, workspace, (hipStream_t)stream));
+}
+
+mhc_status mhc_pre_fused_presplit(const uint16_t *res, const float *hc_fn, const float *hc_scale,
+                                  const float *hc_base, int64_t T, int64_t H, float rms_eps, float pre_eps,
+                                  float sinkhorn_eps, float post_mult, int32_t num_iters, uint16_t *y, float *post,
+                                  float *comb, float *pre, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return pre_common(res, hc_fn, false, kMixRows, hc_scale, 3, hc_base, T, H, rms_eps, pre_eps, sinkhorn_eps,
+                      post_mult, num_iters, false, y, post, comb, pre, workspace, workspace_bytes, stream, false,
+                      true);
 }
 
 mhc_status mhc_pre_fused_noalloc(const uint16_t *res, const float *hc_fn, const float *hc_scale,

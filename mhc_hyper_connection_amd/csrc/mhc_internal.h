@@ -77,7 +77,13 @@ PreGeom pre_geometry(int64_t T, int64_t H, bool with_dy = false);
 hipError_t launch_pre(const uint16_t *res, const void *hc_fn, bool fn_bf16, int fn_rows, const float *hc_scale,
                       const float *hc_base, const PreGeom &g, float rms_eps, float pre_eps, float sinkhorn_eps,
                       float post_mult, int iters, bool head, uint16_t *y, float *post, float *comb, float *pre,
-                      void *workspace, hipStream_t stream, bool vec8);
+                      void *workspace, hipStream_t stream, bool vec8, bool presplit = false);
+// The weight split of the two-pass pre-map (bf16 x 3 MFMA fragments of hc_fn, fp32 or
+// bf16 with `fn_rows` rows) into the fragment area at the start of a pre-map workspace,
+// pre_split_bytes(H) bytes; launch_pre with `presplit` then skips it.
+hipError_t launch_pre_split_any(const void *hc_fn, bool fn_bf16, int fn_rows, int64_t H, void *workspace,
+                                hipStream_t stream);
+size_t pre_split_bytes(int64_t H);
 
 // The pre-map with one read of the streams: on each of the 8 XCDs a group of 32
 // workgroups splits K, holds 16-token steps of the streams in LDS and exchanges partial

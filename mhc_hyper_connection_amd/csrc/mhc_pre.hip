@@ -833,6 +833,9 @@ static void pre_stream_ranges(int Tc, int S, int &ranges, int &tok_per_range)
 // field): thread (token, slice group k) adds slices k, k+4, ... (independent
 // loads in flight), then the four group sums are added in a fixed order.
 constexpr int kSumStride = 32; // floats per token in the sums array (25 used)
+// Up to this many tokens per chunk the collapse sums the slices' records itself instead of
+// a separate slice-sum launch (each of a token's waves redoes 5 sums over the slices).
+constexpr int kFuseSumTokens = 64;
 __global__ __launch_bounds__(256) void pre_mixsum_kernel(const float *__restrict__ rec, int T, int S, int nrec,
                                                          float *__restrict__ sums, float *__restrict__ dots,
                                                          float *__restrict__ sq)
@@ -887,12 +890,78 @@ struct MixArgs {
     int iters;
     int head; // the weighted head: pre weights and y only
     float *post, *comb, *pre_out;
+    // Small batches: the projection's partial records ([tiles][S][nrec][64]) instead of
+    // `sums`; each token's fields are summed over the S slices where they are used.
+    const float *rec;
+    int S, nrec;
 };
 
-// pre weights of token t from its sums (wave-uniform).
-__device__ __forceinline__ void token_pre(const MixArgs &m, int t, float *p, float &rstd)
+// Fields f0 .. f0 + N - 1 of token t: from the sums, or (m.rec set) summed over the slices'
+// records, lane l adding slices l, l + 64, ... in order (all N loads in flight together) and
+// then a butterfly over the wave, so every lane holds the same totals.  Called by whole
+// waves with a wave-uniform t.
+template <int N> __device__ __forceinline__ void mix_fields(const MixArgs &m, int t, int f0, float (&out)[N])
 {
-    const float *d = m.sums + (size_t)t * m.stride;
+    if (m.rec == nullptr) {
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+            out[k] = m.sums[(size_t)t * m.stride + f0 + k];
+        }
+        return;
+    }
+    const int lane = threadIdx.x & (kWave - 1);
+    const size_t rs = (size_t)m.nrec * kPTok; // floats per slice record
+    const float *p = m.rec + (size_t)(t / kPTok) * m.S * rs + (size_t)f0 * kPTok + (t % kPTok);
+    float v[N];
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        v[k] = 0.0f;
+    }
+    for (int s = lane; s < m.S; s += kWave) {
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+            v[k] += p[(size_t)s * rs + (size_t)k * kPTok];
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        out[k] = wave_sum(v[k]);
+    }
+}
+
+// The fields of token t a wave needs: the pre dots and the sum of squares (d[0..4]), and
+// with kAll (the wave that finishes post and comb) also the post and comb dots (d[5..24]);
+// in the records' mode all in one batch of loads.
+template <bool kAll> __device__ __forceinline__ void token_fields(const MixArgs &m, int t, float (&d)[kRec])
+{
+    if (m.rec != nullptr) {
+        float v[kAll ? kRec : kHC + 1];
+        mix_fields(m, t, 0, v);
+#pragma unroll
+        for (int k = 0; k < (kAll ? kRec : kHC + 1); ++k) {
+            d[k] = v[k];
+        }
+        return;
+    }
+    float v[kHC + 1];
+    mix_fields(m, t, 0, v); // field kFSq is the sum of squares only when m.sq is null
+#pragma unroll
+    for (int k = 0; k <= kHC; ++k) {
+        d[k] = v[k];
+    }
+    if (kAll) {
+        float w[kMix - kHC];
+        mix_fields(m, t, m.off_post, w);
+#pragma unroll
+        for (int k = 0; k < kMix - kHC; ++k) {
+            d[kHC + 1 + k] = w[k];
+        }
+    }
+}
+
+// pre weights of token t from its fields (wave-uniform).
+__device__ __forceinline__ void token_pre(const MixArgs &m, int t, const float (&d)[kRec], float *p, float &rstd)
+{
     const float S = m.sq != nullptr ? m.sq[t] : d[kFSq];
     rstd = 1.0f / sqrtf(S / m.k_denom + m.rms_eps);
 #pragma unroll
@@ -901,8 +970,10 @@ __device__ __forceinline__ void token_pre(const MixArgs &m, int t, float *p, flo
     }
 }
 
-// post, comb (Sinkhorn) and the optional pre output of token t (one lane writes).
-__device__ __forceinline__ void token_mix_outputs(const MixArgs &m, int t, const float *p, float rstd, bool writer)
+// post, comb (Sinkhorn) and the optional pre output of token t (one lane writes); d from
+// token_fields<true>.
+__device__ __forceinline__ void token_mix_outputs(const MixArgs &m, int t, const float (&d)[kRec], const float *p,
+                                                  float rstd, bool writer)
 {
     if (m.head) {
         if (writer && m.pre_out) {
@@ -913,16 +984,15 @@ __device__ __forceinline__ void token_mix_outputs(const MixArgs &m, int t, const
         }
         return;
     }
-    const float *d = m.sums + (size_t)t * m.stride;
     float post[kHC];
 #pragma unroll
     for (int i = 0; i < kHC; ++i) {
-        post[i] = sigmoidf_fast(fmaf(d[m.off_post + i] * rstd, m.hc_scale[1], m.hc_base[kHC + i])) * m.post_mult;
+        post[i] = sigmoidf_fast(fmaf(d[kHC + 1 + i] * rstd, m.hc_scale[1], m.hc_base[kHC + i])) * m.post_mult;
     }
     float P16[kHC * kHC];
 #pragma unroll
     for (int e = 0; e < kHC * kHC; ++e) {
-        P16[e] = fmaf(d[m.off_post + kHC + e] * rstd, m.hc_scale[2], m.hc_base[2 * kHC + e]);
+        P16[e] = fmaf(d[2 * kHC + 1 + e] * rstd, m.hc_scale[2], m.hc_base[2 * kHC + e]);
     }
     sinkhorn4x4(P16, m.iters, m.sk_eps);
     if (writer) {
@@ -940,6 +1010,19 @@ __device__ __forceinline__ void token_mix_outputs(const MixArgs &m, int t, const
     }
 }
 
+// A collapse wave's token work: its fields (tile 0 also post and comb, unless the head),
+// then the pre weights; tile 0 then finishes post, comb and the pre output after the collapse.
+__device__ __forceinline__ void token_start(const MixArgs &m, int t, bool first, float (&d)[kRec], float *p,
+                                            float &rstd)
+{
+    if (first && !m.head) {
+        token_fields<true>(m, t, d);
+    } else {
+        token_fields<false>(m, t, d);
+    }
+    token_pre(m, t, d, p, rstd);
+}
+
 __global__ __launch_bounds__(kColBlock) void pre_collapse_vec8_kernel(const uint16_t *__restrict__ res, MixArgs mx,
                                                                       int T, int H, int tiles_per_token,
                                                                       uint16_t *__restrict__ y)
@@ -951,16 +1034,18 @@ __global__ __launch_bounds__(kColBlock) void pre_collapse_vec8_kernel(const uint
     if (t >= T) {
         return;
     }
-    float p[kHC], rstd;
-    token_pre(mx, t, p, rstd);
+    // the streams first: their loads are in flight while the token's fields are summed
     const int h = tile * kColVecTile + lane * 8;
-    if (h < H) {
-    const size_t row = (size_t)t * kHC * H + h;
+    const bool hin = h < H;
+    const size_t row = (size_t)t * kHC * H + (hin ? h : 0);
     u32x4 rw[kHC];
 #pragma unroll
     for (int i = 0; i < kHC; ++i) {
         rw[i] = load_nt16(res + row + (size_t)i * H);
     }
+    float d[kRec], p[kHC], rstd;
+    token_start(mx, t, tile == 0, d, p, rstd);
+    if (hin) {
     u32x4 yw;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -976,7 +1061,7 @@ __global__ __launch_bounds__(kColBlock) void pre_collapse_vec8_kernel(const uint
     store_nt16(y + (size_t)t * H + h, yw);
     }
     if (tile == 0) {
-        token_mix_outputs(mx, t, p, rstd, lane == 0);
+        token_mix_outputs(mx, t, d, p, rstd, lane == 0);
     }
 }
 
@@ -992,20 +1077,26 @@ __global__ __launch_bounds__(kColBlock) void pre_collapse_scalar_kernel(const ui
     if (t >= T) {
         return;
     }
-    float p[kHC], rstd;
-    token_pre(mx, t, p, rstd);
     const int h = tile * kWave + lane;
-    if (h < H) {
-        const size_t row = (size_t)t * kHC * H + h;
-        float a = bf16_to_f32(res[row]) * p[0];
+    const bool hin = h < H;
+    const size_t row = (size_t)t * kHC * H + (hin ? h : 0);
+    float r[kHC];
+#pragma unroll
+    for (int i = 0; i < kHC; ++i) {
+        r[i] = bf16_to_f32(res[row + (size_t)i * H]);
+    }
+    float d[kRec], p[kHC], rstd;
+    token_start(mx, t, tile == 0, d, p, rstd);
+    if (hin) {
+        float a = r[0] * p[0];
 #pragma unroll
         for (int i = 1; i < kHC; ++i) {
-            a = fmaf(bf16_to_f32(res[row + (size_t)i * H]), p[i], a);
+            a = fmaf(r[i], p[i], a);
         }
         y[(size_t)t * H + h] = f32_to_bf16(a);
     }
     if (tile == 0) {
-        token_mix_outputs(mx, t, p, rstd, lane == 0);
+        token_mix_outputs(mx, t, d, p, rstd, lane == 0);
     }
 }
 
@@ -1194,43 +1285,45 @@ __global__ __launch_bounds__(kColBlock) void pre_collapse_f32s_kernel(const floa
     if (t >= T) {
         return;
     }
-    float p[kHC], rstd;
-    token_pre(mx, t, p, rstd);
-    if constexpr (kVec) {
-        const int h = tile * kColVecTileF + lane * 4;
-        if (h < H) {
-            const size_t row = (size_t)t * kHC * H + h;
-            f32x4 r[kHC];
+    // the streams first: their loads are in flight while the token's fields are summed
+    const int h = tile * (kVec ? kColVecTileF : kWave) + lane * (kVec ? 4 : 1);
+    const bool hin = h < H;
+    const size_t row = (size_t)t * kHC * H + (hin ? h : 0);
+    constexpr int kE = kVec ? 4 : 1;
+    float r[kHC][kE];
 #pragma unroll
-            for (int i = 0; i < kHC; ++i) {
-                r[i] = __builtin_bit_cast(f32x4, load_nt16(res + row + (size_t)i * H));
-            }
-            float o[4];
+    for (int i = 0; i < kHC; ++i) {
+        if constexpr (kVec) {
+            const f32x4 v = __builtin_bit_cast(f32x4, load_nt16(res + row + (size_t)i * H));
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                float s = r[0][j] * p[0];
-#pragma unroll
-                for (int i = 1; i < kHC; ++i) {
-                    s = fmaf(r[i][j], p[i], s);
-                }
-                o[j] = s;
+                r[i][j] = v[j];
             }
-            *reinterpret_cast<uint2 *>(y + (size_t)t * H + h) = uint2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+        } else {
+            r[i][0] = res[row + (size_t)i * H];
         }
-    } else {
-        const int h = tile * kWave + lane;
-        if (h < H) {
-            const size_t row = (size_t)t * kHC * H + h;
-            float s = res[row] * p[0];
+    }
+    float d[kRec], p[kHC], rstd;
+    token_start(mx, t, tile == 0, d, p, rstd);
+    if (hin) {
+        float o[kE];
+#pragma unroll
+        for (int j = 0; j < kE; ++j) {
+            float s = r[0][j] * p[0];
 #pragma unroll
             for (int i = 1; i < kHC; ++i) {
-                s = fmaf(res[row + (size_t)i * H], p[i], s);
+                s = fmaf(r[i][j], p[i], s);
             }
-            y[(size_t)t * H + h] = f32_to_bf16(s);
+            o[j] = s;
+        }
+        if constexpr (kVec) {
+            *reinterpret_cast<uint2 *>(y + (size_t)t * H + h) = uint2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+        } else {
+            y[(size_t)t * H + h] = f32_to_bf16(o[0]);
         }
     }
     if (tile == 0) {
-        token_mix_outputs(mx, t, p, rstd, lane == 0);
+        token_mix_outputs(mx, t, d, p, rstd, lane == 0);
     }
 }
 
@@ -1272,6 +1365,29 @@ PreGeom pre_geometry(int64_t T, int64_t H, bool with_dy)
     off += align256((size_t)g.chunk * kSumStride * sizeof(float));
     g.total_bytes = off;
     return g;
+}
+
+hipError_t launch_pre_split_any(const void *hc_fn, bool fn_bf16, int fn_rows, int64_t H, void *workspace,
+                                hipStream_t stream)
+{
+    const PreGeom g = pre_geometry(1, H);
+    u32x4 *frag = reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(workspace) + g.off_frag);
+    const int prep_threads = g.nhb * kHC * (kFragPerHbStream / 3);
+    const dim3 prep_grid((unsigned)((prep_threads + 255) / 256));
+    if (fn_bf16) {
+        pre_prep_kernel<uint16_t><<<prep_grid, dim3(256), 0, stream>>>(reinterpret_cast<const uint16_t *>(hc_fn),
+                                                                       (int)H, g.nhb, fn_rows, frag);
+    } else {
+        pre_prep_kernel<float><<<prep_grid, dim3(256), 0, stream>>>(reinterpret_cast<const float *>(hc_fn), (int)H,
+                                                                    g.nhb, fn_rows, frag);
+    }
+    return hipGetLastError();
+}
+
+size_t pre_split_bytes(int64_t H)
+{
+    const PreGeom g = pre_geometry(1, H);
+    return g.off_rec; // the fragment area, from offset 0
 }
 
 hipError_t launch_pre_split(const float *hc_fn, const PreGeom &g, void *workspace, hipStream_t stream)
@@ -1428,7 +1544,7 @@ hipError_t launch_pre_sums(const uint16_t *res, const uint16_t *dy, const PreGeo
 hipError_t launch_pre(const uint16_t *res, const void *hc_fn, bool fn_bf16, int fn_rows, const float *hc_scale,
                       const float *hc_base, const PreGeom &g, float rms_eps, float pre_eps, float sinkhorn_eps,
                       float post_mult, int iters, bool head, uint16_t *y, float *post, float *comb, float *pre,
-                      void *workspace, hipStream_t stream, bool vec8)
+                      void *workspace, hipStream_t stream, bool vec8, bool presplit)
 {
     if (pre_coop_usable(g.T, g.H, vec8)) {
         return launch_pre_coop(res, hc_fn, fn_bf16, fn_rows, hc_scale, hc_base, g.T, g.H, rms_eps, pre_eps,
@@ -1438,18 +1554,12 @@ hipError_t launch_pre(const uint16_t *res, const void *hc_fn, bool fn_bf16, int 
     u32x4 *frag = reinterpret_cast<u32x4 *>(ws + g.off_frag);
     const int H = (int)g.H;
 
-    const int prep_threads = g.nhb * kHC * (kFragPerHbStream / 3);
-    const dim3 prep_grid((unsigned)((prep_threads + 255) / 256));
-    if (fn_bf16) {
-        pre_prep_kernel<uint16_t><<<prep_grid, dim3(256), 0, stream>>>(reinterpret_cast<const uint16_t *>(hc_fn), H,
-                                                                       g.nhb, fn_rows, frag);
-    } else {
-        pre_prep_kernel<float><<<prep_grid, dim3(256), 0, stream>>>(reinterpret_cast<const float *>(hc_fn), H, g.nhb,
-                                                                    fn_rows, frag);
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) {
-        return e;
+    hipError_t e = hipSuccess;
+    if (!presplit) { // else the caller split these weights into the workspace already
+        e = launch_pre_split_any(hc_fn, fn_bf16, fn_rows, H, workspace, stream);
+        if (e != hipSuccess) {
+            return e;
+        }
     }
     float *sums = reinterpret_cast<float *>(ws + g.off_prew);
     for (int64_t c0 = 0; c0 < g.T; c0 += g.chunk) {
@@ -1483,13 +1593,20 @@ hipError_t launch_pre(const uint16_t *res, const void *hc_fn, bool fn_bf16, int 
         if (e != hipSuccess) {
             return e;
         }
-        pre_mixsum_kernel<<<dim3((unsigned)(tiles * g.nrec)), dim3(256), 0, stream>>>(a.rec, Tc, g.slices, g.nrec,
-                                                                                    sums, nullptr, nullptr);
-        e = hipGetLastError();
-        if (e != hipSuccess) {
-            return e;
+        // small batches: the collapse sums the slices itself (one launch fewer)
+        const bool fuse = Tc <= kFuseSumTokens;
+        if (!fuse) {
+            pre_mixsum_kernel<<<dim3((unsigned)(tiles * g.nrec)), dim3(256), 0, stream>>>(a.rec, Tc, g.slices, g.nrec,
+                                                                                        sums, nullptr, nullptr);
+            e = hipGetLastError();
+            if (e != hipSuccess) {
+                return e;
+            }
         }
         MixArgs mx{};
+        mx.rec = fuse ? a.rec : nullptr;
+        mx.S = g.slices;
+        mx.nrec = g.nrec;
         mx.sums = sums;
         mx.stride = kSumStride;
         mx.off_post = kFSq + 1;
@@ -1559,13 +1676,19 @@ hipError_t launch_pre_f32s(const float *res, const float *hc_fn, const float *hc
         if (e != hipSuccess) {
             return e;
         }
-        pre_mixsum_kernel<<<dim3((unsigned)(tiles * kRec)), dim3(256), 0, stream>>>(a.rec, Tc, g.slices, kRec, sums,
-                                                                                  nullptr, nullptr);
-        e = hipGetLastError();
-        if (e != hipSuccess) {
-            return e;
+        const bool fuse = Tc <= kFuseSumTokens;
+        if (!fuse) {
+            pre_mixsum_kernel<<<dim3((unsigned)(tiles * kRec)), dim3(256), 0, stream>>>(a.rec, Tc, g.slices, kRec, sums,
+                                                                                      nullptr, nullptr);
+            e = hipGetLastError();
+            if (e != hipSuccess) {
+                return e;
+            }
         }
         MixArgs mx{};
+        mx.rec = fuse ? a.rec : nullptr;
+        mx.S = g.slices;
+        mx.nrec = kRec;
         mx.sums = sums;
         mx.stride = kSumStride;
         mx.off_post = kFSq + 1;

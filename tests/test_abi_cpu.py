@@ -500,3 +500,30 @@ def test_f32_stream_post_expand_head_validation():
     assert lib.mhc_head_mean_f32(res, 8, 64, None, NULL) == mhc.MHC_ERROR_INVALID_VALUE
     assert lib.mhc_head_mean_f32(res, 8, 64, ctypes.c_void_p(2 * G + 8), NULL) == mhc.MHC_ERROR_INVALID_VALUE
     assert lib.mhc_head_mean_f32(None, 0, 64, None, NULL) == mhc.MHC_SUCCESS
+
+
+def test_pre_split_weights_validation():
+    lib = mhc.lib()
+    G = 1 << 40
+    fn, ws = ctypes.c_void_p(G), ctypes.c_void_p(2 * G)
+    need = mhc.mhc_pre_split_bytes(7168)
+    assert 0 < need <= mhc.mhc_pre_fused_workspace_bytes(32, 7168)
+    assert mhc.mhc_pre_split_bytes(0) == 0 and mhc.mhc_pre_split_bytes((1 << 21) + 1) == 0
+    assert lib.mhc_pre_split_weights(fn, 0, ws, need, NULL) == mhc.MHC_ERROR_INVALID_VALUE
+    assert lib.mhc_pre_split_weights(None, 7168, ws, need, NULL) == mhc.MHC_ERROR_INVALID_VALUE
+    assert lib.mhc_pre_split_weights(fn, 7168, ws, need - 1, NULL) == mhc.MHC_ERROR_WORKSPACE
+    assert lib.mhc_pre_split_weights(fn, 7168, None, need, NULL) == mhc.MHC_ERROR_WORKSPACE
+    assert lib.mhc_pre_split_weights(fn, 7168, ctypes.c_void_p(2 * G + 64), need, NULL) == mhc.MHC_ERROR_WORKSPACE
+    assert lib.mhc_pre_split_weights(fn, 7168, ctypes.c_void_p(G + 256), need, NULL) == mhc.MHC_ERROR_INVALID_VALUE
+
+
+@pytest.mark.parametrize("kw", [dict(T=-1), dict(H=0), dict(it=0), dict(rms=0.0), dict(res=None), dict(y=None)])
+def test_pre_fused_presplit_validation(kw):
+    a = dict(res=FAKE, fn=ctypes.c_void_p(0x4000000), sc=ctypes.c_void_p(0x8000000), base=ctypes.c_void_p(0x8001000),
+             T=16, H=256, rms=1e-6, pe=1e-6, se=1e-6, pm=1.0, it=20, y=ctypes.c_void_p(0x9000000),
+             post=ctypes.c_void_p(0xA000000), comb=ctypes.c_void_p(0xB000000), pre=None,
+             ws=ctypes.c_void_p(0xC000000), wsb=1 << 30)
+    a.update(kw)
+    assert mhc.lib().mhc_pre_fused_presplit(a["res"], a["fn"], a["sc"], a["base"], a["T"], a["H"], a["rms"], a["pe"],
+                                            a["se"], a["pm"], a["it"], a["y"], a["post"], a["comb"], a["pre"],
+                                            a["ws"], a["wsb"], NULL) == mhc.MHC_ERROR_INVALID_VALUE
