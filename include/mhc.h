@@ -104,11 +104,13 @@ mhc_status mhc_sinkhorn(const float *logits, float *out, int64_t n_mats, int32_t
 
 /*
  * Size in bytes of the device workspace mhc_pre_fused needs for (T, H): enough for
- * either form of the pre-map.  The one-read form (16-byte rows, 1024 < H <= 8192,
+ * either form of the pre-map.  The caller owns this scratch and passes it with every call,
+ * as the mix scratch of a site is caller-owned device memory next to its weights in the
+ * metrale GLM-5 mHC page (Glm5NextMhcSiteWeights); its contents on entry are ignored.  The one-read form (16-byte rows, 1024 < H <= 8192,
  * T >= 1024, on a 256-CU gfx950) keeps a ring of exchange records: 16-byte chunks of
  * partial sums for a few 16-token steps of every workgroup, at most 4.6 MB and
  * independent of T.  The two-pass form keeps the projection weights split into bf16
- * terms in MFMA operand order (384 * H bytes, rounded up), the per-slice partial sums of
+ * terms in MFMA operand order (576 * H bytes, rounded up), the per-slice partial sums of
  * the projection (100 bytes per token per 128-wide slice of H) and the per-token totals
  * (128 bytes per token); tokens beyond 2^31 bytes of partial sums are processed in
  * chunks that reuse the same space.  Returns 0 for T <= 0, H <= 0 or H beyond the
