@@ -164,6 +164,22 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
+// Sum over the 64 lanes of a wavefront on DPP moves and permlane swaps (no LDS round
+// trip): within quads (lanes xor 1, 2), half rows and rows (mirrors), then the four rows
+// ((0 + 1) and (2 + 3) by v_permlane16_swap, the halves by v_permlane32_swap).  Each add
+// meets the same two partial sums in every lane, so every lane gets the same bits.
+__device__ __forceinline__ float wave_sum_dpp(float v)
+{
+    v += dpp_quad_xor1(v);
+    v += dpp_quad_xor2(v);
+    v += dpp_perm<0x141>(v); // row_half_mirror
+    v += dpp_perm<0x140>(v); // row_mirror
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
 // Workgroup barrier over LDS only: waits for this wavefront's LDS accesses, not for
 // its global loads, which stay in flight across it.
 __device__ __forceinline__ void lds_barrier()

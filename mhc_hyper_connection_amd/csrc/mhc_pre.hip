@@ -33,6 +33,7 @@
 #include "mhc_internal.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace mhc {
 
@@ -925,7 +926,7 @@ template <int N> __device__ __forceinline__ void mix_fields(const MixArgs &m, in
     }
 #pragma unroll
     for (int k = 0; k < N; ++k) {
-        out[k] = wave_sum(v[k]);
+        out[k] = wave_sum_dpp(v[k]);
     }
 }
 
@@ -962,7 +963,13 @@ template <bool kAll> __device__ __forceinline__ void token_fields(const MixArgs 
 // pre weights of token t from its fields (wave-uniform).
 __device__ __forceinline__ void token_pre(const MixArgs &m, int t, const float (&d)[kRec], float *p, float &rstd)
 {
-    const float S = m.sq != nullptr ? m.sq[t] : d[kFSq];
+    // the supplied sum of squares through a buffer view: a plain ?: between m.sq[t] and
+    // d[kFSq] becomes one load from a select of the two addresses, which puts d in scratch
+    float S = d[kFSq];
+    if (m.sq != nullptr) {
+        S = __uint_as_float(
+            __builtin_amdgcn_raw_buffer_load_b32(buf_view_uniform(m.sq, (uint32_t)(t + 1) * 4u), t * 4, 0, 0));
+    }
     rstd = 1.0f / sqrtf(S / m.k_denom + m.rms_eps);
 #pragma unroll
     for (int i = 0; i < kHC; ++i) {
@@ -970,56 +977,71 @@ __device__ __forceinline__ void token_pre(const MixArgs &m, int t, const float (
     }
 }
 
-// post, comb (Sinkhorn) and the optional pre output of token t (one lane writes); d from
-// token_fields<true>.
-__device__ __forceinline__ void token_mix_outputs(const MixArgs &m, int t, const float (&d)[kRec], const float *p,
-                                                  float rstd, bool writer)
+// v where the lane's bit of `mask` is clear, a where it is set: one v_cndmask_b32.  Written
+// as one instruction so that a chain of them over a register array stays in registers (the
+// compiler turns a chain of ?: on lane-dependent conditions over an array into an indexed
+// load from scratch memory).
+__device__ __forceinline__ float lane_select(uint64_t mask, float a, float v)
 {
-    if (m.head) {
-        if (writer && m.pre_out) {
+    float r;
+    asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(v), "v"(a), "s"(mask));
+    return r;
+}
+constexpr uint64_t kLane16Mask = 0x0001000100010001ull; // lanes 0, 16, 32, 48
+constexpr uint64_t kLane4Mask = 0x1111111111111111ull;  // lanes 0, 4, 8, ..., 60
+
+// post, comb (Sinkhorn) and the optional pre output of token t; d from token_fields<true>.
+// Called by a whole wave (all 64 lanes active: the Sinkhorn runs on DPP within 16-lane
+// rows, lane e of each row holding entry (e / 4, e % 4); the four rows compute the same
+// matrix).  Lanes 0..15 store comb, lanes 0..3 post and the pre output.
+__device__ __forceinline__ void token_mix_outputs(const MixArgs &m, int t, const float (&d)[kRec], const float *p,
+                                                  float rstd, int lane)
+{
+    const int e = lane & (kHC * kHC - 1);
+    const int i = e & (kHC - 1);
+    float pe = p[0];
 #pragma unroll
-            for (int i = 0; i < kHC; ++i) {
-                m.pre_out[(size_t)t * kHC + i] = p[i];
-            }
+    for (int k = 1; k < kHC; ++k) {
+        pe = lane_select(kLane4Mask << k, p[k], pe);
+    }
+    if (m.head) {
+        if (m.pre_out && lane < kHC) {
+            m.pre_out[(size_t)t * kHC + lane] = pe;
         }
         return;
     }
-    float post[kHC];
+    // this lane's comb logit (entry e) and post dot (entry e mod 4), from the wave-uniform fields
+    float zc = d[2 * kHC + 1];
 #pragma unroll
-    for (int i = 0; i < kHC; ++i) {
-        post[i] = sigmoidf_fast(fmaf(d[kHC + 1 + i] * rstd, m.hc_scale[1], m.hc_base[kHC + i])) * m.post_mult;
+    for (int k = 1; k < kHC * kHC; ++k) {
+        zc = lane_select(kLane16Mask << k, d[2 * kHC + 1 + k], zc);
     }
-    float P16[kHC * kHC];
+    float zp = d[kHC + 1];
 #pragma unroll
-    for (int e = 0; e < kHC * kHC; ++e) {
-        P16[e] = fmaf(d[2 * kHC + 1 + e] * rstd, m.hc_scale[2], m.hc_base[2 * kHC + e]);
+    for (int k = 1; k < kHC; ++k) {
+        zp = lane_select(kLane4Mask << k, d[kHC + 1 + k], zp);
     }
-    sinkhorn4x4(P16, m.iters, m.sk_eps);
-    if (writer) {
-#pragma unroll
-        for (int i = 0; i < kHC; ++i) {
-            m.post[(size_t)t * kHC + i] = post[i];
-            if (m.pre_out) {
-                m.pre_out[(size_t)t * kHC + i] = p[i];
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < kHC * kHC; ++e) {
-            m.comb[(size_t)t * kHC * kHC + e] = P16[e];
+    const float post = sigmoidf_fast(fmaf(zp * rstd, m.hc_scale[1], m.hc_base[kHC + i])) * m.post_mult;
+    const float P = sinkhorn_row16(fmaf(zc * rstd, m.hc_scale[2], m.hc_base[2 * kHC + e]), m.iters, m.sk_eps);
+    if (lane < kHC * kHC) {
+        m.comb[(size_t)t * kHC * kHC + lane] = P;
+    }
+    if (lane < kHC) {
+        m.post[(size_t)t * kHC + lane] = post;
+        if (m.pre_out) {
+            m.pre_out[(size_t)t * kHC + lane] = pe;
         }
     }
 }
 
-// A collapse wave's token work: its fields (tile 0 also post and comb, unless the head),
-// then the pre weights; tile 0 then finishes post, comb and the pre output after the collapse.
-__device__ __forceinline__ void token_start(const MixArgs &m, int t, bool first, float (&d)[kRec], float *p,
-                                            float &rstd)
+// A collapse wave's token work: its fields (the first tile's wave all 25, for post and
+// comb; the others the pre dots and the sum of squares), then the pre weights.  The two
+// kinds of wave are compiled as separate paths (kFirst a template argument), so the field
+// array never merges across a branch (such a merge put it in scratch memory).
+template <bool kFirst>
+__device__ __forceinline__ void token_start(const MixArgs &m, int t, float (&d)[kRec], float *p, float &rstd)
 {
-    if (first && !m.head) {
-        token_fields<true>(m, t, d);
-    } else {
-        token_fields<false>(m, t, d);
-    }
+    token_fields<kFirst>(m, t, d);
     token_pre(m, t, d, p, rstd);
 }
 
@@ -1043,25 +1065,33 @@ __global__ __launch_bounds__(kColBlock) void pre_collapse_vec8_kernel(const uint
     for (int i = 0; i < kHC; ++i) {
         rw[i] = load_nt16(res + row + (size_t)i * H);
     }
-    float d[kRec], p[kHC], rstd;
-    token_start(mx, t, tile == 0, d, p, rstd);
-    if (hin) {
-    u32x4 yw;
+    auto finish = [&](auto first) {
+        constexpr bool kFirst = decltype(first)::value;
+        float d[kRec], p[kHC], rstd;
+        token_start<kFirst>(mx, t, d, p, rstd);
+        if (hin) {
+            u32x4 yw;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        float lo = bf16_lo(rw[0][q]) * p[0];
-        float hi = bf16_hi(rw[0][q]) * p[0];
+            for (int q = 0; q < 4; ++q) {
+                float lo = bf16_lo(rw[0][q]) * p[0];
+                float hi = bf16_hi(rw[0][q]) * p[0];
 #pragma unroll
-        for (int i = 1; i < kHC; ++i) {
-            lo = fmaf(bf16_lo(rw[i][q]), p[i], lo);
-            hi = fmaf(bf16_hi(rw[i][q]), p[i], hi);
+                for (int i = 1; i < kHC; ++i) {
+                    lo = fmaf(bf16_lo(rw[i][q]), p[i], lo);
+                    hi = fmaf(bf16_hi(rw[i][q]), p[i], hi);
+                }
+                yw[q] = pack_bf16x2(lo, hi);
+            }
+            store_nt16(y + (size_t)t * H + h, yw);
         }
-        yw[q] = pack_bf16x2(lo, hi);
-    }
-    store_nt16(y + (size_t)t * H + h, yw);
-    }
+        if constexpr (kFirst) {
+            token_mix_outputs(mx, t, d, p, rstd, lane);
+        }
+    };
     if (tile == 0) {
-        token_mix_outputs(mx, t, d, p, rstd, lane == 0);
+        finish(std::true_type{});
+    } else {
+        finish(std::false_type{});
     }
 }
 
@@ -1085,18 +1115,26 @@ __global__ __launch_bounds__(kColBlock) void pre_collapse_scalar_kernel(const ui
     for (int i = 0; i < kHC; ++i) {
         r[i] = bf16_to_f32(res[row + (size_t)i * H]);
     }
-    float d[kRec], p[kHC], rstd;
-    token_start(mx, t, tile == 0, d, p, rstd);
-    if (hin) {
-        float a = r[0] * p[0];
+    auto finish = [&](auto first) {
+        constexpr bool kFirst = decltype(first)::value;
+        float d[kRec], p[kHC], rstd;
+        token_start<kFirst>(mx, t, d, p, rstd);
+        if (hin) {
+            float a = r[0] * p[0];
 #pragma unroll
-        for (int i = 1; i < kHC; ++i) {
-            a = fmaf(r[i], p[i], a);
+            for (int i = 1; i < kHC; ++i) {
+                a = fmaf(r[i], p[i], a);
+            }
+            y[(size_t)t * H + h] = f32_to_bf16(a);
         }
-        y[(size_t)t * H + h] = f32_to_bf16(a);
-    }
+        if constexpr (kFirst) {
+            token_mix_outputs(mx, t, d, p, rstd, lane);
+        }
+    };
     if (tile == 0) {
-        token_mix_outputs(mx, t, d, p, rstd, lane == 0);
+        finish(std::true_type{});
+    } else {
+        finish(std::false_type{});
     }
 }
 
@@ -1303,27 +1341,36 @@ __global__ __launch_bounds__(kColBlock) void pre_collapse_f32s_kernel(const floa
             r[i][0] = res[row + (size_t)i * H];
         }
     }
-    float d[kRec], p[kHC], rstd;
-    token_start(mx, t, tile == 0, d, p, rstd);
-    if (hin) {
-        float o[kE];
+    auto finish = [&](auto first) {
+        constexpr bool kFirst = decltype(first)::value;
+        float d[kRec], p[kHC], rstd;
+        token_start<kFirst>(mx, t, d, p, rstd);
+        if (hin) {
+            float o[kE];
 #pragma unroll
-        for (int j = 0; j < kE; ++j) {
-            float s = r[0][j] * p[0];
+            for (int j = 0; j < kE; ++j) {
+                float s = r[0][j] * p[0];
 #pragma unroll
-            for (int i = 1; i < kHC; ++i) {
-                s = fmaf(r[i][j], p[i], s);
+                for (int i = 1; i < kHC; ++i) {
+                    s = fmaf(r[i][j], p[i], s);
+                }
+                o[j] = s;
             }
-            o[j] = s;
+            if constexpr (kVec) {
+                *reinterpret_cast<uint2 *>(y + (size_t)t * H + h) =
+                    uint2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+            } else {
+                y[(size_t)t * H + h] = f32_to_bf16(o[0]);
+            }
         }
-        if constexpr (kVec) {
-            *reinterpret_cast<uint2 *>(y + (size_t)t * H + h) = uint2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-        } else {
-            y[(size_t)t * H + h] = f32_to_bf16(o[0]);
+        if constexpr (kFirst) {
+            token_mix_outputs(mx, t, d, p, rstd, lane);
         }
-    }
+    };
     if (tile == 0) {
-        token_mix_outputs(mx, t, d, p, rstd, lane == 0);
+        finish(std::true_type{});
+    } else {
+        finish(std::false_type{});
     }
 }
 

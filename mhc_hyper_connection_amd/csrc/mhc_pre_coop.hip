@@ -23,7 +23,9 @@
 //    slices (device-scope loads: they miss the CU's L1), sums them over the slices in a
 //    fixed order, forms rstd and the pre weights, and collapses its slice of the step
 //    from the LDS ring: the streams are read from HBM once.  A chunk whose tag does not
-//    match has not landed yet and is loaded again (bounded).
+//    match has not landed yet and is loaded again, up to 2^14 times; a step whose records
+//    are still missing then (its writer was never made resident, e.g. behind a long kernel
+//    on another stream) gets NaN outputs rather than stale ones.
 //  * Each token's post weights and Sinkhorn are finished by one workgroup: workgroup s
 //    takes token s mod 16 of the steps whose parity is s / 16.
 //
@@ -450,6 +452,17 @@ __global__ __launch_bounds__(W * 64) void pre_coop_kernel(CoopArgs a)
                 if (!*bf) {
                     break;
                 }
+            }
+            // still missing after the bounded reloads (a workgroup of the group was not
+            // resident in time): the step's sums become NaN, so its outputs are NaN, never
+            // values from a stale record
+            if (*bf) {
+                if (tid < 96) {
+                    sums[tid] = __builtin_nanf("");
+                } else if (tid < 128) {
+                    dsum[tid - 96] = __builtin_nanf("");
+                }
+                __syncthreads();
             }
         }
 
