@@ -60,7 +60,7 @@ def parse():
     ap.add_argument("--only", default="all",
                     choices=["all", "pre", "post", "sinkhorn", "pre_dots", "post_bwd", "sinkhorn_bwd", "pre_dots_bwd",
                              "pre_bf16", "expand", "head", "head_mean", "pre_bwd", "post_project", "fused",
-                             "f32", "pre_f32", "post_f32", "expand_f32", "head_mean_f32"],
+                             "post_pre", "f32", "pre_f32", "post_f32", "expand_f32", "head_mean_f32"],
                     help="run only one call in the timed loop (for profiling)")
     ap.add_argument("--presplit", action="store_true",
                     help="split the fixed weights once before timing and time mhc_pre_fused_presplit (a decode "
@@ -273,6 +273,24 @@ def main():
         mhc.mhc_post_project(x, streams, post, comb, hc_fn, out=streams, dot_mix=pp_dm, sqrsum=pp_sq,
                              workspace=pp_ws)
 
+    if args.only == "post_pre" or steady_state:
+        # the steady-state sublayer step in one call: the post-map and the next pre-map
+        # (the next weights are hc_fn again), the streams updated in place; the mixes
+        # alternate between two buffers, each call reading the previous call's
+        pp2_ws = torch.empty(mhc.mhc_pre_fused_workspace_bytes(T, H), dtype=torch.uint8, device=dev)
+        pp2_streams = res.clone()
+        pp2_y = torch.empty_like(y)
+        call_pre()  # mixes for the first post-map (untimed)
+        pp2_mix = [(post.clone(), comb.clone()), (torch.empty_like(post), torch.empty_like(comb))]
+        pp2_turn = [0]
+
+    def call_post_pre():
+        (pa, ca), (pb, cb) = pp2_mix[pp2_turn[0]], pp2_mix[1 - pp2_turn[0]]
+        mhc.mhc_post_pre_fused(x, pp2_streams, pa, ca, hc_fn, hc_scale, hc_base, p["rms_eps"], p["pre_eps"],
+                               p["sinkhorn_eps"], p["post_mult"], p["num_iters"], out=pp2_streams, y=pp2_y,
+                               post_next=pb, comb_next=cb, workspace=pp2_ws)
+        pp2_turn[0] = 1 - pp2_turn[0]
+
     def step():
         if args.only in ("all", "pre"):
             call_pre()
@@ -302,6 +320,8 @@ def main():
             call_post_project()
         if args.only == "fused":
             call_fused()
+        if args.only == "post_pre":
+            call_post_pre()
         if args.only in ("f32", "pre_f32"):
             call_pre_f32()
         if args.only in ("f32", "post_f32"):
@@ -397,7 +417,7 @@ def main():
         breakdown["post_bwd_ms"] = ms_step
     if args.only == "pre_dots_bwd":
         breakdown["pre_dots_bwd_ms"] = ms_step
-    for mode in ("pre_bf16", "expand", "head", "head_mean", "pre_bwd", "post_project", "fused", "expand_f32",
+    for mode in ("pre_bf16", "expand", "head", "head_mean", "pre_bwd", "post_project", "fused", "post_pre", "expand_f32",
                  "head_mean_f32"):
         if args.only == mode:
             breakdown[mode + "_ms"] = ms_step
@@ -423,6 +443,14 @@ def main():
                   "ms_per_step": round(ms_f, 5), "tokens_per_s": round(T / (ms_f * 1e-3), 1),
                   "effective_GBps": round(eff_f, 1), "hbm_frac": round(eff_f / HBM_PEAK_GBPS, 4),
                   "algorithmic_bytes": step_bytes}
+        # the same step as one call: the post-map and the next pre-map fused
+        for _ in range(max(args.warmup, 1)):
+            call_post_pre()
+        ms_o = timed_reps(call_post_pre, max(args.steps, 1))
+        eff_o = step_bytes / (ms_o * 1e-3) / 1e9
+        steady["one_call"] = {"calls": "mhc_post_pre_fused (in place)", "ms_per_step": round(ms_o, 5),
+                              "tokens_per_s": round(T / (ms_o * 1e-3), 1), "effective_GBps": round(eff_o, 1),
+                              "hbm_frac": round(eff_o / HBM_PEAK_GBPS, 4), "algorithmic_bytes": step_bytes}
 
     # Per-call rooflines.  mhc_post and mhc_sinkhorn are one kernel launch each;
     # mhc_pre_fused is one in its one-read form (16-byte rows, T >= 1024, 1024 < H <= 8192
@@ -476,6 +504,10 @@ def main():
         calls["mhc_expand_f32"] = ("expand_f32s_kernel", breakdown["expand_f32_ms"], step_bytes)
     if "head_mean_f32_ms" in breakdown:
         calls["mhc_head_mean_f32"] = ("head_mean_f32s_kernel", breakdown["head_mean_f32_ms"], step_bytes)
+    if "post_pre_ms" in breakdown:
+        post_k = "post_vec8_kernel" if H % 8 == 0 else "post_scalar_kernel"
+        calls["mhc_post_pre_fused"] = ("pre_coop_kernel" if one_read else post_k + "+" + split_kernels,
+                                       breakdown["post_pre_ms"], step_bytes)
     if "fused_ms" in breakdown:
         calls["mhc_pre_from_dots+mhc_post_project"] = (
             "pre_collapse_vec8_kernel+pre_prep_kernel+post_proj_stream_kernel+pre_mixsum_kernel", breakdown["fused_ms"],
@@ -510,7 +542,8 @@ def main():
     # launched the same way), and what a plain elementwise copy sustains here.
     npre = 1 if pre_one_read(T, H) else 2 + (0 if args.presplit else 1) + (0 if T <= 64 else 1)
     npre32 = 2 + (0 if T <= 64 else 1)
-    nker = {"all": npre + 1, "pre": npre, "post": 1, "post_project": 3, "fused": 4, "f32": npre32 + 1,
+    nker = {"all": npre + 1, "pre": npre, "post": 1, "post_project": 3, "fused": 4,
+            "post_pre": 1 if pre_one_read(T, H) else 1 + npre + (1 if args.presplit else 0), "f32": npre32 + 1,
             "pre_f32": npre32, "post_f32": 1}.get(args.only)
     launch_floor_ms = None
     if nker:
@@ -612,6 +645,7 @@ def step_algorithmic_bytes(only: str, T: int, H: int, sk_logits) -> int:
                             algorithmic_bytes_sinkhorn_backward, algorithmic_bytes_post_project)
     per_mode = {
         "post_project": lambda: algorithmic_bytes_post_project(T, H),
+        "post_pre": lambda: algorithmic_bytes_pre(T, H) + algorithmic_bytes_post(T, H),
         "fused": lambda: algorithmic_bytes_pre_dots(T, H, splits=1, sqrsum=True) + algorithmic_bytes_post_project(T, H),
         "sinkhorn": lambda: algorithmic_bytes_sinkhorn(sk_logits.shape[0]),
         "sinkhorn_bwd": lambda: algorithmic_bytes_sinkhorn_backward(sk_logits.shape[0]),

@@ -381,6 +381,36 @@ mhc_status mhc_post_project(const uint16_t *x, const uint16_t *res, const float 
                             float *sqrsum, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * mhc_post_pre_fused -- the post-map of one sublayer and the whole pre-map of the next in
+ * one call (FlashInfer mHC article: section 1 for the two stages around each layer,
+ * section 2.1 for the post-map, sections 3.4 and 5.2 for the pre-map; metrale dispatch
+ * page: hc_post_site and hc_pre_site).  It computes
+ *     out[t][n][h] = bf16( x[t][h] post[t][n] + sum_o res[t][o][h] comb[t][o][n] )
+ * bit for bit as mhc_post does, and then, over the bf16 `out`, everything mhc_pre_fused
+ * computes with the next weights (hc_fn, hc_scale, hc_base):
+ *     y, post_next, comb_next and optionally pre_next.
+ * With 16-byte rows (H % 8 == 0; x, res, out and y 16-byte aligned), T >= 1024 and
+ * 1024 < H <= 8192 on a 256-CU gfx950 this is one pass: the new streams are written to
+ * `out` and kept on chip for the pre-map, so the streams are read once and written once
+ * (x, res in; out, y out).  Otherwise it runs mhc_post then mhc_pre_fused on `out`.
+ *
+ *   x [T,H] bf16; res [T,4,H] bf16; post [T,4], comb [T,4,4] fp32   the post-map's inputs
+ *   hc_fn [24,4H], hc_scale [3], hc_base [24] fp32                     the next pre-map's weights
+ *   T, H, rms_eps, pre_eps, sinkhorn_eps, post_mult, num_iters         as for mhc_pre_fused
+ *   out [T,4,H] bf16       output; may equal `res` exactly (in place)
+ *   y [T,H] bf16, post_next [T,4], comb_next [T,4,4] fp32, pre_next [T,4] fp32 or NULL
+ *   workspace   at least mhc_pre_fused_workspace_bytes(T, H) bytes, 256-byte aligned
+ * No output may overlap an input, the workspace or another output, except out == res;
+ * in particular post_next and comb_next must not overlap post and comb.  Errors as for
+ * mhc_pre_fused and mhc_post; T == 0 is a no-op.
+ */
+mhc_status mhc_post_pre_fused(const uint16_t *x, const uint16_t *res, const float *post, const float *comb,
+                              const float *hc_fn, const float *hc_scale, const float *hc_base, int64_t T, int64_t H,
+                              float rms_eps, float pre_eps, float sinkhorn_eps, float post_mult, int32_t num_iters,
+                              uint16_t *out, uint16_t *y, float *post_next, float *comb_next, float *pre_next,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * mhc_sinkhorn_backward -- gradient of mhc_sinkhorn with respect to its logits,
  * through the fixed count of iterations (not the limit of the iteration):
  *     d_logits = J(logits)^T grad,   J the Jacobian of the map computed by mhc_sinkhorn

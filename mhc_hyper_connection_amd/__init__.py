@@ -103,6 +103,8 @@ def lib() -> ctypes.CDLL:
     L.mhc_post_project_workspace_bytes.restype = SZ
     L.mhc_post_project.argtypes = [P, P, P, P, P, I64, I64, P, P, P, P, SZ, P]
     L.mhc_post_project.restype = ctypes.c_int
+    L.mhc_post_pre_fused.argtypes = [P, P, P, P, P, P, P, I64, I64, F, F, F, F, I32, P, P, P, P, P, P, SZ, P]
+    L.mhc_post_pre_fused.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -479,6 +481,77 @@ def mhc_post_project(x: torch.Tensor, res: torch.Tensor, post: torch.Tensor, com
     return out, dot_mix, sqrsum
 
 
+def mhc_post_pre_fused(x: torch.Tensor, res: torch.Tensor, post: torch.Tensor, comb: torch.Tensor,
+                       hc_fn: torch.Tensor, hc_scale: torch.Tensor, hc_base: torch.Tensor, rms_eps: float = 1e-6,
+                       pre_eps: float = 1e-6, sinkhorn_eps: float = 1e-6, post_mult: float = 1.0,
+                       num_iters: int = 20, *, out: torch.Tensor | None = None, y=None, post_next=None,
+                       comb_next=None, pre_next=None, return_pre: bool = False,
+                       workspace: torch.Tensor | None = None):
+    """The post-map of one sublayer and the next sublayer's pre-map in one call: out as
+    :func:`mhc_post` writes it (``out`` may be ``res``), then what :func:`mhc_pre_fused`
+    computes over ``out`` with the next weights.  Returns (out, y, post_next, comb_next
+    [, pre_next])."""
+    _need(res, "res", torch.bfloat16)
+    if res.dim() < 2 or res.shape[-2] != HC:
+        raise ValueError(f"res must be [..., 4, H], got {tuple(res.shape)}")
+    H = res.shape[-1]
+    outer = tuple(res.shape[:-2])
+    T = res.numel() // (HC * H) if H > 0 else 0
+    _need(x, "x", torch.bfloat16)
+    if tuple(x.shape) != outer + (H,):
+        raise ValueError(f"x must be {outer + (H,)}, got {tuple(x.shape)}")
+    _need(post, "post", torch.float32)
+    if tuple(post.shape) not in (outer + (HC,), outer + (HC, 1)):
+        raise ValueError(f"post must be {outer + (HC,)} or {outer + (HC, 1)}, got {tuple(post.shape)}")
+    _need(comb, "comb", torch.float32)
+    if tuple(comb.shape) != outer + (HC, HC):
+        raise ValueError(f"comb must be {outer + (HC, HC)}, got {tuple(comb.shape)}")
+    _need(hc_fn, "hc_fn", torch.float32)
+    if tuple(hc_fn.shape) != (MIX, HC * H):
+        raise ValueError(f"hc_fn must be [24, 4H] = [24, {HC * H}], got {tuple(hc_fn.shape)}")
+    _need(hc_scale, "hc_scale", torch.float32)
+    if tuple(hc_scale.shape) != (3,):
+        raise ValueError("hc_scale must be [3] (pre, post, comb)")
+    _need(hc_base, "hc_base", torch.float32)
+    if tuple(hc_base.shape) != (MIX,):
+        raise ValueError("hc_base must be [24]")
+    dev = res.device
+    if out is None:
+        out = torch.empty_like(res)
+    _need(out, "out", torch.bfloat16)
+    if out.shape != res.shape:
+        raise ValueError("out must have the shape of res")
+    if y is None:
+        y = torch.empty(outer + (H,), dtype=torch.bfloat16, device=dev)
+    if post_next is None:
+        post_next = torch.empty(outer + (HC,), dtype=torch.float32, device=dev)
+    if comb_next is None:
+        comb_next = torch.empty(outer + (HC, HC), dtype=torch.float32, device=dev)
+    if pre_next is None and return_pre:
+        pre_next = torch.empty(outer + (HC,), dtype=torch.float32, device=dev)
+    _need(y, "y", torch.bfloat16)
+    _need(post_next, "post_next", torch.float32)
+    _need(comb_next, "comb_next", torch.float32)
+    if y.numel() != T * H or post_next.numel() != T * HC or comb_next.numel() != T * HC * HC:
+        raise ValueError("output sizes do not match res")
+    if pre_next is not None:
+        _need(pre_next, "pre_next", torch.float32)
+        if pre_next.numel() != T * HC:
+            raise ValueError("pre_next must hold [T, 4] values")
+    need = mhc_pre_fused_workspace_bytes(T, H)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8)
+    _same_device(x, res, post, comb, hc_fn, hc_scale, hc_base, out, y, post_next, comb_next, pre_next, workspace)
+    _check("mhc_post_pre_fused", lib().mhc_post_pre_fused(
+        _ptr(x), _ptr(res), _ptr(post), _ptr(comb), _ptr(hc_fn), _ptr(hc_scale), _ptr(hc_base), T, H,
+        float(rms_eps), float(pre_eps), float(sinkhorn_eps), float(post_mult), int(num_iters), _ptr(out), _ptr(y),
+        _ptr(post_next), _ptr(comb_next), _ptr(pre_next), _ptr(workspace), workspace.numel(), _stream(dev)))
+    if return_pre:
+        return out, y, post_next, comb_next, pre_next
+    return out, y, post_next, comb_next
+
+
 SINKHORN_BWD_MAX_ITERS = 255
 
 
@@ -794,6 +867,6 @@ __all__ = ["mhc_sinkhorn", "mhc_pre_fused", "mhc_pre_fused_noalloc", "mhc_pre_fu
            "mhc_pre_fused_workspace_bytes", "mhc_pre_from_dots", "mhc_post",
            "mhc_sinkhorn_backward", "mhc_post_backward", "mhc_pre_from_dots_backward",
            "mhc_pre_backward_workspace_bytes", "mhc_pre_fused_backward", "mhc_pre_fused_backward_workspace_bytes",
-           "mhc_post_project", "mhc_post_project_workspace_bytes",
+           "mhc_post_project", "mhc_post_project_workspace_bytes", "mhc_post_pre_fused",
            "lib", "abi_version", "status_string", "launch_plan", "MHCError", "HC",
            "MIX", "SINKHORN_BWD_MAX_ITERS", "MHC_PRE_FUSED_NOALLOC_MAX_BYTES"]

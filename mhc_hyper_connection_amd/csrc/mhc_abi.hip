@@ -563,6 +563,63 @@ mhc_status mhc_post_project(const uint16_t *x, const uint16_t *res, const float 
                                                   workspace, (hipStream_t)stream));
 }
 
+mhc_status mhc_post_pre_fused(const uint16_t *x, const uint16_t *res, const float *post, const float *comb,
+                              const float *hc_fn, const float *hc_scale, const float *hc_base, int64_t T, int64_t H,
+                              float rms_eps, float pre_eps, float sinkhorn_eps, float post_mult, int32_t num_iters,
+                              uint16_t *out, uint16_t *y, float *post_next, float *comb_next, float *pre_next,
+                              void *workspace, size_t workspace_bytes, void *stream)
+{
+    // the next pre-map over `out`: its parameters, pointers and output overlaps (pre_common
+    // with res = out, nothing launched)
+    const mhc_status v = pre_common(out, hc_fn, false, kMixRows, hc_scale, 3, hc_base, T, H, rms_eps, pre_eps,
+                                    sinkhorn_eps, post_mult, num_iters, false, y, post_next, comb_next, pre_next,
+                                    workspace, workspace_bytes, stream, true);
+    if (v != MHC_SUCCESS || T == 0) {
+        return v;
+    }
+    if (!x || !res || !post || !comb) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    const bool vec8_pre = pre_vec8(out, y, H);
+    const size_t need = mhc::pre_path_workspace_bytes(T, H, vec8_pre);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0) {
+        return MHC_ERROR_WORKSPACE;
+    }
+    // the post-map's inputs against every output (out may equal res exactly)
+    const size_t res_b = (size_t)T * 4 * H * 2, x_b = (size_t)T * H * 2, y_b = (size_t)T * H * 2;
+    const size_t fn_b = (size_t)kMixRows * 4 * H * 4;
+    const void *outs[6] = {out, y, post_next, comb_next, pre_next, workspace};
+    const size_t outn[6] = {res_b, y_b, (size_t)T * 16, (size_t)T * 64, pre_next ? (size_t)T * 16 : 0, need};
+    const void *ins[4] = {res, x, post, comb};
+    const size_t inn[4] = {res_b, x_b, (size_t)T * 16, (size_t)T * 64};
+    for (int o = 0; o < 6; ++o) {
+        for (int i = 0; i < 4; ++i) {
+            const bool in_place = o == 0 && i == 0 && (const void *)out == (const void *)res;
+            if (!in_place && overlaps(outs[o], outn[o], ins[i], inn[i])) {
+                return MHC_ERROR_INVALID_VALUE;
+            }
+        }
+    }
+    if (overlaps(out, res_b, hc_fn, fn_b) || overlaps(out, res_b, hc_scale, 12) || overlaps(out, res_b, hc_base, 96)) {
+        return MHC_ERROR_INVALID_VALUE;
+    }
+    hipStream_t st = (hipStream_t)stream;
+    const bool vec8_post = (H % 8 == 0) && aligned16(x) && aligned16(res) && aligned16(out);
+    if (vec8_post && vec8_pre && mhc::pre_coop_usable(T, H, true)) {
+        return launch_status(mhc::launch_post_pre_coop(x, res, post, comb, hc_fn, hc_scale, hc_base, T, H, rms_eps,
+                                                       pre_eps, sinkhorn_eps, post_mult, num_iters, out, y, post_next,
+                                                       comb_next, pre_next, workspace, st));
+    }
+    // other shapes: the post-map, then the pre-map over the streams it wrote
+    hipError_t e = mhc::launch_post(x, res, post, comb, T, H, out, st, vec8_post);
+    if (e != hipSuccess) {
+        return MHC_ERROR_LAUNCH;
+    }
+    return launch_status(mhc::launch_pre(out, hc_fn, false, kMixRows, hc_scale, hc_base, mhc::pre_geometry(T, H),
+                                         rms_eps, pre_eps, sinkhorn_eps, post_mult, num_iters, false, y, post_next,
+                                         comb_next, pre_next, workspace, st, vec8_pre));
+}
+
 mhc_status mhc_sinkhorn_backward(const float *grad, const float *logits, int64_t n_mats, int32_t num_iters,
                                  float eps, float *d_logits, void *stream)
 {

@@ -70,7 +70,14 @@ struct CoopArgs {
     float *post, *comb, *pre;
     u32x4 *rec;
     uint32_t rec_bytes;
+    // the post-map in front (kPost): the sublayer output x [T][H], the previous mixes
+    // post_in [T][4] and comb_in [T][4][4]; the new streams go to out [T][4][H] and are
+    // the streams the pre-map reads
+    const uint16_t *x;
+    const float *post_in, *comb_in;
+    uint16_t *out;
 };
+constexpr int kCoefVals = kQTok * (kHC + kHC * kHC); // post and comb of one step: 320 floats
 
 __device__ __forceinline__ uint32_t coop_key()
 {
@@ -122,7 +129,7 @@ __device__ __forceinline__ float rows_sum(float v)
     return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
-template <int W, typename WT>
+template <int W, typename WT, bool kPost>
 __global__ __launch_bounds__(W * 64) void pre_coop_kernel(CoopArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -135,6 +142,7 @@ __global__ __launch_bounds__(W * 64) void pre_coop_kernel(CoopArgs a)
     constexpr int kUR = (kQUrgChunks + kHW - 1) / kHW;
     constexpr int kDR = (kQDefChunks + kHW - 1) / kHW;
     constexpr int kRS = (kQChunks + kTh - 1) / kTh;
+    constexpr int kCf = (kCoefVals + kTh - 1) / kTh; // coefficient values per thread (kPost)
 
     const int R = a.R, RR = a.RR, L = a.L;
     // the wave that computes the pre weights and this workgroup's token: wave 3 sits alone on
@@ -147,6 +155,7 @@ __global__ __launch_bounds__(W * 64) void pre_coop_kernel(CoopArgs a)
     float *prel = dsum + 32;                                   // [16][4]
     int *badf = reinterpret_cast<int *>(prel + 64);
     float *dummy = prel + 64 + 4; // [64]: writes of lanes with nothing to write (no divergent branches)
+    float *coefb = dummy + 64;    // [2][320] (kPost): post [16][4] then comb [16][16] of a step, by parity
 
     const int tid = threadIdx.x;
     const int w = uniform(tid >> 6);
@@ -206,7 +215,9 @@ __global__ __launch_bounds__(W * 64) void pre_coop_kernel(CoopArgs a)
 
     // ---- geometry of this thread's loads and of the record chunks
     const int piece = tid % kPieces;
-    const int prow = tid / kPieces; // 0..15: rows prow + 16k of a step (row = token * 4 + stream)
+    // 0..15: this thread's rows of a step (row = token * 4 + stream) are prow + 16k, or with
+    // the post-map in front the 4 streams 4 prow + k of token prow
+    const int prow = tid / kPieces;
     const int hq = s * (32 * W) + piece * 8;
     const uint32_t colq = hq < H ? (uint32_t)hq * 2u : kOob;
     const __amdgpu_buffer_rsrc_t vrec = buf_view_uniform(a.rec, a.rec_bytes);
@@ -228,9 +239,43 @@ __global__ __launch_bounds__(W * 64) void pre_coop_kernel(CoopArgs a)
                                                           (uint32_t)((size_t)ntok * kHC * H * sizeof(uint16_t)));
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const int row = prow + 16 * k;
+            const int row = kPost ? 4 * prow + k : prow + 16 * k;
             d[k] = __builtin_bit_cast(u32x4,
                                       __builtin_amdgcn_raw_buffer_load_b128(v, (int)((uint32_t)(row * H) * 2u + colq), 0, 0));
+        }
+    };
+    // kPost: the x row of token prow (this thread's piece) of step j
+    auto load_x = [&](int j) -> u32x4 {
+        const int t0 = (j * kQGroups + x) * kQTok;
+        const int ntok = (kPost && j >= 0 && j < nst) ? min(kQTok, T - t0) : 0;
+        const __amdgpu_buffer_rsrc_t v = buf_view_uniform(a.x + (size_t)(ntok > 0 ? t0 : 0) * H,
+                                                          (uint32_t)((size_t)ntok * H * sizeof(uint16_t)));
+        return __builtin_bit_cast(u32x4,
+                                  __builtin_amdgcn_raw_buffer_load_b128(v, (int)((uint32_t)(prow * H) * 2u + colq), 0, 0));
+    };
+    // kPost: the post and comb values of step j this thread stages: value tid + k kTh of the
+    // step's 320 (post [16][4] at 0..63, from wave 0; comb [16][16] at 64..319)
+    auto load_coef = [&](int j, float(&cf)[kCf]) {
+        const int t0 = (j * kQGroups + x) * kQTok;
+        const int ntok = (kPost && j >= 0 && j < nst) ? min(kQTok, T - t0) : 0;
+        const __amdgpu_buffer_rsrc_t vp =
+            buf_view_uniform(a.post_in + (size_t)(ntok > 0 ? t0 : 0) * kHC, (uint32_t)(ntok * kHC * 4));
+        const __amdgpu_buffer_rsrc_t vc =
+            buf_view_uniform(a.comb_in + (size_t)(ntok > 0 ? t0 : 0) * kHC * kHC, (uint32_t)(ntok * kHC * kHC * 4));
+#pragma unroll
+        for (int k = 0; k < kCf; ++k) {
+            const int v = tid + k * kTh;
+            const bool from_post = k == 0 && w == 0; // wave-uniform
+            const uint32_t o = from_post ? (uint32_t)v * 4u : (v < kCoefVals ? (uint32_t)(v - 4 * kQTok) * 4u : kOob);
+            cf[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(from_post ? vp : vc, (int)o, 0, 0));
+        }
+    };
+    auto store_coef = [&](int j, const float(&cf)[kCf]) {
+        float *cb = coefb + (j & 1) * kCoefVals;
+#pragma unroll
+        for (int k = 0; k < kCf; ++k) {
+            const int v = tid + k * kTh;
+            *(v < kCoefVals ? cb + v : dummy + lane) = cf[k];
         }
     };
     // the records of step j this thread reads: chunk k of slice sl for its half-wave's k
@@ -340,8 +385,8 @@ __global__ __launch_bounds__(W * 64) void pre_coop_kernel(CoopArgs a)
     // One iteration: sum the records of step cu = i - L; write step i to its slot; projection
     // of step i and collapse of step cu - 1 (from registers, so that its arithmetic overlaps
     // the products); the record of step i; step cu's slot and pre weights into registers.
-    auto iteration = [&](int i, int ri, int qi, u32x4(&cur)[4], u32x4(&ru)[kUR], u32x4(&rd)[kDR],
-                         u32x4(&hold)[kHC], float(&holdp)[kHC]) {
+    auto iteration = [&](int i, int ri, int qi, u32x4(&cur)[4], u32x4 &xcur, float(&cf)[kCf], u32x4(&ru)[kUR],
+                         u32x4(&rd)[kDR], u32x4(&hold)[kHC], float(&holdp)[kHC]) {
         const int cu = i - L;
         const int cc = cu - 1;                    // collapsed this iteration
         const int rcs = wrap(ri + 2, R);          // slot of step cu: i - L = i + 2 (mod R = L + 2)
@@ -354,15 +399,57 @@ __global__ __launch_bounds__(W * 64) void pre_coop_kernel(CoopArgs a)
         // with the next iteration's writes.
         int *bf = badf + (i & 1);
         take_recs(cu, ru, rd, bf);
-        // step i into its slot
         unsigned char *slot = ring + ri * kSlotB;
+        if constexpr (kPost) {
+            // the post-map of step i for this thread's (token prow, piece): the new streams
+            // out[n] = x post[n] + sum_o res[o] comb[o][n] (the post-map's own order of the
+            // products), into the slot and to `out`
+            const float *cb = coefb + (i & 1) * kCoefVals;
+            const f32x4 pq = *reinterpret_cast<const f32x4 *>(cb + prow * kHC);
+            f32x4 cq[kHC];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int row = prow + 16 * k;
-            *reinterpret_cast<u32x4 *>(slot + (row >> 2) * kTokB + (row & 3) * kRowB + piece * 16) = cur[k];
+            for (int o = 0; o < kHC; ++o) {
+                cq[o] = *reinterpret_cast<const f32x4 *>(cb + kHC * kQTok + prow * kHC * kHC + o * kHC);
+            }
+            const int t0 = (i * kQGroups + x) * kQTok;
+            const int ntok = p_ok ? min(kQTok, T - t0) : 0;
+            const __amdgpu_buffer_rsrc_t vo = buf_view_uniform(a.out + (size_t)(ntok > 0 ? t0 : 0) * kHC * H,
+                                                               (uint32_t)((size_t)ntok * kHC * H * sizeof(uint16_t)));
+#pragma unroll
+            for (int n = 0; n < kHC; ++n) {
+                u32x4 nw;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float lo = bf16_lo(xcur[q]) * pq[n];
+                    float hi = bf16_hi(xcur[q]) * pq[n];
+#pragma unroll
+                    for (int o = 0; o < kHC; ++o) {
+                        lo = fmaf(bf16_lo(cur[o][q]), cq[o][n], lo);
+                        hi = fmaf(bf16_hi(cur[o][q]), cq[o][n], hi);
+                    }
+                    nw[q] = pack_bf16x2(lo, hi);
+                }
+                *reinterpret_cast<u32x4 *>(slot + prow * kTokB + n * kRowB + piece * 16) = nw;
+                __builtin_amdgcn_raw_buffer_store_b128(nw, vo, (int)((uint32_t)((4 * prow + n) * H) * 2u + colq), 0, 2);
+            }
+            // the coefficients of step i + 1 (loaded with step i's streams) for the next iteration
+            if (i + 1 >= 1) {
+                store_coef(i + 1, cf);
+            }
+        } else {
+            // step i into its slot
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int row = prow + 16 * k;
+                *reinterpret_cast<u32x4 *>(slot + (row >> 2) * kTokB + (row & 3) * kRowB + piece * 16) = cur[k];
+            }
         }
         // the next loads: records of step cu + 1 first (they return before the streams)
         load_recs(cu + 1, ql, ru, rd);
+        if constexpr (kPost) {
+            load_coef(i + 3, cf);
+            xcur = load_x(i + 2);
+        }
         load_step(i + 2, cur);
         lds_barrier(); // B1: slot i and the slice sums are in LDS
 
@@ -549,6 +636,13 @@ __global__ __launch_bounds__(W * 64) void pre_coop_kernel(CoopArgs a)
     // steps 0 and 1, so every trip of the loop, the first included, issues the same
     // operations and the compiler's wait counts stay exact.
     u32x4 bufA[4], bufB[4], hold[kHC];
+    u32x4 xA = {0u, 0u, 0u, 0u}, xB = {0u, 0u, 0u, 0u};
+    float cfA[kCf], cfB[kCf];
+#pragma unroll
+    for (int k = 0; k < kCf; ++k) {
+        cfA[k] = 0.0f;
+        cfB[k] = 0.0f;
+    }
     float holdp[kHC];
     u32x4 ru[kUR], rd[kDR];
 #pragma unroll
@@ -569,14 +663,20 @@ __global__ __launch_bounds__(W * 64) void pre_coop_kernel(CoopArgs a)
     if (tid < 2) {
         badf[tid] = 0;
     }
+    if constexpr (kPost) {
+        // the coefficients of step 0 (the loop stages those of step j + 1 in iteration j)
+        float c0[kCf];
+        load_coef(0, c0);
+        store_coef(0, c0);
+    }
     __syncthreads();
     const int iend = nst + L + 1; // the last collapse (of step nst - 1) is in iteration nst + L
     int ri = R - 2, qi = RR - 2;  // step -2
     for (int i = -2; i < iend; i += 2) {
-        iteration(i, ri, qi, bufA, ru, rd, hold, holdp);
+        iteration(i, ri, qi, bufA, xA, cfA, ru, rd, hold, holdp);
         ri = wrap(ri + 1, R);
         qi = wrap(qi + 1, RR);
-        iteration(i + 1, ri, qi, bufB, ru, rd, hold, holdp);
+        iteration(i + 1, ri, qi, bufB, xB, cfB, ru, rd, hold, holdp);
         ri = wrap(ri + 1, R);
         qi = wrap(qi + 1, RR);
     }
@@ -623,7 +723,8 @@ CoopCfg coop_config(int64_t H)
     CoopCfg k{};
     k.W = coop_waves(H);
     const size_t slot = (size_t)kQTok * (256 * k.W + 16);
-    const size_t scratch = (size_t)k.W * kQTok * kQRedStride * 4 + (96 + 32 + 64 + 4 + 64) * 4;
+    // the waves' partials, sums, dsum, prel, flags, dummy, and the post-map's coefficients
+    const size_t scratch = (size_t)k.W * kQTok * kQRedStride * 4 + (96 + 32 + 64 + 4 + 64 + 2 * kCoefVals) * 4;
     const size_t lds_max = 160 * 1024;
     k.L = 3;
     while (k.L > 1 && (size_t)(k.L + 2) * slot + scratch > lds_max) {
@@ -654,7 +755,7 @@ bool coop_device_ok()
     return g_coop_device_ok[dev] == 1;
 }
 
-template <int W, typename WT>
+template <int W, typename WT, bool kPost>
 hipError_t launch_coop_w(const CoopArgs &a, size_t lds, hipStream_t stream)
 {
     // the dynamic-LDS limit is a per-device attribute: raised once on each device
@@ -665,37 +766,71 @@ hipError_t launch_coop_w(const CoopArgs &a, size_t lds, hipStream_t stream)
         return e != hipSuccess ? e : hipErrorInvalidDevice;
     }
     if (!attr_set[dev].load(std::memory_order_acquire)) {
-        e = hipFuncSetAttribute((const void *)pre_coop_kernel<W, WT>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        e = hipFuncSetAttribute((const void *)pre_coop_kernel<W, WT, kPost>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)lds);
         if (e != hipSuccess) {
             return e;
         }
         attr_set[dev].store(true, std::memory_order_release);
     }
-    pre_coop_kernel<W, WT><<<dim3(kQGroups * kQSlices), dim3(W * 64), lds, stream>>>(a);
+    pre_coop_kernel<W, WT, kPost><<<dim3(kQGroups * kQSlices), dim3(W * 64), lds, stream>>>(a);
     return hipGetLastError();
 }
 
-template <typename WT>
+template <typename WT, bool kPost>
 hipError_t launch_coop_t(const CoopArgs &a, int W, size_t lds, hipStream_t stream)
 {
     switch (W) {
     case 2:
-        return launch_coop_w<2, WT>(a, lds, stream);
+        return launch_coop_w<2, WT, kPost>(a, lds, stream);
     case 3:
-        return launch_coop_w<3, WT>(a, lds, stream);
+        return launch_coop_w<3, WT, kPost>(a, lds, stream);
     case 4:
-        return launch_coop_w<4, WT>(a, lds, stream);
+        return launch_coop_w<4, WT, kPost>(a, lds, stream);
     case 5:
-        return launch_coop_w<5, WT>(a, lds, stream);
+        return launch_coop_w<5, WT, kPost>(a, lds, stream);
     case 6:
-        return launch_coop_w<6, WT>(a, lds, stream);
+        return launch_coop_w<6, WT, kPost>(a, lds, stream);
     case 7:
-        return launch_coop_w<7, WT>(a, lds, stream);
+        return launch_coop_w<7, WT, kPost>(a, lds, stream);
     case 8:
-        return launch_coop_w<8, WT>(a, lds, stream);
+        return launch_coop_w<8, WT, kPost>(a, lds, stream);
     default:
         return hipErrorInvalidValue;
     }
+}
+
+CoopArgs coop_args(const CoopCfg &k, const uint16_t *res, const void *hc_fn, int fn_rows, const float *hc_scale,
+                   const float *hc_base, int64_t T, int64_t H, float rms_eps, float pre_eps, float sinkhorn_eps,
+                   float post_mult, int iters, bool head, uint16_t *y, float *post, float *comb, float *pre,
+                   void *workspace)
+{
+    CoopArgs a{};
+    a.res = res;
+    a.hc_fn = hc_fn;
+    a.hc_scale = hc_scale;
+    a.hc_base = hc_base;
+    a.T = (int)T;
+    a.H = (int)H;
+    a.nhb = (int)((H + 31) / 32);
+    a.fn_rows = fn_rows;
+    a.L = k.L;
+    a.R = k.R;
+    a.RR = k.RR;
+    a.inv_k = 1.0f / (float)(kHC * H);
+    a.rms_eps = rms_eps;
+    a.pre_eps = pre_eps;
+    a.sk_eps = sinkhorn_eps;
+    a.post_mult = post_mult;
+    a.iters = iters;
+    a.head = head ? 1 : 0;
+    a.y = y;
+    a.post = post;
+    a.comb = comb;
+    a.pre = pre;
+    a.rec = reinterpret_cast<u32x4 *>(workspace);
+    a.rec_bytes = (uint32_t)pre_coop_workspace_bytes(H);
+    return a;
 }
 
 } // namespace
@@ -723,32 +858,26 @@ hipError_t launch_pre_coop(const uint16_t *res, const void *hc_fn, bool fn_bf16,
                            float *comb, float *pre, void *workspace, hipStream_t stream)
 {
     const CoopCfg k = coop_config(H);
-    CoopArgs a{};
-    a.res = res;
-    a.hc_fn = hc_fn;
-    a.hc_scale = hc_scale;
-    a.hc_base = hc_base;
-    a.T = (int)T;
-    a.H = (int)H;
-    a.nhb = (int)((H + 31) / 32);
-    a.fn_rows = fn_rows;
-    a.L = k.L;
-    a.R = k.R;
-    a.RR = k.RR;
-    a.inv_k = 1.0f / (float)(kHC * H);
-    a.rms_eps = rms_eps;
-    a.pre_eps = pre_eps;
-    a.sk_eps = sinkhorn_eps;
-    a.post_mult = post_mult;
-    a.iters = iters;
-    a.head = head ? 1 : 0;
-    a.y = y;
-    a.post = post;
-    a.comb = comb;
-    a.pre = pre;
-    a.rec = reinterpret_cast<u32x4 *>(workspace);
-    a.rec_bytes = (uint32_t)pre_coop_workspace_bytes(H);
-    return fn_bf16 ? launch_coop_t<uint16_t>(a, k.W, k.lds, stream) : launch_coop_t<float>(a, k.W, k.lds, stream);
+    const CoopArgs a = coop_args(k, res, hc_fn, fn_rows, hc_scale, hc_base, T, H, rms_eps, pre_eps, sinkhorn_eps,
+                                 post_mult, iters, head, y, post, comb, pre, workspace);
+    return fn_bf16 ? launch_coop_t<uint16_t, false>(a, k.W, k.lds, stream)
+                   : launch_coop_t<float, false>(a, k.W, k.lds, stream);
+}
+
+hipError_t launch_post_pre_coop(const uint16_t *x, const uint16_t *res, const float *post_in, const float *comb_in,
+                                const float *hc_fn, const float *hc_scale, const float *hc_base, int64_t T, int64_t H,
+                                float rms_eps, float pre_eps, float sinkhorn_eps, float post_mult, int iters,
+                                uint16_t *out, uint16_t *y, float *post, float *comb, float *pre, void *workspace,
+                                hipStream_t stream)
+{
+    const CoopCfg k = coop_config(H);
+    CoopArgs a = coop_args(k, res, hc_fn, kMix, hc_scale, hc_base, T, H, rms_eps, pre_eps, sinkhorn_eps, post_mult,
+                           iters, false, y, post, comb, pre, workspace);
+    a.x = x;
+    a.post_in = post_in;
+    a.comb_in = comb_in;
+    a.out = out;
+    return launch_coop_t<float, true>(a, k.W, k.lds, stream);
 }
 
 } // namespace mhc

@@ -379,6 +379,41 @@ def test_post_project_workspace():
                   ws=None, wsb=0) == mhc.MHC_SUCCESS
 
 
+def _postpre(lib, **kw):
+    # every case below turns one argument invalid: validation fails before any launch
+    a = dict(x=0x100000, res=0x400000, post=0x200000, comb=0x210000, fn=0x1000000, sc=0x300000, base=0x310000, T=8,
+             H=64, rms=1e-6, pre_eps=1e-6, sk=1e-6, pm=1.0, iters=20, out=0x600000, y=0x700000, pn=0x800000,
+             cn=0x810000, pre=0x820000, ws=0x9000000, wsb=1 << 30)
+    a.update(kw)
+    v = lambda n: ctypes.c_void_p(a[n]) if a[n] is not None else None
+    return lib.mhc_post_pre_fused(v("x"), v("res"), v("post"), v("comb"), v("fn"), v("sc"), v("base"), a["T"], a["H"],
+                                  a["rms"], a["pre_eps"], a["sk"], a["pm"], a["iters"], v("out"), v("y"), v("pn"),
+                                  v("cn"), v("pre"), v("ws"), a["wsb"], NULL)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(T=-1), dict(H=0), dict(iters=0), dict(rms=0.0), dict(sk=0.0), dict(pre_eps=-1.0), dict(pm=float("inf")),
+    dict(x=None), dict(res=None), dict(post=None), dict(comb=None), dict(fn=None), dict(sc=None), dict(base=None),
+    dict(out=None), dict(y=None), dict(pn=None), dict(cn=None),
+    dict(out=0x400000 + 16), dict(out=0x100000), dict(out=0x200000), dict(out=0x1000000), dict(out=0x300000),
+    dict(y=0x400000), dict(y=0x600000 + 64), dict(y=0x100000), dict(pn=0x200000), dict(cn=0x210000 + 64),
+    dict(pre=0x200000), dict(pn=0x810000), dict(ws=0x100000), dict(ws=0x400000), dict(ws=0x1000000),
+])
+def test_post_pre_fused_validation_invalid(kw):
+    assert _postpre(mhc.lib(), **kw) == mhc.MHC_ERROR_INVALID_VALUE
+
+
+def test_post_pre_fused_workspace():
+    lib = mhc.lib()
+    need = mhc.mhc_pre_fused_workspace_bytes(8, 64)
+    assert _postpre(lib, wsb=need - 1) == mhc.MHC_ERROR_WORKSPACE
+    assert _postpre(lib, ws=None) == mhc.MHC_ERROR_WORKSPACE
+    assert _postpre(lib, ws=0x9000000 + 16) == mhc.MHC_ERROR_WORKSPACE
+    # T == 0: nothing to do, no pointer is looked at
+    assert _postpre(lib, T=0, x=None, res=None, post=None, comb=None, fn=None, sc=None, base=None, out=None, y=None,
+                    pn=None, cn=None, pre=None, ws=None, wsb=0) == mhc.MHC_SUCCESS
+
+
 def test_binding_rejects_cpu_tensors_before_the_library():
     import torch
     with pytest.raises(ValueError):
@@ -387,6 +422,10 @@ def test_binding_rejects_cpu_tensors_before_the_library():
     with pytest.raises(ValueError):
         mhc.mhc_post_project(torch.zeros(2, 8, dtype=torch.bfloat16), torch.zeros(2, 4, 8, dtype=torch.bfloat16),
                              torch.zeros(2, 4), torch.zeros(2, 4, 4), torch.zeros(24, 32))
+    with pytest.raises(ValueError):
+        mhc.mhc_post_pre_fused(torch.zeros(2, 8, dtype=torch.bfloat16), torch.zeros(2, 4, 8, dtype=torch.bfloat16),
+                               torch.zeros(2, 4), torch.zeros(2, 4, 4), torch.zeros(24, 32), torch.ones(3),
+                               torch.zeros(24))
     with pytest.raises(ValueError):
         mhc.mhc_sinkhorn(torch.zeros(3, 4, 4))
     with pytest.raises(ValueError):
