@@ -150,3 +150,47 @@ def test_post_pre_empty():
                                             torch.zeros(24, 256, device="cuda"), torch.ones(3, device="cuda"),
                                             torch.zeros(24, device="cuda"))
     assert out.shape == (0, HC, 64) and y.shape == (0, 64)
+
+
+def test_post_pre_graph_replays_with_new_inputs():
+    """A captured call replayed on new inputs each time, in place: every replay equals an
+    eager call on the same inputs bit for bit (the exchange tags differ per replay)."""
+    mhc = _mhc()
+    T, H = 1031, 4096
+    nxt, x, res, post, comb = _case(T, H, 1030)
+    xd, rd, pd, cd = to_dev_bf16(x), to_dev_bf16(res), to_dev_f32(post), to_dev_f32(comb)
+    fn, sc, base = to_dev_f32(nxt.hc_fn), to_dev_f32(nxt.hc_scale), to_dev_f32(nxt.hc_base)
+    ws = torch.empty(mhc.mhc_pre_fused_workspace_bytes(T, H), dtype=torch.uint8, device="cuda")
+    y = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
+    pn = torch.empty(T, HC, device="cuda")
+    cn = torch.empty(T, HC, HC, device="cuda")
+
+    def step():
+        mhc.mhc_post_pre_fused(xd, rd, pd, cd, fn, sc, base, out=rd, y=y, post_next=pn, comb_next=cn, workspace=ws)
+
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        step()
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        _, x2, r2, p2, c2 = _case(T, H, 1031 + rep)
+        xd.copy_(to_dev_bf16(x2))
+        rd.copy_(to_dev_bf16(r2))
+        pd.copy_(to_dev_f32(p2))
+        cd.copy_(to_dev_f32(c2))
+        for t in (y, pn, cn):
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = (bits_of(rd), bits_of(y), f32_of(pn), f32_of(cn))
+        eo, ey, ep, ec = mhc.mhc_post_pre_fused(to_dev_bf16(x2), to_dev_bf16(r2), to_dev_f32(p2), to_dev_f32(c2), fn,
+                                                sc, base)
+        torch.cuda.synchronize()
+        for u, v, name in zip(got, (bits_of(eo), bits_of(ey), f32_of(ep), f32_of(ec)), ("out", "y", "post", "comb")):
+            assert np.array_equal(u, v), f"replay {rep}: {name}"
