@@ -69,6 +69,19 @@ int mhc_abi_version(void);
 const char *mhc_status_string(mhc_status status);
 
 /*
+ * mhc_set_exchange_test_hooks -- test hooks of the one-read pre-map (mhc_pre_fused and
+ * mhc_post_pre_fused at T >= 1024, 1024 < H <= 8192), for tests of its failure path only.
+ * That form's workgroups exchange partial sums through memory, tagged with the call and
+ * the step; a reader that finds a record not yet written loads it again, up to max_retry
+ * times (negative: the default, 2^14), and then gives the step NaN outputs rather than
+ * wait for ever or use a stale record.  A nonzero tag_skew makes every record look
+ * missing, so every step takes that path and every output of the call is NaN.  The
+ * setting is process-wide and read when a call is enqueued; normal use leaves
+ * (-1, 0).  Host only, no GPU work.
+ */
+void mhc_set_exchange_test_hooks(int32_t max_retry, uint32_t tag_skew);
+
+/*
  * mhc_launch_plan -- diagnostics, host only (no HIP call, nothing enqueued): how an entry
  * point splits a call into launches of its token-parallel kernel.  `entry` names the
  * entry point without the mhc_ prefix: "post", "expand", "head_mean", "pre_fused" (its

@@ -105,6 +105,8 @@ def lib() -> ctypes.CDLL:
     L.mhc_post_project.restype = ctypes.c_int
     L.mhc_post_pre_fused.argtypes = [P, P, P, P, P, P, P, I64, I64, F, F, F, F, I32, P, P, P, P, P, P, SZ, P]
     L.mhc_post_pre_fused.restype = ctypes.c_int
+    L.mhc_set_exchange_test_hooks.argtypes = [I32, ctypes.c_uint32]
+    L.mhc_set_exchange_test_hooks.restype = None
     _lib = L
     return L
 
@@ -552,6 +554,14 @@ def mhc_post_pre_fused(x: torch.Tensor, res: torch.Tensor, post: torch.Tensor, c
     return out, y, post_next, comb_next
 
 
+def set_exchange_test_hooks(max_retry: int = -1, tag_skew: int = 0) -> None:
+    """Test hooks of the one-read pre-map's exchange (process-wide; tests of its failure
+    path only): reloads of a missing record before the step's outputs become NaN (-1: the
+    default) and a value mixed into the expected tags (nonzero: every record looks
+    missing).  (-1, 0) restores normal operation."""
+    lib().mhc_set_exchange_test_hooks(int(max_retry), int(tag_skew) & 0xFFFFFFFF)
+
+
 SINKHORN_BWD_MAX_ITERS = 255
 
 
@@ -868,5 +878,6 @@ __all__ = ["mhc_sinkhorn", "mhc_pre_fused", "mhc_pre_fused_noalloc", "mhc_pre_fu
            "mhc_sinkhorn_backward", "mhc_post_backward", "mhc_pre_from_dots_backward",
            "mhc_pre_backward_workspace_bytes", "mhc_pre_fused_backward", "mhc_pre_fused_backward_workspace_bytes",
            "mhc_post_project", "mhc_post_project_workspace_bytes", "mhc_post_pre_fused",
+           "set_exchange_test_hooks",
            "lib", "abi_version", "status_string", "launch_plan", "MHCError", "HC",
            "MIX", "SINKHORN_BWD_MAX_ITERS", "MHC_PRE_FUSED_NOALLOC_MAX_BYTES"]

@@ -145,6 +145,11 @@ extern "C" {
 
 int mhc_abi_version(void) { return MHC_ABI_VERSION; }
 
+void mhc_set_exchange_test_hooks(int32_t max_retry, uint32_t tag_skew)
+{
+    mhc::set_exchange_test_hooks(max_retry, tag_skew);
+}
+
 const char *mhc_status_string(mhc_status status)
 {
     switch (status) {

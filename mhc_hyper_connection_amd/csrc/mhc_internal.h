@@ -106,6 +106,10 @@ hipError_t launch_post_pre_coop(const uint16_t *x, const uint16_t *res, const fl
                                 float rms_eps, float pre_eps, float sinkhorn_eps, float post_mult, int iters,
                                 uint16_t *out, uint16_t *y, float *post, float *comb, float *pre, void *workspace,
                                 hipStream_t stream);
+// Test hooks of the one-read form's exchange (mhc_set_exchange_test_hooks): the reloads of a
+// step's records before its outputs become NaN (negative: the default 2^14) and a value
+// mixed into the tags readers expect (0 in normal use).
+void set_exchange_test_hooks(int max_retry, uint32_t tag_skew);
 // Workspace of the pre-map entry points: enough for either form.
 size_t pre_fused_workspace_bytes(int64_t T, int64_t H);
 // Workspace of the form a call with these sizes and 16-byte rows (vec8) or not takes on the

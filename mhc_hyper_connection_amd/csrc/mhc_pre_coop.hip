@@ -55,6 +55,8 @@ constexpr int kQDefChunks = (kQDefFields + 2) / 3;                  // 7
 constexpr int kQChunks = kQUrgChunks + kQTok * kQDefChunks;         // chunks of one record (139)
 constexpr int kQRedStride = 28;                                     // 24 dots + 4 lane-group sums of squares
 constexpr int kQMaxRetry = 1 << 14;                                 // reloads of a step's records before giving up
+std::atomic<int> g_max_retry{kQMaxRetry};
+std::atomic<uint32_t> g_tag_skew{0};
 constexpr uint32_t kOob = 0x80000000u;
 constexpr int64_t kCoopMinTokens = 1024; // below this the pipeline's fill and drain dominate
 
@@ -76,6 +78,11 @@ struct CoopArgs {
     const uint16_t *x;
     const float *post_in, *comb_in;
     uint16_t *out;
+    // reloads of a step's records before its outputs become NaN, and a value mixed into the
+    // tags the readers expect (0; nonzero only to make every record look missing, a test of
+    // the NaN path set through mhc_set_exchange_test_hooks)
+    int max_retry;
+    uint32_t tag_skew;
 };
 constexpr int kCoefVals = kQTok * (kHC + kHC * kHC); // post and comb of one step: 320 floats
 
@@ -298,7 +305,7 @@ __global__ __launch_bounds__(W * 64) void pre_coop_kernel(CoopArgs a)
     // tags of the loaded records of step j (0 if they all match), and their slice sums into LDS
     auto take_recs = [&](int j, const u32x4(&ru)[kUR], const u32x4(&rd)[kDR], int *flag) {
         const bool ok = j >= 0 && j < nst;
-        const uint32_t tag = coop_tag(key, j * kQGroups + x);
+        const uint32_t tag = coop_tag(key, j * kQGroups + x) ^ a.tag_skew;
         const bool dz = designated(j);
         int bad = 0;
 #pragma unroll
@@ -525,7 +532,7 @@ __global__ __launch_bounds__(W * 64) void pre_coop_kernel(CoopArgs a)
             __builtin_amdgcn_raw_buffer_store_b128(yw, vy, (int)((uint32_t)(prow * H) * 2u + colq), 0, 2);
         }
         if (bad_now) { // a record had not landed: load the step's records again
-            for (int tries = 0; tries < kQMaxRetry; ++tries) {
+            for (int tries = 0; tries < a.max_retry; ++tries) {
                 __syncthreads();
                 if (tid == 0) {
                     *bf = 0;
@@ -830,6 +837,8 @@ CoopArgs coop_args(const CoopCfg &k, const uint16_t *res, const void *hc_fn, int
     a.pre = pre;
     a.rec = reinterpret_cast<u32x4 *>(workspace);
     a.rec_bytes = (uint32_t)pre_coop_workspace_bytes(H);
+    a.max_retry = g_max_retry.load(std::memory_order_relaxed);
+    a.tag_skew = g_tag_skew.load(std::memory_order_relaxed);
     return a;
 }
 
@@ -862,6 +871,12 @@ hipError_t launch_pre_coop(const uint16_t *res, const void *hc_fn, bool fn_bf16,
                                  post_mult, iters, head, y, post, comb, pre, workspace);
     return fn_bf16 ? launch_coop_t<uint16_t, false>(a, k.W, k.lds, stream)
                    : launch_coop_t<float, false>(a, k.W, k.lds, stream);
+}
+
+void set_exchange_test_hooks(int max_retry, uint32_t tag_skew)
+{
+    g_max_retry.store(max_retry < 0 ? kQMaxRetry : max_retry, std::memory_order_relaxed);
+    g_tag_skew.store(tag_skew, std::memory_order_relaxed);
 }
 
 hipError_t launch_post_pre_coop(const uint16_t *x, const uint16_t *res, const float *post_in, const float *comb_in,

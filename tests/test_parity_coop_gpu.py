@@ -161,3 +161,42 @@ def test_coop_graph_replays_with_new_inputs():
             assert np.array_equal(u, v), f"replay {rep} {name}"
         inp.res = nxt.res
         check_pre_all_tokens(inp, got + (None,), f"replay {rep}")
+
+
+def test_coop_missing_records_give_nan_not_a_hang():
+    """The exchange's failure path, forced from the host: with a tag skew every record looks
+    missing, so after the (here 2) reloads every step's outputs are NaN and the call still
+    returns; with the hooks reset the same call is correct again."""
+    mhc = _mhc()
+    inp = layer_inputs(1100, 2048, cfg=670)
+    try:
+        mhc.set_exchange_test_hooks(max_retry=2, tag_skew=0x5A5A5A5A)
+        y, post, comb, pre = _run(inp)
+    finally:
+        mhc.set_exchange_test_hooks()
+    assert np.isnan(bf16_bits_to_f32(y)).all()
+    assert np.isnan(post).all() and np.isnan(comb).all() and np.isnan(pre).all()
+    check_pre_all_tokens(inp, _run(inp), "coop after the hooks are reset")
+
+
+def test_post_pre_missing_records_keep_out_and_give_nan():
+    """The same for mhc_post_pre_fused: the post-map's out does not depend on the exchange
+    and stays exact; the pre-map's outputs are NaN."""
+    mhc = _mhc()
+    inp = layer_inputs(1100, 2048, cfg=671)
+    x = to_dev_bf16(inp.x)
+    res = to_dev_bf16(inp.res)
+    post = torch.rand(1100, HC, device="cuda")
+    comb = torch.full((1100, HC, HC), 0.25, device="cuda")
+    fn, sc, base = to_dev_f32(inp.hc_fn), to_dev_f32(inp.hc_scale), to_dev_f32(inp.hc_base)
+    try:
+        mhc.set_exchange_test_hooks(max_retry=2, tag_skew=1)
+        out, y, pn, cn = mhc.mhc_post_pre_fused(x, res, post, comb, fn, sc, base)
+        torch.cuda.synchronize()
+    finally:
+        mhc.set_exchange_test_hooks()
+    ref = mhc.mhc_post(x, res, post, comb)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(out), bits_of(ref))
+    assert np.isnan(bf16_bits_to_f32(bits_of(y))).all()
+    assert np.isnan(f32_of(pn)).all() and np.isnan(f32_of(cn)).all()
