@@ -13,19 +13,26 @@
 //    s of a group owns a slice of W x 32 h across the four streams and keeps that slice of
 //    the weights in VGPRs, split exactly into three bf16 terms for the MFMA.
 //  * The group walks its tokens in 16-token steps (group x takes steps x, x + 8, ...).
-//    A step's slice of the streams is loaded two steps ahead, written into a ring of LDS
-//    slots, projected with v_mfma_f32_16x16x32_bf16 (the sum of squares rides on
-//    v_dot2_f32_bf16), and reduced over the workgroup's waves into one record: 24 partial
-//    dots and the partial sum of squares of its 16 tokens.
+//    A step's slice of the streams is loaded two steps ahead, written into a ring of L + 1
+//    LDS slots, projected with v_mfma_f32_16x16x32_bf16 (the sum of squares rides on
+//    v_dot2_f32_bf16) into per-wave partial sums, and in the next iteration reduced over
+//    the workgroup's waves into one record: 24 partial dots and the partial sum of squares
+//    of its 16 tokens (the partial sums are double-buffered by step parity, so that the
+//    reduction runs beside the next step's products instead of between two barriers).
 //  * Records go through the XCD's L2 as 16-byte chunks of three values and a tag that
 //    names the call (its dispatch id) and the step.  L iterations after producing a step,
-//    every workgroup loads the pre dots and the sums of squares of that step from all 32
-//    slices (device-scope loads: they miss the CU's L1), sums them over the slices in a
-//    fixed order, forms rstd and the pre weights, and collapses its slice of the step
-//    from the LDS ring: the streams are read from HBM once.  A chunk whose tag does not
-//    match has not landed yet and is loaded again, up to 2^14 times; a step whose records
-//    are still missing then (its writer was never made resident, e.g. behind a long kernel
-//    on another stream) gets NaN outputs rather than stale ones.
+//    every workgroup sums the pre dots and the sums of squares of that step from all 32
+//    slices (device-scope loads, issued one iteration earlier: they miss the CU's L1) in a
+//    fixed order; the next iteration forms rstd and the pre weights and collapses its slice
+//    of the step, from registers loaded out of the ring: the streams are read from HBM
+//    once.  A chunk whose tag does not match has not landed yet and is loaded again, up to
+//    2^14 times; a step whose records are still missing then (its writer was never made
+//    resident, e.g. behind a long kernel on another stream) gets NaN outputs rather than
+//    stale ones.
+//  * An iteration has two barriers.  Between them run the slice sums, the products, the
+//    collapse (its arithmetic between the products), the record of the previous step and
+//    the next record loads; between B2 and the next B1 only the pre weights, the new step's
+//    slot and the stream loads.
 //  * Each token's post weights and Sinkhorn are finished by one workgroup: workgroup s
 //    takes token s mod 16 of the steps whose parity is s / 16.
 //
@@ -53,7 +60,10 @@ constexpr int kQUrgChunks = (kQUrgVals + 2) / 3;                    // 27
 constexpr int kQDefFields = kMix - kHC;                             // post and comb dots
 constexpr int kQDefChunks = (kQDefFields + 2) / 3;                  // 7
 constexpr int kQChunks = kQUrgChunks + kQTok * kQDefChunks;         // chunks of one record (139)
-constexpr int kQRedStride = 28;                                     // 24 dots + 4 lane-group sums of squares
+// row stride of the waves' partial sums: 24 dots and the sum of squares, padded to 28 floats
+// (conflict-free writes) except at 8 waves, where the two parity buffers must fit beside a
+// ring of 4 slots
+constexpr int red_stride(int W) { return W == 8 ? 25 : 28; }
 constexpr int kQMaxRetry = 1 << 14;                                 // reloads of a step's records before giving up
 std::atomic<int> g_max_retry{kQMaxRetry};
 std::atomic<uint32_t> g_tag_skew{0};
@@ -141,6 +151,7 @@ __global__ __launch_bounds__(W * 64) void pre_coop_kernel(CoopArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     constexpr int kTh = W * 64;
+    constexpr int kQRedStride = red_stride(W);
     constexpr int kPieces = 4 * W;        // 16-byte pieces of one stream row of the slice
     constexpr int kRowB = 64 * W;         // bytes of one stream row of the slice
     constexpr int kTokB = 4 * kRowB + 16; // token pitch in a slot: (16W + 1) x 16 bytes
@@ -156,8 +167,8 @@ __global__ __launch_bounds__(W * 64) void pre_coop_kernel(CoopArgs a)
     // its SIMD when W < 8 (waves go to SIMDs round robin)
     constexpr int kAux = W >= 4 ? 3 : W - 1;
     unsigned char *ring = smem;
-    float *red = reinterpret_cast<float *>(smem + R * kSlotB); // [W][16][28]
-    float *sums = red + W * kQTok * kQRedStride;               // [81]: value f * 16 + token
+    float *red = reinterpret_cast<float *>(smem + R * kSlotB); // [2][W][16][stride], by step parity
+    float *sums = red + 2 * W * kQTok * kQRedStride;           // [81]: value f * 16 + token
     float *dsum = sums + 96;                                   // [21]: the designated token's post and comb dots
     float *prel = dsum + 32;                                   // [16][4]
     int *badf = reinterpret_cast<int *>(prel + 64);
@@ -322,6 +333,12 @@ __global__ __launch_bounds__(W * 64) void pre_coop_kernel(CoopArgs a)
             dst[1] = v1;
             dst[2] = v2;
         }
+        if (2 * w >= kQDefChunks) { // no deferred chunk in this wave (wave-uniform)
+            if (bad) {
+                *flag = 1;
+            }
+            return;
+        }
 #pragma unroll
         for (int r = 0; r < kDR; ++r) {
             const int k = r * kHW + hw;
@@ -387,25 +404,94 @@ __global__ __launch_bounds__(W * 64) void pre_coop_kernel(CoopArgs a)
         }
     }
 
-    // ---- one iteration: produce step i, collapse step i - L
-    // ri = i mod R (the LDS slot of step i), qi = i mod RR (its record slot), kept as counters.
-    // One iteration: sum the records of step cu = i - L; write step i to its slot; projection
-    // of step i and collapse of step cu - 1 (from registers, so that its arithmetic overlaps
-    // the products); the record of step i; step cu's slot and pre weights into registers.
+    // ---- one iteration i (ri = i mod R, qi = i mod RR, kept as counters).  X = i - L.
+    // Phase A (after the previous iteration's B2): reload the records of step X - 1 if one had
+    // not landed; the auxiliary wave forms the pre weights of step X - 1 (and the designated
+    // token's raw comb and post values); step i goes into its slot; the streams of step i + 2
+    // are loaded.  Phase B (between B1 and B2): the records of step X are summed over the
+    // slices; step i is projected while step X - 1 is collapsed from registers; the partial
+    // sums of step i - 1 (written before the last B2) are reduced over the waves into its
+    // record; the records of step X + 1 are loaded; step X's slot goes into registers for the
+    // next iteration's collapse (the slot is written again, as step i + 1, after B2).
     auto iteration = [&](int i, int ri, int qi, u32x4(&cur)[4], u32x4 &xcur, float(&cf)[kCf], u32x4(&ru)[kUR],
-                         u32x4(&rd)[kDR], u32x4(&hold)[kHC], float(&holdp)[kHC]) {
-        const int cu = i - L;
-        const int cc = cu - 1;                    // collapsed this iteration
-        const int rcs = wrap(ri + 2, R);          // slot of step cu: i - L = i + 2 (mod R = L + 2)
-        const int qc = wrap(qi + RR - L, RR);     // record slot of step cu
-        const int ql = wrap(qi + RR - L + 1, RR); // record slot of step cu + 1
-        const bool cu_ok = cu >= 0 && cu < nst;
+                         u32x4(&rd)[kDR], u32x4(&hold)[kHC]) {
+        const int X = i - L;
+        const int Xp = X - 1;                        // pre weights formed and collapsed this iteration
+        const int rx = wrap(ri + 1, R);              // slot of step X: i - L = i + 1 (mod R = L + 1)
+        const int qxp = wrap(qi + RR - L - 1, RR);   // record slot of step X - 1
+        const int qx1 = wrap(qi + RR - L + 1, RR);   // record slot of step X + 1
+        const int qim1 = wrap(qi + RR - 1, RR);      // record slot of step i - 1
+        const bool xp_ok = Xp >= 0 && Xp < nst;
         const bool p_ok = i >= 0 && i < nst;
-        // records of step cu (loaded last iteration): check and sum over the slices.  The
-        // flag alternates with the iteration's parity, so its reset after B2 cannot race
-        // with the next iteration's writes.
-        int *bf = badf + (i & 1);
-        take_recs(cu, ru, rd, bf);
+        const bool pm1_ok = i - 1 >= 0 && i - 1 < nst;
+
+        // ---- phase A
+        // A1: a record of step X - 1 had not landed when it was summed: load them again
+        {
+            int *bfp = badf + ((i - 1) & 1);
+            if (*bfp) {
+                for (int tries = 0; tries < a.max_retry; ++tries) {
+                    __syncthreads();
+                    if (tid == 0) {
+                        *bfp = 0;
+                    }
+                    __syncthreads();
+                    u32x4 qu[kUR], qd[kDR];
+                    asm volatile("" ::: "memory");
+                    load_recs(Xp, qxp, qu, qd);
+                    take_recs(Xp, qu, qd, bfp);
+                    __syncthreads();
+                    if (!*bfp) {
+                        break;
+                    }
+                }
+                // still missing after the bounded reloads (a workgroup of the group was not
+                // resident in time): the step's sums become NaN, so its outputs are NaN, never
+                // values from a stale record
+                if (*bfp) {
+                    if (tid < 96) {
+                        sums[tid] = __builtin_nanf("");
+                    } else if (tid < 128) {
+                        dsum[tid - 96] = __builtin_nanf("");
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        // A2: pre weights of step X - 1 (the auxiliary wave: lane = 16 k + token, one sigmoid
+        // each); the designated token's comb logits (lane e) and post pre-activations (lanes
+        // 0..3), stored raw into comb and post (the Sinkhorn and the sigmoids run after the
+        // loop); its pre weights to `pre` if asked for.  Every wave issues the stores (elsewhere
+        // into empty views), so that every wave's memory operations stay the same.
+        const bool dz = designated(Xp) && !a.head;
+        const int tdz = (Xp * kQGroups + x) * kQTok + td;
+        {
+            if (w == kAux && xp_ok) {
+                const int tok = lane & 15, k = lane >> 4;
+                const float rstd = rstd_of(sums[4 * kQTok + tok], a.inv_k, a.rms_eps);
+                prel[tok * kHC + k] = sigmoid_rcp(fmaf(sums[k * kQTok + tok] * rstd, s0, bpre)) + a.pre_eps;
+            }
+            float Lg = 0.0f, zp = 0.0f;
+            if (w == kAux && dz) {
+                const float rstd = rstd_of(sums[4 * kQTok + td], a.inv_k, a.rms_eps);
+                const int e = lane & 15;
+                Lg = fmaf(dsum[kHC + e] * rstd, s2, bcomb);
+                zp = fmaf(dsum[e & 3] * rstd, s1, bpost);
+            }
+            const bool tin = dz && tdz < T && w == kAux;
+            const __amdgpu_buffer_rsrc_t vc =
+                buf_view_uniform(a.comb + (size_t)(tin ? tdz : 0) * kHC * kHC, tin ? kHC * kHC * 4 : 0);
+            const __amdgpu_buffer_rsrc_t vp =
+                buf_view_uniform(a.post + (size_t)(tin ? tdz : 0) * kHC, tin ? kHC * 4 : 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(Lg), vc, lane < 16 ? lane * 4 : (int)kOob, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(zp), vp, lane < 4 ? lane * 4 : (int)kOob, 0, 0);
+            const bool pin = designated(Xp) && tdz < T && a.pre != nullptr && w == kAux;
+            const __amdgpu_buffer_rsrc_t vq =
+                buf_view_uniform(pin ? (const void *)(a.pre + (size_t)tdz * kHC) : (const void *)a.y, pin ? kHC * 4 : 0);
+            const float pv = w == kAux ? prel[td * kHC + (lane & 3)] : 0.0f;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pv), vq, lane < 4 ? lane * 4 : (int)kOob, 0, 0);
+        }
+        // A3: step i into its slot
         unsigned char *slot = ring + ri * kSlotB;
         if constexpr (kPost) {
             // the post-map of step i for this thread's (token prow, piece): the new streams
@@ -444,25 +530,38 @@ __global__ __launch_bounds__(W * 64) void pre_coop_kernel(CoopArgs a)
                 store_coef(i + 1, cf);
             }
         } else {
-            // step i into its slot
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int row = prow + 16 * k;
                 *reinterpret_cast<u32x4 *>(slot + (row >> 2) * kTokB + (row & 3) * kRowB + piece * 16) = cur[k];
             }
         }
-        // the next loads: records of step cu + 1 first (they return before the streams)
-        load_recs(cu + 1, ql, ru, rd);
+        // A4: the loads of step i + 2
         if constexpr (kPost) {
             load_coef(i + 3, cf);
             xcur = load_x(i + 2);
         }
         load_step(i + 2, cur);
-        lds_barrier(); // B1: slot i and the slice sums are in LDS
+        lds_barrier(); // B1: slot i, the pre weights of step X - 1 and the coefficients are in LDS
 
-        const int bad_now = *bf; // read before the products; tested after them
-        // projection of step i (this wave's 32 h, all 4 streams): streams 0, 1 and 2, 3 in two
-        // chains per column tile; a step outside the range projects zeros and stores nothing
+        // ---- phase B
+        if (tid == 0) {
+            badf[(i - 1) & 1] = 0; // every thread read it before B1
+        }
+        float holdp[kHC];
+#pragma unroll
+        for (int k = 0; k < kHC; ++k) {
+            holdp[k] = prel[prow * kHC + k];
+        }
+        // B1': the records of step X (loaded last iteration): check and sum over the slices
+        int *bf = badf + (i & 1);
+        take_recs(X, ru, rd, bf);
+        // B2': projection of step i (this wave's 32 h, all 4 streams; streams 0, 1 and 2, 3 in
+        // two chains per column tile; a step outside the range projects zeros and stores
+        // nothing), with the collapse of step X - 1 (y = sum_i pre_i * res_i for this thread's
+        // token and piece) between the products
+        u32x4 yw;
+        float *rw = red + (i & 1) * (W * kQTok * kQRedStride) + w * (kQTok * kQRedStride);
         {
             u32x4 A[kHC];
 #pragma unroll
@@ -495,10 +594,22 @@ __global__ __launch_bounds__(W * 64) void pre_coop_kernel(CoopArgs a)
                     const bf16x2 pr = __builtin_bit_cast(bf16x2, wk);
                     sq = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, sq, false);
                 }
+                // one quarter of the collapse (h pair q = st) while these products run
+                {
+                    const int q = st;
+                    float lo = bf16_lo(hold[0][q]) * holdp[0];
+                    float hi = bf16_hi(hold[0][q]) * holdp[0];
+#pragma unroll
+                    for (int o = 1; o < kHC; ++o) {
+                        lo = fmaf(bf16_lo(hold[o][q]), holdp[o], lo);
+                        hi = fmaf(bf16_hi(hold[o][q]), holdp[o], hi);
+                    }
+                    yw[q] = pack_bf16x2(lo, hi);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
             // the token's sum of squares over the 4 lane groups: (g0 + g1) + (g2 + g3)
             sq = rows_sum(sq);
-            float *rw = red + w * (kQTok * kQRedStride);
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const float d0 = acc0[0][k] + acc0[1][k];
@@ -510,93 +621,20 @@ __global__ __launch_bounds__(W * 64) void pre_coop_kernel(CoopArgs a)
             }
             rw[c * kQRedStride + kMix] = sq; // the same bits from all 4 lane groups
         }
-        // collapse of step cc: y = sum_i pre_i * res_i for this thread's (token, piece)
         {
-            u32x4 yw;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float lo = bf16_lo(hold[0][q]) * holdp[0];
-                float hi = bf16_hi(hold[0][q]) * holdp[0];
-#pragma unroll
-                for (int st = 1; st < kHC; ++st) {
-                    lo = fmaf(bf16_lo(hold[st][q]), holdp[st], lo);
-                    hi = fmaf(bf16_hi(hold[st][q]), holdp[st], hi);
-                }
-                yw[q] = pack_bf16x2(lo, hi);
-            }
-            const bool cc_ok = cc >= 0 && cc < nst;
-            const int t0 = (cc * kQGroups + x) * kQTok;
-            const int ntok = cc_ok ? min(kQTok, T - t0) : 0;
+            const bool xp_in = xp_ok;
+            const int t0 = (Xp * kQGroups + x) * kQTok;
+            const int ntok = xp_in ? min(kQTok, T - t0) : 0;
             const __amdgpu_buffer_rsrc_t vy =
                 buf_view_uniform(a.y + (size_t)(ntok > 0 ? t0 : 0) * H, (uint32_t)((size_t)ntok * H * sizeof(uint16_t)));
             __builtin_amdgcn_raw_buffer_store_b128(yw, vy, (int)((uint32_t)(prow * H) * 2u + colq), 0, 2);
         }
-        if (bad_now) { // a record had not landed: load the step's records again
-            for (int tries = 0; tries < a.max_retry; ++tries) {
-                __syncthreads();
-                if (tid == 0) {
-                    *bf = 0;
-                }
-                __syncthreads();
-                u32x4 qu[kUR], qd[kDR];
-                asm volatile("" ::: "memory");
-                load_recs(cu, qc, qu, qd);
-                take_recs(cu, qu, qd, bf);
-                __syncthreads();
-                if (!*bf) {
-                    break;
-                }
-            }
-            // still missing after the bounded reloads (a workgroup of the group was not
-            // resident in time): the step's sums become NaN, so its outputs are NaN, never
-            // values from a stale record
-            if (*bf) {
-                if (tid < 96) {
-                    sums[tid] = __builtin_nanf("");
-                } else if (tid < 128) {
-                    dsum[tid - 96] = __builtin_nanf("");
-                }
-                __syncthreads();
-            }
-        }
-
-        // pre weights of step cu (the auxiliary wave: lane = 16 k + token, one sigmoid each)
-        if (w == kAux && cu_ok) {
-            const int tok = lane & 15, k = lane >> 4;
-            const float rstd = rstd_of(sums[4 * kQTok + tok], a.inv_k, a.rms_eps);
-            prel[tok * kHC + k] = sigmoid_rcp(fmaf(sums[k * kQTok + tok] * rstd, s0, bpre)) + a.pre_eps;
-        }
-        // this workgroup's token of step cu: its comb logits (lane e of the auxiliary wave) and post
-        // pre-activations (lanes 0..3), stored raw into comb and post; the Sinkhorn and the
-        // sigmoids run after the loop, off the per-step path
-        const bool dz = designated(cu) && !a.head;
-        const int tdz = (cu * kQGroups + x) * kQTok + td;
-        {
-            float Lg = 0.0f, zp = 0.0f;
-            if (w == kAux && dz) {
-                const float rstd = rstd_of(sums[4 * kQTok + td], a.inv_k, a.rms_eps);
-                const int e = lane & 15;
-                Lg = fmaf(dsum[kHC + e] * rstd, s2, bcomb);
-                zp = fmaf(dsum[e & 3] * rstd, s1, bpost);
-            }
-            const bool tin = dz && tdz < T && w == kAux;
-            const __amdgpu_buffer_rsrc_t vc =
-                buf_view_uniform(a.comb + (size_t)(tin ? tdz : 0) * kHC * kHC, tin ? kHC * kHC * 4 : 0);
-            const __amdgpu_buffer_rsrc_t vp =
-                buf_view_uniform(a.post + (size_t)(tin ? tdz : 0) * kHC, tin ? kHC * 4 : 0);
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(Lg), vc, lane < 16 ? lane * 4 : (int)kOob, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(zp), vp, lane < 4 ? lane * 4 : (int)kOob, 0, 0);
-        }
-        lds_barrier(); // B2: partial dots and the pre weights of step cu are in LDS
-        if (tid == 0) {
-            *bf = 0;
-        }
-
-        // the record of step i: this thread's chunk(s), three slice sums over the waves each
-        // (waves holding no chunk skip it)
+        // B3': the record of step i - 1: this thread's chunk(s), three slice sums over the waves
+        // each (waves holding no chunk skip it)
         if (w * kWave < kQChunks) {
-            const uint32_t tag = coop_tag(key, i * kQGroups + x);
-            const uint32_t q = (uint32_t)qi;
+            const float *rp = red + ((i - 1) & 1) * (W * kQTok * kQRedStride);
+            const uint32_t tag = coop_tag(key, (i - 1) * kQGroups + x);
+            const uint32_t q = (uint32_t)qim1;
 #pragma unroll
             for (int rs = 0; rs < kRS; ++rs) {
                 float v[3];
@@ -605,38 +643,26 @@ __global__ __launch_bounds__(W * 64) void pre_coop_kernel(CoopArgs a)
                     float acc = 0.0f;
 #pragma unroll
                     for (int ww = 0; ww < W; ++ww) {
-                        acc += red[ww * (kQTok * kQRedStride) + rc_off[rs][e]];
+                        acc += rp[ww * (kQTok * kQRedStride) + rc_off[rs][e]];
                     }
                     v[e] = (rc_valid[rs] >> e) & 1 ? acc : 0.0f;
                 }
-                const uint32_t o = p_ok && rc_base[rs] != kOob ? rc_base[rs] + q * rc_qstride[rs] : kOob;
+                const uint32_t o = pm1_ok && rc_base[rs] != kOob ? rc_base[rs] + q * rc_qstride[rs] : kOob;
                 const u32x4 chunk = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), tag};
                 __builtin_amdgcn_raw_buffer_store_b128(chunk, vrec, (int)o, 0, 0);
             }
         }
-
-        // step cu's slot (this thread's token prow and piece, 4 streams) and pre weights into
-        // registers for the next iteration's collapse; the slot is free once B1 has passed
+        // B4': the records of step X + 1
+        load_recs(X + 1, qx1, ru, rd);
+        // B5': step X's slot into registers for the next iteration's collapse
         {
-            const unsigned char *cs = ring + rcs * kSlotB + prow * kTokB + piece * 16;
+            const unsigned char *cs = ring + rx * kSlotB + prow * kTokB + piece * 16;
 #pragma unroll
             for (int st = 0; st < kHC; ++st) {
                 hold[st] = *reinterpret_cast<const u32x4 *>(cs + st * kRowB);
             }
-#pragma unroll
-            for (int k = 0; k < kHC; ++k) {
-                holdp[k] = prel[prow * kHC + k];
-            }
         }
-        // the optional pre output of this workgroup's token (the auxiliary wave's lanes 0..3;
-        // every wave issues the store, elsewhere into an empty view)
-        {
-            const bool tin = designated(cu) && tdz < T && a.pre != nullptr && w == kAux;
-            const __amdgpu_buffer_rsrc_t vq =
-                buf_view_uniform(tin ? (const void *)(a.pre + (size_t)tdz * kHC) : (const void *)a.y, tin ? kHC * 4 : 0);
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(prel[td * kHC + (lane & 3)]), vq,
-                                                  lane < 4 ? lane * 4 : (int)kOob, 0, 0);
-        }
+        lds_barrier(); // B2: partial sums of step i, the slice sums of step X, slot X read
     };
 
     // Two warm-up iterations (steps -2 and -1: every memory operation out of range) load
@@ -650,14 +676,12 @@ __global__ __launch_bounds__(W * 64) void pre_coop_kernel(CoopArgs a)
         cfA[k] = 0.0f;
         cfB[k] = 0.0f;
     }
-    float holdp[kHC];
     u32x4 ru[kUR], rd[kDR];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         bufA[k] = u32x4{0u, 0u, 0u, 0u};
         bufB[k] = u32x4{0u, 0u, 0u, 0u};
         hold[k] = u32x4{0u, 0u, 0u, 0u};
-        holdp[k] = 0.0f;
     }
 #pragma unroll
     for (int r = 0; r < kUR; ++r) {
@@ -670,6 +694,9 @@ __global__ __launch_bounds__(W * 64) void pre_coop_kernel(CoopArgs a)
     if (tid < 2) {
         badf[tid] = 0;
     }
+    if (tid < kQTok * kHC) {
+        prel[tid] = 0.0f;
+    }
     if constexpr (kPost) {
         // the coefficients of step 0 (the loop stages those of step j + 1 in iteration j)
         float c0[kCf];
@@ -680,10 +707,10 @@ __global__ __launch_bounds__(W * 64) void pre_coop_kernel(CoopArgs a)
     const int iend = nst + L + 1; // the last collapse (of step nst - 1) is in iteration nst + L
     int ri = R - 2, qi = RR - 2;  // step -2
     for (int i = -2; i < iend; i += 2) {
-        iteration(i, ri, qi, bufA, xA, cfA, ru, rd, hold, holdp);
+        iteration(i, ri, qi, bufA, xA, cfA, ru, rd, hold);
         ri = wrap(ri + 1, R);
         qi = wrap(qi + 1, RR);
-        iteration(i + 1, ri, qi, bufB, xB, cfB, ru, rd, hold, holdp);
+        iteration(i + 1, ri, qi, bufB, xB, cfB, ru, rd, hold);
         ri = wrap(ri + 1, R);
         qi = wrap(qi + 1, RR);
     }
@@ -731,13 +758,11 @@ CoopCfg coop_config(int64_t H)
     k.W = coop_waves(H);
     const size_t slot = (size_t)kQTok * (256 * k.W + 16);
     // the waves' partials, sums, dsum, prel, flags, dummy, and the post-map's coefficients
-    const size_t scratch = (size_t)k.W * kQTok * kQRedStride * 4 + (96 + 32 + 64 + 4 + 64 + 2 * kCoefVals) * 4;
-    const size_t lds_max = 160 * 1024;
+    const size_t scratch = (size_t)2 * k.W * kQTok * red_stride(k.W) * 4 + (96 + 32 + 64 + 4 + 64 + 2 * kCoefVals) * 4;
+    // a record of step j is stored in iteration j + 1 and loaded in iteration j + L - 1, so the
+    // lag must be at least 3; a ring of L + 1 slots fits at every W (161,296 bytes at W = 8)
     k.L = 3;
-    while (k.L > 1 && (size_t)(k.L + 2) * slot + scratch > lds_max) {
-        --k.L;
-    }
-    k.R = k.L + 2;
+    k.R = k.L + 1;
     k.RR = 2 * k.L + 2;
     k.lds = (size_t)k.R * slot + scratch;
     return k;
