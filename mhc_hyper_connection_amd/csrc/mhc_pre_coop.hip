@@ -127,7 +127,10 @@ __device__ __forceinline__ float half_sum(float v)
     v += dpp_perm<0x4E>(v);  // quad_perm [2,3,0,1]
     v += dpp_perm<0x141>(v); // row_half_mirror
     v += dpp_perm<0x140>(v); // row_mirror
-    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+    // rows 1 and 3 add the last lane of rows 0 and 2 (row_bcast:15; rows 0 and 2 are not
+    // written); the s_nop covers the wait a DPP read needs after a VALU write of its source
+    asm volatile("s_nop 1\n\tv_add_f32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf" : "+v"(v));
+    return v;
 }
 constexpr int kHalfSumLane = 16; // the lane of each half-wave (mod 32) that holds its sum
 
@@ -197,8 +200,8 @@ __global__ __launch_bounds__(W * 64) void pre_coop_kernel(CoopArgs a)
     // bf16 terms in the MFMA B layout (lane (g, c): k = hb*32 + 8g .. +8 of stream i).  Column
     // tile 0 holds rows 0..15 (lane c: row c), one operand per term.  Rows 16..23 take two
     // operands: lanes c < 8 hold the hi term of row 16 + c and lanes c >= 8 the mid term of
-    // row 8 + c in the first, lanes c < 8 the lo term of row 16 + c in the second; the
-    // columns c and c + 8 of the first are added after the products.
+    // row 8 + c in the first, lanes c < 8 the lo term of row 16 + c in the second; both
+    // products go into one accumulator, whose columns c and c + 8 are added afterwards.
     const int hb = s * W + w;
     u32x4 b0[kHC][3], b1[kHC][2];
     {
@@ -568,12 +571,10 @@ __global__ __launch_bounds__(W * 64) void pre_coop_kernel(CoopArgs a)
             for (int st = 0; st < kHC; ++st) {
                 A[st] = *reinterpret_cast<const u32x4 *>(slot + c * kTokB + st * kRowB + (4 * w + g) * 16);
             }
-            f32x4 acc0[2], acc1[2], acc2[2];
+            f32x4 acc0[2], acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 acc0[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-                acc1[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-                acc2[u] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
             float sq = 0.0f;
 #pragma unroll
@@ -584,8 +585,8 @@ __global__ __launch_bounds__(W * 64) void pre_coop_kernel(CoopArgs a)
                 for (int t3 = 0; t3 < 3; ++t3) {
                     acc0[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ab, __builtin_bit_cast(bf16x8, b0[st][t3]), acc0[u], 0, 0, 0);
                 }
-                acc1[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ab, __builtin_bit_cast(bf16x8, b1[st][0]), acc1[u], 0, 0, 0);
-                acc2[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ab, __builtin_bit_cast(bf16x8, b1[st][1]), acc2[u], 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ab, __builtin_bit_cast(bf16x8, b1[st][0]), acc1, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ab, __builtin_bit_cast(bf16x8, b1[st][1]), acc1, 0, 0, 0);
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     // a scalar copy first: hipcc (clang 22) miscompiles __builtin_bit_cast applied
@@ -613,9 +614,8 @@ __global__ __launch_bounds__(W * 64) void pre_coop_kernel(CoopArgs a)
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const float d0 = acc0[0][k] + acc0[1][k];
-                // rows 16..23: (hi + mid) + lo, the mid partial coming from column c + 8
-                const float p1 = acc1[0][k] + acc1[1][k];
-                const float d1 = (p1 + dpp_row_ror8(p1)) + (acc2[0][k] + acc2[1][k]);
+                // rows 16..23: hi + lo in column c (one chain), the mid partial from column c + 8
+                const float d1 = acc1[k] + dpp_row_ror8(acc1[k]);
                 rw[(4 * g + k) * kQRedStride + c] = d0;
                 *(c < 8 ? rw + (4 * g + k) * kQRedStride + 16 + c : dummy + lane) = d1;
             }
