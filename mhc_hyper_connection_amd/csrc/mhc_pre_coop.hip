@@ -204,30 +204,6 @@ __global__ __launch_bounds__(W * 64) void pre_coop_kernel(CoopArgs a)
     // products go into one accumulator, whose columns c and c + 8 are added afterwards.
     const int hb = s * W + w;
     u32x4 b0[kHC][3], b1[kHC][2];
-    {
-        const __amdgpu_buffer_rsrc_t vw =
-            buf_view_uniform(a.hc_fn, (uint32_t)((size_t)a.fn_rows * kHC * H * sizeof(WT)));
-        const int h = hb * 32 + 8 * g;
-        const bool hok = hb < a.nhb && h < H;
-        const WT *wt = reinterpret_cast<const WT *>(a.hc_fn);
-        const int r1 = 16 + (c & 7);
-#pragma unroll
-        for (int i = 0; i < kHC; ++i) {
-            float v0[8], v1[8];
-            const uint32_t i0 = hok ? (uint32_t)c * kHC * H + (uint32_t)i * H + h : kOob / 4;
-            const uint32_t i1 = hok ? (uint32_t)r1 * kHC * H + (uint32_t)i * H + h : kOob / 4;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                v0[e] = weight_elem(wt, i0 + e, vw);
-                v1[e] = weight_elem(wt, i1 + e, vw);
-            }
-            split3x8(v0, b0[i][0], b0[i][1], b0[i][2]);
-            u32x4 hi, mid, lo;
-            split3x8(v1, hi, mid, lo);
-            b1[i][0] = c < 8 ? hi : mid;
-            b1[i][1] = c < 8 ? lo : u32x4{0u, 0u, 0u, 0u};
-        }
-    }
     // hc_base per lane: the pre entry lane / 16; with e = lane mod 16 the comb entry e and the
     // post entry e mod 4 (the designated token's row of lanes)
     const float bpre = a.hc_base[lane >> 4]; // lane = 16 k + token computes pre weight k
@@ -665,9 +641,8 @@ __global__ __launch_bounds__(W * 64) void pre_coop_kernel(CoopArgs a)
         lds_barrier(); // B2: partial sums of step i, the slice sums of step X, slot X read
     };
 
-    // Two warm-up iterations (steps -2 and -1: every memory operation out of range) load
-    // steps 0 and 1, so every trip of the loop, the first included, issues the same
-    // operations and the compiler's wait counts stay exact.
+    // Every trip of the loop issues the same memory operations (empty views stand for steps
+    // outside the range), so that the compiler's in-order wait counts stay exact.
     u32x4 bufA[4], bufB[4], hold[kHC];
     u32x4 xA = {0u, 0u, 0u, 0u}, xB = {0u, 0u, 0u, 0u};
     float cfA[kCf], cfB[kCf];
@@ -704,9 +679,46 @@ __global__ __launch_bounds__(W * 64) void pre_coop_kernel(CoopArgs a)
         store_coef(0, c0);
     }
     __syncthreads();
+    // The loads of steps 0 and 1 (what iterations -2 and -1 would issue: every other memory
+    // operation of those iterations is out of range) go out before the weights, so that their
+    // latency and the weights' overlap; the loop starts at step 0.
+    if constexpr (kPost) {
+        load_coef(1, cfA);
+        xA = load_x(0);
+    }
+    load_step(0, bufA);
+    if constexpr (kPost) {
+        load_coef(2, cfB);
+        xB = load_x(1);
+    }
+    load_step(1, bufB);
+    {
+        const __amdgpu_buffer_rsrc_t vw =
+            buf_view_uniform(a.hc_fn, (uint32_t)((size_t)a.fn_rows * kHC * H * sizeof(WT)));
+        const int h = hb * 32 + 8 * g;
+        const bool hok = hb < a.nhb && h < H;
+        const WT *wt = reinterpret_cast<const WT *>(a.hc_fn);
+        const int r1 = 16 + (c & 7);
+#pragma unroll
+        for (int i = 0; i < kHC; ++i) {
+            float v0[8], v1[8];
+            const uint32_t i0 = hok ? (uint32_t)c * kHC * H + (uint32_t)i * H + h : kOob / 4;
+            const uint32_t i1 = hok ? (uint32_t)r1 * kHC * H + (uint32_t)i * H + h : kOob / 4;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                v0[e] = weight_elem(wt, i0 + e, vw);
+                v1[e] = weight_elem(wt, i1 + e, vw);
+            }
+            split3x8(v0, b0[i][0], b0[i][1], b0[i][2]);
+            u32x4 hi, mid, lo;
+            split3x8(v1, hi, mid, lo);
+            b1[i][0] = c < 8 ? hi : mid;
+            b1[i][1] = c < 8 ? lo : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
     const int iend = nst + L + 1; // the last collapse (of step nst - 1) is in iteration nst + L
-    int ri = R - 2, qi = RR - 2;  // step -2
-    for (int i = -2; i < iend; i += 2) {
+    int ri = 0, qi = 0;           // step 0
+    for (int i = 0; i < iend; i += 2) {
         iteration(i, ri, qi, bufA, xA, cfA, ru, rd, hold);
         ri = wrap(ri + 1, R);
         qi = wrap(qi + 1, RR);
