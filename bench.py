@@ -34,6 +34,12 @@ def pre_one_read(T: int, H: int) -> bool:
     return H % 8 == 0 and T >= 1024 and 1024 < H <= 8192
 
 
+def pre_small_batch(T: int, H: int) -> bool:
+    """Whether the library's pre-map takes its one-launch small-batch form (16-byte rows,
+    1 <= T <= 64, H <= 8192, on a 256-CU gfx950)."""
+    return H % 8 == 0 and 1 <= T <= 64 and H <= 8192
+
+
 def sinkhorn_valu_per_wave(iters: int) -> int:
     """VALU instructions one wave of sinkhorn_kernel issues for its 64 matrices, counted
     in the compiled gfx950 code (iters >= 1): 141 outside the iteration loop (loads,
@@ -465,9 +471,11 @@ def main():
     # slice sums (above 64 tokens; below, the collapse sums the slices) and the collapse
     sums = [] if T <= 64 else ["pre_mixsum_kernel"]
     one_read = pre_one_read(T, H)
-    pre_kernels = "pre_coop_kernel" if one_read else "+".join(
+    small = pre_small_batch(T, H)
+    pre_kernels = "pre_coop_kernel" if one_read else "pre_decode_kernel" if small else "+".join(
         ([] if args.presplit else ["pre_prep_kernel"]) + [proj] + sums + [col])
-    split_kernels = "pre_coop_kernel" if one_read else "+".join(["pre_prep_kernel", proj] + sums + [col])
+    split_kernels = "pre_coop_kernel" if one_read else "pre_decode_kernel" if small else "+".join(
+        ["pre_prep_kernel", proj] + sums + [col])
     if "pre_ms" in breakdown:
         calls["mhc_pre_fused"] = (pre_kernels, breakdown["pre_ms"], pre_b)
     if "post_ms" in breakdown:
@@ -543,10 +551,12 @@ def main():
 
     # Sanity figures: the launch floor of the step's kernel count (one-element fills,
     # launched the same way), and what a plain elementwise copy sustains here.
-    npre = 1 if pre_one_read(T, H) else 2 + (0 if args.presplit else 1) + (0 if T <= 64 else 1)
+    one_launch = pre_one_read(T, H) or pre_small_batch(T, H)
+    npre = 1 if one_launch else 2 + (0 if args.presplit else 1) + (0 if T <= 64 else 1)
     npre32 = 2 + (0 if T <= 64 else 1)
     nker = {"all": npre + 1, "pre": npre, "post": 1, "post_project": 3, "fused": 4,
-            "post_pre": 1 if pre_one_read(T, H) else 1 + npre + (1 if args.presplit else 0), "f32": npre32 + 1,
+            "post_pre": 1 if pre_one_read(T, H) else 1 + npre + (1 if args.presplit and not one_launch else 0),
+            "f32": npre32 + 1,
             "pre_f32": npre32, "post_f32": 1}.get(args.only)
     launch_floor_ms = None
     if nker:

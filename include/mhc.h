@@ -122,7 +122,10 @@ mhc_status mhc_sinkhorn(const float *logits, float *out, int64_t n_mats, int32_t
  * metrale GLM-5 mHC page (Glm5NextMhcSiteWeights); its contents on entry are ignored.  The one-read form (16-byte rows, 1024 < H <= 8192,
  * T >= 1024, on a 256-CU gfx950) keeps a ring of exchange records: 16-byte chunks of
  * partial sums for a few 16-token steps of every workgroup, at most 4.6 MB and
- * independent of T.  The two-pass form keeps the projection weights split into bf16
+ * independent of T.  The small-batch form (16-byte rows, 1 <= T <= 64, H <= 8192, on a
+ * 256-CU gfx950) keeps 286,720 bytes of exchange records (16-byte chunks of one call's
+ * partial sums) behind the first mhc_pre_split_bytes(H) bytes, which it leaves untouched.
+ * The two-pass form keeps the projection weights split into bf16
  * terms in MFMA operand order (576 * H bytes, rounded up), the per-slice partial sums of
  * the projection (100 bytes per token per 128-wide slice of H) and the per-token totals
  * (128 bytes per token); tokens beyond 2^31 bytes of partial sums are processed in
@@ -178,10 +181,12 @@ mhc_status mhc_pre_fused(const uint16_t *res, const float *hc_fn, const float *h
  * split of this hc_fn: mhc_pre_split_weights ran on it, ordered before this call (same
  * stream or synchronised), and neither hc_fn nor the workspace's first
  * mhc_pre_split_bytes(H) bytes changed since (mhc_pre_fused calls on the same workspace
- * rewrite them with the same values, so they keep it valid).  The two-pass form then skips
- * its weight-split launch; the one-read form (16-byte rows, T >= 1024, 1024 < H <= 8192)
- * splits in-kernel and ignores the stored split.  Results equal mhc_pre_fused's bit for
- * bit; a stale split gives the results of the weights it was made from.
+ * rewrite them with the same values or leave them alone, so they keep it valid).  The
+ * two-pass form then skips its weight-split launch; the one-read form (16-byte rows,
+ * T >= 1024, 1024 < H <= 8192) splits in-kernel and the small-batch form (16-byte rows,
+ * T <= 64, H <= 8192) reads hc_fn as it is, both ignoring the stored split.  Results equal
+ * mhc_pre_fused's bit for bit; a stale split gives the two-pass form the results of the
+ * weights it was made from.
  */
 size_t mhc_pre_split_bytes(int64_t H);
 mhc_status mhc_pre_split_weights(const float *hc_fn, int64_t H, void *workspace, size_t workspace_bytes,

@@ -15,7 +15,7 @@ ROOT = PKG.parent
 CSRC = PKG / "csrc"
 BUILD = PKG / "_build"
 LIB = PKG / "libmhc.so"
-SOURCES = ["mhc_abi.hip", "mhc_post.hip", "mhc_sinkhorn.hip", "mhc_pre.hip", "mhc_pre_dots.hip", "mhc_backward.hip", "mhc_head.hip", "mhc_pre_coop.hip"]
+SOURCES = ["mhc_abi.hip", "mhc_post.hip", "mhc_sinkhorn.hip", "mhc_pre.hip", "mhc_pre_dots.hip", "mhc_backward.hip", "mhc_head.hip", "mhc_pre_coop.hip", "mhc_pre_decode.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

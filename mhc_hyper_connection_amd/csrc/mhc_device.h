@@ -280,4 +280,47 @@ __device__ __forceinline__ void sum_split_partials(const float *dot_mix, const f
     __syncthreads();
 }
 
+// ---- cross-workgroup exchange through an XCD's L2 (the one-read and small-batch pre-maps)
+
+// A buffer offset that lies past every view: loads read zero, stores are dropped.
+constexpr uint32_t kOob = 0x80000000u;
+
+extern "C" __device__ uint64_t mhc_coop_dispatch_id() __asm("llvm.amdgcn.dispatch.id");
+
+// Tags of exchange records: a key from the dispatch id (distinct for every launch), mixed
+// with a record set's index.
+__device__ __forceinline__ uint32_t coop_key()
+{
+    uint64_t z = mhc_coop_dispatch_id() + 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(z >> 32));
+}
+// Distinct steps of one call get distinct tags (an odd multiplier is a bijection).
+__device__ __forceinline__ uint32_t coop_tag(uint32_t key, int gs) { return key ^ ((uint32_t)gs * 0x85EBCA6Bu + 1u); }
+
+// Sum of v over the 32 lanes of each half-wave, on DPP moves: within each quad (lanes
+// xor 1, 2), the two quads of each 8-lane half row (mirror), the two halves of each
+// 16-lane row (mirror), then row 0 into row 1 and row 2 into row 3 (row_bcast:15).  The
+// total of lanes 0..31 lands in lanes 16..31 and that of lanes 32..63 in lanes 48..63;
+// the order of the additions is fixed.
+__device__ __forceinline__ float half_sum(float v)
+{
+    v += dpp_perm<0xB1>(v);  // quad_perm [1,0,3,2]
+    v += dpp_perm<0x4E>(v);  // quad_perm [2,3,0,1]
+    v += dpp_perm<0x141>(v); // row_half_mirror
+    v += dpp_perm<0x140>(v); // row_mirror
+    // rows 1 and 3 add the last lane of rows 0 and 2 (row_bcast:15; rows 0 and 2 are not
+    // written); the s_nop covers the wait a DPP read needs after a VALU write of its source
+    asm volatile("s_nop 1\n\tv_add_f32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf" : "+v"(v));
+    return v;
+}
+constexpr int kHalfSumLane = 16; // the lane of each half-wave (mod 32) that holds its sum
+
+// rstd and sigmoid on the hardware reciprocal square root and reciprocal (1 ulp each, far
+// inside the 1e-5 tolerance of the mixes), for the exchange kernels' per-token work.
+__device__ __forceinline__ float rstd_of(float S, float inv_k, float eps) { return __builtin_amdgcn_rsqf(fmaf(S, inv_k, eps)); }
+__device__ __forceinline__ float sigmoid_rcp(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
+
 } // namespace mhc

@@ -110,6 +110,25 @@ hipError_t launch_post_pre_coop(const uint16_t *x, const uint16_t *res, const fl
 // step's records before its outputs become NaN (negative: the default 2^14) and a value
 // mixed into the tags readers expect (0 in normal use).
 void set_exchange_test_hooks(int max_retry, uint32_t tag_skew);
+// What those hooks hold now, and whether the current device runs the exchange kernels
+// (256 CUs on gfx950: one workgroup per CU, 32 on each XCD).
+int exchange_max_retry();
+uint32_t exchange_tag_skew();
+bool exchange_device_ok();
+
+// The pre-map for small batches in one launch (mhc_pre_decode.hip): on each XCD a group of
+// 32 workgroups splits K over the group's ceil(T / 8) tokens and exchanges partial sums
+// through the XCD's L2.  Usable for 16-byte rows, 1 <= T <= 64 and H <= 8192 on a 256-CU
+// gfx950; the weights are read as given (fp32 or bf16), never split.  Its exchange records
+// sit at pre_split_bytes(H) in the workspace, behind the place of a weight split, which it
+// leaves as it is; pre_decode_workspace_bytes(H) bytes in all.
+bool pre_decode_shape_ok(int64_t T, int64_t H);
+bool pre_decode_usable(int64_t T, int64_t H, bool vec8);
+size_t pre_decode_workspace_bytes(int64_t H);
+hipError_t launch_pre_decode(const uint16_t *res, const void *hc_fn, bool fn_bf16, int fn_rows,
+                             const float *hc_scale, const float *hc_base, int64_t T, int64_t H, float rms_eps,
+                             float pre_eps, float sinkhorn_eps, float post_mult, int iters, bool head, uint16_t *y,
+                             float *post, float *comb, float *pre, void *workspace, hipStream_t stream);
 // Workspace of the pre-map entry points: enough for either form.
 size_t pre_fused_workspace_bytes(int64_t T, int64_t H);
 // Workspace of the form a call with these sizes and 16-byte rows (vec8) or not takes on the

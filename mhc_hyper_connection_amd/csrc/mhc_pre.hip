@@ -1452,11 +1452,15 @@ size_t pre_fused_workspace_bytes(int64_t T, int64_t H)
 {
     const size_t two_pass = pre_geometry(T, H).total_bytes;
     const size_t coop = pre_coop_shape_ok(T, H) ? pre_coop_workspace_bytes(H) : 0;
-    return coop > two_pass ? coop : two_pass;
+    const size_t decode = pre_decode_shape_ok(T, H) ? pre_decode_workspace_bytes(H) : 0;
+    return std::max(two_pass, std::max(coop, decode));
 }
 
 size_t pre_path_workspace_bytes(int64_t T, int64_t H, bool vec8)
 {
+    if (pre_decode_usable(T, H, vec8)) {
+        return pre_decode_workspace_bytes(H);
+    }
     return pre_coop_usable(T, H, vec8) ? pre_coop_workspace_bytes(H) : pre_geometry(T, H).total_bytes;
 }
 
@@ -1593,6 +1597,10 @@ hipError_t launch_pre(const uint16_t *res, const void *hc_fn, bool fn_bf16, int 
                       float post_mult, int iters, bool head, uint16_t *y, float *post, float *comb, float *pre,
                       void *workspace, hipStream_t stream, bool vec8, bool presplit)
 {
+    if (pre_decode_usable(g.T, g.H, vec8)) { // small batches: one launch, weights as given
+        return launch_pre_decode(res, hc_fn, fn_bf16, fn_rows, hc_scale, hc_base, g.T, g.H, rms_eps, pre_eps,
+                                 sinkhorn_eps, post_mult, iters, head, y, post, comb, pre, workspace, stream);
+    }
     if (pre_coop_usable(g.T, g.H, vec8)) {
         return launch_pre_coop(res, hc_fn, fn_bf16, fn_rows, hc_scale, hc_base, g.T, g.H, rms_eps, pre_eps,
                                sinkhorn_eps, post_mult, iters, head, y, post, comb, pre, workspace, stream);

@@ -50,8 +50,6 @@ namespace mhc {
 
 namespace {
 
-extern "C" __device__ uint64_t mhc_coop_dispatch_id() __asm("llvm.amdgcn.dispatch.id");
-
 constexpr int kQTok = 16;                                           // tokens per step
 constexpr int kQGroups = 8;                                         // one group per XCD
 constexpr int kQSlices = 32;                                        // workgroups per group
@@ -67,7 +65,6 @@ constexpr int red_stride(int W) { return W == 8 ? 25 : 28; }
 constexpr int kQMaxRetry = 1 << 14;                                 // reloads of a step's records before giving up
 std::atomic<int> g_max_retry{kQMaxRetry};
 std::atomic<uint32_t> g_tag_skew{0};
-constexpr uint32_t kOob = 0x80000000u;
 constexpr int64_t kCoopMinTokens = 1024; // below this the pipeline's fill and drain dominate
 
 struct CoopArgs {
@@ -96,17 +93,6 @@ struct CoopArgs {
 };
 constexpr int kCoefVals = kQTok * (kHC + kHC * kHC); // post and comb of one step: 320 floats
 
-__device__ __forceinline__ uint32_t coop_key()
-{
-    uint64_t z = mhc_coop_dispatch_id() + 0x9E3779B97F4A7C15ull;
-    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
-    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
-    z ^= z >> 31;
-    return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(z >> 32));
-}
-// Distinct steps of one call get distinct tags (an odd multiplier is a bijection).
-__device__ __forceinline__ uint32_t coop_tag(uint32_t key, int gs) { return key ^ ((uint32_t)gs * 0x85EBCA6Bu + 1u); }
-
 __device__ __forceinline__ float weight_elem(const float *w, uint32_t i, __amdgpu_buffer_rsrc_t v)
 {
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(v, (int)(i * 4u), 0, 0));
@@ -115,29 +101,6 @@ __device__ __forceinline__ float weight_elem(const uint16_t *w, uint32_t i, __am
 {
     return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(v, (int)(i * 2u), 0, 0));
 }
-
-// Sum of v over the 32 lanes of each half-wave, on DPP moves: within each quad (lanes
-// xor 1, 2), the two quads of each 8-lane half row (mirror), the two halves of each
-// 16-lane row (mirror), then row 0 into row 1 and row 2 into row 3 (row_bcast:15).  The
-// total of lanes 0..31 lands in lanes 16..31 and that of lanes 32..63 in lanes 48..63;
-// the order of the additions is fixed.
-__device__ __forceinline__ float half_sum(float v)
-{
-    v += dpp_perm<0xB1>(v);  // quad_perm [1,0,3,2]
-    v += dpp_perm<0x4E>(v);  // quad_perm [2,3,0,1]
-    v += dpp_perm<0x141>(v); // row_half_mirror
-    v += dpp_perm<0x140>(v); // row_mirror
-    // rows 1 and 3 add the last lane of rows 0 and 2 (row_bcast:15; rows 0 and 2 are not
-    // written); the s_nop covers the wait a DPP read needs after a VALU write of its source
-    asm volatile("s_nop 1\n\tv_add_f32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf" : "+v"(v));
-    return v;
-}
-constexpr int kHalfSumLane = 16; // the lane of each half-wave (mod 32) that holds its sum
-
-// rstd and sigmoid on the hardware reciprocal square root and reciprocal (1 ulp each, far
-// inside the 1e-5 tolerance of the mixes); they are for this kernel's per-step path.
-__device__ __forceinline__ float rstd_of(float S, float inv_k, float eps) { return __builtin_amdgcn_rsqf(fmaf(S, inv_k, eps)); }
-__device__ __forceinline__ float sigmoid_rcp(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // Sum over the four 16-lane rows of the wave, same bits in every lane: rows (0 + 1) and
 // (2 + 3) by v_permlane16_swap, then the two halves by v_permlane32_swap.
@@ -909,6 +872,10 @@ hipError_t launch_pre_coop(const uint16_t *res, const void *hc_fn, bool fn_bf16,
     return fn_bf16 ? launch_coop_t<uint16_t, false>(a, k.W, k.lds, stream)
                    : launch_coop_t<float, false>(a, k.W, k.lds, stream);
 }
+
+bool exchange_device_ok() { return coop_device_ok(); }
+int exchange_max_retry() { return g_max_retry.load(std::memory_order_relaxed); }
+uint32_t exchange_tag_skew() { return g_tag_skew.load(std::memory_order_relaxed); }
 
 void set_exchange_test_hooks(int max_retry, uint32_t tag_skew)
 {

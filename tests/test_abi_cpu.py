@@ -89,8 +89,11 @@ def test_pre_validation_invalid(kw):
 
 def test_pre_validation_workspace():
     lib = mhc.lib()
-    need = mhc.mhc_pre_fused_workspace_bytes(16, 256)
-    assert _pre(lib, wsb=need - 1) == mhc.MHC_ERROR_WORKSPACE
+    # every form needs more than the weight split's place: the two-pass form keeps partial
+    # sums behind it, the small-batch form its exchange records (which of the two a call
+    # takes depends on the device, so the bound tested is below both)
+    assert _pre(lib, wsb=mhc.mhc_pre_split_bytes(256)) == mhc.MHC_ERROR_WORKSPACE
+    assert mhc.mhc_pre_fused_workspace_bytes(16, 256) > mhc.mhc_pre_split_bytes(256)
     assert _pre(lib, ws=None) == mhc.MHC_ERROR_WORKSPACE
     assert _pre(lib, ws=ctypes.c_void_p(0xC000000 + 8)) == mhc.MHC_ERROR_WORKSPACE  # not 256-byte aligned
     assert _pre(lib, T=0, res=None, y=None, ws=None) == mhc.MHC_SUCCESS  # empty: no-op
@@ -291,8 +294,8 @@ def test_head_validation_invalid(kw):
 
 def test_head_workspace_and_bf16_pre_validation():
     lib = mhc.lib()
-    need = mhc.mhc_pre_fused_workspace_bytes(16, 256)
-    assert _head(lib, wsb=need - 1) == mhc.MHC_ERROR_WORKSPACE
+    small = mhc.mhc_pre_split_bytes(256)  # below what either small-batch form needs
+    assert _head(lib, wsb=small) == mhc.MHC_ERROR_WORKSPACE
     assert _head(lib, ws=None) == mhc.MHC_ERROR_WORKSPACE
     assert _head(lib, T=0, res=None, y=None, ws=None) == mhc.MHC_SUCCESS
     # mhc_pre_fused_bf16 shares mhc_pre_fused's checks; bf16 weights are [24, 4H] x 2 bytes
@@ -303,7 +306,7 @@ def test_head_workspace_and_bf16_pre_validation():
                                            ctypes.c_void_p(0xC000000), k.get("wsb", 1 << 30), NULL)
     assert f(it=0) == mhc.MHC_ERROR_INVALID_VALUE
     assert f(y=0x4000000 + 24 * 1024 * 2 - 64) == mhc.MHC_ERROR_INVALID_VALUE   # y overlaps the bf16 weights
-    assert f(wsb=need - 1) == mhc.MHC_ERROR_WORKSPACE
+    assert f(wsb=small) == mhc.MHC_ERROR_WORKSPACE
 
 
 def _fbwd(lib, **kw):
@@ -335,7 +338,8 @@ def test_pre_fused_backward_validation_invalid(kw):
 def test_pre_fused_backward_workspace():
     lib = mhc.lib()
     need = mhc.mhc_pre_fused_backward_workspace_bytes(8, 64)
-    assert need > mhc.mhc_pre_fused_workspace_bytes(8, 64) and need % 256 == 0
+    # the weight split, the recompute's partial sums and the reverse's own sums
+    assert need > mhc.mhc_pre_split_bytes(64) and need % 256 == 0
     assert mhc.mhc_pre_fused_backward_workspace_bytes(8, 60) == 0
     assert mhc.mhc_pre_fused_backward_workspace_bytes(0, 64) == 0
     assert _fbwd(lib, wsb=need - 1) == mhc.MHC_ERROR_WORKSPACE
@@ -368,9 +372,11 @@ def test_post_project_workspace():
     need = mhc.mhc_post_project_workspace_bytes(8, 64)
     assert need > 0 and need % 256 == 0
     assert mhc.mhc_post_project_workspace_bytes(8, 60) == 0 and mhc.mhc_post_project_workspace_bytes(0, 64) == 0
-    # laid out as the pre-map's: the split weights and one token chunk's partial records
+    # laid out as the two-pass pre-map's: the split weights and one token chunk's partial
+    # records (the pre-map's own size also covers its other forms, so it is never smaller)
     for T, H in ((8, 64), (3000, 1000), (8192, 7168)):
-        assert mhc.mhc_post_project_workspace_bytes(T, H) == mhc.mhc_pre_fused_workspace_bytes(T, H)
+        assert mhc.mhc_post_project_workspace_bytes(T, H) <= mhc.mhc_pre_fused_workspace_bytes(T, H)
+    assert mhc.mhc_post_project_workspace_bytes(3000, 1000) == mhc.mhc_pre_fused_workspace_bytes(3000, 1000)
     assert _pproj(lib, wsb=need - 1) == mhc.MHC_ERROR_WORKSPACE
     assert _pproj(lib, ws=None) == mhc.MHC_ERROR_WORKSPACE
     assert _pproj(lib, ws=0x9000000 + 16) == mhc.MHC_ERROR_WORKSPACE
@@ -405,8 +411,7 @@ def test_post_pre_fused_validation_invalid(kw):
 
 def test_post_pre_fused_workspace():
     lib = mhc.lib()
-    need = mhc.mhc_pre_fused_workspace_bytes(8, 64)
-    assert _postpre(lib, wsb=need - 1) == mhc.MHC_ERROR_WORKSPACE
+    assert _postpre(lib, wsb=mhc.mhc_pre_split_bytes(64)) == mhc.MHC_ERROR_WORKSPACE  # below every form's need
     assert _postpre(lib, ws=None) == mhc.MHC_ERROR_WORKSPACE
     assert _postpre(lib, ws=0x9000000 + 16) == mhc.MHC_ERROR_WORKSPACE
     # T == 0: nothing to do, no pointer is looked at

@@ -1,6 +1,8 @@
 """GPU parity of the pre-map with its weight split done ahead of the calls
 (mhc_pre_split_weights + mhc_pre_fused_presplit) against mhc_pre_fused, and of the
-small-batch collapse that sums the slices' records itself (T <= 64 per chunk).
+two-pass form's collapse that sums the slices' records itself (T <= 64 per chunk), which
+batches of at most 64 tokens take when the one-launch small-batch form does not apply
+(rows not 16-byte, or H > 8192).
 
 mhc_pre_fused_presplit must equal mhc_pre_fused bit for bit on a workspace holding the
 split of the same weights, over calls in a row and after a plain mhc_pre_fused call on the
@@ -36,7 +38,7 @@ def _host(out):
 
 
 @pytest.mark.parametrize("T,H", [(1, 7168), (32, 7168), (63, 4096), (64, 4096), (65, 4096), (300, 1000),
-                                 (64, 8), (1100, 4096)])
+                                 (64, 8), (1100, 4096), (33, 1000), (32, 8200)])
 def test_presplit_equals_pre_fused(T, H):
     mhc = _mhc()
     inp = layer_inputs(T, H, cfg=910 + H % 37)
@@ -57,10 +59,11 @@ def test_presplit_equals_pre_fused(T, H):
 
 
 def test_presplit_uses_the_stored_split():
-    """The two-pass form reads the stored split, not hc_fn: a split of other weights gives
-    the results of those weights (the documented contract for a stale split)."""
+    """The two-pass form (here T = 100: above the small-batch form, below the one-read
+    form) reads the stored split, not hc_fn: a split of other weights gives the results of
+    those weights (the documented contract for a stale split)."""
     mhc = _mhc()
-    T, H = 40, 2048
+    T, H = 100, 2048
     a, b = layer_inputs(T, H, cfg=930), layer_inputs(T, H, cfg=931)
     res = to_dev_bf16(a.res)
     sc, base = to_dev_f32(a.hc_scale), to_dev_f32(a.hc_base)
