@@ -517,7 +517,8 @@ def main():
         calls["mhc_head_mean_f32"] = ("head_mean_f32s_kernel", breakdown["head_mean_f32_ms"], step_bytes)
     if "post_pre_ms" in breakdown:
         post_k = "post_vec8_kernel" if H % 8 == 0 else "post_scalar_kernel"
-        calls["mhc_post_pre_fused"] = ("pre_coop_kernel" if one_read else post_k + "+" + split_kernels,
+        calls["mhc_post_pre_fused"] = ("pre_coop_kernel" if one_read else "pre_decode_kernel" if small
+                                       else post_k + "+" + split_kernels,
                                        breakdown["post_pre_ms"], step_bytes)
     if "fused_ms" in breakdown:
         calls["mhc_pre_from_dots+mhc_post_project"] = (
@@ -555,7 +556,7 @@ def main():
     npre = 1 if one_launch else 2 + (0 if args.presplit else 1) + (0 if T <= 64 else 1)
     npre32 = 2 + (0 if T <= 64 else 1)
     nker = {"all": npre + 1, "pre": npre, "post": 1, "post_project": 3, "fused": 4,
-            "post_pre": 1 if pre_one_read(T, H) else 1 + npre + (1 if args.presplit and not one_launch else 0),
+            "post_pre": 1 if one_launch else 1 + npre + (1 if args.presplit else 0),
             "f32": npre32 + 1,
             "pre_f32": npre32, "post_f32": 1}.get(args.only)
     launch_floor_ms = None

@@ -69,10 +69,11 @@ int mhc_abi_version(void);
 const char *mhc_status_string(mhc_status status);
 
 /*
- * mhc_set_exchange_test_hooks -- test hooks of the one-read pre-map (mhc_pre_fused and
- * mhc_post_pre_fused at T >= 1024, 1024 < H <= 8192), for tests of its failure path only.
- * That form's workgroups exchange partial sums through memory, tagged with the call and
- * the step; a reader that finds a record not yet written loads it again, up to max_retry
+ * mhc_set_exchange_test_hooks -- test hooks of the one-read and small-batch pre-maps
+ * (mhc_pre_fused, its variants and mhc_post_pre_fused on 16-byte rows at T >= 1024,
+ * 1024 < H <= 8192, or at T <= 64, H <= 8192), for tests of their failure path only.
+ * Those forms' workgroups exchange partial sums through memory, tagged with the call (and
+ * the step); a reader that finds a record not yet written loads it again, up to max_retry
  * times (negative: the default, 2^14), and then gives the step NaN outputs rather than
  * wait for ever or use a stale record.  A nonzero tag_skew makes every record look
  * missing, so every step takes that path and every output of the call is NaN.  The
@@ -407,10 +408,11 @@ mhc_status mhc_post_project(const uint16_t *x, const uint16_t *res, const float 
  * bit for bit as mhc_post does, and then, over the bf16 `out`, everything mhc_pre_fused
  * computes with the next weights (hc_fn, hc_scale, hc_base):
  *     y, post_next, comb_next and optionally pre_next.
- * With 16-byte rows (H % 8 == 0; x, res, out and y 16-byte aligned), T >= 1024 and
- * 1024 < H <= 8192 on a 256-CU gfx950 this is one pass: the new streams are written to
- * `out` and kept on chip for the pre-map, so the streams are read once and written once
- * (x, res in; out, y out).  Otherwise it runs mhc_post then mhc_pre_fused on `out`.
+ * With 16-byte rows (H % 8 == 0; x, res, out and y 16-byte aligned) on a 256-CU gfx950,
+ * and either T >= 1024 and 1024 < H <= 8192 or 1 <= T <= 64 and H <= 8192, this is one
+ * pass: the new streams are written to `out` and kept on chip for the pre-map, so the
+ * streams are read once and written once (x, res in; out, y out).  Otherwise it runs
+ * mhc_post then mhc_pre_fused on `out`.
  *
  *   x [T,H] bf16; res [T,4,H] bf16; post [T,4], comb [T,4,4] fp32   the post-map's inputs
  *   hc_fn [24,4H], hc_scale [3], hc_base [24] fp32                     the next pre-map's weights

@@ -615,6 +615,11 @@ mhc_status mhc_post_pre_fused(const uint16_t *x, const uint16_t *res, const floa
                                                        pre_eps, sinkhorn_eps, post_mult, num_iters, out, y, post_next,
                                                        comb_next, pre_next, workspace, st));
     }
+    if (vec8_post && vec8_pre && mhc::pre_decode_usable(T, H, true)) {
+        return launch_status(mhc::launch_post_pre_decode(x, res, post, comb, hc_fn, hc_scale, hc_base, T, H, rms_eps,
+                                                         pre_eps, sinkhorn_eps, post_mult, num_iters, out, y,
+                                                         post_next, comb_next, pre_next, workspace, st));
+    }
     // other shapes: the post-map, then the pre-map over the streams it wrote
     hipError_t e = mhc::launch_post(x, res, post, comb, T, H, out, st, vec8_post);
     if (e != hipSuccess) {

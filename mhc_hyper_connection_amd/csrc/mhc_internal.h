@@ -129,6 +129,15 @@ hipError_t launch_pre_decode(const uint16_t *res, const void *hc_fn, bool fn_bf1
                              const float *hc_scale, const float *hc_base, int64_t T, int64_t H, float rms_eps,
                              float pre_eps, float sinkhorn_eps, float post_mult, int iters, bool head, uint16_t *y,
                              float *post, float *comb, float *pre, void *workspace, hipStream_t stream);
+// The post-map and the next pre-map in one launch of the small-batch form: the new streams
+// out = post-map(x, res, post_in, comb_in) are formed in the workgroups' tiles, written,
+// and the pre-map proceeds on them.  Same shape conditions and workspace as
+// launch_pre_decode; fp32 weights; out may equal res.
+hipError_t launch_post_pre_decode(const uint16_t *x, const uint16_t *res, const float *post_in,
+                                  const float *comb_in, const float *hc_fn, const float *hc_scale,
+                                  const float *hc_base, int64_t T, int64_t H, float rms_eps, float pre_eps,
+                                  float sinkhorn_eps, float post_mult, int iters, uint16_t *out, uint16_t *y,
+                                  float *post, float *comb, float *pre, void *workspace, hipStream_t stream);
 // Workspace of the pre-map entry points: enough for either form.
 size_t pre_fused_workspace_bytes(int64_t T, int64_t H);
 // Workspace of the form a call with these sizes and 16-byte rows (vec8) or not takes on the

@@ -68,6 +68,12 @@ struct DecArgs {
     uint32_t rec_bytes;
     int max_retry;
     uint32_t tag_skew;
+    // the post-map in front (kPost): the sublayer output x [T][H], the previous mixes post_in
+    // [T][4] and comb_in [T][4][4]; the new streams go to out [T][4][H] (which may be res) and
+    // are the streams the pre-map reads
+    const uint16_t *x;
+    const float *post_in, *comb_in;
+    uint16_t *out;
 };
 
 // Eight weights of one row from offset o (elements), fp32 or bf16, into fp32.
@@ -132,7 +138,8 @@ template <int V> __device__ __forceinline__ void wave_sums(const float (&v)[V], 
 }
 
 // P tokens per projection pass (1, 2 or 4); a group of more than 4 tokens takes two passes.
-template <typename WT, int P>
+// kPost: the post-map in front, on the workgroup's tile (mhc_post_pre_fused).
+template <typename WT, int P, bool kPost>
 __global__ __launch_bounds__(kDThreads) void pre_decode_kernel(DecArgs a)
 {
     constexpr int V = (P * kDF + 3) / 4 * 4; // a pass's values per thread, padded to a multiple of 4
@@ -141,6 +148,7 @@ __global__ __launch_bounds__(kDThreads) void pre_decode_kernel(DecArgs a)
     __shared__ float usum[3 * kDUrgMax];                        // pre dots [4][nt], then sums of squares [nt]
     __shared__ float dsum[3 * kDDef];                           // the designated token's post and comb dots
     __shared__ float dummy[kWave];
+    __shared__ float coefs[kDMaxTg * (kHC + kHC * kHC)]; // kPost: post [nt][4] at 0, comb [nt][16] at 4 kDMaxTg
     __shared__ int badf;
 
     const int tid = threadIdx.x;
@@ -173,6 +181,22 @@ __global__ __launch_bounds__(kDThreads) void pre_decode_kernel(DecArgs a)
         const uint32_t o = p < npieces && h < H ? ((uint32_t)row * (uint32_t)H + (uint32_t)h) * 2u : kOob;
         rp[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vres, (int)o, 0, 0));
     }
+    // kPost: the x piece of item tid = (t, j) of the tile (nt nch <= 256 items: one a thread),
+    // and the tokens' post and comb values into LDS
+    u32x4 xw = {0u, 0u, 0u, 0u};
+    if constexpr (kPost) {
+        const __amdgpu_buffer_rsrc_t vx =
+            buf_view_uniform(a.x + (size_t)t0 * H, (uint32_t)((size_t)nt * H * sizeof(uint16_t)));
+        const int t = tid / nch, j = tid - t * nch;
+        const int h = h0 + 8 * j;
+        const uint32_t o = tid < nt * nch && h < H ? ((uint32_t)t * (uint32_t)H + (uint32_t)h) * 2u : kOob;
+        xw = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vx, (int)o, 0, 0));
+        if (tid < kHC * nt) {
+            coefs[tid] = a.post_in[(size_t)t0 * kHC + tid];
+        } else if (tid >= 64 && tid < 64 + kHC * kHC * nt) {
+            coefs[kHC * kDMaxTg + tid - 64] = a.comb_in[(size_t)t0 * kHC * kHC + tid - 64];
+        }
+    }
     // ---- this thread's weights: rows 12 g + r of chunk c
     const int g = uniform(tid >> 7), c = tid & 127;
     const bool cval = c < kHC * nch;
@@ -199,6 +223,43 @@ __global__ __launch_bounds__(kDThreads) void pre_decode_kernel(DecArgs a)
         badf = 0;
     }
     __syncthreads();
+
+    // ---- kPost: the post-map of item (t, j): the new streams out[n] = x post[n] + sum_o res[o]
+    // comb[o][n] (mhc_post's products in its order), over the old ones in the tile and to `out`
+    if constexpr (kPost) {
+        const int t = tid / nch, j = tid - t * nch;
+        const int h = h0 + 8 * j;
+        if (tid < nt * nch && h < H) {
+            const __amdgpu_buffer_rsrc_t vo =
+                buf_view_uniform(a.out + (size_t)t0 * kHC * H, (uint32_t)((size_t)nt * kHC * H * sizeof(uint16_t)));
+            u32x4 rw[kHC];
+#pragma unroll
+            for (int o = 0; o < kHC; ++o) {
+                rw[o] = *reinterpret_cast<const u32x4 *>(tile + ((t * kHC + o) * nch + j) * 16);
+            }
+            const float *cp = coefs + t * kHC;
+            const float *cc = coefs + kHC * kDMaxTg + t * kHC * kHC;
+#pragma unroll
+            for (int n = 0; n < kHC; ++n) {
+                u32x4 nw;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float lo = bf16_lo(xw[q]) * cp[n];
+                    float hi = bf16_hi(xw[q]) * cp[n];
+#pragma unroll
+                    for (int o = 0; o < kHC; ++o) {
+                        lo = fmaf(bf16_lo(rw[o][q]), cc[o * kHC + n], lo);
+                        hi = fmaf(bf16_hi(rw[o][q]), cc[o * kHC + n], hi);
+                    }
+                    nw[q] = pack_bf16x2(lo, hi);
+                }
+                *reinterpret_cast<u32x4 *>(tile + ((t * kHC + n) * nch + j) * 16) = nw;
+                __builtin_amdgcn_raw_buffer_store_b128(nw, vo, (int)(((uint32_t)(t * kHC + n) * (uint32_t)H + (uint32_t)h) * 2u),
+                                                       0, 2);
+            }
+        }
+        __syncthreads();
+    }
 
     // ---- partial dots and sums of squares, P tokens a pass.  Rows outermost: the products
     // of row r start as soon as that row's weights have landed, beside the later rows' loads.
@@ -425,42 +486,25 @@ __global__ __launch_bounds__(kDThreads) void pre_decode_kernel(DecArgs a)
     }
 }
 
-template <typename WT>
+template <typename WT, bool kPost>
 hipError_t launch_decode_t(const DecArgs &a, hipStream_t stream)
 {
     const dim3 grid(kDGroups * kDSlices), block(kDThreads);
     if (a.Tg <= 1) {
-        pre_decode_kernel<WT, 1><<<grid, block, 0, stream>>>(a);
+        pre_decode_kernel<WT, 1, kPost><<<grid, block, 0, stream>>>(a);
     } else if (a.Tg <= 2) {
-        pre_decode_kernel<WT, 2><<<grid, block, 0, stream>>>(a);
+        pre_decode_kernel<WT, 2, kPost><<<grid, block, 0, stream>>>(a);
     } else {
-        pre_decode_kernel<WT, 4><<<grid, block, 0, stream>>>(a);
+        pre_decode_kernel<WT, 4, kPost><<<grid, block, 0, stream>>>(a);
     }
     return hipGetLastError();
 }
 
-} // namespace
-
-bool pre_decode_shape_ok(int64_t T, int64_t H)
+DecArgs decode_args(const uint16_t *res, const void *hc_fn, int fn_rows, const float *hc_scale,
+                    const float *hc_base, int64_t T, int64_t H, float rms_eps, float pre_eps, float sinkhorn_eps,
+                    float post_mult, int iters, bool head, uint16_t *y, float *post, float *comb, float *pre,
+                    void *workspace)
 {
-    return T >= 1 && T <= kDMaxTok && H >= 8 && H <= (int64_t)kDSlices * kDMaxHs && H % 8 == 0;
-}
-
-bool pre_decode_usable(int64_t T, int64_t H, bool vec8) { return vec8 && pre_decode_shape_ok(T, H) && exchange_device_ok(); }
-
-size_t pre_decode_workspace_bytes(int64_t H)
-{
-    return pre_split_bytes(H) + (size_t)kDGroups * kDGroupChunks * kDSlices * sizeof(u32x4);
-}
-
-hipError_t launch_pre_decode(const uint16_t *res, const void *hc_fn, bool fn_bf16, int fn_rows,
-                             const float *hc_scale, const float *hc_base, int64_t T, int64_t H, float rms_eps,
-                             float pre_eps, float sinkhorn_eps, float post_mult, int iters, bool head, uint16_t *y,
-                             float *post, float *comb, float *pre, void *workspace, hipStream_t stream)
-{
-    if (!pre_decode_shape_ok(T, H)) {
-        return hipErrorInvalidValue;
-    }
     DecArgs a{};
     a.res = res;
     a.hc_fn = hc_fn;
@@ -486,7 +530,52 @@ hipError_t launch_pre_decode(const uint16_t *res, const void *hc_fn, bool fn_bf1
     a.rec_bytes = (uint32_t)((size_t)kDGroups * kDGroupChunks * kDSlices * sizeof(u32x4));
     a.max_retry = exchange_max_retry();
     a.tag_skew = exchange_tag_skew();
-    return fn_bf16 ? launch_decode_t<uint16_t>(a, stream) : launch_decode_t<float>(a, stream);
+    return a;
+}
+
+} // namespace
+
+bool pre_decode_shape_ok(int64_t T, int64_t H)
+{
+    return T >= 1 && T <= kDMaxTok && H >= 8 && H <= (int64_t)kDSlices * kDMaxHs && H % 8 == 0;
+}
+
+bool pre_decode_usable(int64_t T, int64_t H, bool vec8) { return vec8 && pre_decode_shape_ok(T, H) && exchange_device_ok(); }
+
+size_t pre_decode_workspace_bytes(int64_t H)
+{
+    return pre_split_bytes(H) + (size_t)kDGroups * kDGroupChunks * kDSlices * sizeof(u32x4);
+}
+
+hipError_t launch_pre_decode(const uint16_t *res, const void *hc_fn, bool fn_bf16, int fn_rows,
+                             const float *hc_scale, const float *hc_base, int64_t T, int64_t H, float rms_eps,
+                             float pre_eps, float sinkhorn_eps, float post_mult, int iters, bool head, uint16_t *y,
+                             float *post, float *comb, float *pre, void *workspace, hipStream_t stream)
+{
+    if (!pre_decode_shape_ok(T, H)) {
+        return hipErrorInvalidValue;
+    }
+    const DecArgs a = decode_args(res, hc_fn, fn_rows, hc_scale, hc_base, T, H, rms_eps, pre_eps, sinkhorn_eps,
+                                  post_mult, iters, head, y, post, comb, pre, workspace);
+    return fn_bf16 ? launch_decode_t<uint16_t, false>(a, stream) : launch_decode_t<float, false>(a, stream);
+}
+
+hipError_t launch_post_pre_decode(const uint16_t *x, const uint16_t *res, const float *post_in,
+                                  const float *comb_in, const float *hc_fn, const float *hc_scale,
+                                  const float *hc_base, int64_t T, int64_t H, float rms_eps, float pre_eps,
+                                  float sinkhorn_eps, float post_mult, int iters, uint16_t *out, uint16_t *y,
+                                  float *post, float *comb, float *pre, void *workspace, hipStream_t stream)
+{
+    if (!pre_decode_shape_ok(T, H)) {
+        return hipErrorInvalidValue;
+    }
+    DecArgs a = decode_args(res, hc_fn, kMix, hc_scale, hc_base, T, H, rms_eps, pre_eps, sinkhorn_eps, post_mult,
+                            iters, false, y, post, comb, pre, workspace);
+    a.x = x;
+    a.post_in = post_in;
+    a.comb_in = comb_in;
+    a.out = out;
+    return launch_decode_t<float, true>(a, stream);
 }
 
 } // namespace mhc

@@ -202,3 +202,27 @@ def test_decode_missing_records_give_nan_not_a_hang():
     assert np.isnan(bf16_bits_to_f32(y)).all()
     assert np.isnan(post).all() and np.isnan(comb).all() and np.isnan(pre).all()
     check_pre_all_tokens(inp, _run(inp), "decode after the hooks are reset")
+
+
+def test_post_pre_small_batch_missing_records_keep_out_and_give_nan():
+    """mhc_post_pre_fused in the small-batch form with every record made to look missing:
+    the post-map's out does not depend on the exchange and stays exact, the pre-map's
+    outputs are NaN, and the call returns."""
+    mhc = _mhc()
+    T, H = 32, 2048
+    inp = layer_inputs(T, H, cfg=771)
+    x, res = to_dev_bf16(inp.x), to_dev_bf16(inp.res)
+    post = torch.rand(T, HC, device="cuda")
+    comb = torch.full((T, HC, HC), 0.25, device="cuda")
+    fn, sc, base = to_dev_f32(inp.hc_fn), to_dev_f32(inp.hc_scale), to_dev_f32(inp.hc_base)
+    try:
+        mhc.set_exchange_test_hooks(max_retry=2, tag_skew=1)
+        out, y, pn, cn = mhc.mhc_post_pre_fused(x, res, post, comb, fn, sc, base)
+        torch.cuda.synchronize()
+    finally:
+        mhc.set_exchange_test_hooks()
+    ref = mhc.mhc_post(x, res, post, comb)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(out), bits_of(ref))
+    assert np.isnan(bf16_bits_to_f32(bits_of(y))).all()
+    assert torch.isnan(pn).all() and torch.isnan(cn).all()

@@ -6,8 +6,9 @@ every token of y, post_next, comb_next and pre_next must match the fp64 oracle's
 over that `out` with the next weights, at the pre-map's tolerances (fp32 mixes 1e-5, bf16
 rows 2^-7 |ref| + 1e-3).  The one-pass form runs for 16-byte rows with T >= 1024 and
 1024 < H <= 8192; the shapes span its slice widths (2 to 8 waves per workgroup), ragged
-token counts and H off the 32-wide blocks.  The other shapes take the post-map and then
-the pre-map."""
+token counts and H off the 32-wide blocks.  The small-batch form (16-byte rows, T <= 64,
+H <= 8192) is one launch too: the post-map on each workgroup's tile, then the pre-map on
+it.  The other shapes take the post-map and then the pre-map."""
 import numpy as np
 import pytest
 
@@ -82,8 +83,11 @@ def _check(T, H, cfg, what, **kw):
 # (T, H): one pass (waves per workgroup 2..8, ragged T, H off the 32-wide blocks)
 ONE_PASS = [(1024, 2048), (1037, 1056), (1100, 2080), (1031, 4096), (1500, 4104), (1029, 6144), (1041, 7168),
             (1027, 7200), (1033, 8192), (2047, 5000)]
-# post-map then pre-map: too few tokens, H outside the one-pass range, rows not 16-byte multiples
-TWO_PASS = [(1, 8), (16, 256), (300, 1000), (900, 4096), (64, 7169), (1030, 1024), (1030, 8200)]
+# post-map then pre-map: H outside both one-launch ranges, rows not 16-byte multiples, or
+# between the small-batch and one-pass token counts
+TWO_PASS = [(300, 1000), (900, 4096), (64, 7169), (1030, 1024), (1030, 8200), (65, 7168), (32, 8200)]
+# the small-batch form with the post-map in front (one to eight tokens per group)
+SMALL = [(1, 8), (16, 256), (1, 7168), (5, 4096), (32, 7168), (33, 2056), (64, 8192), (17, 7200)]
 
 
 @pytest.mark.parametrize("T,H", ONE_PASS)
@@ -94,6 +98,30 @@ def test_post_pre_one_pass_every_token(T, H):
 @pytest.mark.parametrize("T,H", TWO_PASS)
 def test_post_pre_two_pass_every_token(T, H):
     _check(T, H, 990 + (T + H) % 31, "two pass")
+
+
+@pytest.mark.parametrize("T,H", SMALL)
+def test_post_pre_small_batch_every_token(T, H):
+    _check(T, H, 1040 + (T + H) % 29, "small batch")
+
+
+def test_post_pre_small_batch_in_place_and_against_two_calls():
+    """The small-batch form in place equals it out of place, and both equal mhc_post then
+    mhc_pre_fused (the same kernel's pre-map on the same streams) bit for bit."""
+    mhc = _mhc()
+    nxt, x, res, post, comb = _case(32, 7168, 1041)
+    a = _run(nxt, x, res, post, comb)
+    b = _run(nxt, x, res, post, comb, in_place=True)
+    assert np.array_equal(a[0], b[0])
+    for u, v in zip(a[1], b[1]):
+        assert np.array_equal(u, v)
+    o2 = mhc.mhc_post(to_dev_bf16(x), to_dev_bf16(res), to_dev_f32(post), to_dev_f32(comb))
+    y2, p2, c2, r2 = mhc.mhc_pre_fused(o2, to_dev_f32(nxt.hc_fn), to_dev_f32(nxt.hc_scale),
+                                       to_dev_f32(nxt.hc_base), return_pre=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(a[0], bits_of(o2))
+    for g, r, name in zip(a[1], (bits_of(y2), f32_of(p2), f32_of(c2), f32_of(r2)), ("y", "post", "comb", "pre")):
+        assert np.array_equal(g, r), name
 
 
 @pytest.mark.parametrize("kw", [dict(post_mult=2.0), dict(num_iters=3), dict(rms_eps=1e-2, pre_eps=0.0)])
