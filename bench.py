@@ -36,8 +36,8 @@ def pre_one_read(T: int, H: int) -> bool:
 
 def pre_small_batch(T: int, H: int) -> bool:
     """Whether the library's pre-map takes its one-launch small-batch form (16-byte rows,
-    1 <= T <= 64, H <= 8192, on a 256-CU gfx950)."""
-    return H % 8 == 0 and 1 <= T <= 64 and H <= 8192
+    1 <= T <= 192, H <= 8192, on a 256-CU gfx950)."""
+    return H % 8 == 0 and 1 <= T <= 192 and H <= 8192
 
 
 def sinkhorn_valu_per_wave(iters: int) -> int:

@@ -71,7 +71,7 @@ const char *mhc_status_string(mhc_status status);
 /*
  * mhc_set_exchange_test_hooks -- test hooks of the one-read and small-batch pre-maps
  * (mhc_pre_fused, its variants and mhc_post_pre_fused on 16-byte rows at T >= 1024,
- * 1024 < H <= 8192, or at T <= 64, H <= 8192), for tests of their failure path only.
+ * 1024 < H <= 8192, or at T <= 192, H <= 8192), for tests of their failure path only.
  * Those forms' workgroups exchange partial sums through memory, tagged with the call (and
  * the step); a reader that finds a record not yet written loads it again, up to max_retry
  * times (negative: the default, 2^14), and then gives the step NaN outputs rather than
@@ -123,8 +123,8 @@ mhc_status mhc_sinkhorn(const float *logits, float *out, int64_t n_mats, int32_t
  * metrale GLM-5 mHC page (Glm5NextMhcSiteWeights); its contents on entry are ignored.  The one-read form (16-byte rows, 1024 < H <= 8192,
  * T >= 1024, on a 256-CU gfx950) keeps a ring of exchange records: 16-byte chunks of
  * partial sums for a few 16-token steps of every workgroup, at most 4.6 MB and
- * independent of T.  The small-batch form (16-byte rows, 1 <= T <= 64, H <= 8192, on a
- * 256-CU gfx950) keeps 286,720 bytes of exchange records (16-byte chunks of one call's
+ * independent of T.  The small-batch form (16-byte rows, 1 <= T <= 192, H <= 8192, on a
+ * 256-CU gfx950) keeps 851,968 bytes of exchange records (16-byte chunks of one call's
  * partial sums) behind the first mhc_pre_split_bytes(H) bytes, which it leaves untouched.
  * The two-pass form keeps the projection weights split into bf16
  * terms in MFMA operand order (576 * H bytes, rounded up), the per-slice partial sums of
@@ -185,7 +185,7 @@ mhc_status mhc_pre_fused(const uint16_t *res, const float *hc_fn, const float *h
  * rewrite them with the same values or leave them alone, so they keep it valid).  The
  * two-pass form then skips its weight-split launch; the one-read form (16-byte rows,
  * T >= 1024, 1024 < H <= 8192) splits in-kernel and the small-batch form (16-byte rows,
- * T <= 64, H <= 8192) reads hc_fn as it is, both ignoring the stored split.  Results equal
+ * T <= 192, H <= 8192) reads hc_fn as it is, both ignoring the stored split.  Results equal
  * mhc_pre_fused's bit for bit; a stale split gives the two-pass form the results of the
  * weights it was made from.
  */
@@ -409,7 +409,7 @@ mhc_status mhc_post_project(const uint16_t *x, const uint16_t *res, const float 
  * computes with the next weights (hc_fn, hc_scale, hc_base):
  *     y, post_next, comb_next and optionally pre_next.
  * With 16-byte rows (H % 8 == 0; x, res, out and y 16-byte aligned) on a 256-CU gfx950,
- * and either T >= 1024 and 1024 < H <= 8192 or 1 <= T <= 64 and H <= 8192, this is one
+ * and either T >= 1024 and 1024 < H <= 8192 or 1 <= T <= 192 and H <= 8192, this is one
  * pass: the new streams are written to `out` and kept on chip for the pre-map, so the
  * streams are read once and written once (x, res in; out, y out).  Otherwise it runs
  * mhc_post then mhc_pre_fused on `out`.

@@ -118,7 +118,7 @@ bool exchange_device_ok();
 
 // The pre-map for small batches in one launch (mhc_pre_decode.hip): on each XCD a group of
 // 32 workgroups splits K over the group's ceil(T / 8) tokens and exchanges partial sums
-// through the XCD's L2.  Usable for 16-byte rows, 1 <= T <= 64 and H <= 8192 on a 256-CU
+// through the XCD's L2.  Usable for 16-byte rows, 1 <= T <= 192 and H <= 8192 on a 256-CU
 // gfx950; the weights are read as given (fp32 or bf16), never split.  Its exchange records
 // sit at pre_split_bytes(H) in the workspace, behind the place of a weight split, which it
 // leaves as it is; pre_decode_workspace_bytes(H) bytes in all.

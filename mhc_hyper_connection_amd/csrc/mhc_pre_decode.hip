@@ -1,4 +1,4 @@
-// mhc_pre_decode.hip -- the mHC pre-map for small batches (T <= 64) in one launch (gfx950).
+// mhc_pre_decode.hip -- the mHC pre-map for small batches (T <= 192) in one launch (gfx950).
 //
 // ("FlashInfer mHC 模块深度解析", section 3.4: per token the RMS statistic and the 24 x 4H
 // projection, then the pre and post weights and the Sinkhorn of the comb logits, then the
@@ -34,6 +34,8 @@
 #include "mhc_device.h"
 #include "mhc_internal.h"
 
+#include <atomic>
+
 namespace mhc {
 
 namespace {
@@ -41,18 +43,20 @@ namespace {
 constexpr int kDGroups = 8;                  // one per XCD
 constexpr int kDSlices = 32;                 // workgroups per group
 constexpr int kDThreads = 256;
-constexpr int kDMaxTok = 64;                 // tokens of a call
-constexpr int kDMaxTg = kDMaxTok / kDGroups; // tokens of a group (8)
+constexpr int kDMaxTok = 192;                // tokens of a call
+constexpr int kDMaxTg = kDMaxTok / kDGroups; // tokens of a group (24)
 constexpr int kDMaxHs = 256;                 // slice width (H <= 8192)
 constexpr int kDMaxChunks = kHC * kDMaxHs / 8; // 16-byte chunks of a slice (128)
 constexpr int kDRows = 12;                   // weight rows of a thread (two row halves)
 constexpr int kDF = kDRows + 1;              // partial values of a thread per token
-constexpr int kDUrgMax = (5 * kDMaxTg + 2) / 3;           // chunks of pre dots and sums of squares (14)
+constexpr int kDUrgMax = (5 * kDMaxTg + 2) / 3;           // chunks of pre dots and sums of squares (40)
 constexpr int kDDef = (kMix - kHC + 2) / 3;               // chunks of a token's post and comb dots (7)
-constexpr int kDGroupChunks = kDUrgMax + kDMaxTg * kDDef; // record chunks of one slice (70)
-constexpr int kDListMax = kDUrgMax + kDDef;               // chunks a workgroup sums (21)
-constexpr int kDRounds = (kDListMax + 7) / 8;             // in rounds of 8 half-waves (3)
-constexpr int kDTileB = kDMaxTg * kDMaxChunks * 16;       // LDS tile of the streams (16 KB)
+constexpr int kDGroupChunks = kDUrgMax + kDMaxTg * kDDef; // record chunks of one slice (208)
+constexpr int kDListMax = kDUrgMax + kDDef;               // chunks a workgroup sums (47)
+constexpr int kDRounds = (kDListMax + 7) / 8;             // in rounds of 8 half-waves (6)
+constexpr int kDTileMaxB = kDMaxTg * kDMaxChunks * 16;    // LDS tile of the streams, at most (48 KB)
+constexpr int kDPieceRounds = kDTileMaxB / 16 / kDThreads; // 16-byte pieces of it per thread, at most (12)
+constexpr int kDMaxPass = kDMaxTg / 4;                     // projection passes, at most (6)
 constexpr int kDMaxRetry = 1 << 14;
 
 struct DecArgs {
@@ -60,6 +64,7 @@ struct DecArgs {
     const void *hc_fn;
     const float *hc_scale, *hc_base;
     int T, H, fn_rows, Tg, hs;
+    int tile_b; // bytes of the LDS tile: [Tg][4][hs / 8] 16-byte chunks rounded up to 256 of them
     float inv_k, rms_eps, pre_eps, sk_eps, post_mult; // inv_k = 1 / (4H)
     int iters, head;
     uint16_t *y;
@@ -137,14 +142,15 @@ template <int V> __device__ __forceinline__ void wave_sums(const float (&v)[V], 
     }
 }
 
-// P tokens per projection pass (1, 2 or 4); a group of more than 4 tokens takes two passes.
+// P tokens per projection pass (1, 2 or 4); a group of more than 4 tokens takes several.
+// The tile of the streams is dynamic LDS: a.tile_b bytes, then 16 zero bytes.
 // kPost: the post-map in front, on the workgroup's tile (mhc_post_pre_fused).
 template <typename WT, int P, bool kPost>
 __global__ __launch_bounds__(kDThreads) void pre_decode_kernel(DecArgs a)
 {
     constexpr int V = (P * kDF + 3) / 4 * 4; // a pass's values per thread, padded to a multiple of 4
-    __shared__ __align__(16) unsigned char tile[kDTileB + 16];  // [nt][4][nch] chunks, then 16 zero bytes
-    __shared__ float part[2][4][V];                             // [pass][wave][value]
+    extern __shared__ __align__(16) unsigned char tile[];      // [nt][4][nch] chunks, then 16 zero bytes
+    __shared__ float part[kDMaxPass][4][V];                     // [pass][wave][value]
     __shared__ float usum[3 * kDUrgMax];                        // pre dots [4][nt], then sums of squares [nt]
     __shared__ float dsum[3 * kDDef];                           // the designated token's post and comb dots
     __shared__ float dummy[kWave];
@@ -169,32 +175,45 @@ __global__ __launch_bounds__(kDThreads) void pre_decode_kernel(DecArgs a)
 
     // ---- the tokens' slice of the streams: piece p = tid + 256 k is chunk p of the tile
     // [nt][4][nch] (stream row (t, i), h = h0 + 8 j); pieces past the tile or past H read 0
+    // (rounds k with k 256 >= npieces are skipped: a wave-uniform test)
     const int npieces = nt * kHC * nch;
     const __amdgpu_buffer_rsrc_t vres =
         buf_view_uniform(a.res + (size_t)t0 * kHC * H, (uint32_t)((size_t)nt * kHC * H * sizeof(uint16_t)));
-    u32x4 rp[kDTileB / 16 / kDThreads];
+    u32x4 rp[kDPieceRounds];
 #pragma unroll
-    for (int k = 0; k < kDTileB / 16 / kDThreads; ++k) {
-        const int p = tid + k * kDThreads;
-        const int row = p / nch, j = p - row * nch; // row = 4 t + i
-        const int h = h0 + 8 * j;
-        const uint32_t o = p < npieces && h < H ? ((uint32_t)row * (uint32_t)H + (uint32_t)h) * 2u : kOob;
-        rp[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vres, (int)o, 0, 0));
+    for (int k = 0; k < kDPieceRounds; ++k) {
+        if (k * kDThreads < npieces) {
+            const int p = tid + k * kDThreads;
+            const int row = p / nch, j = p - row * nch; // row = 4 t + i
+            const int h = h0 + 8 * j;
+            const uint32_t o = p < npieces && h < H ? ((uint32_t)row * (uint32_t)H + (uint32_t)h) * 2u : kOob;
+            rp[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vres, (int)o, 0, 0));
+        }
     }
-    // kPost: the x piece of item tid = (t, j) of the tile (nt nch <= 256 items: one a thread),
+    // kPost: the x pieces of items tid + 256 k = (t, j) of the tile (nt nch <= 768 items),
     // and the tokens' post and comb values into LDS
-    u32x4 xw = {0u, 0u, 0u, 0u};
+    constexpr int kXR = kPost ? kDMaxTg * (kDMaxChunks / kHC) / kDThreads : 1; // 3
+    const int nitems = nt * nch;
+    u32x4 xw[kXR];
     if constexpr (kPost) {
         const __amdgpu_buffer_rsrc_t vx =
             buf_view_uniform(a.x + (size_t)t0 * H, (uint32_t)((size_t)nt * H * sizeof(uint16_t)));
-        const int t = tid / nch, j = tid - t * nch;
-        const int h = h0 + 8 * j;
-        const uint32_t o = tid < nt * nch && h < H ? ((uint32_t)t * (uint32_t)H + (uint32_t)h) * 2u : kOob;
-        xw = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vx, (int)o, 0, 0));
-        if (tid < kHC * nt) {
-            coefs[tid] = a.post_in[(size_t)t0 * kHC + tid];
-        } else if (tid >= 64 && tid < 64 + kHC * kHC * nt) {
-            coefs[kHC * kDMaxTg + tid - 64] = a.comb_in[(size_t)t0 * kHC * kHC + tid - 64];
+#pragma unroll
+        for (int k = 0; k < kXR; ++k) {
+            if (k * kDThreads < nitems) {
+                const int q = tid + k * kDThreads;
+                const int t = q / nch, j = q - t * nch;
+                const int h = h0 + 8 * j;
+                const uint32_t o = q < nitems && h < H ? ((uint32_t)t * (uint32_t)H + (uint32_t)h) * 2u : kOob;
+                xw[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vx, (int)o, 0, 0));
+            }
+        }
+        for (int v = tid; v < (kHC + kHC * kHC) * nt; v += kDThreads) {
+            if (v < kHC * nt) {
+                coefs[v] = a.post_in[(size_t)t0 * kHC + v];
+            } else {
+                coefs[kHC * kDMaxTg + v - kHC * nt] = a.comb_in[(size_t)t0 * kHC * kHC + v - kHC * nt];
+            }
         }
     }
     // ---- this thread's weights: rows 12 g + r of chunk c
@@ -215,11 +234,14 @@ __global__ __launch_bounds__(kDThreads) void pre_decode_kernel(DecArgs a)
         }
     }
 #pragma unroll
-    for (int k = 0; k < kDTileB / 16 / kDThreads; ++k) {
-        *reinterpret_cast<u32x4 *>(tile + (tid + k * kDThreads) * 16) = rp[k];
+    for (int k = 0; k < kDPieceRounds; ++k) {
+        if (k * kDThreads < npieces) {
+            *reinterpret_cast<u32x4 *>(tile + (tid + k * kDThreads) * 16) = rp[k];
+        }
     }
+    const int zpad = a.tile_b; // the 16 zero bytes
     if (tid == 0) {
-        *reinterpret_cast<u32x4 *>(tile + kDTileB) = u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4 *>(tile + zpad) = u32x4{0u, 0u, 0u, 0u};
         badf = 0;
     }
     __syncthreads();
@@ -227,11 +249,14 @@ __global__ __launch_bounds__(kDThreads) void pre_decode_kernel(DecArgs a)
     // ---- kPost: the post-map of item (t, j): the new streams out[n] = x post[n] + sum_o res[o]
     // comb[o][n] (mhc_post's products in its order), over the old ones in the tile and to `out`
     if constexpr (kPost) {
-        const int t = tid / nch, j = tid - t * nch;
+        const __amdgpu_buffer_rsrc_t vo =
+            buf_view_uniform(a.out + (size_t)t0 * kHC * H, (uint32_t)((size_t)nt * kHC * H * sizeof(uint16_t)));
+#pragma unroll
+        for (int k = 0; k < kXR; ++k) {
+        const int q = tid + k * kDThreads;
+        const int t = q / nch, j = q - t * nch;
         const int h = h0 + 8 * j;
-        if (tid < nt * nch && h < H) {
-            const __amdgpu_buffer_rsrc_t vo =
-                buf_view_uniform(a.out + (size_t)t0 * kHC * H, (uint32_t)((size_t)nt * kHC * H * sizeof(uint16_t)));
+        if (k * kDThreads < nitems && q < nitems && h < H) {
             u32x4 rw[kHC];
 #pragma unroll
             for (int o = 0; o < kHC; ++o) {
@@ -244,8 +269,8 @@ __global__ __launch_bounds__(kDThreads) void pre_decode_kernel(DecArgs a)
                 u32x4 nw;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    float lo = bf16_lo(xw[q]) * cp[n];
-                    float hi = bf16_hi(xw[q]) * cp[n];
+                    float lo = bf16_lo(xw[k][q]) * cp[n];
+                    float hi = bf16_hi(xw[k][q]) * cp[n];
 #pragma unroll
                     for (int o = 0; o < kHC; ++o) {
                         lo = fmaf(bf16_lo(rw[o][q]), cc[o * kHC + n], lo);
@@ -258,6 +283,7 @@ __global__ __launch_bounds__(kDThreads) void pre_decode_kernel(DecArgs a)
                                                        0, 2);
             }
         }
+        }
         __syncthreads();
     }
 
@@ -269,7 +295,7 @@ __global__ __launch_bounds__(kDThreads) void pre_decode_kernel(DecArgs a)
 #pragma unroll
         for (int tl = 0; tl < P; ++tl) {
             const int t = pass * P + tl;
-            const int xo = cval && t < nt ? (t * kHC * nch + c) * 16 : kDTileB;
+            const int xo = cval && t < nt ? (t * kHC * nch + c) * 16 : zpad;
             const u32x4 xr = *reinterpret_cast<const u32x4 *>(tile + xo);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -326,19 +352,19 @@ __global__ __launch_bounds__(kDThreads) void pre_decode_kernel(DecArgs a)
     auto chunk_off = [&](int q, int sli) -> uint32_t {
         return (((uint32_t)x * kDGroupChunks + (uint32_t)q) * kDSlices + (uint32_t)sli) * 16u;
     };
-    if (tid < nck) {
+    for (int q = tid; q < nck; q += kDThreads) {
         float vals[3];
 #pragma unroll
         for (int e = 0; e < 3; ++e) {
             float val = 0.0f;
-            if (tid < nu) {
-                const int u = 3 * tid + e;
+            if (q < nu) {
+                const int u = 3 * q + e;
                 if (u < 5 * nt) {
                     const int f = u / nt, t = u - f * nt;
                     val = rec_val(t, f < kHC ? f : kMix);
                 }
             } else {
-                const int dq = tid - nu;
+                const int dq = q - nu;
                 const int t = dq / kDDef, d = dq - kDDef * t;
                 const int fi = 3 * d + e;
                 if (fi < kMix - kHC) {
@@ -348,7 +374,7 @@ __global__ __launch_bounds__(kDThreads) void pre_decode_kernel(DecArgs a)
             vals[e] = val;
         }
         const u32x4 chunk = {__float_as_uint(vals[0]), __float_as_uint(vals[1]), __float_as_uint(vals[2]), tag};
-        __builtin_amdgcn_raw_buffer_store_b128(chunk, vrec, (int)chunk_off(tid, s), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(chunk, vrec, (int)chunk_off(q, s), 0, 0);
     }
     // the record is in L2 before this workgroup reads it back with the others'
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -356,7 +382,8 @@ __global__ __launch_bounds__(kDThreads) void pre_decode_kernel(DecArgs a)
 
     // ---- the group's records: list entry e < nu is urgent chunk e, entries nu .. nu + 6 the
     // post and comb chunks of token s (workgroup s < nt, when there are post and comb).
-    // Half-wave hw takes entries hw, hw + 8, hw + 16; lane sl of it loads slice sl.
+    // Half-wave hw takes entries hw + 8 k; lane sl of it loads slice sl.  Rounds k with 8 k >=
+    // nlist are skipped (a wave-uniform test).
     const bool designated = !a.head && s < nt;
     const int nlist = nu + (designated ? kDDef : 0);
     const int hw = tid >> 5, sl = tid & 31;
@@ -364,28 +391,32 @@ __global__ __launch_bounds__(kDThreads) void pre_decode_kernel(DecArgs a)
     auto load_list = [&](u32x4(&rr)[kDRounds]) {
 #pragma unroll
         for (int k = 0; k < kDRounds; ++k) {
-            const int e = k * 8 + hw;
-            const int q = e < nu ? e : nu + kDDef * s + (e - nu);
-            const uint32_t o = e < nlist ? chunk_off(q, sl) : kOob;
-            rr[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrec, (int)o, 0, 16));
+            if (k * 8 < nlist) {
+                const int e = k * 8 + hw;
+                const int q = e < nu ? e : nu + kDDef * s + (e - nu);
+                const uint32_t o = e < nlist ? chunk_off(q, sl) : kOob;
+                rr[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrec, (int)o, 0, 16));
+            }
         }
     };
     auto take_list = [&](const u32x4(&rr)[kDRounds]) {
         int bad = 0;
 #pragma unroll
         for (int k = 0; k < kDRounds; ++k) {
-            const int e = k * 8 + hw;
-            if (e < nlist && rr[k][3] != want) {
-                bad = 1;
+            if (k * 8 < nlist) {
+                const int e = k * 8 + hw;
+                if (e < nlist && rr[k][3] != want) {
+                    bad = 1;
+                }
+                const float v0 = half_sum(__uint_as_float(rr[k][0]));
+                const float v1 = half_sum(__uint_as_float(rr[k][1]));
+                const float v2 = half_sum(__uint_as_float(rr[k][2]));
+                float *dst = sl == kHalfSumLane && e < nlist ? (e < nu ? usum + 3 * e : dsum + 3 * (e - nu))
+                                                             : dummy + (lane & 0x3C);
+                dst[0] = v0;
+                dst[1] = v1;
+                dst[2] = v2;
             }
-            const float v0 = half_sum(__uint_as_float(rr[k][0]));
-            const float v1 = half_sum(__uint_as_float(rr[k][1]));
-            const float v2 = half_sum(__uint_as_float(rr[k][2]));
-            float *dst = sl == kHalfSumLane && e < nlist ? (e < nu ? usum + 3 * e : dsum + 3 * (e - nu))
-                                                         : dummy + (lane & 0x3C);
-            dst[0] = v0;
-            dst[1] = v1;
-            dst[2] = v2;
         }
         if (bad) {
             badf = 1;
@@ -418,8 +449,9 @@ __global__ __launch_bounds__(kDThreads) void pre_decode_kernel(DecArgs a)
         if (badf) {
             if (tid < 3 * kDUrgMax) {
                 usum[tid] = __builtin_nanf("");
-            } else if (tid >= 64 && tid < 64 + 3 * kDDef) {
-                dsum[tid - 64] = __builtin_nanf("");
+            }
+            if (tid >= 3 * kWave && tid < 3 * kWave + 3 * kDDef) {
+                dsum[tid - 3 * kWave] = __builtin_nanf("");
             }
         }
         __syncthreads();
@@ -486,18 +518,40 @@ __global__ __launch_bounds__(kDThreads) void pre_decode_kernel(DecArgs a)
     }
 }
 
+template <typename WT, int P, bool kPost>
+hipError_t launch_decode_p(const DecArgs &a, hipStream_t stream)
+{
+    // the dynamic-LDS limit is a per-device attribute: raised once on each device to the
+    // largest tile
+    static std::atomic<bool> attr_set[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= 64) {
+        return e != hipSuccess ? e : hipErrorInvalidDevice;
+    }
+    if (!attr_set[dev].load(std::memory_order_acquire)) {
+        e = hipFuncSetAttribute((const void *)pre_decode_kernel<WT, P, kPost>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kDTileMaxB + 16);
+        if (e != hipSuccess) {
+            return e;
+        }
+        attr_set[dev].store(true, std::memory_order_release);
+    }
+    pre_decode_kernel<WT, P, kPost>
+        <<<dim3(kDGroups * kDSlices), dim3(kDThreads), (size_t)a.tile_b + 16, stream>>>(a);
+    return hipGetLastError();
+}
+
 template <typename WT, bool kPost>
 hipError_t launch_decode_t(const DecArgs &a, hipStream_t stream)
 {
-    const dim3 grid(kDGroups * kDSlices), block(kDThreads);
     if (a.Tg <= 1) {
-        pre_decode_kernel<WT, 1, kPost><<<grid, block, 0, stream>>>(a);
-    } else if (a.Tg <= 2) {
-        pre_decode_kernel<WT, 2, kPost><<<grid, block, 0, stream>>>(a);
-    } else {
-        pre_decode_kernel<WT, 4, kPost><<<grid, block, 0, stream>>>(a);
+        return launch_decode_p<WT, 1, kPost>(a, stream);
     }
-    return hipGetLastError();
+    if (a.Tg <= 2) {
+        return launch_decode_p<WT, 2, kPost>(a, stream);
+    }
+    return launch_decode_p<WT, 4, kPost>(a, stream);
 }
 
 DecArgs decode_args(const uint16_t *res, const void *hc_fn, int fn_rows, const float *hc_scale,
@@ -515,6 +569,7 @@ DecArgs decode_args(const uint16_t *res, const void *hc_fn, int fn_rows, const f
     a.fn_rows = fn_rows;
     a.Tg = (int)((T + kDGroups - 1) / kDGroups);
     a.hs = (int)(8 * ((H + 8 * kDSlices - 1) / (8 * kDSlices)));
+    a.tile_b = (a.Tg * kHC * (a.hs / 8) + kDThreads - 1) / kDThreads * kDThreads * 16;
     a.inv_k = 1.0f / (float)(kHC * H);
     a.rms_eps = rms_eps;
     a.pre_eps = pre_eps;

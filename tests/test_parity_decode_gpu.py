@@ -1,8 +1,8 @@
-"""GPU parity of the pre-map's small-batch form: one launch for 1 <= T <= 64 (16-byte rows,
+"""GPU parity of the pre-map's small-batch form: one launch for 1 <= T <= 192 (16-byte rows,
 H <= 8192), a group of 32 workgroups per XCD splitting K over the group's ceil(T / 8)
 tokens, the partial sums exchanged through the XCD's L2, the weights read as given.
 
-The shapes span one to eight tokens per group (one and two projection passes), groups left
+The shapes span one to 24 tokens per group (one to six projection passes), groups left
 without tokens (T < 8 and ragged T), slices that H leaves partly or wholly empty (H not a
 multiple of 256, H below 256) and the widest slice (H = 8192).  Every token is compared with
 the fp64 oracle at the stated tolerances (fp32 mixes 1e-5, bf16 outputs 2^-7 |ref| + 1e-3).
@@ -47,10 +47,11 @@ def _run(inp, workspace=None, **kw):
     return bits_of(y), f32_of(post), f32_of(comb), f32_of(pre)
 
 
-# (T, H): tokens per group ceil(T / 8) from 1 to 8; slice width 8 ceil(H / 256) from 8 to 256
+# (T, H): tokens per group ceil(T / 8) from 1 to 24; slice width 8 ceil(H / 256) from 8 to 256
 DECODE_SHAPES = [(1, 7168), (2, 4096), (3, 7168), (7, 2048), (8, 7168), (9, 1024), (16, 4096), (17, 7200),
                  (24, 8192), (31, 2056), (32, 7168), (33, 6144), (40, 7168), (57, 3000), (63, 8192), (64, 7168),
-                 (32, 8), (5, 64), (64, 248), (12, 520)]
+                 (32, 8), (5, 64), (64, 248), (12, 520), (65, 7168), (100, 4096), (128, 7168), (131, 1000),
+                 (150, 2056), (185, 7200), (192, 8192), (192, 7168), (192, 8)]
 
 
 @pytest.mark.parametrize("T,H", DECODE_SHAPES)
@@ -71,7 +72,7 @@ def test_decode_scale_vectors_and_base():
     check_pre_all_tokens(inp, _run(inp), "decode scales")
 
 
-@pytest.mark.parametrize("T", [1, 32, 64])
+@pytest.mark.parametrize("T", [1, 32, 64, 192])
 def test_decode_bf16_weights(T):
     """mhc_pre_fused_bf16 on the small-batch form: bf16 weights widen exactly to fp32."""
     mhc = _mhc()
@@ -85,7 +86,7 @@ def test_decode_bf16_weights(T):
     check_pre_all_tokens(inp, (bits_of(y), f32_of(post), f32_of(comb), f32_of(pre)), f"decode bf16 weights T={T}")
 
 
-@pytest.mark.parametrize("T,H", [(32, 7168), (5, 4096), (64, 1000 + 24)])
+@pytest.mark.parametrize("T,H", [(32, 7168), (5, 4096), (64, 1000 + 24), (160, 7168)])
 def test_decode_weighted_head(T, H):
     """mhc_head (the pre group alone, 4 weight rows) on the small-batch form."""
     mhc = _mhc()
@@ -104,13 +105,13 @@ def test_decode_stale_and_garbage_workspace():
     own oracle."""
     mhc = _mhc()
     H = 4096
-    need = max(mhc.mhc_pre_fused_workspace_bytes(T, H) for T in (32, 64, 1100))
+    need = max(mhc.mhc_pre_fused_workspace_bytes(T, H) for T in (32, 64, 192, 1100))
     ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
     a = layer_inputs(32, H, cfg=750)
     check_pre_all_tokens(a, _run(a, workspace=ws), "garbage workspace")
     b = layer_inputs(32, H, cfg=751)
     check_pre_all_tokens(b, _run(b, workspace=ws), "workspace after another call")
-    _run(layer_inputs(64, H, cfg=752), workspace=ws)
+    _run(layer_inputs(192, H, cfg=752), workspace=ws)
     c = layer_inputs(32, H, cfg=753)
     check_pre_all_tokens(c, _run(c, workspace=ws), "workspace after another T")
     _run(layer_inputs(1100, H, cfg=754), workspace=ws)
@@ -123,10 +124,10 @@ def test_decode_keeps_the_stored_split():
     workspace leave the split intact: the two-pass call still equals mhc_pre_fused."""
     mhc = _mhc()
     H = 2048
-    big = layer_inputs(100, H, cfg=756)
+    big = layer_inputs(300, H, cfg=756)
     small = layer_inputs(32, H, cfg=757)
     fn, sc, base = to_dev_f32(big.hc_fn), to_dev_f32(big.hc_scale), to_dev_f32(big.hc_base)
-    ws = torch.empty(max(mhc.mhc_pre_fused_workspace_bytes(T, H) for T in (32, 100)), dtype=torch.uint8,
+    ws = torch.empty(max(mhc.mhc_pre_fused_workspace_bytes(T, H) for T in (32, 300)), dtype=torch.uint8,
                      device="cuda")
     mhc.mhc_pre_split_weights(fn, ws)
     for _ in range(2):

@@ -6,7 +6,7 @@ every token of y, post_next, comb_next and pre_next must match the fp64 oracle's
 over that `out` with the next weights, at the pre-map's tolerances (fp32 mixes 1e-5, bf16
 rows 2^-7 |ref| + 1e-3).  The one-pass form runs for 16-byte rows with T >= 1024 and
 1024 < H <= 8192; the shapes span its slice widths (2 to 8 waves per workgroup), ragged
-token counts and H off the 32-wide blocks.  The small-batch form (16-byte rows, T <= 64,
+token counts and H off the 32-wide blocks.  The small-batch form (16-byte rows, T <= 192,
 H <= 8192) is one launch too: the post-map on each workgroup's tile, then the pre-map on
 it.  The other shapes take the post-map and then the pre-map."""
 import numpy as np
@@ -85,9 +85,10 @@ ONE_PASS = [(1024, 2048), (1037, 1056), (1100, 2080), (1031, 4096), (1500, 4104)
             (1027, 7200), (1033, 8192), (2047, 5000)]
 # post-map then pre-map: H outside both one-launch ranges, rows not 16-byte multiples, or
 # between the small-batch and one-pass token counts
-TWO_PASS = [(300, 1000), (900, 4096), (64, 7169), (1030, 1024), (1030, 8200), (65, 7168), (32, 8200)]
-# the small-batch form with the post-map in front (one to eight tokens per group)
-SMALL = [(1, 8), (16, 256), (1, 7168), (5, 4096), (32, 7168), (33, 2056), (64, 8192), (17, 7200)]
+TWO_PASS = [(300, 1000), (900, 4096), (64, 7169), (1030, 1024), (1030, 8200), (193, 7168), (32, 8200)]
+# the small-batch form with the post-map in front (one to 24 tokens per group)
+SMALL = [(1, 8), (16, 256), (1, 7168), (5, 4096), (32, 7168), (33, 2056), (64, 8192), (17, 7200), (97, 1000),
+         (128, 7168), (192, 4096)]
 
 
 @pytest.mark.parametrize("T,H", ONE_PASS)

@@ -59,11 +59,11 @@ def test_presplit_equals_pre_fused(T, H):
 
 
 def test_presplit_uses_the_stored_split():
-    """The two-pass form (here T = 100: above the small-batch form, below the one-read
+    """The two-pass form (here T = 300: above the small-batch form, below the one-read
     form) reads the stored split, not hc_fn: a split of other weights gives the results of
     those weights (the documented contract for a stale split)."""
     mhc = _mhc()
-    T, H = 100, 2048
+    T, H = 300, 2048
     a, b = layer_inputs(T, H, cfg=930), layer_inputs(T, H, cfg=931)
     res = to_dev_bf16(a.res)
     sc, base = to_dev_f32(a.hc_scale), to_dev_f32(a.hc_base)
