@@ -52,12 +52,7 @@ constexpr int kDF = kDRows + 1;              // partial values of a thread per t
 constexpr int kDUrgMax = (5 * kDMaxTg + 2) / 3;           // chunks of pre dots and sums of squares (40)
 constexpr int kDDef = (kMix - kHC + 2) / 3;               // chunks of a token's post and comb dots (7)
 constexpr int kDGroupChunks = kDUrgMax + kDMaxTg * kDDef; // record chunks of one slice (208)
-constexpr int kDListMax = kDUrgMax + kDDef;               // chunks a workgroup sums (47)
-constexpr int kDRounds = (kDListMax + 7) / 8;             // in rounds of 8 half-waves (6)
 constexpr int kDTileMaxB = kDMaxTg * kDMaxChunks * 16;    // LDS tile of the streams, at most (48 KB)
-constexpr int kDPieceRounds = kDTileMaxB / 16 / kDThreads; // 16-byte pieces of it per thread, at most (12)
-constexpr int kDMaxPass = kDMaxTg / 4;                     // projection passes, at most (6)
-constexpr int kDMaxRetry = 1 << 14;
 
 struct DecArgs {
     const uint16_t *res;
@@ -143,18 +138,29 @@ template <int V> __device__ __forceinline__ void wave_sums(const float (&v)[V], 
 }
 
 // P tokens per projection pass (1, 2 or 4); a group of more than 4 tokens takes several.
-// The tile of the streams is dynamic LDS: a.tile_b bytes, then 16 zero bytes.
 // kPost: the post-map in front, on the workgroup's tile (mhc_post_pre_fused).
-template <typename WT, int P, bool kPost>
+// kBig: more than 8 tokens per group (up to 24).  The tile of the streams is then dynamic
+// LDS (a.tile_b bytes, then 16 zero bytes) and the rounds of loads past the group's tokens
+// are skipped by wave-uniform tests; with at most 8 tokens every round is issued (a straight
+// run of loads, the loads past the tile reading zero) and the tile is static.
+template <typename WT, int P, bool kPost, bool kBig>
 __global__ __launch_bounds__(kDThreads) void pre_decode_kernel(DecArgs a)
 {
     constexpr int V = (P * kDF + 3) / 4 * 4; // a pass's values per thread, padded to a multiple of 4
-    extern __shared__ __align__(16) unsigned char tile[];      // [nt][4][nch] chunks, then 16 zero bytes
-    __shared__ float part[kDMaxPass][4][V];                     // [pass][wave][value]
-    __shared__ float usum[3 * kDUrgMax];                        // pre dots [4][nt], then sums of squares [nt]
+    constexpr int kTg = kBig ? kDMaxTg : 8;  // tokens of a group, at most
+    constexpr int kTileB = kTg * kDMaxChunks * 16;
+    constexpr int kPR = kTileB / 16 / kDThreads;                 // 16-byte pieces per thread (4 or 12)
+    constexpr int kUrg = (5 * kTg + 2) / 3;                      // urgent chunks, at most
+    constexpr int kRnd = (kUrg + kDDef + 7) / 8;                 // rounds of record loads (3 or 6)
+    constexpr int kNP = kTg / 4 > 0 ? kTg / 4 : 1;               // projection passes, at most
+    __shared__ __align__(16) unsigned char tile_st[kBig ? 16 : kTileB + 16];
+    extern __shared__ __align__(16) unsigned char tile_dyn[];
+    unsigned char *const tile = kBig ? tile_dyn : tile_st;      // [nt][4][nch] chunks, then 16 zero bytes
+    __shared__ float part[kNP][4][V];                           // [pass][wave][value]
+    __shared__ float usum[3 * kUrg];                            // pre dots [4][nt], then sums of squares [nt]
     __shared__ float dsum[3 * kDDef];                           // the designated token's post and comb dots
     __shared__ float dummy[kWave];
-    __shared__ float coefs[kDMaxTg * (kHC + kHC * kHC)]; // kPost: post [nt][4] at 0, comb [nt][16] at 4 kDMaxTg
+    __shared__ float coefs[kTg * (kHC + kHC * kHC)]; // kPost: post [nt][4] at 0, comb [nt][16] at 4 kTg
     __shared__ int badf;
 
     const int tid = threadIdx.x;
@@ -179,10 +185,10 @@ __global__ __launch_bounds__(kDThreads) void pre_decode_kernel(DecArgs a)
     const int npieces = nt * kHC * nch;
     const __amdgpu_buffer_rsrc_t vres =
         buf_view_uniform(a.res + (size_t)t0 * kHC * H, (uint32_t)((size_t)nt * kHC * H * sizeof(uint16_t)));
-    u32x4 rp[kDPieceRounds];
+    u32x4 rp[kPR];
 #pragma unroll
-    for (int k = 0; k < kDPieceRounds; ++k) {
-        if (k * kDThreads < npieces) {
+    for (int k = 0; k < kPR; ++k) {
+        if (!kBig || k * kDThreads < npieces) {
             const int p = tid + k * kDThreads;
             const int row = p / nch, j = p - row * nch; // row = 4 t + i
             const int h = h0 + 8 * j;
@@ -190,9 +196,8 @@ __global__ __launch_bounds__(kDThreads) void pre_decode_kernel(DecArgs a)
             rp[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vres, (int)o, 0, 0));
         }
     }
-    // kPost: the x pieces of items tid + 256 k = (t, j) of the tile (nt nch <= 768 items),
-    // and the tokens' post and comb values into LDS
-    constexpr int kXR = kPost ? kDMaxTg * (kDMaxChunks / kHC) / kDThreads : 1; // 3
+    // kPost: the x pieces of items tid + 256 k = (t, j) of the tile (nt nch <= 768 items)
+    constexpr int kXR = kPost ? kTg * (kDMaxChunks / kHC) / kDThreads : 1; // 1 or 3
     const int nitems = nt * nch;
     u32x4 xw[kXR];
     if constexpr (kPost) {
@@ -200,7 +205,7 @@ __global__ __launch_bounds__(kDThreads) void pre_decode_kernel(DecArgs a)
             buf_view_uniform(a.x + (size_t)t0 * H, (uint32_t)((size_t)nt * H * sizeof(uint16_t)));
 #pragma unroll
         for (int k = 0; k < kXR; ++k) {
-            if (k * kDThreads < nitems) {
+            if (!kBig || k * kDThreads < nitems) {
                 const int q = tid + k * kDThreads;
                 const int t = q / nch, j = q - t * nch;
                 const int h = h0 + 8 * j;
@@ -212,7 +217,7 @@ __global__ __launch_bounds__(kDThreads) void pre_decode_kernel(DecArgs a)
             if (v < kHC * nt) {
                 coefs[v] = a.post_in[(size_t)t0 * kHC + v];
             } else {
-                coefs[kHC * kDMaxTg + v - kHC * nt] = a.comb_in[(size_t)t0 * kHC * kHC + v - kHC * nt];
+                coefs[kHC * kTg + v - kHC * nt] = a.comb_in[(size_t)t0 * kHC * kHC + v - kHC * nt];
             }
         }
     }
@@ -234,12 +239,12 @@ __global__ __launch_bounds__(kDThreads) void pre_decode_kernel(DecArgs a)
         }
     }
 #pragma unroll
-    for (int k = 0; k < kDPieceRounds; ++k) {
-        if (k * kDThreads < npieces) {
+    for (int k = 0; k < kPR; ++k) {
+        if (!kBig || k * kDThreads < npieces) {
             *reinterpret_cast<u32x4 *>(tile + (tid + k * kDThreads) * 16) = rp[k];
         }
     }
-    const int zpad = a.tile_b; // the 16 zero bytes
+    const int zpad = kBig ? a.tile_b : kTileB; // the 16 zero bytes
     if (tid == 0) {
         *reinterpret_cast<u32x4 *>(tile + zpad) = u32x4{0u, 0u, 0u, 0u};
         badf = 0;
@@ -256,14 +261,14 @@ __global__ __launch_bounds__(kDThreads) void pre_decode_kernel(DecArgs a)
         const int q = tid + k * kDThreads;
         const int t = q / nch, j = q - t * nch;
         const int h = h0 + 8 * j;
-        if (k * kDThreads < nitems && q < nitems && h < H) {
+        if ((!kBig || k * kDThreads < nitems) && q < nitems && h < H) {
             u32x4 rw[kHC];
 #pragma unroll
             for (int o = 0; o < kHC; ++o) {
                 rw[o] = *reinterpret_cast<const u32x4 *>(tile + ((t * kHC + o) * nch + j) * 16);
             }
             const float *cp = coefs + t * kHC;
-            const float *cc = coefs + kHC * kDMaxTg + t * kHC * kHC;
+            const float *cc = coefs + kHC * kTg + t * kHC * kHC;
 #pragma unroll
             for (int n = 0; n < kHC; ++n) {
                 u32x4 nw;
@@ -388,10 +393,10 @@ __global__ __launch_bounds__(kDThreads) void pre_decode_kernel(DecArgs a)
     const int nlist = nu + (designated ? kDDef : 0);
     const int hw = tid >> 5, sl = tid & 31;
     const uint32_t want = tag ^ a.tag_skew;
-    auto load_list = [&](u32x4(&rr)[kDRounds]) {
+    auto load_list = [&](u32x4(&rr)[kRnd]) {
 #pragma unroll
-        for (int k = 0; k < kDRounds; ++k) {
-            if (k * 8 < nlist) {
+        for (int k = 0; k < kRnd; ++k) {
+            if (!kBig || k * 8 < nlist) {
                 const int e = k * 8 + hw;
                 const int q = e < nu ? e : nu + kDDef * s + (e - nu);
                 const uint32_t o = e < nlist ? chunk_off(q, sl) : kOob;
@@ -399,11 +404,11 @@ __global__ __launch_bounds__(kDThreads) void pre_decode_kernel(DecArgs a)
             }
         }
     };
-    auto take_list = [&](const u32x4(&rr)[kDRounds]) {
+    auto take_list = [&](const u32x4(&rr)[kRnd]) {
         int bad = 0;
 #pragma unroll
-        for (int k = 0; k < kDRounds; ++k) {
-            if (k * 8 < nlist) {
+        for (int k = 0; k < kRnd; ++k) {
+            if (!kBig || k * 8 < nlist) {
                 const int e = k * 8 + hw;
                 if (e < nlist && rr[k][3] != want) {
                     bad = 1;
@@ -423,7 +428,7 @@ __global__ __launch_bounds__(kDThreads) void pre_decode_kernel(DecArgs a)
         }
     };
     {
-        u32x4 rr[kDRounds];
+        u32x4 rr[kRnd];
         load_list(rr);
         take_list(rr);
     }
@@ -436,7 +441,7 @@ __global__ __launch_bounds__(kDThreads) void pre_decode_kernel(DecArgs a)
                 badf = 0;
             }
             __syncthreads();
-            u32x4 rr[kDRounds];
+            u32x4 rr[kRnd];
             asm volatile("" ::: "memory");
             load_list(rr);
             take_list(rr);
@@ -447,7 +452,7 @@ __global__ __launch_bounds__(kDThreads) void pre_decode_kernel(DecArgs a)
         }
         // still missing after the bounded reloads: the sums become NaN, so the outputs are NaN
         if (badf) {
-            if (tid < 3 * kDUrgMax) {
+            if (tid < 3 * kUrg) {
                 usum[tid] = __builtin_nanf("");
             }
             if (tid >= 3 * kWave && tid < 3 * kWave + 3 * kDDef) {
@@ -518,8 +523,8 @@ __global__ __launch_bounds__(kDThreads) void pre_decode_kernel(DecArgs a)
     }
 }
 
-template <typename WT, int P, bool kPost>
-hipError_t launch_decode_p(const DecArgs &a, hipStream_t stream)
+template <typename WT, bool kPost>
+hipError_t launch_decode_big(const DecArgs &a, hipStream_t stream)
 {
     // the dynamic-LDS limit is a per-device attribute: raised once on each device to the
     // largest tile
@@ -530,14 +535,14 @@ hipError_t launch_decode_p(const DecArgs &a, hipStream_t stream)
         return e != hipSuccess ? e : hipErrorInvalidDevice;
     }
     if (!attr_set[dev].load(std::memory_order_acquire)) {
-        e = hipFuncSetAttribute((const void *)pre_decode_kernel<WT, P, kPost>,
+        e = hipFuncSetAttribute((const void *)pre_decode_kernel<WT, 4, kPost, true>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, kDTileMaxB + 16);
         if (e != hipSuccess) {
             return e;
         }
         attr_set[dev].store(true, std::memory_order_release);
     }
-    pre_decode_kernel<WT, P, kPost>
+    pre_decode_kernel<WT, 4, kPost, true>
         <<<dim3(kDGroups * kDSlices), dim3(kDThreads), (size_t)a.tile_b + 16, stream>>>(a);
     return hipGetLastError();
 }
@@ -545,13 +550,17 @@ hipError_t launch_decode_p(const DecArgs &a, hipStream_t stream)
 template <typename WT, bool kPost>
 hipError_t launch_decode_t(const DecArgs &a, hipStream_t stream)
 {
+    const dim3 grid(kDGroups * kDSlices), block(kDThreads);
     if (a.Tg <= 1) {
-        return launch_decode_p<WT, 1, kPost>(a, stream);
+        pre_decode_kernel<WT, 1, kPost, false><<<grid, block, 0, stream>>>(a);
+    } else if (a.Tg <= 2) {
+        pre_decode_kernel<WT, 2, kPost, false><<<grid, block, 0, stream>>>(a);
+    } else if (a.Tg <= 8) {
+        pre_decode_kernel<WT, 4, kPost, false><<<grid, block, 0, stream>>>(a);
+    } else {
+        return launch_decode_big<WT, kPost>(a, stream);
     }
-    if (a.Tg <= 2) {
-        return launch_decode_p<WT, 2, kPost>(a, stream);
-    }
-    return launch_decode_p<WT, 4, kPost>(a, stream);
+    return hipGetLastError();
 }
 
 DecArgs decode_args(const uint16_t *res, const void *hc_fn, int fn_rows, const float *hc_scale,
