@@ -154,6 +154,39 @@ __device__ __forceinline__ float sinkhorn_row16(float L, int iters, float eps)
     return P;
 }
 
+// Two matrices per 16-lane row (logits L0 and L1 in the same lane positions), the rounds of
+// both in one loop so that their dependent chains interleave; each result has the bits
+// sinkhorn_row16 gives for it.
+__device__ __forceinline__ void sinkhorn_row16x2(float L0, float L1, int iters, float eps, float &P0, float &P1)
+{
+    float m0 = fmaxf(L0, dpp_quad_xor1(L0));
+    float m1 = fmaxf(L1, dpp_quad_xor1(L1));
+    m0 = fmaxf(m0, dpp_quad_xor2(m0));
+    m1 = fmaxf(m1, dpp_quad_xor2(m1));
+    const float e0 = __expf(L0 - m0);
+    const float e1 = __expf(L1 - m1);
+    float s0 = e0 + dpp_quad_xor1(e0);
+    float s1 = e1 + dpp_quad_xor1(e1);
+    s0 = s0 + dpp_quad_xor2(s0);
+    s1 = s1 + dpp_quad_xor2(s1);
+    P0 = fmaf(e0, fast_rcp(s0), eps);
+    P1 = fmaf(e1, fast_rcp(s1), eps);
+    for (int it = 0; it < iters; ++it) {
+        float r0 = P0 + dpp_quad_xor1(P0);
+        float r1 = P1 + dpp_quad_xor1(P1);
+        r0 = r0 + dpp_quad_xor2(r0);
+        r1 = r1 + dpp_quad_xor2(r1);
+        P0 *= fast_rcp(r0);
+        P1 *= fast_rcp(r1);
+        float c0 = P0 + dpp_row_ror4(P0);
+        float c1 = P1 + dpp_row_ror4(P1);
+        c0 = c0 + dpp_row_ror8(c0);
+        c1 = c1 + dpp_row_ror8(c1);
+        P0 *= fast_rcp(c0);
+        P1 *= fast_rcp(c1);
+    }
+}
+
 // Sum over the 64 lanes of a wavefront (butterfly: every lane gets the total).
 __device__ __forceinline__ float wave_sum(float v)
 {

@@ -72,6 +72,7 @@ struct CoopArgs {
     const void *hc_fn;
     const float *hc_scale, *hc_base;
     int T, H, nhb, fn_rows;
+    int wvec; // hc_fn 16-byte aligned: each lane's 8 weights of a row in 16-byte loads
     int L, R, RR; // collapse lag in iterations, LDS ring slots, record ring slots
     float inv_k, rms_eps, pre_eps, sk_eps, post_mult; // inv_k = 1 / (4H)
     int iters, head;
@@ -100,6 +101,29 @@ __device__ __forceinline__ float weight_elem(const float *w, uint32_t i, __amdgp
 __device__ __forceinline__ float weight_elem(const uint16_t *w, uint32_t i, __amdgpu_buffer_rsrc_t v)
 {
     return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(v, (int)(i * 2u), 0, 0));
+}
+
+// Weights i .. i + 7 (i a multiple of 8, the buffer 16-byte aligned) in 16-byte loads;
+// an index past the view reads zeros.
+__device__ __forceinline__ void load_w8(const float *, uint32_t i, __amdgpu_buffer_rsrc_t v, float (&o)[8])
+{
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+        const u32x4 p = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(v, (int)(i * 4u + 16u * hf), 0, 0));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            o[4 * hf + e] = __uint_as_float(p[e]);
+        }
+    }
+}
+__device__ __forceinline__ void load_w8(const uint16_t *, uint32_t i, __amdgpu_buffer_rsrc_t v, float (&o)[8])
+{
+    const u32x4 p = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(v, (int)(i * 2u), 0, 0));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        o[2 * e] = __uint_as_float(p[e] << 16);
+        o[2 * e + 1] = __uint_as_float(p[e] & 0xFFFF0000u);
+    }
 }
 
 // Sum over the four 16-lane rows of the wave, same bits in every lane: rows (0 + 1) and
@@ -643,18 +667,14 @@ __global__ __launch_bounds__(W * 64) void pre_coop_kernel(CoopArgs a)
     }
     __syncthreads();
     // The loads of steps 0 and 1 (what iterations -2 and -1 would issue: every other memory
-    // operation of those iterations is out of range) go out before the weights, so that their
-    // latency and the weights' overlap; the loop starts at step 0.
+    // operation of those iterations is out of range) go out around the weights, so that their
+    // latency and the weights' overlap; the loop starts at step 0.  Step 1 goes last: the
+    // first projection waits for step 0 and the weights only.
     if constexpr (kPost) {
         load_coef(1, cfA);
         xA = load_x(0);
     }
     load_step(0, bufA);
-    if constexpr (kPost) {
-        load_coef(2, cfB);
-        xB = load_x(1);
-    }
-    load_step(1, bufB);
     {
         const __amdgpu_buffer_rsrc_t vw =
             buf_view_uniform(a.hc_fn, (uint32_t)((size_t)a.fn_rows * kHC * H * sizeof(WT)));
@@ -662,19 +682,34 @@ __global__ __launch_bounds__(W * 64) void pre_coop_kernel(CoopArgs a)
         const bool hok = hb < a.nhb && h < H;
         const WT *wt = reinterpret_cast<const WT *>(a.hc_fn);
         const int r1 = 16 + (c & 7);
+        float v0[kHC][8], v1[kHC][8];
 #pragma unroll
         for (int i = 0; i < kHC; ++i) {
-            float v0[8], v1[8];
             const uint32_t i0 = hok ? (uint32_t)c * kHC * H + (uint32_t)i * H + h : kOob / 4;
             const uint32_t i1 = hok ? (uint32_t)r1 * kHC * H + (uint32_t)i * H + h : kOob / 4;
+            if (a.wvec) {
+                // 16-byte loads: the four lanes g of a row share one 128-byte line, where
+                // element loads touch a line per lane and instruction
+                load_w8(wt, i0, vw, v0[i]);
+                load_w8(wt, i1, vw, v1[i]);
+            } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                v0[e] = weight_elem(wt, i0 + e, vw);
-                v1[e] = weight_elem(wt, i1 + e, vw);
+                for (int e = 0; e < 8; ++e) {
+                    v0[i][e] = weight_elem(wt, i0 + e, vw);
+                    v1[i][e] = weight_elem(wt, i1 + e, vw);
+                }
             }
-            split3x8(v0, b0[i][0], b0[i][1], b0[i][2]);
+        }
+        if constexpr (kPost) {
+            load_coef(2, cfB);
+            xB = load_x(1);
+        }
+        load_step(1, bufB);
+#pragma unroll
+        for (int i = 0; i < kHC; ++i) {
+            split3x8(v0[i], b0[i][0], b0[i][1], b0[i][2]);
             u32x4 hi, mid, lo;
-            split3x8(v1, hi, mid, lo);
+            split3x8(v1[i], hi, mid, lo);
             b1[i][0] = c < 8 ? hi : mid;
             b1[i][1] = c < 8 ? lo : u32x4{0u, 0u, 0u, 0u};
         }
@@ -694,27 +729,38 @@ __global__ __launch_bounds__(W * 64) void pre_coop_kernel(CoopArgs a)
     }
     // Post weights and the Sinkhorn of this workgroup's tokens: token td of the steps j with
     // j mod 2 == s / 16, whose raw comb logits and post pre-activations the loop stored.
-    // Row r of wave w takes the ((round * W + w) * 4 + r)-th of them.
+    // Row r of wave w takes the ((round * W + w) * 4 + r)-th of them and, in the same lanes,
+    // the one 4W further on (two matrices per row: one round where 32 tokens would take two).
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     const int e = lane & 15;
     const int nmine = (nst - (s >> 4) + 1) / 2;
-    for (int base = 0; base < nmine; base += 4 * W) {
-        const int m = base + 4 * w + (lane >> 4);
-        const int j = 2 * m + (s >> 4);
-        const int t = (j * kQGroups + x) * kQTok + td;
-        const bool ok = m < nmine && t < T;
-        float *pc = a.comb + (size_t)(ok ? t : 0) * kHC * kHC + e;
-        float *pp = a.post + (size_t)(ok ? t : 0) * kHC + (e & 3);
-        // device-scope loads: the auxiliary wave stored these, and they must not come from a stale L1 line
-        const float Lg = ok ? __hip_atomic_load(pc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.0f;
-        const float zp = ok && e < kHC ? __hip_atomic_load(pp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.0f;
-        const float P = sinkhorn_row16(Lg, a.iters, a.sk_eps);
-        const float pv = sigmoidf_fast(zp) * a.post_mult;
-        if (ok) {
-            *pc = P;
-            if (e < kHC) {
-                *pp = pv;
+    for (int base = 0; base < nmine; base += 8 * W) {
+        float Lg[2], zp[2];
+        float *pc[2], *pp[2];
+        bool ok[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int m = base + 4 * W * u + 4 * w + (lane >> 4);
+            const int j = 2 * m + (s >> 4);
+            const int t = (j * kQGroups + x) * kQTok + td;
+            ok[u] = m < nmine && t < T;
+            pc[u] = a.comb + (size_t)(ok[u] ? t : 0) * kHC * kHC + e;
+            pp[u] = a.post + (size_t)(ok[u] ? t : 0) * kHC + (e & 3);
+            // device-scope loads: the auxiliary wave stored these, and they must not come from a stale L1 line
+            Lg[u] = ok[u] ? __hip_atomic_load(pc[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.0f;
+            zp[u] = ok[u] && e < kHC ? __hip_atomic_load(pp[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.0f;
+        }
+        float P[2];
+        sinkhorn_row16x2(Lg[0], Lg[1], a.iters, a.sk_eps, P[0], P[1]);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const float pv = sigmoidf_fast(zp[u]) * a.post_mult;
+            if (ok[u]) {
+                *pc[u] = P[u];
+                if (e < kHC) {
+                    *pp[u] = pv;
+                }
             }
         }
     }
@@ -815,6 +861,7 @@ CoopArgs coop_args(const CoopCfg &k, const uint16_t *res, const void *hc_fn, int
     CoopArgs a{};
     a.res = res;
     a.hc_fn = hc_fn;
+    a.wvec = ((uintptr_t)hc_fn & 15u) == 0;
     a.hc_scale = hc_scale;
     a.hc_base = hc_base;
     a.T = (int)T;
